@@ -1,0 +1,178 @@
+"""Seeded synthetic E8RHTLinear layers and activations.
+
+Shared by the tests and the benchmark, for both the GPU library and the CPU
+oracle.  It holds the workload shapes and the random draws only: no codebook,
+no transform, no dequantization.
+
+Recipe (numpy PCG64, numpy.random.default_rng):
+  * a workload has an integer seed; layer k of it draws from
+    default_rng([seed, k]) in this order: sign_in (n_pad), sign_out (m_pad),
+    idx0 (m_pad x n_pad/8), idx1 (same shape, when the recipe has a residual);
+  * signs are 2 * integers(0, 2) - 1 as int8 (Rademacher +-1);
+  * indices are uniform: integers(0, 65536) as uint16, integers(0, 256) as uint8
+    for an 8-bit residual;
+  * activations for batch size B draw from default_rng([seed, k, B]):
+    standard_normal((B, n)) in float64, rounded once (nearest-even) to the
+    activation dtype; both sides consume the rounded values;
+  * weight scale s = 0.02, residual scale s_r = 0.25 for every layer.
+
+Shapes are the checkpoints' layer shapes (SmolLM2-360M, SmolLM3-3B,
+Devstral-Small 24B) with dimensions padded to the next power of two.
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+WSCALE = 0.02
+RESID_SCALE = 0.25
+
+
+def next_pow2(n):
+    p = 1
+    while p < n:
+        p *= 2
+    return p
+
+
+@dataclass(frozen=True)
+class LayerShape:
+    name: str
+    n: int
+    m: int
+    n_pad: int = 0
+    m_pad: int = 0
+
+    def padded(self):
+        return LayerShape(self.name, self.n, self.m,
+                          self.n_pad or next_pow2(self.n), self.m_pad or next_pow2(self.m))
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: str
+    title: str
+    seed: int
+    resid_bits: int          # 0: 2 bpw, 8: 3 bpw (16 + 8), 16: 4 bpw (16 + 16)
+    act_dtype: str           # "f32" | "f16" | "bf16"
+    batches: tuple
+    layers: tuple = field(default_factory=tuple)
+
+    @property
+    def bpw(self):
+        return {0: 2, 8: 3, 16: 4}[self.resid_bits]
+
+
+def _L(name, n, m):
+    return LayerShape(name, n, m).padded()
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", "tiny E8RHTLinear 256->256, fp32, 2 bpw", 1001, 0, "f32", (1,),
+                     (_L("tiny", 256, 256),)),
+    "smollm2_up": Workload("smollm2_up", "SmolLM2-360M MLP up-projection 960->2560, 4 bpw, fp16",
+                           1002, 16, "f16", (1, 5), (_L("up", 960, 2560),)),
+    "smollm3_block": Workload("smollm3_block", "SmolLM3-3B decoder block (7 linears), 3 bpw, fp16",
+                              1003, 8, "f16", (1, 5),
+                              (_L("q", 2048, 2048), _L("k", 2048, 512), _L("v", 2048, 512),
+                               _L("o", 2048, 2048), _L("gate", 2048, 11008), _L("up", 2048, 11008),
+                               _L("down", 11008, 2048))),
+    "devstral_mlp": Workload("devstral_mlp", "Devstral-Small 24B MLP (gate, up, down), 4 bpw, bf16",
+                             1004, 16, "bf16", (1, 4, 16),
+                             (_L("gate", 5120, 32768), _L("up", 5120, 32768), _L("down", 32768, 5120))),
+    "prefill_gateup": Workload("prefill_gateup", "prefill 2048->11008, M=2048 tokens, 3 bpw, bf16",
+                               1005, 8, "bf16", (2048,), (_L("gate", 2048, 11008),)),
+}
+
+
+@dataclass
+class Layer:
+    """One synthetic quantized layer (host numpy arrays)."""
+    shape: LayerShape
+    resid_bits: int
+    sign_in: np.ndarray      # int8 [n_pad]
+    sign_out: np.ndarray     # int8 [m_pad]
+    idx0: np.ndarray         # uint16 [m_pad, n_pad/8]
+    idx1: object             # uint8/uint16 [m_pad, n_pad/8] or None
+    wscale: float = WSCALE
+    resid_scale: float = RESID_SCALE
+
+    @property
+    def n(self):
+        return self.shape.n
+
+    @property
+    def m(self):
+        return self.shape.m
+
+    @property
+    def n_pad(self):
+        return self.shape.n_pad
+
+    @property
+    def m_pad(self):
+        return self.shape.m_pad
+
+    def index_bytes(self):
+        return self.idx0.nbytes + (0 if self.idx1 is None else self.idx1.nbytes)
+
+
+def make_layer(shape, resid_bits, seed, k, rows=None):
+    """Draw layer k of a workload with the given seed.
+
+    rows: optionally keep only the first `rows` rows of the index arrays, used
+    nowhere on the measured path (the draw order is unchanged).
+    """
+    shape = shape.padded()
+    rng = np.random.default_rng([seed, k])
+    sign_in = (2 * rng.integers(0, 2, size=shape.n_pad) - 1).astype(np.int8)
+    sign_out = (2 * rng.integers(0, 2, size=shape.m_pad) - 1).astype(np.int8)
+    gshape = (shape.m_pad, shape.n_pad // 8)
+    idx0 = rng.integers(0, 65536, size=gshape, dtype=np.uint16)
+    idx1 = None
+    if resid_bits == 8:
+        idx1 = rng.integers(0, 256, size=gshape, dtype=np.uint8)
+    elif resid_bits == 16:
+        idx1 = rng.integers(0, 65536, size=gshape, dtype=np.uint16)
+    elif resid_bits != 0:
+        raise ValueError("resid_bits must be 0, 8 or 16")
+    return Layer(shape, resid_bits, sign_in, sign_out, idx0, idx1)
+
+
+def round_to_dtype(x64, dtype):
+    """Round float64 values once, nearest-even, to 'f32' | 'f16' | 'bf16'.
+
+    Returns (values as float64, raw array in that dtype: float32, float16, or
+    uint16 bf16 bit patterns).
+    """
+    x64 = np.asarray(x64, dtype=np.float64)
+    if dtype == "f32":
+        r = x64.astype(np.float32)
+        return r.astype(np.float64), r
+    if dtype == "f16":
+        r = x64.astype(np.float16)
+        return r.astype(np.float64), r
+    if dtype == "bf16":
+        # one rounding to 8 significant bits, ties to even (normal range only)
+        mant, expo = np.frexp(x64)
+        vals = np.ldexp(np.round(np.ldexp(mant, 8)), expo - 8)
+        bits = (vals.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+        return vals, bits
+    raise ValueError(dtype)
+
+
+def make_x(n, B, dtype, seed, k):
+    """Activations [B, n] for layer k: (float64 values, raw dtype array)."""
+    rng = np.random.default_rng([seed, k, B])
+    return round_to_dtype(rng.standard_normal((B, n)), dtype)
+
+
+def workload_layers(key):
+    w = WORKLOADS[key]
+    return [(k, s) for k, s in enumerate(w.layers)]
+
+
+def random_layer(n, m, resid_bits, seed, n_pad=None, m_pad=None):
+    """A layer of arbitrary shape (tests of ragged and tiny shapes)."""
+    shape = LayerShape("t", n, m, n_pad or next_pow2(max(n, 8)), m_pad or next_pow2(max(m, 8)))
+    return make_layer(shape, resid_bits, seed, 0)
