@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the E8RHTLinear forward on one MI355X.
+
+Step = one decode pass (B = 1) through the Devstral-Small 24B-shaped MLP:
+gate 5120->32768, up 5120->32768, down 32768->5120 at 4 bpw (16-bit primary +
+16-bit residual index per 8-weight group), bf16 activations; each layer runs
+input RHT, the decode matmul against the indices and output RHT.  The layers
+are independent calls on seeded synthetic data (no activation between them).
+R copies of the three layers' index arrays (>= 1 GiB in total) are rotated so
+every step reads its indices from HBM, not from the 256 MB Infinity Cache.
+
+value   = sum over the step's layers of (index bytes + x bytes + u bytes)
+          / step time, in GB/s (inputs resident in HBM before timing starts).
+roofline: the decode matmul kernel, timed with events around its launches
+          (same stream) in a second, staged loop over the same steps.
+prefill: the 2048-token prefill of the SmolLM3-3B gate shape (2048->11008,
+          3 bpw), its MFMA matmul timed the same way, in TFLOP/s.
+cpu_baseline: the fp64 oracle on one of the step's layers, on the host cores.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+METRIC = "fused E8-RHT linear: achieved HBM GB/s at B=1 decode; TFLOP/s at prefill"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def act_bytes(dtype):
+    return {"f32": 4, "f16": 2, "bf16": 2}[dtype]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the E8RHTLinear path here has no multi-GPU "
+              "implementation (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import e8_lattice_codebook_amd as glq
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: building codebooks")
+    cb = glq.Codebooks(dev)
+
+    wl = synth.WORKLOADS["devstral_mlp"]
+    B = args.batch
+    host_layers = [synth.make_layer(s, wl.resid_bits, wl.seed, k) for k, s in enumerate(wl.layers)]
+    idx_bytes = sum(l.index_bytes() for l in host_layers)
+    copies = max(2, math.ceil((1 << 30) / idx_bytes))
+    log("bench: %d layers, %.1f MiB of indices per step, %d rotating copies" % (
+        len(host_layers), idx_bytes / 2 ** 20, copies))
+    qls = [[glq.QuantizedLayer.from_synth(l, cb) for l in host_layers] for _ in range(copies)]
+    xs = []
+    for k, l in enumerate(host_layers):
+        _, raw = synth.make_x(l.n, B, wl.act_dtype, wl.seed, k)
+        xs.append(torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16))
+    ys = [torch.empty((B, l.m), dtype=torch.bfloat16, device=dev) for l in host_layers]
+    ws = torch.empty(max(glq.linear_workspace_bytes(q, B) for q in qls[0]), dtype=torch.uint8, device=dev)
+
+    step_bytes = 0
+    gemv_bytes = []
+    for l in host_layers:
+        gb = l.index_bytes() + B * l.n_pad * 4
+        gemv_bytes.append(gb)
+        step_bytes += l.index_bytes() + B * l.n * act_bytes(wl.act_dtype) + B * l.n_pad * 4
+
+    def step(i):
+        row = qls[i % copies]
+        for k in range(len(row)):
+            glq.e8rht_linear(row[k], xs[k], out=ys[k], workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log("bench: timing %d steps" % args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log("bench: %.4f ms/step (wall %.4f), %.1f GB/s" % (ms_per_step, wall * 1e3 / args.steps, value))
+
+    # staged loop: the same three kernels per layer, events around the matmul launches
+    u_bufs = [torch.empty((B, l.n_pad), dtype=torch.float32, device=dev) for l in host_layers]
+    z_bufs = [torch.empty((glq.e8_matmul_splits(q, B), B, q.m_pad), dtype=torch.float32, device=dev)
+              for q in qls[0]]
+    rout_ws = torch.empty(max(1, max(glq.lib().glq_output_rht_workspace_bytes(B, l.m_pad) for l in host_layers)),
+                          dtype=torch.uint8, device=dev)
+    n_ev = args.steps * len(host_layers)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+
+    def staged(i, record):
+        row = qls[i % copies]
+        for k, q in enumerate(row):
+            glq.input_rht(xs[k], q.n_pad, q.sign_in, out=u_bufs[k])
+            if record is not None:
+                record[k][0].record()
+            glq.e8_matmul(q, u_bufs[k], out=z_bufs[k])
+            if record is not None:
+                record[k][1].record()
+            glq.output_rht(z_bufs[k], q.m, q.sign_out, out=ys[k], workspace=rout_ws)
+
+    for i in range(args.warmup):
+        staged(i, None)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        staged(args.warmup + i, evs[i * len(host_layers):(i + 1) * len(host_layers)])
+    torch.cuda.synchronize()
+    per_layer_ms = [[] for _ in host_layers]
+    for i in range(args.steps):
+        for k in range(len(host_layers)):
+            a, b = evs[i * len(host_layers) + k]
+            per_layer_ms[k].append(a.elapsed_time(b))
+    gemv_ms = [float(np.mean(v)) for v in per_layer_ms]
+    # dominant kernel: the decode matmul, all its launches pooled (bytes and time)
+    gemv_total_bytes = sum(gemv_bytes)
+    gemv_total_ms = sum(gemv_ms)
+    achieved = gemv_total_bytes / len(host_layers) / (gemv_total_ms / len(host_layers) * 1e-3) / 1e9
+    log("bench: decode matmul per layer ms %s -> %.1f GB/s" % (["%.4f" % t for t in gemv_ms], achieved))
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "Devstral-Small-24B MLP decode (gate 5120->32768, up 5120->32768, down 32768->5120), "
+                        "4 bpw (16+16-bit E8 indices), B=%d, bf16 activations, uniform seeded indices" % B,
+            "batch": B,
+            "index_bytes_per_step": idx_bytes,
+            "algorithmic_bytes_per_step": step_bytes,
+            "rotating_copies": copies,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gemv_kernel (decode matmul)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "per_layer_ms": [round(t, 5) for t in gemv_ms],
+            "bytes_per_launch": gemv_bytes,
+        },
+    }
+
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(glq, synth, cb, dev, args, log)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(host_layers[0], wl, B, log)
+
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(glq, synth, cb, dev, args, log):
+    import numpy as np
+    import torch
+
+    wl = synth.WORKLOADS["prefill_gateup"]
+    l = synth.make_layer(wl.layers[0], wl.resid_bits, wl.seed, 0)
+    M = wl.batches[0]
+    q = glq.QuantizedLayer.from_synth(l, cb)
+    _, raw = synth.make_x(l.n, M, wl.act_dtype, wl.seed, 0)
+    x = torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
+    u = torch.empty((M, l.n_pad), dtype=torch.float16, device=dev)
+    z = torch.empty((1, M, l.m_pad), dtype=torch.float32, device=dev)
+    y = torch.empty((M, l.m), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(glq.linear_workspace_bytes(q, M), dtype=torch.uint8, device=dev)
+    flops = 2.0 * M * l.m_pad * l.n_pad
+    for _ in range(3):
+        glq.e8rht_linear(q, x, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.prefill_steps):
+        glq.e8rht_linear(q, x, out=y, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    lin_ms = e0.elapsed_time(e1) / args.prefill_steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.prefill_steps)]
+    for a, b in evs:
+        glq.input_rht(x, l.n_pad, q.sign_in, out=u)
+        a.record()
+        glq.e8_matmul(q, u, out=z)
+        b.record()
+        glq.output_rht(z, l.m, q.sign_out, out=y)
+    torch.cuda.synchronize()
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    tflops = flops / (gemm_ms * 1e-3) / 1e12
+    log("bench: prefill linear %.4f ms, MFMA matmul %.4f ms = %.1f TFLOP/s" % (lin_ms, gemm_ms, tflops))
+    return {
+        "workload": "SmolLM3-3B gate 2048->11008 (m_pad 16384), M=2048 tokens, 3 bpw, bf16 activations",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "linear_ms": round(lin_ms, 5),
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (prefill matmul, fp16 MFMA)",
+                     "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops},
+    }
+
+
+def cpu_baseline(layer, wl, B, log):
+    """The oracle (fp64 NumPy, dequantize-then-matmul) on one layer of the step."""
+    import numpy as np
+    import synth
+    from oracle import glq as og
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=None)
+    except Exception:  # noqa: BLE001
+        pass
+    x64, _ = synth.make_x(layer.n, B, wl.act_dtype, wl.seed, 0)
+    log("bench: cpu oracle on one layer (%d x %d)" % (layer.m_pad, layer.n_pad))
+    t0 = time.perf_counter()
+    og.linear(x64, layer.sign_in, layer.sign_out, layer.n_pad, layer.m, layer.idx0, layer.idx1, layer.resid_bits,
+              layer.wscale, layer.resid_scale)
+    dt = time.perf_counter() - t0
+    nbytes = layer.index_bytes() + B * layer.n * act_bytes(wl.act_dtype) + B * layer.n_pad * 4
+    log("bench: cpu oracle %.2f s -> %.3f GB/s" % (dt, nbytes / dt / 1e9))
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": "oracle.glq.linear (fp64 NumPy: dequantize in row blocks, BLAS matmul, FWHTs) on the gate "
+                      "layer (5120->32768, 4 bpw) at B=%d: one of the step's three layers, %.1f s" % (B, dt),
+            "seconds": round(dt, 3)}
+
+
+if __name__ == "__main__":
+    main()

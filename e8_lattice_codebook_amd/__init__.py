@@ -1,0 +1,192 @@
+"""E8RHTLinear (GLQ E8 lattice codebook layers) on AMD MI355X / gfx950.
+
+A thin Python binding over the C ABI of libglq_mi355x.so (include/glq.h):
+every step of the layer runs in the library's HIP kernels; torch supplies
+device memory and the current HIP stream, and this module only marshals
+arguments.  The entry points keep the C names without the glq_ prefix.
+"""
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import GLQ_BF16, GLQ_F16, GLQ_F32, GLQError, GlqLayer  # noqa: F401
+
+CODEBOOK_ENTRIES = 65536
+RESID8_ENTRIES = 256
+
+_DT = {torch.float32: GLQ_F32, torch.float16: GLQ_F16, torch.bfloat16: GLQ_BF16}
+
+
+def lib():
+    return _lib.load()
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dt(dtype):
+    if dtype not in _DT:
+        raise TypeError("dtype must be float32, float16 or bfloat16")
+    return _DT[dtype]
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ---- codebooks ------------------------------------------------------------------
+def e8_codebook(entries=CODEBOOK_ENTRIES):
+    """The E8 codebook as fp16 bit patterns, host numpy uint16 [entries, 8] (glq_e8_codebook)."""
+    out = np.empty((entries, 8), dtype=np.uint16)
+    _lib.check(lib().glq_e8_codebook(out.ctypes.data_as(ctypes.c_void_p), entries), "glq_e8_codebook")
+    return out
+
+
+def codebook_pack(cb_fp16_bits, device="cuda"):
+    """Pack an fp16 codebook [entries, 8] (uint16 bits, host or device) for the kernels."""
+    cb = torch.as_tensor(np.ascontiguousarray(cb_fp16_bits).view(np.int16)) \
+        if isinstance(cb_fp16_bits, np.ndarray) else cb_fp16_bits
+    cb = cb.to(device).contiguous()
+    entries = cb.shape[0]
+    nbytes = lib().glq_codebook_pack_bytes(entries)
+    pack = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    bad = torch.empty(1, dtype=torch.int32, device=device)
+    _lib.check(lib().glq_codebook_pack(_ptr(cb), entries, _ptr(pack), nbytes, _ptr(bad), _stream(pack.device)),
+               "glq_codebook_pack")
+    if int(bad.item()) != 0:
+        raise GLQError(8, "glq_codebook_pack")
+    return pack
+
+
+class Codebooks:
+    """The primary (65,536-entry) and 8-bit residual (256-entry) packs on one device."""
+
+    def __init__(self, device="cuda"):
+        self.device = torch.device(device)
+        self.fp16 = e8_codebook(CODEBOOK_ENTRIES)
+        self.primary = codebook_pack(self.fp16, self.device)
+        self.resid8 = codebook_pack(self.fp16[:RESID8_ENTRIES], self.device)
+
+    def residual(self, resid_bits):
+        return {0: None, 8: self.resid8, 16: self.primary}[resid_bits]
+
+
+# ---- layers ---------------------------------------------------------------------
+class QuantizedLayer:
+    """Device copy of one layer (signs, index arrays) plus its glq_layer descriptor."""
+
+    def __init__(self, n, m, n_pad, m_pad, resid_bits, sign_in, sign_out, idx0, idx1, codebooks,
+                 wscale=0.02, resid_scale=0.25, device=None):
+        device = torch.device(device) if device is not None else codebooks.device
+        self.n, self.m, self.n_pad, self.m_pad = int(n), int(m), int(n_pad), int(m_pad)
+        self.resid_bits = int(resid_bits)
+        self.wscale, self.resid_scale = float(wscale), float(resid_scale)
+        self.sign_in = _to_dev(sign_in, torch.int8, device)
+        self.sign_out = _to_dev(sign_out, torch.int8, device)
+        self.idx0 = _to_dev(idx0, torch.int16, device)
+        self.idx1 = None if idx1 is None else _to_dev(
+            idx1, torch.uint8 if np.asarray(idx1).dtype == np.uint8 else torch.int16, device)
+        self.codebooks = codebooks
+        self.device = device
+        self.desc = GlqLayer(self.n, self.n_pad, self.m, self.m_pad, self.resid_bits, self.wscale, self.resid_scale,
+                             self.sign_in.data_ptr(), self.sign_out.data_ptr(), self.idx0.data_ptr(),
+                             0 if self.idx1 is None else self.idx1.data_ptr(), codebooks.primary.data_ptr(),
+                             0 if resid_bits == 0 else codebooks.residual(resid_bits).data_ptr())
+
+    @classmethod
+    def from_synth(cls, layer, codebooks, device=None):
+        return cls(layer.n, layer.m, layer.n_pad, layer.m_pad, layer.resid_bits, layer.sign_in, layer.sign_out,
+                   layer.idx0, layer.idx1, codebooks, layer.wscale, layer.resid_scale, device)
+
+    def index_bytes(self):
+        return self.idx0.numel() * 2 + (0 if self.idx1 is None else self.idx1.numel() * self.idx1.element_size())
+
+
+def _to_dev(a, dtype, device):
+    if isinstance(a, torch.Tensor):
+        return a.to(device).contiguous()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device=device, dtype=dtype).contiguous()
+
+
+# ---- operations -----------------------------------------------------------------
+def input_rht(x, n_pad, sign_in, u_dtype=torch.float32, out=None):
+    """u = H (sign_in * [x, 0]) / sqrt(n_pad) per row of x [B, n] (glq_input_rht)."""
+    B, n = x.shape
+    x = x.contiguous()
+    u = out if out is not None else torch.empty((B, n_pad), dtype=u_dtype, device=x.device)
+    ws_n = lib().glq_input_rht_workspace_bytes(B, n_pad, _dt(u.dtype))
+    ws = _workspace(ws_n, x.device) if ws_n else None
+    _lib.check(lib().glq_input_rht(_ptr(x), _dt(x.dtype), B, n, n_pad, _ptr(sign_in), _ptr(u), _dt(u.dtype),
+                                   _ptr(ws), ws_n, _stream(x.device)), "glq_input_rht")
+    return u
+
+
+def output_rht(z_parts, m, sign_out, y_dtype=torch.float32, out=None, workspace=None):
+    """y = (sign_out * H (sum_s z_parts[s]) / sqrt(m_pad))[:, :m] (glq_output_rht)."""
+    S, B, m_pad = z_parts.shape
+    z_parts = z_parts.contiguous()
+    y = out if out is not None else torch.empty((B, m), dtype=y_dtype, device=z_parts.device)
+    y_dtype = y.dtype
+    ws_n = lib().glq_output_rht_workspace_bytes(B, m_pad)
+    ws = None
+    if ws_n:
+        ws = workspace if workspace is not None else _workspace(ws_n, z_parts.device)
+        ws_n = ws.numel()
+    _lib.check(lib().glq_output_rht(_ptr(z_parts), S, B, m, m_pad, _ptr(sign_out), _ptr(y), _dt(y_dtype), _ptr(ws),
+                                    ws_n, _stream(y.device)), "glq_output_rht")
+    return y
+
+
+def e8_dequant(layer, dtype=torch.float32):
+    """W~ [m_pad, n_pad] (glq_e8_dequant; tests and debugging only)."""
+    w = torch.empty((layer.m_pad, layer.n_pad), dtype=dtype, device=layer.device)
+    _lib.check(lib().glq_e8_dequant(ctypes.byref(layer.desc), _ptr(w), _dt(dtype), _stream(layer.device)),
+               "glq_e8_dequant")
+    return w
+
+
+def e8_matmul_splits(layer, B):
+    return int(lib().glq_e8_matmul_splits(ctypes.byref(layer.desc), B))
+
+
+def e8_matmul(layer, u, out=None):
+    """Split partial sums z_parts [S, B, m_pad] of z = u W~^T (glq_e8_matmul).
+
+    u is fp32 [B, n_pad] for B <= 16 and fp16 for larger B.
+    """
+    B = u.shape[0]
+    u = u.contiguous()
+    S = e8_matmul_splits(layer, B)
+    z = out if out is not None else torch.empty((S, B, layer.m_pad), dtype=torch.float32, device=u.device)
+    _lib.check(lib().glq_e8_matmul(ctypes.byref(layer.desc), _ptr(u), _dt(u.dtype), B, _ptr(z), _stream(u.device)),
+               "glq_e8_matmul")
+    return z
+
+
+def linear_workspace_bytes(layer, B):
+    return int(lib().glq_e8rht_linear_workspace_bytes(ctypes.byref(layer.desc), B))
+
+
+def e8rht_linear(layer, x, y_dtype=None, workspace=None, out=None):
+    """The E8RHTLinear forward y [B, m] from x [B, n] (glq_e8rht_linear)."""
+    B = x.shape[0]
+    x = x.contiguous()
+    y_dtype = y_dtype or x.dtype
+    y = out if out is not None else torch.empty((B, layer.m), dtype=y_dtype, device=x.device)
+    ws_n = linear_workspace_bytes(layer, B)
+    if workspace is None:
+        workspace = _workspace(ws_n, x.device)
+    _lib.check(lib().glq_e8rht_linear(ctypes.byref(layer.desc), _ptr(x), _dt(x.dtype), B, _ptr(y), _dt(y.dtype),
+                                      _ptr(workspace), workspace.numel(), _stream(x.device)), "glq_e8rht_linear")
+    return y

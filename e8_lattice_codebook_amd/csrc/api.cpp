@@ -1,0 +1,200 @@
+// C ABI entry points: argument validation, workspace layout and dispatch to
+// the gfx950 kernels.  Nothing here allocates, frees or synchronizes.
+#include <cstdint>
+#include <cstring>
+
+#include "internal.h"
+
+using namespace glq;
+
+namespace {
+
+bool valid_dtype(glq_dtype d) { return d == GLQ_F32 || d == GLQ_F16 || d == GLQ_BF16; }
+
+bool valid_pad(int64_t p) { return is_pow2(p) && p >= 8 && p <= GLQ_MAX_PAD; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+glq_status from_hip(hipError_t e) { return e == hipSuccess ? GLQ_OK : GLQ_ERR_HIP; }
+
+// Validation of a layer descriptor.  need_signs: the RHT steps use the signs.
+glq_status check_layer(const glq_layer* L, bool need_signs) {
+  if (!L) return GLQ_ERR_NULL;
+  if (!L->idx0 || !L->cb_pack) return GLQ_ERR_NULL;
+  if (need_signs && (!L->sign_in || !L->sign_out)) return GLQ_ERR_NULL;
+  if (!valid_pad(L->n_pad) || !valid_pad(L->m_pad)) return GLQ_ERR_SHAPE;
+  if (need_signs && (L->n < 1 || L->n > L->n_pad || L->m < 1 || L->m > L->m_pad)) return GLQ_ERR_SHAPE;
+  if (L->resid_bits != 0 && L->resid_bits != 8 && L->resid_bits != 16) return GLQ_ERR_RECIPE;
+  if (L->resid_bits != 0 && (!L->idx1 || !L->cb2_pack)) return GLQ_ERR_NULL;
+  if (!aligned(L->idx0, 16) || !aligned(L->cb_pack, 256)) return GLQ_ERR_ALIGN;
+  if (L->resid_bits != 0 && (!aligned(L->idx1, 16) || !aligned(L->cb2_pack, 256))) return GLQ_ERR_ALIGN;
+  return GLQ_OK;
+}
+
+struct LinearWs {
+  size_t u_off, rin_off, z_off, rout_off, total;
+  int splits;
+  bool prefill;
+};
+
+constexpr int64_t kDecodeMaxB = 16;
+
+LinearWs linear_ws(const glq_layer& L, int64_t B) {
+  LinearWs w{};
+  w.prefill = B > kDecodeMaxB;
+  const int ln = log2_exact(L.n_pad), lm = log2_exact(L.m_pad);
+  size_t off = 0;
+  w.u_off = off;
+  off += align256(size_t(B) * size_t(L.n_pad) * (w.prefill ? 2 : 4));
+  w.rin_off = off;
+  if (w.prefill && ln > kSingleLog2) off += align256(size_t(B) * size_t(L.n_pad) * 4);
+  w.splits = w.prefill ? 1 : gemv_splits(L.n_pad, B);
+  w.z_off = off;
+  off += align256(size_t(w.splits) * size_t(B) * size_t(L.m_pad) * 4);
+  w.rout_off = off;
+  if (lm > kSingleLog2) off += align256(size_t(B) * size_t(L.m_pad) * 4);
+  w.total = off;
+  return w;
+}
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int glq_abi_version(void) { return GLQ_ABI_VERSION; }
+
+const char* glq_status_string(glq_status s) {
+  switch (s) {
+    case GLQ_OK: return "ok";
+    case GLQ_ERR_NULL: return "a required pointer is NULL";
+    case GLQ_ERR_SHAPE: return "a size is out of range or sizes disagree";
+    case GLQ_ERR_DTYPE: return "dtype not supported by this entry point";
+    case GLQ_ERR_RECIPE: return "resid_bits must be 0, 8 or 16";
+    case GLQ_ERR_ALIGN: return "a pointer is not aligned as documented";
+    case GLQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case GLQ_ERR_HIP: return "a HIP launch failed";
+    case GLQ_ERR_CODEBOOK: return "codebook entries outside the representable range";
+  }
+  return "unknown status";
+}
+
+size_t glq_codebook_pack_bytes(int64_t entries) {
+  if (entries < 1 || entries > GLQ_CODEBOOK_ENTRIES) return 0;
+  return pack_bytes(entries);
+}
+
+glq_status glq_codebook_pack(const uint16_t* cb, int64_t entries, void* pack, size_t pack_bytes_given,
+                             int32_t* bad_count, hipStream_t stream) {
+  if (!cb || !pack) return GLQ_ERR_NULL;
+  if (entries < 1 || entries > GLQ_CODEBOOK_ENTRIES) return GLQ_ERR_SHAPE;
+  if (!aligned(pack, 256)) return GLQ_ERR_ALIGN;
+  if (pack_bytes_given < pack_bytes(entries)) return GLQ_ERR_WORKSPACE;
+  return from_hip(launch_codebook_pack(cb, entries, pack, bad_count, stream));
+}
+
+size_t glq_input_rht_workspace_bytes(int64_t B, int64_t n_pad, glq_dtype u_dt) {
+  if (B < 1 || !valid_pad(n_pad)) return 0;
+  if (log2_exact(n_pad) > kSingleLog2 && u_dt != GLQ_F32) return align256(size_t(B) * size_t(n_pad) * 4);
+  return 0;
+}
+
+glq_status glq_input_rht(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t n_pad, const int8_t* sign_in,
+                         void* u, glq_dtype u_dt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !sign_in || !u) return GLQ_ERR_NULL;
+  if (B < 1 || !valid_pad(n_pad) || n < 1 || n > n_pad || B > int64_t(1) << 31) return GLQ_ERR_SHAPE;
+  if (!valid_dtype(x_dt) || !valid_dtype(u_dt)) return GLQ_ERR_DTYPE;
+  const size_t need = glq_input_rht_workspace_bytes(B, n_pad, u_dt);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GLQ_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 256)) return GLQ_ERR_ALIGN;
+  return from_hip(launch_rht_in(x, x_dt, B, n, log2_exact(n_pad), sign_in, u, u_dt,
+                                static_cast<float*>(workspace), stream));
+}
+
+size_t glq_output_rht_workspace_bytes(int64_t B, int64_t m_pad) {
+  if (B < 1 || !valid_pad(m_pad)) return 0;
+  if (log2_exact(m_pad) > kSingleLog2) return align256(size_t(B) * size_t(m_pad) * 4);
+  return 0;
+}
+
+glq_status glq_output_rht(const float* z_parts, int64_t splits, int64_t B, int64_t m, int64_t m_pad,
+                          const int8_t* sign_out, void* y, glq_dtype y_dt, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  if (!z_parts || !sign_out || !y) return GLQ_ERR_NULL;
+  if (B < 1 || splits < 1 || !valid_pad(m_pad) || m < 1 || m > m_pad || B > int64_t(1) << 31)
+    return GLQ_ERR_SHAPE;
+  if (!valid_dtype(y_dt)) return GLQ_ERR_DTYPE;
+  const size_t need = glq_output_rht_workspace_bytes(B, m_pad);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GLQ_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 256)) return GLQ_ERR_ALIGN;
+  return from_hip(launch_rht_out(z_parts, splits, B, m, log2_exact(m_pad), sign_out, y, y_dt,
+                                 static_cast<float*>(workspace), stream));
+}
+
+glq_status glq_e8_dequant(const glq_layer* layer, void* w, glq_dtype w_dt, hipStream_t stream) {
+  glq_status st = check_layer(layer, false);
+  if (st != GLQ_OK) return st;
+  if (!w) return GLQ_ERR_NULL;
+  if (!valid_dtype(w_dt)) return GLQ_ERR_DTYPE;
+  if (!aligned(w, 16)) return GLQ_ERR_ALIGN;
+  return from_hip(launch_dequant(*layer, w, w_dt, stream));
+}
+
+int64_t glq_e8_matmul_splits(const glq_layer* layer, int64_t B) {
+  if (!layer || B < 1 || !valid_pad(layer->n_pad)) return 0;
+  return B > kDecodeMaxB ? 1 : gemv_splits(layer->n_pad, B);
+}
+
+glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, int64_t B, float* z_parts,
+                         hipStream_t stream) {
+  glq_status st = check_layer(layer, false);
+  if (st != GLQ_OK) return st;
+  if (!u || !z_parts) return GLQ_ERR_NULL;
+  if (B < 1 || B > int64_t(1) << 31) return GLQ_ERR_SHAPE;
+  if (u_dt != (B > kDecodeMaxB ? GLQ_F16 : GLQ_F32)) return GLQ_ERR_DTYPE;
+  if (!aligned(u, 16)) return GLQ_ERR_ALIGN;
+  if (B > kDecodeMaxB) return from_hip(launch_gemm(*layer, static_cast<const half_t*>(u), B, z_parts, stream));
+  return from_hip(launch_gemv(*layer, static_cast<const float*>(u), B, z_parts, stream));
+}
+
+size_t glq_e8rht_linear_workspace_bytes(const glq_layer* layer, int64_t B) {
+  if (!layer || B < 1 || !valid_pad(layer->n_pad) || !valid_pad(layer->m_pad)) return 0;
+  return linear_ws(*layer, B).total;
+}
+
+glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_dt, int64_t B, void* y,
+                            glq_dtype y_dt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  glq_status st = check_layer(layer, true);
+  if (st != GLQ_OK) return st;
+  if (!x || !y) return GLQ_ERR_NULL;
+  if (B < 1 || B > int64_t(1) << 31) return GLQ_ERR_SHAPE;
+  if (!valid_dtype(x_dt) || !valid_dtype(y_dt)) return GLQ_ERR_DTYPE;
+  const LinearWs w = linear_ws(*layer, B);
+  if (!workspace || workspace_bytes < w.total) return GLQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return GLQ_ERR_ALIGN;
+  const glq_layer& L = *layer;
+  const int ln = log2_exact(L.n_pad), lm = log2_exact(L.m_pad);
+  hipError_t e;
+  float* z = at<float>(workspace, w.z_off);
+  if (!w.prefill) {
+    float* u = at<float>(workspace, w.u_off);
+    e = launch_rht_in(x, x_dt, B, L.n, ln, L.sign_in, u, GLQ_F32, nullptr, stream);
+    if (e != hipSuccess) return GLQ_ERR_HIP;
+    e = launch_gemv(L, u, B, z, stream);
+    if (e != hipSuccess) return GLQ_ERR_HIP;
+  } else {
+    half_t* u = at<half_t>(workspace, w.u_off);
+    e = launch_rht_in(x, x_dt, B, L.n, ln, L.sign_in, u, GLQ_F16, at<float>(workspace, w.rin_off), stream);
+    if (e != hipSuccess) return GLQ_ERR_HIP;
+    e = launch_gemm(L, u, B, z, stream);
+    if (e != hipSuccess) return GLQ_ERR_HIP;
+  }
+  e = launch_rht_out(z, w.splits, B, L.m, lm, L.sign_out, y, y_dt, at<float>(workspace, w.rout_off), stream);
+  return from_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+// Codebook packing and explicit dequantization on gfx950.
+//
+// glq 0.5.1 (PyPI project page), "How it works", item 1: an 8-weight group is a
+// 16-bit index into the 65,536-entry E8 codebook, refined by an 8-bit (256-entry)
+// or 16-bit residual stage; table "Bit widths": one global scale per layer;
+// "Inference kernels": the kernels gather 8-D codewords from a compact cached
+// codebook.
+//
+// Pack: every E8 coordinate of norm^2 <= 12 is a multiple of 1/2 with |c| <= 3,
+// so 2c is an exact int8; the pack holds that int8 table [entries][8] (512 KiB
+// for the primary codebook, 2 KiB for the 256-entry residual).
+//
+// Dequant: e = c0 + s_r * c1 (exact in fp32 for the codebook values and
+// s_r = 2^-k; in general one rounding), w = RN(s * e); fp16 / bf16 outputs are
+// RN(w).  One thread per 8-weight group, one 16- or 32-byte store per group.
+#include "internal.h"
+
+namespace glq {
+namespace {
+
+__global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
+
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ cb, int64_t count,
+                                                   int8_t* __restrict__ out, int32_t* __restrict__ bad) {
+  const int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (k >= count) return;
+  const float f = (float)__builtin_bit_cast(half_t, cb[k]);
+  const float t = 2.0f * f;
+  const bool ok = (t == rintf(t)) && t >= -8.0f && t <= 7.0f;
+  out[k] = ok ? int8_t(int(t)) : int8_t(0);
+  if (!ok && bad) atomicAdd(bad, 1);
+}
+
+__device__ __forceinline__ float i8_at(uint32_t w, int j) { return float(int8_t(uint8_t(w >> (8 * j)))); }
+
+template <class WT>
+__device__ __forceinline__ void store8(WT* p, const float* v);
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float* v) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <>
+__device__ __forceinline__ void store8<half_t>(half_t* p, const float* v) {
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = __builtin_bit_cast(uint16_t, (half_t)v[2 * k]);
+    const uint32_t hi = __builtin_bit_cast(uint16_t, (half_t)v[2 * k + 1]);
+    w[k] = lo | (hi << 16);
+  }
+  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+template <>
+__device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float* v) {
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = from_f32<bf16_t>(v[2 * k]).bits;
+    const uint32_t hi = from_f32<bf16_t>(v[2 * k + 1]).bits;
+    w[k] = lo | (hi << 16);
+  }
+  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <class WT, int RESID>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint16_t* __restrict__ idx0, const void* __restrict__ idx1,
+                                                      const int8_t* __restrict__ cb0, const int8_t* __restrict__ cb1,
+                                                      float s, float sr, int64_t groups, WT* __restrict__ w) {
+  const int64_t g = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (g >= groups) return;
+  const uint2 c0 = *reinterpret_cast<const uint2*>(cb0 + size_t(idx0[g]) * 8);
+  float e[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    e[j] = 0.5f * i8_at(c0.x, j);
+    e[j + 4] = 0.5f * i8_at(c0.y, j);
+  }
+  if (RESID != 0) {
+    const uint32_t i1 = RESID == 8 ? uint32_t(static_cast<const uint8_t*>(idx1)[g])
+                                   : uint32_t(static_cast<const uint16_t*>(idx1)[g]);
+    const uint2 c1 = *reinterpret_cast<const uint2*>(cb1 + size_t(i1) * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      e[j] = fmaf(sr, 0.5f * i8_at(c1.x, j), e[j]);
+      e[j + 4] = fmaf(sr, 0.5f * i8_at(c1.y, j), e[j + 4]);
+    }
+  }
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = s * e[j];
+  store8<WT>(w + g * 8, v);
+}
+
+template <class WT>
+hipError_t dequant_typed(const glq_layer& L, void* w, hipStream_t stream) {
+  const int64_t groups = L.m_pad * (L.n_pad / 8);
+  const dim3 grid(unsigned((groups + 255) / 256)), block(256);
+  const int8_t* cb0 = static_cast<const int8_t*>(L.cb_pack) + pack_i8_offset();
+  const int8_t* cb1 = L.cb2_pack ? static_cast<const int8_t*>(L.cb2_pack) + pack_i8_offset() : nullptr;
+  WT* out = static_cast<WT*>(w);
+  switch (L.resid_bits) {
+    case 0:
+      hipLaunchKernelGGL((dequant_kernel<WT, 0>), grid, block, 0, stream, L.idx0, L.idx1, cb0, cb1, L.wscale,
+                         L.resid_scale, groups, out);
+      break;
+    case 8:
+      hipLaunchKernelGGL((dequant_kernel<WT, 8>), grid, block, 0, stream, L.idx0, L.idx1, cb0, cb1, L.wscale,
+                         L.resid_scale, groups, out);
+      break;
+    default:
+      hipLaunchKernelGGL((dequant_kernel<WT, 16>), grid, block, 0, stream, L.idx0, L.idx1, cb0, cb1, L.wscale,
+                         L.resid_scale, groups, out);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_codebook_pack(const uint16_t* cb, int64_t entries, void* pack, int32_t* bad, hipStream_t stream) {
+  if (bad) {
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, stream, bad);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t count = entries * 8;
+  hipLaunchKernelGGL(pack_kernel, dim3(unsigned((count + 255) / 256)), dim3(256), 0, stream, cb, count,
+                     static_cast<int8_t*>(pack) + pack_i8_offset(), bad);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const glq_layer& layer, void* w, glq_dtype w_dt, hipStream_t stream) {
+  switch (w_dt) {
+    case GLQ_F32: return dequant_typed<float>(layer, w, stream);
+    case GLQ_F16: return dequant_typed<half_t>(layer, w, stream);
+    case GLQ_BF16: return dequant_typed<bf16_t>(layer, w, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace glq

@@ -1,0 +1,85 @@
+// Internal declarations shared by the HIP sources of the E8RHTLinear library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "glq.h"
+
+namespace glq {
+
+// Longest transform done by one workgroup in LDS (16384 fp32 = 64 KiB).  Longer
+// transforms use the Kronecker split H_{a*b} = H_a (x) H_b in two passes.
+constexpr int kSingleLog2 = 14;
+// Split point of the two-pass transform: the row pass has length 2^kSplitLog2
+// (or n_pad / 64 when that is longer), the column pass the rest (<= 64).
+constexpr int kSplitLog2 = 12;
+
+inline int log2_exact(int64_t v) {
+  int l = 0;
+  while ((int64_t(1) << l) < v) ++l;
+  return l;
+}
+inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Two-pass split of a length-2^L transform: (row pass log2, column pass log2).
+inline void fwht_split(int L, int* l_row, int* l_col) {
+  int r = L - 6 > kSplitLog2 ? L - 6 : kSplitLog2;
+  if (r > L) r = L;
+  *l_row = r;
+  *l_col = L - r;
+}
+
+// ---- numeric storage types -------------------------------------------------
+typedef _Float16 half_t;
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <class T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<half_t>(half_t v) { return (float)v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) {
+  return __uint_as_float(uint32_t(v.bits) << 16);
+}
+
+template <class T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ half_t from_f32<half_t>(float v) { return (half_t)v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
+  // nearest, ties to even (finite values)
+  uint32_t b = __float_as_uint(v);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  bf16_t r;
+  r.bits = uint16_t(b >> 16);
+  return r;
+}
+
+// ---- codebook pack layout ----------------------------------------------------
+// offset 0: int8 [entries][8], each value 2*c (exact for c in Z/2, |c| <= 4)
+inline size_t pack_i8_offset() { return 0; }
+inline size_t pack_bytes(int64_t entries) { return align256(size_t(entries) * 8); }
+
+// ---- launchers (return the launch status) -----------------------------------
+hipError_t launch_codebook_pack(const uint16_t* cb, int64_t entries, void* pack, int32_t* bad,
+                                hipStream_t stream);
+
+// Input transform; ws: fp32 [B][N] scratch used only when N > 2^kSingleLog2 and u_dt != F32.
+hipError_t launch_rht_in(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int L, const int8_t* sign,
+                         void* u, glq_dtype u_dt, float* ws, hipStream_t stream);
+// Output transform of sum_s z[s]; ws: fp32 [B][N] scratch used only when N > 2^kSingleLog2.
+hipError_t launch_rht_out(const float* z, int64_t S, int64_t B, int64_t m, int L, const int8_t* sign,
+                          void* y, glq_dtype y_dt, float* ws, hipStream_t stream);
+
+hipError_t launch_dequant(const glq_layer& layer, void* w, glq_dtype w_dt, hipStream_t stream);
+
+// Decode matmul: partial sums z_parts [S][B][m_pad] with S = gemv_splits(...).
+int gemv_splits(int64_t n_pad, int64_t B);
+hipError_t launch_gemv(const glq_layer& layer, const float* u, int64_t B, float* z_parts,
+                       hipStream_t stream);
+
+// Prefill matmul: z [M][m_pad] fp32 from u16 [M][n_pad] fp16.
+hipError_t launch_gemm(const glq_layer& layer, const half_t* u16, int64_t M, float* z, hipStream_t stream);
+
+}  // namespace glq

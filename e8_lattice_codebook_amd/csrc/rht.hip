@@ -1,0 +1,289 @@
+// Randomized Hadamard transforms on gfx950: the input RHT (sign flip, FWHT,
+// 1/sqrt(n_pad)) and the output RHT (fixed-order sum of split partials, FWHT,
+// 1/sqrt(m_pad), sign flip, truncation to m, cast).
+//
+// glq 0.5.1 (PyPI project page), "How it works", item 2: random sign flips
+// followed by a fast Walsh-Hadamard transform.  Glq v0.3.2 release notes, "What
+// changed": separate input_rht / output_rht operations, one-workgroup transforms
+// up to 16384 and a separate path above that.
+//
+// Transform order is Sylvester's: butterflies (a, b) -> (a + b, a - b) on every
+// index bit.  One workgroup transforms one row of up to 2^14 fp32 values in LDS:
+// the first 4 bits in registers straight from global memory, then radix-16
+// passes over LDS (XOR-swizzled so strided passes spread over the banks), the
+// last pass writing to global memory.  Longer rows use H_{N1 N2} = H_{N1} (x) H_{N2}
+// with index i = a * N2 + c: a row pass of length N2 for every a, then a column
+// pass of length N1 <= 64 per c held in registers.
+#include <math.h>
+
+#include "internal.h"
+
+namespace glq {
+namespace {
+
+template <int R>
+__device__ __forceinline__ void fwht_reg(float* v) {
+#pragma unroll
+  for (int h = 1; h < R; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ int swz(int i) { return i ^ ((i >> 5) & 31); }
+
+// ---- element loaders / storers ------------------------------------------------
+template <class XT>
+struct LoadSignedX {  // x [B][n] -> sign[i] * x[b][i], zero beyond n
+  const XT* x;
+  int64_t n;
+  const int8_t* sign;
+  __device__ float operator()(int64_t b, int64_t i) const {
+    return i < n ? to_f32<XT>(x[b * n + i]) * float(sign[i]) : 0.0f;
+  }
+};
+
+struct LoadF32 {  // p [B][N]
+  const float* p;
+  int64_t N;
+  __device__ float operator()(int64_t b, int64_t i) const { return p[b * N + i]; }
+};
+
+struct LoadSplitSum {  // sum over s = 0..S-1, in order, of z[s][b][i]
+  const float* z;
+  int64_t S, B, N;
+  __device__ float operator()(int64_t b, int64_t i) const {
+    float acc = z[b * N + i];
+    for (int64_t s = 1; s < S; ++s) acc += z[(s * B + b) * N + i];
+    return acc;
+  }
+};
+
+template <class UT>
+struct StoreScaled {  // u[b][i] = RN(v * scale)
+  UT* u;
+  int64_t N;
+  float scale;
+  __device__ void operator()(int64_t b, int64_t i, float v) const { u[b * N + i] = from_f32<UT>(v * scale); }
+};
+
+struct StoreF32 {
+  float* p;
+  int64_t N;
+  __device__ void operator()(int64_t b, int64_t i, float v) const { p[b * N + i] = v; }
+};
+
+template <class YT>
+struct StoreOut {  // y[b][i] = RN(sign[i] * v * scale) for i < m
+  YT* y;
+  int64_t m;
+  const int8_t* sign;
+  float scale;
+  __device__ void operator()(int64_t b, int64_t i, float v) const {
+    if (i < m) y[b * m + i] = from_f32<YT>(v * scale * float(sign[i]));
+  }
+};
+
+// Row r of a segmented pass is (b, a) = (r >> nseg_log2, r & (N1 - 1)); element c of
+// it is element a * N2 + c of row b.
+template <class Inner>
+struct SegLoad {
+  Inner in;
+  int seg_log2, nseg_log2;
+  __device__ float operator()(int64_t r, int64_t c) const {
+    const int64_t a = r & ((int64_t(1) << nseg_log2) - 1);
+    return in(r >> nseg_log2, (a << seg_log2) + c);
+  }
+};
+template <class Inner>
+struct SegStore {
+  Inner in;
+  int seg_log2, nseg_log2;
+  __device__ void operator()(int64_t r, int64_t c, float v) const {
+    const int64_t a = r & ((int64_t(1) << nseg_log2) - 1);
+    in(r >> nseg_log2, (a << seg_log2) + c, v);
+  }
+};
+
+// ---- one row per workgroup -------------------------------------------------------
+template <int R, class Load, class Store>
+__device__ __forceinline__ void first_pass(const Load& ld, const Store& st, int64_t row, int L, float* buf,
+                                           bool last) {
+  const int chunks = (1 << L) / R;
+  for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+    float v[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = ld(row, c * R + j);
+    fwht_reg<R>(v);
+    if (last) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) st(row, c * R + j, v[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < R; ++j) buf[swz(c * R + j)] = v[j];
+    }
+  }
+}
+
+template <int LR, class Store>
+__device__ __forceinline__ void mid_pass(const Store& st, int64_t row, int L, int b0, float* buf, bool last) {
+  constexpr int R = 1 << LR;
+  const int groups = (1 << L) >> LR;
+  const int lowmask = (1 << b0) - 1;
+  for (int g = threadIdx.x; g < groups; g += blockDim.x) {
+    const int base = (g & lowmask) | ((g >> b0) << (b0 + LR));
+    float v[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = buf[swz(base + (j << b0))];
+    fwht_reg<R>(v);
+    if (last) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) st(row, base + (j << b0), v[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < R; ++j) buf[swz(base + (j << b0))] = v[j];
+    }
+  }
+}
+
+template <class Load, class Store>
+__global__ __launch_bounds__(1024) void fwht_rows_kernel(Load ld, Store st, int L) {
+  extern __shared__ float buf[];
+  const int64_t row = blockIdx.x;
+  const int r0 = L < 4 ? L : 4;
+  const bool last0 = (r0 == L);
+  switch (r0) {
+    case 1: first_pass<2>(ld, st, row, L, buf, last0); break;
+    case 2: first_pass<4>(ld, st, row, L, buf, last0); break;
+    case 3: first_pass<8>(ld, st, row, L, buf, last0); break;
+    default: first_pass<16>(ld, st, row, L, buf, last0); break;
+  }
+  for (int b0 = r0; b0 < L; b0 += 4) {
+    __syncthreads();
+    const int rb = (L - b0) < 4 ? (L - b0) : 4;
+    const bool last = (b0 + rb == L);
+    switch (rb) {
+      case 1: mid_pass<1>(st, row, L, b0, buf, last); break;
+      case 2: mid_pass<2>(st, row, L, b0, buf, last); break;
+      case 3: mid_pass<3>(st, row, L, b0, buf, last); break;
+      default: mid_pass<4>(st, row, L, b0, buf, last); break;
+    }
+  }
+}
+
+// ---- column pass of the two-pass transform ------------------------------------
+template <int N1, class Load, class Store>
+__global__ __launch_bounds__(256) void fwht_cols_kernel(Load ld, Store st, int64_t B, int seg_log2) {
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= (B << seg_log2)) return;
+  const int64_t b = t >> seg_log2;
+  const int64_t c = t & ((int64_t(1) << seg_log2) - 1);
+  float v[N1];
+#pragma unroll
+  for (int a = 0; a < N1; ++a) v[a] = ld(b, (int64_t(a) << seg_log2) + c);
+  fwht_reg<N1>(v);
+#pragma unroll
+  for (int a = 0; a < N1; ++a) st(b, (int64_t(a) << seg_log2) + c, v[a]);
+}
+
+template <class Load, class Store>
+hipError_t run_rows(const Load& ld, const Store& st, int64_t rows, int L, hipStream_t stream) {
+  int threads = (1 << L) / 16;
+  if (threads < 64) threads = 64;
+  if (threads > 1024) threads = 1024;
+  const size_t shmem = L > 4 ? (size_t(4) << L) : 0;
+  hipLaunchKernelGGL((fwht_rows_kernel<Load, Store>), dim3(unsigned(rows)), dim3(threads), shmem, stream, ld, st,
+                     L);
+  return hipGetLastError();
+}
+
+template <class Load, class Store>
+hipError_t run_cols(const Load& ld, const Store& st, int64_t B, int seg_log2, int l_col, hipStream_t stream) {
+  const int64_t total = B << seg_log2;
+  const dim3 grid(unsigned((total + 255) / 256)), block(256);
+  switch (l_col) {
+    case 1: hipLaunchKernelGGL((fwht_cols_kernel<2, Load, Store>), grid, block, 0, stream, ld, st, B, seg_log2); break;
+    case 2: hipLaunchKernelGGL((fwht_cols_kernel<4, Load, Store>), grid, block, 0, stream, ld, st, B, seg_log2); break;
+    case 3: hipLaunchKernelGGL((fwht_cols_kernel<8, Load, Store>), grid, block, 0, stream, ld, st, B, seg_log2); break;
+    case 4: hipLaunchKernelGGL((fwht_cols_kernel<16, Load, Store>), grid, block, 0, stream, ld, st, B, seg_log2); break;
+    case 5: hipLaunchKernelGGL((fwht_cols_kernel<32, Load, Store>), grid, block, 0, stream, ld, st, B, seg_log2); break;
+    case 6: hipLaunchKernelGGL((fwht_cols_kernel<64, Load, Store>), grid, block, 0, stream, ld, st, B, seg_log2); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class XT, class UT>
+hipError_t rht_in_typed(const void* x, int64_t B, int64_t n, int L, const int8_t* sign, void* u, float* ws,
+                        hipStream_t stream) {
+  const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
+  const LoadSignedX<XT> ld{static_cast<const XT*>(x), n, sign};
+  const int64_t N = int64_t(1) << L;
+  if (L <= kSingleLog2) {
+    return run_rows(ld, StoreScaled<UT>{static_cast<UT*>(u), N, scale}, B, L, stream);
+  }
+  int lr, lc;
+  fwht_split(L, &lr, &lc);
+  float* mid = (sizeof(UT) == 4) ? reinterpret_cast<float*>(u) : ws;
+  hipError_t e = run_rows(SegLoad<LoadSignedX<XT>>{ld, lr, lc}, SegStore<StoreF32>{StoreF32{mid, N}, lr, lc},
+                          B << lc, lr, stream);
+  if (e != hipSuccess) return e;
+  return run_cols(LoadF32{mid, N}, StoreScaled<UT>{static_cast<UT*>(u), N, scale}, B, lr, lc, stream);
+}
+
+template <class XT>
+hipError_t rht_in_x(const void* x, int64_t B, int64_t n, int L, const int8_t* sign, void* u, glq_dtype u_dt,
+                    float* ws, hipStream_t stream) {
+  switch (u_dt) {
+    case GLQ_F32: return rht_in_typed<XT, float>(x, B, n, L, sign, u, ws, stream);
+    case GLQ_F16: return rht_in_typed<XT, half_t>(x, B, n, L, sign, u, ws, stream);
+    case GLQ_BF16: return rht_in_typed<XT, bf16_t>(x, B, n, L, sign, u, ws, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class YT>
+hipError_t rht_out_typed(const float* z, int64_t S, int64_t B, int64_t m, int L, const int8_t* sign, void* y,
+                         float* ws, hipStream_t stream) {
+  const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
+  const int64_t N = int64_t(1) << L;
+  const LoadSplitSum ld{z, S, B, N};
+  const StoreOut<YT> st{static_cast<YT*>(y), m, sign, scale};
+  if (L <= kSingleLog2) return run_rows(ld, st, B, L, stream);
+  int lr, lc;
+  fwht_split(L, &lr, &lc);
+  hipError_t e = run_rows(SegLoad<LoadSplitSum>{ld, lr, lc}, SegStore<StoreF32>{StoreF32{ws, N}, lr, lc}, B << lc,
+                          lr, stream);
+  if (e != hipSuccess) return e;
+  return run_cols(LoadF32{ws, N}, st, B, lr, lc, stream);
+}
+
+}  // namespace
+
+hipError_t launch_rht_in(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int L, const int8_t* sign, void* u,
+                         glq_dtype u_dt, float* ws, hipStream_t stream) {
+  switch (x_dt) {
+    case GLQ_F32: return rht_in_x<float>(x, B, n, L, sign, u, u_dt, ws, stream);
+    case GLQ_F16: return rht_in_x<half_t>(x, B, n, L, sign, u, u_dt, ws, stream);
+    case GLQ_BF16: return rht_in_x<bf16_t>(x, B, n, L, sign, u, u_dt, ws, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_rht_out(const float* z, int64_t S, int64_t B, int64_t m, int L, const int8_t* sign, void* y,
+                          glq_dtype y_dt, float* ws, hipStream_t stream) {
+  switch (y_dt) {
+    case GLQ_F32: return rht_out_typed<float>(z, S, B, m, L, sign, y, ws, stream);
+    case GLQ_F16: return rht_out_typed<half_t>(z, S, B, m, L, sign, y, ws, stream);
+    case GLQ_BF16: return rht_out_typed<bf16_t>(z, S, B, m, L, sign, y, ws, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace glq

@@ -1,0 +1,230 @@
+/*
+ * glq.h — C ABI of the MI355X (gfx950) E8RHTLinear library.
+ *
+ * The operation (glq 0.5.1, PyPI project page):
+ *   "How it works", item 1: each 8-weight group of a weight matrix is one 16-bit
+ *     index into a 65,536-entry E8 lattice codebook; 3-8 bpw add 8-bit
+ *     (256-entry) or 16-bit residual stages.
+ *   "How it works", item 2: a randomized Hadamard transform (random sign flips,
+ *     then a fast Walsh-Hadamard transform) rotates the weights, so the layer
+ *     applies one to its input and one to its output.
+ *   "How it works", item 4 and "Inference kernels": the matmul is taken directly
+ *     against the indices, Y = X dequant(W)^T, without forming W in memory.
+ *   table "Bit widths": 2 bpw = 16b; 3 bpw = 16b + 8b; 4 bpw = 16b + 16b; one
+ *     global scale per layer.
+ *   Glq v0.3.2 release notes, "What changed": the input and output transforms
+ *     are separate operations (input_rht, output_rht).
+ *
+ * The layer forward computed here, for x [B][n] and y [B][m]:
+ *   u  = H_{n_pad} (sign_in * [x, 0 ... 0]) / sqrt(n_pad)               (input RHT)
+ *   W~[o][8g + j] = s * (C0[idx0[o][g]][j] + s_r * C1[idx1[o][g]][j])    (dequant, never stored)
+ *   z  = u W~^T                                                          ([B][m_pad])
+ *   y  = (sign_out * H_{m_pad} z / sqrt(m_pad))[:, 0:m]                  (output RHT)
+ * with H the Sylvester-ordered Hadamard matrix, H[i][j] = (-1)^popcount(i & j).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are HIP device pointers on the current device;
+ *     "host" pointers are ordinary host memory.  The caller owns every buffer;
+ *     the library allocates and frees nothing and keeps no mutable state.
+ *   - Device work is enqueued asynchronously on `stream` (0 = null stream); the
+ *     library never synchronizes, so calls are safe under stream capture.
+ *   - Arrays are dense and row-major.  n_pad and m_pad are powers of two in
+ *     [8, 2^20]; n <= n_pad, m <= m_pad; batch sizes are >= 1.
+ *   - Every argument is validated before anything is launched; on an error the
+ *     call returns that status and leaves every output untouched.  A failed
+ *     launch returns GLQ_ERR_HIP.  Faults inside kernels surface on the stream.
+ *   - Results are deterministic: the same inputs give bit-identical outputs on
+ *     every call (fixed-order reductions, no atomics on the data path).
+ */
+#ifndef GLQ_H
+#define GLQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GLQ_ABI_VERSION 1
+#define GLQ_CODEBOOK_ENTRIES 65536
+#define GLQ_RESID8_ENTRIES 256
+#define GLQ_MAX_PAD (1 << 20)
+
+typedef enum glq_status {
+  GLQ_OK = 0,
+  GLQ_ERR_NULL = 1,      /* a required pointer is NULL */
+  GLQ_ERR_SHAPE = 2,     /* a size is out of range or sizes disagree */
+  GLQ_ERR_DTYPE = 3,     /* dtype code not supported by this entry point */
+  GLQ_ERR_RECIPE = 4,    /* resid_bits not in {0, 8, 16} */
+  GLQ_ERR_ALIGN = 5,     /* a pointer is not aligned as documented */
+  GLQ_ERR_WORKSPACE = 6, /* workspace missing or smaller than the size query says */
+  GLQ_ERR_HIP = 7,       /* a HIP launch failed */
+  GLQ_ERR_CODEBOOK = 8   /* codebook entries outside what the pack can hold */
+} glq_status;
+
+typedef enum glq_dtype {
+  GLQ_F32 = 0,  /* IEEE binary32 */
+  GLQ_F16 = 1,  /* IEEE binary16 */
+  GLQ_BF16 = 2  /* bfloat16 */
+} glq_dtype;
+
+/*
+ * One quantized layer.  All pointers are device pointers.
+ *   n, n_pad        input features and their padded size (power of two)
+ *   m, m_pad        output features and their padded size (power of two)
+ *   resid_bits      0: 2 bpw, primary stage only ("Bit widths", row 2)
+ *                   8: 3 bpw, + 8-bit index into a 256-entry residual codebook
+ *                   16: 4 bpw, + 16-bit index into a 65,536-entry residual codebook
+ *   wscale          s, the one scale of the layer ("Bit widths", note below the table)
+ *   resid_scale     s_r, the residual stage's scale (the inv_resid_scale argument
+ *                   of glq_dequant_matmul, "Inference kernels"); unused when
+ *                   resid_bits == 0
+ *   sign_in         int8 [n_pad], each +1 or -1 (values other than +-1 are a
+ *                   precondition violation and are not checked)
+ *   sign_out        int8 [m_pad], each +1 or -1
+ *   idx0            uint16 [m_pad][n_pad/8]: group g of output row o covers input
+ *                   columns 8g .. 8g+7; 16-byte aligned
+ *   idx1            uint8 (resid_bits 8) or uint16 (resid_bits 16), same shape
+ *                   as idx0, 16-byte aligned; NULL when resid_bits == 0
+ *   cb_pack         primary codebook pack (glq_codebook_pack of 65,536 entries)
+ *   cb2_pack        residual codebook pack: 256 entries for resid_bits 8, 65,536
+ *                   for resid_bits 16 (it may be the same buffer as cb_pack);
+ *                   NULL when resid_bits == 0
+ */
+typedef struct glq_layer {
+  int64_t n;
+  int64_t n_pad;
+  int64_t m;
+  int64_t m_pad;
+  int32_t resid_bits;
+  float wscale;
+  float resid_scale;
+  const int8_t* sign_in;
+  const int8_t* sign_out;
+  const uint16_t* idx0;
+  const void* idx1;
+  const void* cb_pack;
+  const void* cb2_pack;
+} glq_layer;
+
+/* GLQ_ABI_VERSION of the built library. */
+int glq_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* glq_status_string(glq_status s);
+
+/*
+ * glq_e8_codebook — build the E8 codebook on the host ("How it works", item 1).
+ * Writes the first `entries` points (entries in [1, 65536]) of E8 =
+ * D8 u (D8 + 1/2) ordered by squared norm, then lexicographically ascending on
+ * the coordinates (coordinate 0 most significant), origin first, as fp16 bit
+ * patterns: cb_host is host memory of entries * 8 uint16.  The 256-entry residual
+ * codebook is the first 256 entries of the same table.  Synchronous, host only.
+ * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE.
+ */
+glq_status glq_e8_codebook(uint16_t* cb_host, int64_t entries);
+
+/*
+ * glq_codebook_pack — derive the kernels' codebook representation from an fp16
+ * codebook ("Inference kernels": the kernels gather from a compact codebook).
+ *   cb          device, fp16 bits [entries][8]; every coordinate must be a
+ *               multiple of 1/2 in [-4, 3.5] (true for all E8 points of norm^2 <= 12)
+ *   entries     number of rows, 1 .. 65536
+ *   pack        device, pack_bytes >= glq_codebook_pack_bytes(entries), 256-byte aligned
+ *   bad_count   device int32, optional (NULL to skip): set to the number of
+ *               coordinates that violate the requirement above (0 = valid pack)
+ * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_ALIGN, GLQ_ERR_WORKSPACE, GLQ_ERR_HIP.
+ */
+size_t glq_codebook_pack_bytes(int64_t entries);
+glq_status glq_codebook_pack(const uint16_t* cb, int64_t entries, void* pack, size_t pack_bytes,
+                             int32_t* bad_count, hipStream_t stream);
+
+/*
+ * glq_input_rht — u = H_{n_pad} (sign_in * [x, 0...]) / sqrt(n_pad) for each of B
+ * rows ("How it works", item 2; Glq v0.3.2 "What changed": input_rht).
+ *   x          device [B][n] in x_dt (F32, F16 or BF16)
+ *   sign_in    device int8 [n_pad]
+ *   u          device [B][n_pad] in u_dt (F32, F16 or BF16); rounded to nearest-even
+ *   workspace  device, workspace_bytes >= glq_input_rht_workspace_bytes(B, n_pad, u_dt)
+ *              (0 bytes for most shapes; NULL allowed then), 256-byte aligned
+ * Accumulation is fp32.  n_pad above 16384 runs as two passes (H = H_a (x) H_b).
+ * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_DTYPE, GLQ_ERR_WORKSPACE, GLQ_ERR_HIP.
+ */
+size_t glq_input_rht_workspace_bytes(int64_t B, int64_t n_pad, glq_dtype u_dt);
+glq_status glq_input_rht(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t n_pad,
+                         const int8_t* sign_in, void* u, glq_dtype u_dt, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * glq_output_rht — y = (sign_out * H_{m_pad} z / sqrt(m_pad))[:, 0:m] with
+ * z = sum over s = 0 .. splits-1, in that order, of z_parts[s] (Glq v0.3.2,
+ * "What changed": output_rht; "Inference kernels": fixed-order reduction of
+ * split partial sums instead of atomics).
+ *   z_parts    device fp32 [splits][B][m_pad]
+ *   y          device [B][m] in y_dt (F32, F16 or BF16)
+ *   workspace  device, >= glq_output_rht_workspace_bytes(B, m_pad), 256-byte aligned
+ * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_DTYPE, GLQ_ERR_WORKSPACE, GLQ_ERR_HIP.
+ */
+size_t glq_output_rht_workspace_bytes(int64_t B, int64_t m_pad);
+glq_status glq_output_rht(const float* z_parts, int64_t splits, int64_t B, int64_t m, int64_t m_pad,
+                          const int8_t* sign_out, void* y, glq_dtype y_dt, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * glq_e8_dequant — write the dequantized weight W~ [m_pad][n_pad] ("How it works",
+ * items 1 and 4; "Bit widths").  For tests and debugging: the linear never
+ * forms W~.  In fp32, e = c0 + s_r * c1 is computed exactly and
+ * w = RN(s * e) is the one rounding; F16 / BF16 output is the nearest-even
+ * rounding of that fp32 value.
+ *   layer      idx0, idx1, cb_pack, cb2_pack, resid_bits, wscale, resid_scale,
+ *              n_pad and m_pad are used (signs, n and m are ignored)
+ *   w          device [m_pad][n_pad] in w_dt, 16-byte aligned
+ * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_DTYPE, GLQ_ERR_RECIPE, GLQ_ERR_ALIGN, GLQ_ERR_HIP.
+ */
+glq_status glq_e8_dequant(const glq_layer* layer, void* w, glq_dtype w_dt, hipStream_t stream);
+
+/*
+ * glq_e8_matmul — z = u W~^T without the transforms, the counterpart of
+ * glq_dequant_matmul ("Inference kernels": Y = X dequant(W)^T, N/8 codebook
+ * blocks per output row, gathered and accumulated without forming W; split-K
+ * partial sums in a scratch buffer, reduced in a fixed order instead of with
+ * atomics).  This is the middle step of glq_e8rht_linear, exposed on its own.
+ *   u          device [B][n_pad]: fp32 when B <= 16 (decode kernel, fp32 FMA),
+ *              fp16 when B > 16 (prefill kernel, fp16 MFMA, fp32 accumulate)
+ *   z_parts    device fp32 [S][B][m_pad], S = glq_e8_matmul_splits(layer, B):
+ *              z = sum over s = 0 .. S-1 of z_parts[s]; glq_output_rht takes
+ *              z_parts and S as they are
+ * Only idx0, idx1, packs, resid_bits, wscale, resid_scale, n_pad, m_pad are used.
+ * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_DTYPE (u_dt not the one above),
+ * GLQ_ERR_RECIPE, GLQ_ERR_ALIGN, GLQ_ERR_HIP.
+ */
+int64_t glq_e8_matmul_splits(const glq_layer* layer, int64_t B);
+glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, int64_t B, float* z_parts,
+                         hipStream_t stream);
+
+/*
+ * glq_e8rht_linear — the E8RHTLinear forward, y = RHT_out(RHT_in(x) W~^T)
+ * (glq 0.5.1, "How it works" and "Inference kernels"; E8RHTLinear is the page's
+ * drop-in replacement for a linear layer, "Architecture").
+ *   x          device [B][n] in x_dt (F32, F16 or BF16)
+ *   y          device [B][m] in y_dt (F32, F16 or BF16)
+ *   workspace  device, >= glq_e8rht_linear_workspace_bytes(layer, B), 256-byte aligned
+ * B <= 16: decode path (fp32 activations after the transform, fp32 FMA against
+ * codewords gathered per group, split-K partial sums reduced in fixed order).
+ * B > 16: prefill path (transformed activations rounded to fp16, codeword tiles
+ * dequantized into LDS feeding fp16 MFMA with fp32 accumulation).
+ * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_DTYPE, GLQ_ERR_RECIPE, GLQ_ERR_ALIGN,
+ * GLQ_ERR_WORKSPACE, GLQ_ERR_HIP.
+ */
+size_t glq_e8rht_linear_workspace_bytes(const glq_layer* layer, int64_t B);
+glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_dt, int64_t B, void* y,
+                            glq_dtype y_dt, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLQ_H */

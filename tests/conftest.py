@@ -17,3 +17,12 @@ def pytest_configure(config):
 def oracle_codebook():
     from oracle import e8
     return e8.codebook()
+
+
+@pytest.fixture(scope="session")
+def gpu_codebooks():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import e8_lattice_codebook_amd as glq
+    return glq.Codebooks("cuda:0")

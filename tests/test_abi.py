@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI: the library loads, exports what include/glq.h
+declares, builds the same codebook as the oracle, and rejects bad arguments
+before launching anything.  No GPU is touched here.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "glq.h")
+
+glq = pytest.importorskip("e8_lattice_codebook_amd")
+from e8_lattice_codebook_amd import _lib  # noqa: E402
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="library not built")
+
+NO_GPU = not torch.cuda.is_available()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(glq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported():
+    lib = _lib.load()
+    names = declared_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_abi_version_and_status_strings():
+    lib = _lib.load()
+    assert lib.glq_abi_version() == 1
+    for s in range(9):
+        assert lib.glq_status_string(s)
+    assert lib.glq_status_string(0) == b"ok"
+
+
+def test_library_codebook_equals_oracle_bit_for_bit():
+    from oracle import e8
+    got = glq.e8_codebook(65536)
+    assert np.array_equal(got, e8.codebook_fp16_bits(65536))
+    assert np.array_equal(glq.e8_codebook(256), e8.codebook_fp16_bits(256))
+
+
+def test_codebook_builder_rejects_bad_sizes():
+    lib = _lib.load()
+    buf = np.zeros(16, dtype=np.uint16)
+    assert lib.glq_e8_codebook(None, 1) == 1
+    assert lib.glq_e8_codebook(buf.ctypes.data_as(ctypes.c_void_p), 0) == 2
+    assert lib.glq_e8_codebook(buf.ctypes.data_as(ctypes.c_void_p), 65537) == 2
+
+
+def test_workspace_queries():
+    lib = _lib.load()
+    assert lib.glq_codebook_pack_bytes(65536) == 65536 * 8
+    assert lib.glq_codebook_pack_bytes(0) == 0
+    assert lib.glq_input_rht_workspace_bytes(2, 16384, 1) == 0
+    assert lib.glq_input_rht_workspace_bytes(2, 32768, 1) == 2 * 32768 * 4
+    assert lib.glq_input_rht_workspace_bytes(2, 32768, 0) == 0
+    assert lib.glq_output_rht_workspace_bytes(3, 16384) == 0
+    assert lib.glq_output_rht_workspace_bytes(3, 32768) == 3 * 32768 * 4
+    L = fake_layer(n=5120, n_pad=8192, m=32768, m_pad=32768, resid_bits=16)
+    dec = lib.glq_e8rht_linear_workspace_bytes(ctypes.byref(L), 1)
+    # u fp32 + split partials + output-transform scratch
+    assert dec >= 8192 * 4 + 32768 * 4 + 32768 * 4
+    pre = lib.glq_e8rht_linear_workspace_bytes(ctypes.byref(L), 2048)
+    assert pre >= 2048 * 8192 * 2 + 2 * 2048 * 32768 * 4
+
+
+# ---- validation: fake, never-dereferenced device addresses --------------------
+A = 1 << 20  # 256-byte aligned fake address
+
+
+def fake_layer(n=256, n_pad=256, m=256, m_pad=256, resid_bits=0, **kw):
+    L = _lib.GlqLayer(n, n_pad, m, m_pad, resid_bits, 0.02, 0.25, A, A, A, A if resid_bits else 0, A,
+                      A if resid_bits else 0)
+    for k, v in kw.items():
+        setattr(L, k, v)
+    return L
+
+
+def linear_status(L, B=1, x=A, y=A, xdt=0, ydt=0, ws=A, ws_n=1 << 40):
+    return _lib.load().glq_e8rht_linear(ctypes.byref(L), x, xdt, B, y, ydt, ws, ws_n, None)
+
+
+@pytest.mark.skipif(not NO_GPU, reason="fake-pointer validation runs only where no GPU exists")
+class TestValidation:
+    def test_null_pointers(self):
+        assert linear_status(fake_layer(idx0=None)) == 1
+        assert linear_status(fake_layer(cb_pack=None)) == 1
+        assert linear_status(fake_layer(sign_in=None)) == 1
+        assert linear_status(fake_layer(), x=None) == 1
+        assert linear_status(fake_layer(), y=None) == 1
+        assert linear_status(fake_layer(resid_bits=8, idx1=None)) == 1
+        assert linear_status(fake_layer(resid_bits=8, cb2_pack=None)) == 1
+
+    def test_shapes(self):
+        assert linear_status(fake_layer(n_pad=384)) == 2          # not a power of two
+        assert linear_status(fake_layer(n_pad=4, n=4)) == 2       # below 8
+        assert linear_status(fake_layer(m_pad=1 << 21)) == 2      # above 2^20
+        assert linear_status(fake_layer(n=257)) == 2              # n > n_pad
+        assert linear_status(fake_layer(m=0)) == 2
+        assert linear_status(fake_layer(), B=0) == 2
+
+    def test_recipe_dtype_align_workspace(self):
+        assert linear_status(fake_layer(resid_bits=4)) == 4
+        assert linear_status(fake_layer(), xdt=7) == 3
+        assert linear_status(fake_layer(), ydt=-1) == 3
+        assert linear_status(fake_layer(idx0=A + 2)) == 5
+        assert linear_status(fake_layer(cb_pack=A + 16)) == 5
+        assert linear_status(fake_layer(), ws=None) == 6
+        assert linear_status(fake_layer(), ws_n=16) == 6
+        assert linear_status(fake_layer(), ws=A + 8) == 5
+
+    def test_other_entry_points(self):
+        lib = _lib.load()
+        assert lib.glq_input_rht(A, 0, 1, 300, 256, A, A, 0, None, 0, None) == 2
+        assert lib.glq_input_rht(A, 0, 1, 256, 256, None, A, 0, None, 0, None) == 1
+        assert lib.glq_input_rht(A, 0, 1, 256, 256, A, A, 5, None, 0, None) == 3
+        assert lib.glq_input_rht(A, 0, 1, 256, 32768, A, A, 1, None, 0, None) == 6
+        assert lib.glq_output_rht(A, 0, 1, 256, 256, A, A, 0, None, 0, None) == 2
+        assert lib.glq_output_rht(A, 1, 1, 256, 32768, A, A, 0, None, 0, None) == 6
+        assert lib.glq_e8_dequant(ctypes.byref(fake_layer()), A + 4, 0, None) == 5
+        assert lib.glq_e8_dequant(ctypes.byref(fake_layer(resid_bits=3)), A, 0, None) == 4
+        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 17, A, None) == 3
+        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 1, 16, A, None) == 3
+        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 0, A, None) == 2
+        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A + 4, 0, 1, A, None) == 5
+        assert lib.glq_e8_matmul_splits(ctypes.byref(fake_layer(n_pad=32768)), 1) == 8
+        assert lib.glq_e8_matmul_splits(ctypes.byref(fake_layer(n_pad=32768)), 17) == 1
+        assert lib.glq_codebook_pack(A, 65536, A, 16, None, None) == 6
+        assert lib.glq_codebook_pack(A, 65536, A + 8, 1 << 20, None, None) == 5
+        assert lib.glq_codebook_pack(A, 0, A, 1 << 20, None, None) == 2

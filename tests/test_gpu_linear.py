@@ -1,0 +1,75 @@
+"""GPU parity of the E8RHTLinear forward and of the decode matmul against the
+fp64 oracle (dequantize-then-matmul between the two transforms).
+
+glq 0.5.1, "How it works" and "Inference kernels" (Y = X dequant(W)^T without
+forming W; split-K with a fixed-order reduction).  Tolerances: relative
+Frobenius error of fp32 y over all [B, m] <= 1e-3 for the decode path (fp32
+accumulation) and <= 5e-3 for the prefill path (fp16 MFMA operands, fp32
+accumulation); fp16 / bf16 outputs equal the nearest-even rounding of the
+library's own fp32 output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import glq as og, hadamard
+from gpu_util import TORCH_DT, fp32_to_bf16_rn, fp32_to_f16_rn, layer_from, rel_frob, say, to_f64, x_tensor
+
+pytestmark = pytest.mark.gpu
+glq = pytest.importorskip("e8_lattice_codebook_amd")
+
+DECODE_TOL = 1e-3
+PREFILL_TOL = 5e-3
+
+CASES = []
+for key, w in synth.WORKLOADS.items():
+    for k in range(len(w.layers)):
+        CASES.append((key, k))
+
+
+@pytest.mark.parametrize("key,k", CASES)
+def test_linear_workloads(gpu_codebooks, key, k):
+    w = synth.WORKLOADS[key]
+    layer = layer_from(key, k)
+    ql = glq.QuantizedLayer.from_synth(layer, gpu_codebooks)
+    xs = {B: synth.make_x(layer.n, B, w.act_dtype, w.seed, k) for B in w.batches}
+    # one oracle pass for all batch sizes of the layer
+    u = np.concatenate([hadamard.rht_in(xs[B][0], layer.sign_in, layer.n_pad) for B in w.batches])
+    z = og.matmul_z(u, layer.idx0, layer.idx1, layer.resid_bits, layer.wscale, layer.resid_scale)
+    y_all = hadamard.rht_out(z, layer.sign_out, layer.m)
+    off = 0
+    for B in w.batches:
+        want = y_all[off:off + B]
+        off += B
+        say("linear", key, k, "B", B)
+        x = x_tensor(xs[B][1], w.act_dtype, "cuda:0")
+        y32 = glq.e8rht_linear(ql, x, torch.float32)
+        torch.cuda.synchronize()
+        got = to_f64(y32)
+        err = rel_frob(got, want)
+        tol = DECODE_TOL if B <= 16 else PREFILL_TOL
+        say("  rel_frob", err)
+        assert err <= tol, (key, k, B, err)
+        # output dtype: one nearest-even rounding of the fp32 result
+        for dt, rn in (("f16", fp32_to_f16_rn), ("bf16", fp32_to_bf16_rn)):
+            yd = glq.e8rht_linear(ql, x, TORCH_DT[dt])
+            torch.cuda.synchronize()
+            assert np.array_equal(to_f64(yd), rn(got.astype(np.float32))), (key, k, B, dt)
+
+
+@pytest.mark.parametrize("key,k,B", [("smollm3_block", 6, 1), ("devstral_mlp", 2, 4), ("smollm2_up", 0, 5),
+                                     ("tiny", 0, 1), ("devstral_mlp", 0, 16)])
+def test_decode_matmul(gpu_codebooks, key, k, B):
+    layer = layer_from(key, k)
+    ql = glq.QuantizedLayer.from_synth(layer, gpu_codebooks)
+    rng = np.random.default_rng(B + k)
+    u = rng.standard_normal((B, layer.n_pad)).astype(np.float32)
+    say("matmul", key, k, B)
+    parts = glq.e8_matmul(ql, torch.from_numpy(u).to("cuda:0"))
+    torch.cuda.synchronize()
+    assert parts.shape == (glq.e8_matmul_splits(ql, B), B, layer.m_pad)
+    want = og.matmul_z(u.astype(np.float64), layer.idx0, layer.idx1, layer.resid_bits, layer.wscale,
+                       layer.resid_scale)
+    err = rel_frob(to_f64(parts).sum(0), want)
+    assert err <= 1e-5, err
