@@ -51,19 +51,17 @@ def e8_codebook(entries=CODEBOOK_ENTRIES):
 
 
 def codebook_pack(cb_fp16_bits, device="cuda"):
-    """Pack an fp16 codebook [entries, 8] (uint16 bits, host or device) for the kernels."""
-    cb = torch.as_tensor(np.ascontiguousarray(cb_fp16_bits).view(np.int16)) \
-        if isinstance(cb_fp16_bits, np.ndarray) else cb_fp16_bits
-    cb = cb.to(device).contiguous()
+    """Pack an fp16 codebook [entries, 8] (host uint16 bits) for the kernels (glq_codebook_pack).
+
+    Built on the host by the library, then copied to `device`.
+    """
+    cb = np.ascontiguousarray(cb_fp16_bits, dtype=np.uint16)
     entries = cb.shape[0]
     nbytes = lib().glq_codebook_pack_bytes(entries)
-    pack = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    bad = torch.empty(1, dtype=torch.int32, device=device)
-    _lib.check(lib().glq_codebook_pack(_ptr(cb), entries, _ptr(pack), nbytes, _ptr(bad), _stream(pack.device)),
-               "glq_codebook_pack")
-    if int(bad.item()) != 0:
-        raise GLQError(8, "glq_codebook_pack")
-    return pack
+    host = np.zeros(nbytes, dtype=np.uint8)
+    _lib.check(lib().glq_codebook_pack(cb.ctypes.data_as(ctypes.c_void_p), entries,
+                                       host.ctypes.data_as(ctypes.c_void_p), nbytes), "glq_codebook_pack")
+    return torch.from_numpy(host).to(device)
 
 
 class Codebooks:
@@ -160,7 +158,7 @@ def e8_matmul_splits(layer, B):
     return int(lib().glq_e8_matmul_splits(ctypes.byref(layer.desc), B))
 
 
-def e8_matmul(layer, u, out=None):
+def e8_matmul(layer, u, out=None, workspace=None):
     """Split partial sums z_parts [S, B, m_pad] of z = u W~^T (glq_e8_matmul).
 
     u is fp32 [B, n_pad] for B <= 16 and fp16 for larger B.
@@ -169,8 +167,13 @@ def e8_matmul(layer, u, out=None):
     u = u.contiguous()
     S = e8_matmul_splits(layer, B)
     z = out if out is not None else torch.empty((S, B, layer.m_pad), dtype=torch.float32, device=u.device)
-    _lib.check(lib().glq_e8_matmul(ctypes.byref(layer.desc), _ptr(u), _dt(u.dtype), B, _ptr(z), _stream(u.device)),
-               "glq_e8_matmul")
+    ws_n = int(lib().glq_e8_matmul_workspace_bytes(ctypes.byref(layer.desc), B))
+    ws = None
+    if ws_n:
+        ws = workspace if workspace is not None else _workspace(ws_n, u.device)
+        ws_n = ws.numel()
+    _lib.check(lib().glq_e8_matmul(ctypes.byref(layer.desc), _ptr(u), _dt(u.dtype), B, _ptr(z), _ptr(ws), ws_n,
+                                   _stream(u.device)), "glq_e8_matmul")
     return z
 
 

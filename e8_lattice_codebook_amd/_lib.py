@@ -36,7 +36,7 @@ SIGNATURES = {
     "glq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "glq_e8_codebook": (ctypes.c_int, [c_vp, c_i64]),
     "glq_codebook_pack_bytes": (c_sz, [c_i64]),
-    "glq_codebook_pack": (ctypes.c_int, [c_vp, c_i64, c_vp, c_sz, c_vp, c_vp]),
+    "glq_codebook_pack": (ctypes.c_int, [c_vp, c_i64, c_vp, c_sz]),
     "glq_input_rht_workspace_bytes": (c_sz, [c_i64, c_i64, ctypes.c_int]),
     "glq_input_rht": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp, c_vp, ctypes.c_int, c_vp, c_sz,
                                      c_vp]),
@@ -44,7 +44,8 @@ SIGNATURES = {
     "glq_output_rht": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, ctypes.c_int, c_vp, c_sz, c_vp]),
     "glq_e8_dequant": (ctypes.c_int, [_LP, c_vp, ctypes.c_int, c_vp]),
     "glq_e8_matmul_splits": (c_i64, [_LP, c_i64]),
-    "glq_e8_matmul": (ctypes.c_int, [_LP, c_vp, ctypes.c_int, c_i64, c_vp, c_vp]),
+    "glq_e8_matmul_workspace_bytes": (c_sz, [_LP, c_i64]),
+    "glq_e8_matmul": (ctypes.c_int, [_LP, c_vp, ctypes.c_int, c_i64, c_vp, c_vp, c_sz, c_vp]),
     "glq_e8rht_linear_workspace_bytes": (c_sz, [_LP, c_i64]),
     "glq_e8rht_linear": (ctypes.c_int, [_LP, c_vp, ctypes.c_int, c_i64, c_vp, ctypes.c_int, c_vp, c_sz, c_vp]),
 }

@@ -19,7 +19,8 @@ LIB_NAME = "libglq_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "e8_codebook.cpp", "rht.hip", "dequant.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "e8_codebook.cpp", "pack.cpp", "rht.hip", "dequant.hip", "gemv.hip", "gemv_lds.hip",
+           "gemm.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-I" + INCLUDE, "-I" + CSRC, "-Wall", "-Wno-unused-function"]
 # packed fp32 arithmetic stays off for all device code

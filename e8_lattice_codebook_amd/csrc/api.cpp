@@ -32,29 +32,56 @@ glq_status check_layer(const glq_layer* L, bool need_signs) {
 }
 
 struct LinearWs {
-  size_t u_off, rin_off, z_off, rout_off, total;
+  size_t u_off, uq_off, rin_off, z_off, rout_off, total;
   int splits;
-  bool prefill;
+  bool prefill, lds;
 };
 
 constexpr int64_t kDecodeMaxB = 16;
 
+// the decode kernel with the LDS codebook needs the 16-bit residual stage (if
+// any) to use the primary codebook; otherwise codewords come from global memory
+bool decode_uses_lds(const glq_layer& L) { return L.resid_bits != 16 || L.cb2_pack == L.cb_pack; }
+
+int matmul_splits(const glq_layer& L, int64_t B) {
+  if (B > kDecodeMaxB) return 1;
+  return decode_uses_lds(L) ? gemv_lds_splits(L.n_pad, B) : gemv_splits(L.n_pad, B);
+}
+
+// scratch of glq_e8_matmul: the quantized activations of the LDS decode kernel
+size_t matmul_ws_bytes(const glq_layer& L, int64_t B) {
+  return (B <= kDecodeMaxB && decode_uses_lds(L)) ? uq_bytes(B, L.n_pad) : 0;
+}
+
 LinearWs linear_ws(const glq_layer& L, int64_t B) {
   LinearWs w{};
   w.prefill = B > kDecodeMaxB;
+  w.lds = !w.prefill && decode_uses_lds(L);
   const int ln = log2_exact(L.n_pad), lm = log2_exact(L.m_pad);
   size_t off = 0;
   w.u_off = off;
   off += align256(size_t(B) * size_t(L.n_pad) * (w.prefill ? 2 : 4));
+  w.uq_off = off;
+  if (w.lds) off += align256(uq_bytes(B, L.n_pad));
   w.rin_off = off;
   if (w.prefill && ln > kSingleLog2) off += align256(size_t(B) * size_t(L.n_pad) * 4);
-  w.splits = w.prefill ? 1 : gemv_splits(L.n_pad, B);
+  w.splits = matmul_splits(L, B);
   w.z_off = off;
   off += align256(size_t(w.splits) * size_t(B) * size_t(L.m_pad) * 4);
   w.rout_off = off;
   if (lm > kSingleLog2) off += align256(size_t(B) * size_t(L.m_pad) * 4);
   w.total = off;
   return w;
+}
+
+// decode matmul from fp32 u: quantize into uq (LDS kernel) or gather from global
+hipError_t decode_matmul(const glq_layer& L, const float* u, int64_t B, void* uq, float* z, hipStream_t stream) {
+  if (decode_uses_lds(L)) {
+    hipError_t e = launch_quant_u(u, B, L.n_pad, uq, stream);
+    if (e != hipSuccess) return e;
+    return launch_gemv_lds(L, uq, B, z, stream);
+  }
+  return launch_gemv(L, u, B, z, stream);
 }
 
 template <class T>
@@ -85,16 +112,11 @@ const char* glq_status_string(glq_status s) {
 
 size_t glq_codebook_pack_bytes(int64_t entries) {
   if (entries < 1 || entries > GLQ_CODEBOOK_ENTRIES) return 0;
-  return pack_bytes(entries);
+  return pack_total_bytes(entries);
 }
 
-glq_status glq_codebook_pack(const uint16_t* cb, int64_t entries, void* pack, size_t pack_bytes_given,
-                             int32_t* bad_count, hipStream_t stream) {
-  if (!cb || !pack) return GLQ_ERR_NULL;
-  if (entries < 1 || entries > GLQ_CODEBOOK_ENTRIES) return GLQ_ERR_SHAPE;
-  if (!aligned(pack, 256)) return GLQ_ERR_ALIGN;
-  if (pack_bytes_given < pack_bytes(entries)) return GLQ_ERR_WORKSPACE;
-  return from_hip(launch_codebook_pack(cb, entries, pack, bad_count, stream));
+glq_status glq_codebook_pack(const uint16_t* cb_host, int64_t entries, void* pack_host, size_t pack_bytes_given) {
+  return build_pack(cb_host, entries, pack_host, pack_bytes_given);
 }
 
 size_t glq_input_rht_workspace_bytes(int64_t B, int64_t n_pad, glq_dtype u_dt) {
@@ -146,19 +168,27 @@ glq_status glq_e8_dequant(const glq_layer* layer, void* w, glq_dtype w_dt, hipSt
 
 int64_t glq_e8_matmul_splits(const glq_layer* layer, int64_t B) {
   if (!layer || B < 1 || !valid_pad(layer->n_pad)) return 0;
-  return B > kDecodeMaxB ? 1 : gemv_splits(layer->n_pad, B);
+  return matmul_splits(*layer, B);
+}
+
+size_t glq_e8_matmul_workspace_bytes(const glq_layer* layer, int64_t B) {
+  if (!layer || B < 1 || !valid_pad(layer->n_pad) || !valid_pad(layer->m_pad)) return 0;
+  return matmul_ws_bytes(*layer, B);
 }
 
 glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, int64_t B, float* z_parts,
-                         hipStream_t stream) {
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   glq_status st = check_layer(layer, false);
   if (st != GLQ_OK) return st;
   if (!u || !z_parts) return GLQ_ERR_NULL;
   if (B < 1 || B > int64_t(1) << 31) return GLQ_ERR_SHAPE;
   if (u_dt != (B > kDecodeMaxB ? GLQ_F16 : GLQ_F32)) return GLQ_ERR_DTYPE;
   if (!aligned(u, 16)) return GLQ_ERR_ALIGN;
+  const size_t need = matmul_ws_bytes(*layer, B);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GLQ_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 256)) return GLQ_ERR_ALIGN;
   if (B > kDecodeMaxB) return from_hip(launch_gemm(*layer, static_cast<const half_t*>(u), B, z_parts, stream));
-  return from_hip(launch_gemv(*layer, static_cast<const float*>(u), B, z_parts, stream));
+  return from_hip(decode_matmul(*layer, static_cast<const float*>(u), B, workspace, z_parts, stream));
 }
 
 size_t glq_e8rht_linear_workspace_bytes(const glq_layer* layer, int64_t B) {
@@ -184,7 +214,7 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
     float* u = at<float>(workspace, w.u_off);
     e = launch_rht_in(x, x_dt, B, L.n, ln, L.sign_in, u, GLQ_F32, nullptr, stream);
     if (e != hipSuccess) return GLQ_ERR_HIP;
-    e = launch_gemv(L, u, B, z, stream);
+    e = decode_matmul(L, u, B, at<char>(workspace, w.uq_off), z, stream);
     if (e != hipSuccess) return GLQ_ERR_HIP;
   } else {
     half_t* u = at<half_t>(workspace, w.u_off);

@@ -6,9 +6,8 @@
 // "Inference kernels": the kernels gather 8-D codewords from a compact cached
 // codebook.
 //
-// Pack: every E8 coordinate of norm^2 <= 12 is a multiple of 1/2 with |c| <= 3,
-// so 2c is an exact int8; the pack holds that int8 table [entries][8] (512 KiB
-// for the primary codebook, 2 KiB for the 256-entry residual).
+// The codebook pack holds 2c as an int8 table [entries][8] (exact: every E8
+// coordinate of norm^2 <= 12 is a multiple of 1/2 with |c| <= 3).
 //
 // Dequant: e = c0 + s_r * c1 (exact in fp32 for the codebook values and
 // s_r = 2^-k; in general one rounding), w = RN(s * e); fp16 / bf16 outputs are
@@ -17,19 +16,6 @@
 
 namespace glq {
 namespace {
-
-__global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
-
-__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ cb, int64_t count,
-                                                   int8_t* __restrict__ out, int32_t* __restrict__ bad) {
-  const int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (k >= count) return;
-  const float f = (float)__builtin_bit_cast(half_t, cb[k]);
-  const float t = 2.0f * f;
-  const bool ok = (t == rintf(t)) && t >= -8.0f && t <= 7.0f;
-  out[k] = ok ? int8_t(int(t)) : int8_t(0);
-  if (!ok && bad) atomicAdd(bad, 1);
-}
 
 __device__ __forceinline__ float i8_at(uint32_t w, int j) { return float(int8_t(uint8_t(w >> (8 * j)))); }
 
@@ -117,18 +103,6 @@ hipError_t dequant_typed(const glq_layer& L, void* w, hipStream_t stream) {
 }
 
 }  // namespace
-
-hipError_t launch_codebook_pack(const uint16_t* cb, int64_t entries, void* pack, int32_t* bad, hipStream_t stream) {
-  if (bad) {
-    hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, stream, bad);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int64_t count = entries * 8;
-  hipLaunchKernelGGL(pack_kernel, dim3(unsigned((count + 255) / 256)), dim3(256), 0, stream, cb, count,
-                     static_cast<int8_t*>(pack) + pack_i8_offset(), bad);
-  return hipGetLastError();
-}
 
 hipError_t launch_dequant(const glq_layer& layer, void* w, glq_dtype w_dt, hipStream_t stream) {
   switch (w_dt) {

@@ -1,0 +1,453 @@
+// Decode matmul (B <= 16) with the E8 codebook resident in LDS, on gfx950.
+//
+// glq 0.5.1 (PyPI project page), "Inference kernels": for each output row the
+// kernel walks the N/8 codebook blocks, gathers each 8-D codeword and accumulates
+// the matmul against the indices without forming W; split-K partial sums go to a
+// scratch buffer and are reduced in a fixed order.  "How it works", items 1 and
+// 4; table "Bit widths" (16-bit primary; 8-bit or 16-bit residual stage).
+//
+// Gathers: the pack's LDS image (page table + 4-byte codeword slots, each
+// negation-symmetric shell stored once) is copied into LDS by every workgroup;
+// a codeword costs two LDS reads (descriptor, slot).  A negated shell entry is
+// read as its bitwise complement n ^ ~0, whose signed 4-bit lanes are -2c - 1.
+//
+// Arithmetic: u is quantized per 64 columns to integers U (|U| <= 30583) written
+// as four signed base-16 digit planes d_p (U = sum_p 16^p d_p).  For one group,
+// v_dot8_i32_i4(n, d_p) gives sum_j 2c_j d_pj exactly, so four of them give
+// sum_j 2c_j U_j; for a complemented codeword the result is -sum 2c U - sum U,
+// and sum_j U_j of the group (precomputed) is added back.  Per row and lane the
+// integer total is exact (< 2^24), converted to fp32, scaled by the lane's 64-
+// column scale, reduced over the lanes of the row with DPP adds in a fixed order,
+// and one lane writes (s / 2) * total to z_parts[split][b][o].
+//
+// Mapping: 1024-thread persistent workgroups (one per CU, the image takes ~151
+// KiB).  A wave owns a K-chunk of LPR * GL groups (lane: GL groups, digits for
+// every batch row in registers) and walks contiguous row-steps of 64 / LPR rows,
+// prefetching the next row-step's index vectors with non-temporal loads.
+#include "internal.h"
+
+namespace glq {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kUqMax = 30583;  // 7 * (16^3 + 16^2 + 16 + 1): four balanced base-16 digits
+
+// quantized u: digits [B][G][4] u32 | gsum [B][G] i32 | scale [B][nblk] f32
+struct UqLayout {
+  size_t dig_off, sum_off, scale_off, total;
+  int64_t nblk, bg;
+};
+
+UqLayout uq_layout(int64_t B, int64_t n_pad) {
+  UqLayout L;
+  const int64_t G = n_pad / 8;
+  L.bg = G < 8 ? G : 8;
+  L.nblk = G / L.bg;
+  L.dig_off = 0;
+  L.sum_off = align256(size_t(B * G) * 16);
+  L.scale_off = L.sum_off + align256(size_t(B * G) * 4);
+  L.total = L.scale_off + align256(size_t(B * L.nblk) * 4);
+  return L;
+}
+
+// ---- u -> digit planes -----------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_u_kernel(const float* __restrict__ u, int64_t B, int64_t G, int bg_log2,
+                                                      uint32_t* __restrict__ dig, int32_t* __restrict__ gsum,
+                                                      float* __restrict__ scale) {
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const bool live = t < B * G;
+  const int64_t tt = live ? t : 0;
+  const float4 a = reinterpret_cast<const float4*>(u)[tt * 2];
+  const float4 b = reinterpret_cast<const float4*>(u)[tt * 2 + 1];
+  float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  float mx = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[j]));
+  // a block is 2^bg_log2 consecutive groups = consecutive threads
+  for (int off = 1; off < (1 << bg_log2); off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  const float inv = mx > 0.0f ? float(kUqMax) / mx : 0.0f;
+  uint32_t planes[4] = {0u, 0u, 0u, 0u};
+  int32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int U = int(rintf(v[j] * inv));
+    U = U > kUqMax ? kUqMax : (U < -kUqMax ? -kUqMax : U);
+    s += U;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int d = ((U + 8) & 15) - 8;  // balanced digit in [-8, 7]
+      planes[p] |= uint32_t(d & 15) << (4 * j);
+      U = (U - d) >> 4;
+    }
+  }
+  if (!live) return;
+  reinterpret_cast<uint4*>(dig)[t] = make_uint4(planes[0], planes[1], planes[2], planes[3]);
+  gsum[t] = s;
+  if ((t & ((int64_t(1) << bg_log2) - 1)) == 0) scale[t >> bg_log2] = mx / float(kUqMax);
+}
+
+// ---- DPP reduction over LPR consecutive lanes; the sum lands in lane LPR - 1 ---------
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+  int r;
+  const int x = __float_as_int(v);
+  switch (ctrl_sel) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+    case 1: r = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    case 2: r = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    case 3: r = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false); break;  // row_mirror
+    case 4: r = __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false); break;  // row_bcast15 -> rows 1,3
+    default: r = __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false); break; // row_bcast31 -> rows 2,3
+  }
+  return v + __int_as_float(r);
+}
+
+__device__ __forceinline__ float lane_reduce(float v, int lpr_log2) {
+  if (lpr_log2 >= 1) v = dpp_add(v, 0);
+  if (lpr_log2 >= 2) v = dpp_add(v, 1);
+  if (lpr_log2 >= 3) v = dpp_add(v, 2);
+  if (lpr_log2 >= 4) v = dpp_add(v, 3);
+  if (lpr_log2 >= 5) v = dpp_add(v, 4);
+  if (lpr_log2 >= 6) v = dpp_add(v, 5);
+  return v;
+}
+
+template <int GL>
+struct IdxRow {
+  uint32_t w[GL >= 2 ? GL / 2 : 1];
+};
+
+template <int GL>
+__device__ __forceinline__ void load_idx16(const uint16_t* p, IdxRow<GL>& r) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (GL == 8) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  } else if constexpr (GL == 4) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    r.w[0] = v.x; r.w[1] = v.y;
+  } else if constexpr (GL == 2) {
+    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const unsigned int*>(p));
+  } else {
+    r.w[0] = __builtin_nontemporal_load(p);
+  }
+}
+
+template <int GL>
+__device__ __forceinline__ uint32_t idx16_at(const IdxRow<GL>& r, int q) {
+  if constexpr (GL == 1) return r.w[0] & 0xFFFFu;
+  return (r.w[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
+}
+
+template <int GL>
+struct Idx8Row {
+  uint32_t w[GL >= 4 ? GL / 4 : 1];
+};
+
+template <int GL>
+__device__ __forceinline__ void load_idx8(const uint8_t* p, Idx8Row<GL>& r) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (GL == 8) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    r.w[0] = v.x; r.w[1] = v.y;
+  } else if constexpr (GL == 4) {
+    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const unsigned int*>(p));
+  } else if constexpr (GL == 2) {
+    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p));
+  } else {
+    r.w[0] = __builtin_nontemporal_load(p);
+  }
+}
+
+template <int GL>
+__device__ __forceinline__ uint32_t idx8_at(const Idx8Row<GL>& r, int q) {
+  if constexpr (GL < 4) return (r.w[0] >> (8 * q)) & 0xFFu;
+  return (r.w[q >> 2] >> (8 * (q & 3))) & 0xFFu;
+}
+
+// codeword lookup through the page table: returns the slot word and the
+// complement mask (0 or ~0)
+__device__ __forceinline__ uint32_t lookup(const uint32_t* lds, uint32_t idx, int32_t& m) {
+  const uint32_t desc = lds[idx >> 8];
+  const int32_t d = int32_t(idx) - int32_t(desc & 0xFFFFu);
+  m = d >> 31;
+  const uint32_t slot = uint32_t(d ^ m) + (desc >> 16);
+  return lds[kPageCount + slot] ^ uint32_t(m);
+}
+
+template <int NB, int GL, int RESID>
+__global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
+    const uint16_t* __restrict__ idx0, const void* __restrict__ idx1v, const uint32_t* __restrict__ pack0_hdr,
+    const uint32_t* __restrict__ img0, const uint32_t* __restrict__ res_slots, const uint32_t* __restrict__ uq_dig,
+    const int32_t* __restrict__ uq_sum, const float* __restrict__ uq_scale, int B, int64_t n_pad, int64_t m_pad,
+    int lpr_log2, int bg_log2, int64_t nblk, int64_t units_per_wave, int64_t row_steps, int splits, float out_scale,
+    float sr, float* __restrict__ z_parts) {
+  extern __shared__ uint32_t lds[];
+  const int tid = threadIdx.x;
+  // ---- LDS image: page table + slots (+ 8-bit residual slots after the budget)
+  {
+    uint32_t nd = pack0_hdr[3];
+    nd = nd > uint32_t(kImageMaxDwords) ? uint32_t(kImageMaxDwords) : nd;
+    const uint32_t nd4 = nd >> 2;
+    const uint4* src4 = reinterpret_cast<const uint4*>(img0);
+    uint4* dst4 = reinterpret_cast<uint4*>(lds);
+    for (uint32_t i = tid; i < nd4; i += kThreads) dst4[i] = src4[i];
+    for (uint32_t i = (nd4 << 2) + tid; i < nd; i += kThreads) lds[i] = img0[i];
+    if (RESID == 8) {
+      for (int i = tid; i < kResidDwords; i += kThreads) lds[kImageMaxDwords + i] = res_slots[i];
+    }
+  }
+  __syncthreads();
+
+  const int lane = tid & 63;
+  const int LPR = 1 << lpr_log2;
+  const int RPS = 64 >> lpr_log2;
+  const int lane_in_row = lane & (LPR - 1);
+  const int row_in_step = lane >> lpr_log2;
+  const int64_t G = n_pad >> 3;
+  const int64_t total_units = row_steps * splits;
+  const int64_t wave_global = int64_t(blockIdx.x) * (kThreads / 64) + (tid >> 6);
+  const int64_t u_begin = wave_global * units_per_wave;
+  int64_t u_end = u_begin + units_per_wave;
+  if (u_end > total_units) u_end = total_units;
+  const uint8_t* idx1_8 = static_cast<const uint8_t*>(idx1v);
+  const uint16_t* idx1_16 = static_cast<const uint16_t*>(idx1v);
+
+  uint32_t dig[NB][GL][4];
+  int32_t gs[NB][GL];
+  float sc[NB];
+  int cur_split = -1;
+  int64_t g0 = 0;
+  (void)g0;
+
+  // row-step `unit` -> split, row, first group of this lane
+  auto unit_split = [&](int64_t unit) { return int(unit / row_steps); };
+  auto unit_row = [&](int64_t unit, int split) { return (unit - int64_t(split) * row_steps) * RPS + row_in_step; };
+  auto lane_g0 = [&](int split) { return int64_t(split) * (LPR * GL) + int64_t(lane_in_row) * GL; };
+
+  IdxRow<GL> n0, n1w;
+  Idx8Row<GL> n1b;
+  if (u_begin < u_end) {
+    const int sp = unit_split(u_begin);
+    int64_t o = unit_row(u_begin, sp);
+    o = o < m_pad ? o : 0;
+    const int64_t off = o * G + lane_g0(sp);
+    load_idx16<GL>(idx0 + off, n0);
+    if (RESID == 16) load_idx16<GL>(idx1_16 + off, n1w);
+    if (RESID == 8) load_idx8<GL>(idx1_8 + off, n1b);
+  }
+
+  for (int64_t unit = u_begin; unit < u_end; ++unit) {
+    const int split = unit_split(unit);
+    const int64_t o = unit_row(unit, split);
+    const bool valid = o < m_pad;
+    const IdxRow<GL> i0 = n0;
+    const IdxRow<GL> i1w = n1w;
+    const Idx8Row<GL> i1b = n1b;
+    if (unit + 1 < u_end) {
+      const int sp = unit_split(unit + 1);
+      int64_t on = unit_row(unit + 1, sp);
+      on = on < m_pad ? on : 0;
+      const int64_t off = on * G + lane_g0(sp);
+      load_idx16<GL>(idx0 + off, n0);
+      if (RESID == 16) load_idx16<GL>(idx1_16 + off, n1w);
+      if (RESID == 8) load_idx8<GL>(idx1_8 + off, n1b);
+    }
+    if (split != cur_split) {
+      cur_split = split;
+      g0 = lane_g0(split);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int bb = b < B ? b : 0;
+#pragma unroll
+        for (int q = 0; q < GL; ++q) {
+          const uint4 v = reinterpret_cast<const uint4*>(uq_dig)[int64_t(bb) * G + g0 + q];
+          dig[b][q][0] = v.x; dig[b][q][1] = v.y; dig[b][q][2] = v.z; dig[b][q][3] = v.w;
+          gs[b][q] = uq_sum[int64_t(bb) * G + g0 + q];
+        }
+        sc[b] = b < B ? uq_scale[int64_t(bb) * nblk + (g0 >> bg_log2)] : 0.0f;
+      }
+    }
+
+    int acc0[NB][4], acc1[NB][4], corr0[NB], corr1[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      corr0[b] = corr1[b] = 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) acc0[b][p] = acc1[b][p] = 0;
+    }
+#pragma unroll
+    for (int q = 0; q < GL; ++q) {
+      int32_t m;
+      const uint32_t n = lookup(lds, idx16_at<GL>(i0, q), m);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc0[b][p] = __builtin_amdgcn_sdot8(int(n), int(dig[b][q][p]), acc0[b][p], false);
+        corr0[b] += m & gs[b][q];
+      }
+      if (RESID == 16) {
+        int32_t m1;
+        const uint32_t n1 = lookup(lds, idx16_at<GL>(i1w, q), m1);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            acc1[b][p] = __builtin_amdgcn_sdot8(int(n1), int(dig[b][q][p]), acc1[b][p], false);
+          corr1[b] += m1 & gs[b][q];
+        }
+      }
+      if (RESID == 8) {
+        const uint32_t n1 = lds[kImageMaxDwords + idx8_at<GL>(i1b, q)];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            acc1[b][p] = __builtin_amdgcn_sdot8(int(n1), int(dig[b][q][p]), acc1[b][p], false);
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int t0 = (((acc0[b][3] * 16 + acc0[b][2]) * 16 + acc0[b][1]) * 16 + acc0[b][0]) + corr0[b];
+      float v = float(t0);
+      if (RESID != 0) {
+        const int t1 = (((acc1[b][3] * 16 + acc1[b][2]) * 16 + acc1[b][1]) * 16 + acc1[b][0]) + corr1[b];
+        v = fmaf(sr, float(t1), v);
+      }
+      v = lane_reduce(v * sc[b], lpr_log2);
+      if (valid && lane_in_row == LPR - 1 && b < B) z_parts[(int64_t(split) * B + b) * m_pad + o] = v * out_scale;
+    }
+  }
+}
+
+constexpr int gl_for(int nb) { return nb <= 1 ? 8 : nb <= 2 ? 4 : nb <= 8 ? 2 : 1; }
+
+int nb_tile(int64_t B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : 16; }
+
+struct Plan {
+  int nb, gl, lpr_log2, splits;
+};
+
+Plan make_plan(int64_t n_pad, int64_t B) {
+  Plan p;
+  p.nb = nb_tile(B);
+  const int64_t G = n_pad / 8;
+  int gl = gl_for(p.nb);
+  while (gl > G) gl >>= 1;
+  p.gl = gl;
+  const int64_t lanes = G / gl;
+  int l = 0;
+  while ((int64_t(1) << l) < lanes && l < 6) ++l;
+  p.lpr_log2 = l;
+  p.splits = int(G / (int64_t(gl) << l));
+  return p;
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+constexpr size_t kLdsBytes = size_t(kImageMaxDwords + kResidDwords) * 4;
+
+template <int NB, int GL, int RESID>
+hipError_t launch_t(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream) {
+  auto kern = gemv_lds_kernel<NB, GL, RESID>;
+  static bool attr_set = false;  // per-process attribute, set before the first launch
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsBytes));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int rps = 64 >> p.lpr_log2;
+  const int64_t row_steps = (L.m_pad + rps - 1) / rps;
+  const int64_t units = row_steps * p.splits;
+  const int64_t max_waves = int64_t(device_cus()) * (kThreads / 64);
+  const int64_t upw = (units + max_waves - 1) / max_waves;
+  const int64_t waves = (units + upw - 1) / upw;
+  const int64_t blocks = (waves + (kThreads / 64) - 1) / (kThreads / 64);
+  const UqLayout U = uq_layout(B, L.n_pad);
+  const char* uqc = static_cast<const char*>(uq);
+  const char* p0 = static_cast<const char*>(L.cb_pack);
+  const uint32_t* img0 = reinterpret_cast<const uint32_t*>(p0 + pack_image_offset(GLQ_CODEBOOK_ENTRIES));
+  const uint32_t* res = nullptr;
+  if (RESID == 8)
+    res = reinterpret_cast<const uint32_t*>(static_cast<const char*>(L.cb2_pack) +
+                                            pack_image_offset(GLQ_RESID8_ENTRIES)) + kPageCount;
+  int bg_log2 = 0;
+  while ((int64_t(1) << bg_log2) < U.bg) ++bg_log2;
+  hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), kLdsBytes, stream, L.idx0, L.idx1,
+                     reinterpret_cast<const uint32_t*>(p0), img0, res,
+                     reinterpret_cast<const uint32_t*>(uqc + U.dig_off), reinterpret_cast<const int32_t*>(uqc + U.sum_off),
+                     reinterpret_cast<const float*>(uqc + U.scale_off), int(B), L.n_pad, L.m_pad, p.lpr_log2, bg_log2,
+                     U.nblk, upw, row_steps, p.splits, 0.5f * L.wscale, L.resid_scale, z);
+  return hipGetLastError();
+}
+
+template <int NB, int GL>
+hipError_t launch_r(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream) {
+  switch (L.resid_bits) {
+    case 0: return launch_t<NB, GL, 0>(L, uq, B, z, p, stream);
+    case 8: return launch_t<NB, GL, 8>(L, uq, B, z, p, stream);
+    default: return launch_t<NB, GL, 16>(L, uq, B, z, p, stream);
+  }
+}
+
+template <int NB>
+hipError_t launch_nb(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream) {
+  switch (p.gl) {
+    case 8:
+      if constexpr (gl_for(NB) >= 8) return launch_r<NB, 8>(L, uq, B, z, p, stream);
+      break;
+    case 4:
+      if constexpr (gl_for(NB) >= 4) return launch_r<NB, 4>(L, uq, B, z, p, stream);
+      break;
+    case 2:
+      if constexpr (gl_for(NB) >= 2) return launch_r<NB, 2>(L, uq, B, z, p, stream);
+      break;
+    default:
+      return launch_r<NB, 1>(L, uq, B, z, p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t uq_bytes(int64_t B, int64_t n_pad) { return uq_layout(B, n_pad).total; }
+
+int gemv_lds_splits(int64_t n_pad, int64_t B) { return make_plan(n_pad, B).splits; }
+
+hipError_t launch_quant_u(const float* u, int64_t B, int64_t n_pad, void* uq, hipStream_t stream) {
+  const UqLayout U = uq_layout(B, n_pad);
+  const int64_t G = n_pad / 8;
+  int bg_log2 = 0;
+  while ((int64_t(1) << bg_log2) < U.bg) ++bg_log2;
+  char* q = static_cast<char*>(uq);
+  const int64_t threads = B * G;
+  hipLaunchKernelGGL(quant_u_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, stream, u, B, G, bg_log2,
+                     reinterpret_cast<uint32_t*>(q + U.dig_off), reinterpret_cast<int32_t*>(q + U.sum_off),
+                     reinterpret_cast<float*>(q + U.scale_off));
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_lds(const glq_layer& L, const void* uq, int64_t B, float* z_parts, hipStream_t stream) {
+  const Plan p = make_plan(L.n_pad, B);
+  switch (p.nb) {
+    case 1: return launch_nb<1>(L, uq, B, z_parts, p, stream);
+    case 2: return launch_nb<2>(L, uq, B, z_parts, p, stream);
+    case 4: return launch_nb<4>(L, uq, B, z_parts, p, stream);
+    case 8: return launch_nb<8>(L, uq, B, z_parts, p, stream);
+    default: return launch_nb<16>(L, uq, B, z_parts, p, stream);
+  }
+}
+
+}  // namespace glq

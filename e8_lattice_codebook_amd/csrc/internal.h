@@ -57,13 +57,19 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
 }
 
 // ---- codebook pack layout ----------------------------------------------------
-// offset 0: int8 [entries][8], each value 2*c (exact for c in Z/2, |c| <= 4)
-inline size_t pack_i8_offset() { return 0; }
-inline size_t pack_bytes(int64_t entries) { return align256(size_t(entries) * 8); }
+// header (256 B) | int8 table [entries][8] = 2c | LDS image (page table + slots)
+constexpr uint32_t kPackMagic = 0x32514C47u;  // "GLQ2"
+constexpr uint32_t kPackVersion = 2;
+constexpr int kPageSize = 256;                 // indices per page
+constexpr int kPageCount = 256;                // pages of a 16-bit index
+constexpr int kImageMaxDwords = 38912;         // LDS image budget: 152 KiB
+constexpr int kResidDwords = 256;              // 8-bit residual slots (direct)
+inline size_t pack_i8_offset() { return 256; }
+inline size_t pack_image_offset(int64_t entries) { return align256(256 + size_t(entries) * 8); }
+size_t pack_total_bytes(int64_t entries);
+glq_status build_pack(const uint16_t* cb_host, int64_t entries, void* pack_host, size_t pack_bytes);
 
 // ---- launchers (return the launch status) -----------------------------------
-hipError_t launch_codebook_pack(const uint16_t* cb, int64_t entries, void* pack, int32_t* bad,
-                                hipStream_t stream);
 
 // Input transform; ws: fp32 [B][N] scratch used only when N > 2^kSingleLog2 and u_dt != F32.
 hipError_t launch_rht_in(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int L, const int8_t* sign,
@@ -74,10 +80,20 @@ hipError_t launch_rht_out(const float* z, int64_t S, int64_t B, int64_t m, int L
 
 hipError_t launch_dequant(const glq_layer& layer, void* w, glq_dtype w_dt, hipStream_t stream);
 
-// Decode matmul: partial sums z_parts [S][B][m_pad] with S = gemv_splits(...).
+// Decode matmul, codewords gathered from the packs' int8 tables in global memory
+// (used when a 16-bit residual stage has its own codebook): z_parts [S][B][m_pad].
 int gemv_splits(int64_t n_pad, int64_t B);
 hipError_t launch_gemv(const glq_layer& layer, const float* u, int64_t B, float* z_parts,
                        hipStream_t stream);
+
+// Decode matmul with the codebook image resident in LDS.  u is first quantized to
+// 16-bit fixed point (4 int4 digit planes per 8-column group, one scale per 64
+// columns) into uq_bytes(B, n_pad) of scratch; z_parts [S][B][m_pad] with
+// S = gemv_lds_splits(n_pad, B).
+size_t uq_bytes(int64_t B, int64_t n_pad);
+int gemv_lds_splits(int64_t n_pad, int64_t B);
+hipError_t launch_quant_u(const float* u, int64_t B, int64_t n_pad, void* uq, hipStream_t stream);
+hipError_t launch_gemv_lds(const glq_layer& layer, const void* uq, int64_t B, float* z_parts, hipStream_t stream);
 
 // Prefill matmul: z [M][m_pad] fp32 from u16 [M][n_pad] fp16.
 hipError_t launch_gemm(const glq_layer& layer, const half_t* u16, int64_t M, float* z, hipStream_t stream);

@@ -1,0 +1,188 @@
+// Host construction of a codebook pack (glq_codebook_pack).
+//
+// glq 0.5.1 (PyPI project page), "How it works", item 1 and "Inference kernels":
+// the kernels gather 8-D codewords from a compact cached codebook.  On gfx950 the
+// codebook is gathered from LDS, which holds 160 KB per CU, so the pack carries
+// an LDS image in which every codeword takes 4 bytes (eight signed 4-bit values
+// 2c, c in Z/2, |2c| <= 8) and each negation-symmetric shell is stored once.
+//
+// Layout (offsets in bytes, all 256-byte aligned):
+//   0                header: kPackMagic, version, entries, image dwords, slots, flags
+//   256              int8 table [entries][8], value 2c (kernels that dequantize)
+//   image_offset     LDS image: page table [256] u32, then slot words
+//
+// Page table: index i falls in page i >> 8.  desc = (R << 16) | M.  The kernels
+// compute d = i - M, m = d >> 31 (0 or -1), slot = R + (d ^ m): for a shell stored
+// by distance from its centre M (entries M + r and M - 1 - r are negatives of each
+// other) this reads the same slot for both, and m = -1 marks the negated one.
+// Non-symmetric runs and pages that straddle two runs are stored directly
+// (M at or below the page start, so m = 0 and slot = R + i - M).
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+struct Run {
+  int64_t start, size;
+  bool mirrored;
+  int64_t center;  // M
+  int64_t base;    // R (slot of distance 0, or of the run start); -1 until allocated
+};
+
+}  // namespace
+
+namespace glq {
+
+size_t pack_total_bytes(int64_t entries) {
+  return size_t(pack_image_offset(entries)) + size_t(kImageMaxDwords) * 4;
+}
+
+glq_status build_pack(const uint16_t* cb, int64_t entries, void* out_pack, size_t out_bytes) {
+  if (!cb || !out_pack) return GLQ_ERR_NULL;
+  if (entries < 1 || entries > GLQ_CODEBOOK_ENTRIES) return GLQ_ERR_SHAPE;
+  if (out_bytes < pack_total_bytes(entries)) return GLQ_ERR_WORKSPACE;
+  // doubled coordinates
+  std::vector<int> t(size_t(entries) * 8);
+  for (int64_t i = 0; i < entries * 8; ++i) {
+    const uint16_t h = cb[i];
+    const int sign = (h >> 15) & 1, ex = (h >> 10) & 31, man = h & 1023;
+    if (ex == 31) return GLQ_ERR_CODEBOOK;  // inf / nan
+    // value = (-1)^sign * (ex ? (1024 + man) * 2^(ex - 25) : man * 2^-24); need 2 * value integer
+    int64_t mant = ex ? (1024 + man) : man;
+    int shift = (ex ? ex : 1) - 25 + 1;  // doubled value = mant * 2^shift
+    int64_t v;
+    if (shift >= 0) {
+      if (shift > 8) return GLQ_ERR_CODEBOOK;
+      v = mant << shift;
+    } else {
+      if (-shift >= 40) {
+        if (mant != 0) return GLQ_ERR_CODEBOOK;
+        v = 0;
+      } else {
+        if (mant & ((int64_t(1) << -shift) - 1)) return GLQ_ERR_CODEBOOK;  // not a multiple of 1/2
+        v = mant >> -shift;
+      }
+    }
+    if (sign) v = -v;
+    if (v < -8 || v > 7) return GLQ_ERR_CODEBOOK;
+    t[size_t(i)] = int(v);
+  }
+  auto word = [&](int64_t i) {
+    uint32_t w = 0;
+    for (int j = 0; j < 8; ++j) w |= uint32_t(t[size_t(i * 8 + j)] & 15) << (4 * j);
+    return w;
+  };
+  auto norm2 = [&](int64_t i) {
+    int s = 0;
+    for (int j = 0; j < 8; ++j) s += t[size_t(i * 8 + j)] * t[size_t(i * 8 + j)];
+    return s;
+  };
+
+  // maximal runs of equal squared norm; symmetric runs (entry O + k is the
+  // negation of entry O + N - 1 - k, N even) are stored by distance from the centre
+  std::vector<Run> runs;
+  for (int64_t i = 0; i < entries;) {
+    int64_t j = i + 1;
+    const int nn = norm2(i);
+    while (j < entries && norm2(j) == nn) ++j;
+    Run r{i, j - i, false, i, -1};
+    if (r.size >= 2 && r.size % 2 == 0) {
+      bool sym = true;
+      for (int64_t k = 0; k < r.size / 2 && sym; ++k)
+        for (int c = 0; c < 8 && sym; ++c)
+          if (t[size_t((i + k) * 8 + c)] != -t[size_t((i + r.size - 1 - k) * 8 + c)]) sym = false;
+      if (sym) {
+        r.mirrored = true;
+        r.center = i + r.size / 2;
+      }
+    }
+    runs.push_back(r);
+    i = j;
+  }
+  auto run_of = [&](int64_t i) {
+    int64_t lo = 0, hi = int64_t(runs.size()) - 1;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (runs[size_t(mid)].start <= i) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+
+  // pages: a page whose indices (those below `entries`) lie in one run uses that
+  // run's descriptor; packs of at most 256 entries and straddling pages are direct
+  const int64_t n_pages = (entries + kPageSize - 1) / kPageSize;
+  std::vector<int64_t> page_run(size_t(kPageCount), -1);
+  for (int64_t p = 0; p < n_pages; ++p) {
+    const int64_t a = p * kPageSize, b = std::min<int64_t>(entries, a + kPageSize) - 1;
+    const int64_t ra = run_of(a), rb = run_of(b);
+    if (ra == rb && entries > kPageSize) page_run[size_t(p)] = ra;
+  }
+  std::vector<uint32_t> slots;
+  std::vector<uint32_t> desc(size_t(kPageCount), 0);
+  // exception (direct) pages first, in page order: a pack of <= 256 entries is slot = index
+  for (int64_t p = 0; p < n_pages; ++p) {
+    if (page_run[size_t(p)] >= 0) continue;
+    const int64_t a = p * kPageSize;
+    const int64_t R = int64_t(slots.size());
+    for (int64_t k = 0; k < kPageSize; ++k) slots.push_back(a + k < entries ? word(a + k) : 0u);
+    // d = i - M with M = a >= 0 -> slot = R + i - a
+    if (R > 0xFFFF || a > 0xFFFF) return GLQ_ERR_CODEBOOK;
+    desc[size_t(p)] = uint32_t(R << 16) | uint32_t(a);
+  }
+  for (int64_t p = 0; p < n_pages; ++p) {
+    const int64_t ri = page_run[size_t(p)];
+    if (ri < 0) continue;
+    Run& r = runs[size_t(ri)];
+    if (r.base < 0) {
+      r.base = int64_t(slots.size());
+      if (r.mirrored) {
+        for (int64_t k = 0; k < r.size / 2; ++k) slots.push_back(word(r.center + k));
+      } else {
+        for (int64_t k = 0; k < r.size; ++k) slots.push_back(word(r.start + k));
+      }
+    }
+    if (r.base > 0xFFFF || r.center > 0xFFFF) return GLQ_ERR_CODEBOOK;
+    desc[size_t(p)] = uint32_t(r.base << 16) | uint32_t(r.center);
+  }
+  const int64_t image_dwords = kPageCount + int64_t(slots.size());
+  if (image_dwords > kImageMaxDwords) return GLQ_ERR_CODEBOOK;
+
+  // self-check: every index resolves to its own codeword
+  for (int64_t i = 0; i < entries; ++i) {
+    const uint32_t dsc = desc[size_t(i >> 8)];
+    const int32_t d = int32_t(i) - int32_t(dsc & 0xFFFF);
+    const int32_t m = d >> 31;
+    const uint32_t slot = uint32_t(d ^ m) + (dsc >> 16);
+    if (slot >= slots.size()) return GLQ_ERR_CODEBOOK;
+    uint32_t w = slots[slot];
+    if (m) {  // negate every 4-bit lane
+      uint32_t neg = 0;
+      for (int j = 0; j < 8; ++j) {
+        const int v = int32_t(((w >> (4 * j)) & 15u) << 28) >> 28;
+        neg |= uint32_t(-v & 15) << (4 * j);
+      }
+      w = neg;
+    }
+    if (w != word(i)) return GLQ_ERR_CODEBOOK;
+  }
+
+  // write the pack
+  std::memset(out_pack, 0, pack_total_bytes(entries));
+  uint32_t* hdr = static_cast<uint32_t*>(out_pack);
+  hdr[0] = kPackMagic;
+  hdr[1] = kPackVersion;
+  hdr[2] = uint32_t(entries);
+  hdr[3] = uint32_t(image_dwords);
+  hdr[4] = uint32_t(slots.size());
+  int8_t* i8 = static_cast<int8_t*>(out_pack) + pack_i8_offset();
+  for (int64_t i = 0; i < entries * 8; ++i) i8[i] = int8_t(t[size_t(i)]);
+  uint32_t* img = reinterpret_cast<uint32_t*>(static_cast<char*>(out_pack) + pack_image_offset(entries));
+  std::memcpy(img, desc.data(), size_t(kPageCount) * 4);
+  std::memcpy(img + kPageCount, slots.data(), slots.size() * 4);
+  return GLQ_OK;
+}
+
+}  // namespace glq

@@ -128,19 +128,24 @@ const char* glq_status_string(glq_status s);
 glq_status glq_e8_codebook(uint16_t* cb_host, int64_t entries);
 
 /*
- * glq_codebook_pack — derive the kernels' codebook representation from an fp16
- * codebook ("Inference kernels": the kernels gather from a compact codebook).
- *   cb          device, fp16 bits [entries][8]; every coordinate must be a
- *               multiple of 1/2 in [-4, 3.5] (true for all E8 points of norm^2 <= 12)
- *   entries     number of rows, 1 .. 65536
- *   pack        device, pack_bytes >= glq_codebook_pack_bytes(entries), 256-byte aligned
- *   bad_count   device int32, optional (NULL to skip): set to the number of
- *               coordinates that violate the requirement above (0 = valid pack)
- * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_ALIGN, GLQ_ERR_WORKSPACE, GLQ_ERR_HIP.
+ * glq_codebook_pack — build the kernels' representation of an fp16 codebook, on
+ * the host ("Inference kernels": the kernels gather 8-D codewords from a compact
+ * cached codebook).  The pack holds 2c as an int8 table and an LDS image that
+ * stores each codeword in 4 bytes (eight signed 4-bit values) and every
+ * negation-symmetric shell once, behind a 256-entry page table; the E8 codebook's
+ * image takes about 151 KiB, which the decode kernel keeps in LDS.
+ *   cb_host     host, fp16 bits [entries][8]; every coordinate a multiple of 1/2
+ *               in [-4, 3.5] (true for all E8 points of norm^2 <= 12)
+ *   entries     1 .. 65536 (the layer uses 65,536-entry packs for the primary and
+ *               16-bit residual stages, a 256-entry pack for the 8-bit residual)
+ *   pack_host   host, pack_bytes >= glq_codebook_pack_bytes(entries); the caller
+ *               copies it to device memory (256-byte aligned) for the layer
+ * Synchronous, host only.  Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_WORKSPACE,
+ * GLQ_ERR_CODEBOOK (a coordinate outside the set above, or an image larger than
+ * the LDS budget).
  */
 size_t glq_codebook_pack_bytes(int64_t entries);
-glq_status glq_codebook_pack(const uint16_t* cb, int64_t entries, void* pack, size_t pack_bytes,
-                             int32_t* bad_count, hipStream_t stream);
+glq_status glq_codebook_pack(const uint16_t* cb_host, int64_t entries, void* pack_host, size_t pack_bytes);
 
 /*
  * glq_input_rht — u = H_{n_pad} (sign_in * [x, 0...]) / sqrt(n_pad) for each of B
@@ -192,18 +197,23 @@ glq_status glq_e8_dequant(const glq_layer* layer, void* w, glq_dtype w_dt, hipSt
  * blocks per output row, gathered and accumulated without forming W; split-K
  * partial sums in a scratch buffer, reduced in a fixed order instead of with
  * atomics).  This is the middle step of glq_e8rht_linear, exposed on its own.
- *   u          device [B][n_pad]: fp32 when B <= 16 (decode kernel, fp32 FMA),
- *              fp16 when B > 16 (prefill kernel, fp16 MFMA, fp32 accumulate)
+ *   u          device [B][n_pad]: fp32 when B <= 16 (decode kernel: u quantized
+ *              to 16-bit fixed point per 64 columns, exact integer dot products
+ *              against the codewords), fp16 when B > 16 (prefill kernel, fp16
+ *              MFMA, fp32 accumulate)
  *   z_parts    device fp32 [S][B][m_pad], S = glq_e8_matmul_splits(layer, B):
  *              z = sum over s = 0 .. S-1 of z_parts[s]; glq_output_rht takes
  *              z_parts and S as they are
+ *   workspace  device, >= glq_e8_matmul_workspace_bytes(layer, B) (may be 0 and
+ *              NULL), 256-byte aligned
  * Only idx0, idx1, packs, resid_bits, wscale, resid_scale, n_pad, m_pad are used.
  * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_DTYPE (u_dt not the one above),
- * GLQ_ERR_RECIPE, GLQ_ERR_ALIGN, GLQ_ERR_HIP.
+ * GLQ_ERR_RECIPE, GLQ_ERR_ALIGN, GLQ_ERR_WORKSPACE, GLQ_ERR_HIP.
  */
 int64_t glq_e8_matmul_splits(const glq_layer* layer, int64_t B);
+size_t glq_e8_matmul_workspace_bytes(const glq_layer* layer, int64_t B);
 glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, int64_t B, float* z_parts,
-                         hipStream_t stream);
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * glq_e8rht_linear — the E8RHTLinear forward, y = RHT_out(RHT_in(x) W~^T)
@@ -212,8 +222,9 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
  *   x          device [B][n] in x_dt (F32, F16 or BF16)
  *   y          device [B][m] in y_dt (F32, F16 or BF16)
  *   workspace  device, >= glq_e8rht_linear_workspace_bytes(layer, B), 256-byte aligned
- * B <= 16: decode path (fp32 activations after the transform, fp32 FMA against
- * codewords gathered per group, split-K partial sums reduced in fixed order).
+ * B <= 16: decode path (transformed activations quantized to 16-bit fixed point
+ * per 64 columns, exact integer dot products against codewords gathered from the
+ * LDS-resident codebook, split-K partial sums reduced in a fixed order).
  * B > 16: prefill path (transformed activations rounded to fp16, codeword tiles
  * dequantized into LDS feeding fp16 MFMA with fp32 accumulation).
  * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_DTYPE, GLQ_ERR_RECIPE, GLQ_ERR_ALIGN,

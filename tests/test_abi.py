@@ -61,7 +61,7 @@ def test_codebook_builder_rejects_bad_sizes():
 
 def test_workspace_queries():
     lib = _lib.load()
-    assert lib.glq_codebook_pack_bytes(65536) == 65536 * 8
+    assert lib.glq_codebook_pack_bytes(65536) >= 256 + 65536 * 8 + 151 * 1024
     assert lib.glq_codebook_pack_bytes(0) == 0
     assert lib.glq_input_rht_workspace_bytes(2, 16384, 1) == 0
     assert lib.glq_input_rht_workspace_bytes(2, 32768, 1) == 2 * 32768 * 4
@@ -131,12 +131,11 @@ class TestValidation:
         assert lib.glq_output_rht(A, 1, 1, 256, 32768, A, A, 0, None, 0, None) == 6
         assert lib.glq_e8_dequant(ctypes.byref(fake_layer()), A + 4, 0, None) == 5
         assert lib.glq_e8_dequant(ctypes.byref(fake_layer(resid_bits=3)), A, 0, None) == 4
-        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 17, A, None) == 3
-        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 1, 16, A, None) == 3
-        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 0, A, None) == 2
-        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A + 4, 0, 1, A, None) == 5
+        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 17, A, A, 1 << 30, None) == 3
+        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 1, 16, A, A, 1 << 30, None) == 3
+        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 0, A, A, 1 << 30, None) == 2
+        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A + 4, 0, 1, A, A, 1 << 30, None) == 5
+        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 1, A, None, 0, None) == 6
+        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 1, A, A, 8, None) == 6
         assert lib.glq_e8_matmul_splits(ctypes.byref(fake_layer(n_pad=32768)), 1) == 8
         assert lib.glq_e8_matmul_splits(ctypes.byref(fake_layer(n_pad=32768)), 17) == 1
-        assert lib.glq_codebook_pack(A, 65536, A, 16, None, None) == 6
-        assert lib.glq_codebook_pack(A, 65536, A + 8, 1 << 20, None, None) == 5
-        assert lib.glq_codebook_pack(A, 0, A, 1 << 20, None, None) == 2
