@@ -23,6 +23,7 @@ glq_status check_layer(const glq_layer* L, bool need_signs) {
   if (!L->idx0 || !L->cb_pack) return GLQ_ERR_NULL;
   if (need_signs && (!L->sign_in || !L->sign_out)) return GLQ_ERR_NULL;
   if (!valid_pad(L->n_pad) || !valid_pad(L->m_pad)) return GLQ_ERR_SHAPE;
+  if (L->m_pad * (L->n_pad / 8) >= (int64_t(1) << 31)) return GLQ_ERR_SHAPE;  // 32-bit group offsets
   if (need_signs && (L->n < 1 || L->n > L->n_pad || L->m < 1 || L->m > L->m_pad)) return GLQ_ERR_SHAPE;
   if (L->resid_bits != 0 && L->resid_bits != 8 && L->resid_bits != 16) return GLQ_ERR_RECIPE;
   if (L->resid_bits != 0 && (!L->idx1 || !L->cb2_pack)) return GLQ_ERR_NULL;

@@ -10,12 +10,13 @@
 // negation-symmetric shell stored once) is copied into LDS by every workgroup;
 // a codeword costs two LDS reads (descriptor, slot).  A negated shell entry is
 // read as its bitwise complement n ^ ~0, whose signed 4-bit lanes are -2c - 1.
+// The image takes ~155 KiB of the CU's 160 KiB.
 //
 // Arithmetic: u is quantized per 64 columns to integers U (|U| <= 30583) written
 // as four signed base-16 digit planes d_p (U = sum_p 16^p d_p).  For one group,
 // v_dot8_i32_i4(n, d_p) gives sum_j 2c_j d_pj exactly, so four of them give
 // sum_j 2c_j U_j; for a complemented codeword the result is -sum 2c U - sum U,
-// and sum_j U_j of the group (precomputed) is added back.  Per row and lane the
+// and sum_j U_j of the group (precomputed) is added back into plane 0.  Per row and lane the
 // integer total is exact (< 2^24), converted to fp32, scaled by the lane's 64-
 // column scale, reduced over the lanes of the row with DPP adds in a fixed order,
 // and one lane writes (s / 2) * total to z_parts[split][b][o].
@@ -165,158 +166,268 @@ __device__ __forceinline__ uint32_t idx8_at(const Idx8Row<GL>& r, int q) {
   return (r.w[q >> 2] >> (8 * (q & 3))) & 0xFFu;
 }
 
-// codeword lookup through the page table: returns the slot word and the
-// complement mask (0 or ~0)
-__device__ __forceinline__ uint32_t lookup(const uint32_t* lds, uint32_t idx, int32_t& m) {
-  const uint32_t desc = lds[idx >> 8];
-  const int32_t d = int32_t(idx) - int32_t(desc & 0xFFFFu);
-  m = d >> 31;
-  const uint32_t slot = uint32_t(d ^ m) + (desc >> 16);
-  return lds[kPageCount + slot] ^ uint32_t(m);
+// ---- VALU byte selects (SDWA) ----------------------------------------------------
+// The index words hold two 16-bit indices (bytes 0-1 and 2-3) or four 8-bit ones.
+// 4 * byte SEL of w, and (byte SEL of w) ^ (byte 0 of d), in one instruction each.
+template <int SEL>
+__device__ __forceinline__ uint32_t byte_x4(uint32_t w, uint32_t two) {
+  uint32_t r;
+  if constexpr (SEL == 0)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(r) : "v"(two), "v"(w));
+  else if constexpr (SEL == 1)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(r) : "v"(two), "v"(w));
+  else if constexpr (SEL == 2)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+        : "=v"(r) : "v"(two), "v"(w));
+  else
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+        : "=v"(r) : "v"(two), "v"(w));
+  return r;
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t xor_byte(uint32_t w, uint32_t d) {
+  uint32_t r;
+  if constexpr (SEL == 0)
+    asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:BYTE_0"
+        : "=v"(r) : "v"(w), "v"(d));
+  else
+    asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:BYTE_0"
+        : "=v"(r) : "v"(w), "v"(d));
+  return r;
 }
 
-template <int NB, int GL, int RESID>
+// LDS layout of the decode kernel (dwords): [0, 256) the 8-bit residual slots,
+// [256, 256 + image) the primary image (page table, then slots).
+constexpr int kResOff = 0;
+constexpr int kImgOff = kResidDwords;
+constexpr int kLdsDwords = kResidDwords + kImageMaxDwords;
+
+__device__ __forceinline__ uint32_t lds_at(const uint32_t* lds, uint32_t byte_addr) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lds) + byte_addr);
+}
+
+// Primary-codebook lookup of the 16-bit index in half HI of word w: the page
+// descriptor (image word idx >> 8), then the slot at image byte offset
+// 4 * ((idx ^ desc) & 255) + (desc >> 8), complemented (m = ~0) on descending pages.
+template <int HI>
+__device__ __forceinline__ uint32_t page_desc(const uint32_t* lds, uint32_t w, uint32_t two) {
+  return lds_at(lds + kImgOff, byte_x4<HI ? 3 : 1>(w, two));
+}
+template <int HI>
+__device__ __forceinline__ uint32_t slot_word(const uint32_t* lds, uint32_t w, uint32_t desc) {
+  const uint32_t x = xor_byte<HI ? 2 : 0>(w, desc);
+  return lds_at(lds + kImgOff, (x << 2) + (desc >> 8));
+}
+
+template <int NB, int GL, int RESID, bool FULL>
 __global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
     const uint16_t* __restrict__ idx0, const void* __restrict__ idx1v, const uint32_t* __restrict__ pack0_hdr,
     const uint32_t* __restrict__ img0, const uint32_t* __restrict__ res_slots, const uint32_t* __restrict__ uq_dig,
-    const int32_t* __restrict__ uq_sum, const float* __restrict__ uq_scale, int B, int64_t n_pad, int64_t m_pad,
-    int lpr_log2, int bg_log2, int64_t nblk, int64_t units_per_wave, int64_t row_steps, int splits, float out_scale,
-    float sr, float* __restrict__ z_parts) {
-  extern __shared__ uint32_t lds[];
+    const int32_t* __restrict__ uq_sum, const float* __restrict__ uq_scale, int B, int G, int m_pad, int lpr_log2,
+    int bg_log2, int nblk, int units_per_wave, int row_steps, int splits, float out_scale, float sr,
+    float* __restrict__ z_parts) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsDwords];
   const int tid = threadIdx.x;
-  // ---- LDS image: page table + slots (+ 8-bit residual slots after the budget)
+  // ---- LDS: 8-bit residual slots, then the primary image (page table + slots)
   {
     uint32_t nd = pack0_hdr[3];
     nd = nd > uint32_t(kImageMaxDwords) ? uint32_t(kImageMaxDwords) : nd;
     const uint32_t nd4 = nd >> 2;
     const uint4* src4 = reinterpret_cast<const uint4*>(img0);
-    uint4* dst4 = reinterpret_cast<uint4*>(lds);
-    for (uint32_t i = tid; i < nd4; i += kThreads) dst4[i] = src4[i];
-    for (uint32_t i = (nd4 << 2) + tid; i < nd; i += kThreads) lds[i] = img0[i];
-    if (RESID == 8) {
-      for (int i = tid; i < kResidDwords; i += kThreads) lds[kImageMaxDwords + i] = res_slots[i];
-    }
+    uint4* dst4 = reinterpret_cast<uint4*>(lds + kImgOff);
+    // all loads in flight before the first LDS store (clamped, unconditional loads)
+    constexpr int kIt = (kImageMaxDwords / 4 + kThreads - 1) / kThreads;
+    const uint32_t last4 = nd4 > 0 ? nd4 - 1 : 0;
+    uint4 t0 = src4[min(uint32_t(tid), last4)];
+    uint4 t1 = src4[min(uint32_t(tid) + 1 * kThreads, last4)];
+    uint4 t2 = src4[min(uint32_t(tid) + 2 * kThreads, last4)];
+    uint4 t3 = src4[min(uint32_t(tid) + 3 * kThreads, last4)];
+    uint4 t4 = src4[min(uint32_t(tid) + 4 * kThreads, last4)];
+    uint4 t5 = src4[min(uint32_t(tid) + 5 * kThreads, last4)];
+    uint4 t6 = src4[min(uint32_t(tid) + 6 * kThreads, last4)];
+    uint4 t7 = src4[min(uint32_t(tid) + 7 * kThreads, last4)];
+    uint4 t8 = src4[min(uint32_t(tid) + 8 * kThreads, last4)];
+    uint4 t9 = src4[min(uint32_t(tid) + 9 * kThreads, last4)];
+    static_assert(kIt == 10, "image load unrolled for 10 steps");
+    uint32_t tail = 0, res = 0;
+    const uint32_t ti = (nd4 << 2) + tid;
+    if (ti < nd) tail = img0[ti];
+    if (RESID == 8 && tid < kResidDwords) res = res_slots[tid];
+    if (uint32_t(tid) + 0 * kThreads < nd4) dst4[tid + 0 * kThreads] = t0;
+    if (uint32_t(tid) + 1 * kThreads < nd4) dst4[tid + 1 * kThreads] = t1;
+    if (uint32_t(tid) + 2 * kThreads < nd4) dst4[tid + 2 * kThreads] = t2;
+    if (uint32_t(tid) + 3 * kThreads < nd4) dst4[tid + 3 * kThreads] = t3;
+    if (uint32_t(tid) + 4 * kThreads < nd4) dst4[tid + 4 * kThreads] = t4;
+    if (uint32_t(tid) + 5 * kThreads < nd4) dst4[tid + 5 * kThreads] = t5;
+    if (uint32_t(tid) + 6 * kThreads < nd4) dst4[tid + 6 * kThreads] = t6;
+    if (uint32_t(tid) + 7 * kThreads < nd4) dst4[tid + 7 * kThreads] = t7;
+    if (uint32_t(tid) + 8 * kThreads < nd4) dst4[tid + 8 * kThreads] = t8;
+    if (uint32_t(tid) + 9 * kThreads < nd4) dst4[tid + 9 * kThreads] = t9;
+    if (ti < nd) lds[kImgOff + ti] = tail;
+    if (RESID == 8 && tid < kResidDwords) lds[kResOff + tid] = res;
   }
-  __syncthreads();
+  const uint32_t two = 2;
 
   const int lane = tid & 63;
-  const int LPR = 1 << lpr_log2;
-  const int RPS = 64 >> lpr_log2;
+  const int lpr = FULL ? 6 : lpr_log2;
+  const int LPR = 1 << lpr;
+  const int RPS = 64 >> lpr;
   const int lane_in_row = lane & (LPR - 1);
-  const int row_in_step = lane >> lpr_log2;
-  const int64_t G = n_pad >> 3;
-  const int64_t total_units = row_steps * splits;
-  const int64_t wave_global = int64_t(blockIdx.x) * (kThreads / 64) + (tid >> 6);
-  const int64_t u_begin = wave_global * units_per_wave;
-  int64_t u_end = u_begin + units_per_wave;
-  if (u_end > total_units) u_end = total_units;
+  const int row_in_step = lane >> lpr;
+  const int total_units = row_steps * splits;
+  const int wave_global = int(blockIdx.x) * (kThreads / 64) + (tid >> 6);
+  const int u_begin = wave_global * units_per_wave;
+  const int u_end = min(u_begin + units_per_wave, total_units);
   const uint8_t* idx1_8 = static_cast<const uint8_t*>(idx1v);
   const uint16_t* idx1_16 = static_cast<const uint16_t*>(idx1v);
 
   uint32_t dig[NB][GL][4];
   int32_t gs[NB][GL];
   float sc[NB];
-  int cur_split = -1;
-  int64_t g0 = 0;
-  (void)g0;
 
-  // row-step `unit` -> split, row, first group of this lane
-  auto unit_split = [&](int64_t unit) { return int(unit / row_steps); };
-  auto unit_row = [&](int64_t unit, int split) { return (unit - int64_t(split) * row_steps) * RPS + row_in_step; };
-  auto lane_g0 = [&](int split) { return int64_t(split) * (LPR * GL) + int64_t(lane_in_row) * GL; };
+  // (split, row-step) of the wave's current unit, advanced without divisions
+  int split = u_begin / row_steps;
+  int rs = u_begin - split * row_steps;
+  int nsplit = split, nrs = rs;
+  auto lane_g0 = [&](int sp) { return sp * (LPR * GL) + lane_in_row * GL; };
+  auto row_off = [&](int sp, int r) {
+    const int o = r * RPS + row_in_step;
+    return (o < m_pad ? o : 0) * G + lane_g0(sp);
+  };
 
   IdxRow<GL> n0, n1w;
   Idx8Row<GL> n1b;
   if (u_begin < u_end) {
-    const int sp = unit_split(u_begin);
-    int64_t o = unit_row(u_begin, sp);
-    o = o < m_pad ? o : 0;
-    const int64_t off = o * G + lane_g0(sp);
+    const int off = row_off(split, rs);
     load_idx16<GL>(idx0 + off, n0);
     if (RESID == 16) load_idx16<GL>(idx1_16 + off, n1w);
     if (RESID == 8) load_idx8<GL>(idx1_8 + off, n1b);
   }
+  __syncthreads();
 
-  for (int64_t unit = u_begin; unit < u_end; ++unit) {
-    const int split = unit_split(unit);
-    const int64_t o = unit_row(unit, split);
+  int cur_split = -1;
+  for (int unit = u_begin; unit < u_end; ++unit) {
+    split = nsplit;
+    rs = nrs;
+    if (++nrs == row_steps) {
+      nrs = 0;
+      ++nsplit;
+    }
+    const int o = rs * RPS + row_in_step;
     const bool valid = o < m_pad;
     const IdxRow<GL> i0 = n0;
     const IdxRow<GL> i1w = n1w;
     const Idx8Row<GL> i1b = n1b;
-    if (unit + 1 < u_end) {
-      const int sp = unit_split(unit + 1);
-      int64_t on = unit_row(unit + 1, sp);
-      on = on < m_pad ? on : 0;
-      const int64_t off = on * G + lane_g0(sp);
-      load_idx16<GL>(idx0 + off, n0);
-      if (RESID == 16) load_idx16<GL>(idx1_16 + off, n1w);
-      if (RESID == 8) load_idx8<GL>(idx1_8 + off, n1b);
-    }
     if (split != cur_split) {
       cur_split = split;
-      g0 = lane_g0(split);
+      const int g0 = lane_g0(split);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int bb = b < B ? b : 0;
 #pragma unroll
         for (int q = 0; q < GL; ++q) {
-          const uint4 v = reinterpret_cast<const uint4*>(uq_dig)[int64_t(bb) * G + g0 + q];
+          const uint4 v = reinterpret_cast<const uint4*>(uq_dig)[bb * G + g0 + q];
           dig[b][q][0] = v.x; dig[b][q][1] = v.y; dig[b][q][2] = v.z; dig[b][q][3] = v.w;
-          gs[b][q] = uq_sum[int64_t(bb) * G + g0 + q];
+          gs[b][q] = -uq_sum[bb * G + g0 + q];  // negated: added on complemented reads
         }
-        sc[b] = b < B ? uq_scale[int64_t(bb) * nblk + (g0 >> bg_log2)] : 0.0f;
+        sc[b] = b < B ? uq_scale[bb * nblk + (g0 >> bg_log2)] : 0.0f;
       }
     }
 
-    int acc0[NB][4], acc1[NB][4], corr0[NB], corr1[NB];
+    if (unit + 1 < u_end) {
+      const int off = row_off(nsplit, nrs);
+      load_idx16<GL>(idx0 + off, n0);
+      if (RESID == 16) load_idx16<GL>(idx1_16 + off, n1w);
+      if (RESID == 8) load_idx8<GL>(idx1_8 + off, n1b);
+    }
+
+    int acc0[NB][4], acc1[NB][4];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      corr0[b] = corr1[b] = 0;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) acc0[b][p] = acc1[b][p] = 0;
+      for (int p = 0; p < 4; ++p) acc1[b][p] = 0;
     }
+    // phase 1: every page descriptor of the row (both stages)
+    uint32_t d0[GL], d1[GL], n0w[GL], n1w_[GL];
 #pragma unroll
     for (int q = 0; q < GL; ++q) {
-      int32_t m;
-      const uint32_t n = lookup(lds, idx16_at<GL>(i0, q), m);
+      d0[q] = (q & 1) ? page_desc<1>(lds, i0.w[q >> 1], two) : page_desc<0>(lds, i0.w[q >> 1], two);
+      if (RESID == 16)
+        d1[q] = (q & 1) ? page_desc<1>(lds, i1w.w[q >> 1], two) : page_desc<0>(lds, i1w.w[q >> 1], two);
+    }
+    // phase 2: every slot word
+#pragma unroll
+    for (int q = 0; q < GL; ++q) {
+      n0w[q] = (q & 1) ? slot_word<1>(lds, i0.w[q >> 1], d0[q]) : slot_word<0>(lds, i0.w[q >> 1], d0[q]);
+      if (RESID == 16)
+        n1w_[q] = (q & 1) ? slot_word<1>(lds, i1w.w[q >> 1], d1[q]) : slot_word<0>(lds, i1w.w[q >> 1], d1[q]);
+      if (RESID == 8) {
+        const uint32_t w1 = i1b.w[q >> 2];
+        uint32_t a1;
+        switch (q & 3) {
+          case 0: a1 = byte_x4<0>(w1, two); break;
+          case 1: a1 = byte_x4<1>(w1, two); break;
+          case 2: a1 = byte_x4<2>(w1, two); break;
+          default: a1 = byte_x4<3>(w1, two); break;
+        }
+        n1w_[q] = lds_at(lds + kResOff, a1);
+      }
+    }
+    // phase 3: dot products (complemented words on descending pages)
+#pragma unroll
+    for (int q = 0; q < GL; ++q) {
+      const int32_t m = __builtin_amdgcn_sbfe(d0[q], 7, 1);
+      const uint32_t n = n0w[q] ^ uint32_t(m);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
+        // plane 0 also carries the correction sum_j U_j of complemented reads
+        acc0[b][0] = __mul24(m, gs[b][q]) + (q == 0 ? 0 : acc0[b][0]);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) acc0[b][p] = __builtin_amdgcn_sdot8(int(n), int(dig[b][q][p]), acc0[b][p], false);
-        corr0[b] += m & gs[b][q];
+        for (int p = 0; p < 4; ++p)
+          acc0[b][p] = __builtin_amdgcn_sdot8(int(n), int(dig[b][q][p]), (q == 0 && p > 0) ? 0 : acc0[b][p], false);
       }
       if (RESID == 16) {
-        int32_t m1;
-        const uint32_t n1 = lookup(lds, idx16_at<GL>(i1w, q), m1);
+        const int32_t m1 = __builtin_amdgcn_sbfe(d1[q], 7, 1);
+        const uint32_t n1 = n1w_[q] ^ uint32_t(m1);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
+          acc1[b][0] = __mul24(m1, gs[b][q]) + (q == 0 ? 0 : acc1[b][0]);
 #pragma unroll
           for (int p = 0; p < 4; ++p)
-            acc1[b][p] = __builtin_amdgcn_sdot8(int(n1), int(dig[b][q][p]), acc1[b][p], false);
-          corr1[b] += m1 & gs[b][q];
+            acc1[b][p] = __builtin_amdgcn_sdot8(int(n1), int(dig[b][q][p]), (q == 0 && p > 0) ? 0 : acc1[b][p], false);
         }
       }
       if (RESID == 8) {
-        const uint32_t n1 = lds[kImageMaxDwords + idx8_at<GL>(i1b, q)];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
 #pragma unroll
           for (int p = 0; p < 4; ++p)
-            acc1[b][p] = __builtin_amdgcn_sdot8(int(n1), int(dig[b][q][p]), acc1[b][p], false);
+            acc1[b][p] = __builtin_amdgcn_sdot8(int(n1w_[q]), int(dig[b][q][p]), q == 0 ? 0 : acc1[b][p], false);
         }
       }
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int t0 = (((acc0[b][3] * 16 + acc0[b][2]) * 16 + acc0[b][1]) * 16 + acc0[b][0]) + corr0[b];
+      const int t0 = ((acc0[b][3] * 16 + acc0[b][2]) * 16 + acc0[b][1]) * 16 + acc0[b][0];
       float v = float(t0);
       if (RESID != 0) {
-        const int t1 = (((acc1[b][3] * 16 + acc1[b][2]) * 16 + acc1[b][1]) * 16 + acc1[b][0]) + corr1[b];
+        const int t1 = ((acc1[b][3] * 16 + acc1[b][2]) * 16 + acc1[b][1]) * 16 + acc1[b][0];
         v = fmaf(sr, float(t1), v);
       }
-      v = lane_reduce(v * sc[b], lpr_log2);
-      if (valid && lane_in_row == LPR - 1 && b < B) z_parts[(int64_t(split) * B + b) * m_pad + o] = v * out_scale;
+      v *= sc[b];
+      if (FULL) {
+        v = dpp_add(v, 0);
+        v = dpp_add(v, 1);
+        v = dpp_add(v, 2);
+        v = dpp_add(v, 3);
+        v = dpp_add(v, 4);
+        v = dpp_add(v, 5);
+      } else {
+        v = lane_reduce(v, lpr);
+      }
+      if (valid && lane_in_row == LPR - 1 && b < B) z_parts[(split * B + b) * m_pad + o] = v * out_scale;
     }
   }
 }
@@ -356,18 +467,10 @@ int device_cus() {
   return cus[dev];
 }
 
-constexpr size_t kLdsBytes = size_t(kImageMaxDwords + kResidDwords) * 4;
 
-template <int NB, int GL, int RESID>
+template <int NB, int GL, int RESID, bool FULL>
 hipError_t launch_t(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream) {
-  auto kern = gemv_lds_kernel<NB, GL, RESID>;
-  static bool attr_set = false;  // per-process attribute, set before the first launch
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsBytes));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  auto kern = gemv_lds_kernel<NB, GL, RESID, FULL>;
   const int rps = 64 >> p.lpr_log2;
   const int64_t row_steps = (L.m_pad + rps - 1) / rps;
   const int64_t units = row_steps * p.splits;
@@ -385,20 +488,27 @@ hipError_t launch_t(const glq_layer& L, const void* uq, int64_t B, float* z, con
                                             pack_image_offset(GLQ_RESID8_ENTRIES)) + kPageCount;
   int bg_log2 = 0;
   while ((int64_t(1) << bg_log2) < U.bg) ++bg_log2;
-  hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), kLdsBytes, stream, L.idx0, L.idx1,
+  hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, L.idx0, L.idx1,
                      reinterpret_cast<const uint32_t*>(p0), img0, res,
                      reinterpret_cast<const uint32_t*>(uqc + U.dig_off), reinterpret_cast<const int32_t*>(uqc + U.sum_off),
-                     reinterpret_cast<const float*>(uqc + U.scale_off), int(B), L.n_pad, L.m_pad, p.lpr_log2, bg_log2,
-                     U.nblk, upw, row_steps, p.splits, 0.5f * L.wscale, L.resid_scale, z);
+                     reinterpret_cast<const float*>(uqc + U.scale_off), int(B), int(L.n_pad / 8), int(L.m_pad),
+                     p.lpr_log2, bg_log2, int(U.nblk), int(upw), int(row_steps), p.splits, 0.5f * L.wscale,
+                     L.resid_scale, z);
   return hipGetLastError();
+}
+
+template <int NB, int GL, int RESID>
+hipError_t launch_f(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream) {
+  if (p.lpr_log2 == 6) return launch_t<NB, GL, RESID, true>(L, uq, B, z, p, stream);
+  return launch_t<NB, GL, RESID, false>(L, uq, B, z, p, stream);
 }
 
 template <int NB, int GL>
 hipError_t launch_r(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream) {
   switch (L.resid_bits) {
-    case 0: return launch_t<NB, GL, 0>(L, uq, B, z, p, stream);
-    case 8: return launch_t<NB, GL, 8>(L, uq, B, z, p, stream);
-    default: return launch_t<NB, GL, 16>(L, uq, B, z, p, stream);
+    case 0: return launch_f<NB, GL, 0>(L, uq, B, z, p, stream);
+    case 8: return launch_f<NB, GL, 8>(L, uq, B, z, p, stream);
+    default: return launch_f<NB, GL, 16>(L, uq, B, z, p, stream);
   }
 }
 

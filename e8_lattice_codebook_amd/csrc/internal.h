@@ -62,7 +62,7 @@ constexpr uint32_t kPackMagic = 0x32514C47u;  // "GLQ2"
 constexpr uint32_t kPackVersion = 2;
 constexpr int kPageSize = 256;                 // indices per page
 constexpr int kPageCount = 256;                // pages of a 16-bit index
-constexpr int kImageMaxDwords = 38912;         // LDS image budget: 152 KiB
+constexpr int kImageMaxDwords = 39680;         // LDS image budget: 155 KiB
 constexpr int kResidDwords = 256;              // 8-bit residual slots (direct)
 inline size_t pack_i8_offset() { return 256; }
 inline size_t pack_image_offset(int64_t entries) { return align256(256 + size_t(entries) * 8); }

@@ -11,12 +11,15 @@
 //   256              int8 table [entries][8], value 2c (kernels that dequantize)
 //   image_offset     LDS image: page table [256] u32, then slot words
 //
-// Page table: index i falls in page i >> 8.  desc = (R << 16) | M.  The kernels
-// compute d = i - M, m = d >> 31 (0 or -1), slot = R + (d ^ m): for a shell stored
-// by distance from its centre M (entries M + r and M - 1 - r are negatives of each
-// other) this reads the same slot for both, and m = -1 marks the negated one.
-// Non-symmetric runs and pages that straddle two runs are stored directly
-// (M at or below the page start, so m = 0 and slot = R + i - M).
+// Page table: index i falls in page p = i >> 8 at offset t = i & 255.  A page is
+// ascending (slot = base + t) or descending (slot = base + (255 - t)); its
+// descriptor is desc = ((4 * (base + 256)) << 8) | f with f = 0 or 255, so the
+// kernels read the image word at byte offset 4 * ((i ^ desc) & 255) + (desc >> 8)
+// (the slots follow the 256-dword page table).  A symmetric shell (entries M + r and
+// M - 1 - r are negatives of each other, M its centre) stores its upper half
+// once: its upper-half pages ascend, its lower-half pages descend and read the
+// negated words, flagged by f = 255.  Non-symmetric runs ascend; pages that hold
+// a run boundary or a shell centre are stored whole, ascending.
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -118,19 +121,23 @@ glq_status build_pack(const uint16_t* cb, int64_t entries, void* out_pack, size_
   for (int64_t p = 0; p < n_pages; ++p) {
     const int64_t a = p * kPageSize, b = std::min<int64_t>(entries, a + kPageSize) - 1;
     const int64_t ra = run_of(a), rb = run_of(b);
-    if (ra == rb && entries > kPageSize) page_run[size_t(p)] = ra;
+    if (ra != rb || entries <= kPageSize) continue;
+    const Run& r = runs[size_t(ra)];
+    if (r.mirrored && a < r.center && b >= r.center) continue;  // holds the centre
+    page_run[size_t(p)] = ra;
   }
   std::vector<uint32_t> slots;
   std::vector<uint32_t> desc(size_t(kPageCount), 0);
+  auto make_desc = [](int64_t base, bool descending) {
+    return (uint32_t(4 * (base + kPageCount)) << 8) | (descending ? 0xFFu : 0u);
+  };
   // exception (direct) pages first, in page order: a pack of <= 256 entries is slot = index
   for (int64_t p = 0; p < n_pages; ++p) {
     if (page_run[size_t(p)] >= 0) continue;
     const int64_t a = p * kPageSize;
     const int64_t R = int64_t(slots.size());
     for (int64_t k = 0; k < kPageSize; ++k) slots.push_back(a + k < entries ? word(a + k) : 0u);
-    // d = i - M with M = a >= 0 -> slot = R + i - a
-    if (R > 0xFFFF || a > 0xFFFF) return GLQ_ERR_CODEBOOK;
-    desc[size_t(p)] = uint32_t(R << 16) | uint32_t(a);
+    desc[size_t(p)] = make_desc(R, false);
   }
   for (int64_t p = 0; p < n_pages; ++p) {
     const int64_t ri = page_run[size_t(p)];
@@ -144,8 +151,15 @@ glq_status build_pack(const uint16_t* cb, int64_t entries, void* out_pack, size_
         for (int64_t k = 0; k < r.size; ++k) slots.push_back(word(r.start + k));
       }
     }
-    if (r.base > 0xFFFF || r.center > 0xFFFF) return GLQ_ERR_CODEBOOK;
-    desc[size_t(p)] = uint32_t(r.base << 16) | uint32_t(r.center);
+    const int64_t a = p * kPageSize;
+    if (!r.mirrored) {
+      desc[size_t(p)] = make_desc(r.base + a - r.start, false);           // slot = R + i - start
+    } else if (a >= r.center) {
+      desc[size_t(p)] = make_desc(r.base + a - r.center, false);          // slot = R + i - M
+    } else {
+      // slot = R + (M - 1 - i) = (R + M - 1 - a - 255) + (255 - t)
+      desc[size_t(p)] = make_desc(r.base + r.center - 1 - a - (kPageSize - 1), true);
+    }
   }
   const int64_t image_dwords = kPageCount + int64_t(slots.size());
   if (image_dwords > kImageMaxDwords) return GLQ_ERR_CODEBOOK;
@@ -153,9 +167,10 @@ glq_status build_pack(const uint16_t* cb, int64_t entries, void* out_pack, size_
   // self-check: every index resolves to its own codeword
   for (int64_t i = 0; i < entries; ++i) {
     const uint32_t dsc = desc[size_t(i >> 8)];
-    const int32_t d = int32_t(i) - int32_t(dsc & 0xFFFF);
-    const int32_t m = d >> 31;
-    const uint32_t slot = uint32_t(d ^ m) + (dsc >> 16);
+    const bool m = (dsc & 0x80u) != 0;
+    const uint32_t ba = ((uint32_t(i) ^ dsc) & 0xFFu) * 4 + (dsc >> 8);  // byte offset in the image
+    if (ba < 4u * kPageCount || ba % 4 != 0) return GLQ_ERR_CODEBOOK;
+    const uint32_t slot = ba / 4 - kPageCount;
     if (slot >= slots.size()) return GLQ_ERR_CODEBOOK;
     uint32_t w = slots[slot];
     if (m) {  // negate every 4-bit lane

@@ -1,11 +1,11 @@
 """The codebook pack, built on the host by the library (glq_codebook_pack).
 
 The decode kernel gathers codewords from the pack's LDS image: a 256-entry page
-table (desc = R << 16 | M) and 4-byte slots of eight signed 4-bit values 2c,
-each negation-symmetric shell stored once.  These tests resolve every index the
-way the kernel does (d = i - M, m = d >> 31, slot = R + (d ^ m), complement when
-m = -1) and compare with the oracle's codebook; they also check the integer
-identity the kernel's dot products rest on.  glq 0.5.1, "How it works", item 1;
+table and 4-byte slots of eight signed 4-bit values 2c, each negation-symmetric
+shell stored once.  These tests resolve every index the way the kernel does
+(byte address 4 * ((i ^ desc) & 255) + (desc >> 8), complemented when bit 7 of
+desc is set) and compare with the oracle's codebook; they also check the
+integer identity the kernel's dot products rest on.  glq 0.5.1, "How it works", item 1;
 "Inference kernels".
 """
 import ctypes
@@ -20,7 +20,7 @@ from oracle import e8  # noqa: E402
 
 pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="library not built")
 
-LDS_BUDGET_DWORDS = 38912
+LDS_BUDGET_DWORDS = 39680
 
 
 def build(cb_bits):
@@ -47,12 +47,14 @@ def nibbles_signed(words):
 
 
 def resolve(img, idx):
+    # the kernel's lookup: image byte offset 4 * ((i ^ desc) & 255) + (desc >> 8),
+    # complemented when bit 7 of desc is set
     idx = np.asarray(idx, dtype=np.int64)
     desc = img[idx >> 8].astype(np.int64)
-    d = idx - (desc & 0xFFFF)
-    m = np.where(d < 0, -1, 0)
-    slot = (d ^ m) + (desc >> 16)
-    words = img[256 + slot]
+    m = np.where(desc & 0x80, -1, 0)
+    ba = ((idx ^ desc) & 0xFF) * 4 + (desc >> 8)
+    assert (ba % 4 == 0).all() and (ba >= 1024).all()
+    words = img[ba // 4]
     return words, m
 
 
@@ -62,7 +64,7 @@ def test_e8_pack_resolves_every_index():
     hdr, img = image_of(pack, 65536)
     assert hdr[0] == 0x32514C47 and hdr[2] == 65536
     assert hdr[3] <= LDS_BUDGET_DWORDS            # fits the LDS budget of the decode kernel
-    assert hdr[3] * 4 < 152 * 1024
+    assert hdr[3] * 4 < 155 * 1024
     t = (2 * e8.codebook()).astype(np.int64)
     # int8 table
     assert np.array_equal(pack[256:256 + 65536 * 8].view(np.int8).reshape(-1, 8), t)
