@@ -15,7 +15,7 @@ roofline: the decode matmul kernel, timed with events around its launches
           (same stream) in a second, staged loop over the same steps.
 prefill: the 2048-token prefill of the SmolLM3-3B gate shape (2048->11008,
           3 bpw), its MFMA matmul timed the same way, in TFLOP/s.
-cpu_baseline: the fp64 oracle on one of the step's layers, on the host cores.
+cpu_baseline: the fp64 oracle on the step's layers in turn, for >= 10 s of host CPU work.
 """
 
 import argparse
@@ -172,7 +172,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_kernel (decode matmul)",
+            "kernel": "quant_u_kernel + gemv_lds_kernel (decode matmul)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -187,7 +187,7 @@ def main():
         result["prefill"] = bench_prefill(glq, synth, cb, dev, args, log)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(host_layers[0], wl, B, log)
+        result["cpu_baseline"] = cpu_baseline(host_layers, wl, B, log)
 
     print(json.dumps(result), flush=True)
 
@@ -241,8 +241,9 @@ def bench_prefill(glq, synth, cb, dev, args, log):
     }
 
 
-def cpu_baseline(layer, wl, B, log):
-    """The oracle (fp64 NumPy, dequantize-then-matmul) on one layer of the step."""
+def cpu_baseline(layers, wl, B, log, min_seconds=10.0):
+    """The oracle (fp64 NumPy, dequantize-then-matmul) on the step's layers, repeated
+    until at least min_seconds of CPU work: a bounded sample of the same workload."""
     import numpy as np
     import synth
     from oracle import glq as og
@@ -253,18 +254,23 @@ def cpu_baseline(layer, wl, B, log):
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=None)
     except Exception:  # noqa: BLE001
         pass
-    x64, _ = synth.make_x(layer.n, B, wl.act_dtype, wl.seed, 0)
-    log("bench: cpu oracle on one layer (%d x %d)" % (layer.m_pad, layer.n_pad))
+    xs = [synth.make_x(l.n, B, wl.act_dtype, wl.seed, k)[0] for k, l in enumerate(layers)]
     t0 = time.perf_counter()
-    og.linear(x64, layer.sign_in, layer.sign_out, layer.n_pad, layer.m, layer.idx0, layer.idx1, layer.resid_bits,
-              layer.wscale, layer.resid_scale)
+    nbytes, calls = 0, 0
+    while time.perf_counter() - t0 < min_seconds:
+        k = calls % len(layers)
+        l = layers[k]
+        og.linear(xs[k], l.sign_in, l.sign_out, l.n_pad, l.m, l.idx0, l.idx1, l.resid_bits, l.wscale,
+                  l.resid_scale)
+        nbytes += l.index_bytes() + B * l.n * act_bytes(wl.act_dtype) + B * l.n_pad * 4
+        calls += 1
     dt = time.perf_counter() - t0
-    nbytes = layer.index_bytes() + B * layer.n * act_bytes(wl.act_dtype) + B * layer.n_pad * 4
-    log("bench: cpu oracle %.2f s -> %.3f GB/s" % (dt, nbytes / dt / 1e9))
+    log("bench: cpu oracle %d layer calls in %.2f s -> %.3f GB/s" % (calls, dt, nbytes / dt / 1e9))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads or os.cpu_count(),
             "kind": "oracle",
-            "sample": "oracle.glq.linear (fp64 NumPy: dequantize in row blocks, BLAS matmul, FWHTs) on the gate "
-                      "layer (5120->32768, 4 bpw) at B=%d: one of the step's three layers, %.1f s" % (B, dt),
+            "sample": "oracle.glq.linear (fp64 NumPy: row-block dequantization, BLAS matmul, FWHTs) on the "
+                      "step's layers in turn at B=%d: %d layer calls (%.2f steps) in %.1f s; dequantization "
+                      "runs single-threaded, BLAS on `cores` threads" % (B, calls, calls / len(layers), dt),
             "seconds": round(dt, 3)}
 
 
