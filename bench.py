@@ -9,10 +9,11 @@ are independent calls on seeded synthetic data (no activation between them).
 R copies of the three layers' index arrays (>= 1 GiB in total) are rotated so
 every step reads its indices from HBM, not from the 256 MB Infinity Cache.
 
-value   = sum over the step's layers of (index bytes + x bytes + u bytes)
-          / step time, in GB/s (inputs resident in HBM before timing starts).
-roofline: the decode matmul kernel, timed with events around its launches
-          (same stream) in a second, staged loop over the same steps.
+value   = sum over the step's layers of (index bytes + x bytes + y bytes + sign
+          bytes) / step time, in GB/s (inputs resident in HBM before timing starts).
+roofline: at B = 1 each layer call is one kernel launch (fused_decode_kernel);
+          events around every call (same stream) in a second loop give its
+          average duration; achieved = the launches' bytes / their time.
 prefill: the 2048-token prefill of the SmolLM3-3B gate shape (2048->11008,
           3 bpw), its MFMA matmul timed the same way, in TFLOP/s.
 cpu_baseline: the fp64 oracle on the step's layers in turn, for >= 10 s of host CPU work.
@@ -80,14 +81,12 @@ def main():
         _, raw = synth.make_x(l.n, B, wl.act_dtype, wl.seed, k)
         xs.append(torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16))
     ys = [torch.empty((B, l.m), dtype=torch.bfloat16, device=dev) for l in host_layers]
-    ws = torch.empty(max(glq.linear_workspace_bytes(q, B) for q in qls[0]), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(glq.linear_workspace_bytes(q, B) for q in qls[0]), dtype=torch.uint8, device=dev)
 
-    step_bytes = 0
-    gemv_bytes = []
-    for l in host_layers:
-        gb = l.index_bytes() + B * l.n_pad * 4
-        gemv_bytes.append(gb)
-        step_bytes += l.index_bytes() + B * l.n * act_bytes(wl.act_dtype) + B * l.n_pad * 4
+    # algorithmic bytes of one layer call: indices + x + y + the two sign vectors
+    launch_bytes = [l.index_bytes() + B * (l.n + l.m) * act_bytes(wl.act_dtype) + l.n_pad + l.m_pad
+                    for l in host_layers]
+    step_bytes = sum(launch_bytes)
 
     def step(i):
         row = qls[i % copies]
@@ -111,43 +110,22 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     log("bench: %.4f ms/step (wall %.4f), %.1f GB/s" % (ms_per_step, wall * 1e3 / args.steps, value))
 
-    # staged loop: the same three kernels per layer, events around the matmul launches
-    u_bufs = [torch.empty((B, l.n_pad), dtype=torch.float32, device=dev) for l in host_layers]
-    z_bufs = [torch.empty((glq.e8_matmul_splits(q, B), B, q.m_pad), dtype=torch.float32, device=dev)
-              for q in qls[0]]
-    rout_ws = torch.empty(max(1, max(glq.lib().glq_output_rht_workspace_bytes(B, l.m_pad) for l in host_layers)),
-                          dtype=torch.uint8, device=dev)
+    # per-launch timing: at B = 1 every layer call is one fused kernel launch
+    # (fused_decode_kernel); events on the launch stream around each call
     n_ev = args.steps * len(host_layers)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
-
-    def staged(i, record):
-        row = qls[i % copies]
-        for k, q in enumerate(row):
-            glq.input_rht(xs[k], q.n_pad, q.sign_in, out=u_bufs[k])
-            if record is not None:
-                record[k][0].record()
-            glq.e8_matmul(q, u_bufs[k], out=z_bufs[k])
-            if record is not None:
-                record[k][1].record()
-            glq.output_rht(z_bufs[k], q.m, q.sign_out, out=ys[k], workspace=rout_ws)
-
-    for i in range(args.warmup):
-        staged(i, None)
-    torch.cuda.synchronize()
     for i in range(args.steps):
-        staged(args.warmup + i, evs[i * len(host_layers):(i + 1) * len(host_layers)])
+        row = qls[(args.warmup + i) % copies]
+        for k in range(len(row)):
+            a, b = evs[i * len(row) + k]
+            a.record()
+            glq.e8rht_linear(row[k], xs[k], out=ys[k], workspace=ws)
+            b.record()
     torch.cuda.synchronize()
-    per_layer_ms = [[] for _ in host_layers]
-    for i in range(args.steps):
-        for k in range(len(host_layers)):
-            a, b = evs[i * len(host_layers) + k]
-            per_layer_ms[k].append(a.elapsed_time(b))
-    gemv_ms = [float(np.mean(v)) for v in per_layer_ms]
-    # dominant kernel: the decode matmul, all its launches pooled (bytes and time)
-    gemv_total_bytes = sum(gemv_bytes)
-    gemv_total_ms = sum(gemv_ms)
-    achieved = gemv_total_bytes / len(host_layers) / (gemv_total_ms / len(host_layers) * 1e-3) / 1e9
-    log("bench: decode matmul per layer ms %s -> %.1f GB/s" % (["%.4f" % t for t in gemv_ms], achieved))
+    per_layer_ms = [float(np.mean([evs[i * len(host_layers) + k][0].elapsed_time(evs[i * len(host_layers) + k][1])
+                                   for i in range(args.steps)])) for k in range(len(host_layers))]
+    achieved = sum(launch_bytes) / (sum(per_layer_ms) * 1e-3) / 1e9
+    log("bench: per-launch ms %s -> %.1f GB/s" % (["%.4f" % t for t in per_layer_ms], achieved))
 
     result = {
         "metric": METRIC,
@@ -161,6 +139,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "arith": "activations in 16-bit fixed point per 64 columns (4 int4 digit planes), exact i32 dot "
+                 "products against the int4-packed codewords, f32 scaling, reduction and transforms",
         "data": "synthetic",
         "config": {
             "workload": "Devstral-Small-24B MLP decode (gate 5120->32768, up 5120->32768, down 32768->5120), "
@@ -172,14 +152,15 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "quant_u_kernel + gemv_lds_kernel (decode matmul)",
+            "kernel": ("fused_decode_kernel (input RHT + decode matmul + split reduction + output RHT, one "
+                       "launch per layer)") if B == 1 else "staged decode launches (RHT, quant_u, gemv_lds, RHT)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "per_layer_ms": [round(t, 5) for t in gemv_ms],
-            "bytes_per_launch": gemv_bytes,
+            "per_launch_ms": [round(t, 5) for t in per_layer_ms],
+            "bytes_per_launch": launch_bytes,
         },
     }
 
@@ -205,7 +186,7 @@ def bench_prefill(glq, synth, cb, dev, args, log):
     u = torch.empty((M, l.n_pad), dtype=torch.float16, device=dev)
     z = torch.empty((1, M, l.m_pad), dtype=torch.float32, device=dev)
     y = torch.empty((M, l.m), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(glq.linear_workspace_bytes(q, M), dtype=torch.uint8, device=dev)
+    ws = glq.linear_workspace(q, M, dev)
     flops = 2.0 * M * l.m_pad * l.n_pad
     for _ in range(3):
         glq.e8rht_linear(q, x, out=y, workspace=ws)
@@ -262,7 +243,7 @@ def cpu_baseline(layers, wl, B, log, min_seconds=10.0):
         l = layers[k]
         og.linear(xs[k], l.sign_in, l.sign_out, l.n_pad, l.m, l.idx0, l.idx1, l.resid_bits, l.wscale,
                   l.resid_scale)
-        nbytes += l.index_bytes() + B * l.n * act_bytes(wl.act_dtype) + B * l.n_pad * 4
+        nbytes += l.index_bytes() + B * (l.n + l.m) * act_bytes(wl.act_dtype) + l.n_pad + l.m_pad
         calls += 1
     dt = time.perf_counter() - t0
     log("bench: cpu oracle %d layer calls in %.2f s -> %.3f GB/s" % (calls, dt, nbytes / dt / 1e9))

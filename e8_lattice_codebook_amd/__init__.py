@@ -181,15 +181,24 @@ def linear_workspace_bytes(layer, B):
     return int(lib().glq_e8rht_linear_workspace_bytes(ctypes.byref(layer.desc), B))
 
 
+def linear_workspace(layer, B, device=None):
+    """A zeroed workspace for e8rht_linear(layer, x[B]): its first 256 bytes must
+    be zero before the first call, and every call leaves them zero."""
+    device = device if device is not None else layer.device
+    return torch.zeros(max(linear_workspace_bytes(layer, B), 1), dtype=torch.uint8, device=device)
+
+
 def e8rht_linear(layer, x, y_dtype=None, workspace=None, out=None):
-    """The E8RHTLinear forward y [B, m] from x [B, n] (glq_e8rht_linear)."""
+    """The E8RHTLinear forward y [B, m] from x [B, n] (glq_e8rht_linear).
+
+    workspace: from linear_workspace (zeroed once; reusable by later calls on the
+    same stream, whatever the layer or B, if large enough)."""
     B = x.shape[0]
     x = x.contiguous()
     y_dtype = y_dtype or x.dtype
     y = out if out is not None else torch.empty((B, layer.m), dtype=y_dtype, device=x.device)
-    ws_n = linear_workspace_bytes(layer, B)
     if workspace is None:
-        workspace = _workspace(ws_n, x.device)
+        workspace = linear_workspace(layer, B, x.device)
     _lib.check(lib().glq_e8rht_linear(ctypes.byref(layer.desc), _ptr(x), _dt(x.dtype), B, _ptr(y), _dt(y.dtype),
                                       _ptr(workspace), workspace.numel(), _stream(x.device)), "glq_e8rht_linear")
     return y

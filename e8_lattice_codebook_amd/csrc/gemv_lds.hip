@@ -31,7 +31,6 @@ namespace glq {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kUqMax = 30583;  // 7 * (16^3 + 16^2 + 16 + 1): four balanced base-16 digits
 
 // quantized u: digits [B][G][4] u32 | gsum [B][G] i32 | scale [B][nblk] f32
 struct UqLayout {
@@ -67,20 +66,9 @@ __global__ __launch_bounds__(256) void quant_u_kernel(const float* __restrict__ 
   // a block is 2^bg_log2 consecutive groups = consecutive threads
   for (int off = 1; off < (1 << bg_log2); off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
   const float inv = mx > 0.0f ? float(kUqMax) / mx : 0.0f;
-  uint32_t planes[4] = {0u, 0u, 0u, 0u};
-  int32_t s = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int U = int(rintf(v[j] * inv));
-    U = U > kUqMax ? kUqMax : (U < -kUqMax ? -kUqMax : U);
-    s += U;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int d = ((U + 8) & 15) - 8;  // balanced digit in [-8, 7]
-      planes[p] |= uint32_t(d & 15) << (4 * j);
-      U = (U - d) >> 4;
-    }
-  }
+  uint32_t planes[4];
+  int32_t s;
+  quantize_group(v, inv, planes, s);
   if (!live) return;
   reinterpret_cast<uint4*>(dig)[t] = make_uint4(planes[0], planes[1], planes[2], planes[3]);
   gsum[t] = s;
@@ -96,45 +84,7 @@ __global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
     float* __restrict__ z_parts) {
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsDwords];
   const int tid = threadIdx.x;
-  // ---- LDS: 8-bit residual slots, then the primary image (page table + slots)
-  {
-    uint32_t nd = pack0_hdr[3];
-    nd = nd > uint32_t(kImageMaxDwords) ? uint32_t(kImageMaxDwords) : nd;
-    const uint32_t nd4 = nd >> 2;
-    const uint4* src4 = reinterpret_cast<const uint4*>(img0);
-    uint4* dst4 = reinterpret_cast<uint4*>(lds + kImgOff);
-    // all loads in flight before the first LDS store (clamped, unconditional loads)
-    constexpr int kIt = (kImageMaxDwords / 4 + kThreads - 1) / kThreads;
-    const uint32_t last4 = nd4 > 0 ? nd4 - 1 : 0;
-    uint4 t0 = src4[min(uint32_t(tid), last4)];
-    uint4 t1 = src4[min(uint32_t(tid) + 1 * kThreads, last4)];
-    uint4 t2 = src4[min(uint32_t(tid) + 2 * kThreads, last4)];
-    uint4 t3 = src4[min(uint32_t(tid) + 3 * kThreads, last4)];
-    uint4 t4 = src4[min(uint32_t(tid) + 4 * kThreads, last4)];
-    uint4 t5 = src4[min(uint32_t(tid) + 5 * kThreads, last4)];
-    uint4 t6 = src4[min(uint32_t(tid) + 6 * kThreads, last4)];
-    uint4 t7 = src4[min(uint32_t(tid) + 7 * kThreads, last4)];
-    uint4 t8 = src4[min(uint32_t(tid) + 8 * kThreads, last4)];
-    uint4 t9 = src4[min(uint32_t(tid) + 9 * kThreads, last4)];
-    static_assert(kIt == 10, "image load unrolled for 10 steps");
-    uint32_t tail = 0, res = 0;
-    const uint32_t ti = (nd4 << 2) + tid;
-    if (ti < nd) tail = img0[ti];
-    if (RESID == 8 && tid < kResidDwords) res = res_slots[tid];
-    if (uint32_t(tid) + 0 * kThreads < nd4) dst4[tid + 0 * kThreads] = t0;
-    if (uint32_t(tid) + 1 * kThreads < nd4) dst4[tid + 1 * kThreads] = t1;
-    if (uint32_t(tid) + 2 * kThreads < nd4) dst4[tid + 2 * kThreads] = t2;
-    if (uint32_t(tid) + 3 * kThreads < nd4) dst4[tid + 3 * kThreads] = t3;
-    if (uint32_t(tid) + 4 * kThreads < nd4) dst4[tid + 4 * kThreads] = t4;
-    if (uint32_t(tid) + 5 * kThreads < nd4) dst4[tid + 5 * kThreads] = t5;
-    if (uint32_t(tid) + 6 * kThreads < nd4) dst4[tid + 6 * kThreads] = t6;
-    if (uint32_t(tid) + 7 * kThreads < nd4) dst4[tid + 7 * kThreads] = t7;
-    if (uint32_t(tid) + 8 * kThreads < nd4) dst4[tid + 8 * kThreads] = t8;
-    if (uint32_t(tid) + 9 * kThreads < nd4) dst4[tid + 9 * kThreads] = t9;
-    if (ti < nd) lds[kImgOff + ti] = tail;
-    if (RESID == 8 && tid < kResidDwords) lds[kResOff + tid] = res;
-  }
-  const uint32_t two = 2;
+  load_image_1024<RESID>(lds, pack0_hdr, img0, res_slots, tid);
 
   const int lane = tid & 63;
   const int lpr = FULL ? 6 : lpr_log2;
@@ -209,80 +159,11 @@ __global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
       if (RESID == 8) load_idx8<GL>(idx1_8 + off, n1b);
     }
 
-    int acc0[NB][4], acc1[NB][4];
+    float vv[NB];
+    row_dots<NB, GL, RESID>(lds, i0, i1w, i1b, dig, gs, sr, vv);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) acc1[b][p] = 0;
-    }
-    // phase 1: every page descriptor of the row (both stages)
-    uint32_t d0[GL], d1[GL], n0w[GL], n1w_[GL];
-#pragma unroll
-    for (int q = 0; q < GL; ++q) {
-      d0[q] = (q & 1) ? page_desc<1>(lds, i0.w[q >> 1], two) : page_desc<0>(lds, i0.w[q >> 1], two);
-      if (RESID == 16)
-        d1[q] = (q & 1) ? page_desc<1>(lds, i1w.w[q >> 1], two) : page_desc<0>(lds, i1w.w[q >> 1], two);
-    }
-    // phase 2: every slot word
-#pragma unroll
-    for (int q = 0; q < GL; ++q) {
-      n0w[q] = (q & 1) ? slot_word<1>(lds, i0.w[q >> 1], d0[q]) : slot_word<0>(lds, i0.w[q >> 1], d0[q]);
-      if (RESID == 16)
-        n1w_[q] = (q & 1) ? slot_word<1>(lds, i1w.w[q >> 1], d1[q]) : slot_word<0>(lds, i1w.w[q >> 1], d1[q]);
-      if (RESID == 8) {
-        const uint32_t w1 = i1b.w[q >> 2];
-        uint32_t a1;
-        switch (q & 3) {
-          case 0: a1 = byte_x4<0>(w1, two); break;
-          case 1: a1 = byte_x4<1>(w1, two); break;
-          case 2: a1 = byte_x4<2>(w1, two); break;
-          default: a1 = byte_x4<3>(w1, two); break;
-        }
-        n1w_[q] = lds_at(lds + kResOff, a1);
-      }
-    }
-    // phase 3: dot products (complemented words on descending pages)
-#pragma unroll
-    for (int q = 0; q < GL; ++q) {
-      const int32_t m = __builtin_amdgcn_sbfe(d0[q], 7, 1);
-      const uint32_t n = n0w[q] ^ uint32_t(m);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        // plane 0 also carries the correction sum_j U_j of complemented reads
-        acc0[b][0] = __mul24(m, gs[b][q]) + (q == 0 ? 0 : acc0[b][0]);
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          acc0[b][p] = __builtin_amdgcn_sdot8(int(n), int(dig[b][q][p]), (q == 0 && p > 0) ? 0 : acc0[b][p], false);
-      }
-      if (RESID == 16) {
-        const int32_t m1 = __builtin_amdgcn_sbfe(d1[q], 7, 1);
-        const uint32_t n1 = n1w_[q] ^ uint32_t(m1);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          acc1[b][0] = __mul24(m1, gs[b][q]) + (q == 0 ? 0 : acc1[b][0]);
-#pragma unroll
-          for (int p = 0; p < 4; ++p)
-            acc1[b][p] = __builtin_amdgcn_sdot8(int(n1), int(dig[b][q][p]), (q == 0 && p > 0) ? 0 : acc1[b][p], false);
-        }
-      }
-      if (RESID == 8) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-#pragma unroll
-          for (int p = 0; p < 4; ++p)
-            acc1[b][p] = __builtin_amdgcn_sdot8(int(n1w_[q]), int(dig[b][q][p]), q == 0 ? 0 : acc1[b][p], false);
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int t0 = ((acc0[b][3] * 16 + acc0[b][2]) * 16 + acc0[b][1]) * 16 + acc0[b][0];
-      float v = float(t0);
-      if (RESID != 0) {
-        const int t1 = ((acc1[b][3] * 16 + acc1[b][2]) * 16 + acc1[b][1]) * 16 + acc1[b][0];
-        v = fmaf(sr, float(t1), v);
-      }
-      v *= sc[b];
+      float v = vv[b] * sc[b];
       if (FULL) {
         v = dpp_add(v, 0);
         v = dpp_add(v, 1);

@@ -1,7 +1,8 @@
 // Device helpers shared by the decode kernels that keep the E8 codebook image
 // in LDS (the page table + 4-byte slot words of a codebook pack, built on the
 // host): index-vector loads, SDWA byte selects, the two-level lookup, DPP lane
-// reductions.
+// reductions, the image load, the per-row integer dot products and the
+// fixed-point digit planes of the activations.
 #pragma once
 
 #include "internal.h"
@@ -141,6 +142,195 @@ template <int HI>
 __device__ __forceinline__ uint32_t slot_word(const uint32_t* lds, uint32_t w, uint32_t desc) {
   const uint32_t x = xor_byte<HI ? 2 : 0>(w, desc);
   return lds_at(lds + kImgOff, (x << 2) + (desc >> 8));
+}
+
+
+// ---- activations in 16-bit fixed point ----------------------------------------------
+// Per 64 columns, U = rint(u * kUqMax / max|u|); U is written as four balanced
+// base-16 digits d_p in [-8, 7] (U = sum_p 16^p d_p), one 4-bit lane per column
+// of the 8-column group in each of four digit-plane words.
+constexpr int kUqMax = 30583;  // 7 * (16^3 + 16^2 + 16 + 1): four balanced base-16 digits
+
+__device__ __forceinline__ void quantize_group(const float (&v)[8], float inv, uint32_t (&planes)[4], int32_t& sum) {
+  planes[0] = planes[1] = planes[2] = planes[3] = 0u;
+  sum = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int U = int(rintf(v[j] * inv));
+    U = U > kUqMax ? kUqMax : (U < -kUqMax ? -kUqMax : U);
+    sum += U;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int d = ((U + 8) & 15) - 8;  // balanced digit in [-8, 7]
+      planes[p] |= uint32_t(d & 15) << (4 * j);
+      U = (U - d) >> 4;
+    }
+  }
+}
+
+// ---- the codebook image into LDS (1024 threads) ---------------------------------------
+// The primary image (its dword count is word 3 of the pack header, clamped to
+// the budget) goes to kImgOff, the 8-bit residual slots (RESID == 8) to kResOff.
+// image_issue puts every global load in flight (clamped, unconditional loads);
+// image_store<K0, K1> writes parts K0 .. K1-1 (part k: uint4 k * 1024 + tid of
+// the image, i.e. LDS dwords below kImgOff + 4 * 1024 * (k + 1)), and with
+// TAIL the last nd % 4 dwords and the residual slots.
+typedef uint32_t img_x4 __attribute__((ext_vector_type(4)));  // native vector: stays in registers
+
+struct ImageRegs {
+  img_x4 t0, t1, t2, t3, t4, t5, t6, t7, t8, t9;
+  uint32_t tail, res, nd, nd4;
+};
+
+template <int RESID>
+__device__ __forceinline__ void image_issue(ImageRegs& r, const uint32_t* __restrict__ pack0_hdr,
+                                            const uint32_t* __restrict__ img0,
+                                            const uint32_t* __restrict__ res_slots, int tid) {
+  constexpr int kT = 1024;
+  static_assert((kImageMaxDwords / 4 + kT - 1) / kT == 10, "image load unrolled for 10 parts");
+  uint32_t nd = pack0_hdr[3];
+  nd = nd > uint32_t(kImageMaxDwords) ? uint32_t(kImageMaxDwords) : nd;
+  r.nd = nd;
+  r.nd4 = nd >> 2;
+  const img_x4* src4 = reinterpret_cast<const img_x4*>(img0);
+  const uint32_t last4 = r.nd4 > 0 ? r.nd4 - 1 : 0;
+  r.t0 = src4[min(uint32_t(tid), last4)];
+  r.t1 = src4[min(uint32_t(tid) + 1 * kT, last4)];
+  r.t2 = src4[min(uint32_t(tid) + 2 * kT, last4)];
+  r.t3 = src4[min(uint32_t(tid) + 3 * kT, last4)];
+  r.t4 = src4[min(uint32_t(tid) + 4 * kT, last4)];
+  r.t5 = src4[min(uint32_t(tid) + 5 * kT, last4)];
+  r.t6 = src4[min(uint32_t(tid) + 6 * kT, last4)];
+  r.t7 = src4[min(uint32_t(tid) + 7 * kT, last4)];
+  r.t8 = src4[min(uint32_t(tid) + 8 * kT, last4)];
+  r.t9 = src4[min(uint32_t(tid) + 9 * kT, last4)];
+  r.tail = 0;
+  r.res = 0;
+  const uint32_t ti = (r.nd4 << 2) + tid;
+  if (ti < nd) r.tail = img0[ti];
+  if (RESID == 8 && tid < kResidDwords) r.res = res_slots[tid];
+}
+
+template <int K0, int K1, bool TAIL, int RESID>
+__device__ __forceinline__ void image_store(const ImageRegs& r, uint32_t* lds, int tid) {
+  constexpr int kT = 1024;
+  img_x4* dst4 = reinterpret_cast<img_x4*>(lds + kImgOff);
+  // clamped like the loads: a thread past the end writes the last uint4 with
+  // the value it loaded from there, the same value its owner writes
+  const uint32_t last4 = r.nd4 > 0 ? r.nd4 - 1 : 0;
+#define GLQ_IMAGE_PART(k, v) \
+  if (K0 <= k && k < K1) dst4[min(uint32_t(tid) + k * kT, last4)] = r.v;
+  GLQ_IMAGE_PART(0, t0)
+  GLQ_IMAGE_PART(1, t1)
+  GLQ_IMAGE_PART(2, t2)
+  GLQ_IMAGE_PART(3, t3)
+  GLQ_IMAGE_PART(4, t4)
+  GLQ_IMAGE_PART(5, t5)
+  GLQ_IMAGE_PART(6, t6)
+  GLQ_IMAGE_PART(7, t7)
+  GLQ_IMAGE_PART(8, t8)
+  GLQ_IMAGE_PART(9, t9)
+#undef GLQ_IMAGE_PART
+  if (TAIL) {
+    const uint32_t ti = (r.nd4 << 2) + tid;
+    if (ti < r.nd) lds[kImgOff + ti] = r.tail;
+    if (RESID == 8 && tid < kResidDwords) lds[kResOff + tid] = r.res;
+  }
+}
+
+template <int RESID>
+__device__ __forceinline__ void load_image_1024(uint32_t* lds, const uint32_t* __restrict__ pack0_hdr,
+                                                const uint32_t* __restrict__ img0,
+                                                const uint32_t* __restrict__ res_slots, int tid) {
+  ImageRegs r;
+  image_issue<RESID>(r, pack0_hdr, img0, res_slots, tid);
+  image_store<0, 10, true, RESID>(r, lds, tid);
+}
+
+// ---- one row-step: the lane's GL groups against NB activation rows -------------------
+// v[b] = T0 + sr * T1 with T_k = sum over the lane's columns of 2 c_k U (exact
+// integers, converted once to fp32): stage-0 codewords from the primary image,
+// stage-1 codewords from the primary image (16-bit residual) or the residual
+// slots (8-bit residual).  Reads go in three phases (every page descriptor,
+// every slot word, then the dot products) so the LDS latencies overlap.  On a
+// descending page the complemented word n ^ ~0 has lanes -2c - 1, and the
+// group's -sum_j U_j (gs) is added to plane 0 to undo the -1s.
+template <int NB, int GL, int RESID>
+__device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& i0, const IdxRow<GL>& i1w,
+                                         const Idx8Row<GL>& i1b, const uint32_t (&dig)[NB][GL][4],
+                                         const int32_t (&gs)[NB][GL], float sr, float (&v)[NB]) {
+  const uint32_t two = 2;
+  int acc0[NB][4], acc1[NB][4];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) acc1[b][p] = 0;
+  }
+  uint32_t d0[GL], d1[GL], n0w[GL], n1w_[GL];
+#pragma unroll
+  for (int q = 0; q < GL; ++q) {
+    d0[q] = (q & 1) ? page_desc<1>(lds, i0.w[q >> 1], two) : page_desc<0>(lds, i0.w[q >> 1], two);
+    if (RESID == 16)
+      d1[q] = (q & 1) ? page_desc<1>(lds, i1w.w[q >> 1], two) : page_desc<0>(lds, i1w.w[q >> 1], two);
+  }
+#pragma unroll
+  for (int q = 0; q < GL; ++q) {
+    n0w[q] = (q & 1) ? slot_word<1>(lds, i0.w[q >> 1], d0[q]) : slot_word<0>(lds, i0.w[q >> 1], d0[q]);
+    if (RESID == 16)
+      n1w_[q] = (q & 1) ? slot_word<1>(lds, i1w.w[q >> 1], d1[q]) : slot_word<0>(lds, i1w.w[q >> 1], d1[q]);
+    if (RESID == 8) {
+      const uint32_t w1 = i1b.w[q >> 2];
+      uint32_t a1;
+      switch (q & 3) {
+        case 0: a1 = byte_x4<0>(w1, two); break;
+        case 1: a1 = byte_x4<1>(w1, two); break;
+        case 2: a1 = byte_x4<2>(w1, two); break;
+        default: a1 = byte_x4<3>(w1, two); break;
+      }
+      n1w_[q] = lds_at(lds + kResOff, a1);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < GL; ++q) {
+    const int32_t m = __builtin_amdgcn_sbfe(d0[q], 7, 1);
+    const uint32_t n = n0w[q] ^ uint32_t(m);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      acc0[b][0] = __mul24(m, gs[b][q]) + (q == 0 ? 0 : acc0[b][0]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        acc0[b][p] = __builtin_amdgcn_sdot8(int(n), int(dig[b][q][p]), (q == 0 && p > 0) ? 0 : acc0[b][p], false);
+    }
+    if (RESID == 16) {
+      const int32_t m1 = __builtin_amdgcn_sbfe(d1[q], 7, 1);
+      const uint32_t n1 = n1w_[q] ^ uint32_t(m1);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        acc1[b][0] = __mul24(m1, gs[b][q]) + (q == 0 ? 0 : acc1[b][0]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          acc1[b][p] = __builtin_amdgcn_sdot8(int(n1), int(dig[b][q][p]), (q == 0 && p > 0) ? 0 : acc1[b][p], false);
+      }
+    }
+    if (RESID == 8) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          acc1[b][p] = __builtin_amdgcn_sdot8(int(n1w_[q]), int(dig[b][q][p]), q == 0 ? 0 : acc1[b][p], false);
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int t0 = ((acc0[b][3] * 16 + acc0[b][2]) * 16 + acc0[b][1]) * 16 + acc0[b][0];
+    float r = float(t0);
+    if (RESID != 0) {
+      const int t1 = ((acc1[b][3] * 16 + acc1[b][2]) * 16 + acc1[b][1]) * 16 + acc1[b][0];
+      r = fmaf(sr, float(t1), r);
+    }
+    v[b] = r;
+  }
 }
 
 }  // namespace

@@ -16,27 +16,10 @@
 // pass of length N1 <= 64 per c held in registers.
 #include <math.h>
 
-#include "internal.h"
+#include "fwht_lds.h"
 
 namespace glq {
 namespace {
-
-template <int R>
-__device__ __forceinline__ void fwht_reg(float* v) {
-#pragma unroll
-  for (int h = 1; h < R; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      if ((i & h) == 0) {
-        const float a = v[i], b = v[i + h];
-        v[i] = a + b;
-        v[i + h] = a - b;
-      }
-    }
-  }
-}
-
-__device__ __forceinline__ int swz(int i) { return i ^ ((i >> 5) & 31); }
 
 // ---- element loaders / storers ------------------------------------------------
 template <class XT>
@@ -55,16 +38,6 @@ struct LoadF32 {  // p [B][N]
   __device__ float operator()(int64_t b, int64_t i) const { return p[b * N + i]; }
 };
 
-struct LoadSplitSum {  // sum over s = 0..S-1, in order, of z[s][b][i]
-  const float* z;
-  int64_t S, B, N;
-  __device__ float operator()(int64_t b, int64_t i) const {
-    float acc = z[b * N + i];
-    for (int64_t s = 1; s < S; ++s) acc += z[(s * B + b) * N + i];
-    return acc;
-  }
-};
-
 template <class UT>
 struct StoreScaled {  // u[b][i] = RN(v * scale)
   UT* u;
@@ -77,17 +50,6 @@ struct StoreF32 {
   float* p;
   int64_t N;
   __device__ void operator()(int64_t b, int64_t i, float v) const { p[b * N + i] = v; }
-};
-
-template <class YT>
-struct StoreOut {  // y[b][i] = RN(sign[i] * v * scale) for i < m
-  YT* y;
-  int64_t m;
-  const int8_t* sign;
-  float scale;
-  __device__ void operator()(int64_t b, int64_t i, float v) const {
-    if (i < m) y[b * m + i] = from_f32<YT>(v * scale * float(sign[i]));
-  }
 };
 
 // Row r of a segmented pass is (b, a) = (r >> nseg_log2, r & (N1 - 1)); element c of
@@ -111,70 +73,10 @@ struct SegStore {
   }
 };
 
-// ---- one row per workgroup -------------------------------------------------------
-template <int R, class Load, class Store>
-__device__ __forceinline__ void first_pass(const Load& ld, const Store& st, int64_t row, int L, float* buf,
-                                           bool last) {
-  const int chunks = (1 << L) / R;
-  for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
-    float v[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) v[j] = ld(row, c * R + j);
-    fwht_reg<R>(v);
-    if (last) {
-#pragma unroll
-      for (int j = 0; j < R; ++j) st(row, c * R + j, v[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < R; ++j) buf[swz(c * R + j)] = v[j];
-    }
-  }
-}
-
-template <int LR, class Store>
-__device__ __forceinline__ void mid_pass(const Store& st, int64_t row, int L, int b0, float* buf, bool last) {
-  constexpr int R = 1 << LR;
-  const int groups = (1 << L) >> LR;
-  const int lowmask = (1 << b0) - 1;
-  for (int g = threadIdx.x; g < groups; g += blockDim.x) {
-    const int base = (g & lowmask) | ((g >> b0) << (b0 + LR));
-    float v[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) v[j] = buf[swz(base + (j << b0))];
-    fwht_reg<R>(v);
-    if (last) {
-#pragma unroll
-      for (int j = 0; j < R; ++j) st(row, base + (j << b0), v[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < R; ++j) buf[swz(base + (j << b0))] = v[j];
-    }
-  }
-}
-
 template <class Load, class Store>
 __global__ __launch_bounds__(1024) void fwht_rows_kernel(Load ld, Store st, int L) {
   extern __shared__ float buf[];
-  const int64_t row = blockIdx.x;
-  const int r0 = L < 4 ? L : 4;
-  const bool last0 = (r0 == L);
-  switch (r0) {
-    case 1: first_pass<2>(ld, st, row, L, buf, last0); break;
-    case 2: first_pass<4>(ld, st, row, L, buf, last0); break;
-    case 3: first_pass<8>(ld, st, row, L, buf, last0); break;
-    default: first_pass<16>(ld, st, row, L, buf, last0); break;
-  }
-  for (int b0 = r0; b0 < L; b0 += 4) {
-    __syncthreads();
-    const int rb = (L - b0) < 4 ? (L - b0) : 4;
-    const bool last = (b0 + rb == L);
-    switch (rb) {
-      case 1: mid_pass<1>(st, row, L, b0, buf, last); break;
-      case 2: mid_pass<2>(st, row, L, b0, buf, last); break;
-      case 3: mid_pass<3>(st, row, L, b0, buf, last); break;
-      default: mid_pass<4>(st, row, L, b0, buf, last); break;
-    }
-  }
+  fwht_row_lds(ld, st, int64_t(blockIdx.x), L, buf);
 }
 
 // ---- column pass of the two-pass transform ------------------------------------

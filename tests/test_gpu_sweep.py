@@ -67,7 +67,7 @@ def test_hip_graph_replay(gpu_codebooks, B):
     ql = glq.QuantizedLayer.from_synth(layer, gpu_codebooks)
     dev = "cuda:0"
     x = torch.randn(B, 5120, device=dev, dtype=torch.bfloat16)
-    ws = torch.empty(glq.linear_workspace_bytes(ql, B), dtype=torch.uint8, device=dev)
+    ws = glq.linear_workspace(ql, B, dev)
     y = torch.empty(B, 4000, device=dev, dtype=torch.float32)
     eager = glq.e8rht_linear(ql, x, torch.float32, workspace=ws).clone()
     s = torch.cuda.Stream()
