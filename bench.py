@@ -51,7 +51,16 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run 10 plain device-to-device copies of BYTES (scale for HBM traffic counters)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="only summarize four rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of this "
+                         "bench and of --calibrate-copy) into " + os.path.relpath(TRAFFIC_FILE, ROOT))
+    ap.add_argument("--copy-bytes", type=int, default=1 << 28, help="BYTES of the --calibrate-copy run summarized")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, args.copy_bytes)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the E8RHTLinear path here has no multi-GPU "
               "implementation (run with --gpus 1)", file=sys.stderr)
@@ -65,6 +74,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.calibrate_copy, "copies": 10}), flush=True)
+        return
     log("bench: building codebooks")
     cb = glq.Codebooks(dev)
 
@@ -158,7 +175,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(launch_bytes) if B == 1 else None,
             "per_launch_ms": [round(t, 5) for t in per_layer_ms],
             "bytes_per_launch": launch_bytes,
         },
@@ -171,6 +188,94 @@ def main():
         result["cpu_baseline"] = cpu_baseline(host_layers, wl, B, log)
 
     print(json.dumps(result), flush=True)
+
+
+# ---- HBM traffic of the fused kernel from rocprofv3 counters -------------------------
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_decode_kernel_devstral_mlp_b1_traffic.txt")
+FUSED_KERNEL_NAME = "fused_decode_kernel"
+KERNEL_SOURCES = ["fused_decode.hip", "lds_codebook.h", "fwht_lds.h", "internal.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "e8_lattice_codebook_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _pmc_rows(folder, counter):
+    """(kernel name, value) of every dispatch in a rocprofv3 --pmc csv output folder."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r.get("Kernel_Name", ""), float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit("no %s rows under %s" % (counter, folder))
+    return rows
+
+
+def pmc_summary(dirs, copy_bytes):
+    """Write TRAFFIC_FILE: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the fused kernel,
+    each scaled by bytes / counter of a plain copy of copy_bytes (reads and writes
+    copy_bytes each)."""
+    import numpy as np
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+    out = {}
+    for name, folder, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        vals = [v for k, v in _pmc_rows(folder, counter) if FUSED_KERNEL_NAME in k]
+        out[name + "_kib"] = float(np.median(vals))
+        out[name + "_dispatches"] = len(vals)
+    for name, folder, counter in (("copy_fetch", cfetch_dir, "FETCH_SIZE"), ("copy_write", cwrite_dir, "WRITE_SIZE")):
+        rows = _pmc_rows(folder, counter)
+        big = max(v for _, v in rows)
+        vals = [v for _, v in rows if v > 0.5 * big]  # the copy dispatches (not small setup kernels)
+        out[name + "_kib"] = float(np.median(vals))
+    sf = copy_bytes / (out["copy_fetch_kib"] * 1024.0)
+    sw = copy_bytes / (out["copy_write_kib"] * 1024.0)
+    traffic = out["fetch_kib"] * 1024.0 * sf + out["write_kib"] * 1024.0 * sw
+    lines = [
+        "# HBM traffic of %s, Devstral-Small-24B MLP decode (B = 1), per dispatch" % FUSED_KERNEL_NAME,
+        "# commands (from the repository root, after cd /tmp && export TMPDIR=/tmp for the profiler):",
+        "#   rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR --output-format csv -- python3 bench.py --steps 3 --warmup 1 "
+        "--no-cpu-baseline --no-prefill",
+        "#   rocprofv3 --pmc WRITE_SIZE -d WRITE_DIR --output-format csv -- (same)",
+        "#   rocprofv3 --pmc FETCH_SIZE -d COPY_FETCH_DIR --output-format csv -- python3 bench.py --calibrate-copy %d"
+        % copy_bytes,
+        "#   rocprofv3 --pmc WRITE_SIZE -d COPY_WRITE_DIR --output-format csv -- (same)",
+        "#   python3 bench.py --pmc-summary FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR --copy-bytes %d"
+        % copy_bytes,
+        "kernel_source_sha256: %s" % kernel_source_hash(),
+        "fetch_kib_median: %.1f (%d dispatches)" % (out["fetch_kib"], out["fetch_dispatches"]),
+        "write_kib_median: %.1f (%d dispatches)" % (out["write_kib"], out["write_dispatches"]),
+        "copy_bytes: %d" % copy_bytes,
+        "copy_fetch_kib: %.1f -> fetch scale %.4f" % (out["copy_fetch_kib"], sf),
+        "copy_write_kib: %.1f -> write scale %.4f" % (out["copy_write_kib"], sw),
+        "traffic_bytes_per_dispatch: %d" % int(round(traffic)),
+    ]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def measured_traffic(launch_bytes):
+    """HBM bytes per launch from TRAFFIC_FILE, or None when it is missing or was taken
+    on other kernel sources.  The file holds the median over the three layers'
+    dispatches, so it is reported against their mean algorithmic bytes."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(l.split(": ", 1) for l in fh.read().splitlines() if ": " in l and not l.startswith("#"))
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return int(kv["traffic_bytes_per_dispatch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def bench_prefill(glq, synth, cb, dev, args, log):
