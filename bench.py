@@ -11,9 +11,10 @@ every step reads its indices from HBM, not from the 256 MB Infinity Cache.
 
 value   = sum over the step's layers of (index bytes + x bytes + y bytes + sign
           bytes) / step time, in GB/s (inputs resident in HBM before timing starts).
-roofline: at B = 1 each layer call is one kernel launch (fused_decode_kernel);
-          events around every call (same stream) in a second loop give its
-          average duration; achieved = the launches' bytes / their time.
+roofline: at B = 1 each layer call is two kernel launches (fused_decode_kernel,
+          then the small output_blocks_kernel); events around every call (same
+          stream) in a second loop give their average duration; achieved = the
+          calls' bytes / their time.
 prefill: the 2048-token prefill of the SmolLM3-3B gate shape (2048->11008,
           3 bpw), its MFMA matmul timed the same way, in TFLOP/s.
 cpu_baseline: the fp64 oracle on the step's layers in turn, for >= 10 s of host CPU work.
@@ -127,8 +128,8 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     log("bench: %.4f ms/step (wall %.4f), %.1f GB/s" % (ms_per_step, wall * 1e3 / args.steps, value))
 
-    # per-launch timing: at B = 1 every layer call is one fused kernel launch
-    # (fused_decode_kernel); events on the launch stream around each call
+    # per-call timing: at B = 1 every layer call is fused_decode_kernel followed by
+    # output_blocks_kernel; events on the launch stream around each call
     n_ev = args.steps * len(host_layers)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
     for i in range(args.steps):
@@ -169,8 +170,10 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("fused_decode_kernel (input RHT + decode matmul + split reduction + output RHT, one "
-                       "launch per layer)") if B == 1 else "staged decode launches (RHT, quant_u, gemv_lds, RHT)",
+            "kernel": ("fused_decode_kernel + output_blocks_kernel (one E8RHTLinear call at B = 1: input RHT, "
+                       "decode matmul, row-block output transform; then the fixed-order split sum and the "
+                       "cross-block output transform)") if B == 1 else
+                      "staged decode launches (RHT, quant_u, gemv_lds, RHT)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -182,17 +182,16 @@ def linear_workspace_bytes(layer, B):
 
 
 def linear_workspace(layer, B, device=None):
-    """A zeroed workspace for e8rht_linear(layer, x[B]): its first 256 bytes must
-    be zero before the first call, and every call leaves them zero."""
+    """A workspace for e8rht_linear(layer, x[B]) (scratch; reusable by later calls on
+    the same stream, whatever the layer or B, if large enough)."""
     device = device if device is not None else layer.device
-    return torch.zeros(max(linear_workspace_bytes(layer, B), 1), dtype=torch.uint8, device=device)
+    return torch.empty(max(linear_workspace_bytes(layer, B), 1), dtype=torch.uint8, device=device)
 
 
 def e8rht_linear(layer, x, y_dtype=None, workspace=None, out=None):
     """The E8RHTLinear forward y [B, m] from x [B, n] (glq_e8rht_linear).
 
-    workspace: from linear_workspace (zeroed once; reusable by later calls on the
-    same stream, whatever the layer or B, if large enough)."""
+    workspace: from linear_workspace (or any device buffer of linear_workspace_bytes)."""
     B = x.shape[0]
     x = x.contiguous()
     y_dtype = y_dtype or x.dtype

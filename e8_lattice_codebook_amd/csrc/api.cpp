@@ -32,15 +32,14 @@ glq_status check_layer(const glq_layer* L, bool need_signs) {
   return GLQ_OK;
 }
 
-// Linear workspace: [0, 256) the arrival counter of the fused B = 1 kernel
-// (zero between calls), then the buffers of the fused or of the staged path.
+// Linear workspace: the buffers of the B = 1 two-launch path or of the staged path.
 struct LinearWs {
   size_t u_off, uq_off, rin_off, z_off, rout_off, total;
   int splits;
   bool prefill, lds, fused;
 };
 
-constexpr size_t kSyncBytes = 256;
+
 
 constexpr int64_t kDecodeMaxB = 16;
 
@@ -63,7 +62,7 @@ LinearWs linear_ws(const glq_layer& L, int64_t B) {
   w.prefill = B > kDecodeMaxB;
   w.lds = !w.prefill && decode_uses_lds(L);
   w.fused = fused_decode_supported(L, B);
-  size_t off = kSyncBytes;
+  size_t off = 0;
   if (w.fused) {
     w.z_off = off;
     w.total = off + align256(fused_decode_z_bytes(L));
@@ -218,9 +217,7 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
   if (!workspace || workspace_bytes < w.total) return GLQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return GLQ_ERR_ALIGN;
   const glq_layer& L = *layer;
-  if (w.fused)
-    return from_hip(launch_fused_decode(L, x, x_dt, y, y_dt, at<uint32_t>(workspace, 0), at<float>(workspace, w.z_off),
-                                        stream));
+  if (w.fused) return from_hip(launch_fused_decode(L, x, x_dt, y, y_dt, at<float>(workspace, w.z_off), stream));
   const int ln = log2_exact(L.n_pad), lm = log2_exact(L.m_pad);
   hipError_t e;
   float* z = at<float>(workspace, w.z_off);

@@ -1,6 +1,8 @@
-// The whole E8RHTLinear forward for one activation row (B = 1) in one launch on
+// The E8RHTLinear forward for one activation row (B = 1) in two launches on
 // gfx950: input RHT, decode matmul against the E8 indices with the codebook
-// resident in LDS, fixed-order reduction of the split-K partials, output RHT.
+// resident in LDS and the row-local part of the output RHT in the first; the
+// fixed-order reduction of the split-K partials and the rest of the output RHT
+// in the second.
 //
 // glq 0.5.1 (PyPI project page), "How it works", items 1-4 (sign flips + fast
 // Walsh-Hadamard transform on both sides of a weight quantized to 16-bit E8
@@ -8,25 +10,25 @@
 // kernels" (the matmul reads the indices and codewords, never W; split-K
 // partials reduced in a fixed order, not with atomics).  Glq v0.3.2 release
 // notes, "What changed": the input_rht / dequant_matmul / output_rht sequence
-// that this kernel performs in one launch.
+// that these two kernels perform.
 //
-// Workgroup (s, w) of the grid (S splits x W workgroups per split) owns the
-// columns [s K, (s + 1) K) of the transformed activation u (K = 8 * 8 * lanes
-// per row, 4096 at most) and a contiguous range of output rows:
+// fused_decode_kernel: workgroup (s, w) of the grid (S splits x W workgroups per
+// split) owns the columns [s K, (s + 1) K) of the transformed activation u
+// (K = 8 * 8 * lanes per row, 4096 at most) and the R output rows [w R, (w+1) R):
 //  1. its chunk of u, from the Kronecker split H_N = H_{N/K} (x) H_K with the
 //     index i = a K + b:  u[s K + b] = (H_K t)[b] / sqrt(N),
 //     t[b] = sum_a (-1)^popcount(s & a) sign[a K + b] x[a K + b]
 //     (a ascending; x is zero beyond n); t is summed straight from global
 //     memory, H_K runs in LDS;
-//  2. each lane quantizes its 64 columns of the chunk to 16-bit fixed-point
-//     digit planes in registers (one scale per 64 columns);
+//  2. the chunk is quantized to 16-bit fixed-point digit planes (one scale per
+//     64 columns), which every lane keeps in registers;
 //  3. the codebook image is copied into the same LDS and the rows are walked
-//     as in the staged decode matmul, the partials going to z_parts[s][o];
-//  4. every workgroup then adds 1 to an arrival counter; the one that brings it
-//     to S W sums z_parts over s = 0 .. S-1 in order, transforms the sum in LDS
-//     (H_{m_pad} / sqrt(m_pad), sign flip, truncation to m, cast) and sets the
-//     counter back to zero, so the counter is zero again when the launch ends.
-// No workgroup waits for another, so the kernel never depends on co-residency.
+//     as in the staged decode matmul, the row partials kept in LDS;
+//  4. H_R of the R row partials (the output index is i = a R + b and
+//     H_{m_pad} = H_W (x) H_R, linear in the partials) goes to z_parts[s].
+// output_blocks_kernel: for every column b, T = sum_s z_parts[s] in order, then
+// the W-point transform over the blocks a, 1/sqrt(m_pad), sign flip, truncation
+// to m and cast.
 #include <math.h>
 
 #include "fwht_lds.h"
@@ -39,6 +41,8 @@ constexpr int kThreads = 1024;
 // LDS of the chunk of u (4096 fp32 at most), at the top of the LDS array: above
 // image parts 0-7 (kImgOff + 4 * 8192 = 33024 <= kLdsDwords - kChunkDwords)
 constexpr int kChunkDwords = 4096;
+// rows of the workgroup kept in LDS for its share of the output transform
+constexpr int kRowBuf = 1024;
 // digit planes of the chunk, between image parts 0-7 and the chunk: uint4
 // [8 groups][64 lanes], negated group sums int4 [2][64 lanes], scales [64 lanes]
 constexpr int kDigOff = kImgOff + 4 * 8 * 1024;
@@ -49,26 +53,21 @@ static_assert(kScOff + 64 <= kLdsDwords - kChunkDwords, "digit region overlaps t
 struct FusedArgs {
   const void* x;
   const int8_t* sign_in;
-  const int8_t* sign_out;
   const uint16_t* idx0;
   const void* idx1;
   const uint32_t* pack0_hdr;
   const uint32_t* img0;       // primary pack's LDS image
   const uint32_t* res_slots;  // 8-bit residual slots (8-bit residual stage only)
-  float* z_parts;             // [S][m_pad]
-  uint32_t* counter;          // arrival counter: zero before and after a launch
-  void* y;                    // [m] in y_dt
-  int64_t n, m;
-  int x_dt, y_dt;
-  int ln, lk, lm;  // log2 of n_pad, of the chunk length K, of m_pad
-  int vec_in;      // x and sign_in may be read 4 elements at a time
-  int vec_out;     // sign_out may be read 32 entries at a time (16-byte aligned, m_pad >= 32)
-  int vec_y;       // y may be written 8 outputs at a time (16-byte aligned, m % 8 == 0)
+  float* z_parts;             // [S][m_pad]: H_R of each workgroup's row block
+  int64_t n;
+  int x_dt;
+  int ln, lk;  // log2 of n_pad and of the chunk length K
+  int vec_in;  // x and sign_in may be read 4 elements at a time
   int G, m_pad, lpr_log2, row_steps, wgs_per_split, rs_per_wg;
+  int lr;           // log2 R, the rows of a workgroup's block
   float sc_scale;   // 1 / (sqrt(n_pad) kUqMax): u = t_H / sqrt(n_pad), scale = max|t_H| * sc_scale
   float out_scale;  // s / 2 (codebook entries are held doubled)
   float sr;         // residual scale
-  float y_scale;    // 1 / sqrt(m_pad)
 };
 
 __device__ __forceinline__ float x_at(const void* x, int dt, int64_t j) {
@@ -80,6 +79,11 @@ __device__ __forceinline__ float x_at(const void* x, int dt, int64_t j) {
 }
 
 __device__ __forceinline__ float sign_f(uint32_t w, int k) { return float(int8_t(uint8_t(w >> (8 * k)))); }
+
+struct StoreZ {  // element i of a workgroup's row block -> its place in z_parts
+  float* p;
+  __device__ void operator()(int64_t, int64_t i, float v) const { p[i] = v; }
+};
 
 struct StoreLds {  // element i of the row -> its swizzled LDS position
   float* buf;
@@ -146,142 +150,34 @@ __device__ __forceinline__ void x_accumulate(const XRaw& r, int dt, bool neg, fl
 // bits; then every thread writes 8 consecutive outputs at a time, scaled,
 // sign-flipped (sign_out packed to one bit per output in LDS beforehand) and
 // cast, with 16-byte stores where y allows.
-template <class YT>
-__device__ __forceinline__ void store8(YT* y, const float (&v)[8]);
-template <>
-__device__ __forceinline__ void store8<float>(float* y, const float (&v)[8]) {
-  reinterpret_cast<float4*>(y)[0] = make_float4(v[0], v[1], v[2], v[3]);
-  reinterpret_cast<float4*>(y)[1] = make_float4(v[4], v[5], v[6], v[7]);
-}
-template <class YT>
-__device__ __forceinline__ void store8(YT* y, const float (&v)[8]) {
-  img_x4 w;
+// H_R on the workgroup's R = 64 E rows in rowbuf by one wave: lane l holds rows
+// l E .. l E + E - 1 (bits below log2 E in registers, the six lane bits by
+// shuffles), then stores them to p with 16-byte stores.
+template <int E>
+__device__ __forceinline__ void wave_block_transform(const float* rowbuf, float* p, int lane) {
+  float v[E];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t lo = __builtin_bit_cast(uint16_t, from_f32<YT>(v[2 * k]));
-    const uint32_t hi = __builtin_bit_cast(uint16_t, from_f32<YT>(v[2 * k + 1]));
-    w[k] = lo | (hi << 16);
-  }
-  *reinterpret_cast<img_x4*>(y) = w;
-}
-
-template <class YT, int IT>
-__device__ __forceinline__ void output_transform(const FusedArgs& a, int S, float* buf) {
-  const int M = a.m_pad;
-  const int tid = threadIdx.x;
-  const int c = tid * 4;
-  uint32_t* neg = reinterpret_cast<uint32_t*>(buf) + M;  // one bit per output, set = negative
-  float t[4 * IT];
-  if (c < M) {
-    const float* z = a.z_parts;
-    float4 acc[IT];
+  for (int e = 0; e < E; ++e) v[e] = rowbuf[swz(lane * E + e)];
+  fwht_reg<E>(v);
 #pragma unroll
-    for (int i = 0; i < IT; ++i) acc[i] = *reinterpret_cast<const float4*>(z + c + 4096 * i);
-    constexpr int UN = IT >= 8 ? 1 : 8 / IT;
-    int s = 1;
-    for (; s + UN <= S; s += UN) {
-      float4 v[UN][IT];
+  for (int k = 0; k < 6; ++k) {
+    const bool upper = (lane >> k) & 1;
 #pragma unroll
-      for (int u = 0; u < UN; ++u) {
-#pragma unroll
-        for (int i = 0; i < IT; ++i) v[u][i] = *reinterpret_cast<const float4*>(z + int64_t(s + u) * M + c + 4096 * i);
-      }
-#pragma unroll
-      for (int u = 0; u < UN; ++u) {
-#pragma unroll
-        for (int i = 0; i < IT; ++i) {
-          acc[i].x += v[u][i].x;
-          acc[i].y += v[u][i].y;
-          acc[i].z += v[u][i].z;
-          acc[i].w += v[u][i].w;
-        }
-      }
-    }
-    for (; s < S; ++s) {
-#pragma unroll
-      for (int i = 0; i < IT; ++i) {
-        const float4 v = *reinterpret_cast<const float4*>(z + int64_t(s) * M + c + 4096 * i);
-        acc[i].x += v.x;
-        acc[i].y += v.y;
-        acc[i].z += v.z;
-        acc[i].w += v.w;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      t[4 * i + 0] = acc[i].x;
-      t[4 * i + 1] = acc[i].y;
-      t[4 * i + 2] = acc[i].z;
-      t[4 * i + 3] = acc[i].w;
+    for (int e = 0; e < E; ++e) {
+      const float q = __shfl_xor(v[e], 1 << k, 64);
+      v[e] = upper ? q - v[e] : v[e] + q;
     }
   }
-  // sign_out -> bits, while the partials are in flight
-  if (a.vec_out) {
-    for (int w = tid; w < (M >> 5); w += kThreads) {
-      const img_x4 lo = reinterpret_cast<const img_x4*>(a.sign_out)[2 * w];
-      const img_x4 hi = reinterpret_cast<const img_x4*>(a.sign_out)[2 * w + 1];
-      uint32_t bits = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bits |= ((lo[k] >> (8 * e + 7)) & 1u) << (4 * k + e);
-          bits |= ((hi[k] >> (8 * e + 7)) & 1u) << (16 + 4 * k + e);
-        }
-      }
-      neg[w] = bits;
-    }
-  } else {  // unaligned signs or m_pad < 32: byte loads
-    for (int w = tid; w < ((M + 31) >> 5); w += kThreads) {
-      uint32_t bits = 0;
-      for (int i = 0; i < 32 && 32 * w + i < M; ++i) bits |= uint32_t(a.sign_out[32 * w + i] < 0) << i;
-      neg[w] = bits;
-    }
-  }
-  if (c < M) {
-    fwht_reg<4 * IT>(t);
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) buf[swz(c + 4096 * i + e)] = t[4 * i + e];
-    }
-  }
-  const int b_end = a.lm < 12 ? a.lm : 12;
-  fwht_lds_passes<StoreLds, 5>(StoreLds{buf}, 0, a.lm, 2, buf, b_end);
-  __syncthreads();
-  YT* y = static_cast<YT*>(a.y);
-  const float scale = a.y_scale;
-  if (a.vec_y) {
-    for (int o = tid * 8; o < a.m; o += kThreads * 8) {
-      const uint32_t nb = neg[o >> 5] >> (o & 31);
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(__float_as_uint(buf[swz(o + e)] * scale) ^ (((nb >> e) & 1u) << 31));
-      store8<YT>(y + o, v);
-    }
-  } else {
-    for (int o = tid; o < a.m; o += kThreads) {
-      const uint32_t bit = (neg[o >> 5] >> (o & 31)) & 1u;
-      y[o] = from_f32<YT>(__uint_as_float(__float_as_uint(buf[swz(o)] * scale) ^ (bit << 31)));
-    }
-  }
-}
-
-template <class YT>
-__device__ __forceinline__ void output_transform_any(const FusedArgs& a, int S, float* buf) {
-  switch (a.lm <= 12 ? 1 : 1 << (a.lm - 12)) {
-    case 1: output_transform<YT, 1>(a, S, buf); break;
-    case 2: output_transform<YT, 2>(a, S, buf); break;
-    case 4: output_transform<YT, 4>(a, S, buf); break;
-    default: output_transform<YT, 8>(a, S, buf); break;
-  }
+  for (int e = 0; e < E; e += 4)
+    *reinterpret_cast<float4*>(p + lane * E + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
 }
 
 template <int RESID, bool FULL>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   constexpr int GL = 8;
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsDwords];
-  __shared__ int s_last;
+  __shared__ __attribute__((aligned(16))) float rowbuf[kRowBuf];  // the workgroup's row block (swizzled)
   float* fbuf = reinterpret_cast<float*>(lds);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -432,30 +328,127 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
     } else {
       v = lane_reduce(v, lpr);
     }
-    if (valid && lane_in_row == LPR - 1) a.z_parts[int64_t(split) * a.m_pad + o] = v * a.out_scale;
+    if (valid && lane_in_row == LPR - 1) rowbuf[swz(o - wg * (a.rs_per_wg * RPS))] = v * a.out_scale;
   }
 
-  // ---- step 4: arrival; the last workgroup reduces and transforms.  Every wave
-  // waits for its partial-sum stores, then one release (thread 0's add: the L2
-  // write-back) publishes the workgroup's stores; only the last workgroup
-  // acquires (L2 invalidate), once, before its waves read the partials.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = prev + 1 == gridDim.x;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    s_last = last ? 1 : 0;
+  // ---- step 4: H_R of the workgroup's rows into z_parts[split]
+  {
+    float* zb = a.z_parts + int64_t(split) * a.m_pad + (int64_t(wg) << a.lr);
+    if (a.lr >= 8) {
+      __syncthreads();
+      if (tid < 64) {
+        switch (a.lr) {
+          case 8: wave_block_transform<4>(rowbuf, zb, tid); break;
+          case 9: wave_block_transform<8>(rowbuf, zb, tid); break;
+          default: wave_block_transform<16>(rowbuf, zb, tid); break;
+        }
+      }
+    } else {
+      fwht_lds_passes<StoreZ, 4>(StoreZ{zb}, 0, a.lr, 0, rowbuf);
+    }
   }
-  __syncthreads();
-  if (!s_last) return;
-  const int S = int(gridDim.x) / a.wgs_per_split;
-  switch (a.y_dt) {
-    case GLQ_F32: output_transform_any<float>(a, S, fbuf); break;
-    case GLQ_F16: output_transform_any<half_t>(a, S, fbuf); break;
-    default: output_transform_any<bf16_t>(a, S, fbuf); break;
+
+}
+
+// ---- the cross-block part of the output transform ------------------------------------
+// Output i = a R + b (block a < W, column b < R).  z_parts[s] holds H_R of every
+// block, so y[a R + b] = sign[i] / sqrt(m_pad) * sum_a' H_W[a][a'] T[a' R + b] with
+// T = sum over s = 0 .. S-1, in order, of z_parts[s].  One wave per CB consecutive
+// columns; lane l holds blocks a = l E + e (e < E; W = 64 E, or W < 64 with E = 1
+// and lanes >= W idle): the bits of e in registers, the lane bits by shuffles.
+struct BlocksArgs {
+  const float* z;
+  const int8_t* sign;
+  void* y;
+  int64_t m;
+  int S, m_pad, lr, lw;
+  float scale;
+};
+
+template <class YT, int E, int CB>
+__global__ __launch_bounds__(64) void output_blocks_kernel(BlocksArgs a) {
+  const int lane = threadIdx.x;
+  const int b0 = int(blockIdx.x) * CB;
+  const bool live = (lane * E) < (1 << a.lw);
+  float v[E][CB];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int64_t i0 = (int64_t(lane * E + e) << a.lr) + b0;
+#pragma unroll
+    for (int c = 0; c < CB; ++c) v[e][c] = 0.0f;
+    if (!live) continue;
+    for (int s = 0; s < a.S; ++s) {
+      const float* zs = a.z + int64_t(s) * a.m_pad + i0;
+      if (CB == 4) {
+        const float4 q = *reinterpret_cast<const float4*>(zs);
+        v[e][0] += q.x;
+        v[e][1 % CB] += q.y;
+        v[e][2 % CB] += q.z;
+        v[e][3 % CB] += q.w;
+      } else {
+#pragma unroll
+        for (int c = 0; c < CB; ++c) v[e][c] += zs[c];
+      }
+    }
   }
-  if (tid == 0) __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+  for (int c = 0; c < CB; ++c) {
+    float t[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) t[e] = v[e][c];
+    fwht_reg<E>(t);
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e][c] = t[e];
+  }
+  int le = 0;
+  while ((1 << le) < E) ++le;
+  for (int k = 0; k < a.lw - le; ++k) {
+    const bool upper = (lane >> k) & 1;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const float q = __shfl_xor(v[e][c], 1 << k, 64);
+        v[e][c] = upper ? q - v[e][c] : v[e][c] + q;
+      }
+    }
+  }
+  if (!live) return;
+  YT* y = static_cast<YT*>(a.y);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int64_t i0 = (int64_t(lane * E + e) << a.lr) + b0;
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const int64_t i = i0 + c;
+      if (i < a.m) {
+        const uint32_t neg = a.sign[i] < 0 ? 0x80000000u : 0u;
+        y[i] = from_f32<YT>(__uint_as_float(__float_as_uint(v[e][c] * a.scale) ^ neg));
+      }
+    }
+  }
+}
+
+template <class YT, int CB>
+hipError_t launch_blocks_e(const BlocksArgs& a, hipStream_t stream) {
+  const dim3 grid(unsigned((1 << a.lr) / CB)), block(64);
+  switch (a.lw <= 6 ? 1 : 1 << (a.lw - 6)) {
+    case 1: hipLaunchKernelGGL((output_blocks_kernel<YT, 1, CB>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((output_blocks_kernel<YT, 2, CB>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((output_blocks_kernel<YT, 4, CB>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((output_blocks_kernel<YT, 8, CB>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((output_blocks_kernel<YT, 16, CB>), grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <class YT>
+hipError_t launch_blocks(const BlocksArgs& a, hipStream_t stream) {
+  switch (a.lr) {
+    case 0: return launch_blocks_e<YT, 1>(a, stream);
+    case 1: return launch_blocks_e<YT, 2>(a, stream);
+    default: return launch_blocks_e<YT, 4>(a, stream);
+  }
 }
 
 int device_cus() {
@@ -471,7 +464,8 @@ int device_cus() {
 }
 
 struct FusedPlan {
-  int lpr_log2, splits, rps, row_steps, wgs_per_split, rs_per_wg;
+  int lpr_log2, splits, rps, row_steps, wgs_per_split, rs_per_wg, lr;
+  bool ok;
 };
 
 FusedPlan fused_plan(const glq_layer& L) {
@@ -491,15 +485,21 @@ FusedPlan fused_plan(const glq_layer& L) {
   if (w > wmax) w = wmax;
   p.rs_per_wg = (p.row_steps + w - 1) / w;
   p.wgs_per_split = (p.row_steps + p.rs_per_wg - 1) / p.rs_per_wg;
+  // the workgroups' row blocks must tile m_pad in power-of-two blocks that fit
+  // kRowBuf, and the blocks per split fit the cross-block kernel (W <= 1024)
+  int64_t R = int64_t(p.rs_per_wg) * p.rps;
+  if (p.wgs_per_split == 1 && R > L.m_pad) R = L.m_pad;
+  p.ok = is_pow2(R) && R <= kRowBuf && R * p.wgs_per_split == L.m_pad && p.wgs_per_split <= 1024;
+  p.lr = p.ok ? log2_exact(R) : 0;
   return p;
 }
 
 }  // namespace
 
 bool fused_decode_supported(const glq_layer& L, int64_t B) {
-  // one activation row; 64 <= n_pad (8 groups per lane); the chunk of u fits
-  // (K <= 4096 always holds); m_pad floats fit the LDS of the output transform
-  return B == 1 && L.n_pad >= 64 && L.m_pad <= 32768 && (L.resid_bits != 16 || L.cb2_pack == L.cb_pack);
+  // one activation row; 64 <= n_pad (8 groups per lane; the chunk of u, K <= 4096,
+  // always fits); the residual stage in the LDS image; row blocks as fused_plan needs
+  return B == 1 && L.n_pad >= 64 && (L.resid_bits != 16 || L.cb2_pack == L.cb_pack) && fused_plan(L).ok;
 }
 
 size_t fused_decode_z_bytes(const glq_layer& L) {
@@ -508,12 +508,11 @@ size_t fused_decode_z_bytes(const glq_layer& L) {
 }
 
 hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt, void* y, glq_dtype y_dt,
-                               uint32_t* counter, float* z_parts, hipStream_t stream) {
+                               float* z_parts, hipStream_t stream) {
   const FusedPlan p = fused_plan(L);
   FusedArgs a;
   a.x = x;
   a.sign_in = L.sign_in;
-  a.sign_out = L.sign_out;
   a.idx0 = L.idx0;
   a.idx1 = L.idx1;
   const char* p0 = static_cast<const char*>(L.cb_pack);
@@ -524,29 +523,22 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
     a.res_slots = reinterpret_cast<const uint32_t*>(static_cast<const char*>(L.cb2_pack) +
                                                     pack_image_offset(GLQ_RESID8_ENTRIES)) + kPageCount;
   a.z_parts = z_parts;
-  a.counter = counter;
-  a.y = y;
   a.n = L.n;
-  a.m = L.m;
   a.x_dt = x_dt;
-  a.y_dt = y_dt;
   a.ln = log2_exact(L.n_pad);
-  a.lm = log2_exact(L.m_pad);
   a.lk = a.ln - log2_exact(p.splits);
   const size_t xal = x_dt == GLQ_F32 ? 16 : 8;
   a.vec_in = (reinterpret_cast<uintptr_t>(x) % xal == 0) && (reinterpret_cast<uintptr_t>(L.sign_in) % 4 == 0);
-  a.vec_out = (reinterpret_cast<uintptr_t>(L.sign_out) % 16 == 0) && L.m_pad >= 32;
-  a.vec_y = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && L.m % 8 == 0;
   a.G = int(L.n_pad / 8);
   a.m_pad = int(L.m_pad);
   a.lpr_log2 = p.lpr_log2;
   a.row_steps = p.row_steps;
   a.wgs_per_split = p.wgs_per_split;
   a.rs_per_wg = p.rs_per_wg;
+  a.lr = p.lr;
   a.sc_scale = float(1.0 / (sqrt(double(L.n_pad)) * double(kUqMax)));
   a.out_scale = 0.5f * L.wscale;
   a.sr = L.resid_scale;
-  a.y_scale = float(1.0 / sqrt(double(L.m_pad)));
   const dim3 grid(unsigned(p.splits * p.wgs_per_split)), block(kThreads);
   const bool full = p.lpr_log2 == 6;
   switch (L.resid_bits) {
@@ -563,7 +555,23 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
       else hipLaunchKernelGGL((fused_decode_kernel<16, false>), grid, block, 0, stream, a);
       break;
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  BlocksArgs b;
+  b.z = z_parts;
+  b.sign = L.sign_out;
+  b.y = y;
+  b.m = L.m;
+  b.S = p.splits;
+  b.m_pad = int(L.m_pad);
+  b.lr = p.lr;
+  b.lw = log2_exact(L.m_pad) - p.lr;
+  b.scale = float(1.0 / sqrt(double(L.m_pad)));
+  switch (y_dt) {
+    case GLQ_F32: return launch_blocks<float>(b, stream);
+    case GLQ_F16: return launch_blocks<half_t>(b, stream);
+    default: return launch_blocks<bf16_t>(b, stream);
+  }
 }
 
 }  // namespace glq

@@ -95,13 +95,14 @@ int gemv_lds_splits(int64_t n_pad, int64_t B);
 hipError_t launch_quant_u(const float* u, int64_t B, int64_t n_pad, void* uq, hipStream_t stream);
 hipError_t launch_gemv_lds(const glq_layer& layer, const void* uq, int64_t B, float* z_parts, hipStream_t stream);
 
-// The whole linear for B = 1 in one launch (input RHT, decode matmul with the
-// LDS codebook, split reduction, output RHT).  counter: one zero u32 that the
-// launch leaves zero; z_parts: fused_decode_z_bytes(layer) of scratch.
+// The whole linear for B = 1 in two launches (input RHT, decode matmul with the
+// LDS codebook and the row-local part of the output RHT; then the fixed-order
+// split reduction and the rest of the output RHT).  z_parts:
+// fused_decode_z_bytes(layer) of scratch.
 bool fused_decode_supported(const glq_layer& layer, int64_t B);
 size_t fused_decode_z_bytes(const glq_layer& layer);
 hipError_t launch_fused_decode(const glq_layer& layer, const void* x, glq_dtype x_dt, void* y, glq_dtype y_dt,
-                               uint32_t* counter, float* z_parts, hipStream_t stream);
+                               float* z_parts, hipStream_t stream);
 
 // Prefill matmul: z [M][m_pad] fp32 from u16 [M][n_pad] fp16.
 hipError_t launch_gemm(const glq_layer& layer, const half_t* u16, int64_t M, float* z, hipStream_t stream);

@@ -221,18 +221,15 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
  * drop-in replacement for a linear layer, "Architecture").
  *   x          device [B][n] in x_dt (F32, F16 or BF16)
  *   y          device [B][m] in y_dt (F32, F16 or BF16)
- *   workspace  device, >= glq_e8rht_linear_workspace_bytes(layer, B), 256-byte aligned.
- *              Its first 256 bytes must be zero before the first call (they hold
- *              the arrival counter of the one-launch B = 1 path); every call that
- *              completes leaves them zero, so one zeroed workspace serves any
- *              sequence of calls, layers and B on one stream.  Calls that may
+ *   workspace  device, >= glq_e8rht_linear_workspace_bytes(layer, B), 256-byte aligned;
+ *              scratch whose contents need not be initialized.  Calls that may
  *              overlap (different streams) need separate workspaces.
- * B = 1, n_pad >= 64, m_pad <= 32768 and the residual stage (if any) in the
- * primary pack or an 8-bit one: one launch does the whole forward (every
- * workgroup forms its own column chunk of the input transform in LDS via
- * H_N = H_{N/K} (x) H_K, quantizes it, walks its rows against the LDS codebook;
- * the last workgroup to finish reduces the split partials in a fixed order and
- * runs the output transform).
+ * B = 1, n_pad >= 64 and the residual stage (if any) in the primary pack or an
+ * 8-bit one: two launches.  The first forms, in every workgroup, its column chunk
+ * of the input transform in LDS via H_N = H_{N/K} (x) H_K, quantizes it, walks its
+ * rows against the LDS codebook and applies H_R to its block of R output rows
+ * (H_{m_pad} = H_W (x) H_R); the second sums the split partials in a fixed order
+ * and applies the W-point transform across the blocks, the sign flip and the cast.
  * B <= 16 otherwise: decode path (transformed activations quantized to 16-bit fixed point
  * per 64 columns, exact integer dot products against codewords gathered from the
  * LDS-resident codebook, split-K partial sums reduced in a fixed order).

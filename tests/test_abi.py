@@ -70,11 +70,11 @@ def test_workspace_queries():
     assert lib.glq_output_rht_workspace_bytes(3, 32768) == 3 * 32768 * 4
     L = fake_layer(n=5120, n_pad=8192, m=32768, m_pad=32768, resid_bits=16)
     one = lib.glq_e8rht_linear_workspace_bytes(ctypes.byref(L), 1)
-    # one-launch path: arrival counter + 2 split partials of m_pad fp32
-    assert one >= 256 + 2 * 32768 * 4
+    # B = 1 path: 2 split partials of m_pad fp32
+    assert one >= 2 * 32768 * 4
     dec = lib.glq_e8rht_linear_workspace_bytes(ctypes.byref(L), 2)
-    # staged decode: counter + u fp32 + split partials + output-transform scratch
-    assert dec >= 256 + 2 * 8192 * 4 + 2 * 32768 * 4 + 2 * 32768 * 4
+    # staged decode: u fp32 + split partials + output-transform scratch
+    assert dec >= 2 * 8192 * 4 + 2 * 32768 * 4 + 2 * 32768 * 4
     pre = lib.glq_e8rht_linear_workspace_bytes(ctypes.byref(L), 2048)
     assert pre >= 2048 * 8192 * 2 + 2 * 2048 * 32768 * 4
 
