@@ -195,7 +195,7 @@ def main():
 
 # ---- HBM traffic of the fused kernel from rocprofv3 counters -------------------------
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_decode_kernel_devstral_mlp_b1_traffic.txt")
-FUSED_KERNEL_NAME = "fused_decode_kernel"
+FUSED_KERNEL_NAMES = ("fused_decode_kernel", "output_blocks_kernel")  # the two launches of a B = 1 call
 KERNEL_SOURCES = ["fused_decode.hip", "lds_codebook.h", "fwht_lds.h", "internal.h"]
 
 
@@ -224,16 +224,20 @@ def _pmc_rows(folder, counter):
 
 
 def pmc_summary(dirs, copy_bytes):
-    """Write TRAFFIC_FILE: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the fused kernel,
-    each scaled by bytes / counter of a plain copy of copy_bytes (reads and writes
-    copy_bytes each)."""
+    """Write TRAFFIC_FILE: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the two kernels of
+    a B = 1 call, each scaled by bytes / counter of a plain copy of copy_bytes (reads
+    and writes copy_bytes each)."""
     import numpy as np
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
     out = {}
     for name, folder, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
-        vals = [v for k, v in _pmc_rows(folder, counter) if FUSED_KERNEL_NAME in k]
-        out[name + "_kib"] = float(np.median(vals))
-        out[name + "_dispatches"] = len(vals)
+        rows = _pmc_rows(folder, counter)
+        out[name + "_kib"] = 0.0
+        out[name + "_dispatches"] = 0
+        for kname in FUSED_KERNEL_NAMES:  # per call: the sum of the two kernels' medians
+            vals = [v for k, v in rows if kname in k]
+            out[name + "_kib"] += float(np.median(vals))
+            out[name + "_dispatches"] += len(vals)
     for name, folder, counter in (("copy_fetch", cfetch_dir, "FETCH_SIZE"), ("copy_write", cwrite_dir, "WRITE_SIZE")):
         rows = _pmc_rows(folder, counter)
         big = max(v for _, v in rows)
@@ -243,7 +247,7 @@ def pmc_summary(dirs, copy_bytes):
     sw = copy_bytes / (out["copy_write_kib"] * 1024.0)
     traffic = out["fetch_kib"] * 1024.0 * sf + out["write_kib"] * 1024.0 * sw
     lines = [
-        "# HBM traffic of %s, Devstral-Small-24B MLP decode (B = 1), per dispatch" % FUSED_KERNEL_NAME,
+        "# HBM traffic of one B = 1 call (%s), Devstral-Small-24B MLP decode" % " + ".join(FUSED_KERNEL_NAMES),
         "# commands (from the repository root, after cd /tmp && export TMPDIR=/tmp for the profiler):",
         "#   rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR --output-format csv -- python3 bench.py --steps 3 --warmup 1 "
         "--no-cpu-baseline --no-prefill",
@@ -259,7 +263,7 @@ def pmc_summary(dirs, copy_bytes):
         "copy_bytes: %d" % copy_bytes,
         "copy_fetch_kib: %.1f -> fetch scale %.4f" % (out["copy_fetch_kib"], sf),
         "copy_write_kib: %.1f -> write scale %.4f" % (out["copy_write_kib"], sw),
-        "traffic_bytes_per_dispatch: %d" % int(round(traffic)),
+        "traffic_bytes_per_call: %d" % int(round(traffic)),
     ]
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
@@ -268,15 +272,15 @@ def pmc_summary(dirs, copy_bytes):
 
 
 def measured_traffic(launch_bytes):
-    """HBM bytes per launch from TRAFFIC_FILE, or None when it is missing or was taken
-    on other kernel sources.  The file holds the median over the three layers'
+    """HBM bytes per B = 1 call from TRAFFIC_FILE, or None when it is missing or was
+    taken on other kernel sources.  The file holds medians over the three layers'
     dispatches, so it is reported against their mean algorithmic bytes."""
     try:
         with open(TRAFFIC_FILE) as fh:
             kv = dict(l.split(": ", 1) for l in fh.read().splitlines() if ": " in l and not l.startswith("#"))
         if kv.get("kernel_source_sha256") != kernel_source_hash():
             return None
-        return int(kv["traffic_bytes_per_dispatch"])
+        return int(kv["traffic_bytes_per_call"])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -291,7 +295,8 @@ def bench_prefill(glq, synth, cb, dev, args, log):
     q = glq.QuantizedLayer.from_synth(l, cb)
     _, raw = synth.make_x(l.n, M, wl.act_dtype, wl.seed, 0)
     x = torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
-    u = torch.empty((M, l.n_pad), dtype=torch.float16, device=dev)
+    assert glq.e8_matmul_prefill_supported(q)
+    u = torch.empty(glq.lib().glq_prefill_u_bytes(M, l.n_pad), dtype=torch.uint8, device=dev)
     z = torch.empty((1, M, l.m_pad), dtype=torch.float32, device=dev)
     y = torch.empty((M, l.m), dtype=torch.bfloat16, device=dev)
     ws = glq.linear_workspace(q, M, dev)
@@ -308,10 +313,11 @@ def bench_prefill(glq, synth, cb, dev, args, log):
     lin_ms = e0.elapsed_time(e1) / args.prefill_steps
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.prefill_steps)]
+    # the linear's prefill steps one by one, events around the matmul (gemm_lds_kernel)
     for a, b in evs:
-        glq.input_rht(x, l.n_pad, q.sign_in, out=u)
+        glq.input_rht_prefill(x, l.n_pad, q.sign_in, out=u)
         a.record()
-        glq.e8_matmul(q, u, out=z)
+        glq.e8_matmul_prefill(q, u, M, out=z)
         b.record()
         glq.output_rht(z, l.m, q.sign_out, out=y)
     torch.cuda.synchronize()
@@ -323,7 +329,8 @@ def bench_prefill(glq, synth, cb, dev, args, log):
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "linear_ms": round(lin_ms, 5),
-        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (prefill matmul, fp16 MFMA)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_lds_kernel (prefill matmul: codewords from the LDS "
+                     "codebook dequantized into fp16 MFMA operands, fp32 accumulation)",
                      "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
                      "flops_per_launch": flops},

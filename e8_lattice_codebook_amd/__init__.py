@@ -177,6 +177,32 @@ def e8_matmul(layer, u, out=None, workspace=None):
     return z
 
 
+def e8_matmul_prefill_supported(layer):
+    return bool(lib().glq_e8_matmul_prefill_supported(ctypes.byref(layer.desc)))
+
+
+def input_rht_prefill(x, n_pad, sign_in, out=None):
+    """fp16 u = H (sign_in * [x, 0]) / sqrt(n_pad) in the prefill matmul's fragment
+    order, as a flat uint8 tensor of prefill_u_bytes (glq_input_rht_prefill)."""
+    B, n = x.shape
+    x = x.contiguous()
+    nbytes = int(lib().glq_prefill_u_bytes(B, n_pad))
+    u = out if out is not None else torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    ws_n = lib().glq_input_rht_workspace_bytes(B, n_pad, GLQ_F16)
+    ws = _workspace(ws_n, x.device) if ws_n else None
+    _lib.check(lib().glq_input_rht_prefill(_ptr(x), _dt(x.dtype), B, n, n_pad, _ptr(sign_in), _ptr(u), _ptr(ws),
+                                           ws_n, _stream(x.device)), "glq_input_rht_prefill")
+    return u
+
+
+def e8_matmul_prefill(layer, u_frag, B, out=None):
+    """z [1, B, m_pad] fp32 = u W~^T from fragment-order fp16 u (glq_e8_matmul_prefill)."""
+    z = out if out is not None else torch.empty((1, B, layer.m_pad), dtype=torch.float32, device=u_frag.device)
+    _lib.check(lib().glq_e8_matmul_prefill(ctypes.byref(layer.desc), _ptr(u_frag), B, _ptr(z),
+                                           _stream(u_frag.device)), "glq_e8_matmul_prefill")
+    return z
+
+
 def linear_workspace_bytes(layer, B):
     return int(lib().glq_e8rht_linear_workspace_bytes(ctypes.byref(layer.desc), B))
 

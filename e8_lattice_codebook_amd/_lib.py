@@ -46,6 +46,10 @@ SIGNATURES = {
     "glq_e8_matmul_splits": (c_i64, [_LP, c_i64]),
     "glq_e8_matmul_workspace_bytes": (c_sz, [_LP, c_i64]),
     "glq_e8_matmul": (ctypes.c_int, [_LP, c_vp, ctypes.c_int, c_i64, c_vp, c_vp, c_sz, c_vp]),
+    "glq_prefill_u_bytes": (c_sz, [c_i64, c_i64]),
+    "glq_e8_matmul_prefill_supported": (ctypes.c_int, [_LP]),
+    "glq_input_rht_prefill": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "glq_e8_matmul_prefill": (ctypes.c_int, [_LP, c_vp, c_i64, c_vp, c_vp]),
     "glq_e8rht_linear_workspace_bytes": (c_sz, [_LP, c_i64]),
     "glq_e8rht_linear": (ctypes.c_int, [_LP, c_vp, ctypes.c_int, c_i64, c_vp, ctypes.c_int, c_vp, c_sz, c_vp]),
 }

@@ -70,7 +70,7 @@ LinearWs linear_ws(const glq_layer& L, int64_t B) {
   }
   const int ln = log2_exact(L.n_pad), lm = log2_exact(L.m_pad);
   w.u_off = off;
-  off += align256(size_t(B) * size_t(L.n_pad) * (w.prefill ? 2 : 4));
+  off += align256(w.prefill ? tiled_u_bytes(B, L.n_pad) : size_t(B) * size_t(L.n_pad) * 4);
   w.uq_off = off;
   if (w.lds) off += align256(uq_bytes(B, L.n_pad));
   w.rin_off = off;
@@ -201,6 +201,39 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
   return from_hip(decode_matmul(*layer, static_cast<const float*>(u), B, workspace, z_parts, stream));
 }
 
+size_t glq_prefill_u_bytes(int64_t B, int64_t n_pad) {
+  if (B < 1 || !valid_pad(n_pad)) return 0;
+  return tiled_u_bytes(B, n_pad);
+}
+
+int glq_e8_matmul_prefill_supported(const glq_layer* layer) {
+  if (!layer || check_layer(layer, false) != GLQ_OK) return 0;
+  return gemm_lds_supported(*layer) ? 1 : 0;
+}
+
+glq_status glq_input_rht_prefill(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t n_pad,
+                                 const int8_t* sign_in, void* u16, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (!x || !sign_in || !u16) return GLQ_ERR_NULL;
+  if (B < 1 || !valid_pad(n_pad) || n_pad < 256 || n < 1 || n > n_pad || B > int64_t(1) << 31) return GLQ_ERR_SHAPE;
+  if (!valid_dtype(x_dt)) return GLQ_ERR_DTYPE;
+  if (!aligned(u16, 16)) return GLQ_ERR_ALIGN;
+  const size_t need = glq_input_rht_workspace_bytes(B, n_pad, GLQ_F16);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GLQ_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 256)) return GLQ_ERR_ALIGN;
+  return from_hip(launch_rht_in_tiled(x, x_dt, B, n, log2_exact(n_pad), sign_in, static_cast<half_t*>(u16),
+                                      static_cast<float*>(workspace), stream));
+}
+
+glq_status glq_e8_matmul_prefill(const glq_layer* layer, const void* u16, int64_t B, float* z, hipStream_t stream) {
+  glq_status st = check_layer(layer, false);
+  if (st != GLQ_OK) return st;
+  if (!u16 || !z) return GLQ_ERR_NULL;
+  if (B < 1 || B > int64_t(1) << 31 || !gemm_lds_supported(*layer)) return GLQ_ERR_SHAPE;
+  if (!aligned(u16, 16)) return GLQ_ERR_ALIGN;
+  return from_hip(launch_gemm_lds(*layer, static_cast<const half_t*>(u16), B, true, z, stream));
+}
+
 size_t glq_e8rht_linear_workspace_bytes(const glq_layer* layer, int64_t B) {
   if (!layer || B < 1 || !valid_pad(layer->n_pad) || !valid_pad(layer->m_pad)) return 0;
   return linear_ws(*layer, B).total;
@@ -229,9 +262,15 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
     if (e != hipSuccess) return GLQ_ERR_HIP;
   } else {
     half_t* u = at<half_t>(workspace, w.u_off);
-    e = launch_rht_in(x, x_dt, B, L.n, ln, L.sign_in, u, GLQ_F16, at<float>(workspace, w.rin_off), stream);
-    if (e != hipSuccess) return GLQ_ERR_HIP;
-    e = launch_gemm(L, u, B, z, stream);
+    if (gemm_lds_supported(L)) {  // u in the matmul's fragment order
+      e = launch_rht_in_tiled(x, x_dt, B, L.n, ln, L.sign_in, u, at<float>(workspace, w.rin_off), stream);
+      if (e != hipSuccess) return GLQ_ERR_HIP;
+      e = launch_gemm_lds(L, u, B, true, z, stream);
+    } else {
+      e = launch_rht_in(x, x_dt, B, L.n, ln, L.sign_in, u, GLQ_F16, at<float>(workspace, w.rin_off), stream);
+      if (e != hipSuccess) return GLQ_ERR_HIP;
+      e = launch_gemm(L, u, B, z, stream);
+    }
     if (e != hipSuccess) return GLQ_ERR_HIP;
   }
   e = launch_rht_out(z, w.splits, B, L.m, lm, L.sign_out, y, y_dt, at<float>(workspace, w.rout_off), stream);

@@ -303,18 +303,10 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   }
   __syncthreads();
 
-  for (int r = r_begin; r < r_end; ++r) {
+  // one row-step: the lane's groups of row r against the digit planes, the
+  // fixed-order lane reduction, the row partial into rowbuf
+  auto row_step = [&](const IdxRow<GL>& i0, const IdxRow<GL>& i1w, const Idx8Row<GL>& i1b, int r) {
     const int o = r * RPS + row_in_step;
-    const bool valid = o < a.m_pad;
-    const IdxRow<GL> i0 = n0;
-    const IdxRow<GL> i1w = n1w;
-    const Idx8Row<GL> i1b = n1b;
-    if (r + 1 < r_end) {
-      const int off = row_off(r + 1);
-      load_idx16<GL>(a.idx0 + off, n0);
-      if (RESID == 16) load_idx16<GL>(idx1_16 + off, n1w);
-      if (RESID == 8) load_idx8<GL>(idx1_8 + off, n1b);
-    }
     float vv[1];
     row_dots<1, GL, RESID>(lds, i0, i1w, i1b, dig, gs, a.sr, vv);
     float v = vv[0] * sc[0];
@@ -328,7 +320,24 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
     } else {
       v = lane_reduce(v, lpr);
     }
-    if (valid && lane_in_row == LPR - 1) rowbuf[swz(o - wg * (a.rs_per_wg * RPS))] = v * a.out_scale;
+    if (o < a.m_pad && lane_in_row == LPR - 1) rowbuf[swz(o - wg * (a.rs_per_wg * RPS))] = v * a.out_scale;
+  };
+  auto load_row = [&](int r, IdxRow<GL>& i0, IdxRow<GL>& i1w, Idx8Row<GL>& i1b) {
+    const int off = row_off(r < r_end ? r : r_end - 1);  // past the end: reload the last row
+    load_idx16<GL>(a.idx0 + off, i0);
+    if (RESID == 16) load_idx16<GL>(idx1_16 + off, i1w);
+    if (RESID == 8) load_idx8<GL>(idx1_8 + off, i1b);
+  };
+  // two row-steps per iteration on two register sets, each loaded one step ahead
+  IdxRow<GL> m0, m1w;
+  Idx8Row<GL> m1b;
+  for (int r = r_begin; r < r_end; r += 2) {
+    load_row(r + 1, m0, m1w, m1b);
+    row_step(n0, n1w, n1b, r);
+    if (r + 1 < r_end) {
+      load_row(r + 2, n0, n1w, n1b);
+      row_step(m0, m1w, m1b, r + 1);
+    }
   }
 
   // ---- step 4: H_R of the workgroup's rows into z_parts[split]

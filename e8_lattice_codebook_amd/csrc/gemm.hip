@@ -132,6 +132,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const half_t* __restrict__ A,
 }  // namespace
 
 hipError_t launch_gemm(const glq_layer& L, const half_t* u16, int64_t M, float* z, hipStream_t stream) {
+  if (gemm_lds_supported(L)) return launch_gemm_lds(L, u16, M, false, z, stream);
   const dim3 grid(unsigned((L.m_pad + BN - 1) / BN), unsigned((M + BM - 1) / BM)), block(256);
   const int8_t* cb0 = static_cast<const int8_t*>(L.cb_pack) + pack_i8_offset();
   const int8_t* cb1 = L.cb2_pack ? static_cast<const int8_t*>(L.cb2_pack) + pack_i8_offset() : nullptr;

@@ -59,11 +59,15 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
 // ---- codebook pack layout ----------------------------------------------------
 // header (256 B) | int8 table [entries][8] = 2c | LDS image (page table + slots)
 constexpr uint32_t kPackMagic = 0x32514C47u;  // "GLQ2"
-constexpr uint32_t kPackVersion = 2;
+constexpr uint32_t kPackVersion = 3;
 constexpr int kPageSize = 256;                 // indices per page
 constexpr int kPageCount = 256;                // pages of a 16-bit index
 constexpr int kImageMaxDwords = 39680;         // LDS image budget: 155 KiB
 constexpr int kResidDwords = 256;              // 8-bit residual slots (direct)
+// A slot word holds the 8 coordinates 2c as signed 4-bit lanes; coordinate e sits
+// in nibble lane_nibble(e), so that nibbles j and j + 4 (16 bits apart) hold the
+// adjacent coordinates 2j and 2j + 1.
+__host__ __device__ constexpr int lane_nibble(int e) { return (e >> 1) + 4 * (e & 1); }
 inline size_t pack_i8_offset() { return 256; }
 inline size_t pack_image_offset(int64_t entries) { return align256(256 + size_t(entries) * 8); }
 size_t pack_total_bytes(int64_t entries);
@@ -104,7 +108,17 @@ size_t fused_decode_z_bytes(const glq_layer& layer);
 hipError_t launch_fused_decode(const glq_layer& layer, const void* x, glq_dtype x_dt, void* y, glq_dtype y_dt,
                                float* z_parts, hipStream_t stream);
 
-// Prefill matmul: z [M][m_pad] fp32 from u16 [M][n_pad] fp16.
+// Prefill matmul: z [M][m_pad] fp32 from u16 [M][n_pad] fp16.  launch_gemm takes the
+// LDS-codebook kernel (launch_gemm_lds) when gemm_lds_supported(layer), else the
+// kernel that gathers codewords from the pack's int8 tables.
+// tiled: u16 in fragment order [ceil(M/16)][n_pad/32][4][16][8] (tiled_u_bytes), as
+// launch_rht_in_tiled writes it; otherwise [M][n_pad].
+bool gemm_lds_supported(const glq_layer& layer);
+size_t tiled_u_bytes(int64_t M, int64_t n_pad);
+hipError_t launch_gemm_lds(const glq_layer& layer, const half_t* u16, int64_t M, bool tiled, float* z,
+                           hipStream_t stream);
+hipError_t launch_rht_in_tiled(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int L, const int8_t* sign,
+                               half_t* u16, float* ws, hipStream_t stream);
 hipError_t launch_gemm(const glq_layer& layer, const half_t* u16, int64_t M, float* z, hipStream_t stream);
 
 }  // namespace glq

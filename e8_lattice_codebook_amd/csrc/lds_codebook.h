@@ -162,7 +162,7 @@ __device__ __forceinline__ void quantize_group(const float (&v)[8], float inv, u
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int d = ((U + 8) & 15) - 8;  // balanced digit in [-8, 7]
-      planes[p] |= uint32_t(d & 15) << (4 * j);
+      planes[p] |= uint32_t(d & 15) << (4 * lane_nibble(j));
       U = (U - d) >> 4;
     }
   }

@@ -75,7 +75,7 @@ glq_status build_pack(const uint16_t* cb, int64_t entries, void* out_pack, size_
   }
   auto word = [&](int64_t i) {
     uint32_t w = 0;
-    for (int j = 0; j < 8; ++j) w |= uint32_t(t[size_t(i * 8 + j)] & 15) << (4 * j);
+    for (int j = 0; j < 8; ++j) w |= uint32_t(t[size_t(i * 8 + j)] & 15) << (4 * lane_nibble(j));
     return w;
   };
   auto norm2 = [&](int64_t i) {

@@ -46,6 +46,21 @@ struct StoreScaled {  // u[b][i] = RN(v * scale)
   __device__ void operator()(int64_t b, int64_t i, float v) const { u[b * N + i] = from_f32<UT>(v * scale); }
 };
 
+// u16 in the prefill matmul's fragment order: token b, column i of group g = i / 8
+// (k-step ks = g mod KS, lane quarter q = g / KS, KS = N / 32) at
+// (((b / 16) KS + ks) 4 + q) 128 + (b mod 16) 8 + i mod 8
+struct StoreTiledHalf {
+  half_t* u;
+  int ks_log2;
+  float scale;
+  __device__ void operator()(int64_t b, int64_t i, float v) const {
+    const int64_t g = i >> 3;
+    const int64_t ks = g & ((int64_t(1) << ks_log2) - 1), q = g >> ks_log2;
+    const int64_t off = (((((b >> 4) << ks_log2) + ks) * 4 + q) * 16 + (b & 15)) * 8 + (i & 7);
+    u[off] = from_f32<half_t>(v * scale);
+  }
+};
+
 struct StoreF32 {
   float* p;
   int64_t N;
@@ -150,6 +165,23 @@ hipError_t rht_in_x(const void* x, int64_t B, int64_t n, int L, const int8_t* si
   return hipErrorInvalidValue;
 }
 
+// input transform into the prefill matmul's fragment order (fp16)
+template <class XT>
+hipError_t rht_in_tiled_x(const void* x, int64_t B, int64_t n, int L, const int8_t* sign, half_t* u16, float* ws,
+                          hipStream_t stream) {
+  const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
+  const LoadSignedX<XT> ld{static_cast<const XT*>(x), n, sign};
+  const int64_t N = int64_t(1) << L;
+  const StoreTiledHalf st{u16, L - 5, scale};
+  if (L <= kSingleLog2) return run_rows(ld, st, B, L, stream);
+  int lr, lc;
+  fwht_split(L, &lr, &lc);
+  hipError_t e = run_rows(SegLoad<LoadSignedX<XT>>{ld, lr, lc}, SegStore<StoreF32>{StoreF32{ws, N}, lr, lc}, B << lc,
+                          lr, stream);
+  if (e != hipSuccess) return e;
+  return run_cols(LoadF32{ws, N}, st, B, lr, lc, stream);
+}
+
 template <class YT>
 hipError_t rht_out_typed(const float* z, int64_t S, int64_t B, int64_t m, int L, const int8_t* sign, void* y,
                          float* ws, hipStream_t stream) {
@@ -174,6 +206,16 @@ hipError_t launch_rht_in(const void* x, glq_dtype x_dt, int64_t B, int64_t n, in
     case GLQ_F32: return rht_in_x<float>(x, B, n, L, sign, u, u_dt, ws, stream);
     case GLQ_F16: return rht_in_x<half_t>(x, B, n, L, sign, u, u_dt, ws, stream);
     case GLQ_BF16: return rht_in_x<bf16_t>(x, B, n, L, sign, u, u_dt, ws, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_rht_in_tiled(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int L, const int8_t* sign,
+                               half_t* u16, float* ws, hipStream_t stream) {
+  switch (x_dt) {
+    case GLQ_F32: return rht_in_tiled_x<float>(x, B, n, L, sign, u16, ws, stream);
+    case GLQ_F16: return rht_in_tiled_x<half_t>(x, B, n, L, sign, u16, ws, stream);
+    case GLQ_BF16: return rht_in_tiled_x<bf16_t>(x, B, n, L, sign, u16, ws, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -216,6 +216,39 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The prefill (B > 16) steps of glq_e8rht_linear on their own, with u in the
+ * matmul's fragment order ("Inference kernels": the tensor-core path for B >= 2;
+ * "How it works", item 2 for the transform).  Fragment order, for n_pad = 32 KS:
+ * element (b, i) of u, with group g = i / 8, k-step ks = g mod KS and quarter
+ * q = g / KS, sits at half index (((b / 16) KS + ks) 4 + q) 128 + (b mod 16) 8 + i mod 8;
+ * a buffer holds ceil(B / 16) * 16 rows (rows past B are never read into y).
+ *
+ * glq_prefill_u_bytes — bytes of fragment-order u for B rows (0 for an invalid n_pad).
+ * glq_e8_matmul_prefill_supported — 1 if glq_e8_matmul_prefill takes the layer:
+ *   n_pad >= 256, m_pad a multiple of 256, residual stage 0, 8 bits or 16 bits in
+ *   the primary pack.
+ * glq_input_rht_prefill — u = H (sign_in * [x, 0]) / sqrt(n_pad) rounded to fp16,
+ *   written in fragment order.
+ *   x          device [B][n] in x_dt (F32, F16 or BF16)
+ *   u16        device, >= glq_prefill_u_bytes(B, n_pad), 16-byte aligned
+ *   workspace  device fp32 [B][n_pad] when n_pad > 16384 (else may be NULL),
+ *              glq_input_rht_workspace_bytes(B, n_pad, GLQ_F16) bytes, 256-byte aligned
+ * glq_e8_matmul_prefill — z [B][m_pad] fp32 = u W~^T from fragment-order u16
+ *   (codewords dequantized from the LDS-resident codebook into fp16 MFMA
+ *   operands, fp32 accumulation, one split: glq_output_rht takes z with S = 1).
+ * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE (B < 1, or a layer the prefill matmul does
+ * not take), GLQ_ERR_DTYPE, GLQ_ERR_RECIPE, GLQ_ERR_ALIGN, GLQ_ERR_WORKSPACE,
+ * GLQ_ERR_HIP.
+ */
+size_t glq_prefill_u_bytes(int64_t B, int64_t n_pad);
+int glq_e8_matmul_prefill_supported(const glq_layer* layer);
+glq_status glq_input_rht_prefill(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t n_pad,
+                                 const int8_t* sign_in, void* u16, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+glq_status glq_e8_matmul_prefill(const glq_layer* layer, const void* u16, int64_t B, float* z,
+                                 hipStream_t stream);
+
+/*
  * glq_e8rht_linear — the E8RHTLinear forward, y = RHT_out(RHT_in(x) W~^T)
  * (glq 0.5.1, "How it works" and "Inference kernels"; E8RHTLinear is the page's
  * drop-in replacement for a linear layer, "Architecture").

@@ -40,9 +40,14 @@ def image_of(pack, entries):
     return hdr, img
 
 
+# coordinate e of a slot word sits in nibble (e >> 1) + 4 (e & 1): nibbles j and j + 4
+# hold the adjacent coordinates 2j and 2j + 1
+LANE_NIBBLE = np.array([(e >> 1) + 4 * (e & 1) for e in range(8)], dtype=np.uint32)
+
+
 def nibbles_signed(words):
     w = np.asarray(words, dtype=np.uint32)[:, None]
-    v = ((w >> (4 * np.arange(8, dtype=np.uint32))) & 15).astype(np.int64)
+    v = ((w >> (4 * LANE_NIBBLE)) & 15).astype(np.int64)
     return np.where(v >= 8, v - 16, v)
 
 
