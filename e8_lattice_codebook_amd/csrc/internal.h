@@ -21,6 +21,7 @@ inline int log2_exact(int64_t v) {
   return l;
 }
 inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+__host__ __device__ constexpr int log2_exact_dev(int v) { return v <= 1 ? 0 : 1 + log2_exact_dev(v >> 1); }
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Two-pass split of a length-2^L transform: (row pass log2, column pass log2).

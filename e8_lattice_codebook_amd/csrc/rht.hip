@@ -182,11 +182,149 @@ hipError_t rht_in_tiled_x(const void* x, int64_t B, int64_t n, int L, const int8
   return run_cols(LoadF32{ws, N}, st, B, lr, lc, stream);
 }
 
+// ---- output transform of one row per workgroup, 4096 <= N <= 32768 ---------------------
+// Thread t holds the float4s at 4 t + 4096 i (i < IT = N / 4096) of the row's split
+// sum (s = 0 .. S-1 in order, all loads of a split in flight), so bits 0-1 and the
+// bits of i (12 and up) are transformed in registers and bits 2-11 in two LDS passes
+// of 5 bits; then each thread writes 8 consecutive outputs at a time (16-byte stores
+// where y allows), sign-flipped, scaled and cast.
+template <class YT>
+__device__ __forceinline__ void store8(YT* y, const float (&v)[8]);
+template <>
+__device__ __forceinline__ void store8<float>(float* y, const float (&v)[8]) {
+  reinterpret_cast<float4*>(y)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(y)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <class YT>
+__device__ __forceinline__ void store8(YT* y, const float (&v)[8]) {
+  uint4 w;
+  uint32_t h[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) h[k] = __builtin_bit_cast(uint16_t, from_f32<YT>(v[k]));
+  w.x = h[0] | (h[1] << 16);
+  w.y = h[2] | (h[3] << 16);
+  w.z = h[4] | (h[5] << 16);
+  w.w = h[6] | (h[7] << 16);
+  *reinterpret_cast<uint4*>(y) = w;
+}
+
+struct StoreLdsRow {  // element i of the row -> its swizzled LDS position
+  float* buf;
+  __device__ void operator()(int64_t, int64_t i, float v) const { buf[swz(int(i))] = v; }
+};
+
+template <class YT, int IT>
+__global__ __launch_bounds__(1024) void rows_out_kernel(const float* __restrict__ z, int S, int B, int64_t m,
+                                                       const int8_t* __restrict__ sign, YT* __restrict__ y,
+                                                       float scale, int vec_y) {
+  extern __shared__ float buf[];
+  constexpr int N = 4096 * IT;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int c = tid * 4;
+  float4 acc[IT];
+  const float* zr = z + int64_t(row) * N;
+#pragma unroll
+  for (int i = 0; i < IT; ++i) acc[i] = *reinterpret_cast<const float4*>(zr + c + 4096 * i);
+  constexpr int UN = IT >= 8 ? 1 : 8 / IT;
+  int s = 1;
+  for (; s + UN <= S; s += UN) {
+    float4 v[UN][IT];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+#pragma unroll
+      for (int i = 0; i < IT; ++i)
+        v[u][i] = *reinterpret_cast<const float4*>(zr + (int64_t(s + u) * B) * N + c + 4096 * i);
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        acc[i].x += v[u][i].x;
+        acc[i].y += v[u][i].y;
+        acc[i].z += v[u][i].z;
+        acc[i].w += v[u][i].w;
+      }
+    }
+  }
+  for (; s < S; ++s) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(zr + (int64_t(s) * B) * N + c + 4096 * i);
+      acc[i].x += v.x;
+      acc[i].y += v.y;
+      acc[i].z += v.z;
+      acc[i].w += v.w;
+    }
+  }
+  float t[4 * IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    t[4 * i + 0] = acc[i].x;
+    t[4 * i + 1] = acc[i].y;
+    t[4 * i + 2] = acc[i].z;
+    t[4 * i + 3] = acc[i].w;
+  }
+  fwht_reg<4 * IT>(t);  // bits 0-1 and 12 + log2 i
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) buf[swz(c + 4096 * i + e)] = t[4 * i + e];
+  }
+  fwht_lds_passes<StoreLdsRow, 5>(StoreLdsRow{buf}, 0, 12 + log2_exact_dev(IT), 2, buf, 12);
+  __syncthreads();
+  YT* yr = y + int64_t(row) * m;
+  if (vec_y) {
+    for (int o = tid * 8; o < m; o += 1024 * 8) {
+      const uint2 sg = *reinterpret_cast<const uint2*>(sign + o);
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t neg = ((e < 4 ? sg.x : sg.y) >> (8 * (e & 3) + 7)) & 1u;
+        v[e] = __uint_as_float(__float_as_uint(buf[swz(o + e)] * scale) ^ (neg << 31));
+      }
+      store8<YT>(yr + o, v);
+    }
+  } else {
+    for (int o = tid; o < m; o += 1024) {
+      const uint32_t neg = sign[o] < 0 ? 0x80000000u : 0u;
+      yr[o] = from_f32<YT>(__uint_as_float(__float_as_uint(buf[swz(o)] * scale) ^ neg));
+    }
+  }
+}
+
 template <class YT>
 hipError_t rht_out_typed(const float* z, int64_t S, int64_t B, int64_t m, int L, const int8_t* sign, void* y,
                          float* ws, hipStream_t stream) {
   const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
   const int64_t N = int64_t(1) << L;
+  if (L >= 12 && L <= 15) {
+    // 16-byte output stores need y 16-byte aligned, m % 8 == 0 and 8-byte aligned signs
+    const int vec_y = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && m % 8 == 0 &&
+                      (reinterpret_cast<uintptr_t>(sign) % 8 == 0);
+    const size_t shmem = size_t(4) << L;
+    const dim3 grid{unsigned(B)}, block{1024};
+    YT* yp = static_cast<YT*>(y);
+    switch (L) {
+      case 12: hipLaunchKernelGGL((rows_out_kernel<YT, 1>), grid, block, shmem, stream, z, int(S), int(B), m, sign, yp, scale, vec_y); break;
+      case 13: hipLaunchKernelGGL((rows_out_kernel<YT, 2>), grid, block, shmem, stream, z, int(S), int(B), m, sign, yp, scale, vec_y); break;
+      case 14: hipLaunchKernelGGL((rows_out_kernel<YT, 4>), grid, block, shmem, stream, z, int(S), int(B), m, sign, yp, scale, vec_y); break;
+      default: {
+        // 128 KiB of dynamic LDS: raise the kernel's limit once
+        static bool lds_set = false;
+        if (!lds_set) {
+          hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_out_kernel<YT, 8>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
+          if (e != hipSuccess) return e;
+          lds_set = true;
+        }
+        hipLaunchKernelGGL((rows_out_kernel<YT, 8>), grid, block, shmem, stream, z, int(S), int(B), m, sign, yp, scale,
+                           vec_y);
+        break;
+      }
+    }
+    return hipGetLastError();
+  }
   const LoadSplitSum ld{z, S, B, N};
   const StoreOut<YT> st{static_cast<YT*>(y), m, sign, scale};
   if (L <= kSingleLog2) return run_rows(ld, st, B, L, stream);
