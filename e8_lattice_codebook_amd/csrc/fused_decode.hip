@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   const uint16_t* idx1_16 = static_cast<const uint16_t*>(a.idx1);
 
   // the wave's row-steps
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r_wg0 = wg * a.rs_per_wg;
   const int r_wg1 = min(r_wg0 + a.rs_per_wg, a.row_steps);
   const int per_wave = (a.rs_per_wg + (kThreads / 64) - 1) / (kThreads / 64);
@@ -203,6 +203,16 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   auto row_off = [&](int r) {
     const int o = r * RPS + row_in_step;
     return (o < a.m_pad ? o : 0) * G + g0;
+  };
+  // with 64 lanes per row the row is wave-uniform: a scalar row base plus the
+  // lane's 32-bit offset (g0 elements) addresses the index loads
+  const uint32_t g0b = uint32_t(g0);
+  auto load_full = [&](int r, IdxRow<GL>& i0, IdxRow<GL>& i1w, Idx8Row<GL>& i1b) {
+    const int64_t rb = int64_t(r < a.m_pad ? r : 0) * G;
+    load_idx16<GL>(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(a.idx0 + rb) + 2 * g0b), i0);
+    if (RESID == 16)
+      load_idx16<GL>(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(idx1_16 + rb) + 2 * g0b), i1w);
+    if (RESID == 8) load_idx8<GL>(idx1_8 + rb + g0b, i1b);
   };
 
   // ---- steps 1-2.  The x loads go first, then the codebook image fetch; the
@@ -296,10 +306,14 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   IdxRow<GL> n0, n1w;
   Idx8Row<GL> n1b;
   if (r_begin < r_end) {
-    const int off = row_off(r_begin);
-    load_idx16<GL>(a.idx0 + off, n0);
-    if (RESID == 16) load_idx16<GL>(idx1_16 + off, n1w);
-    if (RESID == 8) load_idx8<GL>(idx1_8 + off, n1b);
+    if (FULL) {
+      load_full(r_begin, n0, n1w, n1b);
+    } else {
+      const int off = row_off(r_begin);
+      load_idx16<GL>(a.idx0 + off, n0);
+      if (RESID == 16) load_idx16<GL>(idx1_16 + off, n1w);
+      if (RESID == 8) load_idx8<GL>(idx1_8 + off, n1b);
+    }
   }
   __syncthreads();
 
@@ -323,6 +337,10 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
     if (o < a.m_pad && lane_in_row == LPR - 1) rowbuf[swz(o - wg * (a.rs_per_wg * RPS))] = v * a.out_scale;
   };
   auto load_row = [&](int r, IdxRow<GL>& i0, IdxRow<GL>& i1w, Idx8Row<GL>& i1b) {
+    if (FULL) {
+      load_full(r < r_end ? r : r_end - 1, i0, i1w, i1b);  // past the end: reload the last row
+      return;
+    }
     const int off = row_off(r < r_end ? r : r_end - 1);  // past the end: reload the last row
     load_idx16<GL>(a.idx0 + off, i0);
     if (RESID == 16) load_idx16<GL>(idx1_16 + off, i1w);

@@ -77,8 +77,8 @@ __device__ __forceinline__ half8 word_to_half8(uint32_t w, uint32_t m) {
 template <int HI>
 __device__ __forceinline__ half8 primary_half8(const uint32_t* lds, uint32_t w, uint32_t two) {
   const uint32_t desc = page_desc<HI>(lds, w, two);
-  const uint32_t word = slot_word<HI>(lds, w, desc);
-  const uint32_t m = uint32_t(__builtin_amdgcn_sbfe(desc, 7, 1));
+  const uint32_t m = page_mask(desc);
+  const uint32_t word = slot_word<HI>(lds, w, desc, m, two);
   return word_to_half8(word, m);
 }
 

@@ -60,7 +60,7 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
 // ---- codebook pack layout ----------------------------------------------------
 // header (256 B) | int8 table [entries][8] = 2c | LDS image (page table + slots)
 constexpr uint32_t kPackMagic = 0x32514C47u;  // "GLQ2"
-constexpr uint32_t kPackVersion = 3;
+constexpr uint32_t kPackVersion = 4;
 constexpr int kPageSize = 256;                 // indices per page
 constexpr int kPageCount = 256;                // pages of a 16-bit index
 constexpr int kImageMaxDwords = 39680;         // LDS image budget: 155 KiB

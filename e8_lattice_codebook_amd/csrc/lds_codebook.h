@@ -91,7 +91,7 @@ __device__ __forceinline__ uint32_t idx8_at(const Idx8Row<GL>& r, int q) {
 
 // ---- VALU byte selects (SDWA) ----------------------------------------------------
 // The index words hold two 16-bit indices (bytes 0-1 and 2-3) or four 8-bit ones.
-// 4 * byte SEL of w, and (byte SEL of w) ^ (byte 0 of d), in one instruction each.
+// 4 * byte SEL of w in one instruction.
 template <int SEL>
 __device__ __forceinline__ uint32_t byte_x4(uint32_t w, uint32_t two) {
   uint32_t r;
@@ -109,17 +109,6 @@ __device__ __forceinline__ uint32_t byte_x4(uint32_t w, uint32_t two) {
         : "=v"(r) : "v"(two), "v"(w));
   return r;
 }
-template <int SEL>
-__device__ __forceinline__ uint32_t xor_byte(uint32_t w, uint32_t d) {
-  uint32_t r;
-  if constexpr (SEL == 0)
-    asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:BYTE_0"
-        : "=v"(r) : "v"(w), "v"(d));
-  else
-    asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:BYTE_0"
-        : "=v"(r) : "v"(w), "v"(d));
-  return r;
-}
 
 // LDS layout of the decode kernel (dwords): [0, 256) the 8-bit residual slots,
 // [256, 256 + image) the primary image (page table, then slots).
@@ -133,15 +122,17 @@ __device__ __forceinline__ uint32_t lds_at(const uint32_t* lds, uint32_t byte_ad
 
 // Primary-codebook lookup of the 16-bit index in half HI of word w: the page
 // descriptor (image word idx >> 8), then the slot at image byte offset
-// 4 * ((idx ^ desc) & 255) + (desc >> 8), complemented (m = ~0) on descending pages.
+// ((4 (idx & 255)) ^ m) + desc with m = -(desc & 1), all ones on descending pages,
+// whose words are read complemented (m again).
 template <int HI>
 __device__ __forceinline__ uint32_t page_desc(const uint32_t* lds, uint32_t w, uint32_t two) {
   return lds_at(lds + kImgOff, byte_x4<HI ? 3 : 1>(w, two));
 }
+__device__ __forceinline__ uint32_t page_mask(uint32_t desc) { return uint32_t(__builtin_amdgcn_sbfe(desc, 0, 1)); }
 template <int HI>
-__device__ __forceinline__ uint32_t slot_word(const uint32_t* lds, uint32_t w, uint32_t desc) {
-  const uint32_t x = xor_byte<HI ? 2 : 0>(w, desc);
-  return lds_at(lds + kImgOff, (x << 2) + (desc >> 8));
+__device__ __forceinline__ uint32_t slot_word(const uint32_t* lds, uint32_t w, uint32_t desc, uint32_t m,
+                                              uint32_t two) {
+  return lds_at(lds + kImgOff, (byte_x4<HI ? 2 : 0>(w, two) ^ m) + desc);
 }
 
 
@@ -266,7 +257,7 @@ __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& 
 #pragma unroll
     for (int p = 0; p < 4; ++p) acc1[b][p] = 0;
   }
-  uint32_t d0[GL], d1[GL], n0w[GL], n1w_[GL];
+  uint32_t d0[GL], d1[GL], m0[GL], m1[GL], n0w[GL], n1w_[GL];
 #pragma unroll
   for (int q = 0; q < GL; ++q) {
     d0[q] = (q & 1) ? page_desc<1>(lds, i0.w[q >> 1], two) : page_desc<0>(lds, i0.w[q >> 1], two);
@@ -275,9 +266,14 @@ __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& 
   }
 #pragma unroll
   for (int q = 0; q < GL; ++q) {
-    n0w[q] = (q & 1) ? slot_word<1>(lds, i0.w[q >> 1], d0[q]) : slot_word<0>(lds, i0.w[q >> 1], d0[q]);
-    if (RESID == 16)
-      n1w_[q] = (q & 1) ? slot_word<1>(lds, i1w.w[q >> 1], d1[q]) : slot_word<0>(lds, i1w.w[q >> 1], d1[q]);
+    m0[q] = page_mask(d0[q]);
+    n0w[q] = (q & 1) ? slot_word<1>(lds, i0.w[q >> 1], d0[q], m0[q], two)
+                     : slot_word<0>(lds, i0.w[q >> 1], d0[q], m0[q], two);
+    if (RESID == 16) {
+      m1[q] = page_mask(d1[q]);
+      n1w_[q] = (q & 1) ? slot_word<1>(lds, i1w.w[q >> 1], d1[q], m1[q], two)
+                        : slot_word<0>(lds, i1w.w[q >> 1], d1[q], m1[q], two);
+    }
     if (RESID == 8) {
       const uint32_t w1 = i1b.w[q >> 2];
       uint32_t a1;
@@ -292,8 +288,8 @@ __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& 
   }
 #pragma unroll
   for (int q = 0; q < GL; ++q) {
-    const int32_t m = __builtin_amdgcn_sbfe(d0[q], 7, 1);
-    const uint32_t n = n0w[q] ^ uint32_t(m);
+    const int32_t m = int32_t(m0[q]);
+    const uint32_t n = n0w[q] ^ m0[q];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       acc0[b][0] = __mul24(m, gs[b][q]) + (q == 0 ? 0 : acc0[b][0]);
@@ -302,11 +298,10 @@ __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& 
         acc0[b][p] = __builtin_amdgcn_sdot8(int(n), int(dig[b][q][p]), (q == 0 && p > 0) ? 0 : acc0[b][p], false);
     }
     if (RESID == 16) {
-      const int32_t m1 = __builtin_amdgcn_sbfe(d1[q], 7, 1);
-      const uint32_t n1 = n1w_[q] ^ uint32_t(m1);
+      const uint32_t n1 = n1w_[q] ^ m1[q];
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        acc1[b][0] = __mul24(m1, gs[b][q]) + (q == 0 ? 0 : acc1[b][0]);
+        acc1[b][0] = __mul24(int32_t(m1[q]), gs[b][q]) + (q == 0 ? 0 : acc1[b][0]);
 #pragma unroll
         for (int p = 0; p < 4; ++p)
           acc1[b][p] = __builtin_amdgcn_sdot8(int(n1), int(dig[b][q][p]), (q == 0 && p > 0) ? 0 : acc1[b][p], false);

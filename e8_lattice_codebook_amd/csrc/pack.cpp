@@ -12,14 +12,17 @@
 //   image_offset     LDS image: page table [256] u32, then slot words
 //
 // Page table: index i falls in page p = i >> 8 at offset t = i & 255.  A page is
-// ascending (slot = base + t) or descending (slot = base + (255 - t)); its
-// descriptor is desc = ((4 * (base + 256)) << 8) | f with f = 0 or 255, so the
-// kernels read the image word at byte offset 4 * ((i ^ desc) & 255) + (desc >> 8)
-// (the slots follow the 256-dword page table).  A symmetric shell (entries M + r and
-// M - 1 - r are negatives of each other, M its centre) stores its upper half
-// once: its upper-half pages ascend, its lower-half pages descend and read the
-// negated words, flagged by f = 255.  Non-symmetric runs ascend; pages that hold
-// a run boundary or a shell centre are stored whole, ascending.
+// ascending (slot = base + t) or descending (slot = base + (255 - t)).  With
+// B = 4 * (base + 256), the byte address of slot `base` in the image (the slots
+// follow the 256-dword page table), its descriptor is desc = B on an ascending
+// page and desc = B + 1021 on a descending one, so bit 0 flags the direction and
+// with m = -(desc & 1) (0 or all ones) the kernels read the image word at byte
+// offset ((4 t) ^ m) + desc, i.e. B + 4 t or B + 1020 - 4 t, one xor-add.  A
+// symmetric shell (entries M + r and M - 1 - r are negatives of each other, M its
+// centre) stores its upper half once: its upper-half pages ascend, its lower-half
+// pages descend and read the negated words (the kernels complement every lane,
+// m again).  Non-symmetric runs ascend; pages that hold a run boundary or a shell
+// centre are stored whole, ascending.
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -129,7 +132,7 @@ glq_status build_pack(const uint16_t* cb, int64_t entries, void* out_pack, size_
   std::vector<uint32_t> slots;
   std::vector<uint32_t> desc(size_t(kPageCount), 0);
   auto make_desc = [](int64_t base, bool descending) {
-    return (uint32_t(4 * (base + kPageCount)) << 8) | (descending ? 0xFFu : 0u);
+    return uint32_t(4 * (base + kPageCount)) + (descending ? 1021u : 0u);
   };
   // exception (direct) pages first, in page order: a pack of <= 256 entries is slot = index
   for (int64_t p = 0; p < n_pages; ++p) {
@@ -167,8 +170,8 @@ glq_status build_pack(const uint16_t* cb, int64_t entries, void* out_pack, size_
   // self-check: every index resolves to its own codeword
   for (int64_t i = 0; i < entries; ++i) {
     const uint32_t dsc = desc[size_t(i >> 8)];
-    const bool m = (dsc & 0x80u) != 0;
-    const uint32_t ba = ((uint32_t(i) ^ dsc) & 0xFFu) * 4 + (dsc >> 8);  // byte offset in the image
+    const bool m = (dsc & 1u) != 0;
+    const uint32_t ba = ((uint32_t(i & 0xFF) * 4) ^ (m ? 0xFFFFFFFFu : 0u)) + dsc;  // byte offset in the image
     if (ba < 4u * kPageCount || ba % 4 != 0) return GLQ_ERR_CODEBOOK;
     const uint32_t slot = ba / 4 - kPageCount;
     if (slot >= slots.size()) return GLQ_ERR_CODEBOOK;

@@ -3,8 +3,8 @@
 The decode kernel gathers codewords from the pack's LDS image: a 256-entry page
 table and 4-byte slots of eight signed 4-bit values 2c, each negation-symmetric
 shell stored once.  These tests resolve every index the way the kernel does
-(byte address 4 * ((i ^ desc) & 255) + (desc >> 8), complemented when bit 7 of
-desc is set) and compare with the oracle's codebook; they also check the
+(m = -(desc & 1); byte address ((4 (i & 255)) ^ m) + desc mod 2^32, the word
+complemented when m is all ones) and compare with the oracle's codebook; they also check the
 integer identity the kernel's dot products rest on.  glq 0.5.1, "How it works", item 1;
 "Inference kernels".
 """
@@ -52,12 +52,12 @@ def nibbles_signed(words):
 
 
 def resolve(img, idx):
-    # the kernel's lookup: image byte offset 4 * ((i ^ desc) & 255) + (desc >> 8),
-    # complemented when bit 7 of desc is set
+    # the kernel's lookup: m = -(desc & 1), image byte offset ((4 (i & 255)) ^ m) + desc
+    # in 32-bit arithmetic, the word complemented when m is all ones
     idx = np.asarray(idx, dtype=np.int64)
     desc = img[idx >> 8].astype(np.int64)
-    m = np.where(desc & 0x80, -1, 0)
-    ba = ((idx ^ desc) & 0xFF) * 4 + (desc >> 8)
+    m = np.where(desc & 1, -1, 0)
+    ba = ((((idx & 0xFF) * 4) ^ (m & 0xFFFFFFFF)) + desc) & 0xFFFFFFFF
     assert (ba % 4 == 0).all() and (ba >= 1024).all()
     words = img[ba // 4]
     return words, m
