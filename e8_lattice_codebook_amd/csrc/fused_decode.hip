@@ -31,6 +31,8 @@
 // to m and cast.
 #include <math.h>
 
+#include <type_traits>
+
 #include "fwht_lds.h"
 #include "lds_codebook.h"
 
@@ -389,8 +391,49 @@ struct BlocksArgs {
   void* y;
   int64_t m;
   int S, m_pad, lr, lw;
+  int vec_sign;  // sign_out 4-byte aligned: one 32-bit load per CB = 4 signs
+  int vec_y;     // y aligned for CB-element stores
   float scale;
 };
+
+template <int CB>
+__device__ __forceinline__ void add_parts(float (&v)[CB], const float* zs) {
+  if constexpr (CB == 4) {
+    const float4 q = *reinterpret_cast<const float4*>(zs);
+    v[0] += q.x;
+    v[1 % CB] += q.y;
+    v[2 % CB] += q.z;
+    v[3 % CB] += q.w;
+  } else {
+#pragma unroll
+    for (int c = 0; c < CB; ++c) v[c] += zs[c];
+  }
+}
+
+__device__ __forceinline__ uint32_t bits16(half_t v) { return __builtin_bit_cast(uint16_t, v); }
+__device__ __forceinline__ uint32_t bits16(bf16_t v) { return v.bits; }
+
+// CB consecutive outputs with one store (p aligned to CB elements)
+template <class YT, int CB>
+__device__ __forceinline__ void store_vec(YT* p, const YT (&o)[CB]) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (std::is_same<YT, float>::value) {
+    if constexpr (CB == 4) *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+    else if constexpr (CB == 2) *reinterpret_cast<float2*>(p) = make_float2(o[0], o[1]);
+    else p[0] = o[0];
+  } else {
+    if constexpr (CB == 4) {
+      u32x2 w;
+      w.x = bits16(o[0]) | (bits16(o[1]) << 16);
+      w.y = bits16(o[2]) | (bits16(o[3]) << 16);
+      *reinterpret_cast<u32x2*>(p) = w;
+    } else if constexpr (CB == 2) {
+      *reinterpret_cast<uint32_t*>(p) = bits16(o[0]) | (bits16(o[1]) << 16);
+    } else {
+      p[0] = o[0];
+    }
+  }
+}
 
 template <class YT, int E, int CB>
 __global__ __launch_bounds__(64) void output_blocks_kernel(BlocksArgs a) {
@@ -398,23 +441,44 @@ __global__ __launch_bounds__(64) void output_blocks_kernel(BlocksArgs a) {
   const int b0 = int(blockIdx.x) * CB;
   const bool live = (lane * E) < (1 << a.lw);
   float v[E][CB];
+  uint32_t sg[E];  // sign bytes of the lane's CB outputs per block (sign_out has m_pad entries)
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int64_t i0 = (int64_t(lane * E + e) << a.lr) + b0;
 #pragma unroll
     for (int c = 0; c < CB; ++c) v[e][c] = 0.0f;
-    if (!live) continue;
-    for (int s = 0; s < a.S; ++s) {
-      const float* zs = a.z + int64_t(s) * a.m_pad + i0;
-      if (CB == 4) {
-        const float4 q = *reinterpret_cast<const float4*>(zs);
-        v[e][0] += q.x;
-        v[e][1 % CB] += q.y;
-        v[e][2 % CB] += q.z;
-        v[e][3 % CB] += q.w;
+    sg[e] = 0;
+  }
+  if (live) {
+    // every load is issued before the first use: signs, then the partials of
+    // four splits at a time, summed in split order
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int64_t i0 = (int64_t(lane * E + e) << a.lr) + b0;
+      if (CB == 4 && a.vec_sign) {
+        sg[e] = *reinterpret_cast<const uint32_t*>(a.sign + i0);
       } else {
 #pragma unroll
-        for (int c = 0; c < CB; ++c) v[e][c] += zs[c];
+        for (int c = 0; c < CB; ++c) sg[e] |= uint32_t(uint8_t(a.sign[i0 + c])) << (8 * c);
+      }
+    }
+    for (int s = 0; s < a.S; s += 4) {
+      float t[4][E][CB];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+#pragma unroll
+          for (int c = 0; c < CB; ++c) t[k][e][c] = 0.0f;
+          const int sk = s + k < a.S ? s + k : a.S - 1;  // past the last split: a valid address, not summed
+          add_parts<CB>(t[k][e], a.z + int64_t(sk) * a.m_pad + (int64_t(lane * E + e) << a.lr) + b0);
+        }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bool in = s + k < a.S;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+#pragma unroll
+          for (int c = 0; c < CB; ++c) v[e][c] += in ? t[k][e][c] : 0.0f;
       }
     }
   }
@@ -445,20 +509,27 @@ __global__ __launch_bounds__(64) void output_blocks_kernel(BlocksArgs a) {
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int64_t i0 = (int64_t(lane * E + e) << a.lr) + b0;
+    YT o[CB];
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
-      const int64_t i = i0 + c;
-      if (i < a.m) {
-        const uint32_t neg = a.sign[i] < 0 ? 0x80000000u : 0u;
-        y[i] = from_f32<YT>(__uint_as_float(__float_as_uint(v[e][c] * a.scale) ^ neg));
-      }
+      const uint32_t neg = (sg[e] >> (8 * c + 7)) << 31;  // sign bit of the c-th byte
+      o[c] = from_f32<YT>(__uint_as_float(__float_as_uint(v[e][c] * a.scale) ^ neg));
+    }
+    if (a.vec_y && i0 + CB <= a.m) {
+      store_vec<YT, CB>(y + i0, o);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+        if (i0 + c < a.m) y[i0 + c] = o[c];
     }
   }
 }
 
 template <class YT, int CB>
-hipError_t launch_blocks_e(const BlocksArgs& a, hipStream_t stream) {
+hipError_t launch_blocks_e(BlocksArgs a, hipStream_t stream) {
   const dim3 grid(unsigned((1 << a.lr) / CB)), block(64);
+  a.vec_sign = CB == 4 && reinterpret_cast<uintptr_t>(a.sign) % 4 == 0;
+  a.vec_y = reinterpret_cast<uintptr_t>(a.y) % (sizeof(YT) * CB) == 0;
   switch (a.lw <= 6 ? 1 : 1 << (a.lw - 6)) {
     case 1: hipLaunchKernelGGL((output_blocks_kernel<YT, 1, CB>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((output_blocks_kernel<YT, 2, CB>), grid, block, 0, stream, a); break;
