@@ -219,8 +219,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
     };
 
     // software pipeline: the fragments of k-step ks + 1 are dequantized while the
-    // MFMAs of ks run; A is loaded two k-steps ahead (ping-pong av / aw), a[mi] of
-    // ks + 2 right after the last MFMA that reads a[mi] of ks
+    // MFMAs of ks run; A is loaded two k-steps ahead (ping-pong av / aw)
     half8 av[kMB], aw[kMB];
 #pragma unroll
     for (int mi = 0; mi < kMB; ++mi) {
@@ -255,17 +254,12 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
 #pragma unroll
           for (int ni = 0; ni < kNB; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac[mi], bc[ni], acc[mi][ni], 0, 0, 0);
-          ac[mi] = *reinterpret_cast<const half8*>(abase + arow_off(mi) + ka);
         }
-        // interleave: each MFMA followed by a share of the VALU, LDS and global
-        // work of the next fragments, so the matrix core and the vector ALU overlap
+        // the A loads of ks + 2 after every MFMA of ks: with these loads (or
+        // scheduling barriers) among the MFMAs the register allocator rotates the
+        // accumulators through copies in every iteration
 #pragma unroll
-        for (int i = 0; i < kMB * kNB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
-          if (i < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-          if (i >= 16 && i < 24) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
-        }
+        for (int mi = 0; mi < kMB; ++mi) ac[mi] = *reinterpret_cast<const half8*>(abase + arow_off(mi) + ka);
       }
 #pragma unroll
       for (int ni = 0; ni < kNB; ++ni) {
