@@ -144,11 +144,15 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
   const uint16_t* idx1_16 = static_cast<const uint16_t*>(a.idx1);
 
   for (int tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
-    // tiles of one output slice go to one XCD (workgroup ids are dealt to the 8 XCDs in turn)
+    // workgroup ids are dealt to the 8 XCDs in turn: XCD x takes the output tiles
+    // x, x + 8, ..., token-tile major, so the workgroups running at once on an XCD
+    // share a few token tiles (A) and eight output tiles (index rows) in its L2
     int out_tile, tok_tile;
     if ((a.out_tiles & 7) == 0) {
-      tok_tile = (tile >> 3) % a.tok_tiles;
-      out_tile = (tile & 7) + 8 * (tile / (8 * a.tok_tiles));
+      const int per = a.out_tiles >> 3;  // output tiles of one XCD
+      const int i = tile >> 3;           // the tile's place in its XCD's order
+      tok_tile = i / per;
+      out_tile = (tile & 7) + 8 * (i - tok_tile * per);
     } else {
       out_tile = tile % a.out_tiles;
       tok_tile = tile / a.out_tiles;
