@@ -175,6 +175,30 @@ __device__ __forceinline__ void wave_block_transform(const float* rowbuf, float*
     *reinterpret_cast<float4*>(p + lane * E + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
 }
 
+// Butterfly of the chunk transform on lane bit k of the wave (column bit k + 2:
+// thread t holds columns 4 t .. 4 t + 3): v + partner on the lower lane of each
+// pair, partner - v on the upper one (s = -1 there); the partner comes from DPP
+// (quad permutes, row rotates; lane bit 2 takes the rotate by 12 on rows' banks
+// 0 and 2 and by 4 on banks 1 and 3), a swizzle (bit 4) or a permute (bit 5).
+__device__ __forceinline__ float lane_butterfly(float v, int k, float s, int lane) {
+  const int x = __float_as_int(v);
+  int pv;
+  switch (k) {
+    case 0: pv = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+    case 1: pv = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    case 2:
+      pv = __builtin_amdgcn_update_dpp(0, x, 0x12C, 0xF, 0x5, false);               // row_ror:12 -> lanes i + 4
+      pv = __builtin_amdgcn_update_dpp(pv, x, 0x124, 0xF, 0xA, false);              // row_ror:4  -> lanes i - 4
+      break;
+    case 3: pv = __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false); break;  // row_ror:8
+    case 4: pv = __builtin_amdgcn_ds_swizzle(x, 0x401F); break;                      // lane ^ 16 within 32
+    default: pv = __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, x); break;          // lane ^ 32
+  }
+  return fmaf(s, v, __int_as_float(pv));
+}
+
+__device__ __forceinline__ int dpp_partner1(int x) { return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false); }
+
 template <int RESID, bool FULL>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   constexpr int GL = 8;
@@ -221,6 +245,20 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   // chunk of u sits in the top kChunkDwords of LDS and the digit planes in the
   // region above image parts 0-7, so those parts are stored as soon as they
   // arrive and only parts 8-9 wait until every lane has its digits.
+  // the first row-step's index vectors go first of all: their latency overlaps
+  // the whole prologue
+  IdxRow<GL> n0, n1w;
+  Idx8Row<GL> n1b;
+  if (r_begin < r_end) {
+    if (FULL) {
+      load_full(r_begin, n0, n1w, n1b);
+    } else {
+      const int off = row_off(r_begin);
+      load_idx16<GL>(a.idx0 + off, n0);
+      if (RESID == 16) load_idx16<GL>(idx1_16 + off, n1w);
+      if (RESID == 8) load_idx8<GL>(idx1_8 + off, n1b);
+    }
+  }
   float* chunk = reinterpret_cast<float*>(lds + (kLdsDwords - kChunkDwords));
   const int K = 1 << a.lk;
   const int nsrc = 1 << (a.ln - a.lk);
@@ -243,41 +281,75 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
     for (int i = 0; i < 8; ++i)
       if (src0 + i < nsrc && c4 < K) x_accumulate(xr[i], a.x_dt, __popc(unsigned(split & (src0 + i))) & 1, t);
   }
+  // bits 0-1 in registers, bits 2-7 across the lanes of the wave (threads past
+  // the chunk hold zeros and never pair with one inside it), bits 8-11 in one
+  // LDS pass; the same butterflies in the same order as a transform of the row
+  fwht_reg<4>(t);
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    if (k + 2 < a.lk) {
+      const float sk = ((lane >> k) & 1) ? -1.0f : 1.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = lane_butterfly(t[e], k, sk, lane);
+    }
+  }
   if (c4 < K) {
-    fwht_reg<4>(t);
 #pragma unroll
     for (int e = 0; e < 4; ++e) chunk[swz(c4 + e)] = t[e];
   }
-  fwht_lds_passes(StoreLds{chunk}, 0, a.lk, 2, chunk);
+  fwht_lds_passes(StoreLds{chunk}, 0, a.lk, 8, chunk);
   __syncthreads();
   image_store<0, 8, false, RESID>(img, lds, tid);
 
-  // the chunk's 8 * LPR groups, one per thread; threads 8l .. 8l+7 hold lane l's
-  // 64 columns (one scale block)
-  if (tid < 8 * LPR) {
-    const int l = tid >> 3, q = tid & 7;
-    float v[8];
+  // quantization: thread t < 16 LPR takes half h = t & 1 (columns 4 h .. 4 h + 3)
+  // of group g = t >> 1, the group q = g & 7 of lane l = g >> 3; the 16 threads of
+  // a lane's 64 columns (one scale block) are one DPP row.  U = rint(u kUqMax / max)
+  // has the balanced base-16 digits d_p = nibble p of (U + 0x8888) minus 8, whose
+  // 4-bit two's complement is nibble p of W = (U + 0x8888) ^ 0x8888.
+  if (tid < 16 * LPR) {
+    const int g = tid >> 1, h = tid & 1;
+    const int l = g >> 3, q = g & 7;
+    float v[4];
     float mx = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v[j] = chunk[swz(tid * 8 + j)];
-      mx = fmaxf(mx, fabsf(v[j]));
+    for (int e = 0; e < 4; ++e) {
+      v[e] = chunk[swz(4 * tid + e)];
+      mx = fmaxf(mx, fabsf(v[e]));
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x128, 0xF, 0xF, false)));
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x124, 0xF, 0xF, false)));
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x122, 0xF, 0xF, false)));
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x121, 0xF, 0xF, false)));
     const float inv = mx > 0.0f ? float(kUqMax) / mx : 0.0f;
-    uint32_t planes[4];
-    int32_t gsum;
-    quantize_group(v, inv, planes, gsum);
-    img_x4 pv;
-    pv.x = planes[0];
-    pv.y = planes[1];
-    pv.z = planes[2];
-    pv.w = planes[3];
-    *reinterpret_cast<img_x4*>(lds + kDigOff + 4 * (q * LPR + l)) = pv;
-    lds[kGsOff + 4 * ((q >> 2) * LPR + l) + (q & 3)] = uint32_t(-gsum);  // negated: added on complemented reads
-    if (q == 0) lds[kScOff + l] = __float_as_uint(mx * a.sc_scale);
+    uint32_t w[4];
+    int32_t gsum = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      int U = int(rintf(v[e] * inv));
+      U = U > kUqMax ? kUqMax : (U < -kUqMax ? -kUqMax : U);
+      gsum += U;
+      w[e] = uint32_t(U + 0x8888) ^ 0x8888u;
+    }
+    gsum += dpp_partner1(gsum);
+    // columns 4 h + e sit in nibble (h 2) + lane_nibble(e) of the plane word
+    const uint32_t r0 = w[0] | (w[1] << 16), r1 = w[2] | (w[3] << 16);
+    uint32_t pl[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const uint32_t part = ((r0 >> (4 * pp)) & 0x000F000Fu) | (((r1 >> (4 * pp)) & 0x000F000Fu) << 4);
+      const uint32_t mine = part << (8 * h);
+      pl[pp] = mine | uint32_t(dpp_partner1(int(mine)));
+    }
+    if (h == 0) {
+      img_x4 pv;
+      pv.x = pl[0];
+      pv.y = pl[1];
+      pv.z = pl[2];
+      pv.w = pl[3];
+      *reinterpret_cast<img_x4*>(lds + kDigOff + 4 * (q * LPR + l)) = pv;
+      lds[kGsOff + 4 * ((q >> 2) * LPR + l) + (q & 3)] = uint32_t(-gsum);  // negated: added on complemented reads
+      if (q == 0) lds[kScOff + l] = __float_as_uint(mx * a.sc_scale);
+    }
   }
   __syncthreads();
   uint32_t dig[1][GL][4];
@@ -302,21 +374,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   sc[0] = __uint_as_float(lds[kScOff + lane_in_row]);
   __syncthreads();  // every lane has its digits before image parts 8-9 overwrite them
 
-  // ---- step 3: the rest of the image, then the rows; the first row-step's
-  // index vectors are in flight meanwhile
+  // ---- step 3: the rest of the image, then the rows
   image_store<8, 10, true, RESID>(img, lds, tid);
-  IdxRow<GL> n0, n1w;
-  Idx8Row<GL> n1b;
-  if (r_begin < r_end) {
-    if (FULL) {
-      load_full(r_begin, n0, n1w, n1b);
-    } else {
-      const int off = row_off(r_begin);
-      load_idx16<GL>(a.idx0 + off, n0);
-      if (RESID == 16) load_idx16<GL>(idx1_16 + off, n1w);
-      if (RESID == 8) load_idx8<GL>(idx1_8 + off, n1b);
-    }
-  }
   __syncthreads();
 
   // one row-step: the lane's groups of row r against the digit planes, the
