@@ -8,6 +8,10 @@ input RHT, the decode matmul against the indices and output RHT.  The layers
 are independent calls on seeded synthetic data (no activation between them).
 R copies of the three layers' index arrays (>= 1 GiB in total) are rotated so
 every step reads its indices from HBM, not from the 256 MB Infinity Cache.
+The 16-bit index arrays are relabelled once, before timing, as slot codes
+(glq_slot_codes: the same codebook entries, decoded with one LDS read);
+--index-format codebook times the codebook indices themselves, and the run
+reports the other format beside the headline.
 
 value   = sum over the step's layers of (index bytes + x bytes + y bytes + sign
           bytes) / step time, in GB/s (inputs resident in HBM before timing starts).
@@ -46,12 +50,14 @@ def act_bytes(dtype):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--index-format", choices=["slot", "codebook"], default="slot",
+                    help="16-bit index arrays as slot codes (default) or as codebook indices")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run 10 plain device-to-device copies of BYTES (scale for HBM traffic counters)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -93,7 +99,10 @@ def main():
     copies = max(2, math.ceil((1 << 30) / idx_bytes))
     log("bench: %d layers, %.1f MiB of indices per step, %d rotating copies" % (
         len(host_layers), idx_bytes / 2 ** 20, copies))
-    qls = [[glq.QuantizedLayer.from_synth(l, cb) for l in host_layers] for _ in range(copies)]
+    qls_cb = [[glq.QuantizedLayer.from_synth(l, cb) for l in host_layers] for _ in range(copies)]
+    qls_slot = [[q.to_slot_codes() for q in row] for row in qls_cb]
+    slot = args.index_format == "slot"
+    qls, qls_other = (qls_slot, qls_cb) if slot else (qls_cb, qls_slot)
     xs = []
     for k, l in enumerate(host_layers):
         _, raw = synth.make_x(l.n, B, wl.act_dtype, wl.seed, k)
@@ -145,6 +154,18 @@ def main():
     achieved = sum(launch_bytes) / (sum(per_layer_ms) * 1e-3) / 1e9
     log("bench: per-launch ms %s -> %.1f GB/s" % (["%.4f" % t for t in per_layer_ms], achieved))
 
+    # the other index format, same loop and step count
+    other_steps = min(args.steps, 300)
+    e0.record()
+    for i in range(other_steps):
+        row = qls_other[i % copies]
+        for k in range(len(row)):
+            glq.e8rht_linear(row[k], xs[k], out=ys[k], workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    other_value = step_bytes / (e0.elapsed_time(e1) / other_steps * 1e-3) / 1e9
+    log("bench: %s indices: %.1f GB/s" % ("codebook" if slot else "slot-code", other_value))
+
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -164,6 +185,8 @@ def main():
             "workload": "Devstral-Small-24B MLP decode (gate 5120->32768, up 5120->32768, down 32768->5120), "
                         "4 bpw (16+16-bit E8 indices), B=%d, bf16 activations, uniform seeded indices" % B,
             "batch": B,
+            "index_format": ("slot codes: the 16-bit indices relabelled once at load (glq_slot_codes), "
+                             "same entries and bytes") if slot else "codebook indices",
             "index_bytes_per_step": idx_bytes,
             "algorithmic_bytes_per_step": step_bytes,
             "rotating_copies": copies,
@@ -183,6 +206,9 @@ def main():
             "bytes_per_launch": launch_bytes,
         },
     }
+
+    result["other_index_format"] = {"index_format": "codebook indices" if slot else "slot codes",
+                                    "value": round(other_value, 2), "unit": "GB/s", "steps": other_steps}
 
     if not args.no_prefill:
         result["prefill"] = bench_prefill(glq, synth, cb, dev, args, log)
@@ -292,7 +318,9 @@ def bench_prefill(glq, synth, cb, dev, args, log):
     wl = synth.WORKLOADS["prefill_gateup"]
     l = synth.make_layer(wl.layers[0], wl.resid_bits, wl.seed, 0)
     M = wl.batches[0]
-    q = glq.QuantizedLayer.from_synth(l, cb)
+    q_cb = glq.QuantizedLayer.from_synth(l, cb)
+    q_slot = q_cb.to_slot_codes()
+    q, q_other = (q_slot, q_cb) if args.index_format == "slot" else (q_cb, q_slot)
     _, raw = synth.make_x(l.n, M, wl.act_dtype, wl.seed, 0)
     x = torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
     assert glq.e8_matmul_prefill_supported(q)
@@ -323,12 +351,20 @@ def bench_prefill(glq, synth, cb, dev, args, log):
     torch.cuda.synchronize()
     gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     tflops = flops / (gemm_ms * 1e-3) / 1e12
+    for a, b in evs:  # the matmul on the other index format
+        a.record()
+        glq.e8_matmul_prefill(q_other, u, M, out=z)
+        b.record()
+    torch.cuda.synchronize()
+    other_tflops = flops / (float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3) / 1e12
     log("bench: prefill linear %.4f ms, MFMA matmul %.4f ms = %.1f TFLOP/s" % (lin_ms, gemm_ms, tflops))
     return {
         "workload": "SmolLM3-3B gate 2048->11008 (m_pad 16384), M=2048 tokens, 3 bpw, bf16 activations",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "linear_ms": round(lin_ms, 5),
+        "other_index_format": {"index_format": "codebook indices" if args.index_format == "slot" else "slot codes",
+                               "value": round(other_tflops, 2), "unit": "TFLOP/s"},
         "roofline": {"bound": "mfma", "kernel": "gemm_lds_kernel (prefill matmul: codewords from the LDS "
                      "codebook dequantized into fp16 MFMA operands, fp32 accumulation)",
                      "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -16,6 +16,7 @@ from ._lib import GLQ_BF16, GLQ_F16, GLQ_F32, GLQError, GlqLayer  # noqa: F401
 
 CODEBOOK_ENTRIES = 65536
 RESID8_ENTRIES = 256
+INDEX_CODEBOOK, INDEX_SLOT = 0, 1  # glq_index_format
 
 _DT = {torch.float32: GLQ_F32, torch.float16: GLQ_F16, torch.bfloat16: GLQ_BF16}
 
@@ -82,7 +83,7 @@ class QuantizedLayer:
     """Device copy of one layer (signs, index arrays) plus its glq_layer descriptor."""
 
     def __init__(self, n, m, n_pad, m_pad, resid_bits, sign_in, sign_out, idx0, idx1, codebooks,
-                 wscale=0.02, resid_scale=0.25, device=None):
+                 wscale=0.02, resid_scale=0.25, device=None, index_format=INDEX_CODEBOOK):
         device = torch.device(device) if device is not None else codebooks.device
         self.n, self.m, self.n_pad, self.m_pad = int(n), int(m), int(n_pad), int(m_pad)
         self.resid_bits = int(resid_bits)
@@ -90,19 +91,35 @@ class QuantizedLayer:
         self.sign_in = _to_dev(sign_in, torch.int8, device)
         self.sign_out = _to_dev(sign_out, torch.int8, device)
         self.idx0 = _to_dev(idx0, torch.int16, device)
-        self.idx1 = None if idx1 is None else _to_dev(
-            idx1, torch.uint8 if np.asarray(idx1).dtype == np.uint8 else torch.int16, device)
+        if idx1 is None:
+            self.idx1 = None
+        else:
+            i1_8 = idx1.dtype == torch.uint8 if isinstance(idx1, torch.Tensor) else np.asarray(idx1).dtype == np.uint8
+            self.idx1 = _to_dev(idx1, torch.uint8 if i1_8 else torch.int16, device)
         self.codebooks = codebooks
         self.device = device
+        self.index_format = int(index_format)
         self.desc = GlqLayer(self.n, self.n_pad, self.m, self.m_pad, self.resid_bits, self.wscale, self.resid_scale,
                              self.sign_in.data_ptr(), self.sign_out.data_ptr(), self.idx0.data_ptr(),
                              0 if self.idx1 is None else self.idx1.data_ptr(), codebooks.primary.data_ptr(),
-                             0 if resid_bits == 0 else codebooks.residual(resid_bits).data_ptr())
+                             0 if resid_bits == 0 else codebooks.residual(resid_bits).data_ptr(), self.index_format)
 
     @classmethod
     def from_synth(cls, layer, codebooks, device=None):
         return cls(layer.n, layer.m, layer.n_pad, layer.m_pad, layer.resid_bits, layer.sign_in, layer.sign_out,
                    layer.idx0, layer.idx1, codebooks, layer.wscale, layer.resid_scale, device)
+
+    def to_slot_codes(self):
+        """The same layer with its 16-bit index arrays relabelled as slot codes
+        (glq_slot_codes): idx0, and idx1 when the residual stage is 16-bit."""
+        if self.index_format == INDEX_SLOT:
+            return self
+        idx0 = slot_codes(self.idx0, self.codebooks)
+        idx1 = self.idx1
+        if self.resid_bits == 16:
+            idx1 = slot_codes(self.idx1, self.codebooks)
+        return QuantizedLayer(self.n, self.m, self.n_pad, self.m_pad, self.resid_bits, self.sign_in, self.sign_out,
+                              idx0, idx1, self.codebooks, self.wscale, self.resid_scale, self.device, INDEX_SLOT)
 
     def index_bytes(self):
         return self.idx0.numel() * 2 + (0 if self.idx1 is None else self.idx1.numel() * self.idx1.element_size())
@@ -118,6 +135,15 @@ def _to_dev(a, dtype, device):
 
 
 # ---- operations -----------------------------------------------------------------
+def slot_codes(idx, codebooks, out=None):
+    """codes[i] = the slot code of codebook index idx[i] (glq_slot_codes); int16/uint16 tensors."""
+    idx = idx.contiguous()
+    codes = out if out is not None else torch.empty_like(idx)
+    _lib.check(lib().glq_slot_codes(codebooks.primary.data_ptr(), _ptr(idx), idx.numel(), _ptr(codes),
+                                    _stream(idx.device)), "glq_slot_codes")
+    return codes
+
+
 def input_rht(x, n_pad, sign_in, u_dtype=torch.float32, out=None):
     """u = H (sign_in * [x, 0]) / sqrt(n_pad) per row of x [B, n] (glq_input_rht)."""
     B, n = x.shape

@@ -25,7 +25,7 @@ class GlqLayer(ctypes.Structure):
         ("n", c_i64), ("n_pad", c_i64), ("m", c_i64), ("m_pad", c_i64),
         ("resid_bits", c_i32), ("wscale", c_f32), ("resid_scale", c_f32),
         ("sign_in", c_vp), ("sign_out", c_vp), ("idx0", c_vp), ("idx1", c_vp),
-        ("cb_pack", c_vp), ("cb2_pack", c_vp),
+        ("cb_pack", c_vp), ("cb2_pack", c_vp), ("index_format", c_i32),
     ]
 
 
@@ -43,6 +43,7 @@ SIGNATURES = {
     "glq_output_rht_workspace_bytes": (c_sz, [c_i64, c_i64]),
     "glq_output_rht": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, ctypes.c_int, c_vp, c_sz, c_vp]),
     "glq_e8_dequant": (ctypes.c_int, [_LP, c_vp, ctypes.c_int, c_vp]),
+    "glq_slot_codes": (ctypes.c_int, [c_vp, c_vp, c_i64, c_vp, c_vp]),
     "glq_e8_matmul_splits": (c_i64, [_LP, c_i64]),
     "glq_e8_matmul_workspace_bytes": (c_sz, [_LP, c_i64]),
     "glq_e8_matmul": (ctypes.c_int, [_LP, c_vp, ctypes.c_int, c_i64, c_vp, c_vp, c_sz, c_vp]),

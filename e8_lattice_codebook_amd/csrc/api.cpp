@@ -29,6 +29,9 @@ glq_status check_layer(const glq_layer* L, bool need_signs) {
   if (L->resid_bits != 0 && (!L->idx1 || !L->cb2_pack)) return GLQ_ERR_NULL;
   if (!aligned(L->idx0, 16) || !aligned(L->cb_pack, 256)) return GLQ_ERR_ALIGN;
   if (L->resid_bits != 0 && (!aligned(L->idx1, 16) || !aligned(L->cb2_pack, 256))) return GLQ_ERR_ALIGN;
+  if (L->index_format != GLQ_INDEX_CODEBOOK && L->index_format != GLQ_INDEX_SLOT) return GLQ_ERR_RECIPE;
+  // slot codes of a 16-bit residual stage name entries of the primary pack
+  if (L->index_format == GLQ_INDEX_SLOT && L->resid_bits == 16 && L->cb2_pack != L->cb_pack) return GLQ_ERR_RECIPE;
   return GLQ_OK;
 }
 
@@ -127,6 +130,14 @@ size_t glq_codebook_pack_bytes(int64_t entries) {
 
 glq_status glq_codebook_pack(const uint16_t* cb_host, int64_t entries, void* pack_host, size_t pack_bytes_given) {
   return build_pack(cb_host, entries, pack_host, pack_bytes_given);
+}
+
+glq_status glq_slot_codes(const void* cb_pack, const uint16_t* idx, int64_t count, uint16_t* codes,
+                          hipStream_t stream) {
+  if (!cb_pack || (count > 0 && (!idx || !codes))) return GLQ_ERR_NULL;
+  if (count < 0) return GLQ_ERR_SHAPE;
+  if (!aligned(cb_pack, 256) || !aligned(idx, 2) || !aligned(codes, 2)) return GLQ_ERR_ALIGN;
+  return from_hip(launch_slot_codes(cb_pack, idx, count, codes, stream));
 }
 
 size_t glq_input_rht_workspace_bytes(int64_t B, int64_t n_pad, glq_dtype u_dt) {

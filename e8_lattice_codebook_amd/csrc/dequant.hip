@@ -49,13 +49,18 @@ __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float* v) {
   *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// map0 / map1: the pack's code -> index tables when the 16-bit stages hold slot
+// codes, else null
 template <class WT, int RESID>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint16_t* __restrict__ idx0, const void* __restrict__ idx1,
                                                       const int8_t* __restrict__ cb0, const int8_t* __restrict__ cb1,
-                                                      float s, float sr, int64_t groups, WT* __restrict__ w) {
+                                                      const uint16_t* __restrict__ map0,
+                                                      const uint16_t* __restrict__ map1, float s, float sr,
+                                                      int64_t groups, WT* __restrict__ w) {
   const int64_t g = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (g >= groups) return;
-  const uint2 c0 = *reinterpret_cast<const uint2*>(cb0 + size_t(idx0[g]) * 8);
+  const uint32_t i0 = map0 ? uint32_t(map0[idx0[g]]) : uint32_t(idx0[g]);
+  const uint2 c0 = *reinterpret_cast<const uint2*>(cb0 + size_t(i0) * 8);
   float e[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -63,8 +68,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint16_t* __restrict
     e[j + 4] = 0.5f * i8_at(c0.y, j);
   }
   if (RESID != 0) {
-    const uint32_t i1 = RESID == 8 ? uint32_t(static_cast<const uint8_t*>(idx1)[g])
-                                   : uint32_t(static_cast<const uint16_t*>(idx1)[g]);
+    uint32_t i1 = RESID == 8 ? uint32_t(static_cast<const uint8_t*>(idx1)[g])
+                             : uint32_t(static_cast<const uint16_t*>(idx1)[g]);
+    if (RESID == 16 && map1) i1 = map1[i1];
     const uint2 c1 = *reinterpret_cast<const uint2*>(cb1 + size_t(i1) * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -85,24 +91,69 @@ hipError_t dequant_typed(const glq_layer& L, void* w, hipStream_t stream) {
   const int8_t* cb0 = static_cast<const int8_t*>(L.cb_pack) + pack_i8_offset();
   const int8_t* cb1 = L.cb2_pack ? static_cast<const int8_t*>(L.cb2_pack) + pack_i8_offset() : nullptr;
   WT* out = static_cast<WT*>(w);
+  const uint16_t* map0 = nullptr;
+  const uint16_t* map1 = nullptr;
+  if (L.index_format == GLQ_INDEX_SLOT) {
+    map0 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(L.cb_pack) +
+                                             pack_index_of_offset(GLQ_CODEBOOK_ENTRIES));
+    if (L.resid_bits == 16)
+      map1 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(L.cb2_pack) +
+                                               pack_index_of_offset(GLQ_CODEBOOK_ENTRIES));
+  }
   switch (L.resid_bits) {
     case 0:
-      hipLaunchKernelGGL((dequant_kernel<WT, 0>), grid, block, 0, stream, L.idx0, L.idx1, cb0, cb1, L.wscale,
-                         L.resid_scale, groups, out);
+      hipLaunchKernelGGL((dequant_kernel<WT, 0>), grid, block, 0, stream, L.idx0, L.idx1, cb0, cb1, map0, map1,
+                         L.wscale, L.resid_scale, groups, out);
       break;
     case 8:
-      hipLaunchKernelGGL((dequant_kernel<WT, 8>), grid, block, 0, stream, L.idx0, L.idx1, cb0, cb1, L.wscale,
-                         L.resid_scale, groups, out);
+      hipLaunchKernelGGL((dequant_kernel<WT, 8>), grid, block, 0, stream, L.idx0, L.idx1, cb0, cb1, map0, map1,
+                         L.wscale, L.resid_scale, groups, out);
       break;
     default:
-      hipLaunchKernelGGL((dequant_kernel<WT, 16>), grid, block, 0, stream, L.idx0, L.idx1, cb0, cb1, L.wscale,
-                         L.resid_scale, groups, out);
+      hipLaunchKernelGGL((dequant_kernel<WT, 16>), grid, block, 0, stream, L.idx0, L.idx1, cb0, cb1, map0, map1,
+                         L.wscale, L.resid_scale, groups, out);
       break;
   }
   return hipGetLastError();
 }
 
+// codes[i] = code_of[idx[i]], eight values per thread where the buffers allow
+__global__ __launch_bounds__(256) void slot_codes_kernel(const uint16_t* __restrict__ code_of, const uint16_t* idx,
+                                                         int64_t count, uint16_t* codes, int vec) {
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (vec) {
+    if (t * 8 + 8 > count) return;
+    const uint4 v = reinterpret_cast<const uint4*>(idx)[t];
+    uint4 r;
+    r.x = uint32_t(code_of[v.x & 0xFFFFu]) | (uint32_t(code_of[v.x >> 16]) << 16);
+    r.y = uint32_t(code_of[v.y & 0xFFFFu]) | (uint32_t(code_of[v.y >> 16]) << 16);
+    r.z = uint32_t(code_of[v.z & 0xFFFFu]) | (uint32_t(code_of[v.z >> 16]) << 16);
+    r.w = uint32_t(code_of[v.w & 0xFFFFu]) | (uint32_t(code_of[v.w >> 16]) << 16);
+    reinterpret_cast<uint4*>(codes)[t] = r;
+  } else {
+    if (t >= count) return;
+    codes[t] = code_of[idx[t]];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_slot_codes(const void* cb_pack, const uint16_t* idx, int64_t count, uint16_t* codes,
+                             hipStream_t stream) {
+  if (count == 0) return hipSuccess;
+  const uint16_t* code_of = reinterpret_cast<const uint16_t*>(static_cast<const char*>(cb_pack) +
+                                                              pack_code_of_offset(GLQ_CODEBOOK_ENTRIES));
+  const bool vec = (reinterpret_cast<uintptr_t>(idx) % 16 == 0) && (reinterpret_cast<uintptr_t>(codes) % 16 == 0);
+  const int64_t vcount = vec ? count / 8 : 0;
+  if (vcount > 0)
+    hipLaunchKernelGGL(slot_codes_kernel, dim3(unsigned((vcount + 255) / 256)), dim3(256), 0, stream, code_of, idx,
+                       vcount * 8, codes, 1);
+  const int64_t rest = count - vcount * 8;
+  if (rest > 0)
+    hipLaunchKernelGGL(slot_codes_kernel, dim3(unsigned((rest + 255) / 256)), dim3(256), 0, stream, code_of,
+                       idx + vcount * 8, rest, codes + vcount * 8, 0);
+  return hipGetLastError();
+}
 
 hipError_t launch_dequant(const glq_layer& layer, void* w, glq_dtype w_dt, hipStream_t stream) {
   switch (w_dt) {

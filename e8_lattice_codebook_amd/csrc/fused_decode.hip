@@ -199,7 +199,7 @@ __device__ __forceinline__ float lane_butterfly(float v, int k, float s, int lan
 
 __device__ __forceinline__ int dpp_partner1(int x) { return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false); }
 
-template <int RESID, bool FULL>
+template <int RESID, bool FULL, bool CODES>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   constexpr int GL = 8;
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsDwords];
@@ -207,6 +207,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   float* fbuf = reinterpret_cast<float*>(lds);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const uint32_t delta = CODES ? slot_delta(a.pack0_hdr) : 0u;
   const int split = int(blockIdx.x) / a.wgs_per_split;
   const int wg = int(blockIdx.x) - split * a.wgs_per_split;
   const int lpr = FULL ? 6 : a.lpr_log2;
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   for (int i = 0; i < 8; ++i)
     if (i < nsrc && c4 < K) x_issue(a, (int64_t(i) << a.lk) + c4, xr[i]);
   ImageRegs img;
-  image_issue<RESID>(img, a.pack0_hdr, a.img0, a.res_slots, tid);
+  image_issue<RESID>(img, a.pack0_hdr, a.img0, a.res_slots, tid, CODES ? kHdrSlotDwords : 3);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     if (i < nsrc && c4 < K) x_accumulate(xr[i], a.x_dt, __popc(unsigned(split & i)) & 1, t);
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   auto row_step = [&](const IdxRow<GL>& i0, const IdxRow<GL>& i1w, const Idx8Row<GL>& i1b, int r) {
     const int o = r * RPS + row_in_step;
     float vv[1];
-    row_dots<1, GL, RESID>(lds, i0, i1w, i1b, dig, gs, a.sr, vv);
+    row_dots<1, GL, RESID, CODES>(lds, i0, i1w, i1b, dig, gs, a.sr, vv, delta);
     float v = vv[0] * sc[0];
     if (FULL) {
       v = dpp_add(v, 0);
@@ -674,7 +675,9 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
   a.idx1 = L.idx1;
   const char* p0 = static_cast<const char*>(L.cb_pack);
   a.pack0_hdr = reinterpret_cast<const uint32_t*>(p0);
-  a.img0 = reinterpret_cast<const uint32_t*>(p0 + pack_image_offset(GLQ_CODEBOOK_ENTRIES));
+  const bool codes = L.index_format == GLQ_INDEX_SLOT;
+  a.img0 = reinterpret_cast<const uint32_t*>(
+      p0 + (codes ? pack_slot_image_offset(GLQ_CODEBOOK_ENTRIES) : pack_image_offset(GLQ_CODEBOOK_ENTRIES)));
   a.res_slots = nullptr;
   if (L.resid_bits == 8)
     a.res_slots = reinterpret_cast<const uint32_t*>(static_cast<const char*>(L.cb2_pack) +
@@ -698,19 +701,20 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
   a.sr = L.resid_scale;
   const dim3 grid(unsigned(p.splits * p.wgs_per_split)), block(kThreads);
   const bool full = p.lpr_log2 == 6;
-  switch (L.resid_bits) {
-    case 0:
-      if (full) hipLaunchKernelGGL((fused_decode_kernel<0, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((fused_decode_kernel<0, false>), grid, block, 0, stream, a);
-      break;
-    case 8:
-      if (full) hipLaunchKernelGGL((fused_decode_kernel<8, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((fused_decode_kernel<8, false>), grid, block, 0, stream, a);
-      break;
-    default:
-      if (full) hipLaunchKernelGGL((fused_decode_kernel<16, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((fused_decode_kernel<16, false>), grid, block, 0, stream, a);
-      break;
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, a); };
+  switch (L.resid_bits * 4 + (full ? 2 : 0) + (codes ? 1 : 0)) {
+    case 0: go(fused_decode_kernel<0, false, false>); break;
+    case 1: go(fused_decode_kernel<0, false, true>); break;
+    case 2: go(fused_decode_kernel<0, true, false>); break;
+    case 3: go(fused_decode_kernel<0, true, true>); break;
+    case 32: go(fused_decode_kernel<8, false, false>); break;
+    case 33: go(fused_decode_kernel<8, false, true>); break;
+    case 34: go(fused_decode_kernel<8, true, false>); break;
+    case 35: go(fused_decode_kernel<8, true, true>); break;
+    case 64: go(fused_decode_kernel<16, false, false>); break;
+    case 65: go(fused_decode_kernel<16, false, true>); break;
+    case 66: go(fused_decode_kernel<16, true, false>); break;
+    default: go(fused_decode_kernel<16, true, true>); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -32,7 +32,8 @@ template <int RESID>
 __global__ __launch_bounds__(256) void gemm_kernel(const half_t* __restrict__ A, int64_t M, int64_t n_pad,
                                                    int64_t m_pad, const uint16_t* __restrict__ idx0,
                                                    const void* __restrict__ idx1v, const int8_t* __restrict__ cb0,
-                                                   const int8_t* __restrict__ cb1, float s, float sr,
+                                                   const int8_t* __restrict__ cb1,
+                                                   const uint16_t* __restrict__ map, float s, float sr,
                                                    float* __restrict__ z) {
   __shared__ __attribute__((aligned(16))) half_t As[BM * LDK];
   __shared__ __attribute__((aligned(16))) half_t Bs[BN * LDK];
@@ -72,7 +73,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const half_t* __restrict__ A,
       const int64_t o = o0 + r, g = (k0 >> 3) + gq;
       half8 w = half8{0, 0, 0, 0, 0, 0, 0, 0};
       if (o < m_pad && g < gpr) {
-        const uint2 c0 = *reinterpret_cast<const uint2*>(cb0 + size_t(idx0[o * gpr + g]) * 8);
+        const uint32_t i0 = map ? uint32_t(map[idx0[o * gpr + g]]) : uint32_t(idx0[o * gpr + g]);
+        const uint2 c0 = *reinterpret_cast<const uint2*>(cb0 + size_t(i0) * 8);
         float e[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -81,10 +83,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const half_t* __restrict__ A,
         }
         if (RESID != 0) {
           uint2 c1;
-          if (RESID == 8)
+          if (RESID == 8) {
             c1 = res_tab[idx1_8[o * gpr + g]];
-          else
-            c1 = *reinterpret_cast<const uint2*>(cb1 + size_t(idx1_16[o * gpr + g]) * 8);
+          } else {
+            const uint32_t i1 = map ? uint32_t(map[idx1_16[o * gpr + g]]) : uint32_t(idx1_16[o * gpr + g]);
+            c1 = *reinterpret_cast<const uint2*>(cb1 + size_t(i1) * 8);
+          }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             e[j] = fmaf(sr, 0.5f * i8_at(c1.x, j), e[j]);
@@ -136,18 +140,23 @@ hipError_t launch_gemm(const glq_layer& L, const half_t* u16, int64_t M, float* 
   const dim3 grid(unsigned((L.m_pad + BN - 1) / BN), unsigned((M + BM - 1) / BM)), block(256);
   const int8_t* cb0 = static_cast<const int8_t*>(L.cb_pack) + pack_i8_offset();
   const int8_t* cb1 = L.cb2_pack ? static_cast<const int8_t*>(L.cb2_pack) + pack_i8_offset() : nullptr;
+  // slot codes (16-bit stages, one pack): back to indices through the pack's table
+  const uint16_t* map = L.index_format == GLQ_INDEX_SLOT
+                            ? reinterpret_cast<const uint16_t*>(static_cast<const char*>(L.cb_pack) +
+                                                                pack_index_of_offset(GLQ_CODEBOOK_ENTRIES))
+                            : nullptr;
   switch (L.resid_bits) {
     case 0:
       hipLaunchKernelGGL((gemm_kernel<0>), grid, block, 0, stream, u16, M, L.n_pad, L.m_pad, L.idx0, L.idx1, cb0,
-                         cb1, L.wscale, L.resid_scale, z);
+                         cb1, map, L.wscale, L.resid_scale, z);
       break;
     case 8:
       hipLaunchKernelGGL((gemm_kernel<8>), grid, block, 0, stream, u16, M, L.n_pad, L.m_pad, L.idx0, L.idx1, cb0,
-                         cb1, L.wscale, L.resid_scale, z);
+                         cb1, map, L.wscale, L.resid_scale, z);
       break;
     default:
       hipLaunchKernelGGL((gemm_kernel<16>), grid, block, 0, stream, u16, M, L.n_pad, L.m_pad, L.idx0, L.idx1, cb0,
-                         cb1, L.wscale, L.resid_scale, z);
+                         cb1, map, L.wscale, L.resid_scale, z);
       break;
   }
   return hipGetLastError();

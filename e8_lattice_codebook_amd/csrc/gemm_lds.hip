@@ -74,11 +74,17 @@ __device__ __forceinline__ half8 word_to_half8(uint32_t w, uint32_t m) {
   return half8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
 }
 
-template <int HI>
-__device__ __forceinline__ half8 primary_half8(const uint32_t* lds, uint32_t w, uint32_t two) {
-  const uint32_t desc = page_desc<HI>(lds, w, two);
-  const uint32_t m = page_mask(desc);
-  const uint32_t word = slot_word<HI>(lds, w, desc, m, two);
+// the codeword of the 16-bit index (page image) or slot code (slot image) in half HI of w
+template <int HI, bool CODES>
+__device__ __forceinline__ half8 primary_half8(const uint32_t* lds, uint32_t w, uint32_t two, uint32_t delta) {
+  uint32_t m, word;
+  if constexpr (CODES) {
+    word = code_word<HI>(lds, w, delta, m);
+  } else {
+    const uint32_t desc = page_desc<HI>(lds, w, two);
+    m = page_mask(desc);
+    word = slot_word<HI>(lds, w, desc, m, two);
+  }
   return word_to_half8(word, m);
 }
 
@@ -94,7 +100,7 @@ __device__ __forceinline__ uint32_t byte_x16(uint32_t w) {
   return r;
 }
 
-template <int RESID, bool TILED>
+template <int RESID, bool TILED, bool CODES>
 __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsDwords];
   __shared__ __attribute__((aligned(16))) uint32_t res16[RESID == 8 ? 256 * 4 : 4];  // fp16 2c1, natural order
@@ -102,10 +108,11 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const uint32_t two = 2;
+  const uint32_t delta = CODES ? slot_delta(a.pack0_hdr) : 0u;
 
   // ---- the image (and the fp16 residual table) into LDS, once per workgroup
   {
-    uint32_t nd = a.pack0_hdr[3];
+    uint32_t nd = a.pack0_hdr[CODES ? kHdrSlotDwords : 3];
     nd = nd > uint32_t(kImageMaxDwords) ? uint32_t(kImageMaxDwords) : nd;
     const uint32_t nd4 = nd >> 2;
     const u32x4* src4 = reinterpret_cast<const u32x4*>(a.img0);
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
     auto dequant = [&](const u32x2 (&i0)[kNB], const uint32_t (&i1b)[kNB], const u32x2 (&i1w)[kNB], int ni,
                        int kk) -> half8 {
       const uint32_t w0 = (kk < 2) ? i0[ni].x : i0[ni].y;
-      half8 b = (kk & 1) ? primary_half8<1>(lds, w0, two) : primary_half8<0>(lds, w0, two);
+      half8 b = (kk & 1) ? primary_half8<1, CODES>(lds, w0, two, delta) : primary_half8<0, CODES>(lds, w0, two, delta);
       if (RESID != 0) {
         half8 r;
         if (RESID == 8) {
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
           r = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(res16) + ra));
         } else {
           const uint32_t w1 = (kk < 2) ? i1w[ni].x : i1w[ni].y;
-          r = (kk & 1) ? primary_half8<1>(lds, w1, two) : primary_half8<0>(lds, w1, two);
+          r = (kk & 1) ? primary_half8<1, CODES>(lds, w1, two, delta) : primary_half8<0, CODES>(lds, w1, two, delta);
         }
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
@@ -323,7 +330,9 @@ hipError_t launch_gemm_lds(const glq_layer& L, const half_t* u16, int64_t M, boo
   a.idx1 = L.idx1;
   const char* p0 = static_cast<const char*>(L.cb_pack);
   a.pack0_hdr = reinterpret_cast<const uint32_t*>(p0);
-  a.img0 = reinterpret_cast<const uint32_t*>(p0 + pack_image_offset(GLQ_CODEBOOK_ENTRIES));
+  const bool codes = L.index_format == GLQ_INDEX_SLOT;
+  a.img0 = reinterpret_cast<const uint32_t*>(
+      p0 + (codes ? pack_slot_image_offset(GLQ_CODEBOOK_ENTRIES) : pack_image_offset(GLQ_CODEBOOK_ENTRIES)));
   a.res_i8 = L.resid_bits == 8 ? static_cast<const int8_t*>(L.cb2_pack) + pack_i8_offset() : nullptr;
   a.z = z;
   a.M = M;
@@ -336,7 +345,11 @@ hipError_t launch_gemm_lds(const glq_layer& L, const half_t* u16, int64_t M, boo
   a.scale = 0.5f * L.wscale;
   a.sr = L.resid_scale;
   const int grid = a.tiles < cus_of_device() ? a.tiles : cus_of_device();
-#define GLQ_LAUNCH(R, T) hipLaunchKernelGGL((gemm_lds_kernel<R, T>), dim3(grid), dim3(kPThreads), 0, stream, a)
+#define GLQ_LAUNCH(R, T)                                                                                    \
+  do {                                                                                                      \
+    if (codes) hipLaunchKernelGGL((gemm_lds_kernel<R, T, true>), dim3(grid), dim3(kPThreads), 0, stream, a); \
+    else hipLaunchKernelGGL((gemm_lds_kernel<R, T, false>), dim3(grid), dim3(kPThreads), 0, stream, a);     \
+  } while (0)
   switch (L.resid_bits) {
     case 0: if (tiled) GLQ_LAUNCH(0, true); else GLQ_LAUNCH(0, false); break;
     case 8: if (tiled) GLQ_LAUNCH(8, true); else GLQ_LAUNCH(8, false); break;

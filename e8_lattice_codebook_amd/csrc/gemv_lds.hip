@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void quant_u_kernel(const float* __restrict__ 
   if ((t & ((int64_t(1) << bg_log2) - 1)) == 0) scale[t >> bg_log2] = mx / float(kUqMax);
 }
 
-template <int NB, int GL, int RESID, bool FULL>
+template <int NB, int GL, int RESID, bool FULL, bool CODES>
 __global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
     const uint16_t* __restrict__ idx0, const void* __restrict__ idx1v, const uint32_t* __restrict__ pack0_hdr,
     const uint32_t* __restrict__ img0, const uint32_t* __restrict__ res_slots, const uint32_t* __restrict__ uq_dig,
@@ -84,7 +84,8 @@ __global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
     float* __restrict__ z_parts) {
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsDwords];
   const int tid = threadIdx.x;
-  load_image_1024<RESID>(lds, pack0_hdr, img0, res_slots, tid);
+  load_image_1024<RESID>(lds, pack0_hdr, img0, res_slots, tid, CODES ? kHdrSlotDwords : 3);
+  const uint32_t delta = CODES ? slot_delta(pack0_hdr) : 0u;
 
   const int lane = tid & 63;
   const int lpr = FULL ? 6 : lpr_log2;
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
     }
 
     float vv[NB];
-    row_dots<NB, GL, RESID>(lds, i0, i1w, i1b, dig, gs, sr, vv);
+    row_dots<NB, GL, RESID, CODES>(lds, i0, i1w, i1b, dig, gs, sr, vv, delta);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       float v = vv[b] * sc[b];
@@ -215,9 +216,9 @@ int device_cus() {
 }
 
 
-template <int NB, int GL, int RESID, bool FULL>
+template <int NB, int GL, int RESID, bool FULL, bool CODES>
 hipError_t launch_t(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream) {
-  auto kern = gemv_lds_kernel<NB, GL, RESID, FULL>;
+  auto kern = gemv_lds_kernel<NB, GL, RESID, FULL, CODES>;
   const int rps = 64 >> p.lpr_log2;
   const int64_t row_steps = (L.m_pad + rps - 1) / rps;
   const int64_t units = row_steps * p.splits;
@@ -228,7 +229,8 @@ hipError_t launch_t(const glq_layer& L, const void* uq, int64_t B, float* z, con
   const UqLayout U = uq_layout(B, L.n_pad);
   const char* uqc = static_cast<const char*>(uq);
   const char* p0 = static_cast<const char*>(L.cb_pack);
-  const uint32_t* img0 = reinterpret_cast<const uint32_t*>(p0 + pack_image_offset(GLQ_CODEBOOK_ENTRIES));
+  const uint32_t* img0 = reinterpret_cast<const uint32_t*>(
+      p0 + (CODES ? pack_slot_image_offset(GLQ_CODEBOOK_ENTRIES) : pack_image_offset(GLQ_CODEBOOK_ENTRIES)));
   const uint32_t* res = nullptr;
   if (RESID == 8)
     res = reinterpret_cast<const uint32_t*>(static_cast<const char*>(L.cb2_pack) +
@@ -246,8 +248,12 @@ hipError_t launch_t(const glq_layer& L, const void* uq, int64_t B, float* z, con
 
 template <int NB, int GL, int RESID>
 hipError_t launch_f(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream) {
-  if (p.lpr_log2 == 6) return launch_t<NB, GL, RESID, true>(L, uq, B, z, p, stream);
-  return launch_t<NB, GL, RESID, false>(L, uq, B, z, p, stream);
+  const bool codes = L.index_format == GLQ_INDEX_SLOT;
+  if (p.lpr_log2 == 6)
+    return codes ? launch_t<NB, GL, RESID, true, true>(L, uq, B, z, p, stream)
+                 : launch_t<NB, GL, RESID, true, false>(L, uq, B, z, p, stream);
+  return codes ? launch_t<NB, GL, RESID, false, true>(L, uq, B, z, p, stream)
+               : launch_t<NB, GL, RESID, false, false>(L, uq, B, z, p, stream);
 }
 
 template <int NB, int GL>

@@ -60,7 +60,7 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
 // ---- codebook pack layout ----------------------------------------------------
 // header (256 B) | int8 table [entries][8] = 2c | LDS image (page table + slots)
 constexpr uint32_t kPackMagic = 0x32514C47u;  // "GLQ2"
-constexpr uint32_t kPackVersion = 4;
+constexpr uint32_t kPackVersion = 5;
 constexpr int kPageSize = 256;                 // indices per page
 constexpr int kPageCount = 256;                // pages of a 16-bit index
 constexpr int kImageMaxDwords = 39680;         // LDS image budget: 155 KiB
@@ -71,6 +71,17 @@ constexpr int kResidDwords = 256;              // 8-bit residual slots (direct)
 __host__ __device__ constexpr int lane_nibble(int e) { return (e >> 1) + 4 * (e & 1); }
 inline size_t pack_i8_offset() { return 256; }
 inline size_t pack_image_offset(int64_t entries) { return align256(256 + size_t(entries) * 8); }
+// Slot-code format (header words 5 and 6: slot image dwords, 0 when the codebook
+// has no slot format, and delta): a 16-bit code c, read as int16 with m = c >> 15
+// (0 or all ones), names slot (c ^ m) + (m & delta) of the slot image, a plain
+// 4-byte word like a page slot, read complemented when m is all ones.  code_of
+// [entries] maps an index to its code and index_of [65536] a code to its index.
+constexpr int kHdrSlotDwords = 5;
+constexpr int kHdrSlotDelta = 6;
+constexpr int kSlotShared = 32768;  // codes below, and complemented codes, both reach [delta, 32768)
+inline size_t pack_slot_image_offset(int64_t entries) { return pack_image_offset(entries) + size_t(kImageMaxDwords) * 4; }
+inline size_t pack_code_of_offset(int64_t entries) { return pack_slot_image_offset(entries) + size_t(kImageMaxDwords) * 4; }
+inline size_t pack_index_of_offset(int64_t entries) { return pack_code_of_offset(entries) + align256(size_t(entries) * 2); }
 size_t pack_total_bytes(int64_t entries);
 glq_status build_pack(const uint16_t* cb_host, int64_t entries, void* pack_host, size_t pack_bytes);
 
@@ -84,6 +95,8 @@ hipError_t launch_rht_out(const float* z, int64_t S, int64_t B, int64_t m, int L
                           void* y, glq_dtype y_dt, float* ws, hipStream_t stream);
 
 hipError_t launch_dequant(const glq_layer& layer, void* w, glq_dtype w_dt, hipStream_t stream);
+hipError_t launch_slot_codes(const void* cb_pack, const uint16_t* idx, int64_t count, uint16_t* codes,
+                             hipStream_t stream);
 
 // Decode matmul, codewords gathered from the packs' int8 tables in global memory
 // (used when a 16-bit residual stage has its own codebook): z_parts [S][B][m_pad].

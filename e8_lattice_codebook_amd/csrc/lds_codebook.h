@@ -135,6 +135,31 @@ __device__ __forceinline__ uint32_t slot_word(const uint32_t* lds, uint32_t w, u
   return lds_at(lds + kImgOff, (byte_x4<HI ? 2 : 0>(w, two) ^ m) + desc);
 }
 
+// Slot-code lookup of the code in half HI of w (the slot image in LDS at kImgOff):
+// m = all ones when the code is negative as int16, slot (code ^ m) + (m & delta),
+// the word to be read complemented when m is all ones.  delta <= kImageMaxDwords -
+// 32768 keeps every slot inside the image.
+template <int HI>
+__device__ __forceinline__ uint32_t code_word(const uint32_t* lds, uint32_t w, uint32_t delta, uint32_t& m) {
+  uint32_t x;
+  if (HI) {
+    m = uint32_t(int32_t(w) >> 31);
+    asm("v_xor_b32_sdwa %0, sext(%1), %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1 src1_sel:DWORD"
+        : "=v"(x) : "v"(w), "v"(m));
+  } else {
+    m = uint32_t(__builtin_amdgcn_sbfe(w, 15, 1));
+    asm("v_xor_b32_sdwa %0, sext(%1), %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:DWORD"
+        : "=v"(x) : "v"(w), "v"(m));
+  }
+  return lds_at(lds + kImgOff, (x + (m & delta)) << 2);
+}
+
+// delta of a pack's slot-code format, clamped so that no slot leaves the image
+__device__ __forceinline__ uint32_t slot_delta(const uint32_t* pack_hdr) {
+  const uint32_t d = pack_hdr[kHdrSlotDelta];
+  return d < uint32_t(kImageMaxDwords - kSlotShared) ? d : uint32_t(kImageMaxDwords - kSlotShared);
+}
+
 
 // ---- activations in 16-bit fixed point ----------------------------------------------
 // Per 64 columns, U = rint(u * kUqMax / max|u|); U is written as four balanced
@@ -176,10 +201,10 @@ struct ImageRegs {
 template <int RESID>
 __device__ __forceinline__ void image_issue(ImageRegs& r, const uint32_t* __restrict__ pack0_hdr,
                                             const uint32_t* __restrict__ img0,
-                                            const uint32_t* __restrict__ res_slots, int tid) {
+                                            const uint32_t* __restrict__ res_slots, int tid, int nd_word) {
   constexpr int kT = 1024;
   static_assert((kImageMaxDwords / 4 + kT - 1) / kT == 10, "image load unrolled for 10 parts");
-  uint32_t nd = pack0_hdr[3];
+  uint32_t nd = pack0_hdr[nd_word];
   nd = nd > uint32_t(kImageMaxDwords) ? uint32_t(kImageMaxDwords) : nd;
   r.nd = nd;
   r.nd4 = nd >> 2;
@@ -232,9 +257,9 @@ __device__ __forceinline__ void image_store(const ImageRegs& r, uint32_t* lds, i
 template <int RESID>
 __device__ __forceinline__ void load_image_1024(uint32_t* lds, const uint32_t* __restrict__ pack0_hdr,
                                                 const uint32_t* __restrict__ img0,
-                                                const uint32_t* __restrict__ res_slots, int tid) {
+                                                const uint32_t* __restrict__ res_slots, int tid, int nd_word) {
   ImageRegs r;
-  image_issue<RESID>(r, pack0_hdr, img0, res_slots, tid);
+  image_issue<RESID>(r, pack0_hdr, img0, res_slots, tid, nd_word);
   image_store<0, 10, true, RESID>(r, lds, tid);
 }
 
@@ -246,10 +271,10 @@ __device__ __forceinline__ void load_image_1024(uint32_t* lds, const uint32_t* _
 // every slot word, then the dot products) so the LDS latencies overlap.  On a
 // descending page the complemented word n ^ ~0 has lanes -2c - 1, and the
 // group's -sum_j U_j (gs) is added to plane 0 to undo the -1s.
-template <int NB, int GL, int RESID>
+template <int NB, int GL, int RESID, bool CODES>
 __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& i0, const IdxRow<GL>& i1w,
                                          const Idx8Row<GL>& i1b, const uint32_t (&dig)[NB][GL][4],
-                                         const int32_t (&gs)[NB][GL], float sr, float (&v)[NB]) {
+                                         const int32_t (&gs)[NB][GL], float sr, float (&v)[NB], uint32_t delta) {
   const uint32_t two = 2;
   int acc0[NB][4], acc1[NB][4];
 #pragma unroll
@@ -258,22 +283,35 @@ __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& 
     for (int p = 0; p < 4; ++p) acc1[b][p] = 0;
   }
   uint32_t d0[GL], d1[GL], m0[GL], m1[GL], n0w[GL], n1w_[GL];
+  if constexpr (CODES) {
 #pragma unroll
-  for (int q = 0; q < GL; ++q) {
-    d0[q] = (q & 1) ? page_desc<1>(lds, i0.w[q >> 1], two) : page_desc<0>(lds, i0.w[q >> 1], two);
-    if (RESID == 16)
-      d1[q] = (q & 1) ? page_desc<1>(lds, i1w.w[q >> 1], two) : page_desc<0>(lds, i1w.w[q >> 1], two);
+    for (int q = 0; q < GL; ++q) {
+      n0w[q] = (q & 1) ? code_word<1>(lds, i0.w[q >> 1], delta, m0[q]) : code_word<0>(lds, i0.w[q >> 1], delta, m0[q]);
+      if (RESID == 16)
+        n1w_[q] = (q & 1) ? code_word<1>(lds, i1w.w[q >> 1], delta, m1[q])
+                          : code_word<0>(lds, i1w.w[q >> 1], delta, m1[q]);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < GL; ++q) {
+      d0[q] = (q & 1) ? page_desc<1>(lds, i0.w[q >> 1], two) : page_desc<0>(lds, i0.w[q >> 1], two);
+      if (RESID == 16)
+        d1[q] = (q & 1) ? page_desc<1>(lds, i1w.w[q >> 1], two) : page_desc<0>(lds, i1w.w[q >> 1], two);
+    }
+#pragma unroll
+    for (int q = 0; q < GL; ++q) {
+      m0[q] = page_mask(d0[q]);
+      n0w[q] = (q & 1) ? slot_word<1>(lds, i0.w[q >> 1], d0[q], m0[q], two)
+                       : slot_word<0>(lds, i0.w[q >> 1], d0[q], m0[q], two);
+      if (RESID == 16) {
+        m1[q] = page_mask(d1[q]);
+        n1w_[q] = (q & 1) ? slot_word<1>(lds, i1w.w[q >> 1], d1[q], m1[q], two)
+                          : slot_word<0>(lds, i1w.w[q >> 1], d1[q], m1[q], two);
+      }
+    }
   }
 #pragma unroll
   for (int q = 0; q < GL; ++q) {
-    m0[q] = page_mask(d0[q]);
-    n0w[q] = (q & 1) ? slot_word<1>(lds, i0.w[q >> 1], d0[q], m0[q], two)
-                     : slot_word<0>(lds, i0.w[q >> 1], d0[q], m0[q], two);
-    if (RESID == 16) {
-      m1[q] = page_mask(d1[q]);
-      n1w_[q] = (q & 1) ? slot_word<1>(lds, i1w.w[q >> 1], d1[q], m1[q], two)
-                        : slot_word<0>(lds, i1w.w[q >> 1], d1[q], m1[q], two);
-    }
     if (RESID == 8) {
       const uint32_t w1 = i1b.w[q >> 2];
       uint32_t a1;

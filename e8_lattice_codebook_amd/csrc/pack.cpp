@@ -23,8 +23,11 @@
 // pages descend and read the negated words (the kernels complement every lane,
 // m again).  Non-symmetric runs ascend; pages that hold a run boundary or a shell
 // centre are stored whole, ascending.
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "internal.h"
@@ -42,9 +45,7 @@ struct Run {
 
 namespace glq {
 
-size_t pack_total_bytes(int64_t entries) {
-  return size_t(pack_image_offset(entries)) + size_t(kImageMaxDwords) * 4;
-}
+size_t pack_total_bytes(int64_t entries) { return pack_index_of_offset(entries) + size_t(65536) * 2; }
 
 glq_status build_pack(const uint16_t* cb, int64_t entries, void* out_pack, size_t out_bytes) {
   if (!cb || !out_pack) return GLQ_ERR_NULL;
@@ -187,6 +188,91 @@ glq_status build_pack(const uint16_t* cb, int64_t entries, void* out_pack, size_
     if (w != word(i)) return GLQ_ERR_CODEBOOK;
   }
 
+  // ---- slot-code format: every codeword whose negation is also an entry shares
+  // one slot with it (the pair's second member reads it complemented); the other
+  // entries fill [0, delta) plain and [32768, 32768 + delta) negated
+  std::unordered_map<uint32_t, int64_t> pos;
+  for (int64_t i = 0; i < entries; ++i) pos.emplace(word(i), i);
+  auto neg_word = [&](int64_t i, bool& ok) {  // the negated codeword's word, if its lanes fit
+    uint32_t w = 0;
+    ok = true;
+    for (int j = 0; j < 8; ++j) {
+      const int v = -t[size_t(i * 8 + j)];
+      if (v > 7) ok = false;
+      w |= uint32_t(v & 15) << (4 * lane_nibble(j));
+    }
+    return w;
+  };
+  std::vector<int64_t> partner(size_t(entries), -1);
+  std::vector<std::pair<int64_t, int64_t>> pairs;  // (plain member, complemented member)
+  for (int64_t i = 0; i < entries; ++i) {
+    if (partner[size_t(i)] >= 0) continue;
+    bool ok;
+    const uint32_t nw = neg_word(i, ok);
+    if (!ok) continue;
+    auto it = pos.find(nw);
+    if (it == pos.end() || it->second == i || partner[size_t(it->second)] >= 0) continue;
+    const int64_t j = it->second;
+    partner[size_t(i)] = j;
+    partner[size_t(j)] = i;
+    pairs.emplace_back(std::max(i, j), std::min(i, j));
+  }
+  const int64_t F = int64_t(pairs.size());
+  const int64_t delta = kSlotShared - F;
+  std::vector<int64_t> lone_plain, lone_neg;
+  for (int64_t i = 0; i < entries; ++i) {  // entries that cannot be negated stay plain
+    if (partner[size_t(i)] >= 0) continue;
+    bool ok;
+    neg_word(i, ok);
+    if (!ok) lone_plain.push_back(i);
+  }
+  for (int64_t i = 0; i < entries; ++i) {
+    if (partner[size_t(i)] >= 0) continue;
+    bool ok;
+    neg_word(i, ok);
+    if (!ok) continue;
+    if (int64_t(lone_plain.size()) < delta) lone_plain.push_back(i);
+    else lone_neg.push_back(i);
+  }
+  const int64_t slot_dwords = kSlotShared + int64_t(lone_neg.size());
+  const bool slot_ok = int64_t(lone_plain.size()) <= delta && int64_t(lone_neg.size()) <= delta &&
+                       slot_dwords <= kImageMaxDwords;
+  std::vector<uint32_t> slot_img;
+  std::vector<uint16_t> code_of(size_t(entries), 0), index_of(65536, 0);
+  if (slot_ok) {
+    slot_img.assign(size_t(slot_dwords), 0u);
+    for (size_t r = 0; r < lone_plain.size(); ++r) {
+      slot_img[r] = word(lone_plain[r]);
+      code_of[size_t(lone_plain[r])] = uint16_t(r);
+    }
+    for (size_t k = 0; k < pairs.size(); ++k) {
+      slot_img[size_t(delta) + k] = word(pairs[k].first);
+      code_of[size_t(pairs[k].first)] = uint16_t(delta + int64_t(k));
+      code_of[size_t(pairs[k].second)] = uint16_t(0xFFFFu - uint32_t(k));  // int16 ~k
+    }
+    for (size_t r = 0; r < lone_neg.size(); ++r) {
+      bool ok;
+      slot_img[size_t(kSlotShared) + r] = neg_word(lone_neg[r], ok);
+      const uint32_t x = uint32_t(kSlotShared) + uint32_t(r) - uint32_t(delta);
+      code_of[size_t(lone_neg[r])] = uint16_t(0xFFFFu - x);
+    }
+    // self-check: every code decodes, as the kernels read it, to its entry
+    std::vector<uint8_t> used(65536, 0);
+    for (int64_t i = 0; i < entries; ++i) {
+      const int32_t c = int16_t(code_of[size_t(i)]);
+      const uint32_t m = uint32_t(c >> 15);
+      const uint32_t P = (uint32_t(c) ^ m) + (m & uint32_t(delta));
+      if (P >= uint32_t(slot_dwords) || used[code_of[size_t(i)]]) return GLQ_ERR_CODEBOOK;
+      used[code_of[size_t(i)]] = 1;
+      index_of[code_of[size_t(i)]] = uint16_t(i);
+      const uint32_t w = slot_img[P];
+      for (int j = 0; j < 8; ++j) {
+        const int v = int32_t(((w >> (4 * lane_nibble(j))) & 15u) << 28) >> 28;
+        if ((m ? -v : v) != t[size_t(i * 8 + j)]) return GLQ_ERR_CODEBOOK;
+      }
+    }
+  }
+
   // write the pack
   std::memset(out_pack, 0, pack_total_bytes(entries));
   uint32_t* hdr = static_cast<uint32_t*>(out_pack);
@@ -200,6 +286,14 @@ glq_status build_pack(const uint16_t* cb, int64_t entries, void* out_pack, size_
   uint32_t* img = reinterpret_cast<uint32_t*>(static_cast<char*>(out_pack) + pack_image_offset(entries));
   std::memcpy(img, desc.data(), size_t(kPageCount) * 4);
   std::memcpy(img + kPageCount, slots.data(), slots.size() * 4);
+  if (slot_ok) {
+    hdr[kHdrSlotDwords] = uint32_t(slot_dwords);
+    hdr[kHdrSlotDelta] = uint32_t(delta);
+    char* base = static_cast<char*>(out_pack);
+    std::memcpy(base + pack_slot_image_offset(entries), slot_img.data(), slot_img.size() * 4);
+    std::memcpy(base + pack_code_of_offset(entries), code_of.data(), code_of.size() * 2);
+    std::memcpy(base + pack_index_of_offset(entries), index_of.data(), index_of.size() * 2);
+  }
   return GLQ_OK;
 }
 

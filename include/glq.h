@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define GLQ_ABI_VERSION 1
+#define GLQ_ABI_VERSION 2
 #define GLQ_CODEBOOK_ENTRIES 65536
 #define GLQ_RESID8_ENTRIES 256
 #define GLQ_MAX_PAD (1 << 20)
@@ -64,6 +64,12 @@ typedef enum glq_status {
   GLQ_ERR_HIP = 7,       /* a HIP launch failed */
   GLQ_ERR_CODEBOOK = 8   /* codebook entries outside what the pack can hold */
 } glq_status;
+
+/* What the layer's 16-bit index arrays hold (glq_layer.index_format). */
+typedef enum glq_index_format {
+  GLQ_INDEX_CODEBOOK = 0, /* indices into the 65,536-entry codebook ("How it works", item 1) */
+  GLQ_INDEX_SLOT = 1      /* the same entries relabelled as slot codes by glq_slot_codes */
+} glq_index_format;
 
 typedef enum glq_dtype {
   GLQ_F32 = 0,  /* IEEE binary32 */
@@ -93,6 +99,10 @@ typedef enum glq_dtype {
  *   cb2_pack        residual codebook pack: 256 entries for resid_bits 8, 65,536
  *                   for resid_bits 16 (it may be the same buffer as cb_pack);
  *                   NULL when resid_bits == 0
+ *   index_format    GLQ_INDEX_CODEBOOK, or GLQ_INDEX_SLOT: idx0 (and idx1 when
+ *                   resid_bits == 16) hold slot codes of cb_pack, written by
+ *                   glq_slot_codes; with resid_bits 16 cb2_pack must then be
+ *                   cb_pack.  8-bit residual indices are never relabelled.
  */
 typedef struct glq_layer {
   int64_t n;
@@ -108,6 +118,7 @@ typedef struct glq_layer {
   const void* idx1;
   const void* cb_pack;
   const void* cb2_pack;
+  int32_t index_format;
 } glq_layer;
 
 /* GLQ_ABI_VERSION of the built library. */
@@ -146,6 +157,26 @@ glq_status glq_e8_codebook(uint16_t* cb_host, int64_t entries);
  */
 size_t glq_codebook_pack_bytes(int64_t entries);
 glq_status glq_codebook_pack(const uint16_t* cb_host, int64_t entries, void* pack_host, size_t pack_bytes);
+
+/*
+ * glq_slot_codes — relabel a layer's 16-bit codebook indices as slot codes, once,
+ * when the layer is loaded.  A slot code names the same codebook entry (the map
+ * is a bijection of the 65,536 values, kept in the pack) in the form the LDS
+ * kernels read without a page table: as int16 c with m = c >> 15, the entry is
+ * slot (c ^ m) + (m & delta) of the pack's slot image, negated when m is all
+ * ones; each codeword whose negation is also an entry shares its slot with it.
+ * The pages' decode is unchanged: one 16-bit value per 8-weight group, decoded
+ * in registers/LDS ("How it works", item 1; "Inference kernels").
+ *   cb_pack     device, a 65,536-entry pack from glq_codebook_pack, 256-byte aligned
+ *   idx         device uint16 [count] codebook indices
+ *   codes       device uint16 [count]; may be idx itself (in place)
+ * Asynchronous on stream.  Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE (count < 0),
+ * GLQ_ERR_ALIGN, GLQ_ERR_HIP.  A pack whose codebook has no slot format (header
+ * word 5 is 0; the E8 codebook always has one) yields codes that decode wrongly:
+ * build layers for it in GLQ_INDEX_CODEBOOK.
+ */
+glq_status glq_slot_codes(const void* cb_pack, const uint16_t* idx, int64_t count, uint16_t* codes,
+                          hipStream_t stream);
 
 /*
  * glq_input_rht — u = H_{n_pad} (sign_in * [x, 0...]) / sqrt(n_pad) for each of B

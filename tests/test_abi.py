@@ -38,7 +38,7 @@ def test_header_declarations_are_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.glq_abi_version() == 1
+    assert lib.glq_abi_version() == 2
     for s in range(9):
         assert lib.glq_status_string(s)
     assert lib.glq_status_string(0) == b"ok"
@@ -138,6 +138,19 @@ class TestValidation:
         assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 1, 16, A, A, 1 << 30, None) == 3
         assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 0, A, A, 1 << 30, None) == 2
         assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A + 4, 0, 1, A, A, 1 << 30, None) == 5
+
+    def test_index_format(self):
+        lib = _lib.load()
+        assert linear_status(fake_layer(index_format=2)) == 4
+        assert linear_status(fake_layer(index_format=-1)) == 4
+        # slot codes of a 16-bit residual stage need the primary pack there too
+        assert linear_status(fake_layer(resid_bits=16, index_format=1, cb2_pack=A + 256)) == 4
+        assert lib.glq_slot_codes(None, A, 8, A, None) == 1
+        assert lib.glq_slot_codes(A, None, 8, A, None) == 1
+        assert lib.glq_slot_codes(A, A, -1, A, None) == 2
+        assert lib.glq_slot_codes(A + 16, A, 8, A, None) == 5
+        assert lib.glq_slot_codes(A, A + 1, 8, A, None) == 5
+        assert lib.glq_slot_codes(A, None, 0, None, None) == 0  # nothing to do
         assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 1, A, None, 0, None) == 6
         assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 1, A, A, 8, None) == 6
         assert lib.glq_e8_matmul_splits(ctypes.byref(fake_layer(n_pad=32768)), 1) == 8

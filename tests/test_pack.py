@@ -125,3 +125,62 @@ def test_complement_identity_of_the_dot_products():
     assert (r == 0).all()
     assert np.array_equal(sum(p * 16 ** k for k, p in enumerate(planes)), U)
     assert all((p >= -8).all() and (p <= 7).all() for p in planes)
+
+
+# ---- slot-code format -----------------------------------------------------------
+# Header word 5: slot image dwords, word 6: delta.  After the 256-dword-aligned
+# int8 table come the page image and the slot image (39,680 dwords each), then
+# code_of [entries] uint16 (256-byte aligned) and index_of [65536] uint16.
+IMAGE_MAX = 39680
+
+
+def slot_tables(pack, entries):
+    hdr = pack[:256].view(np.uint32)
+    img_off = (256 + entries * 8 + 255) // 256 * 256
+    slot_off = img_off + IMAGE_MAX * 4
+    code_off = slot_off + IMAGE_MAX * 4
+    index_off = code_off + (entries * 2 + 255) // 256 * 256
+    slots = pack[slot_off:slot_off + int(hdr[5]) * 4].view(np.uint32)
+    code_of = pack[code_off:code_off + entries * 2].view(np.uint16)
+    index_of = pack[index_off:index_off + 65536 * 2].view(np.uint16)
+    return hdr, slots, code_of, index_of
+
+
+def decode_codes(slots, delta, codes):
+    # the kernels' lookup: c as int16, m = c >> 15, slot (c ^ m) + (m & delta),
+    # the entry is the slot word's lanes, negated when m is all ones
+    c = np.asarray(codes, dtype=np.uint16).view(np.int16).astype(np.int64)
+    m = c >> 15
+    P = (c ^ m) + (m & delta)
+    assert (P >= 0).all() and (P < slots.size).all()
+    vals = nibbles_signed(slots[P])
+    return np.where(m[:, None] == -1, -vals, vals)
+
+
+def test_e8_slot_codes_decode_every_index():
+    st, pack = build(e8.codebook_fp16_bits())
+    assert st == 0
+    hdr, slots, code_of, index_of = slot_tables(pack, 65536)
+    assert hdr[1] == 5                                # pack format
+    # 28,440 negation pairs share slots: delta = 32768 - 28440; the 8,656 entries
+    # without a partner (origin, the 8,655 of norm^2 12) fill both lone regions
+    assert hdr[6] == 32768 - 28440 and hdr[5] == 32768 + 4328
+    assert hdr[5] <= LDS_BUDGET_DWORDS
+    assert np.array_equal(np.sort(code_of), np.arange(65536))   # a bijection
+    assert np.array_equal(index_of[code_of], np.arange(65536))   # index_of inverts code_of
+    t = (2 * e8.codebook()).astype(np.int64)
+    assert np.array_equal(decode_codes(slots, int(hdr[6]), code_of), t)
+
+
+def test_slot_codes_of_negation_pairs_share_a_slot():
+    st, pack = build(e8.codebook_fp16_bits())
+    hdr, slots, code_of, index_of = slot_tables(pack, 65536)
+    cb = (2 * e8.codebook()).astype(np.int64)
+    # idx 1 = (-1,-1,0,...) and idx 240 = (1,1,0,...) are negatives (hand pins)
+    assert np.array_equal(cb[1], -cb[240])
+    c1, c240 = int(code_of[1]), int(code_of[240])
+    assert (c1 >= 32768) != (c240 >= 32768)           # one plain, one complemented
+    s = lambda c: (np.int16(np.uint16(c)) ^ (np.int16(np.uint16(c)) >> 15)) + ((np.int16(np.uint16(c)) >> 15) & int(hdr[6]))
+    assert s(c1) == s(c240)
+    # the origin has no partner and is stored plain
+    assert int(code_of[0]) < 32768
