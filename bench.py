@@ -21,6 +21,9 @@ roofline: at B = 1 each layer call is two kernel launches (fused_decode_kernel,
           calls' bytes / their time.
 prefill: the 2048-token prefill of the SmolLM3-3B gate shape (2048->11008,
           3 bpw), its MFMA matmul timed the same way, in TFLOP/s.
+block_b1: the seven linears of a SmolLM3-3B decoder block (3 bpw, fp16) at B = 1,
+          issued eagerly from Python and replayed from one captured HIP graph; the
+          small layers are launch-bound, and the graph removes the host launch cost.
 cpu_baseline: the fp64 oracle on the step's layers in turn, for >= 10 s of host CPU work.
 """
 
@@ -56,6 +59,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-block", action="store_true")
+    ap.add_argument("--block-steps", type=int, default=500)
     ap.add_argument("--index-format", choices=["slot", "codebook"], default="slot",
                     help="16-bit index arrays as slot codes (default) or as codebook indices")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -213,6 +218,9 @@ def main():
     if not args.no_prefill:
         result["prefill"] = bench_prefill(glq, synth, cb, dev, args, log)
 
+    if not args.no_block:
+        result["block_b1"] = bench_block_graph(glq, synth, cb, dev, args, log)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host_layers, wl, B, log)
 
@@ -276,7 +284,7 @@ def pmc_summary(dirs, copy_bytes):
         "# HBM traffic of one B = 1 call (%s), Devstral-Small-24B MLP decode" % " + ".join(FUSED_KERNEL_NAMES),
         "# commands (from the repository root, after cd /tmp && export TMPDIR=/tmp for the profiler):",
         "#   rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR --output-format csv -- python3 bench.py --steps 3 --warmup 1 "
-        "--no-cpu-baseline --no-prefill",
+        "--no-cpu-baseline --no-prefill --no-block",
         "#   rocprofv3 --pmc WRITE_SIZE -d WRITE_DIR --output-format csv -- (same)",
         "#   rocprofv3 --pmc FETCH_SIZE -d COPY_FETCH_DIR --output-format csv -- python3 bench.py --calibrate-copy %d"
         % copy_bytes,
@@ -370,6 +378,80 @@ def bench_prefill(glq, synth, cb, dev, args, log):
                      "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
                      "flops_per_launch": flops},
+    }
+
+
+def bench_block_graph(glq, synth, cb, dev, args, log):
+    import numpy as np
+    import torch
+
+    wl = synth.WORKLOADS["smollm3_block"]
+    host = [synth.make_layer(sh, wl.resid_bits, wl.seed, k) for k, sh in enumerate(wl.layers)]
+    qs = [glq.QuantizedLayer.from_synth(l, cb) for l in host]
+    if args.index_format == "slot":
+        qs = [q.to_slot_codes() for q in qs]
+    xs = []
+    for k, l in enumerate(host):
+        _, raw = synth.make_x(l.n, 1, wl.act_dtype, wl.seed, k)
+        xs.append(torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.float16))
+    ys = [torch.empty((1, l.m), dtype=torch.float16, device=dev) for l in host]
+    ws = torch.empty(max(glq.linear_workspace_bytes(q, 1) for q in qs), dtype=torch.uint8, device=dev)
+    nbytes = sum(l.index_bytes() + 2 * (l.n + l.m) + l.n_pad + l.m_pad for l in host)
+
+    def block():
+        for k in range(len(qs)):
+            glq.e8rht_linear(qs[k], xs[k], out=ys[k], workspace=ws)
+
+    n = args.block_steps
+    for _ in range(50):
+        block()
+    torch.cuda.synchronize()
+    eager_ref = [y.clone() for y in ys]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        block()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / n
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        block()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            block()
+    torch.cuda.synchronize()
+    for y in ys:
+        y.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(ys, eager_ref))
+    for _ in range(20):
+        g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / n
+    log("bench: SmolLM3 block B=1: eager %.4f ms, graph %.4f ms per block (replay equals eager: %s)" % (
+        eager_ms, graph_ms, same))
+    return {
+        "workload": "SmolLM3-3B decoder block, 7 linears (q, k, v, o 2048-wide; gate, up 2048->11008; down "
+                    "11008->2048), 3 bpw, fp16 activations, B=1; %.1f MB of indices, resident in the 256 MB "
+                    "MALL across iterations" % (sum(l.index_bytes() for l in host) / 1e6),
+        "eager_ms_per_block": round(eager_ms, 5),
+        "graph_ms_per_block": round(graph_ms, 5),
+        "layer_calls_per_s_eager": round(len(host) / (eager_ms * 1e-3), 1),
+        "layer_calls_per_s_graph": round(len(host) / (graph_ms * 1e-3), 1),
+        "graph_speedup": round(eager_ms / graph_ms, 3),
+        "graph_gbs": round(nbytes / (graph_ms * 1e-3) / 1e9, 1),
+        "replay_equals_eager": bool(same),
+        "launches_per_block": 2 * len(host),
     }
 
 
