@@ -96,6 +96,7 @@ class Layer:
     idx1: object             # uint8/uint16 [m_pad, n_pad/8] or None
     wscale: float = WSCALE
     resid_scale: float = RESID_SCALE
+    extra: tuple = ()        # further residual stages (5-8 bpw): (bits, index array, scale) each
 
     @property
     def n(self):
@@ -114,11 +115,28 @@ class Layer:
         return self.shape.m_pad
 
     def index_bytes(self):
-        return self.idx0.nbytes + (0 if self.idx1 is None else self.idx1.nbytes)
+        return self.idx0.nbytes + (0 if self.idx1 is None else self.idx1.nbytes) + sum(e[1].nbytes for e in self.extra)
+
+    @property
+    def bpw(self):
+        return 2 + self.resid_bits // 8 + sum(b // 8 for b, _, _ in self.extra)
+
+    def oracle_extra(self):
+        """The extra stages as the oracle takes them: (index array, bits, scale)."""
+        return tuple((idx, bits, scale) for bits, idx, scale in self.extra)
 
 
-def make_layer(shape, resid_bits, seed, k, rows=None):
+# bpw -> (bits of the first residual stage, bits of the further stages), glq 0.5.1,
+# table "Bit widths"
+RECIPES = {2: (0, ()), 3: (8, ()), 4: (16, ()), 5: (16, (8,)), 6: (16, (16,)), 7: (16, (16, 8)), 8: (16, (16, 16))}
+
+
+def make_layer(shape, resid_bits, seed, k, rows=None, extra_bits=()):
     """Draw layer k of a workload with the given seed.
+
+    extra_bits: bits (8 or 16) of residual stages 2, 3 (5-8 bpw), drawn after the
+    other arrays; stage j is scaled by RESID_SCALE ** j (a reading: each stage
+    refines the previous one's error by the same factor).
 
     rows: optionally keep only the first `rows` rows of the index arrays, used
     nowhere on the measured path (the draw order is unchanged).
@@ -136,7 +154,13 @@ def make_layer(shape, resid_bits, seed, k, rows=None):
         idx1 = rng.integers(0, 65536, size=gshape, dtype=np.uint16)
     elif resid_bits != 0:
         raise ValueError("resid_bits must be 0, 8 or 16")
-    return Layer(shape, resid_bits, sign_in, sign_out, idx0, idx1)
+    extra = []
+    for j, bits in enumerate(extra_bits):
+        if bits not in (8, 16) or resid_bits == 0:
+            raise ValueError("extra stages are 8 or 16 bits, after a residual stage")
+        idx = rng.integers(0, 256 if bits == 8 else 65536, size=gshape, dtype=np.uint8 if bits == 8 else np.uint16)
+        extra.append((bits, idx, float(np.float32(RESID_SCALE ** (j + 2)))))
+    return Layer(shape, resid_bits, sign_in, sign_out, idx0, idx1, extra=tuple(extra))
 
 
 def round_to_dtype(x64, dtype):
@@ -172,7 +196,13 @@ def workload_layers(key):
     return [(k, s) for k, s in enumerate(w.layers)]
 
 
-def random_layer(n, m, resid_bits, seed, n_pad=None, m_pad=None):
+def random_layer(n, m, resid_bits, seed, n_pad=None, m_pad=None, extra_bits=()):
     """A layer of arbitrary shape (tests of ragged and tiny shapes)."""
     shape = LayerShape("t", n, m, n_pad or next_pow2(max(n, 8)), m_pad or next_pow2(max(m, 8)))
-    return make_layer(shape, resid_bits, seed, 0)
+    return make_layer(shape, resid_bits, seed, 0, extra_bits=extra_bits)
+
+
+def recipe_layer(n, m, bpw, seed, n_pad=None, m_pad=None):
+    """A layer of a 2-8 bpw recipe of the "Bit widths" table."""
+    resid_bits, extra_bits = RECIPES[bpw]
+    return random_layer(n, m, resid_bits, seed, n_pad, m_pad, extra_bits)

@@ -146,3 +146,78 @@ def test_workload_shapes():
         (2048, 2048), (2048, 512), (2048, 512), (2048, 2048), (2048, 16384), (2048, 16384), (16384, 2048)]
     assert [(l.n_pad, l.m_pad) for l in w["devstral_mlp"].layers] == [(8192, 32768), (8192, 32768), (32768, 8192)]
     assert (w["smollm2_up"].layers[0].n_pad, w["smollm2_up"].layers[0].m_pad) == (1024, 4096)
+
+
+# ---- 5-8 bpw: further residual stages ("Bit widths") ---------------------------------
+def test_recipe_table_matches_bit_widths():
+    # 16-bit primary + the stages' bits = 8 bpw bits per 8-weight group
+    for bpw, (r, extra) in synth.RECIPES.items():
+        assert 16 + r + sum(extra) == 8 * bpw
+    assert synth.RECIPES[5] == (16, (8,)) and synth.RECIPES[7] == (16, (16, 8))
+
+
+def test_dequant_hand_group_multistage():
+    with open(os.path.join(HERE, "golden", "dequant_multistage_group.txt")) as f:
+        rows = [line.split() for line in f if line.strip() and not line.startswith("#")]
+    assert len(rows) == 4
+    s = float(np.float32(0.02))
+    for p in rows:
+        bpw, idx = int(p[0]), p[1:5]
+        want = np.array([float(t) for t in p[5:]])
+        r, extra_bits = synth.RECIPES[bpw]
+        i = lambda v, bits: np.array([[int(v)]], dtype=np.uint8 if bits == 8 else np.uint16)
+        extra = [(i(idx[2 + j], b), b, 0.25 ** (j + 2)) for j, b in enumerate(extra_bits)]
+        w = glq.dequant_rows(i(idx[0], 16), i(idx[1], r), r, 0.02, 0.25, extra=extra)
+        np.testing.assert_array_equal(w[0], want * s)
+        w32 = glq.dequant_fp32(i(idx[0], 16), i(idx[1], r), r, 0.02, 0.25, extra=extra)
+        assert np.array_equal(w32[0], (want * s).astype(np.float32))
+
+
+@pytest.mark.parametrize("bpw", [5, 6, 7, 8])
+def test_dequant_fp32_multistage_single_rounding(bpw):
+    layer = synth.recipe_layer(64, 16, bpw, seed=30 + bpw)
+    ex = layer.oracle_extra()
+    w32 = glq.dequant_fp32(layer.idx0, layer.idx1, layer.resid_bits, 0.02, 0.25, extra=ex)
+    c0 = e8.codebook()
+    s = Fraction(float(np.float32(0.02)))
+    rng = np.random.default_rng(bpw)
+    for _ in range(200):
+        o, k = int(rng.integers(16)), int(rng.integers(64))
+        g, j = divmod(k, 8)
+        e = Fraction(c0[layer.idx0[o, g]][j]) + Fraction(1, 4) * Fraction(
+            e8.residual_codebook(layer.resid_bits)[layer.idx1[o, g]][j])
+        for st, (idx, bits, scale) in enumerate(ex):
+            assert Fraction(scale) == Fraction(1, 4 ** (st + 2))
+            e += Fraction(scale) * Fraction(e8.residual_codebook(bits)[idx[o, g]][j])
+        exact = s * e
+        got = Fraction(float(w32[o, k]))
+        up = Fraction(float(np.nextafter(w32[o, k], np.float32(np.inf))))
+        dn = Fraction(float(np.nextafter(w32[o, k], np.float32(-np.inf))))
+        assert abs(got - exact) <= abs(up - exact) and abs(got - exact) <= abs(dn - exact)
+
+
+@pytest.mark.parametrize("bpw", [5, 8])
+def test_multistage_fused_equals_dense_conjugated(bpw):
+    layer = synth.recipe_layer(100, 70, bpw, seed=40 + bpw, n_pad=128, m_pad=128)
+    x = np.random.default_rng(bpw).standard_normal((3, 100))
+    y = glq.linear(x, layer.sign_in, layer.sign_out, layer.n_pad, layer.m, layer.idx0, layer.idx1,
+                   layer.resid_bits, layer.wscale, layer.resid_scale, extra=layer.oracle_extra())
+    w = glq.dequant_rows(layer.idx0, layer.idx1, layer.resid_bits, layer.wscale, layer.resid_scale,
+                         extra=layer.oracle_extra())
+    h_n, h_m = scipy.linalg.hadamard(128), scipy.linalg.hadamard(128)
+    dense = (np.diag(layer.sign_out.astype(float)) @ h_m @ w @ h_n @ np.diag(layer.sign_in.astype(float))
+             / np.sqrt(128 * 128))[:70, :100]
+    want = x @ dense.T
+    np.testing.assert_allclose(y, want, rtol=0, atol=1e-12 * max(1.0, np.abs(want).max()))
+
+
+def test_multistage_zero_indices_give_zero_output():
+    layer = synth.recipe_layer(64, 64, 8, seed=5)
+    layer.idx0[:] = 0
+    layer.idx1[:] = 0
+    for _, idx, _ in layer.extra:
+        idx[:] = 0
+    x = np.random.default_rng(0).standard_normal((2, 64))
+    y = glq.linear(x, layer.sign_in, layer.sign_out, layer.n_pad, layer.m, layer.idx0, layer.idx1,
+                   layer.resid_bits, layer.wscale, layer.resid_scale, extra=layer.oracle_extra())
+    assert np.array_equal(y, np.zeros((2, 64)))
