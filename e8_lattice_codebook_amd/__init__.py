@@ -83,7 +83,8 @@ class QuantizedLayer:
     """Device copy of one layer (signs, index arrays) plus its glq_layer descriptor."""
 
     def __init__(self, n, m, n_pad, m_pad, resid_bits, sign_in, sign_out, idx0, idx1, codebooks,
-                 wscale=0.02, resid_scale=0.25, device=None, index_format=INDEX_CODEBOOK):
+                 wscale=0.02, resid_scale=0.25, device=None, index_format=INDEX_CODEBOOK, extra=()):
+        """extra: further residual stages of 5-8 bpw, (bits, index array, scale) each."""
         device = torch.device(device) if device is not None else codebooks.device
         self.n, self.m, self.n_pad, self.m_pad = int(n), int(m), int(n_pad), int(m_pad)
         self.resid_bits = int(resid_bits)
@@ -99,30 +100,44 @@ class QuantizedLayer:
         self.codebooks = codebooks
         self.device = device
         self.index_format = int(index_format)
+        self.extra = tuple((int(b), _to_dev(i, torch.uint8 if int(b) == 8 else torch.int16, device), float(sc))
+                           for b, i, sc in extra)
         self.desc = GlqLayer(self.n, self.n_pad, self.m, self.m_pad, self.resid_bits, self.wscale, self.resid_scale,
                              self.sign_in.data_ptr(), self.sign_out.data_ptr(), self.idx0.data_ptr(),
                              0 if self.idx1 is None else self.idx1.data_ptr(), codebooks.primary.data_ptr(),
                              0 if resid_bits == 0 else codebooks.residual(resid_bits).data_ptr(), self.index_format)
+        self.desc.n_extra = len(self.extra)
+        for k, (b, i, sc) in enumerate(self.extra):
+            self.desc.extra_bits[k] = b
+            self.desc.extra_scale[k] = sc
+            self.desc.extra_idx[k] = i.data_ptr()
+            if b == 8:
+                self.desc.cb8_pack = codebooks.resid8.data_ptr()
 
     @classmethod
     def from_synth(cls, layer, codebooks, device=None):
         return cls(layer.n, layer.m, layer.n_pad, layer.m_pad, layer.resid_bits, layer.sign_in, layer.sign_out,
-                   layer.idx0, layer.idx1, codebooks, layer.wscale, layer.resid_scale, device)
+                   layer.idx0, layer.idx1, codebooks, layer.wscale, layer.resid_scale, device,
+                   extra=getattr(layer, "extra", ()))
 
     def to_slot_codes(self):
         """The same layer with its 16-bit index arrays relabelled as slot codes
-        (glq_slot_codes): idx0, and idx1 when the residual stage is 16-bit."""
+        (glq_slot_codes): idx0, idx1 when the residual stage is 16-bit, and the
+        16-bit further stages."""
         if self.index_format == INDEX_SLOT:
             return self
         idx0 = slot_codes(self.idx0, self.codebooks)
         idx1 = self.idx1
         if self.resid_bits == 16:
             idx1 = slot_codes(self.idx1, self.codebooks)
+        extra = tuple((b, slot_codes(i, self.codebooks) if b == 16 else i, sc) for b, i, sc in self.extra)
         return QuantizedLayer(self.n, self.m, self.n_pad, self.m_pad, self.resid_bits, self.sign_in, self.sign_out,
-                              idx0, idx1, self.codebooks, self.wscale, self.resid_scale, self.device, INDEX_SLOT)
+                              idx0, idx1, self.codebooks, self.wscale, self.resid_scale, self.device, INDEX_SLOT,
+                              extra=extra)
 
     def index_bytes(self):
-        return self.idx0.numel() * 2 + (0 if self.idx1 is None else self.idx1.numel() * self.idx1.element_size())
+        return (self.idx0.numel() * 2 + (0 if self.idx1 is None else self.idx1.numel() * self.idx1.element_size())
+                + sum(i.numel() * i.element_size() for _, i, _ in self.extra))
 
 
 def _to_dev(a, dtype, device):

@@ -26,6 +26,8 @@ class GlqLayer(ctypes.Structure):
         ("resid_bits", c_i32), ("wscale", c_f32), ("resid_scale", c_f32),
         ("sign_in", c_vp), ("sign_out", c_vp), ("idx0", c_vp), ("idx1", c_vp),
         ("cb_pack", c_vp), ("cb2_pack", c_vp), ("index_format", c_i32),
+        ("n_extra", c_i32), ("extra_bits", c_i32 * 2), ("extra_scale", c_f32 * 2), ("extra_idx", c_vp * 2),
+        ("cb8_pack", c_vp),
     ]
 
 

@@ -30,9 +30,67 @@ glq_status check_layer(const glq_layer* L, bool need_signs) {
   if (!aligned(L->idx0, 16) || !aligned(L->cb_pack, 256)) return GLQ_ERR_ALIGN;
   if (L->resid_bits != 0 && (!aligned(L->idx1, 16) || !aligned(L->cb2_pack, 256))) return GLQ_ERR_ALIGN;
   if (L->index_format != GLQ_INDEX_CODEBOOK && L->index_format != GLQ_INDEX_SLOT) return GLQ_ERR_RECIPE;
+  // further residual stages: the 5-8 bpw rows of "Bit widths"
+  if (L->n_extra < 0 || L->n_extra > 2) return GLQ_ERR_RECIPE;
+  if (L->n_extra > 0) {
+    if (L->resid_bits != 16 || L->cb2_pack != L->cb_pack) return GLQ_ERR_RECIPE;
+    if (L->n_extra == 2 && L->extra_bits[0] != 16) return GLQ_ERR_RECIPE;
+    for (int k = 0; k < L->n_extra; ++k) {
+      if (L->extra_bits[k] != 8 && L->extra_bits[k] != 16) return GLQ_ERR_RECIPE;
+      if (!(L->extra_scale[k] == L->extra_scale[k]) || L->extra_scale[k] == 0.0f) return GLQ_ERR_RECIPE;
+      if (!L->extra_idx[k]) return GLQ_ERR_NULL;
+      if (!aligned(L->extra_idx[k], 16)) return GLQ_ERR_ALIGN;
+      if (L->extra_bits[k] == 8 && !L->cb8_pack) return GLQ_ERR_NULL;
+      if (L->extra_bits[k] == 8 && !aligned(L->cb8_pack, 256)) return GLQ_ERR_ALIGN;
+    }
+  }
   // slot codes of a 16-bit residual stage name entries of the primary pack
   if (L->index_format == GLQ_INDEX_SLOT && L->resid_bits == 16 && L->cb2_pack != L->cb_pack) return GLQ_ERR_RECIPE;
   return GLQ_OK;
+}
+
+// A 5-8 bpw layer as two passes shaped like 2-4 bpw layers whose partial outputs
+// add (every kernel then needs only an accumulating store): pass a is the primary
+// with one residual stage, pass b the remaining stages with their scale folded
+// into wscale.
+//   16+16+8:    a = (0, 2 [8 bit]),  b = (1)
+//   16+16+16:   a = (0, 1),          b = (2)
+//   16+16+16+x: a = (0, 1),          b = (2, 3 [x bit])
+struct Passes {
+  glq_layer a, b;
+  bool two;
+};
+
+Passes split_passes(const glq_layer& L) {
+  Passes P{L, L, false};
+  P.a.n_extra = P.b.n_extra = 0;
+  if (L.n_extra == 0) return P;
+  P.two = true;
+  if (L.n_extra == 1 && L.extra_bits[0] == 8) {
+    P.a.idx1 = L.extra_idx[0];
+    P.a.resid_bits = 8;
+    P.a.resid_scale = L.extra_scale[0];
+    P.a.cb2_pack = L.cb8_pack;
+    P.b.idx0 = static_cast<const uint16_t*>(L.idx1);
+    P.b.idx1 = nullptr;
+    P.b.resid_bits = 0;
+    P.b.cb2_pack = nullptr;
+    P.b.wscale = L.wscale * L.resid_scale;
+  } else if (L.n_extra == 1) {
+    P.b.idx0 = static_cast<const uint16_t*>(L.extra_idx[0]);
+    P.b.idx1 = nullptr;
+    P.b.resid_bits = 0;
+    P.b.cb2_pack = nullptr;
+    P.b.wscale = L.wscale * L.extra_scale[0];
+  } else {
+    P.b.idx0 = static_cast<const uint16_t*>(L.extra_idx[0]);
+    P.b.idx1 = L.extra_idx[1];
+    P.b.resid_bits = L.extra_bits[1];
+    P.b.resid_scale = L.extra_scale[1] / L.extra_scale[0];
+    P.b.cb2_pack = L.extra_bits[1] == 8 ? L.cb8_pack : L.cb_pack;
+    P.b.wscale = L.wscale * L.extra_scale[0];
+  }
+  return P;
 }
 
 // Linear workspace: the buffers of the B = 1 two-launch path or of the staged path.
@@ -89,12 +147,24 @@ LinearWs linear_ws(const glq_layer& L, int64_t B) {
 
 // decode matmul from fp32 u: quantize into uq (LDS kernel) or gather from global
 hipError_t decode_matmul(const glq_layer& L, const float* u, int64_t B, void* uq, float* z, hipStream_t stream) {
-  if (decode_uses_lds(L)) {
+  if (decode_uses_lds(L)) {  // always for 5-8 bpw (their 16-bit stages use the primary pack)
+    const Passes P = split_passes(L);
     hipError_t e = launch_quant_u(u, B, L.n_pad, uq, stream);
     if (e != hipSuccess) return e;
-    return launch_gemv_lds(L, uq, B, z, stream);
+    e = launch_gemv_lds(P.a, uq, B, z, stream);
+    if (e != hipSuccess || !P.two) return e;
+    return launch_gemv_lds(P.b, uq, B, z, stream, true);
   }
   return launch_gemv(L, u, B, z, stream);
+}
+
+// prefill matmul of every pass: u16 tiled for the LDS kernel, else row-major
+hipError_t prefill_matmul(const glq_layer& L, const half_t* u16, int64_t M, bool tiled, float* z,
+                          hipStream_t stream) {
+  const Passes P = split_passes(L);
+  hipError_t e = tiled ? launch_gemm_lds(P.a, u16, M, true, z, stream) : launch_gemm(P.a, u16, M, z, stream);
+  if (e != hipSuccess || !P.two) return e;
+  return tiled ? launch_gemm_lds(P.b, u16, M, true, z, stream, true) : launch_gemm(P.b, u16, M, z, stream, true);
 }
 
 template <class T>
@@ -114,7 +184,7 @@ const char* glq_status_string(glq_status s) {
     case GLQ_ERR_NULL: return "a required pointer is NULL";
     case GLQ_ERR_SHAPE: return "a size is out of range or sizes disagree";
     case GLQ_ERR_DTYPE: return "dtype not supported by this entry point";
-    case GLQ_ERR_RECIPE: return "resid_bits must be 0, 8 or 16";
+    case GLQ_ERR_RECIPE: return "not a recipe of the bit-width table, or a bad index_format";
     case GLQ_ERR_ALIGN: return "a pointer is not aligned as documented";
     case GLQ_ERR_WORKSPACE: return "workspace missing or too small";
     case GLQ_ERR_HIP: return "a HIP launch failed";
@@ -208,7 +278,7 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
   const size_t need = matmul_ws_bytes(*layer, B);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GLQ_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 256)) return GLQ_ERR_ALIGN;
-  if (B > kDecodeMaxB) return from_hip(launch_gemm(*layer, static_cast<const half_t*>(u), B, z_parts, stream));
+  if (B > kDecodeMaxB) return from_hip(prefill_matmul(*layer, static_cast<const half_t*>(u), B, false, z_parts, stream));
   return from_hip(decode_matmul(*layer, static_cast<const float*>(u), B, workspace, z_parts, stream));
 }
 
@@ -242,7 +312,7 @@ glq_status glq_e8_matmul_prefill(const glq_layer* layer, const void* u16, int64_
   if (!u16 || !z) return GLQ_ERR_NULL;
   if (B < 1 || B > int64_t(1) << 31 || !gemm_lds_supported(*layer)) return GLQ_ERR_SHAPE;
   if (!aligned(u16, 16)) return GLQ_ERR_ALIGN;
-  return from_hip(launch_gemm_lds(*layer, static_cast<const half_t*>(u16), B, true, z, stream));
+  return from_hip(prefill_matmul(*layer, static_cast<const half_t*>(u16), B, true, z, stream));
 }
 
 size_t glq_e8rht_linear_workspace_bytes(const glq_layer* layer, int64_t B) {
@@ -261,7 +331,13 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
   if (!workspace || workspace_bytes < w.total) return GLQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return GLQ_ERR_ALIGN;
   const glq_layer& L = *layer;
-  if (w.fused) return from_hip(launch_fused_decode(L, x, x_dt, y, y_dt, at<float>(workspace, w.z_off), stream));
+  if (w.fused) {
+    const Passes P = split_passes(L);
+    float* zp = at<float>(workspace, w.z_off);
+    if (!P.two) return from_hip(launch_fused_decode(L, x, x_dt, y, y_dt, zp, stream));
+    if (launch_fused_decode(P.a, x, x_dt, y, y_dt, zp, stream, 1) != hipSuccess) return GLQ_ERR_HIP;
+    return from_hip(launch_fused_decode(P.b, x, x_dt, y, y_dt, zp, stream, 2));
+  }
   const int ln = log2_exact(L.n_pad), lm = log2_exact(L.m_pad);
   hipError_t e;
   float* z = at<float>(workspace, w.z_off);
@@ -276,11 +352,11 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
     if (gemm_lds_supported(L)) {  // u in the matmul's fragment order
       e = launch_rht_in_tiled(x, x_dt, B, L.n, ln, L.sign_in, u, at<float>(workspace, w.rin_off), stream);
       if (e != hipSuccess) return GLQ_ERR_HIP;
-      e = launch_gemm_lds(L, u, B, true, z, stream);
+      e = prefill_matmul(L, u, B, true, z, stream);
     } else {
       e = launch_rht_in(x, x_dt, B, L.n, ln, L.sign_in, u, GLQ_F16, at<float>(workspace, w.rin_off), stream);
       if (e != hipSuccess) return GLQ_ERR_HIP;
-      e = launch_gemm(L, u, B, z, stream);
+      e = prefill_matmul(L, u, B, false, z, stream);
     }
     if (e != hipSuccess) return GLQ_ERR_HIP;
   }

@@ -49,6 +49,16 @@ __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float* v) {
   *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Further residual stages (5-8 bpw): added in order, e = RN32(e + s_k c_k).
+struct ExtraStages {
+  int n;
+  const void* idx[2];
+  int bits[2];
+  float scale[2];
+  const int8_t* tab[2];   // int8 table of the stage's pack
+  const uint16_t* map;    // code -> index of 16-bit stages with slot codes, else null
+};
+
 // map0 / map1: the pack's code -> index tables when the 16-bit stages hold slot
 // codes, else null
 template <class WT, int RESID>
@@ -56,7 +66,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint16_t* __restrict
                                                       const int8_t* __restrict__ cb0, const int8_t* __restrict__ cb1,
                                                       const uint16_t* __restrict__ map0,
                                                       const uint16_t* __restrict__ map1, float s, float sr,
-                                                      int64_t groups, WT* __restrict__ w) {
+                                                      int64_t groups, WT* __restrict__ w, ExtraStages x) {
   const int64_t g = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (g >= groups) return;
   const uint32_t i0 = map0 ? uint32_t(map0[idx0[g]]) : uint32_t(idx0[g]);
@@ -76,6 +86,17 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint16_t* __restrict
     for (int j = 0; j < 4; ++j) {
       e[j] = fmaf(sr, 0.5f * i8_at(c1.x, j), e[j]);
       e[j + 4] = fmaf(sr, 0.5f * i8_at(c1.y, j), e[j + 4]);
+    }
+  }
+  for (int k = 0; k < x.n; ++k) {
+    uint32_t ik = x.bits[k] == 8 ? uint32_t(static_cast<const uint8_t*>(x.idx[k])[g])
+                                 : uint32_t(static_cast<const uint16_t*>(x.idx[k])[g]);
+    if (x.bits[k] == 16 && x.map) ik = x.map[ik];
+    const uint2 ck = *reinterpret_cast<const uint2*>(x.tab[k] + size_t(ik) * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      e[j] = fmaf(x.scale[k], 0.5f * i8_at(ck.x, j), e[j]);
+      e[j + 4] = fmaf(x.scale[k], 0.5f * i8_at(ck.y, j), e[j + 4]);
     }
   }
   float v[8];
@@ -100,18 +121,27 @@ hipError_t dequant_typed(const glq_layer& L, void* w, hipStream_t stream) {
       map1 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(L.cb2_pack) +
                                                pack_index_of_offset(GLQ_CODEBOOK_ENTRIES));
   }
+  ExtraStages x{};
+  x.n = L.n_extra;
+  x.map = map0;
+  for (int k = 0; k < L.n_extra && k < 2; ++k) {
+    x.idx[k] = L.extra_idx[k];
+    x.bits[k] = L.extra_bits[k];
+    x.scale[k] = L.extra_scale[k];
+    x.tab[k] = static_cast<const int8_t*>(L.extra_bits[k] == 8 ? L.cb8_pack : L.cb_pack) + pack_i8_offset();
+  }
   switch (L.resid_bits) {
     case 0:
       hipLaunchKernelGGL((dequant_kernel<WT, 0>), grid, block, 0, stream, L.idx0, L.idx1, cb0, cb1, map0, map1,
-                         L.wscale, L.resid_scale, groups, out);
+                         L.wscale, L.resid_scale, groups, out, x);
       break;
     case 8:
       hipLaunchKernelGGL((dequant_kernel<WT, 8>), grid, block, 0, stream, L.idx0, L.idx1, cb0, cb1, map0, map1,
-                         L.wscale, L.resid_scale, groups, out);
+                         L.wscale, L.resid_scale, groups, out, x);
       break;
     default:
       hipLaunchKernelGGL((dequant_kernel<WT, 16>), grid, block, 0, stream, L.idx0, L.idx1, cb0, cb1, map0, map1,
-                         L.wscale, L.resid_scale, groups, out);
+                         L.wscale, L.resid_scale, groups, out, x);
       break;
   }
   return hipGetLastError();

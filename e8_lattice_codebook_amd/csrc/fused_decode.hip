@@ -70,6 +70,7 @@ struct FusedArgs {
   float sc_scale;   // 1 / (sqrt(n_pad) kUqMax): u = t_H / sqrt(n_pad), scale = max|t_H| * sc_scale
   float out_scale;  // s / 2 (codebook entries are held doubled)
   float sr;         // residual scale
+  int accumulate;   // add H_R of the row block to z_parts (second pass of a 5-8 bpw layer)
 };
 
 __device__ __forceinline__ float x_at(const void* x, int dt, int64_t j) {
@@ -84,7 +85,8 @@ __device__ __forceinline__ float sign_f(uint32_t w, int k) { return float(int8_t
 
 struct StoreZ {  // element i of a workgroup's row block -> its place in z_parts
   float* p;
-  __device__ void operator()(int64_t, int64_t i, float v) const { p[i] = v; }
+  int acc;
+  __device__ void operator()(int64_t, int64_t i, float v) const { p[i] = acc ? p[i] + v : v; }
 };
 
 struct StoreLds {  // element i of the row -> its swizzled LDS position
@@ -156,7 +158,7 @@ __device__ __forceinline__ void x_accumulate(const XRaw& r, int dt, bool neg, fl
 // l E .. l E + E - 1 (bits below log2 E in registers, the six lane bits by
 // shuffles), then stores them to p with 16-byte stores.
 template <int E>
-__device__ __forceinline__ void wave_block_transform(const float* rowbuf, float* p, int lane) {
+__device__ __forceinline__ void wave_block_transform(const float* rowbuf, float* p, int lane, int acc) {
   float v[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) v[e] = rowbuf[swz(lane * E + e)];
@@ -171,8 +173,15 @@ __device__ __forceinline__ void wave_block_transform(const float* rowbuf, float*
     }
   }
 #pragma unroll
-  for (int e = 0; e < E; e += 4)
-    *reinterpret_cast<float4*>(p + lane * E + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+  for (int e = 0; e < E; e += 4) {
+    float4* q = reinterpret_cast<float4*>(p + lane * E + e);
+    float4 w = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+    if (acc) {
+      const float4 o = *q;
+      w = make_float4(o.x + w.x, o.y + w.y, o.z + w.z, o.w + w.w);
+    }
+    *q = w;
+  }
 }
 
 // Butterfly of the chunk transform on lane bit k of the wave (column bit k + 2:
@@ -427,13 +436,13 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
       __syncthreads();
       if (tid < 64) {
         switch (a.lr) {
-          case 8: wave_block_transform<4>(rowbuf, zb, tid); break;
-          case 9: wave_block_transform<8>(rowbuf, zb, tid); break;
-          default: wave_block_transform<16>(rowbuf, zb, tid); break;
+          case 8: wave_block_transform<4>(rowbuf, zb, tid, a.accumulate); break;
+          case 9: wave_block_transform<8>(rowbuf, zb, tid, a.accumulate); break;
+          default: wave_block_transform<16>(rowbuf, zb, tid, a.accumulate); break;
         }
       }
     } else {
-      fwht_lds_passes<StoreZ, 4>(StoreZ{zb}, 0, a.lr, 0, rowbuf);
+      fwht_lds_passes<StoreZ, 4>(StoreZ{zb, a.accumulate}, 0, a.lr, 0, rowbuf);
     }
   }
 
@@ -666,7 +675,7 @@ size_t fused_decode_z_bytes(const glq_layer& L) {
 }
 
 hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt, void* y, glq_dtype y_dt,
-                               float* z_parts, hipStream_t stream) {
+                               float* z_parts, hipStream_t stream, int pass) {
   const FusedPlan p = fused_plan(L);
   FusedArgs a;
   a.x = x;
@@ -699,6 +708,7 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
   a.sc_scale = float(1.0 / (sqrt(double(L.n_pad)) * double(kUqMax)));
   a.out_scale = 0.5f * L.wscale;
   a.sr = L.resid_scale;
+  a.accumulate = pass == 2;
   const dim3 grid(unsigned(p.splits * p.wgs_per_split)), block(kThreads);
   const bool full = p.lpr_log2 == 6;
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, a); };
@@ -717,7 +727,7 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
     default: go(fused_decode_kernel<16, true, true>); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || pass == 1) return e;
   BlocksArgs b;
   b.z = z_parts;
   b.sign = L.sign_out;

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const half_t* __restrict__ A,
                                                    const void* __restrict__ idx1v, const int8_t* __restrict__ cb0,
                                                    const int8_t* __restrict__ cb1,
                                                    const uint16_t* __restrict__ map, float s, float sr,
-                                                   float* __restrict__ z) {
+                                                   float* __restrict__ z, int accumulate) {
   __shared__ __attribute__((aligned(16))) half_t As[BM * LDK];
   __shared__ __attribute__((aligned(16))) half_t Bs[BN * LDK];
   __shared__ uint2 res_tab[RESID == 8 ? 256 : 1];
@@ -127,7 +127,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const half_t* __restrict__ A,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t row = m0 + wm * 64 + mi * 16 + (lane >> 4) * 4 + i;
-        if (row < M && col < m_pad) z[row * m_pad + col] = acc[mi][ni][i] * s;
+        if (row < M && col < m_pad) {
+          float* zo = z + row * m_pad + col;
+          *zo = accumulate ? *zo + acc[mi][ni][i] * s : acc[mi][ni][i] * s;
+        }
       }
     }
   }
@@ -135,8 +138,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const half_t* __restrict__ A,
 
 }  // namespace
 
-hipError_t launch_gemm(const glq_layer& L, const half_t* u16, int64_t M, float* z, hipStream_t stream) {
-  if (gemm_lds_supported(L)) return launch_gemm_lds(L, u16, M, false, z, stream);
+hipError_t launch_gemm(const glq_layer& L, const half_t* u16, int64_t M, float* z, hipStream_t stream,
+                       bool accumulate) {
+  if (gemm_lds_supported(L)) return launch_gemm_lds(L, u16, M, false, z, stream, accumulate);
   const dim3 grid(unsigned((L.m_pad + BN - 1) / BN), unsigned((M + BM - 1) / BM)), block(256);
   const int8_t* cb0 = static_cast<const int8_t*>(L.cb_pack) + pack_i8_offset();
   const int8_t* cb1 = L.cb2_pack ? static_cast<const int8_t*>(L.cb2_pack) + pack_i8_offset() : nullptr;
@@ -148,15 +152,15 @@ hipError_t launch_gemm(const glq_layer& L, const half_t* u16, int64_t M, float* 
   switch (L.resid_bits) {
     case 0:
       hipLaunchKernelGGL((gemm_kernel<0>), grid, block, 0, stream, u16, M, L.n_pad, L.m_pad, L.idx0, L.idx1, cb0,
-                         cb1, map, L.wscale, L.resid_scale, z);
+                         cb1, map, L.wscale, L.resid_scale, z, int(accumulate));
       break;
     case 8:
       hipLaunchKernelGGL((gemm_kernel<8>), grid, block, 0, stream, u16, M, L.n_pad, L.m_pad, L.idx0, L.idx1, cb0,
-                         cb1, map, L.wscale, L.resid_scale, z);
+                         cb1, map, L.wscale, L.resid_scale, z, int(accumulate));
       break;
     default:
       hipLaunchKernelGGL((gemm_kernel<16>), grid, block, 0, stream, u16, M, L.n_pad, L.m_pad, L.idx0, L.idx1, cb0,
-                         cb1, map, L.wscale, L.resid_scale, z);
+                         cb1, map, L.wscale, L.resid_scale, z, int(accumulate));
       break;
   }
   return hipGetLastError();

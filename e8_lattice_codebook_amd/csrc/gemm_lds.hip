@@ -59,6 +59,7 @@ struct GemmArgs {
   int out_tiles, tok_tiles, tiles;
   float scale;                // s / 2
   float sr;
+  int accumulate;             // add to z (second pass of a 5-8 bpw layer)
 };
 
 // fp16 (2c_0 .. 2c_7) of a slot word w, negated (complement) when m = ~0
@@ -290,7 +291,8 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
         if (t < a.M) {
           float* zr = a.z + t * a.m_pad + o_w + r16;
 #pragma unroll
-          for (int ni = 0; ni < kNB; ++ni) zr[16 * ni] = acc[mi][ni][i] * a.scale;
+          for (int ni = 0; ni < kNB; ++ni)
+            zr[16 * ni] = a.accumulate ? zr[16 * ni] + acc[mi][ni][i] * a.scale : acc[mi][ni][i] * a.scale;
         }
       }
     }
@@ -323,7 +325,7 @@ bool gemm_lds_supported(const glq_layer& L) {
 size_t tiled_u_bytes(int64_t M, int64_t n_pad) { return size_t((M + 15) / 16) * 16 * size_t(n_pad) * 2; }
 
 hipError_t launch_gemm_lds(const glq_layer& L, const half_t* u16, int64_t M, bool tiled, float* z,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool accumulate) {
   GemmArgs a;
   a.u = u16;
   a.idx0 = L.idx0;
@@ -344,6 +346,7 @@ hipError_t launch_gemm_lds(const glq_layer& L, const half_t* u16, int64_t M, boo
   a.tiles = a.out_tiles * a.tok_tiles;
   a.scale = 0.5f * L.wscale;
   a.sr = L.resid_scale;
+  a.accumulate = int(accumulate);
   const int grid = a.tiles < cus_of_device() ? a.tiles : cus_of_device();
 #define GLQ_LAUNCH(R, T)                                                                                    \
   do {                                                                                                      \

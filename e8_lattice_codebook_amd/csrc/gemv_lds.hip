@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
     const uint32_t* __restrict__ img0, const uint32_t* __restrict__ res_slots, const uint32_t* __restrict__ uq_dig,
     const int32_t* __restrict__ uq_sum, const float* __restrict__ uq_scale, int B, int G, int m_pad, int lpr_log2,
     int bg_log2, int nblk, int units_per_wave, int row_steps, int splits, float out_scale, float sr,
-    float* __restrict__ z_parts) {
+    float* __restrict__ z_parts, int accumulate) {
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsDwords];
   const int tid = threadIdx.x;
   load_image_1024<RESID>(lds, pack0_hdr, img0, res_slots, tid, CODES ? kHdrSlotDwords : 3);
@@ -175,7 +175,10 @@ __global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
       } else {
         v = lane_reduce(v, lpr);
       }
-      if (valid && lane_in_row == LPR - 1 && b < B) z_parts[(split * B + b) * m_pad + o] = v * out_scale;
+      if (valid && lane_in_row == LPR - 1 && b < B) {
+        float* zo = z_parts + (split * B + b) * m_pad + o;
+        *zo = accumulate ? *zo + v * out_scale : v * out_scale;
+      }
     }
   }
 }
@@ -217,7 +220,8 @@ int device_cus() {
 
 
 template <int NB, int GL, int RESID, bool FULL, bool CODES>
-hipError_t launch_t(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream) {
+hipError_t launch_t(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream,
+                    bool accumulate) {
   auto kern = gemv_lds_kernel<NB, GL, RESID, FULL, CODES>;
   const int rps = 64 >> p.lpr_log2;
   const int64_t row_steps = (L.m_pad + rps - 1) / rps;
@@ -242,43 +246,46 @@ hipError_t launch_t(const glq_layer& L, const void* uq, int64_t B, float* z, con
                      reinterpret_cast<const uint32_t*>(uqc + U.dig_off), reinterpret_cast<const int32_t*>(uqc + U.sum_off),
                      reinterpret_cast<const float*>(uqc + U.scale_off), int(B), int(L.n_pad / 8), int(L.m_pad),
                      p.lpr_log2, bg_log2, int(U.nblk), int(upw), int(row_steps), p.splits, 0.5f * L.wscale,
-                     L.resid_scale, z);
+                     L.resid_scale, z, int(accumulate));
   return hipGetLastError();
 }
 
 template <int NB, int GL, int RESID>
-hipError_t launch_f(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream) {
+hipError_t launch_f(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream,
+                    bool acc) {
   const bool codes = L.index_format == GLQ_INDEX_SLOT;
   if (p.lpr_log2 == 6)
-    return codes ? launch_t<NB, GL, RESID, true, true>(L, uq, B, z, p, stream)
-                 : launch_t<NB, GL, RESID, true, false>(L, uq, B, z, p, stream);
-  return codes ? launch_t<NB, GL, RESID, false, true>(L, uq, B, z, p, stream)
-               : launch_t<NB, GL, RESID, false, false>(L, uq, B, z, p, stream);
+    return codes ? launch_t<NB, GL, RESID, true, true>(L, uq, B, z, p, stream, acc)
+                 : launch_t<NB, GL, RESID, true, false>(L, uq, B, z, p, stream, acc);
+  return codes ? launch_t<NB, GL, RESID, false, true>(L, uq, B, z, p, stream, acc)
+               : launch_t<NB, GL, RESID, false, false>(L, uq, B, z, p, stream, acc);
 }
 
 template <int NB, int GL>
-hipError_t launch_r(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream) {
+hipError_t launch_r(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream,
+                    bool acc) {
   switch (L.resid_bits) {
-    case 0: return launch_f<NB, GL, 0>(L, uq, B, z, p, stream);
-    case 8: return launch_f<NB, GL, 8>(L, uq, B, z, p, stream);
-    default: return launch_f<NB, GL, 16>(L, uq, B, z, p, stream);
+    case 0: return launch_f<NB, GL, 0>(L, uq, B, z, p, stream, acc);
+    case 8: return launch_f<NB, GL, 8>(L, uq, B, z, p, stream, acc);
+    default: return launch_f<NB, GL, 16>(L, uq, B, z, p, stream, acc);
   }
 }
 
 template <int NB>
-hipError_t launch_nb(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream) {
+hipError_t launch_nb(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream,
+                     bool acc) {
   switch (p.gl) {
     case 8:
-      if constexpr (gl_for(NB) >= 8) return launch_r<NB, 8>(L, uq, B, z, p, stream);
+      if constexpr (gl_for(NB) >= 8) return launch_r<NB, 8>(L, uq, B, z, p, stream, acc);
       break;
     case 4:
-      if constexpr (gl_for(NB) >= 4) return launch_r<NB, 4>(L, uq, B, z, p, stream);
+      if constexpr (gl_for(NB) >= 4) return launch_r<NB, 4>(L, uq, B, z, p, stream, acc);
       break;
     case 2:
-      if constexpr (gl_for(NB) >= 2) return launch_r<NB, 2>(L, uq, B, z, p, stream);
+      if constexpr (gl_for(NB) >= 2) return launch_r<NB, 2>(L, uq, B, z, p, stream, acc);
       break;
     default:
-      return launch_r<NB, 1>(L, uq, B, z, p, stream);
+      return launch_r<NB, 1>(L, uq, B, z, p, stream, acc);
   }
   return hipErrorInvalidValue;
 }
@@ -302,14 +309,15 @@ hipError_t launch_quant_u(const float* u, int64_t B, int64_t n_pad, void* uq, hi
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_lds(const glq_layer& L, const void* uq, int64_t B, float* z_parts, hipStream_t stream) {
+hipError_t launch_gemv_lds(const glq_layer& L, const void* uq, int64_t B, float* z_parts, hipStream_t stream,
+                           bool accumulate) {
   const Plan p = make_plan(L.n_pad, B);
   switch (p.nb) {
-    case 1: return launch_nb<1>(L, uq, B, z_parts, p, stream);
-    case 2: return launch_nb<2>(L, uq, B, z_parts, p, stream);
-    case 4: return launch_nb<4>(L, uq, B, z_parts, p, stream);
-    case 8: return launch_nb<8>(L, uq, B, z_parts, p, stream);
-    default: return launch_nb<16>(L, uq, B, z_parts, p, stream);
+    case 1: return launch_nb<1>(L, uq, B, z_parts, p, stream, accumulate);
+    case 2: return launch_nb<2>(L, uq, B, z_parts, p, stream, accumulate);
+    case 4: return launch_nb<4>(L, uq, B, z_parts, p, stream, accumulate);
+    case 8: return launch_nb<8>(L, uq, B, z_parts, p, stream, accumulate);
+    default: return launch_nb<16>(L, uq, B, z_parts, p, stream, accumulate);
   }
 }
 

@@ -111,7 +111,9 @@ hipError_t launch_gemv(const glq_layer& layer, const float* u, int64_t B, float*
 size_t uq_bytes(int64_t B, int64_t n_pad);
 int gemv_lds_splits(int64_t n_pad, int64_t B);
 hipError_t launch_quant_u(const float* u, int64_t B, int64_t n_pad, void* uq, hipStream_t stream);
-hipError_t launch_gemv_lds(const glq_layer& layer, const void* uq, int64_t B, float* z_parts, hipStream_t stream);
+// accumulate: add to z_parts instead of storing (the second pass of a 5-8 bpw layer)
+hipError_t launch_gemv_lds(const glq_layer& layer, const void* uq, int64_t B, float* z_parts, hipStream_t stream,
+                           bool accumulate = false);
 
 // The whole linear for B = 1 in two launches (input RHT, decode matmul with the
 // LDS codebook and the row-local part of the output RHT; then the fixed-order
@@ -119,8 +121,10 @@ hipError_t launch_gemv_lds(const glq_layer& layer, const void* uq, int64_t B, fl
 // fused_decode_z_bytes(layer) of scratch.
 bool fused_decode_supported(const glq_layer& layer, int64_t B);
 size_t fused_decode_z_bytes(const glq_layer& layer);
+// pass: 0 the whole call; 1 the first pass of a 5-8 bpw layer (z_parts only);
+// 2 its second pass (adds to z_parts, then the cross-block launch writes y)
 hipError_t launch_fused_decode(const glq_layer& layer, const void* x, glq_dtype x_dt, void* y, glq_dtype y_dt,
-                               float* z_parts, hipStream_t stream);
+                               float* z_parts, hipStream_t stream, int pass = 0);
 
 // Prefill matmul: z [M][m_pad] fp32 from u16 [M][n_pad] fp16.  launch_gemm takes the
 // LDS-codebook kernel (launch_gemm_lds) when gemm_lds_supported(layer), else the
@@ -130,9 +134,10 @@ hipError_t launch_fused_decode(const glq_layer& layer, const void* x, glq_dtype 
 bool gemm_lds_supported(const glq_layer& layer);
 size_t tiled_u_bytes(int64_t M, int64_t n_pad);
 hipError_t launch_gemm_lds(const glq_layer& layer, const half_t* u16, int64_t M, bool tiled, float* z,
-                           hipStream_t stream);
+                           hipStream_t stream, bool accumulate = false);
 hipError_t launch_rht_in_tiled(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int L, const int8_t* sign,
                                half_t* u16, float* ws, hipStream_t stream);
-hipError_t launch_gemm(const glq_layer& layer, const half_t* u16, int64_t M, float* z, hipStream_t stream);
+hipError_t launch_gemm(const glq_layer& layer, const half_t* u16, int64_t M, float* z, hipStream_t stream,
+                       bool accumulate = false);
 
 }  // namespace glq

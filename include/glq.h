@@ -58,7 +58,7 @@ typedef enum glq_status {
   GLQ_ERR_NULL = 1,      /* a required pointer is NULL */
   GLQ_ERR_SHAPE = 2,     /* a size is out of range or sizes disagree */
   GLQ_ERR_DTYPE = 3,     /* dtype code not supported by this entry point */
-  GLQ_ERR_RECIPE = 4,    /* resid_bits not in {0, 8, 16} */
+  GLQ_ERR_RECIPE = 4,    /* not a recipe of "Bit widths" (resid_bits, further stages) or bad index_format */
   GLQ_ERR_ALIGN = 5,     /* a pointer is not aligned as documented */
   GLQ_ERR_WORKSPACE = 6, /* workspace missing or smaller than the size query says */
   GLQ_ERR_HIP = 7,       /* a HIP launch failed */
@@ -103,6 +103,16 @@ typedef enum glq_dtype {
  *                   resid_bits == 16) hold slot codes of cb_pack, written by
  *                   glq_slot_codes; with resid_bits 16 cb2_pack must then be
  *                   cb_pack.  8-bit residual indices are never relabelled.
+ *   n_extra         further residual stages, 5-8 bpw ("Bit widths": 16b + 16b + 8b,
+ *                   16b + 16b + 16b, 16b + 16b + 16b + 8b, 16b x 4): 0, 1 or 2; with
+ *                   1 or 2, resid_bits is 16 and cb2_pack is cb_pack
+ *   extra_bits      per further stage: 8, or 16 (16 for the first of two)
+ *   extra_scale     per further stage: its scale relative to s, like resid_scale
+ *                   (W~ = s (C0 + s_r C1 + sum_k extra_scale[k] C_k))
+ *   extra_idx       per further stage: uint8 / uint16 [m_pad][n_pad/8], 16-byte
+ *                   aligned; 16-bit stages index cb_pack (slot codes with
+ *                   GLQ_INDEX_SLOT), 8-bit stages cb8_pack
+ *   cb8_pack        the 256-entry pack of an 8-bit further stage; NULL otherwise
  */
 typedef struct glq_layer {
   int64_t n;
@@ -119,6 +129,11 @@ typedef struct glq_layer {
   const void* cb_pack;
   const void* cb2_pack;
   int32_t index_format;
+  int32_t n_extra;
+  int32_t extra_bits[2];
+  float extra_scale[2];
+  const void* extra_idx[2];
+  const void* cb8_pack;
 } glq_layer;
 
 /* GLQ_ABI_VERSION of the built library. */

@@ -138,6 +138,11 @@ class TestValidation:
         assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 1, 16, A, A, 1 << 30, None) == 3
         assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 0, A, A, 1 << 30, None) == 2
         assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A + 4, 0, 1, A, A, 1 << 30, None) == 5
+        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 1, A, None, 0, None) == 6
+        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 1, A, A, 8, None) == 6
+        assert lib.glq_e8_matmul_splits(ctypes.byref(fake_layer(n_pad=32768)), 1) == 8
+        assert lib.glq_e8_matmul_splits(ctypes.byref(fake_layer(n_pad=32768)), 17) == 1
+
 
     def test_index_format(self):
         lib = _lib.load()
@@ -151,7 +156,31 @@ class TestValidation:
         assert lib.glq_slot_codes(A + 16, A, 8, A, None) == 5
         assert lib.glq_slot_codes(A, A + 1, 8, A, None) == 5
         assert lib.glq_slot_codes(A, None, 0, None, None) == 0  # nothing to do
-        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 1, A, None, 0, None) == 6
-        assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 1, A, A, 8, None) == 6
-        assert lib.glq_e8_matmul_splits(ctypes.byref(fake_layer(n_pad=32768)), 1) == 8
-        assert lib.glq_e8_matmul_splits(ctypes.byref(fake_layer(n_pad=32768)), 17) == 1
+
+    def test_further_stages(self):
+        def multi(n_extra, bits, **kw):
+            L = fake_layer(resid_bits=16, cb2_pack=A, n_extra=n_extra)
+            for k, b in enumerate(bits):
+                L.extra_bits[k] = b
+                L.extra_scale[k] = 0.25 ** (k + 2)
+                L.extra_idx[k] = A
+            L.cb8_pack = A
+            for k, v in kw.items():
+                setattr(L, k, v)
+            return L
+        assert linear_status(multi(3, [16, 16])) == 4              # at most two further stages
+        assert linear_status(multi(2, [8, 16])) == 4               # 16 bits for the first of two
+        assert linear_status(multi(1, [4])) == 4
+        assert linear_status(multi(1, [16], resid_bits=8)) == 4    # after a 16-bit residual stage only
+        assert linear_status(multi(1, [16], cb2_pack=A + 256)) == 4
+        assert linear_status(multi(1, [8], cb8_pack=None)) == 1
+        assert linear_status(multi(1, [8], cb8_pack=A + 16)) == 5
+        L = multi(1, [16])
+        L.extra_idx[0] = None
+        assert linear_status(L) == 1
+        L = multi(1, [16])
+        L.extra_idx[0] = A + 2
+        assert linear_status(L) == 5
+        L = multi(1, [16])
+        L.extra_scale[0] = 0.0
+        assert linear_status(L) == 4
