@@ -125,11 +125,20 @@ def matmul_z(u, idx0, idx1, resid_bits, wscale, resid_scale, row_block=2048, ext
     return z
 
 
-def linear(x, sign_in, sign_out, n_pad, m, idx0, idx1, resid_bits, wscale, resid_scale, extra=()):
+def linear(x, sign_in, sign_out, n_pad, m, idx0, idx1, resid_bits, wscale, resid_scale, extra=(), block_diag=False):
     """E8RHTLinear forward in float64: y [B, m] from x [B, n].
 
     Dequantize-then-matmul, the page's CPU path, between the two transforms.
+    block_diag: the transforms are block-diagonal over the power-of-two blocks of
+    n and m (oracle.hadamard.rht_in_blocks / rht_out_blocks); then n_pad == n and
+    the index arrays have m rows.
     """
+    if block_diag:
+        if np.asarray(x).shape[-1] != n_pad or np.asarray(idx0).shape[0] != m:
+            raise ValueError("a block-diagonal layer is unpadded")
+        u = hadamard.rht_in_blocks(x, sign_in)
+        z = matmul_z(u, idx0, idx1, resid_bits, wscale, resid_scale, extra=extra)
+        return hadamard.rht_out_blocks(z, sign_out)
     u = hadamard.rht_in(x, sign_in, n_pad)
     z = matmul_z(u, idx0, idx1, resid_bits, wscale, resid_scale, extra=extra)
     return hadamard.rht_out(z, sign_out, m)

@@ -11,6 +11,13 @@ Readings (listed in the design notes): natural (Sylvester) order, i.e.
 H[i][j] = (-1)^popcount(i & j); each transform is orthonormal (divided by
 sqrt of its padded length); input: sign then H; output: H then sign; inputs are
 zero-padded from n to n_pad and outputs truncated from m_pad to m.
+
+Block-diagonal form (glq 0.5.1, table "Bit widths" and the paragraph under it:
+sizes that are not powers of two are split into power-of-two blocks, 2688 as
+2048 + 512 + 128, so nothing is padded).  Readings: the blocks are the powers of
+two of the length's binary expansion, largest first, at consecutive offsets;
+each block is transformed on its own, orthonormal (divided by the square root
+of the block length); the sign vectors have the unpadded lengths.
 All arithmetic is float64.
 """
 
@@ -62,3 +69,47 @@ def rht_out(z, sign_out, m):
     m_pad = z.shape[-1]
     s = np.asarray(sign_out, dtype=np.float64)
     return (s[None, :] * fwht(z) / np.sqrt(m_pad))[:, :m]
+
+
+def pow2_blocks(n):
+    """Block lengths of the block-diagonal transform of length n, largest first:
+    the powers of two whose sum is n (its binary expansion)."""
+    if n < 1:
+        raise ValueError("length must be positive")
+    out = []
+    bit = 1 << (int(n).bit_length() - 1)
+    while bit:
+        if n & bit:
+            out.append(bit)
+        bit >>= 1
+    return out
+
+
+def block_fwht(v):
+    """Orthonormal block-diagonal transform along the last axis: block b of length
+    L (at its offset) becomes H_L v_b / sqrt(L)."""
+    a = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(a)
+    off = 0
+    for L in pow2_blocks(a.shape[-1]):
+        out[..., off:off + L] = fwht(a[..., off:off + L]) / np.sqrt(L)
+        off += L
+    return out
+
+
+def rht_in_blocks(x, sign_in):
+    """Block-diagonal input RHT: u = D_n (s_in * x), rows of x [B, n], no padding."""
+    x = np.asarray(x, dtype=np.float64)
+    s = np.asarray(sign_in, dtype=np.float64)
+    if s.shape[-1] != x.shape[-1]:
+        raise ValueError("sign_in must have n entries")
+    return block_fwht(x * s[None, :])
+
+
+def rht_out_blocks(z, sign_out):
+    """Block-diagonal output RHT: y = s_out * D_m z, rows of z [B, m], no padding."""
+    z = np.asarray(z, dtype=np.float64)
+    s = np.asarray(sign_out, dtype=np.float64)
+    if s.shape[-1] != z.shape[-1]:
+        raise ValueError("sign_out must have m entries")
+    return s[None, :] * block_fwht(z)

@@ -97,6 +97,7 @@ class Layer:
     wscale: float = WSCALE
     resid_scale: float = RESID_SCALE
     extra: tuple = ()        # further residual stages (5-8 bpw): (bits, index array, scale) each
+    block_diag: bool = False  # unpadded, block-diagonal transforms (n_pad == n, m_pad == m)
 
     @property
     def n(self):
@@ -131,7 +132,7 @@ class Layer:
 RECIPES = {2: (0, ()), 3: (8, ()), 4: (16, ()), 5: (16, (8,)), 6: (16, (16,)), 7: (16, (16, 8)), 8: (16, (16, 16))}
 
 
-def make_layer(shape, resid_bits, seed, k, rows=None, extra_bits=()):
+def make_layer(shape, resid_bits, seed, k, rows=None, extra_bits=(), block_diag=False):
     """Draw layer k of a workload with the given seed.
 
     extra_bits: bits (8 or 16) of residual stages 2, 3 (5-8 bpw), drawn after the
@@ -140,8 +141,11 @@ def make_layer(shape, resid_bits, seed, k, rows=None, extra_bits=()):
 
     rows: optionally keep only the first `rows` rows of the index arrays, used
     nowhere on the measured path (the draw order is unchanged).
+
+    block_diag: the layer is unpadded (n_pad = n, m_pad = m) for block-diagonal
+    transforms; the draws keep their order, with the unpadded lengths.
     """
-    shape = shape.padded()
+    shape = LayerShape(shape.name, shape.n, shape.m, shape.n, shape.m) if block_diag else shape.padded()
     rng = np.random.default_rng([seed, k])
     sign_in = (2 * rng.integers(0, 2, size=shape.n_pad) - 1).astype(np.int8)
     sign_out = (2 * rng.integers(0, 2, size=shape.m_pad) - 1).astype(np.int8)
@@ -160,7 +164,7 @@ def make_layer(shape, resid_bits, seed, k, rows=None, extra_bits=()):
             raise ValueError("extra stages are 8 or 16 bits, after a residual stage")
         idx = rng.integers(0, 256 if bits == 8 else 65536, size=gshape, dtype=np.uint8 if bits == 8 else np.uint16)
         extra.append((bits, idx, float(np.float32(RESID_SCALE ** (j + 2)))))
-    return Layer(shape, resid_bits, sign_in, sign_out, idx0, idx1, extra=tuple(extra))
+    return Layer(shape, resid_bits, sign_in, sign_out, idx0, idx1, extra=tuple(extra), block_diag=block_diag)
 
 
 def round_to_dtype(x64, dtype):
@@ -200,6 +204,11 @@ def random_layer(n, m, resid_bits, seed, n_pad=None, m_pad=None, extra_bits=()):
     """A layer of arbitrary shape (tests of ragged and tiny shapes)."""
     shape = LayerShape("t", n, m, n_pad or next_pow2(max(n, 8)), m_pad or next_pow2(max(m, 8)))
     return make_layer(shape, resid_bits, seed, 0, extra_bits=extra_bits)
+
+
+def block_layer(n, m, resid_bits, seed, extra_bits=()):
+    """An unpadded layer with block-diagonal transforms (n, m multiples of 8)."""
+    return make_layer(LayerShape("t", n, m), resid_bits, seed, 0, extra_bits=extra_bits, block_diag=True)
 
 
 def recipe_layer(n, m, bpw, seed, n_pad=None, m_pad=None):

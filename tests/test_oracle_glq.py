@@ -53,6 +53,36 @@ def test_fused_equals_dense_conjugated(resid_bits, n, m, n_pad, m_pad):
     np.testing.assert_allclose(y, want, rtol=0, atol=1e-12 * max(1.0, np.abs(want).max()))
 
 
+def dense_block_reference(x, layer):
+    """y = x W^T with W = S_out D_m W~ D_n S_in, D the block-diagonal orthonormal
+    Hadamard matrix built from scipy.linalg.block_diag of scipy.linalg.hadamard."""
+    n, m = layer.n, layer.m
+    c0 = e8.codebook()
+    W = c0[layer.idx0.astype(np.int64)].reshape(m, n)
+    if layer.resid_bits:
+        c1 = e8.residual_codebook(layer.resid_bits)
+        W = W + 0.25 * c1[layer.idx1.astype(np.int64)].reshape(m, n)
+    W = float(np.float32(0.02)) * W
+
+    def D(k):
+        return scipy.linalg.block_diag(*[scipy.linalg.hadamard(b).astype(np.float64) / np.sqrt(b)
+                                         for b in hadamard.pow2_blocks(k)])
+    Wc = np.diag(layer.sign_out.astype(np.float64)) @ D(m) @ W @ D(n) @ np.diag(layer.sign_in.astype(np.float64))
+    return x @ Wc.T
+
+
+@pytest.mark.parametrize("resid_bits", [0, 8, 16])
+@pytest.mark.parametrize("n,m", [(24, 40), (8, 56), (96, 64), (200, 328)])
+def test_block_diag_linear_equals_dense(resid_bits, n, m):
+    layer = synth.block_layer(n, m, resid_bits, seed=n + 7 * m + resid_bits)
+    assert layer.n_pad == n and layer.m_pad == m and layer.idx0.shape == (m, n // 8)
+    x = np.random.default_rng(n * m).standard_normal((3, n))
+    y = glq.linear(x, layer.sign_in, layer.sign_out, n, m, layer.idx0, layer.idx1, resid_bits,
+                   layer.wscale, layer.resid_scale, block_diag=True)
+    want = dense_block_reference(x, layer)
+    np.testing.assert_allclose(y, want, rtol=0, atol=1e-12 * max(1.0, np.abs(want).max()))
+
+
 def test_zero_indices_give_zero_output():
     layer = synth.random_layer(64, 64, 16, seed=5)
     layer.idx0[:] = 0

@@ -77,3 +77,61 @@ def test_rht_out_matches_dense():
 def test_rejects_non_power_of_two():
     with pytest.raises(ValueError):
         hadamard.fwht(np.zeros(12))
+
+
+# ---- block-diagonal transforms (glq 0.5.1, "Bit widths": non-power-of-two sizes
+# split into power-of-two blocks, the example 2688 = 2048 + 512 + 128) -------------------
+def test_block_split_of_the_pages_example():
+    assert hadamard.pow2_blocks(2688) == [2048, 512, 128]
+
+
+def test_block_split_is_the_binary_expansion():
+    # distinct powers of two, largest first, summing to n: the unique such set
+    for n in range(1, 5000):
+        bl = hadamard.pow2_blocks(n)
+        assert sum(bl) == n
+        assert all(b & (b - 1) == 0 for b in bl)
+        assert all(bl[i] > bl[i + 1] for i in range(len(bl) - 1))
+    assert hadamard.pow2_blocks(4096) == [4096]
+    assert hadamard.pow2_blocks(11008) == [8192, 2048, 512, 256]
+    assert hadamard.pow2_blocks(5120) == [4096, 1024]
+
+
+def dense_block_diag(n):
+    bl = hadamard.pow2_blocks(n)
+    return scipy.linalg.block_diag(*[scipy.linalg.hadamard(b).astype(np.float64) / np.sqrt(b) for b in bl])
+
+
+@pytest.mark.parametrize("n", [1, 3, 7, 24, 100, 960])
+def test_block_rht_matches_dense(n):
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal((3, n))
+    s_in = (2 * rng.integers(0, 2, size=n) - 1).astype(np.int8)
+    D = dense_block_diag(n)
+    np.testing.assert_allclose(hadamard.rht_in_blocks(x, s_in), (x * s_in) @ D.T, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(hadamard.rht_out_blocks(x, s_in), s_in * (x @ D.T), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [64, 1024])
+def test_block_rht_of_a_power_of_two_is_the_full_rht(n):
+    rng = np.random.default_rng(n + 1)
+    x = rng.standard_normal((2, n))
+    s = (2 * rng.integers(0, 2, size=n) - 1).astype(np.int8)
+    assert np.array_equal(hadamard.rht_in_blocks(x, s), hadamard.rht_in(x, s, n))
+    assert np.array_equal(hadamard.rht_out_blocks(x, s), hadamard.rht_out(x, s, n))
+
+
+def test_block_rht_orthonormal():
+    rng = np.random.default_rng(7)
+    n = 2688
+    x = rng.standard_normal((2, n))
+    s = (2 * rng.integers(0, 2, size=n) - 1).astype(np.int8)
+    u = hadamard.rht_in_blocks(x, s)
+    np.testing.assert_allclose(np.linalg.norm(u, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    # each orthonormal block is its own inverse: out(in(x)) with the same signs is x
+    np.testing.assert_allclose(hadamard.rht_out_blocks(u, s), x, rtol=0, atol=1e-12)
+
+
+def test_block_rht_rejects_wrong_sign_length():
+    with pytest.raises(ValueError):
+        hadamard.rht_in_blocks(np.zeros((1, 24)), np.ones(32, dtype=np.int8))
