@@ -11,7 +11,17 @@ namespace {
 
 bool valid_dtype(glq_dtype d) { return d == GLQ_F32 || d == GLQ_F16 || d == GLQ_BF16; }
 
-bool valid_pad(int64_t p) { return is_pow2(p) && p >= 8 && p <= GLQ_MAX_PAD; }
+// a transform length: a power of two in [8, GLQ_MAX_PAD], or a multiple of 64 below
+// GLQ_MAX_PAD (block-diagonal transform over its binary expansion)
+bool valid_pad(int64_t p) {
+  return p >= 8 && p <= GLQ_MAX_PAD && (is_pow2(p) || p % 64 == 0);
+}
+
+// scratch of the two-pass transform: a block longer than one workgroup's, unless
+// the output is fp32 of one block (its own scratch)
+bool rht_needs_ws(int64_t N, bool f32_out) {
+  return largest_block(N) > (int64_t(1) << kSingleLog2) && !(f32_out && is_pow2(N));
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -129,18 +139,17 @@ LinearWs linear_ws(const glq_layer& L, int64_t B) {
     w.total = off + align256(fused_decode_z_bytes(L));
     return w;
   }
-  const int ln = log2_exact(L.n_pad), lm = log2_exact(L.m_pad);
   w.u_off = off;
   off += align256(w.prefill ? tiled_u_bytes(B, L.n_pad) : size_t(B) * size_t(L.n_pad) * 4);
   w.uq_off = off;
   if (w.lds) off += align256(uq_bytes(B, L.n_pad));
   w.rin_off = off;
-  if (w.prefill && ln > kSingleLog2) off += align256(size_t(B) * size_t(L.n_pad) * 4);
+  if (rht_needs_ws(L.n_pad, !w.prefill)) off += align256(size_t(B) * size_t(L.n_pad) * 4);
   w.splits = matmul_splits(L, B);
   w.z_off = off;
   off += align256(size_t(w.splits) * size_t(B) * size_t(L.m_pad) * 4);
   w.rout_off = off;
-  if (lm > kSingleLog2) off += align256(size_t(B) * size_t(L.m_pad) * 4);
+  if (rht_needs_ws(L.m_pad, false)) off += align256(size_t(B) * size_t(L.m_pad) * 4);
   w.total = off;
   return w;
 }
@@ -212,7 +221,7 @@ glq_status glq_slot_codes(const void* cb_pack, const uint16_t* idx, int64_t coun
 
 size_t glq_input_rht_workspace_bytes(int64_t B, int64_t n_pad, glq_dtype u_dt) {
   if (B < 1 || !valid_pad(n_pad)) return 0;
-  if (log2_exact(n_pad) > kSingleLog2 && u_dt != GLQ_F32) return align256(size_t(B) * size_t(n_pad) * 4);
+  if (rht_needs_ws(n_pad, u_dt == GLQ_F32)) return align256(size_t(B) * size_t(n_pad) * 4);
   return 0;
 }
 
@@ -224,13 +233,13 @@ glq_status glq_input_rht(const void* x, glq_dtype x_dt, int64_t B, int64_t n, in
   const size_t need = glq_input_rht_workspace_bytes(B, n_pad, u_dt);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GLQ_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 256)) return GLQ_ERR_ALIGN;
-  return from_hip(launch_rht_in(x, x_dt, B, n, log2_exact(n_pad), sign_in, u, u_dt,
+  return from_hip(launch_rht_in(x, x_dt, B, n, n_pad, sign_in, u, u_dt,
                                 static_cast<float*>(workspace), stream));
 }
 
 size_t glq_output_rht_workspace_bytes(int64_t B, int64_t m_pad) {
   if (B < 1 || !valid_pad(m_pad)) return 0;
-  if (log2_exact(m_pad) > kSingleLog2) return align256(size_t(B) * size_t(m_pad) * 4);
+  if (rht_needs_ws(m_pad, false)) return align256(size_t(B) * size_t(m_pad) * 4);
   return 0;
 }
 
@@ -244,7 +253,7 @@ glq_status glq_output_rht(const float* z_parts, int64_t splits, int64_t B, int64
   const size_t need = glq_output_rht_workspace_bytes(B, m_pad);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GLQ_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 256)) return GLQ_ERR_ALIGN;
-  return from_hip(launch_rht_out(z_parts, splits, B, m, log2_exact(m_pad), sign_out, y, y_dt,
+  return from_hip(launch_rht_out(z_parts, splits, B, m, m_pad, sign_out, y, y_dt,
                                  static_cast<float*>(workspace), stream));
 }
 
@@ -302,7 +311,7 @@ glq_status glq_input_rht_prefill(const void* x, glq_dtype x_dt, int64_t B, int64
   const size_t need = glq_input_rht_workspace_bytes(B, n_pad, GLQ_F16);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GLQ_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 256)) return GLQ_ERR_ALIGN;
-  return from_hip(launch_rht_in_tiled(x, x_dt, B, n, log2_exact(n_pad), sign_in, static_cast<half_t*>(u16),
+  return from_hip(launch_rht_in_tiled(x, x_dt, B, n, n_pad, sign_in, static_cast<half_t*>(u16),
                                       static_cast<float*>(workspace), stream));
 }
 
@@ -338,29 +347,28 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
     if (launch_fused_decode(P.a, x, x_dt, y, y_dt, zp, stream, 1) != hipSuccess) return GLQ_ERR_HIP;
     return from_hip(launch_fused_decode(P.b, x, x_dt, y, y_dt, zp, stream, 2));
   }
-  const int ln = log2_exact(L.n_pad), lm = log2_exact(L.m_pad);
   hipError_t e;
   float* z = at<float>(workspace, w.z_off);
   if (!w.prefill) {
     float* u = at<float>(workspace, w.u_off);
-    e = launch_rht_in(x, x_dt, B, L.n, ln, L.sign_in, u, GLQ_F32, nullptr, stream);
+    e = launch_rht_in(x, x_dt, B, L.n, L.n_pad, L.sign_in, u, GLQ_F32, at<float>(workspace, w.rin_off), stream);
     if (e != hipSuccess) return GLQ_ERR_HIP;
     e = decode_matmul(L, u, B, at<char>(workspace, w.uq_off), z, stream);
     if (e != hipSuccess) return GLQ_ERR_HIP;
   } else {
     half_t* u = at<half_t>(workspace, w.u_off);
     if (gemm_lds_supported(L)) {  // u in the matmul's fragment order
-      e = launch_rht_in_tiled(x, x_dt, B, L.n, ln, L.sign_in, u, at<float>(workspace, w.rin_off), stream);
+      e = launch_rht_in_tiled(x, x_dt, B, L.n, L.n_pad, L.sign_in, u, at<float>(workspace, w.rin_off), stream);
       if (e != hipSuccess) return GLQ_ERR_HIP;
       e = prefill_matmul(L, u, B, true, z, stream);
     } else {
-      e = launch_rht_in(x, x_dt, B, L.n, ln, L.sign_in, u, GLQ_F16, at<float>(workspace, w.rin_off), stream);
+      e = launch_rht_in(x, x_dt, B, L.n, L.n_pad, L.sign_in, u, GLQ_F16, at<float>(workspace, w.rin_off), stream);
       if (e != hipSuccess) return GLQ_ERR_HIP;
       e = prefill_matmul(L, u, B, false, z, stream);
     }
     if (e != hipSuccess) return GLQ_ERR_HIP;
   }
-  e = launch_rht_out(z, w.splits, B, L.m, lm, L.sign_out, y, y_dt, at<float>(workspace, w.rout_off), stream);
+  e = launch_rht_out(z, w.splits, B, L.m, L.m_pad, L.sign_out, y, y_dt, at<float>(workspace, w.rout_off), stream);
   return from_hip(e);
 }
 

@@ -43,6 +43,7 @@ constexpr int kThreads = 1024;
 // LDS of the chunk of u (4096 fp32 at most), at the top of the LDS array: above
 // image parts 0-7 (kImgOff + 4 * 8192 = 33024 <= kLdsDwords - kChunkDwords)
 constexpr int kChunkDwords = 4096;
+constexpr int kLenLog2s = 21;  // transform block lengths 2^0 .. 2^20
 // rows of the workgroup kept in LDS for its share of the output transform
 constexpr int kRowBuf = 1024;
 // digit planes of the chunk, between image parts 0-7 and the chunk: uint4
@@ -63,11 +64,12 @@ struct FusedArgs {
   float* z_parts;             // [S][m_pad]: H_R of each workgroup's row block
   int64_t n;
   int x_dt;
-  int ln, lk;  // log2 of n_pad and of the chunk length K
+  int n_pad;   // transform length (block-diagonal over its binary expansion)
+  int lk;      // log2 of the chunk length K (K divides every block of n_pad)
   int vec_in;  // x and sign_in may be read 4 elements at a time
   int G, m_pad, lpr_log2, row_steps, wgs_per_split, rs_per_wg;
   int lr;           // log2 R, the rows of a workgroup's block
-  float sc_scale;   // 1 / (sqrt(n_pad) kUqMax): u = t_H / sqrt(n_pad), scale = max|t_H| * sc_scale
+  float sc_tab[kLenLog2s];  // [log2 L] 1 / (sqrt(L) kUqMax): u = t_H / sqrt(L), scale = max|t_H| * sc_tab
   float out_scale;  // s / 2 (codebook entries are held doubled)
   float sr;         // residual scale
   int accumulate;   // add H_R of the row block to z_parts (second pass of a 5-8 bpw layer)
@@ -270,26 +272,34 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
     }
   }
   float* chunk = reinterpret_cast<float*>(lds + (kLdsDwords - kChunkDwords));
+  // the split's chunk lies in the transform block of length 2^lb that starts at
+  // column blk0: the block of a column c < n_pad is the highest set bit of
+  // n_pad ^ c (the blocks are n_pad's binary expansion, largest first); the
+  // chunk is number s_loc of the block's nsrc chunks
   const int K = 1 << a.lk;
-  const int nsrc = 1 << (a.ln - a.lk);
+  const int col0 = split << a.lk;
+  const int lb = 31 - __clz(a.n_pad ^ col0);
+  const int blk0 = col0 & ~((1 << lb) - 1);
+  const int s_loc = (col0 - blk0) >> a.lk;
+  const int nsrc = 1 << (lb - a.lk);
   const int c4 = tid * 4;  // the thread's four columns of the chunk (K <= 4096)
   float t[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   XRaw xr[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    if (i < nsrc && c4 < K) x_issue(a, (int64_t(i) << a.lk) + c4, xr[i]);
+    if (i < nsrc && c4 < K) x_issue(a, blk0 + (int64_t(i) << a.lk) + c4, xr[i]);
   ImageRegs img;
   image_issue<RESID>(img, a.pack0_hdr, a.img0, a.res_slots, tid, CODES ? kHdrSlotDwords : 3);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    if (i < nsrc && c4 < K) x_accumulate(xr[i], a.x_dt, __popc(unsigned(split & i)) & 1, t);
+    if (i < nsrc && c4 < K) x_accumulate(xr[i], a.x_dt, __popc(unsigned(s_loc & i)) & 1, t);
   for (int src0 = 8; src0 < nsrc; src0 += 8) {  // n_pad > 8 * 4096
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (src0 + i < nsrc && c4 < K) x_issue(a, (int64_t(src0 + i) << a.lk) + c4, xr[i]);
+      if (src0 + i < nsrc && c4 < K) x_issue(a, blk0 + (int64_t(src0 + i) << a.lk) + c4, xr[i]);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (src0 + i < nsrc && c4 < K) x_accumulate(xr[i], a.x_dt, __popc(unsigned(split & (src0 + i))) & 1, t);
+      if (src0 + i < nsrc && c4 < K) x_accumulate(xr[i], a.x_dt, __popc(unsigned(s_loc & (src0 + i))) & 1, t);
   }
   // bits 0-1 in registers, bits 2-7 across the lanes of the wave (threads past
   // the chunk hold zeros and never pair with one inside it), bits 8-11 in one
@@ -358,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
       pv.w = pl[3];
       *reinterpret_cast<img_x4*>(lds + kDigOff + 4 * (q * LPR + l)) = pv;
       lds[kGsOff + 4 * ((q >> 2) * LPR + l) + (q & 3)] = uint32_t(-gsum);  // negated: added on complemented reads
-      if (q == 0) lds[kScOff + l] = __float_as_uint(mx * a.sc_scale);
+      if (q == 0) lds[kScOff + l] = __float_as_uint(mx * a.sc_tab[lb]);
     }
   }
   __syncthreads();
@@ -449,20 +459,25 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
 }
 
 // ---- the cross-block part of the output transform ------------------------------------
-// Output i = a R + b (block a < W, column b < R).  z_parts[s] holds H_R of every
-// block, so y[a R + b] = sign[i] / sqrt(m_pad) * sum_a' H_W[a][a'] T[a' R + b] with
-// T = sum over s = 0 .. S-1, in order, of z_parts[s].  One wave per CB consecutive
-// columns; lane l holds blocks a = l E + e (e < E; W = 64 E, or W < 64 with E = 1
-// and lanes >= W idle): the bits of e in registers, the lane bits by shuffles.
+// Output i = a R + b (row block a < W = m_pad / R, column b < R).  z_parts[s] holds
+// H_R of every row block, so for a power-of-two m_pad
+// y[a R + b] = sign[i] / sqrt(m_pad) * sum_a' H_W[a][a'] T[a' R + b] with
+// T = sum over s = 0 .. S-1, in order, of z_parts[s].  A block-diagonal m_pad
+// (R divides its smallest block) does the same inside each of its blocks: the
+// butterfly on bit k of a joins a and a ^ 2^k only when both lie in one block,
+// i.e. when that block holds more than 2^k row blocks, and the scale is
+// 1 / sqrt(block length).  One wave per CB consecutive columns; lane l holds row
+// blocks a = l E + e (e < E, 64 E >= W; blocks past W are idle): the bits of e in
+// registers, the lane bits by shuffles.
 struct BlocksArgs {
   const float* z;
   const int8_t* sign;
   void* y;
   int64_t m;
-  int S, m_pad, lr, lw;
+  int S, m_pad, lr, lw, W;  // lw = ceil(log2 W)
   int vec_sign;  // sign_out 4-byte aligned: one 32-bit load per CB = 4 signs
   int vec_y;     // y aligned for CB-element stores
-  float scale;
+  float sc_tab[kLenLog2s];  // [log2 L] 1 / sqrt(L)
 };
 
 template <int CB>
@@ -508,21 +523,25 @@ template <class YT, int E, int CB>
 __global__ __launch_bounds__(64) void output_blocks_kernel(BlocksArgs a) {
   const int lane = threadIdx.x;
   const int b0 = int(blockIdx.x) * CB;
-  const bool live = (lane * E) < (1 << a.lw);
+  const bool live = (lane * E) < a.W;
   float v[E][CB];
   uint32_t sg[E];  // sign bytes of the lane's CB outputs per block (sign_out has m_pad entries)
+  int gl[E];       // log2 of the length of the transform block holding row block l E + e
 #pragma unroll
   for (int e = 0; e < E; ++e) {
 #pragma unroll
     for (int c = 0; c < CB; ++c) v[e][c] = 0.0f;
     sg[e] = 0;
+    const int ab = lane * E + e;
+    gl[e] = ab < a.W ? 31 - __clz(a.m_pad ^ (ab << a.lr)) : 0;
   }
   if (live) {
     // every load is issued before the first use: signs, then the partials of
-    // four splits at a time, summed in split order
+    // four splits at a time, summed in split order; row blocks past W (only in
+    // the last live lane) read a valid address and are not summed
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int64_t i0 = (int64_t(lane * E + e) << a.lr) + b0;
+      const int64_t i0 = (int64_t(min(lane * E + e, a.W - 1)) << a.lr) + b0;
       if (CB == 4 && a.vec_sign) {
         sg[e] = *reinterpret_cast<const uint32_t*>(a.sign + i0);
       } else {
@@ -539,26 +558,36 @@ __global__ __launch_bounds__(64) void output_blocks_kernel(BlocksArgs a) {
 #pragma unroll
           for (int c = 0; c < CB; ++c) t[k][e][c] = 0.0f;
           const int sk = s + k < a.S ? s + k : a.S - 1;  // past the last split: a valid address, not summed
-          add_parts<CB>(t[k][e], a.z + int64_t(sk) * a.m_pad + (int64_t(lane * E + e) << a.lr) + b0);
+          add_parts<CB>(t[k][e], a.z + int64_t(sk) * a.m_pad + (int64_t(min(lane * E + e, a.W - 1)) << a.lr) + b0);
         }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const bool in = s + k < a.S;
 #pragma unroll
-        for (int e = 0; e < E; ++e)
+        for (int e = 0; e < E; ++e) {
+          const bool use = in && lane * E + e < a.W;
 #pragma unroll
-          for (int c = 0; c < CB; ++c) v[e][c] += in ? t[k][e][c] : 0.0f;
+          for (int c = 0; c < CB; ++c) v[e][c] += use ? t[k][e][c] : 0.0f;
+        }
       }
     }
   }
+  // register bits: the butterfly (e, e + h) acts when its transform block holds
+  // more than h row blocks (both then lie in it; always for a power-of-two m_pad)
 #pragma unroll
-  for (int c = 0; c < CB; ++c) {
-    float t[E];
+  for (int h = 1; h < E; h <<= 1) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) t[e] = v[e][c];
-    fwht_reg<E>(t);
+    for (int e = 0; e < E; ++e) {
+      if ((e & h) == 0) {
+        const bool act = gl[e] - a.lr > log2_exact_dev(h);
 #pragma unroll
-    for (int e = 0; e < E; ++e) v[e][c] = t[e];
+        for (int c = 0; c < CB; ++c) {
+          const float x0 = v[e][c], x1 = v[e + h][c];
+          v[e][c] = act ? x0 + x1 : x0;
+          v[e + h][c] = act ? x0 - x1 : x1;
+        }
+      }
+    }
   }
   int le = 0;
   while ((1 << le) < E) ++le;
@@ -566,10 +595,12 @@ __global__ __launch_bounds__(64) void output_blocks_kernel(BlocksArgs a) {
     const bool upper = (lane >> k) & 1;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
+      const bool act = gl[e] - a.lr > k + le;  // the same on both lanes of the pair
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
         const float q = __shfl_xor(v[e][c], 1 << k, 64);
-        v[e][c] = upper ? q - v[e][c] : v[e][c] + q;
+        const float r = upper ? q - v[e][c] : v[e][c] + q;
+        v[e][c] = act ? r : v[e][c];
       }
     }
   }
@@ -577,12 +608,14 @@ __global__ __launch_bounds__(64) void output_blocks_kernel(BlocksArgs a) {
   YT* y = static_cast<YT*>(a.y);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
+    if (lane * E + e >= a.W) continue;
     const int64_t i0 = (int64_t(lane * E + e) << a.lr) + b0;
+    const float scale = a.sc_tab[gl[e]];
     YT o[CB];
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
       const uint32_t neg = (sg[e] >> (8 * c + 7)) << 31;  // sign bit of the c-th byte
-      o[c] = from_f32<YT>(__uint_as_float(__float_as_uint(v[e][c] * a.scale) ^ neg));
+      o[c] = from_f32<YT>(__uint_as_float(__float_as_uint(v[e][c] * scale) ^ neg));
     }
     if (a.vec_y && i0 + CB <= a.m) {
       store_vec<YT, CB>(y + i0, o);
@@ -641,6 +674,9 @@ FusedPlan fused_plan(const glq_layer& L) {
   const int64_t lanes = G / 8;
   int l = 0;
   while ((int64_t(1) << l) < lanes && l < 6) ++l;
+  // a split's chunk (64 columns per lane) must lie in one transform block: the
+  // smallest block of a block-diagonal n_pad bounds it
+  while (l > 0 && L.n_pad % (int64_t(64) << l) != 0) --l;
   p.lpr_log2 = l;
   p.splits = int(G / (int64_t(8) << l));
   p.rps = 64 >> l;
@@ -650,13 +686,25 @@ FusedPlan fused_plan(const glq_layer& L) {
   const int min_per_wg = kThreads / 64;  // at least one row-step per wave
   const int wmax = (p.row_steps + min_per_wg - 1) / min_per_wg;
   if (w > wmax) w = wmax;
-  p.rs_per_wg = (p.row_steps + w - 1) / w;
-  p.wgs_per_split = (p.row_steps + p.rs_per_wg - 1) / p.rs_per_wg;
+  int64_t R;
+  if (is_pow2(L.m_pad)) {
+    p.rs_per_wg = (p.row_steps + w - 1) / w;
+    p.wgs_per_split = (p.row_steps + p.rs_per_wg - 1) / p.rs_per_wg;
+    R = int64_t(p.rs_per_wg) * p.rps;
+    if (p.wgs_per_split == 1 && R > L.m_pad) R = L.m_pad;
+  } else {
+    // block-diagonal m_pad: a power-of-two R of whole row-steps inside the
+    // smallest transform block, about m_pad / w rows
+    R = p.rps;
+    while (R * 2 <= L.m_pad / w && R * 2 <= smallest_block(L.m_pad) && R * 2 <= kRowBuf) R *= 2;
+    p.rs_per_wg = int(R / p.rps);
+    p.wgs_per_split = int(L.m_pad / R);
+  }
   // the workgroups' row blocks must tile m_pad in power-of-two blocks that fit
-  // kRowBuf, and the blocks per split fit the cross-block kernel (W <= 1024)
-  int64_t R = int64_t(p.rs_per_wg) * p.rps;
-  if (p.wgs_per_split == 1 && R > L.m_pad) R = L.m_pad;
-  p.ok = is_pow2(R) && R <= kRowBuf && R * p.wgs_per_split == L.m_pad && p.wgs_per_split <= 1024;
+  // kRowBuf and divide every transform block, and the blocks per split fit the
+  // cross-block kernel (W <= 1024)
+  p.ok = is_pow2(R) && R <= kRowBuf && R * p.wgs_per_split == L.m_pad && L.m_pad % R == 0 &&
+         smallest_block(L.m_pad) >= R && p.wgs_per_split <= 1024;
   p.lr = p.ok ? log2_exact(R) : 0;
   return p;
 }
@@ -694,8 +742,8 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
   a.z_parts = z_parts;
   a.n = L.n;
   a.x_dt = x_dt;
-  a.ln = log2_exact(L.n_pad);
-  a.lk = a.ln - log2_exact(p.splits);
+  a.n_pad = int(L.n_pad);
+  a.lk = 6 + p.lpr_log2;
   const size_t xal = x_dt == GLQ_F32 ? 16 : 8;
   a.vec_in = (reinterpret_cast<uintptr_t>(x) % xal == 0) && (reinterpret_cast<uintptr_t>(L.sign_in) % 4 == 0);
   a.G = int(L.n_pad / 8);
@@ -705,7 +753,8 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
   a.wgs_per_split = p.wgs_per_split;
   a.rs_per_wg = p.rs_per_wg;
   a.lr = p.lr;
-  a.sc_scale = float(1.0 / (sqrt(double(L.n_pad)) * double(kUqMax)));
+  for (int k = 0; k < kLenLog2s; ++k)
+    a.sc_tab[k] = float(1.0 / (sqrt(double(int64_t(1) << k)) * double(kUqMax)));
   a.out_scale = 0.5f * L.wscale;
   a.sr = L.resid_scale;
   a.accumulate = pass == 2;
@@ -736,8 +785,9 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
   b.S = p.splits;
   b.m_pad = int(L.m_pad);
   b.lr = p.lr;
-  b.lw = log2_exact(L.m_pad) - p.lr;
-  b.scale = float(1.0 / sqrt(double(L.m_pad)));
+  b.W = p.wgs_per_split;
+  b.lw = log2_exact(b.W);
+  for (int k = 0; k < kLenLog2s; ++k) b.sc_tab[k] = float(1.0 / sqrt(double(int64_t(1) << k)));
   switch (y_dt) {
     case GLQ_F32: return launch_blocks<float>(b, stream);
     case GLQ_F16: return launch_blocks<half_t>(b, stream);

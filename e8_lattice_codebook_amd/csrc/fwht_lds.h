@@ -31,24 +31,27 @@ __device__ __forceinline__ int swz(int i) { return i ^ ((i >> 5) & 31); }
 // LDS position of element i of a row: XOR of the low 5 bits with bits 5..9, so
 // strided passes spread over the banks (a permutation inside each 32-block).
 
-struct LoadSplitSum {  // sum over s = 0..S-1, in order, of z[s][b][i]
+// The loaders and storers address element i of a transform block that starts at
+// column `off` of its row (off = 0 and one block for a power-of-two length).
+struct LoadSplitSum {  // sum over s = 0..S-1, in order, of z[s][b][off + i]; rows of N
   const float* z;
-  int64_t S, B, N;
+  int64_t S, B, N, off;
   __device__ float operator()(int64_t b, int64_t i) const {
-    float acc = z[b * N + i];
-    for (int64_t s = 1; s < S; ++s) acc += z[(s * B + b) * N + i];
+    float acc = z[b * N + off + i];
+    for (int64_t s = 1; s < S; ++s) acc += z[(s * B + b) * N + off + i];
     return acc;
   }
 };
 
 template <class YT>
-struct StoreOut {  // y[b][i] = RN(sign[i] * v * scale) for i < m
+struct StoreOut {  // y[b][c] = RN(sign[c] * v * scale) for c = off + i < m
   YT* y;
-  int64_t m;
+  int64_t m, off;
   const int8_t* sign;
   float scale;
   __device__ void operator()(int64_t b, int64_t i, float v) const {
-    if (i < m) y[b * m + i] = from_f32<YT>(v * scale * float(sign[i]));
+    const int64_t c = off + i;
+    if (c < m) y[b * m + c] = from_f32<YT>(v * scale * float(sign[c]));
   }
 };
 

@@ -160,11 +160,13 @@ Plan make_plan(int64_t n_pad, int64_t B) {
   p.nb = nb_tile(B);
   const int64_t gpr = n_pad / 8;
   int gl = gl_for(p.nb);
-  while (gl > gpr) gl >>= 1;
+  while (gl > gpr || gpr % gl != 0) gl >>= 1;
   p.gl = gl;
   int64_t lanes = gpr / gl;  // lanes needed to cover a row once
   int lpr_log2 = 0;
   while ((int64_t(1) << lpr_log2) < lanes && lpr_log2 < 6) ++lpr_log2;
+  // the splits must tile the row (a block-diagonal n_pad is not a power of two)
+  while (lpr_log2 > 0 && gpr % (int64_t(gl) << lpr_log2) != 0) --lpr_log2;
   p.lpr_log2 = lpr_log2;
   p.splits = int(gpr / (int64_t(gl) << lpr_log2));
   return p;

@@ -196,11 +196,14 @@ Plan make_plan(int64_t n_pad, int64_t B) {
   p.nb = nb_tile(B);
   const int64_t G = n_pad / 8;
   int gl = gl_for(p.nb);
-  while (gl > G) gl >>= 1;
+  while (gl > G || G % gl != 0) gl >>= 1;
   p.gl = gl;
   const int64_t lanes = G / gl;
   int l = 0;
   while ((int64_t(1) << l) < lanes && l < 6) ++l;
+  // a split's columns (gl groups on each of 2^l lanes) must tile the row: with a
+  // block-diagonal n_pad, G is a multiple of only its smallest block's groups
+  while (l > 0 && G % (int64_t(gl) << l) != 0) --l;
   p.lpr_log2 = l;
   p.splits = int(G / (int64_t(gl) << l));
   return p;

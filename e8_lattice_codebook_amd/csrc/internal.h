@@ -21,6 +21,14 @@ inline int log2_exact(int64_t v) {
   return l;
 }
 inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+// A transform length: a power of two (one block), or a multiple of 64 that is
+// transformed block-diagonally over its binary expansion (largest block first).
+inline int64_t largest_block(int64_t v) {
+  int64_t b = 1;
+  while (b <= v / 2) b *= 2;
+  return b;
+}
+inline int64_t smallest_block(int64_t v) { return v & -v; }
 __host__ __device__ constexpr int log2_exact_dev(int v) { return v <= 1 ? 0 : 1 + log2_exact_dev(v >> 1); }
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -87,11 +95,14 @@ glq_status build_pack(const uint16_t* cb_host, int64_t entries, void* pack_host,
 
 // ---- launchers (return the launch status) -----------------------------------
 
-// Input transform; ws: fp32 [B][N] scratch used only when N > 2^kSingleLog2 and u_dt != F32.
-hipError_t launch_rht_in(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int L, const int8_t* sign,
+// Transforms of length N (block-diagonal when N is not a power of two).
+// Input transform; ws: fp32 [B][N] scratch, used only when a block is longer than
+// 2^kSingleLog2 and u is not fp32 of one block.
+hipError_t launch_rht_in(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t N, const int8_t* sign,
                          void* u, glq_dtype u_dt, float* ws, hipStream_t stream);
-// Output transform of sum_s z[s]; ws: fp32 [B][N] scratch used only when N > 2^kSingleLog2.
-hipError_t launch_rht_out(const float* z, int64_t S, int64_t B, int64_t m, int L, const int8_t* sign,
+// Output transform of sum_s z[s] (rows of N); ws: fp32 [B][N] scratch used only
+// when a block is longer than 2^kSingleLog2.
+hipError_t launch_rht_out(const float* z, int64_t S, int64_t B, int64_t m, int64_t N, const int8_t* sign,
                           void* y, glq_dtype y_dt, float* ws, hipStream_t stream);
 
 hipError_t launch_dequant(const glq_layer& layer, void* w, glq_dtype w_dt, hipStream_t stream);
@@ -135,7 +146,7 @@ bool gemm_lds_supported(const glq_layer& layer);
 size_t tiled_u_bytes(int64_t M, int64_t n_pad);
 hipError_t launch_gemm_lds(const glq_layer& layer, const half_t* u16, int64_t M, bool tiled, float* z,
                            hipStream_t stream, bool accumulate = false);
-hipError_t launch_rht_in_tiled(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int L, const int8_t* sign,
+hipError_t launch_rht_in_tiled(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t N, const int8_t* sign,
                                half_t* u16, float* ws, hipStream_t stream);
 hipError_t launch_gemm(const glq_layer& layer, const half_t* u16, int64_t M, float* z, hipStream_t stream,
                        bool accumulate = false);

@@ -7,6 +7,12 @@
 // changed": separate input_rht / output_rht operations, one-workgroup transforms
 // up to 16384 and a separate path above that.
 //
+// A length that is not a power of two is transformed block-diagonally: its
+// blocks are the powers of two of its binary expansion, largest first, each
+// transformed on its own and scaled by 1/sqrt(block length) (glq 0.5.1, table
+// "Bit widths" and the note below it: 2688 = 2048 + 512 + 128, no padding).  A
+// power of two is one block.
+//
 // Transform order is Sylvester's: butterflies (a, b) -> (a + b, a - b) on every
 // index bit.  One workgroup transforms one row of up to 2^14 fp32 values in LDS:
 // the first 4 bits in registers straight from global memory, then radix-16
@@ -23,12 +29,13 @@ namespace {
 
 // ---- element loaders / storers ------------------------------------------------
 template <class XT>
-struct LoadSignedX {  // x [B][n] -> sign[i] * x[b][i], zero beyond n
+struct LoadSignedX {  // x [B][n] -> sign[c] * x[b][c] at c = off + i, zero beyond n
   const XT* x;
-  int64_t n;
+  int64_t n, off;
   const int8_t* sign;
   __device__ float operator()(int64_t b, int64_t i) const {
-    return i < n ? to_f32<XT>(x[b * n + i]) * float(sign[i]) : 0.0f;
+    const int64_t c = off + i;
+    return c < n ? to_f32<XT>(x[b * n + c]) * float(sign[c]) : 0.0f;
   }
 };
 
@@ -39,25 +46,27 @@ struct LoadF32 {  // p [B][N]
 };
 
 template <class UT>
-struct StoreScaled {  // u[b][i] = RN(v * scale)
+struct StoreScaled {  // u[b][off + i] = RN(v * scale), rows of N
   UT* u;
-  int64_t N;
+  int64_t N, off;
   float scale;
-  __device__ void operator()(int64_t b, int64_t i, float v) const { u[b * N + i] = from_f32<UT>(v * scale); }
+  __device__ void operator()(int64_t b, int64_t i, float v) const { u[b * N + off + i] = from_f32<UT>(v * scale); }
 };
 
-// u16 in the prefill matmul's fragment order: token b, column i of group g = i / 8
-// (k-step ks = g mod KS, lane quarter q = g / KS, KS = N / 32) at
-// (((b / 16) KS + ks) 4 + q) 128 + (b mod 16) 8 + i mod 8
+// u16 in the prefill matmul's fragment order: token b, column c = off + i of group
+// g = c / 8 (k-step ks = g mod KS, lane quarter q = g / KS, KS = n_pad / 32) at
+// (((b / 16) KS + ks) 4 + q) 128 + (b mod 16) 8 + c mod 8
 struct StoreTiledHalf {
   half_t* u;
-  int ks_log2;
+  uint32_t KS;
+  int64_t off;
   float scale;
   __device__ void operator()(int64_t b, int64_t i, float v) const {
-    const int64_t g = i >> 3;
-    const int64_t ks = g & ((int64_t(1) << ks_log2) - 1), q = g >> ks_log2;
-    const int64_t off = (((((b >> 4) << ks_log2) + ks) * 4 + q) * 16 + (b & 15)) * 8 + (i & 7);
-    u[off] = from_f32<half_t>(v * scale);
+    const int64_t c = off + i;
+    const uint32_t g = uint32_t(c >> 3);
+    const uint32_t q = g / KS, ks = g - q * KS;
+    const int64_t o = ((((b >> 4) * KS + ks) * 4 + q) * 16 + (b & 15)) * 8 + (c & 7);
+    u[o] = from_f32<half_t>(v * scale);
   }
 };
 
@@ -136,50 +145,65 @@ hipError_t run_cols(const Load& ld, const Store& st, int64_t B, int seg_log2, in
   return hipGetLastError();
 }
 
-template <class XT, class UT>
-hipError_t rht_in_typed(const void* x, int64_t B, int64_t n, int L, const int8_t* sign, void* u, float* ws,
-                        hipStream_t stream) {
-  const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
-  const LoadSignedX<XT> ld{static_cast<const XT*>(x), n, sign};
+// One block of 2^L columns at column `off`: one-workgroup rows up to 2^14, else the
+// row pass into `mid` (rows of 2^L floats) and the column pass from it.
+template <class Load, class Store>
+hipError_t run_block(const Load& ld, const Store& st, int64_t B, int L, float* mid, hipStream_t stream) {
+  if (L <= kSingleLog2) return run_rows(ld, st, B, L, stream);
   const int64_t N = int64_t(1) << L;
-  if (L <= kSingleLog2) {
-    return run_rows(ld, StoreScaled<UT>{static_cast<UT*>(u), N, scale}, B, L, stream);
-  }
   int lr, lc;
   fwht_split(L, &lr, &lc);
-  float* mid = (sizeof(UT) == 4) ? reinterpret_cast<float*>(u) : ws;
-  hipError_t e = run_rows(SegLoad<LoadSignedX<XT>>{ld, lr, lc}, SegStore<StoreF32>{StoreF32{mid, N}, lr, lc},
-                          B << lc, lr, stream);
+  hipError_t e = run_rows(SegLoad<Load>{ld, lr, lc}, SegStore<StoreF32>{StoreF32{mid, N}, lr, lc}, B << lc, lr,
+                          stream);
   if (e != hipSuccess) return e;
-  return run_cols(LoadF32{mid, N}, StoreScaled<UT>{static_cast<UT*>(u), N, scale}, B, lr, lc, stream);
+  return run_cols(LoadF32{mid, N}, st, B, lr, lc, stream);
+}
+
+// the blocks of length N, largest first: calls f(offset, log2 length)
+template <class F>
+hipError_t for_blocks(int64_t N, F f) {
+  int64_t off = 0;
+  for (int L = 62; L >= 0; --L) {
+    if (!((N >> L) & 1)) continue;
+    hipError_t e = f(off, L);
+    if (e != hipSuccess) return e;
+    off += int64_t(1) << L;
+  }
+  return hipSuccess;
+}
+
+template <class XT, class UT>
+hipError_t rht_in_typed(const void* x, int64_t B, int64_t n, int64_t N, const int8_t* sign, void* u, float* ws,
+                        hipStream_t stream) {
+  return for_blocks(N, [&](int64_t off, int L) {
+    const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
+    const LoadSignedX<XT> ld{static_cast<const XT*>(x), n, off, sign};
+    // an fp32 u is its own two-pass buffer when it is one block
+    float* mid = (sizeof(UT) == 4 && off == 0 && N == (int64_t(1) << L)) ? reinterpret_cast<float*>(u) : ws;
+    return run_block(ld, StoreScaled<UT>{static_cast<UT*>(u), N, off, scale}, B, L, mid, stream);
+  });
 }
 
 template <class XT>
-hipError_t rht_in_x(const void* x, int64_t B, int64_t n, int L, const int8_t* sign, void* u, glq_dtype u_dt,
+hipError_t rht_in_x(const void* x, int64_t B, int64_t n, int64_t N, const int8_t* sign, void* u, glq_dtype u_dt,
                     float* ws, hipStream_t stream) {
   switch (u_dt) {
-    case GLQ_F32: return rht_in_typed<XT, float>(x, B, n, L, sign, u, ws, stream);
-    case GLQ_F16: return rht_in_typed<XT, half_t>(x, B, n, L, sign, u, ws, stream);
-    case GLQ_BF16: return rht_in_typed<XT, bf16_t>(x, B, n, L, sign, u, ws, stream);
+    case GLQ_F32: return rht_in_typed<XT, float>(x, B, n, N, sign, u, ws, stream);
+    case GLQ_F16: return rht_in_typed<XT, half_t>(x, B, n, N, sign, u, ws, stream);
+    case GLQ_BF16: return rht_in_typed<XT, bf16_t>(x, B, n, N, sign, u, ws, stream);
   }
   return hipErrorInvalidValue;
 }
 
 // input transform into the prefill matmul's fragment order (fp16)
 template <class XT>
-hipError_t rht_in_tiled_x(const void* x, int64_t B, int64_t n, int L, const int8_t* sign, half_t* u16, float* ws,
-                          hipStream_t stream) {
-  const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
-  const LoadSignedX<XT> ld{static_cast<const XT*>(x), n, sign};
-  const int64_t N = int64_t(1) << L;
-  const StoreTiledHalf st{u16, L - 5, scale};
-  if (L <= kSingleLog2) return run_rows(ld, st, B, L, stream);
-  int lr, lc;
-  fwht_split(L, &lr, &lc);
-  hipError_t e = run_rows(SegLoad<LoadSignedX<XT>>{ld, lr, lc}, SegStore<StoreF32>{StoreF32{ws, N}, lr, lc}, B << lc,
-                          lr, stream);
-  if (e != hipSuccess) return e;
-  return run_cols(LoadF32{ws, N}, st, B, lr, lc, stream);
+hipError_t rht_in_tiled_x(const void* x, int64_t B, int64_t n, int64_t N, const int8_t* sign, half_t* u16,
+                          float* ws, hipStream_t stream) {
+  return for_blocks(N, [&](int64_t off, int L) {
+    const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
+    const LoadSignedX<XT> ld{static_cast<const XT*>(x), n, off, sign};
+    return run_block(ld, StoreTiledHalf{u16, uint32_t(N / 32), off, scale}, B, L, ws, stream);
+  });
 }
 
 // ---- output transform of one row per workgroup, 4096 <= N <= 32768 ---------------------
@@ -213,17 +237,19 @@ struct StoreLdsRow {  // element i of the row -> its swizzled LDS position
   __device__ void operator()(int64_t, int64_t i, float v) const { buf[swz(int(i))] = v; }
 };
 
+// The block is columns off .. off + N - 1 of rows of ldz partials (z + off and
+// sign + off are passed in) and of m outputs, mv = min(N, m - off) of them kept.
 template <class YT, int IT>
-__global__ __launch_bounds__(1024) void rows_out_kernel(const float* __restrict__ z, int S, int B, int64_t m,
-                                                       const int8_t* __restrict__ sign, YT* __restrict__ y,
-                                                       float scale, int vec_y) {
+__global__ __launch_bounds__(1024) void rows_out_kernel(const float* __restrict__ z, int64_t ldz, int S, int B,
+                                                       int64_t m, int mv, const int8_t* __restrict__ sign,
+                                                       YT* __restrict__ y, float scale, int vec_y) {
   extern __shared__ float buf[];
   constexpr int N = 4096 * IT;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int c = tid * 4;
   float4 acc[IT];
-  const float* zr = z + int64_t(row) * N;
+  const float* zr = z + int64_t(row) * ldz;
 #pragma unroll
   for (int i = 0; i < IT; ++i) acc[i] = *reinterpret_cast<const float4*>(zr + c + 4096 * i);
   constexpr int UN = IT >= 8 ? 1 : 8 / IT;
@@ -234,7 +260,7 @@ __global__ __launch_bounds__(1024) void rows_out_kernel(const float* __restrict_
     for (int u = 0; u < UN; ++u) {
 #pragma unroll
       for (int i = 0; i < IT; ++i)
-        v[u][i] = *reinterpret_cast<const float4*>(zr + (int64_t(s + u) * B) * N + c + 4096 * i);
+        v[u][i] = *reinterpret_cast<const float4*>(zr + (int64_t(s + u) * B) * ldz + c + 4096 * i);
     }
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
@@ -250,7 +276,7 @@ __global__ __launch_bounds__(1024) void rows_out_kernel(const float* __restrict_
   for (; s < S; ++s) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      const float4 v = *reinterpret_cast<const float4*>(zr + (int64_t(s) * B) * N + c + 4096 * i);
+      const float4 v = *reinterpret_cast<const float4*>(zr + (int64_t(s) * B) * ldz + c + 4096 * i);
       acc[i].x += v.x;
       acc[i].y += v.y;
       acc[i].z += v.z;
@@ -275,7 +301,7 @@ __global__ __launch_bounds__(1024) void rows_out_kernel(const float* __restrict_
   __syncthreads();
   YT* yr = y + int64_t(row) * m;
   if (vec_y) {
-    for (int o = tid * 8; o < m; o += 1024 * 8) {
+    for (int o = tid * 8; o < mv; o += 1024 * 8) {
       const uint2 sg = *reinterpret_cast<const uint2*>(sign + o);
       float v[8];
 #pragma unroll
@@ -286,7 +312,7 @@ __global__ __launch_bounds__(1024) void rows_out_kernel(const float* __restrict_
       store8<YT>(yr + o, v);
     }
   } else {
-    for (int o = tid; o < m; o += 1024) {
+    for (int o = tid; o < mv; o += 1024) {
       const uint32_t neg = sign[o] < 0 ? 0x80000000u : 0u;
       yr[o] = from_f32<YT>(__uint_as_float(__float_as_uint(buf[swz(o)] * scale) ^ neg));
     }
@@ -294,21 +320,24 @@ __global__ __launch_bounds__(1024) void rows_out_kernel(const float* __restrict_
 }
 
 template <class YT>
-hipError_t rht_out_typed(const float* z, int64_t S, int64_t B, int64_t m, int L, const int8_t* sign, void* y,
-                         float* ws, hipStream_t stream) {
+hipError_t rht_out_block(const float* z, int64_t S, int64_t B, int64_t m, int64_t ldz, int64_t off, int L,
+                         const int8_t* sign, void* y, float* ws, hipStream_t stream) {
   const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
-  const int64_t N = int64_t(1) << L;
   if (L >= 12 && L <= 15) {
-    // 16-byte output stores need y 16-byte aligned, m % 8 == 0 and 8-byte aligned signs
-    const int vec_y = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && m % 8 == 0 &&
-                      (reinterpret_cast<uintptr_t>(sign) % 8 == 0);
+    const int64_t mv = m - off < (int64_t(1) << L) ? m - off : (int64_t(1) << L);
+    // 16-byte output stores need y + off 16-byte aligned, mv % 8 == 0 and 8-byte aligned signs
+    YT* yp = static_cast<YT*>(y) + off;
+    const int8_t* sg = sign + off;
+    const int vec_y = (reinterpret_cast<uintptr_t>(static_cast<YT*>(y) + off) % 16 == 0) && m % 8 == 0 &&
+                      mv % 8 == 0 && (reinterpret_cast<uintptr_t>(sg) % 8 == 0);
+    const float* zb = z + off;
     const size_t shmem = size_t(4) << L;
     const dim3 grid{unsigned(B)}, block{1024};
-    YT* yp = static_cast<YT*>(y);
+    const int S_ = int(S), B_ = int(B), mv_ = int(mv);
     switch (L) {
-      case 12: hipLaunchKernelGGL((rows_out_kernel<YT, 1>), grid, block, shmem, stream, z, int(S), int(B), m, sign, yp, scale, vec_y); break;
-      case 13: hipLaunchKernelGGL((rows_out_kernel<YT, 2>), grid, block, shmem, stream, z, int(S), int(B), m, sign, yp, scale, vec_y); break;
-      case 14: hipLaunchKernelGGL((rows_out_kernel<YT, 4>), grid, block, shmem, stream, z, int(S), int(B), m, sign, yp, scale, vec_y); break;
+      case 12: hipLaunchKernelGGL((rows_out_kernel<YT, 1>), grid, block, shmem, stream, zb, ldz, S_, B_, m, mv_, sg, yp, scale, vec_y); break;
+      case 13: hipLaunchKernelGGL((rows_out_kernel<YT, 2>), grid, block, shmem, stream, zb, ldz, S_, B_, m, mv_, sg, yp, scale, vec_y); break;
+      case 14: hipLaunchKernelGGL((rows_out_kernel<YT, 4>), grid, block, shmem, stream, zb, ldz, S_, B_, m, mv_, sg, yp, scale, vec_y); break;
       default: {
         // 128 KiB of dynamic LDS: raise the kernel's limit once
         static bool lds_set = false;
@@ -318,52 +347,56 @@ hipError_t rht_out_typed(const float* z, int64_t S, int64_t B, int64_t m, int L,
           if (e != hipSuccess) return e;
           lds_set = true;
         }
-        hipLaunchKernelGGL((rows_out_kernel<YT, 8>), grid, block, shmem, stream, z, int(S), int(B), m, sign, yp, scale,
-                           vec_y);
+        hipLaunchKernelGGL((rows_out_kernel<YT, 8>), grid, block, shmem, stream, zb, ldz, S_, B_, m, mv_, sg, yp,
+                           scale, vec_y);
         break;
       }
     }
     return hipGetLastError();
   }
-  const LoadSplitSum ld{z, S, B, N};
-  const StoreOut<YT> st{static_cast<YT*>(y), m, sign, scale};
-  if (L <= kSingleLog2) return run_rows(ld, st, B, L, stream);
-  int lr, lc;
-  fwht_split(L, &lr, &lc);
-  hipError_t e = run_rows(SegLoad<LoadSplitSum>{ld, lr, lc}, SegStore<StoreF32>{StoreF32{ws, N}, lr, lc}, B << lc,
-                          lr, stream);
-  if (e != hipSuccess) return e;
-  return run_cols(LoadF32{ws, N}, st, B, lr, lc, stream);
+  const LoadSplitSum ld{z, S, B, ldz, off};
+  const StoreOut<YT> st{static_cast<YT*>(y), m, off, sign, scale};
+  return run_block(ld, st, B, L, ws, stream);
+}
+
+template <class YT>
+hipError_t rht_out_typed(const float* z, int64_t S, int64_t B, int64_t m, int64_t N, const int8_t* sign, void* y,
+                         float* ws, hipStream_t stream) {
+  return for_blocks(N, [&](int64_t off, int L) {
+    // blocks wholly past m (possible only with padding) are not computed
+    if (off >= m) return hipSuccess;
+    return rht_out_block<YT>(z, S, B, m, N, off, L, sign, y, ws, stream);
+  });
 }
 
 }  // namespace
 
-hipError_t launch_rht_in(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int L, const int8_t* sign, void* u,
-                         glq_dtype u_dt, float* ws, hipStream_t stream) {
+hipError_t launch_rht_in(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t N, const int8_t* sign,
+                         void* u, glq_dtype u_dt, float* ws, hipStream_t stream) {
   switch (x_dt) {
-    case GLQ_F32: return rht_in_x<float>(x, B, n, L, sign, u, u_dt, ws, stream);
-    case GLQ_F16: return rht_in_x<half_t>(x, B, n, L, sign, u, u_dt, ws, stream);
-    case GLQ_BF16: return rht_in_x<bf16_t>(x, B, n, L, sign, u, u_dt, ws, stream);
+    case GLQ_F32: return rht_in_x<float>(x, B, n, N, sign, u, u_dt, ws, stream);
+    case GLQ_F16: return rht_in_x<half_t>(x, B, n, N, sign, u, u_dt, ws, stream);
+    case GLQ_BF16: return rht_in_x<bf16_t>(x, B, n, N, sign, u, u_dt, ws, stream);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_rht_in_tiled(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int L, const int8_t* sign,
+hipError_t launch_rht_in_tiled(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t N, const int8_t* sign,
                                half_t* u16, float* ws, hipStream_t stream) {
   switch (x_dt) {
-    case GLQ_F32: return rht_in_tiled_x<float>(x, B, n, L, sign, u16, ws, stream);
-    case GLQ_F16: return rht_in_tiled_x<half_t>(x, B, n, L, sign, u16, ws, stream);
-    case GLQ_BF16: return rht_in_tiled_x<bf16_t>(x, B, n, L, sign, u16, ws, stream);
+    case GLQ_F32: return rht_in_tiled_x<float>(x, B, n, N, sign, u16, ws, stream);
+    case GLQ_F16: return rht_in_tiled_x<half_t>(x, B, n, N, sign, u16, ws, stream);
+    case GLQ_BF16: return rht_in_tiled_x<bf16_t>(x, B, n, N, sign, u16, ws, stream);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_rht_out(const float* z, int64_t S, int64_t B, int64_t m, int L, const int8_t* sign, void* y,
+hipError_t launch_rht_out(const float* z, int64_t S, int64_t B, int64_t m, int64_t N, const int8_t* sign, void* y,
                           glq_dtype y_dt, float* ws, hipStream_t stream) {
   switch (y_dt) {
-    case GLQ_F32: return rht_out_typed<float>(z, S, B, m, L, sign, y, ws, stream);
-    case GLQ_F16: return rht_out_typed<half_t>(z, S, B, m, L, sign, y, ws, stream);
-    case GLQ_BF16: return rht_out_typed<bf16_t>(z, S, B, m, L, sign, y, ws, stream);
+    case GLQ_F32: return rht_out_typed<float>(z, S, B, m, N, sign, y, ws, stream);
+    case GLQ_F16: return rht_out_typed<half_t>(z, S, B, m, N, sign, y, ws, stream);
+    case GLQ_BF16: return rht_out_typed<bf16_t>(z, S, B, m, N, sign, y, ws, stream);
   }
   return hipErrorInvalidValue;
 }

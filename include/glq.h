@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define GLQ_ABI_VERSION 2
+#define GLQ_ABI_VERSION 3
 #define GLQ_CODEBOOK_ENTRIES 65536
 #define GLQ_RESID8_ENTRIES 256
 #define GLQ_MAX_PAD (1 << 20)
@@ -79,8 +79,16 @@ typedef enum glq_dtype {
 
 /*
  * One quantized layer.  All pointers are device pointers.
- *   n, n_pad        input features and their padded size (power of two)
- *   m, m_pad        output features and their padded size (power of two)
+ *   n, n_pad        input features and the input transform's length, n <= n_pad
+ *   m, m_pad        output features and the output transform's length, m <= m_pad
+ *                   A transform length is a power of two in [8, GLQ_MAX_PAD]
+ *                   (x zero-padded to it, y truncated from it), or a multiple of
+ *                   64 below GLQ_MAX_PAD whose transform is block-diagonal: its
+ *                   blocks are the powers of two of its binary expansion, largest
+ *                   first, each transformed on its own and orthonormal ("Bit
+ *                   widths", note below the table: non-power-of-two sizes use a
+ *                   block-diagonal transform, e.g. 2688 = 2048 + 512 + 128, so
+ *                   nothing is padded).  n_pad = n and m_pad = m store no padding.
  *   resid_bits      0: 2 bpw, primary stage only ("Bit widths", row 2)
  *                   8: 3 bpw, + 8-bit index into a 256-entry residual codebook
  *                   16: 4 bpw, + 16-bit index into a 65,536-entry residual codebook
@@ -195,13 +203,16 @@ glq_status glq_slot_codes(const void* cb_pack, const uint16_t* idx, int64_t coun
 
 /*
  * glq_input_rht — u = H_{n_pad} (sign_in * [x, 0...]) / sqrt(n_pad) for each of B
- * rows ("How it works", item 2; Glq v0.3.2 "What changed": input_rht).
+ * rows ("How it works", item 2; Glq v0.3.2 "What changed": input_rht).  When
+ * n_pad is not a power of two (a multiple of 64), H_{n_pad} / sqrt(n_pad) stands
+ * for the block-diagonal transform of the layer description: block b of length L
+ * gets H_L / sqrt(L).
  *   x          device [B][n] in x_dt (F32, F16 or BF16)
  *   sign_in    device int8 [n_pad]
  *   u          device [B][n_pad] in u_dt (F32, F16 or BF16); rounded to nearest-even
  *   workspace  device, workspace_bytes >= glq_input_rht_workspace_bytes(B, n_pad, u_dt)
  *              (0 bytes for most shapes; NULL allowed then), 256-byte aligned
- * Accumulation is fp32.  n_pad above 16384 runs as two passes (H = H_a (x) H_b).
+ * Accumulation is fp32.  A block above 16384 runs as two passes (H = H_a (x) H_b).
  * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_DTYPE, GLQ_ERR_WORKSPACE, GLQ_ERR_HIP.
  */
 size_t glq_input_rht_workspace_bytes(int64_t B, int64_t n_pad, glq_dtype u_dt);
@@ -213,7 +224,8 @@ glq_status glq_input_rht(const void* x, glq_dtype x_dt, int64_t B, int64_t n, in
  * glq_output_rht — y = (sign_out * H_{m_pad} z / sqrt(m_pad))[:, 0:m] with
  * z = sum over s = 0 .. splits-1, in that order, of z_parts[s] (Glq v0.3.2,
  * "What changed": output_rht; "Inference kernels": fixed-order reduction of
- * split partial sums instead of atomics).
+ * split partial sums instead of atomics); block-diagonal when m_pad is not a
+ * power of two, as for glq_input_rht.
  *   z_parts    device fp32 [splits][B][m_pad]
  *   y          device [B][m] in y_dt (F32, F16 or BF16)
  *   workspace  device, >= glq_output_rht_workspace_bytes(B, m_pad), 256-byte aligned

@@ -38,7 +38,7 @@ def test_header_declarations_are_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.glq_abi_version() == 2
+    assert lib.glq_abi_version() == 3
     for s in range(9):
         assert lib.glq_status_string(s)
     assert lib.glq_status_string(0) == b"ok"
@@ -68,6 +68,11 @@ def test_workspace_queries():
     assert lib.glq_input_rht_workspace_bytes(2, 32768, 0) == 0
     assert lib.glq_output_rht_workspace_bytes(3, 16384) == 0
     assert lib.glq_output_rht_workspace_bytes(3, 32768) == 3 * 32768 * 4
+    # block-diagonal lengths: scratch when a block is above 16384, also for fp32 u
+    assert lib.glq_input_rht_workspace_bytes(2, 16384 + 64, 1) == 0
+    assert lib.glq_input_rht_workspace_bytes(2, 32768 + 1024, 0) == 2 * (32768 + 1024) * 4
+    assert lib.glq_output_rht_workspace_bytes(3, 32768 + 64) == 3 * (32768 + 64) * 4
+    assert lib.glq_input_rht_workspace_bytes(2, 100, 0) == 0   # not a transform length
     L = fake_layer(n=5120, n_pad=8192, m=32768, m_pad=32768, resid_bits=16)
     one = lib.glq_e8rht_linear_workspace_bytes(ctypes.byref(L), 1)
     # B = 1 path: 2 split partials of m_pad fp32
@@ -107,7 +112,10 @@ class TestValidation:
         assert linear_status(fake_layer(resid_bits=8, cb2_pack=None)) == 1
 
     def test_shapes(self):
-        assert linear_status(fake_layer(n_pad=384)) == 2          # not a power of two
+        assert linear_status(fake_layer(n_pad=384, n=384)) == 7   # block-diagonal 256 + 128: valid, no GPU to launch on
+        assert linear_status(fake_layer(n_pad=392, n=392)) == 2   # neither a power of two nor a multiple of 64
+        assert linear_status(fake_layer(m_pad=11008, m=11008)) == 7
+        assert linear_status(fake_layer(m_pad=(1 << 20) + 64)) == 2
         assert linear_status(fake_layer(n_pad=4, n=4)) == 2       # below 8
         assert linear_status(fake_layer(m_pad=1 << 21)) == 2      # above 2^20
         assert linear_status(fake_layer(n=257)) == 2              # n > n_pad
