@@ -61,6 +61,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--block-steps", type=int, default=500)
+    ap.add_argument("--no-recipes", action="store_true", help="skip the 5-8 bpw decode measurement")
+    ap.add_argument("--recipe-steps", type=int, default=300)
+    ap.add_argument("--no-blockdiag", action="store_true", help="skip the unpadded (block-diagonal) measurement")
     ap.add_argument("--index-format", choices=["slot", "codebook"], default="slot",
                     help="16-bit index arrays as slot codes (default) or as codebook indices")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -220,6 +223,12 @@ def main():
 
     if not args.no_block:
         result["block_b1"] = bench_block_graph(glq, synth, cb, dev, args, log)
+
+    if not args.no_recipes and B == 1:
+        result["recipes_b1"] = bench_recipes(glq, synth, cb, dev, args, log, value)
+
+    if not args.no_blockdiag and B == 1:
+        result["blockdiag_b1"] = bench_blockdiag(glq, synth, cb, dev, args, log, ms_per_step)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host_layers, wl, B, log)
@@ -453,6 +462,112 @@ def bench_block_graph(glq, synth, cb, dev, args, log):
         "replay_equals_eager": bool(same),
         "launches_per_block": 2 * len(host),
     }
+
+
+def bench_recipes(glq, synth, cb, dev, args, log, value_4bpw):
+    """The Devstral MLP decode step at B = 1 with the 5-8 bpw recipes (16-bit
+    primary and residual stage plus one or two further 8/16-bit stages), same
+    activations, rotating copies and loop as the 4 bpw measurement."""
+    import numpy as np
+    import torch
+
+    wl = synth.WORKLOADS["devstral_mlp"]
+    xs, ys = [], []
+    for k, s in enumerate(wl.layers):
+        sp = s.padded()
+        _, raw = synth.make_x(sp.n, 1, wl.act_dtype, wl.seed, k)
+        xs.append(torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16))
+        ys.append(torch.empty((1, sp.m), dtype=torch.bfloat16, device=dev))
+    out = {"workload": "Devstral-Small-24B MLP decode (gate, up, down), B=1, bf16 activations; recipes of the "
+                       "bit-width table: 16+16+8, 16+16+16, 16+16+16+8, 16+16+16+16 bits per 8 weights",
+           "index_format": args.index_format, "steps": args.recipe_steps, "unit": "GB/s",
+           "value_4bpw": round(value_4bpw, 2), "by_bpw": {}}
+    for bpw in (5, 6, 7, 8):
+        resid_bits, extra_bits = synth.RECIPES[bpw]
+        host = [synth.make_layer(s, resid_bits, wl.seed, k, extra_bits=extra_bits) for k, s in enumerate(wl.layers)]
+        idx_bytes = sum(l.index_bytes() for l in host)
+        copies = max(2, math.ceil((1 << 30) / idx_bytes))
+        qls = [[glq.QuantizedLayer.from_synth(l, cb) for l in host] for _ in range(copies)]
+        if args.index_format == "slot":
+            qls = [[q.to_slot_codes() for q in row] for row in qls]
+        del host
+        ws = torch.zeros(max(glq.linear_workspace_bytes(q, 1) for q in qls[0]), dtype=torch.uint8, device=dev)
+        step_bytes = sum(q.index_bytes() + (q.n + q.m) * 2 + q.n_pad + q.m_pad for q in qls[0])
+
+        def step(i):
+            row = qls[i % copies]
+            for k in range(len(row)):
+                glq.e8rht_linear(row[k], xs[k], out=ys[k], workspace=ws)
+
+        for i in range(50):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.recipe_steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.recipe_steps
+        gbs = step_bytes / (ms * 1e-3) / 1e9
+        log("bench: %d bpw Devstral MLP B=1: %.4f ms/step, %.1f GB/s (%d copies)" % (bpw, ms, gbs, copies))
+        out["by_bpw"][str(bpw)] = {"ms_per_step": round(ms, 5), "value": round(gbs, 2),
+                                   "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": step_bytes,
+                                   "launches_per_layer": 3}
+        del qls, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_blockdiag(glq, synth, cb, dev, args, log, padded_ms):
+    """The Devstral MLP decode step at B = 1 with unpadded layers: 5120 is
+    transformed block-diagonally (4096 + 1024) instead of being padded to 8192, so
+    gate and up store 5120 / 8 groups per row and down 5120 rows."""
+    import numpy as np
+    import torch
+
+    wl = synth.WORKLOADS["devstral_mlp"]
+    host = [synth.make_layer(s, wl.resid_bits, wl.seed, k, block_diag=True) for k, s in enumerate(wl.layers)]
+    idx_bytes = sum(l.index_bytes() for l in host)
+    copies = max(2, math.ceil((1 << 30) / idx_bytes))
+    qls = [[glq.QuantizedLayer.from_synth(l, cb) for l in host] for _ in range(copies)]
+    if args.index_format == "slot":
+        qls = [[q.to_slot_codes() for q in row] for row in qls]
+    xs, ys = [], []
+    for k, l in enumerate(host):
+        _, raw = synth.make_x(l.n, 1, wl.act_dtype, wl.seed, k)
+        xs.append(torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16))
+        ys.append(torch.empty((1, l.m), dtype=torch.bfloat16, device=dev))
+    del host
+    ws = torch.zeros(max(glq.linear_workspace_bytes(q, 1) for q in qls[0]), dtype=torch.uint8, device=dev)
+    step_bytes = sum(q.index_bytes() + (q.n + q.m) * 2 + q.n_pad + q.m_pad for q in qls[0])
+
+    def step(i):
+        row = qls[i % copies]
+        for k in range(len(row)):
+            glq.e8rht_linear(row[k], xs[k], out=ys[k], workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    log("bench: unpadded Devstral MLP B=1: %.4f ms/step, %.1f GB/s (padded %.4f ms/step)" % (ms, gbs, padded_ms))
+    out = {"workload": "Devstral-Small-24B MLP decode, B=1, bf16, 4 bpw, unpadded: gate, up 5120 -> 32768 and down "
+                       "32768 -> 5120 with block-diagonal transforms over 5120 = 4096 + 1024",
+           "index_format": args.index_format, "steps": args.steps, "ms_per_step": round(ms, 5),
+           "value": round(gbs, 2), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "algorithmic_bytes_per_step": step_bytes, "index_bytes_per_step": idx_bytes,
+           "padded_ms_per_step": round(padded_ms, 5), "step_speedup_vs_padded": round(padded_ms / ms, 3)}
+    del qls, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(layers, wl, B, log, min_seconds=10.0):

@@ -85,10 +85,12 @@ __device__ __forceinline__ float x_at(const void* x, int dt, int64_t j) {
 
 __device__ __forceinline__ float sign_f(uint32_t w, int k) { return float(int8_t(uint8_t(w >> (8 * k)))); }
 
-struct StoreZ {  // element i of a workgroup's row block -> its place in z_parts
+struct StoreZ {  // element i < lim of a workgroup's rows -> its place in z_parts
   float* p;
-  int acc;
-  __device__ void operator()(int64_t, int64_t i, float v) const { p[i] = acc ? p[i] + v : v; }
+  int acc, lim;
+  __device__ void operator()(int64_t, int64_t i, float v) const {
+    if (i < lim) p[i] = acc ? p[i] + v : v;
+  }
 };
 
 struct StoreLds {  // element i of the row -> its swizzled LDS position
@@ -156,14 +158,15 @@ __device__ __forceinline__ void x_accumulate(const XRaw& r, int dt, bool neg, fl
 // bits; then every thread writes 8 consecutive outputs at a time, scaled,
 // sign-flipped (sign_out packed to one bit per output in LDS beforehand) and
 // cast, with 16-byte stores where y allows.
-// H_R on the workgroup's R = 64 E rows in rowbuf by one wave: lane l holds rows
-// l E .. l E + E - 1 (bits below log2 E in registers, the six lane bits by
-// shuffles), then stores them to p with 16-byte stores.
+// H_R on the R = 64 E rows base .. base + R - 1 of the workgroup's rows in rowbuf
+// by one wave: lane l holds rows base + l E .. + E - 1 (bits below log2 E in
+// registers, the six lane bits by shuffles), then stores them to p with 16-byte
+// stores.
 template <int E>
-__device__ __forceinline__ void wave_block_transform(const float* rowbuf, float* p, int lane, int acc) {
+__device__ __forceinline__ void wave_block_transform(const float* rowbuf, int base, float* p, int lane, int acc) {
   float v[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) v[e] = rowbuf[swz(lane * E + e)];
+  for (int e = 0; e < E; ++e) v[e] = rowbuf[swz(base + lane * E + e)];
   fwht_reg<E>(v);
 #pragma unroll
   for (int k = 0; k < 6; ++k) {
@@ -439,20 +442,29 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
     }
   }
 
-  // ---- step 4: H_R of the workgroup's rows into z_parts[split]
+  // ---- step 4: H_R of each of the workgroup's row blocks into z_parts[split]
   {
-    float* zb = a.z_parts + int64_t(split) * a.m_pad + (int64_t(wg) << a.lr);
+    const int rows_wg = a.rs_per_wg * RPS;
+    const int row0 = wg * rows_wg;
+    const int rows = min(rows_wg, a.m_pad - row0);  // whole row blocks: R divides m_pad
+    float* zb = a.z_parts + int64_t(split) * a.m_pad + row0;
     if (a.lr >= 8) {
       __syncthreads();
-      if (tid < 64) {
+      const int nrb = rows >> a.lr;
+      for (int j = wave; j < nrb; j += kThreads / 64) {
+        const int base = j << a.lr;
         switch (a.lr) {
-          case 8: wave_block_transform<4>(rowbuf, zb, tid, a.accumulate); break;
-          case 9: wave_block_transform<8>(rowbuf, zb, tid, a.accumulate); break;
-          default: wave_block_transform<16>(rowbuf, zb, tid, a.accumulate); break;
+          case 8: wave_block_transform<4>(rowbuf, base, zb + base, lane, a.accumulate); break;
+          case 9: wave_block_transform<8>(rowbuf, base, zb + base, lane, a.accumulate); break;
+          default: wave_block_transform<16>(rowbuf, base, zb + base, lane, a.accumulate); break;
         }
       }
     } else {
-      fwht_lds_passes<StoreZ, 4>(StoreZ{zb, a.accumulate}, 0, a.lr, 0, rowbuf);
+      // the butterflies on bits 0 .. lr-1 of every row block at once, over the
+      // power-of-two span of rowbuf that covers the rows (rows past them unused)
+      int span = a.lr;
+      while ((1 << span) < rows) ++span;
+      fwht_lds_passes<StoreZ, 4>(StoreZ{zb, a.accumulate, rows}, 0, span, 0, rowbuf, a.lr);
     }
   }
 
@@ -642,13 +654,13 @@ hipError_t launch_blocks_e(BlocksArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// CB columns per wave: 4 when R >= 256, fewer below so that the launch keeps R / CB
+// >= 64 waves (each element is computed the same way whatever CB is)
 template <class YT>
 hipError_t launch_blocks(const BlocksArgs& a, hipStream_t stream) {
-  switch (a.lr) {
-    case 0: return launch_blocks_e<YT, 1>(a, stream);
-    case 1: return launch_blocks_e<YT, 2>(a, stream);
-    default: return launch_blocks_e<YT, 4>(a, stream);
-  }
+  if (a.lr >= 8) return launch_blocks_e<YT, 4>(a, stream);
+  if (a.lr == 7) return launch_blocks_e<YT, 2>(a, stream);
+  return launch_blocks_e<YT, 1>(a, stream);
 }
 
 int device_cus() {
@@ -665,6 +677,7 @@ int device_cus() {
 
 struct FusedPlan {
   int lpr_log2, splits, rps, row_steps, wgs_per_split, rs_per_wg, lr;
+  int W;  // row blocks of R = 2^lr rows (the cross-block transform's length)
   bool ok;
 };
 
@@ -686,26 +699,47 @@ FusedPlan fused_plan(const glq_layer& L) {
   const int min_per_wg = kThreads / 64;  // at least one row-step per wave
   const int wmax = (p.row_steps + min_per_wg - 1) / min_per_wg;
   if (w > wmax) w = wmax;
-  int64_t R;
+  // power-of-two m_pad and splits: one row block of R = m_pad / w rows per workgroup
   if (is_pow2(L.m_pad)) {
     p.rs_per_wg = (p.row_steps + w - 1) / w;
     p.wgs_per_split = (p.row_steps + p.rs_per_wg - 1) / p.rs_per_wg;
-    R = int64_t(p.rs_per_wg) * p.rps;
+    int64_t R = int64_t(p.rs_per_wg) * p.rps;
     if (p.wgs_per_split == 1 && R > L.m_pad) R = L.m_pad;
-  } else {
-    // block-diagonal m_pad: a power-of-two R of whole row-steps inside the
-    // smallest transform block, about m_pad / w rows
-    R = p.rps;
-    while (R * 2 <= L.m_pad / w && R * 2 <= smallest_block(L.m_pad) && R * 2 <= kRowBuf) R *= 2;
-    p.rs_per_wg = int(R / p.rps);
-    p.wgs_per_split = int(L.m_pad / R);
+    p.ok = is_pow2(R) && R <= kRowBuf && R * p.wgs_per_split == L.m_pad && p.wgs_per_split <= 1024;
+    p.lr = p.ok ? log2_exact(R) : 0;
+    p.W = p.wgs_per_split;
+    if (p.ok) return p;
   }
-  // the workgroups' row blocks must tile m_pad in power-of-two blocks that fit
-  // kRowBuf and divide every transform block, and the blocks per split fit the
-  // cross-block kernel (W <= 1024)
-  p.ok = is_pow2(R) && R <= kRowBuf && R * p.wgs_per_split == L.m_pad && L.m_pad % R == 0 &&
-         smallest_block(L.m_pad) >= R && p.wgs_per_split <= 1024;
-  p.lr = p.ok ? log2_exact(R) : 0;
+  // otherwise (a block-diagonal m_pad, or a split count that does not divide the
+  // CUs): a workgroup takes c row blocks of R rows, R a power of two dividing every
+  // transform block of m_pad, with c R rows covering m_pad in at most CUs / splits
+  // workgroups per split (one round).  Cost in rows of the first launch: its
+  // rows per workgroup, plus 16 per row block above 2 that each lane of the
+  // cross-block launch sums and transforms (W / 64 of them), plus a quarter for
+  // R < 64 (fewer than 64 waves there); ties go to the larger R.
+  const int64_t wps = device_cus() / p.splits > 0 ? device_cus() / p.splits : 1;
+  const int64_t T = (L.m_pad + wps - 1) / wps;
+  const int64_t cap = smallest_block(L.m_pad) < kRowBuf ? smallest_block(L.m_pad) : kRowBuf;
+  int64_t best_rows = 0, best_R = 0;
+  for (int64_t R = p.rps > 8 ? p.rps : 8; R <= cap; R *= 2) {
+    if (L.m_pad % R != 0 || L.m_pad / R > 1024) continue;
+    const int64_t rows = (T + R - 1) / R * R;
+    if (rows > kRowBuf) continue;
+    auto cost_of = [&](int64_t rw, int64_t r) {
+      const int64_t e = (L.m_pad / r + 63) / 64;
+      return rw + 16 * (e > 2 ? e - 2 : 0) + (r < 64 ? rw / 4 : 0);
+    };
+    if (best_R == 0 || cost_of(rows, R) <= cost_of(best_rows, best_R)) {
+      best_rows = rows;
+      best_R = R;
+    }
+  }
+  p.ok = best_R > 0;
+  if (!p.ok) return p;
+  p.rs_per_wg = int(best_rows / p.rps);
+  p.wgs_per_split = int((L.m_pad + best_rows - 1) / best_rows);
+  p.lr = log2_exact(best_R);
+  p.W = int(L.m_pad / best_R);
   return p;
 }
 
@@ -785,7 +819,7 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
   b.S = p.splits;
   b.m_pad = int(L.m_pad);
   b.lr = p.lr;
-  b.W = p.wgs_per_split;
+  b.W = p.W;
   b.lw = log2_exact(b.W);
   for (int k = 0; k < kLenLog2s; ++k) b.sc_tab[k] = float(1.0 / sqrt(double(int64_t(1) << k)));
   switch (y_dt) {
