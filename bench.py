@@ -293,7 +293,7 @@ def pmc_summary(dirs, copy_bytes):
         "# HBM traffic of one B = 1 call (%s), Devstral-Small-24B MLP decode" % " + ".join(FUSED_KERNEL_NAMES),
         "# commands (from the repository root, after cd /tmp && export TMPDIR=/tmp for the profiler):",
         "#   rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR --output-format csv -- python3 bench.py --steps 3 --warmup 1 "
-        "--no-cpu-baseline --no-prefill --no-block",
+        "--no-cpu-baseline --no-prefill --no-block --no-recipes --no-blockdiag",
         "#   rocprofv3 --pmc WRITE_SIZE -d WRITE_DIR --output-format csv -- (same)",
         "#   rocprofv3 --pmc FETCH_SIZE -d COPY_FETCH_DIR --output-format csv -- python3 bench.py --calibrate-copy %d"
         % copy_bytes,
