@@ -215,3 +215,76 @@ def recipe_layer(n, m, bpw, seed, n_pad=None, m_pad=None):
     """A layer of a 2-8 bpw recipe of the "Bit widths" table."""
     resid_bits, extra_bits = RECIPES[bpw]
     return random_layer(n, m, resid_bits, seed, n_pad, m_pad, extra_bits)
+
+
+# ---- E8-compressed paged KV cache (decode attention) ------------------------------
+KV_RESID_SCALE = 0.25
+
+
+@dataclass
+class KVCache:
+    """A synthetic paged K/V cache of E8 indices (host numpy arrays).
+
+    k_idx0 / k_idx1 / v_idx0 / v_idx1: uint16 [pages, page_size, num_kv_heads, head_dim / 8]
+    (idx1 None for one stage); k_scale / v_scale: float32 [pages, page_size, num_kv_heads];
+    block_table: int32 [B, max_pages]; seq_lens: int32 [B].
+    """
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    stages: int
+    k_idx0: np.ndarray
+    k_idx1: object
+    v_idx0: np.ndarray
+    v_idx1: object
+    k_scale: np.ndarray
+    v_scale: np.ndarray
+    block_table: np.ndarray
+    seq_lens: np.ndarray
+    resid_scale: float = KV_RESID_SCALE
+
+    @property
+    def pages(self):
+        return self.k_idx0.shape[0]
+
+    def kv_bytes(self):
+        """Bytes the decode reads: each sequence's tokens of K and V (indices and scales)."""
+        per_tok = self.num_kv_heads * (self.stages * self.head_dim // 8 * 2 + 4)
+        return int(2 * per_tok * int(np.sum(self.seq_lens)))
+
+
+def make_kv(seq_lens, num_kv_heads, head_dim, stages, page_size, seed, spare_pages=3):
+    """Draw a paged cache: default_rng([seed, 7]) in this order: the physical page of
+    every logical page (a permutation of all pages, so sequences are scattered),
+    k_idx0, k_idx1 (two stages), v_idx0, v_idx1, k_scale, v_scale (uniform in
+    [0.5, 2), float32).  Pages beyond the sequences' own (spare_pages) hold indices
+    too and are never referenced."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = len(seq_lens)
+    need = [(int(L) + page_size - 1) // page_size for L in seq_lens]
+    max_pages = max(need)
+    pages = sum(need) + spare_pages
+    rng = np.random.default_rng([seed, 7])
+    perm = rng.permutation(pages).astype(np.int32)
+    table = np.zeros((B, max_pages), dtype=np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[off:off + need[b]]
+        off += need[b]
+    shape = (pages, page_size, num_kv_heads, head_dim // 8)
+    draw = lambda: rng.integers(0, 65536, size=shape, dtype=np.uint16)
+    k0 = draw()
+    k1 = draw() if stages == 2 else None
+    v0 = draw()
+    v1 = draw() if stages == 2 else None
+    ks = rng.uniform(0.5, 2.0, size=shape[:3]).astype(np.float32)
+    vs = rng.uniform(0.5, 2.0, size=shape[:3]).astype(np.float32)
+    return KVCache(num_kv_heads, head_dim, page_size, stages, k0, k1, v0, v1, ks, vs, table, seq_lens)
+
+
+def make_q(B, num_q_heads, head_dim, dtype, seed):
+    """Decode queries [B, num_q_heads, head_dim]: N(0, 1) from default_rng([seed, 8]),
+    rounded once to dtype.  Returns (float64 values, raw array)."""
+    rng = np.random.default_rng([seed, 8])
+    v, raw = round_to_dtype(rng.standard_normal((B, num_q_heads * head_dim)), dtype)
+    return v.reshape(B, num_q_heads, head_dim), raw.reshape(B, num_q_heads, head_dim)
