@@ -268,3 +268,73 @@ def e8rht_linear(layer, x, y_dtype=None, workspace=None, out=None):
     _lib.check(lib().glq_e8rht_linear(ctypes.byref(layer.desc), _ptr(x), _dt(x.dtype), B, _ptr(y), _dt(y.dtype),
                                       _ptr(workspace), workspace.numel(), _stream(x.device)), "glq_e8rht_linear")
     return y
+
+
+class KVCache:
+    """An E8-compressed paged K/V cache on the device (glq_kv_cache).
+
+    k_idx / v_idx: one or two uint16 arrays [pages, page_size, num_kv_heads, head_dim/8]
+    per stage; k_scale / v_scale: fp32 [pages, page_size, num_kv_heads].
+    """
+
+    def __init__(self, k_idx, v_idx, k_scale, v_scale, codebooks, resid_scale=0.25, device=None,
+                 index_format=INDEX_CODEBOOK):
+        device = device if device is not None else codebooks.device
+        self.codebooks = codebooks
+        self.device = torch.device(device)
+        self.k_idx = [_to_dev(a, torch.int16, device) for a in k_idx]
+        self.v_idx = [_to_dev(a, torch.int16, device) for a in v_idx]
+        self.k_scale = _to_dev(k_scale, torch.float32, device)
+        self.v_scale = _to_dev(v_scale, torch.float32, device)
+        pages, page_size, heads, groups = self.k_idx[0].shape
+        self.num_pages, self.page_size, self.num_kv_heads, self.head_dim = pages, page_size, heads, groups * 8
+        self.stages = len(self.k_idx)
+        self.resid_scale = float(resid_scale)
+        self.index_format = int(index_format)
+        d = _lib.GlqKvCache()
+        d.num_pages, d.page_size, d.num_kv_heads, d.head_dim = pages, page_size, heads, groups * 8
+        d.stages, d.resid_scale, d.index_format = self.stages, self.resid_scale, self.index_format
+        for s in range(self.stages):
+            d.k_idx[s] = self.k_idx[s].data_ptr()
+            d.v_idx[s] = self.v_idx[s].data_ptr()
+        d.k_scale, d.v_scale = self.k_scale.data_ptr(), self.v_scale.data_ptr()
+        d.cb_pack = codebooks.primary.data_ptr()
+        self.desc = d
+
+    @classmethod
+    def from_synth(cls, cache, codebooks, device=None):
+        k = [cache.k_idx0] + ([] if cache.k_idx1 is None else [cache.k_idx1])
+        v = [cache.v_idx0] + ([] if cache.v_idx1 is None else [cache.v_idx1])
+        return cls(k, v, cache.k_scale, cache.v_scale, codebooks, cache.resid_scale, device)
+
+    def to_slot_codes(self):
+        """The same cache with every index relabelled as a slot code (glq_slot_codes)."""
+        return KVCache([slot_codes(a, self.codebooks) for a in self.k_idx],
+                       [slot_codes(a, self.codebooks) for a in self.v_idx], self.k_scale, self.v_scale,
+                       self.codebooks, self.resid_scale, self.device, INDEX_SLOT)
+
+    def nbytes(self):
+        return sum(a.numel() * 2 for a in self.k_idx + self.v_idx) + 4 * (self.k_scale.numel() + self.v_scale.numel())
+
+
+def e8kv_attention_workspace_bytes(cache, B, num_q_heads, max_seq_len):
+    return int(lib().glq_e8kv_attention_workspace_bytes(ctypes.byref(cache.desc), B, num_q_heads, max_seq_len))
+
+
+def e8kv_attention_decode(cache, q, block_table, seq_lens, max_seq_len, sm_scale=None, out_dtype=None,
+                          workspace=None, out=None):
+    """Decode attention out [B, Hq, D] over the compressed cache (glq_e8kv_attention_decode).
+
+    q [B, Hq, D]; block_table int32 [B, max_pages]; seq_lens int32 [B] (device tensors)."""
+    B, Hq, D = q.shape
+    q = q.contiguous()
+    sm_scale = float(D) ** -0.5 if sm_scale is None else float(sm_scale)
+    out_dtype = out_dtype or q.dtype
+    o = out if out is not None else torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    ws_n = e8kv_attention_workspace_bytes(cache, B, Hq, max_seq_len)
+    ws = workspace if workspace is not None else _workspace(max(ws_n, 1), q.device)
+    _lib.check(lib().glq_e8kv_attention_decode(ctypes.byref(cache.desc), _ptr(q), _dt(q.dtype), B, Hq,
+                                               _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                               int(max_seq_len), sm_scale, _ptr(o), _dt(o.dtype), _ptr(ws),
+                                               ws.numel(), _stream(q.device)), "glq_e8kv_attention_decode")
+    return o

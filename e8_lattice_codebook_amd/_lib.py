@@ -33,6 +33,17 @@ class GlqLayer(ctypes.Structure):
 
 _LP = ctypes.POINTER(GlqLayer)
 
+
+class GlqKvCache(ctypes.Structure):
+    _fields_ = [
+        ("num_pages", c_i64), ("page_size", c_i32), ("num_kv_heads", c_i32), ("head_dim", c_i32),
+        ("stages", c_i32), ("resid_scale", c_f32), ("index_format", c_i32),
+        ("k_idx", c_vp * 2), ("v_idx", c_vp * 2), ("k_scale", c_vp), ("v_scale", c_vp), ("cb_pack", c_vp),
+    ]
+
+
+_KP = ctypes.POINTER(GlqKvCache)
+
 SIGNATURES = {
     "glq_abi_version": (ctypes.c_int, []),
     "glq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -55,6 +66,9 @@ SIGNATURES = {
     "glq_e8_matmul_prefill": (ctypes.c_int, [_LP, c_vp, c_i64, c_vp, c_vp]),
     "glq_e8rht_linear_workspace_bytes": (c_sz, [_LP, c_i64]),
     "glq_e8rht_linear": (ctypes.c_int, [_LP, c_vp, ctypes.c_int, c_i64, c_vp, ctypes.c_int, c_vp, c_sz, c_vp]),
+    "glq_e8kv_attention_workspace_bytes": (c_sz, [_KP, c_i64, c_i32, c_i64]),
+    "glq_e8kv_attention_decode": (ctypes.c_int, [_KP, c_vp, ctypes.c_int, c_i64, c_i32, c_vp, c_i64, c_vp, c_i64,
+                                                 c_f32, c_vp, ctypes.c_int, c_vp, c_sz, c_vp]),
 }
 
 _lib = None

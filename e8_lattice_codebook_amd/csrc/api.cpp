@@ -372,4 +372,63 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
   return from_hip(e);
 }
 
+static glq_status check_kv(const glq_kv_cache* kv) {
+  if (!kv) return GLQ_ERR_NULL;
+  if (!kv->k_idx[0] || !kv->v_idx[0] || !kv->k_scale || !kv->v_scale || !kv->cb_pack) return GLQ_ERR_NULL;
+  if (kv->stages != 1 && kv->stages != 2) return GLQ_ERR_RECIPE;
+  if (kv->stages == 2 && (!kv->k_idx[1] || !kv->v_idx[1])) return GLQ_ERR_NULL;
+  if (kv->stages == 2 && !(kv->resid_scale == kv->resid_scale)) return GLQ_ERR_RECIPE;
+  if (kv->index_format != GLQ_INDEX_CODEBOOK && kv->index_format != GLQ_INDEX_SLOT) return GLQ_ERR_RECIPE;
+  if (kv->head_dim != 64 && kv->head_dim != 128) return GLQ_ERR_SHAPE;
+  if (kv->num_kv_heads < 1 || kv->num_pages < 1 || kv->page_size < 1 || kv->page_size > 1024 ||
+      !is_pow2(kv->page_size))
+    return GLQ_ERR_SHAPE;
+  // 32-bit rows of the kernel: pages * page_size * heads * D / 8 groups
+  if (kv->num_pages * kv->page_size * kv->num_kv_heads * (kv->head_dim / 8) >= (int64_t(1) << 31))
+    return GLQ_ERR_SHAPE;
+  if (!aligned(kv->cb_pack, 256) || !aligned(kv->k_scale, 4) || !aligned(kv->v_scale, 4)) return GLQ_ERR_ALIGN;
+  for (int s = 0; s < kv->stages; ++s)
+    if (!aligned(kv->k_idx[s], 2) || !aligned(kv->v_idx[s], 2)) return GLQ_ERR_ALIGN;
+  return GLQ_OK;
+}
+
+static bool kv_heads_ok(const glq_kv_cache* kv, int32_t num_q_heads) {
+  if (num_q_heads < 1 || num_q_heads % kv->num_kv_heads != 0) return false;
+  const int32_t G = num_q_heads / kv->num_kv_heads;
+  return G == 1 || G == 2 || G == 4 || G == 8;
+}
+
+size_t glq_e8kv_attention_workspace_bytes(const glq_kv_cache* kv, int64_t B, int32_t num_q_heads,
+                                          int64_t max_seq_len) {
+  if (!kv || B < 1 || max_seq_len < 1 || kv->num_kv_heads < 1 || !kv_heads_ok(kv, num_q_heads)) return 0;
+  if (kv->head_dim != 64 && kv->head_dim != 128) return 0;
+  const int64_t G = num_q_heads / kv->num_kv_heads;
+  const KvPlan p = kv_plan(B, kv->num_kv_heads, G, max_seq_len);
+  return align256(size_t(p.units) * size_t(G) * size_t(kv->head_dim) * 4) + align256(size_t(p.units) * size_t(G) * 8);
+}
+
+glq_status glq_e8kv_attention_decode(const glq_kv_cache* kv, const void* q, glq_dtype q_dt, int64_t B,
+                                     int32_t num_q_heads, const int32_t* block_table, int64_t max_pages,
+                                     const int32_t* seq_lens, int64_t max_seq_len, float sm_scale, void* out,
+                                     glq_dtype out_dt, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  glq_status st = check_kv(kv);
+  if (st != GLQ_OK) return st;
+  if (!q || !block_table || !seq_lens || !out) return GLQ_ERR_NULL;
+  if (B < 1 || B > (int64_t(1) << 20) || max_pages < 1 || max_seq_len < 1 || max_seq_len > (int64_t(1) << 30) ||
+      !kv_heads_ok(kv, num_q_heads))
+    return GLQ_ERR_SHAPE;
+  if (!valid_dtype(q_dt) || !valid_dtype(out_dt)) return GLQ_ERR_DTYPE;
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4)) return GLQ_ERR_ALIGN;
+  const size_t need = glq_e8kv_attention_workspace_bytes(kv, B, num_q_heads, max_seq_len);
+  if (!workspace || workspace_bytes < need) return GLQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return GLQ_ERR_ALIGN;
+  const int64_t G = num_q_heads / kv->num_kv_heads;
+  const KvPlan p = kv_plan(B, kv->num_kv_heads, G, max_seq_len);
+  float* part_o = static_cast<float*>(workspace);
+  float* part_ml = at<float>(workspace, align256(size_t(p.units) * size_t(G) * size_t(kv->head_dim) * 4));
+  return from_hip(launch_kv_attention(*kv, q, q_dt, B, num_q_heads, block_table, max_pages, seq_lens, max_seq_len,
+                                      sm_scale, out, out_dt, part_o, part_ml, stream));
+}
+
 }  // extern "C"

@@ -151,4 +151,18 @@ hipError_t launch_rht_in_tiled(const void* x, glq_dtype x_dt, int64_t B, int64_t
 hipError_t launch_gemm(const glq_layer& layer, const half_t* u16, int64_t M, float* z, hipStream_t stream,
                        bool accumulate = false);
 
+// Decode attention over an E8-compressed paged K/V cache: chunks of T tokens per
+// (sequence, KV head) in a persistent kernel, then the chunks merged in order.
+// Workspace: units * G * D floats of partial outputs, then units * G * 2 floats of
+// (max, exp-sum), units = B * num_kv_heads * splits.
+struct KvPlan {
+  int T, splits;
+  int64_t units;
+};
+KvPlan kv_plan(int64_t B, int64_t Hkv, int64_t G, int64_t max_seq_len);
+hipError_t launch_kv_attention(const glq_kv_cache& kv, const void* q, glq_dtype q_dt, int64_t B, int64_t Hq,
+                               const int32_t* block_table, int64_t max_pages, const int32_t* seq_lens,
+                               int64_t max_seq_len, float sm_scale, void* out, glq_dtype out_dt, float* part_o,
+                               float* part_ml, hipStream_t stream);
+
 }  // namespace glq

@@ -144,6 +144,43 @@ typedef struct glq_layer {
   const void* cb8_pack;
 } glq_layer;
 
+/*
+ * An E8-compressed paged K/V cache for decode attention (Glq v0.5.0 release notes,
+ * "Highlights"; glq 0.5.1, "KV cache compression" -> "E8 lattice cache": the same
+ * E8 quantizer as the weights, e8_relaxed:1 / e8_relaxed:2 with the 4 bpw
+ * e8_relaxed:2 the inline-dequant recipe).  All pointers are device pointers.
+ * A cached K or V vector of head_dim D is D/8 groups of 8; group g reads back as
+ * s * H8 e_g / sqrt(8) (H8 the Sylvester 8-point Hadamard), e_g = C[i0] for one
+ * stage or C[i0] + resid_scale * C[i1] for two, with one scale s per vector.
+ *   num_pages       physical pages; page indices read from a block table are
+ *                   clamped to [0, num_pages)
+ *   page_size       tokens per page, a power of two in [1, 1024]
+ *   num_kv_heads    KV heads (H_kv)
+ *   head_dim        D, 64 or 128
+ *   stages          1 (2 bpw) or 2 (4 bpw)
+ *   resid_scale     the second stage's scale (ignored with one stage)
+ *   index_format    GLQ_INDEX_CODEBOOK or GLQ_INDEX_SLOT (codes of cb_pack, as for
+ *                   a layer)
+ *   k_idx[s], v_idx[s]   uint16 [num_pages][page_size][num_kv_heads][D/8] per stage
+ *                   (index 1 unused with one stage), 2-byte aligned
+ *   k_scale, v_scale     fp32 [num_pages][page_size][num_kv_heads]
+ *   cb_pack         a 65,536-entry pack from glq_codebook_pack, 256-byte aligned
+ */
+typedef struct glq_kv_cache {
+  int64_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t stages;
+  float resid_scale;
+  int32_t index_format;
+  const uint16_t* k_idx[2];
+  const uint16_t* v_idx[2];
+  const float* k_scale;
+  const float* v_scale;
+  const void* cb_pack;
+} glq_kv_cache;
+
 /* GLQ_ABI_VERSION of the built library. */
 int glq_abi_version(void);
 
@@ -332,6 +369,39 @@ glq_status glq_e8_matmul_prefill(const glq_layer* layer, const void* u16, int64_
 size_t glq_e8rht_linear_workspace_bytes(const glq_layer* layer, int64_t B);
 glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_dt, int64_t B, void* y,
                             glq_dtype y_dt, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * glq_e8kv_attention_decode — one decode step of attention over an E8-compressed
+ * paged K/V cache, the cache dequantized inside the kernel (Glq v0.5.0 release
+ * notes, "Highlights": no decompress-to-workspace pass, an 8-point FHT butterfly
+ * for the inverse Hadamard, flash-decoding split of long contexts).
+ *   out[b][hq] = softmax_t(sm_scale q[b][hq] . K_t) . V_t over the tokens
+ *   t < seq_lens[b] of sequence b, with K_t, V_t the vectors of KV head
+ *   hq / (num_q_heads / num_kv_heads) at slot t mod page_size of page
+ *   block_table[b][t / page_size].
+ *   q            device [B][num_q_heads][head_dim] in q_dt (F32, F16 or BF16)
+ *   num_q_heads  a multiple of num_kv_heads with num_q_heads / num_kv_heads in
+ *                {1, 2, 4, 8}
+ *   block_table  device int32 [B][max_pages]
+ *   seq_lens     device int32 [B]; clamped to [0, min(max_seq_len, max_pages *
+ *                page_size)]; a sequence of 0 tokens gives zeros
+ *   max_seq_len  host bound on seq_lens (sizes the split of the contexts)
+ *   out          device [B][num_q_heads][head_dim] in out_dt (F32, F16 or BF16)
+ *   workspace    device, >= glq_e8kv_attention_workspace_bytes(...), 256-byte
+ *                aligned; scratch (the chunks' partial results), no initial contents
+ * Each chunk's softmax statistics and partial output are merged in chunk order:
+ * run-to-run bit identity.  Accumulation is fp32; q is rotated and quantized to
+ * 16-bit fixed point per head for exact integer dot products against the codewords.
+ * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_DTYPE, GLQ_ERR_RECIPE, GLQ_ERR_ALIGN,
+ * GLQ_ERR_WORKSPACE, GLQ_ERR_HIP.
+ */
+size_t glq_e8kv_attention_workspace_bytes(const glq_kv_cache* kv, int64_t B, int32_t num_q_heads,
+                                          int64_t max_seq_len);
+glq_status glq_e8kv_attention_decode(const glq_kv_cache* kv, const void* q, glq_dtype q_dt, int64_t B,
+                                     int32_t num_q_heads, const int32_t* block_table, int64_t max_pages,
+                                     const int32_t* seq_lens, int64_t max_seq_len, float sm_scale, void* out,
+                                     glq_dtype out_dt, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -192,3 +192,56 @@ class TestValidation:
         L = multi(1, [16])
         L.extra_scale[0] = 0.0
         assert linear_status(L) == 4
+
+
+def fake_kv(**kw):
+    kv = _lib.GlqKvCache()
+    kv.num_pages, kv.page_size, kv.num_kv_heads, kv.head_dim, kv.stages = 64, 16, 4, 128, 2
+    kv.resid_scale, kv.index_format = 0.25, 0
+    kv.k_idx[0] = kv.k_idx[1] = kv.v_idx[0] = kv.v_idx[1] = A
+    kv.k_scale = kv.v_scale = kv.cb_pack = A
+    for k, v in kw.items():
+        setattr(kv, k, v)
+    return kv
+
+
+def kv_status(kv, B=2, hq=16, bt=A, lens=A, max_len=1000, q=A, out=A, qdt=2, odt=2, ws=A, ws_n=1 << 40):
+    return _lib.load().glq_e8kv_attention_decode(ctypes.byref(kv), q, qdt, B, hq, bt, 64, lens, max_len, 0.088, out,
+                                                 odt, ws, ws_n, None)
+
+
+def test_kv_workspace_query():
+    lib = _lib.load()
+    kv = fake_kv()
+    n = lib.glq_e8kv_attention_workspace_bytes(ctypes.byref(kv), 2, 16, 1000)
+    # at least one chunk per (sequence, KV head): G * (D + 2) floats each
+    assert n >= 2 * 4 * 4 * (128 + 2) * 4
+    assert lib.glq_e8kv_attention_workspace_bytes(ctypes.byref(kv), 2, 12, 1000) == 0   # 12 / 4 = 3 heads per group
+    assert lib.glq_e8kv_attention_workspace_bytes(ctypes.byref(kv), 2, 16, 0) == 0
+
+
+@pytest.mark.skipif(not NO_GPU, reason="fake-pointer validation runs only where no GPU exists")
+def test_kv_validation():
+    assert kv_status(fake_kv()) == 7                         # valid: no GPU to launch on
+    assert kv_status(fake_kv(cb_pack=None)) == 1
+    assert kv_status(fake_kv(), q=None) == 1
+    assert kv_status(fake_kv(), lens=None) == 1
+    assert kv_status(fake_kv(stages=3)) == 4
+    assert kv_status(fake_kv(index_format=2)) == 4
+    assert kv_status(fake_kv(head_dim=96)) == 2
+    assert kv_status(fake_kv(page_size=24)) == 2
+    assert kv_status(fake_kv(page_size=2048)) == 2
+    assert kv_status(fake_kv(), hq=12) == 2                   # 3 query heads per KV head
+    assert kv_status(fake_kv(), hq=64) == 2                   # 16 per KV head
+    assert kv_status(fake_kv(), max_len=0) == 2
+    assert kv_status(fake_kv(), qdt=5) == 3
+    assert kv_status(fake_kv(cb_pack=A + 16)) == 5
+    assert kv_status(fake_kv(), bt=A + 2) == 5
+    assert kv_status(fake_kv(), ws=None) == 6
+    assert kv_status(fake_kv(), ws_n=16) == 6
+    kv1 = fake_kv(stages=1)
+    kv1.k_idx[1] = 0
+    assert kv_status(kv1) == 7                               # one stage: the second arrays are unused
+    kv2 = fake_kv()
+    kv2.v_idx[1] = 0
+    assert kv_status(kv2) == 1
