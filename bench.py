@@ -64,6 +64,8 @@ def main():
     ap.add_argument("--no-recipes", action="store_true", help="skip the 5-8 bpw decode measurement")
     ap.add_argument("--recipe-steps", type=int, default=300)
     ap.add_argument("--no-blockdiag", action="store_true", help="skip the unpadded (block-diagonal) measurement")
+    ap.add_argument("--no-kv", action="store_true", help="skip the E8 KV-cache decode attention measurement")
+    ap.add_argument("--kv-steps", type=int, default=50)
     ap.add_argument("--index-format", choices=["slot", "codebook"], default="slot",
                     help="16-bit index arrays as slot codes (default) or as codebook indices")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -229,6 +231,9 @@ def main():
 
     if not args.no_blockdiag and B == 1:
         result["blockdiag_b1"] = bench_blockdiag(glq, synth, cb, dev, args, log, ms_per_step)
+
+    if not args.no_kv:
+        result["kv_attention"] = bench_kv(glq, synth, cb, dev, args, log)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host_layers, wl, B, log)
@@ -568,6 +573,60 @@ def bench_blockdiag(glq, synth, cb, dev, args, log, padded_ms):
     del qls, ws
     torch.cuda.empty_cache()
     return out
+
+
+def bench_kv(glq, synth, cb, dev, args, log, layers=36, B=4, ctx=16384):
+    """Decode attention over E8-compressed K/V caches, SmolLM3-3B shapes: 16 query
+    heads on 4 KV heads, head_dim 128, the 4 bpw recipe (two 16-bit stages), pages of
+    16 tokens; B sequences of ctx tokens in every one of the model's layers (one
+    call per layer, each with its own cache), so a step streams every cache once."""
+    import numpy as np
+    import torch
+
+    Hq, Hkv, D = 16, 4, 128
+    caches, tables = [], []
+    for layer in range(layers):
+        host = synth.make_kv([ctx] * B, Hkv, D, 2, 16, seed=2000 + layer, spare_pages=0)
+        c = glq.KVCache.from_synth(host, cb)
+        if args.index_format == "slot":
+            c = c.to_slot_codes()
+        caches.append(c)
+        tables.append(torch.from_numpy(host.block_table).to(dev))
+        kv_bytes = host.kv_bytes()
+    lens = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+    _, raw = synth.make_q(B, Hq, D, "bf16", seed=2999)
+    q = torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(glq.e8kv_attention_workspace_bytes(caches[0], B, Hq, ctx), dtype=torch.uint8, device=dev)
+
+    def step():
+        for layer in range(layers):
+            glq.e8kv_attention_decode(caches[layer], q, tables[layer], lens, ctx, out=out, workspace=ws)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.kv_steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.kv_steps
+    gbs = layers * kv_bytes / (ms * 1e-3) / 1e9
+    log("bench: E8 KV attention, SmolLM3-3B shapes, B=%d ctx=%d, %d layers: %.4f ms/step (%.2f us per layer call), "
+        "%.1f GB/s of cache" % (B, ctx, layers, ms, ms * 1e3 / layers, gbs))
+    out_d = {"workload": "decode attention over E8-compressed paged K/V caches, SmolLM3-3B shapes (16 query heads, 4 KV "
+                         "heads, head_dim 128), 4 bpw cache (two 16-bit E8 stages per 8 values, fp32 scale per vector), "
+                         "pages of 16 tokens, B=%d sequences of %d tokens, %d layers' caches per step, bf16 q and out"
+                         % (B, ctx, layers),
+             "index_format": args.index_format, "steps": args.kv_steps, "ms_per_step": round(ms, 5),
+             "us_per_layer_call": round(ms * 1e3 / layers, 3), "value": round(gbs, 2), "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4), "cache_bytes_per_layer_call": kv_bytes,
+             "tokens_attended_per_s": round(layers * B * ctx / (ms * 1e-3), 1)}
+    del caches, tables, ws
+    torch.cuda.empty_cache()
+    return out_d
 
 
 def cpu_baseline(layers, wl, B, log, min_seconds=10.0):

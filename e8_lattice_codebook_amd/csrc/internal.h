@@ -156,7 +156,7 @@ hipError_t launch_gemm(const glq_layer& layer, const half_t* u16, int64_t M, flo
 // Workspace: units * G * D floats of partial outputs, then units * G * 2 floats of
 // (max, exp-sum), units = B * num_kv_heads * splits.
 struct KvPlan {
-  int T, splits;
+  int T, TS, splits;  // tokens per unit, per sub-chunk; units per (sequence, KV head)
   int64_t units;
 };
 KvPlan kv_plan(int64_t B, int64_t Hkv, int64_t G, int64_t max_seq_len);

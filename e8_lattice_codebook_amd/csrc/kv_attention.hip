@@ -16,12 +16,11 @@
 //
 // Kernel 1 (kv_split_kernel): persistent workgroups, one per CU, the codebook image
 // loaded into LDS once.  A unit is (sequence b, KV head h, chunk of T tokens).  Per
-// unit: the G query heads of h are rotated and quantized to 16-bit fixed point
-// (four int4 digit planes per group); every wave scores tokens (lanes = token x
-// stage x group, exact i32 dot products, a DPP reduction per token); one wave per
-// head takes the chunk's max and exp-sums; then wave w accumulates group w mod D/8
-// of V over its tokens (lane = token) in fp32.  The unit's (max, sum, o) go to the
-// workspace.  Kernel 2 (kv_combine_kernel) merges a sequence's chunks in chunk
+// unit: the G query heads of h are rotated and held as fp16 pairs; every wave
+// scores tokens (lanes = token x stage x group: the codeword's int4 lanes become
+// exact fp16 pairs, fp32 dot products with the query, a DPP reduction per token);
+// one wave per head keeps the running max and exp-sum; the same lanes sum V in
+// fp32.  The unit's (max, sum, o) go to the workspace.  Kernel 2 (kv_combine_kernel) merges a sequence's chunks in chunk
 // order, divides, applies the 8-point butterfly and 1/sqrt(8), and casts.
 #include <math.h>
 
@@ -31,7 +30,9 @@
 namespace glq {
 namespace {
 
-constexpr int kKvThreads = 1024;
+// 8 waves (2 per SIMD, up to 256 registers each): the query digits, the per-head V
+// sums and a batch of loads in flight fit without serializing the loads
+constexpr int kKvThreads = 512;
 constexpr int kKvWaves = kKvThreads / 64;
 constexpr int kKvBuf = 1280;  // floats of LDS beside the image: query staging, planes, scores
 
@@ -51,7 +52,8 @@ struct KvArgs {
   const uint32_t* img;
   float* part_o;   // [units][G][D]
   float* part_ml;  // [units][G][2]: chunk max, sum of exp(score - max)
-  int Hkv, lp, T, splits, units;
+  int Hkv, lp, T, splits, units;  // T: tokens per unit
+  int TS;                          // tokens per sub-chunk (the scores buffer holds TS x G)
   int num_pages;    // page indices are clamped to [0, num_pages)
   int max_len;      // seq_lens are clamped to [0, max_len] (max_seq_len, and the block table's reach)
   float sm_scale, resid_scale;
@@ -86,6 +88,21 @@ __device__ __forceinline__ uint32_t kv_word(const uint32_t* img, uint32_t c, uin
   }
 }
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// The entry's 2c as four fp16 pairs (2c_2k, 2c_2k+1) from its stored word w and m
+// (all ones: the entry is the word's negation): with t = w ^ m ^ 0x8888_8888 each
+// nibble is lane + 8 (or 7 - lane), 1024 + nibble is an exact fp16 when placed in
+// the mantissa, and the bias -(1024 + 8) (or -(1024 + 7)) leaves the value; nibbles
+// k and k + 4 hold coordinates 2k and 2k + 1.
+__device__ __forceinline__ void word_pairs(uint32_t w, uint32_t m, half2v (&p)[4]) {
+  const uint32_t t = w ^ m ^ 0x88888888u;
+  const half2v bias = __builtin_bit_cast(half2v, 0xE408E408u ^ (m & 0x000F000Fu));
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    p[k] = __builtin_bit_cast(half2v, ((t >> (4 * k)) & 0x000F000Fu) | 0x64006400u) + bias;
+}
+
 __device__ __forceinline__ float dpp_max(float v, int ctrl_sel) {
   int r;
   const int x = __float_as_int(v);
@@ -113,7 +130,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
   constexpr int LPT = ST * GPS;       // lanes per token in the K phase
   constexpr int LPT_LOG2 = LPT == 8 ? 3 : LPT == 16 ? 4 : 5;
   constexpr int TPI = 64 / LPT;       // tokens per wave instruction
-  constexpr int PARTS = kKvWaves / GPS;  // V-phase waves per group
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   static_assert(G * D <= kKvBuf && G * GPS * 5 <= kKvBuf, "query staging fits");
 
@@ -159,19 +175,20 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
     const int L = min(max(a.seq_lens[b], 0), a.max_len);
     const int t0 = split * a.T;
     if (t0 >= L) continue;  // the same for the whole workgroup
-    const int nt = min(a.T, L - t0);
+    const int nt_unit = min(a.T, L - t0);
     const int32_t* bt = a.block_table + int64_t(b) * a.bt_stride;
+    // row of token t: (page, slot, head); rows * D / 8 < 2^31 (checked by the caller)
     auto row_of = [&](int t) {
       const int pg = min(max(bt[t >> a.lp], 0), a.num_pages - 1);
-      return (int64_t(pg) * P + (t & (P - 1))) * a.Hkv + h;
+      return (pg * P + (t & (P - 1))) * a.Hkv + h;
     };
 
-    // ---- the G query heads of h: H8 q_g / sqrt(8) * sm_scale, then digit planes
+    // ---- the G query heads of h: q' = H8 q_g / sqrt(8) * sm_scale, as fp16 pairs
     const int64_t qbase = (int64_t(b) * a.Hkv + h) * G * D;
     for (int i = tid; i < G * D; i += kKvThreads) buf[i] = q_value(a.q, a.q_dt, qbase + i);
     __syncthreads();
-    float qv[8];
     const bool qlane = tid < G * GPS;
+    float qv[8];
     if (qlane) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) qv[j] = buf[tid * 8 + j];
@@ -186,177 +203,163 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
       for (int j = 0; j < 8; ++j) buf[tid * 8 + j] = qv[j];
     }
     __syncthreads();
-    if (wave < G) {  // the head's max |q'|
-      float mx = 0.0f;
-      for (int d = lane; d < D; d += 64) mx = fmaxf(mx, fabsf(buf[wave * D + d]));
-      mx = wave_max63(mx);
-      if (lane == 63) buf[kKvBuf - 8 + wave] = mx;
-    }
-    __syncthreads();
-    uint32_t pl[4];
-    int32_t gsum = 0;
-    float qsc = 0.0f;
-    if (qlane) {
-      const float mx = buf[kKvBuf - 8 + tid / GPS];
-      quantize_group(qv, mx > 0.0f ? float(kUqMax) / mx : 0.0f, pl, gsum);
-      qsc = mx / float(kUqMax);
-    }
-    __syncthreads();
-    if (qlane) {
+    half2v qh[G][4];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) buf[tid * 5 + p] = __uint_as_float(pl[p]);
-      buf[tid * 5 + 4] = __int_as_float(gsum);
-    }
-    if (qlane && tid % GPS == 0) buf[kKvBuf - 16 + tid / GPS] = qsc;
-    __syncthreads();
-    uint32_t dig[G][4];
-    float qs[G];
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) dig[g][p] = __float_as_uint(buf[(g * GPS + lg) * 5 + p]);
-      qs[g] = buf[kKvBuf - 16 + g];
-    }
+      for (int k = 0; k < 4; ++k)
+        qh[g][k] = half2v{_Float16(buf[(g * GPS + lg) * 8 + 2 * k]), _Float16(buf[(g * GPS + lg) * 8 + 2 * k + 1])};
     __syncthreads();  // buf becomes the chunk's scores [T][G]
 
-    // ---- K: score of every token of the chunk, 0.5 s_k q' . (2 c0 + s_r 2 c1)
-    // a wave takes batches wave, wave + 16, ...; KB of them have their loads in
-    // flight at once (the page numbers first, then the indices and scales)
-    const uint16_t* kidx = lst == 0 ? a.k0 : a.k1;
-    const int batches = (nt + TPI - 1) / TPI;
-    constexpr int KB = 8;
-    for (int bi0 = wave; bi0 < batches; bi0 += kKvWaves * KB) {
-      int64_t rows[KB];
-#pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        const int tt = (bi0 + k * kKvWaves) * TPI + lt;
-        rows[k] = row_of(t0 + (tt < nt ? tt : 0));
-      }
-      uint32_t cs[KB];
-      float kss[KB];
-#pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        cs[k] = kidx[rows[k] * GPS + lg];
-        kss[k] = a.ks[rows[k]];
-      }
-#pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        const int tt = (bi0 + k * kKvWaves) * TPI + lt;
-        if (bi0 + k * kKvWaves >= batches) break;  // the same for the whole wave
-        const bool valid = tt < nt;
-        uint32_t m;
-        const uint32_t w = kv_word<CODES>(img, cs[k], delta, m);
-        const float f = (m ? -0.5f : 0.5f) * (lst ? rs : 1.0f);
-        float sc[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          int acc[4];
-#pragma unroll
-          for (int p = 0; p < 4; ++p) acc[p] = __builtin_amdgcn_sdot8(int(w), int(dig[g][p]), 0, false);
-          const int tot = ((acc[3] * 16 + acc[2]) * 16 + acc[1]) * 16 + acc[0];
-          sc[g] = lane_reduce(float(tot) * f, LPT_LOG2);
-        }
-        if ((lane & (LPT - 1)) == LPT - 1 && tt < a.T) {
-#pragma unroll
-          for (int g = 0; g < G; ++g) buf[tt * G + g] = valid ? sc[g] * kss[k] * qs[g] : -INFINITY;
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- softmax statistics of the chunk, one wave per head
-    if (wave < G) {
-      float mx = -INFINITY;
-      for (int tt = lane; tt < nt; tt += 64) mx = fmaxf(mx, buf[tt * G + wave]);
-      mx = __shfl(wave_max63(mx), 63, 64);
-      float sum = 0.0f;
-      for (int tt = lane; tt < nt; tt += 64) {
-        const float p = __expf(buf[tt * G + wave] - mx);
-        buf[tt * G + wave] = p;
-        sum += p;
-      }
-      sum = lane_reduce(sum, 6);
-      if (lane == 63) {
-        a.part_ml[(int64_t(unit) * G + wave) * 2 + 0] = mx;
-        a.part_ml[(int64_t(unit) * G + wave) * 2 + 1] = sum;
-      }
-    }
-    __syncthreads();
-
-    // ---- V: wave w sums group w mod GPS of its tokens, lane = token
-    const int gv = wave % GPS;
-    const int part = wave / GPS;
+    // ---- the unit's tokens in sub-chunks of TS: scores, an online softmax (running
+    // max and exp-sum per head, the V sums rescaled when the max grows), V sums
+    // Lane (token of the batch, stage, group) as in the K phase: the lane sums its
+    // group and stage of V over the wave's tokens; at the end of the unit the lanes
+    // of a group and then the waves are added.
     float o[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[g][j] = 0.0f;
-    constexpr int VB = 4;  // tokens per lane with their loads in flight at once
-    for (int tb = part * 64 + lane; tb < nt; tb += 64 * PARTS * VB) {
-      int64_t rows[VB];
+    float m_run = -INFINITY, l_run = 0.0f;  // wave g < G: head g's running statistics
+    const uint16_t* kidx = lst == 0 ? a.k0 : a.k1;
+    const uint16_t* vidx = lst == 0 ? a.v0 : a.v1;
+    // Loads run ahead of their use: the next sub-chunk's K indices are issued once
+    // this one's scores are done (in flight during its softmax and V), its V indices
+    // once this one's V is done (in flight during the next scores).  A wave's KBW
+    // batches (wave, wave + 8, ...) cover a sub-chunk of up to 256 tokens; slots
+    // past it load a valid row and are not used.
+    constexpr int KBW = (256 / TPI + kKvWaves - 1) / kKvWaves;
+    auto load_side = [&](int ts0, int nt, const uint16_t* idx, const float* scl, uint32_t (&c)[KBW],
+                         float (&sv)[KBW]) {
+      int rows[KBW];
 #pragma unroll
-      for (int k = 0; k < VB; ++k) {
-        const int tt = tb + k * 64 * PARTS;
-        rows[k] = row_of(t0 + (tt < nt ? tt : 0));
+      for (int k = 0; k < KBW; ++k) {
+        const int tt = (wave + k * kKvWaves) * TPI + lt;
+        rows[k] = row_of(ts0 + (tt < nt ? tt : 0));
       }
-      uint32_t cs[VB][ST];
-      float vss[VB];
 #pragma unroll
-      for (int k = 0; k < VB; ++k) {
-        cs[k][0] = a.v0[rows[k] * GPS + gv];
-        if (ST == 2) cs[k][ST - 1] = a.v1[rows[k] * GPS + gv];
-        vss[k] = a.vs[rows[k]];
+      for (int k = 0; k < KBW; ++k) {
+        c[k] = idx[rows[k] * GPS + lg];
+        sv[k] = scl[rows[k]];
+      }
+    };
+    uint32_t kc[KBW], vc[KBW];
+    float kks[KBW], vvs[KBW];
+    load_side(t0, min(a.TS, nt_unit), kidx, a.ks, kc, kks);
+    load_side(t0, min(a.TS, nt_unit), vidx, a.vs, vc, vvs);
+    for (int sc = 0; sc < nt_unit; sc += a.TS) {
+      const int nt = min(a.TS, nt_unit - sc);
+      const int batches = (nt + TPI - 1) / TPI;
+
+      // K: scores 0.5 s_k q' . (2 c0 + s_r 2 c1) of the sub-chunk's tokens
+#pragma unroll
+      for (int k = 0; k < KBW; ++k) {
+        const int bi = wave + k * kKvWaves;
+        if (bi >= batches) break;  // the same for the whole wave
+        const int tt = bi * TPI + lt;
+        const bool valid = tt < nt;
+        uint32_t m;
+        const uint32_t w = kv_word<CODES>(img, kc[k], delta, m);
+        half2v pr[4];
+        word_pairs(w, m, pr);
+        const float f = (lst ? 0.5f * rs : 0.5f) * kks[k];
+        float scv[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_fdot2(pr[kk], qh[g][kk], acc, false);
+          scv[g] = lane_reduce(acc * f, LPT_LOG2);
+        }
+        if ((lane & (LPT - 1)) == LPT - 1 && tt < a.TS) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) buf[tt * G + g] = valid ? scv[g] : -INFINITY;
+        }
+      }
+      const int sc2 = sc + a.TS < nt_unit ? sc + a.TS : sc;  // past the unit: this one again, unused
+      load_side(t0 + sc2, min(a.TS, nt_unit - sc2), kidx, a.ks, kc, kks);
+      __syncthreads();
+
+      // softmax statistics, one wave per head: p = exp(s - m_new), the factor
+      // exp(m_run - m_new) for what was summed before (0 on the first sub-chunk)
+      if (wave < G) {
+        float mx = -INFINITY;
+        for (int tt = lane; tt < nt; tt += 64) mx = fmaxf(mx, buf[tt * G + wave]);
+        mx = __shfl(wave_max63(mx), 63, 64);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __expf(m_run - m_new);
+        float sum = 0.0f;
+        for (int tt = lane; tt < nt; tt += 64) {
+          const float pv = __expf(buf[tt * G + wave] - m_new);
+          buf[tt * G + wave] = pv;
+          sum += pv;
+        }
+        sum = __shfl(lane_reduce(sum, 6), 63, 64);
+        l_run = l_run * alpha + sum;
+        m_run = m_new;
+        if (lane == 0) buf[kKvBuf - 8 + wave] = alpha;
+      }
+      __syncthreads();
+
+      // V: o += p_t * 0.5 s_v * (+-1, s_r) * 2c over the wave's tokens
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float al = buf[kKvBuf - 8 + g];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[g][j] *= al;
       }
 #pragma unroll
-      for (int k = 0; k < VB; ++k) {
-        const int tt = tb + k * 64 * PARTS;
-        if (tt >= nt) continue;
-        const float vsc = 0.5f * vss[k];
-        float pw[G];
+      for (int k = 0; k < KBW; ++k) {
+        const int bi = wave + k * kKvWaves;
+        if (bi >= batches) break;
+        const int tt = bi * TPI + lt;
+        const bool valid = tt < nt;
+        const int ts = valid ? tt : 0;
+        uint32_t m;
+        const uint32_t w = kv_word<CODES>(img, vc[k], delta, m);
+        half2v pr[4];
+        word_pairs(w, m, pr);
+        const float f = (lst ? 0.5f * rs : 0.5f) * vvs[k];
 #pragma unroll
-        for (int g = 0; g < G; ++g) pw[g] = buf[tt * G + g] * vsc;
+        for (int g = 0; g < G; ++g) {
+          const float sv = valid ? buf[ts * G + g] * f : 0.0f;
 #pragma unroll
-        for (int st = 0; st < ST; ++st) {
-          uint32_t m;
-          const uint32_t w = kv_word<CODES>(img, cs[k][st], delta, m);
-          const float f = (m ? -1.0f : 1.0f) * (st ? rs : 1.0f);
-          float x[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j)  // the builtin's result type is unsigned: read it as the signed lane
-            x[j] = float(int32_t(__builtin_amdgcn_sbfe(w, 4 * lane_nibble(j), 4)));
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float s = pw[g] * f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o[g][j] = fmaf(s, x[j], o[g][j]);
+          for (int kk = 0; kk < 4; ++kk) {
+            o[g][2 * kk] = fmaf(sv, float(pr[kk].x), o[g][2 * kk]);
+            o[g][2 * kk + 1] = fmaf(sv, float(pr[kk].y), o[g][2 * kk + 1]);
           }
         }
       }
+      load_side(t0 + sc2, min(a.TS, nt_unit - sc2), vidx, a.vs, vc, vvs);
+      __syncthreads();  // the next sub-chunk overwrites the scores
+    }
+
+    // ---- the unit's results: statistics; V sums over the lanes of a group (the
+    // lane bits above the group), then over the waves in wave order in LDS
+    if (wave < G && lane == 63) {
+      a.part_ml[(int64_t(unit) * G + wave) * 2 + 0] = m_run;
+      a.part_ml[(int64_t(unit) * G + wave) * 2 + 1] = l_run;
     }
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o[g][j] = lane_reduce(o[g][j], 6);
-    __syncthreads();  // every wave is done with the scores
-    if (PARTS > 1 && part > 0 && lane == 63) {
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+        for (int bit = GPS; bit < 64; bit <<= 1) o[g][j] += __shfl_xor(o[g][j], bit, 64);
+    for (int ww = 0; ww < kKvWaves; ++ww) {
+      if (wave == ww && lane < GPS) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) buf[((part - 1) * GPS + gv) * G * 8 + g * 8 + j] = o[g][j];
-    }
-    __syncthreads();
-    if (part == 0 && lane == 63) {
-      float* po = a.part_o + int64_t(unit) * G * D + gv * 8;
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float v = o[g][j];
-          for (int pp = 1; pp < PARTS; ++pp) v += buf[((pp - 1) * GPS + gv) * G * 8 + g * 8 + j];
-          po[g * D + j] = v;
-        }
+          for (int j = 0; j < 8; ++j) {
+            float* d = &buf[g * D + lane * 8 + j];
+            *d = ww == 0 ? o[g][j] : *d + o[g][j];
+          }
       }
+      __syncthreads();
     }
+    for (int i = tid; i < G * D; i += kKvThreads) a.part_o[int64_t(unit) * G * D + i] = buf[i];
     __syncthreads();  // buf is reused by the next unit
   }
 }
@@ -375,13 +378,33 @@ __global__ __launch_bounds__(D) void kv_combine_kernel(const float* __restrict__
   const int h = hq / G, g = hq % G;
   const int n = (min(max(seq_lens[b], 0), max_len) + T - 1) / T;
   const int64_t u0 = (int64_t(b) * Hkv + h) * splits;
+  // loads in batches of 8 chunks (in flight together), sums in chunk order
+  constexpr int CB = 8;
   float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, part_ml[((u0 + s) * G + g) * 2]);
+  for (int s0 = 0; s0 < n; s0 += CB) {
+    float mv[CB];
+#pragma unroll
+    for (int k = 0; k < CB; ++k) mv[k] = s0 + k < n ? part_ml[((u0 + s0 + k) * G + g) * 2] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < CB; ++k) M = fmaxf(M, mv[k]);
+  }
   float acc = 0.0f, lsum = 0.0f;
-  for (int s = 0; s < n; ++s) {
-    const float e = __expf(part_ml[((u0 + s) * G + g) * 2] - M);
-    acc = fmaf(e, part_o[(u0 + s) * G * D + g * D + d], acc);
-    lsum = fmaf(e, part_ml[((u0 + s) * G + g) * 2 + 1], lsum);
+  for (int s0 = 0; s0 < n; s0 += CB) {
+    float mv[CB], lv[CB], ov[CB];
+#pragma unroll
+    for (int k = 0; k < CB; ++k) {
+      const int64_t u = u0 + min(s0 + k, n - 1);
+      mv[k] = part_ml[(u * G + g) * 2];
+      lv[k] = part_ml[(u * G + g) * 2 + 1];
+      ov[k] = part_o[u * G * D + g * D + d];
+    }
+#pragma unroll
+    for (int k = 0; k < CB; ++k) {
+      if (s0 + k >= n) break;
+      const float e = __expf(mv[k] - M);
+      acc = fmaf(e, ov[k], acc);
+      lsum = fmaf(e, lv[k], lsum);
+    }
   }
   float v = n > 0 ? acc / lsum : 0.0f;
   // the 8-point butterfly over the 8 consecutive threads of the group
@@ -448,14 +471,21 @@ int kv_cus() {
 
 }  // namespace
 
-// tokens per chunk: the largest of 256, 128, 64 whose units still fill the CUs
-// (and whose scores fit beside the image: T G <= 1024)
+// Sub-chunks of TS tokens (the scores beside the image: TS G <= 1024; smaller when the
+// sub-chunks would not fill the CUs), units of as many sub-chunks as leave about one
+// unit per CU.
 KvPlan kv_plan(int64_t B, int64_t Hkv, int64_t G, int64_t max_seq_len) {
   KvPlan p;
-  int T = G <= 4 ? 256 : 128;
-  while (T > 64 && B * Hkv * ((max_seq_len + T - 1) / T) < kv_cus()) T >>= 1;
-  p.T = T;
-  p.splits = int((max_seq_len + T - 1) / T);
+  const int64_t cus = kv_cus();
+  int TS = G <= 4 ? 256 : 128;
+  while (TS > 64 && B * Hkv * ((max_seq_len + TS - 1) / TS) < cus) TS >>= 1;
+  const int64_t subs = B * Hkv * ((max_seq_len + TS - 1) / TS);
+  int64_t ns = subs / cus;
+  if (ns < 1) ns = 1;
+  if (ns > 64) ns = 64;
+  p.TS = TS;
+  p.T = int(TS * ns);
+  p.splits = int((max_seq_len + p.T - 1) / p.T);
   p.units = B * Hkv * p.splits;
   return p;
 }
@@ -490,6 +520,7 @@ hipError_t launch_kv_attention(const glq_kv_cache& kv, const void* q, glq_dtype 
   a.max_len = int(max_seq_len < max_pages * kv.page_size ? max_seq_len : max_pages * kv.page_size);
   a.lp = log2_exact(kv.page_size);
   a.T = p.T;
+  a.TS = p.TS;
   a.splits = p.splits;
   a.units = int(p.units);
   a.sm_scale = sm_scale;

@@ -390,8 +390,9 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
  *   workspace    device, >= glq_e8kv_attention_workspace_bytes(...), 256-byte
  *                aligned; scratch (the chunks' partial results), no initial contents
  * Each chunk's softmax statistics and partial output are merged in chunk order:
- * run-to-run bit identity.  Accumulation is fp32; q is rotated and quantized to
- * 16-bit fixed point per head for exact integer dot products against the codewords.
+ * run-to-run bit identity.  Accumulation is fp32; q is rotated once (the rotation is
+ * orthonormal and symmetric, so no cached vector is rotated) and held in fp16, whose
+ * products with the codewords' exact fp16 values accumulate in fp32.
  * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_DTYPE, GLQ_ERR_RECIPE, GLQ_ERR_ALIGN,
  * GLQ_ERR_WORKSPACE, GLQ_ERR_HIP.
  */

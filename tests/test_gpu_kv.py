@@ -3,8 +3,8 @@ fp64 oracle (Glq v0.5.0 release notes, "Highlights"; glq 0.5.1, "KV cache
 compression": the cache dequantized inside the attention kernel, the 8-point
 inverse Hadamard, flash-decoding over chunks of the context).
 
-Tolerance: the query is rotated and rounded to 16-bit fixed point per head (a
-relative step of 1 / 30583 of its largest entry), scores and sums are fp32 and
+Tolerance: the query is rotated once and held in fp16 (products with the exact
+fp16 codeword values accumulate in fp32), scores and sums are fp32 and
 exp is the hardware's; the output's relative Frobenius error is bounded by 1e-3,
 the decode bound of the linear.  Slot-code caches give bit for bit the output of
 codebook-index caches, and repeated calls are bit-identical.
