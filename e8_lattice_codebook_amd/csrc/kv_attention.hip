@@ -12,16 +12,21 @@
 //   q . x = s (H8 q_g / sqrt(8)) . e_g   (the query is rotated once), and
 //   sum_t p_t x_t = H8 (sum_t p_t s_t e_t) / sqrt(8)   (rotated once, after the sum).
 // What remains per token is a codebook lookup (slot image in LDS, as in the
-// linear) and integer dot products (K) or FMAs (V) on the int4 codeword lanes.
+// linear), the codeword's int4 lanes as exact fp16 pairs, and fp32 dot products
+// (K) or FMAs (V).
 //
-// Kernel 1 (kv_split_kernel): persistent workgroups, one per CU, the codebook image
-// loaded into LDS once.  A unit is (sequence b, KV head h, chunk of T tokens).  Per
-// unit: the G query heads of h are rotated and held as fp16 pairs; every wave
-// scores tokens (lanes = token x stage x group: the codeword's int4 lanes become
-// exact fp16 pairs, fp32 dot products with the query, a DPP reduction per token);
-// one wave per head keeps the running max and exp-sum; the same lanes sum V in
-// fp32.  The unit's (max, sum, o) go to the workspace.  Kernel 2 (kv_combine_kernel) merges a sequence's chunks in chunk
-// order, divides, applies the 8-point butterfly and 1/sqrt(8), and casts.
+// Kernel 1 (kv_split_kernel): persistent workgroups of 512 threads, one per CU, the
+// codebook image loaded into LDS once.  A unit is (sequence b, KV head h, chunk of
+// T tokens) taken in sub-chunks of up to 256 tokens.  Per unit the G query heads
+// of h are rotated and held as fp16 pairs.  Per sub-chunk every wave scores its
+// tokens (lanes = token x stage x group, a DPP reduction per token), one wave per
+// head updates the running max and exp-sum (an online softmax: earlier V sums are
+// rescaled when the max grows), and the same lanes add p s_v 2c into their V sums;
+// the next sub-chunk's loads are issued one phase ahead.  At the end of the unit
+// the lanes of a group and then the waves (in wave order) are added and the
+// unit's (max, sum, o) go to the workspace.  Kernel 2 (kv_combine_kernel) merges a
+// sequence's chunks in chunk order, divides, applies the 8-point butterfly and
+// 1/sqrt(8), and casts.
 #include <math.h>
 
 #include "fwht_lds.h"
