@@ -94,6 +94,8 @@ __device__ __forceinline__ uint32_t kv_word(const uint32_t* img, uint32_t c, uin
 }
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // The entry's 2c as four fp16 pairs (2c_2k, 2c_2k+1) from its stored word w and m
 // (all ones: the entry is the word's negation): with t = w ^ m ^ 0x8888_8888 each
@@ -132,9 +134,7 @@ __device__ __forceinline__ float wave_max63(float v) {
 template <int D, int G, int ST, bool CODES>
 __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
   constexpr int GPS = D / 8;          // groups per vector
-  constexpr int LPT = ST * GPS;       // lanes per token in the K phase
-  constexpr int LPT_LOG2 = LPT == 8 ? 3 : LPT == 16 ? 4 : 5;
-  constexpr int TPI = 64 / LPT;       // tokens per wave instruction
+  constexpr int TPV = 64 / GPS;       // V phase: tokens per wave instruction (lane = token x group)
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   static_assert(G * D <= kKvBuf && G * GPS * 5 <= kKvBuf, "query staging fits");
 
@@ -165,9 +165,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
     if (ti < nd) img[ti] = tail;
   }
   const uint32_t delta = CODES ? slot_delta(a.pack_hdr) : 0u;
-  const int lt = lane >> LPT_LOG2;          // token of the lane in a K-phase batch
-  const int lst = (lane / GPS) % ST;        // stage of the lane
-  const int lg = lane % GPS;                // group of the lane
+  const int vt = lane / GPS;                // V phase: token of the lane in a batch
+  const int vg = lane % GPS;                // V phase: group of the lane
   const int P = 1 << a.lp;
   const float rs = a.resid_scale;
   __syncthreads();
@@ -208,82 +207,115 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
       for (int j = 0; j < 8; ++j) buf[tid * 8 + j] = qv[j];
     }
     __syncthreads();
-    half2v qh[G][4];
+    // the scores are an MFMA 16 x 16 x 32 per k-step of 32 dimensions: A = the query
+    // heads (rows, zero past G) x dimensions, B = dimensions x 16 tokens, one codeword
+    // (8 dimensions of one token) per lane; lane l holds A row l mod 16, dimensions
+    // 8 (l / 16) .. + 7 of each k-step
+    constexpr int KS = D / 32;
+    half8 qa[KS];
+    {
+      const int hr = lane & 15;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+      for (int ks = 0; ks < KS; ++ks) {
+        half8 v;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        qh[g][k] = half2v{_Float16(buf[(g * GPS + lg) * 8 + 2 * k]), _Float16(buf[(g * GPS + lg) * 8 + 2 * k + 1])};
+        for (int j = 0; j < 8; ++j)
+          v[j] = hr < G ? _Float16(buf[hr * D + ks * 32 + 8 * (lane >> 4) + j]) : _Float16(0.0f);
+        qa[ks] = v;
+      }
+    }
     __syncthreads();  // buf becomes the chunk's scores [T][G]
 
     // ---- the unit's tokens in sub-chunks of TS: scores, an online softmax (running
     // max and exp-sum per head, the V sums rescaled when the max grows), V sums
-    // Lane (token of the batch, stage, group) as in the K phase: the lane sums its
-    // group and stage of V over the wave's tokens; at the end of the unit the lanes
-    // of a group and then the waves are added.
+    // V: lane (token of the batch, group) sums its group of V, both stages combined
+    // exactly in fp16, over the wave's tokens; at the end of the unit the lanes of a
+    // group and then the waves are added.
     float o[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[g][j] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;  // wave g < G: head g's running statistics
-    const uint16_t* kidx = lst == 0 ? a.k0 : a.k1;
-    const uint16_t* vidx = lst == 0 ? a.v0 : a.v1;
     // Loads run ahead of their use: the next sub-chunk's K indices are issued once
     // this one's scores are done (in flight during its softmax and V), its V indices
-    // once this one's V is done (in flight during the next scores).  A wave's KBW
-    // batches (wave, wave + 8, ...) cover a sub-chunk of up to 256 tokens; slots
-    // past it load a valid row and are not used.
-    constexpr int KBW = (256 / TPI + kKvWaves - 1) / kKvWaves;
-    auto load_side = [&](int ts0, int nt, const uint16_t* idx, const float* scl, uint32_t (&c)[KBW],
-                         float (&sv)[KBW]) {
-      int rows[KBW];
+    // once this one's V is done (in flight during the next scores).  A wave's KBV
+    // batches (wave, wave + 8, ...) cover a sub-chunk of up to 256 tokens; slots past
+    // it load a valid row and are not used.
+    constexpr int KBV = 256 / TPV / kKvWaves;
+    auto load_v = [&](int ts0, int nt, uint32_t (&c)[KBV][ST], float (&sv)[KBV]) {
+      int rows[KBV];
 #pragma unroll
-      for (int k = 0; k < KBW; ++k) {
-        const int tt = (wave + k * kKvWaves) * TPI + lt;
+      for (int k = 0; k < KBV; ++k) {
+        const int tt = (wave + k * kKvWaves) * TPV + vt;
         rows[k] = row_of(ts0 + (tt < nt ? tt : 0));
       }
 #pragma unroll
-      for (int k = 0; k < KBW; ++k) {
-        c[k] = idx[rows[k] * GPS + lg];
-        sv[k] = scl[rows[k]];
+      for (int k = 0; k < KBV; ++k) {
+        c[k][0] = a.v0[rows[k] * GPS + vg];
+        if (ST == 2) c[k][ST - 1] = a.v1[rows[k] * GPS + vg];
+        sv[k] = a.vs[rows[k]];
       }
     };
-    uint32_t kc[KBW], vc[KBW];
-    float kks[KBW], vvs[KBW];
-    load_side(t0, min(a.TS, nt_unit), kidx, a.ks, kc, kks);
-    load_side(t0, min(a.TS, nt_unit), vidx, a.vs, vc, vvs);
+    // K: a wave takes token blocks wave, wave + 8, ... of 16 tokens; lane l loads
+    // token l mod 16's group 4 ks + l / 16 of every k-step ks, both stages
+    constexpr int KTB = 256 / 16 / kKvWaves;
+    const int ktok = lane & 15, kq = lane >> 4;
+    auto load_k = [&](int ts0, int nt, uint32_t (&c)[KTB][KS][ST], float (&sv)[KTB]) {
+      int rows[KTB];
+#pragma unroll
+      for (int k = 0; k < KTB; ++k) {
+        const int tt = (wave + k * kKvWaves) * 16 + ktok;
+        rows[k] = row_of(ts0 + (tt < nt ? tt : 0));
+      }
+#pragma unroll
+      for (int k = 0; k < KTB; ++k) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          c[k][ks][0] = a.k0[rows[k] * GPS + ks * 4 + kq];
+          if (ST == 2) c[k][ks][ST - 1] = a.k1[rows[k] * GPS + ks * 4 + kq];
+        }
+        sv[k] = a.ks[rows[k]];
+      }
+    };
+    uint32_t kc[KTB][KS][ST], vc[KBV][ST];
+    float kks[KTB], vvs[KBV];
+    load_k(t0, min(a.TS, nt_unit), kc, kks);
+    load_v(t0, min(a.TS, nt_unit), vc, vvs);
+    const half2v rs2 = half2v{_Float16(rs), _Float16(rs)};
     for (int sc = 0; sc < nt_unit; sc += a.TS) {
       const int nt = min(a.TS, nt_unit - sc);
-      const int batches = (nt + TPI - 1) / TPI;
 
-      // K: scores 0.5 s_k q' . (2 c0 + s_r 2 c1) of the sub-chunk's tokens
+      // K: scores 0.5 s_k q' . (2 c0 + s_r 2 c1) of the sub-chunk's tokens, by MFMA
+      // (2c0 + s_r 2c1 is exact in fp16 for s_r = 1/4: multiples of 1/4 below 8)
 #pragma unroll
-      for (int k = 0; k < KBW; ++k) {
-        const int bi = wave + k * kKvWaves;
-        if (bi >= batches) break;  // the same for the whole wave
-        const int tt = bi * TPI + lt;
-        const bool valid = tt < nt;
-        uint32_t m;
-        const uint32_t w = kv_word<CODES>(img, kc[k], delta, m);
-        half2v pr[4];
-        word_pairs(w, m, pr);
-        const float f = (lst ? 0.5f * rs : 0.5f) * kks[k];
-        float scv[G];
+      for (int k = 0; k < KTB; ++k) {
+        const int tb = wave + k * kKvWaves;
+        if (tb * 16 >= nt) break;  // the same for the whole wave
+        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float acc = 0.0f;
+        for (int ks = 0; ks < KS; ++ks) {
+          uint32_t m;
+          half2v p0[4];
+          word_pairs(kv_word<CODES>(img, kc[k][ks][0], delta, m), m, p0);
+          if (ST == 2) {
+            half2v p1[4];
+            word_pairs(kv_word<CODES>(img, kc[k][ks][ST - 1], delta, m), m, p1);
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_fdot2(pr[kk], qh[g][kk], acc, false);
-          scv[g] = lane_reduce(acc * f, LPT_LOG2);
+            for (int j = 0; j < 4; ++j) p0[j] = p1[j] * rs2 + p0[j];
+          }
+          const half8 bk = half8{p0[0].x, p0[0].y, p0[1].x, p0[1].y, p0[2].x, p0[2].y, p0[3].x, p0[3].y};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[ks], bk, acc, 0, 0, 0);
         }
-        if ((lane & (LPT - 1)) == LPT - 1 && tt < a.TS) {
+        const int tt = tb * 16 + ktok;
 #pragma unroll
-          for (int g = 0; g < G; ++g) buf[tt * G + g] = valid ? scv[g] : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          const int hh = 4 * kq + i;
+          if (hh < G && tt < a.TS) buf[tt * G + hh] = tt < nt ? acc[i] * 0.5f * kks[k] : -INFINITY;
         }
       }
       const int sc2 = sc + a.TS < nt_unit ? sc + a.TS : sc;  // past the unit: this one again, unused
-      load_side(t0 + sc2, min(a.TS, nt_unit - sc2), kidx, a.ks, kc, kks);
+      load_k(t0 + sc2, min(a.TS, nt_unit - sc2), kc, kks);
       __syncthreads();
 
       // softmax statistics, one wave per head: p = exp(s - m_new), the factor
@@ -307,36 +339,42 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
       }
       __syncthreads();
 
-      // V: o += p_t * 0.5 s_v * (+-1, s_r) * 2c over the wave's tokens
+      // V: o += p_t * 0.5 s_v * (2c0 + s_r 2c1) over the wave's tokens
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float al = buf[kKvBuf - 8 + g];
 #pragma unroll
         for (int j = 0; j < 8; ++j) o[g][j] *= al;
       }
+      const int vbatches = (nt + TPV - 1) / TPV;
 #pragma unroll
-      for (int k = 0; k < KBW; ++k) {
+      for (int k = 0; k < KBV; ++k) {
         const int bi = wave + k * kKvWaves;
-        if (bi >= batches) break;
-        const int tt = bi * TPI + lt;
+        if (bi >= vbatches) break;
+        const int tt = bi * TPV + vt;
         const bool valid = tt < nt;
         const int ts = valid ? tt : 0;
         uint32_t m;
-        const uint32_t w = kv_word<CODES>(img, vc[k], delta, m);
-        half2v pr[4];
-        word_pairs(w, m, pr);
-        const float f = (lst ? 0.5f * rs : 0.5f) * vvs[k];
+        half2v p0[4];
+        word_pairs(kv_word<CODES>(img, vc[k][0], delta, m), m, p0);
+        if (ST == 2) {
+          half2v p1[4];
+          word_pairs(kv_word<CODES>(img, vc[k][ST - 1], delta, m), m, p1);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p0[j] = p1[j] * rs2 + p0[j];
+        }
+        const float f = 0.5f * vvs[k];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float sv = valid ? buf[ts * G + g] * f : 0.0f;
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
-            o[g][2 * kk] = fmaf(sv, float(pr[kk].x), o[g][2 * kk]);
-            o[g][2 * kk + 1] = fmaf(sv, float(pr[kk].y), o[g][2 * kk + 1]);
+            o[g][2 * kk] = fmaf(sv, float(p0[kk].x), o[g][2 * kk]);
+            o[g][2 * kk + 1] = fmaf(sv, float(p0[kk].y), o[g][2 * kk + 1]);
           }
         }
       }
-      load_side(t0 + sc2, min(a.TS, nt_unit - sc2), vidx, a.vs, vc, vvs);
+      load_v(t0 + sc2, min(a.TS, nt_unit - sc2), vc, vvs);
       __syncthreads();  // the next sub-chunk overwrites the scores
     }
 
