@@ -340,13 +340,8 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
   if (!workspace || workspace_bytes < w.total) return GLQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return GLQ_ERR_ALIGN;
   const glq_layer& L = *layer;
-  if (w.fused) {
-    const Passes P = split_passes(L);
-    float* zp = at<float>(workspace, w.z_off);
-    if (!P.two) return from_hip(launch_fused_decode(L, x, x_dt, y, y_dt, zp, stream));
-    if (launch_fused_decode(P.a, x, x_dt, y, y_dt, zp, stream, 1) != hipSuccess) return GLQ_ERR_HIP;
-    return from_hip(launch_fused_decode(P.b, x, x_dt, y, y_dt, zp, stream, 2));
-  }
+  if (w.fused)  // every stage in one pass (5-8 bpw included)
+    return from_hip(launch_fused_decode(L, x, x_dt, y, y_dt, at<float>(workspace, w.z_off), stream));
   hipError_t e;
   float* z = at<float>(workspace, w.z_off);
   if (!w.prefill) {

@@ -72,7 +72,21 @@ struct FusedArgs {
   float sc_tab[kLenLog2s];  // [log2 L] 1 / (sqrt(L) kUqMax): u = t_H / sqrt(L), scale = max|t_H| * sc_tab
   float out_scale;  // s / 2 (codebook entries are held doubled)
   float sr;         // residual scale
-  int accumulate;   // add H_R of the row block to z_parts (second pass of a 5-8 bpw layer)
+  // further stages of a 5-8 bpw layer in one pass: 16-bit stages (primary image) and an
+  // 8-bit stage (the residual slots), each with its scale relative to s
+  const uint16_t* idx_x16[2];
+  const uint8_t* idx_x8;
+  float sc_x16[2];
+  float sc_x8;
+};
+
+// The index words of one row-step for every stage of the layer.
+template <int GL, int X16>
+struct RowIdx {
+  IdxRow<GL> i0, i1w;
+  Idx8Row<GL> i1b;
+  IdxRow<GL> x16[X16 > 0 ? X16 : 1];
+  Idx8Row<GL> x8;
 };
 
 __device__ __forceinline__ float x_at(const void* x, int dt, int64_t j) {
@@ -87,9 +101,9 @@ __device__ __forceinline__ float sign_f(uint32_t w, int k) { return float(int8_t
 
 struct StoreZ {  // element i < lim of a workgroup's rows -> its place in z_parts
   float* p;
-  int acc, lim;
+  int lim;
   __device__ void operator()(int64_t, int64_t i, float v) const {
-    if (i < lim) p[i] = acc ? p[i] + v : v;
+    if (i < lim) p[i] = v;
   }
 };
 
@@ -163,7 +177,7 @@ __device__ __forceinline__ void x_accumulate(const XRaw& r, int dt, bool neg, fl
 // registers, the six lane bits by shuffles), then stores them to p with 16-byte
 // stores.
 template <int E>
-__device__ __forceinline__ void wave_block_transform(const float* rowbuf, int base, float* p, int lane, int acc) {
+__device__ __forceinline__ void wave_block_transform(const float* rowbuf, int base, float* p, int lane) {
   float v[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) v[e] = rowbuf[swz(base + lane * E + e)];
@@ -179,13 +193,7 @@ __device__ __forceinline__ void wave_block_transform(const float* rowbuf, int ba
   }
 #pragma unroll
   for (int e = 0; e < E; e += 4) {
-    float4* q = reinterpret_cast<float4*>(p + lane * E + e);
-    float4 w = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
-    if (acc) {
-      const float4 o = *q;
-      w = make_float4(o.x + w.x, o.y + w.y, o.z + w.z, o.w + w.w);
-    }
-    *q = w;
+    *reinterpret_cast<float4*>(p + lane * E + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
   }
 }
 
@@ -213,9 +221,12 @@ __device__ __forceinline__ float lane_butterfly(float v, int k, float s, int lan
 
 __device__ __forceinline__ int dpp_partner1(int x) { return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false); }
 
-template <int RESID, bool FULL, bool CODES>
+// RESID: the first residual stage (0, 8 or 16 bits); X16, X8: further 16-bit stages
+// (0-2) and a trailing 8-bit stage (0-1) of a 5-8 bpw layer (after RESID 16)
+template <int RESID, int X16, int X8, bool FULL, bool CODES>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   constexpr int GL = 8;
+  constexpr int R8 = (RESID == 8 || X8) ? 8 : 0;  // the 8-bit table in LDS
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsDwords];
   __shared__ __attribute__((aligned(16))) float rowbuf[kRowBuf];  // the workgroup's row block (swizzled)
   float* fbuf = reinterpret_cast<float*>(lds);
@@ -248,12 +259,25 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   // with 64 lanes per row the row is wave-uniform: a scalar row base plus the
   // lane's 32-bit offset (g0 elements) addresses the index loads
   const uint32_t g0b = uint32_t(g0);
-  auto load_full = [&](int r, IdxRow<GL>& i0, IdxRow<GL>& i1w, Idx8Row<GL>& i1b) {
+  auto load16 = [&](const uint16_t* base, int64_t rb, IdxRow<GL>& d) {
+    load_idx16<GL>(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(base + rb) + 2 * g0b), d);
+  };
+  auto load_full = [&](int r, RowIdx<GL, X16>& n) {
     const int64_t rb = int64_t(r < a.m_pad ? r : 0) * G;
-    load_idx16<GL>(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(a.idx0 + rb) + 2 * g0b), i0);
-    if (RESID == 16)
-      load_idx16<GL>(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(idx1_16 + rb) + 2 * g0b), i1w);
-    if (RESID == 8) load_idx8<GL>(idx1_8 + rb + g0b, i1b);
+    load16(a.idx0, rb, n.i0);
+    if (RESID == 16) load16(idx1_16, rb, n.i1w);
+    if (RESID == 8) load_idx8<GL>(idx1_8 + rb + g0b, n.i1b);
+#pragma unroll
+    for (int k = 0; k < X16; ++k) load16(a.idx_x16[k], rb, n.x16[k]);
+    if (X8) load_idx8<GL>(a.idx_x8 + rb + g0b, n.x8);
+  };
+  auto load_off = [&](int off, RowIdx<GL, X16>& n) {
+    load_idx16<GL>(a.idx0 + off, n.i0);
+    if (RESID == 16) load_idx16<GL>(idx1_16 + off, n.i1w);
+    if (RESID == 8) load_idx8<GL>(idx1_8 + off, n.i1b);
+#pragma unroll
+    for (int k = 0; k < X16; ++k) load_idx16<GL>(a.idx_x16[k] + off, n.x16[k]);
+    if (X8) load_idx8<GL>(a.idx_x8 + off, n.x8);
   };
 
   // ---- steps 1-2.  The x loads go first, then the codebook image fetch; the
@@ -262,17 +286,12 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   // arrive and only parts 8-9 wait until every lane has its digits.
   // the first row-step's index vectors go first of all: their latency overlaps
   // the whole prologue
-  IdxRow<GL> n0, n1w;
-  Idx8Row<GL> n1b;
+  RowIdx<GL, X16> n;
   if (r_begin < r_end) {
-    if (FULL) {
-      load_full(r_begin, n0, n1w, n1b);
-    } else {
-      const int off = row_off(r_begin);
-      load_idx16<GL>(a.idx0 + off, n0);
-      if (RESID == 16) load_idx16<GL>(idx1_16 + off, n1w);
-      if (RESID == 8) load_idx8<GL>(idx1_8 + off, n1b);
-    }
+    if (FULL)
+      load_full(r_begin, n);
+    else
+      load_off(row_off(r_begin), n);
   }
   float* chunk = reinterpret_cast<float*>(lds + (kLdsDwords - kChunkDwords));
   // the split's chunk lies in the transform block of length 2^lb that starts at
@@ -292,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   for (int i = 0; i < 8; ++i)
     if (i < nsrc && c4 < K) x_issue(a, blk0 + (int64_t(i) << a.lk) + c4, xr[i]);
   ImageRegs img;
-  image_issue<RESID>(img, a.pack0_hdr, a.img0, a.res_slots, tid, CODES ? kHdrSlotDwords : 3);
+  image_issue<R8>(img, a.pack0_hdr, a.img0, a.res_slots, tid, CODES ? kHdrSlotDwords : 3);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     if (i < nsrc && c4 < K) x_accumulate(xr[i], a.x_dt, __popc(unsigned(s_loc & i)) & 1, t);
@@ -322,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   }
   fwht_lds_passes(StoreLds{chunk}, 0, a.lk, 8, chunk);
   __syncthreads();
-  image_store<0, 8, false, RESID>(img, lds, tid);
+  image_store<0, 8, false, R8>(img, lds, tid);
 
   // quantization: thread t < 16 LPR takes half h = t & 1 (columns 4 h .. 4 h + 3)
   // of group g = t >> 1, the group q = g & 7 of lane l = g >> 3; the 16 threads of
@@ -398,15 +417,19 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   __syncthreads();  // every lane has its digits before image parts 8-9 overwrite them
 
   // ---- step 3: the rest of the image, then the rows
-  image_store<8, 10, true, RESID>(img, lds, tid);
+  image_store<8, 10, true, R8>(img, lds, tid);
   __syncthreads();
 
   // one row-step: the lane's groups of row r against the digit planes, the
   // fixed-order lane reduction, the row partial into rowbuf
-  auto row_step = [&](const IdxRow<GL>& i0, const IdxRow<GL>& i1w, const Idx8Row<GL>& i1b, int r) {
+  auto row_step = [&](const RowIdx<GL, X16>& ix, int r) {
     const int o = r * RPS + row_in_step;
     float vv[1];
-    row_dots<1, GL, RESID, CODES>(lds, i0, i1w, i1b, dig, gs, a.sr, vv, delta);
+    row_dots<1, GL, RESID, CODES>(lds, ix.i0, ix.i1w, ix.i1b, dig, gs, a.sr, vv, delta);
+#pragma unroll
+    for (int k = 0; k < X16; ++k)
+      vv[0] = fmaf(a.sc_x16[k], float(stage16_total<GL, CODES>(lds, ix.x16[k], dig, gs, delta)), vv[0]);
+    if (X8) vv[0] = fmaf(a.sc_x8, float(stage8_total<GL>(lds, ix.x8, dig)), vv[0]);
     float v = vv[0] * sc[0];
     if (FULL) {
       v = dpp_add(v, 0);
@@ -420,25 +443,20 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
     }
     if (o < a.m_pad && lane_in_row == LPR - 1) rowbuf[swz(o - wg * (a.rs_per_wg * RPS))] = v * a.out_scale;
   };
-  auto load_row = [&](int r, IdxRow<GL>& i0, IdxRow<GL>& i1w, Idx8Row<GL>& i1b) {
-    if (FULL) {
-      load_full(r < r_end ? r : r_end - 1, i0, i1w, i1b);  // past the end: reload the last row
-      return;
-    }
-    const int off = row_off(r < r_end ? r : r_end - 1);  // past the end: reload the last row
-    load_idx16<GL>(a.idx0 + off, i0);
-    if (RESID == 16) load_idx16<GL>(idx1_16 + off, i1w);
-    if (RESID == 8) load_idx8<GL>(idx1_8 + off, i1b);
+  auto load_row = [&](int r, RowIdx<GL, X16>& ix) {
+    if (FULL)
+      load_full(r < r_end ? r : r_end - 1, ix);  // past the end: reload the last row
+    else
+      load_off(row_off(r < r_end ? r : r_end - 1), ix);
   };
   // two row-steps per iteration on two register sets, each loaded one step ahead
-  IdxRow<GL> m0, m1w;
-  Idx8Row<GL> m1b;
+  RowIdx<GL, X16> m;
   for (int r = r_begin; r < r_end; r += 2) {
-    load_row(r + 1, m0, m1w, m1b);
-    row_step(n0, n1w, n1b, r);
+    load_row(r + 1, m);
+    row_step(n, r);
     if (r + 1 < r_end) {
-      load_row(r + 2, n0, n1w, n1b);
-      row_step(m0, m1w, m1b, r + 1);
+      load_row(r + 2, n);
+      row_step(m, r + 1);
     }
   }
 
@@ -454,9 +472,9 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
       for (int j = wave; j < nrb; j += kThreads / 64) {
         const int base = j << a.lr;
         switch (a.lr) {
-          case 8: wave_block_transform<4>(rowbuf, base, zb + base, lane, a.accumulate); break;
-          case 9: wave_block_transform<8>(rowbuf, base, zb + base, lane, a.accumulate); break;
-          default: wave_block_transform<16>(rowbuf, base, zb + base, lane, a.accumulate); break;
+          case 8: wave_block_transform<4>(rowbuf, base, zb + base, lane); break;
+          case 9: wave_block_transform<8>(rowbuf, base, zb + base, lane); break;
+          default: wave_block_transform<16>(rowbuf, base, zb + base, lane); break;
         }
       }
     } else {
@@ -464,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
       // power-of-two span of rowbuf that covers the rows (rows past them unused)
       int span = a.lr;
       while ((1 << span) < rows) ++span;
-      fwht_lds_passes<StoreZ, 4>(StoreZ{zb, a.accumulate, rows}, 0, span, 0, rowbuf, a.lr);
+      fwht_lds_passes<StoreZ, 4>(StoreZ{zb, rows}, 0, span, 0, rowbuf, a.lr);
     }
   }
 
@@ -675,6 +693,11 @@ int device_cus() {
   return cus[dev];
 }
 
+template <int R_, int X_, int Y_>
+struct Stages {
+  static constexpr int R = R_, X = X_, Y = Y_;
+};
+
 struct FusedPlan {
   int lpr_log2, splits, rps, row_steps, wgs_per_split, rs_per_wg, lr;
   int W;  // row blocks of R = 2^lr rows (the cross-block transform's length)
@@ -757,7 +780,7 @@ size_t fused_decode_z_bytes(const glq_layer& L) {
 }
 
 hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt, void* y, glq_dtype y_dt,
-                               float* z_parts, hipStream_t stream, int pass) {
+                               float* z_parts, hipStream_t stream) {
   const FusedPlan p = fused_plan(L);
   FusedArgs a;
   a.x = x;
@@ -769,9 +792,20 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
   const bool codes = L.index_format == GLQ_INDEX_SLOT;
   a.img0 = reinterpret_cast<const uint32_t*>(
       p0 + (codes ? pack_slot_image_offset(GLQ_CODEBOOK_ENTRIES) : pack_image_offset(GLQ_CODEBOOK_ENTRIES)));
+  // further stages (5-8 bpw in one pass): 16-bit ones index the primary pack, an
+  // 8-bit one (always the last) the 256-entry residual pack
+  const int x16 = (L.n_extra >= 1 && L.extra_bits[0] == 16 ? 1 : 0) + (L.n_extra == 2 && L.extra_bits[1] == 16 ? 1 : 0);
+  const int x8 = L.n_extra >= 1 && L.extra_bits[L.n_extra - 1] == 8 ? 1 : 0;
+  for (int k = 0; k < 2; ++k) {
+    a.idx_x16[k] = k < x16 ? static_cast<const uint16_t*>(L.extra_idx[k]) : nullptr;
+    a.sc_x16[k] = k < x16 ? L.extra_scale[k] : 0.0f;
+  }
+  a.idx_x8 = x8 ? static_cast<const uint8_t*>(L.extra_idx[L.n_extra - 1]) : nullptr;
+  a.sc_x8 = x8 ? L.extra_scale[L.n_extra - 1] : 0.0f;
   a.res_slots = nullptr;
-  if (L.resid_bits == 8)
-    a.res_slots = reinterpret_cast<const uint32_t*>(static_cast<const char*>(L.cb2_pack) +
+  const void* res8 = L.resid_bits == 8 ? L.cb2_pack : x8 ? L.cb8_pack : nullptr;
+  if (res8)
+    a.res_slots = reinterpret_cast<const uint32_t*>(static_cast<const char*>(res8) +
                                                     pack_image_offset(GLQ_RESID8_ENTRIES)) + kPageCount;
   a.z_parts = z_parts;
   a.n = L.n;
@@ -791,26 +825,28 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
     a.sc_tab[k] = float(1.0 / (sqrt(double(int64_t(1) << k)) * double(kUqMax)));
   a.out_scale = 0.5f * L.wscale;
   a.sr = L.resid_scale;
-  a.accumulate = pass == 2;
   const dim3 grid(unsigned(p.splits * p.wgs_per_split)), block(kThreads);
   const bool full = p.lpr_log2 == 6;
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, a); };
-  switch (L.resid_bits * 4 + (full ? 2 : 0) + (codes ? 1 : 0)) {
-    case 0: go(fused_decode_kernel<0, false, false>); break;
-    case 1: go(fused_decode_kernel<0, false, true>); break;
-    case 2: go(fused_decode_kernel<0, true, false>); break;
-    case 3: go(fused_decode_kernel<0, true, true>); break;
-    case 32: go(fused_decode_kernel<8, false, false>); break;
-    case 33: go(fused_decode_kernel<8, false, true>); break;
-    case 34: go(fused_decode_kernel<8, true, false>); break;
-    case 35: go(fused_decode_kernel<8, true, true>); break;
-    case 64: go(fused_decode_kernel<16, false, false>); break;
-    case 65: go(fused_decode_kernel<16, false, true>); break;
-    case 66: go(fused_decode_kernel<16, true, false>); break;
-    default: go(fused_decode_kernel<16, true, true>); break;
+  // the stage layout: (RESID, X16, X8)
+  auto launch_fc = [&](auto tag) {
+    constexpr int R = decltype(tag)::R, X = decltype(tag)::X, Y = decltype(tag)::Y;
+    if (full)
+      codes ? go(fused_decode_kernel<R, X, Y, true, true>) : go(fused_decode_kernel<R, X, Y, true, false>);
+    else
+      codes ? go(fused_decode_kernel<R, X, Y, false, true>) : go(fused_decode_kernel<R, X, Y, false, false>);
+  };
+  switch (L.resid_bits * 16 + x16 * 2 + x8) {
+    case 0: launch_fc(Stages<0, 0, 0>{}); break;
+    case 128: launch_fc(Stages<8, 0, 0>{}); break;
+    case 256: launch_fc(Stages<16, 0, 0>{}); break;
+    case 257: launch_fc(Stages<16, 0, 1>{}); break;  // 16 + 16 + 8
+    case 258: launch_fc(Stages<16, 1, 0>{}); break;  // 16 + 16 + 16
+    case 259: launch_fc(Stages<16, 1, 1>{}); break;  // 16 + 16 + 16 + 8
+    default: launch_fc(Stages<16, 2, 0>{}); break;   // 16 + 16 + 16 + 16
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pass == 1) return e;
+  if (e != hipSuccess) return e;
   BlocksArgs b;
   b.z = z_parts;
   b.sign = L.sign_out;

@@ -132,10 +132,9 @@ hipError_t launch_gemv_lds(const glq_layer& layer, const void* uq, int64_t B, fl
 // fused_decode_z_bytes(layer) of scratch.
 bool fused_decode_supported(const glq_layer& layer, int64_t B);
 size_t fused_decode_z_bytes(const glq_layer& layer);
-// pass: 0 the whole call; 1 the first pass of a 5-8 bpw layer (z_parts only);
-// 2 its second pass (adds to z_parts, then the cross-block launch writes y)
+// Every stage of the layer (5-8 bpw included) is summed in the one pass.
 hipError_t launch_fused_decode(const glq_layer& layer, const void* x, glq_dtype x_dt, void* y, glq_dtype y_dt,
-                               float* z_parts, hipStream_t stream, int pass = 0);
+                               float* z_parts, hipStream_t stream);
 
 // Prefill matmul: z [M][m_pad] fp32 from u16 [M][n_pad] fp16.  launch_gemm takes the
 // LDS-codebook kernel (launch_gemm_lds) when gemm_lds_supported(layer), else the

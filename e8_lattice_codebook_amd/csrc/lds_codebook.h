@@ -366,5 +366,67 @@ __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& 
   }
 }
 
+// ---- one further stage of a 5-8 bpw layer (one activation row) ---------------------
+// The exact integer total sum_j 2c_j U_j over the lane's GL groups of a 16-bit stage
+// (primary image, the same lookup and complement correction as the primary stage of
+// row_dots) or of an 8-bit stage (the 256-entry residual slots, no complement).
+template <int GL, bool CODES>
+__device__ __forceinline__ int stage16_total(const uint32_t* lds, const IdxRow<GL>& ix,
+                                             const uint32_t (&dig)[1][GL][4], const int32_t (&gs)[1][GL],
+                                             uint32_t delta) {
+  const uint32_t two = 2;
+  uint32_t nw[GL], mm[GL];
+  if constexpr (CODES) {
+#pragma unroll
+    for (int q = 0; q < GL; ++q)
+      nw[q] = (q & 1) ? code_word<1>(lds, ix.w[q >> 1], delta, mm[q]) : code_word<0>(lds, ix.w[q >> 1], delta, mm[q]);
+  } else {
+    uint32_t d[GL];
+#pragma unroll
+    for (int q = 0; q < GL; ++q) d[q] = (q & 1) ? page_desc<1>(lds, ix.w[q >> 1], two) : page_desc<0>(lds, ix.w[q >> 1], two);
+#pragma unroll
+    for (int q = 0; q < GL; ++q) {
+      mm[q] = page_mask(d[q]);
+      nw[q] = (q & 1) ? slot_word<1>(lds, ix.w[q >> 1], d[q], mm[q], two)
+                      : slot_word<0>(lds, ix.w[q >> 1], d[q], mm[q], two);
+    }
+  }
+  int acc[4];
+#pragma unroll
+  for (int q = 0; q < GL; ++q) {
+    const uint32_t n = nw[q] ^ mm[q];
+    acc[0] = __mul24(int32_t(mm[q]), gs[0][q]) + (q == 0 ? 0 : acc[0]);
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      acc[p] = __builtin_amdgcn_sdot8(int(n), int(dig[0][q][p]), (q == 0 && p > 0) ? 0 : acc[p], false);
+  }
+  return ((acc[3] * 16 + acc[2]) * 16 + acc[1]) * 16 + acc[0];
+}
+
+template <int GL>
+__device__ __forceinline__ int stage8_total(const uint32_t* lds, const Idx8Row<GL>& ix,
+                                            const uint32_t (&dig)[1][GL][4]) {
+  const uint32_t two = 2;
+  uint32_t nw[GL];
+#pragma unroll
+  for (int q = 0; q < GL; ++q) {
+    const uint32_t w1 = ix.w[q >> 2];
+    uint32_t a1;
+    switch (q & 3) {
+      case 0: a1 = byte_x4<0>(w1, two); break;
+      case 1: a1 = byte_x4<1>(w1, two); break;
+      case 2: a1 = byte_x4<2>(w1, two); break;
+      default: a1 = byte_x4<3>(w1, two); break;
+    }
+    nw[q] = lds_at(lds + kResOff, a1);
+  }
+  int acc[4];
+#pragma unroll
+  for (int q = 0; q < GL; ++q)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) acc[p] = __builtin_amdgcn_sdot8(int(nw[q]), int(dig[0][q][p]), q == 0 ? 0 : acc[p], false);
+  return ((acc[3] * 16 + acc[2]) * 16 + acc[1]) * 16 + acc[0];
+}
+
 }  // namespace
 }  // namespace glq
