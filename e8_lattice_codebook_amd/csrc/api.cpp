@@ -292,7 +292,7 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
 }
 
 size_t glq_prefill_u_bytes(int64_t B, int64_t n_pad) {
-  if (B < 1 || !valid_pad(n_pad)) return 0;
+  if (B < 1 || !valid_pad(n_pad) || n_pad % 128 != 0) return 0;
   return tiled_u_bytes(B, n_pad);
 }
 
@@ -305,7 +305,8 @@ glq_status glq_input_rht_prefill(const void* x, glq_dtype x_dt, int64_t B, int64
                                  const int8_t* sign_in, void* u16, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream) {
   if (!x || !sign_in || !u16) return GLQ_ERR_NULL;
-  if (B < 1 || !valid_pad(n_pad) || n_pad < 256 || n < 1 || n > n_pad || B > int64_t(1) << 31) return GLQ_ERR_SHAPE;
+  if (B < 1 || !valid_pad(n_pad) || n_pad < 256 || n_pad % 128 != 0 || n < 1 || n > n_pad || B > int64_t(1) << 31)
+    return GLQ_ERR_SHAPE;
   if (!valid_dtype(x_dt)) return GLQ_ERR_DTYPE;
   if (!aligned(u16, 16)) return GLQ_ERR_ALIGN;
   const size_t need = glq_input_rht_workspace_bytes(B, n_pad, GLQ_F16);

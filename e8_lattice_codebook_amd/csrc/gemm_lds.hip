@@ -18,9 +18,11 @@
 // epilogue.  The A operand (u, fp16) is read from global memory by every wave;
 // the four waves of a workgroup share it through L1.
 //
-// K order: lane quarter q = lane / 16 of every MFMA takes the groups
-// [q G/4, (q+1) G/4) in turn (G = n_pad / 8), so a lane's indices are contiguous
-// in memory; A uses the same order.  The linear's input transform writes u in
+// K order: at k-step ks, lane quarter q = lane / 16 of every MFMA takes group
+// 16 (ks / 4) + 4 q + ks % 4 (G = n_pad / 8 groups, KS = G / 4 k-steps), so over
+// a block of 4 k-steps a lane's indices are 4 consecutive groups and the four
+// quarters of a row read 16 consecutive groups (one 32-byte piece per row per
+// index load); A uses the same order.  The linear's input transform writes u in
 // fragment order (each 16-token x 32-k fragment 1 KiB contiguous) so that every
 // A load is one coalesced 1 KiB read; u in plain row order is also accepted.
 //
@@ -176,9 +178,9 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
 
     // A fragments.  TILED: u in fragment order [ceil(M/16)][KS][4][16][8] (the
     // fragment of token block tb at k-step ks is 1 KiB at (tb KS + ks) 512 + 8 lane
-    // halves).  Natural: u [M][n_pad], the lane's row at group q KS + ks.
-    const half_t* abase = TILED ? a.u + (t0 >> 4) * int64_t(KS) * 512 + 8 * lane
-                                : a.u + t0 * a.n_pad + int64_t(q * KS) * 8;
+    // halves).  Natural: u [M][n_pad], the lane's row at group 16 (ks / 4) + 4 q + ks % 4.
+    const half_t* abase = TILED ? a.u + (t0 >> 4) * int64_t(KS) * 512 + 8 * lane : a.u + t0 * a.n_pad + 32 * q;
+    auto akoff = [&](int ks) { return TILED ? uint32_t(ks) * 512 : uint32_t(128 * (ks >> 2) + 8 * (ks & 3)); };
     // Token blocks past ceil(M / 16) (TILED) or rows past M read the tile's first
     // block or row instead: the buffer holds no more, and those rows are masked.
     auto arow_off = [&](int mi) {
@@ -186,9 +188,8 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
       const int64_t t = t0 + mi * 16 + r16;
       return uint32_t(t < a.M ? (mi * 16 + r16) * a.n_pad : 0);
     };
-    const uint32_t astep = TILED ? 512 : 8;  // halves per k-step
-    // index rows of the lane: output o = o_w + 16 ni + r16, groups from q * KS
-    const int64_t ibase = int64_t(o_w + r16) * G + q * KS;
+    // index rows of the lane: output o = o_w + 16 ni + r16, groups 4 kb + 4 q ..
+    const int64_t ibase = int64_t(o_w + r16) * G + 4 * q;
 
     // codeword fragment of out-block ni at k-step kk of the current index block
     auto dequant = [&](const u32x2 (&i0)[kNB], const uint32_t (&i1b)[kNB], const u32x2 (&i1w)[kNB], int ni,
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
       const int kc = kb < KS ? kb : KS - kKB;  // past the end: reload the last block
 #pragma unroll
       for (int ni = 0; ni < kNB; ++ni) {
-        const int64_t off = ibase + int64_t(16 * ni) * G + kc;
+        const int64_t off = ibase + int64_t(16 * ni) * G + 4 * kc;
         i0[ni] = *reinterpret_cast<const u32x2*>(a.idx0 + off);
         if (RESID == 8) i1b[ni] = *reinterpret_cast<const uint32_t*>(idx1_8 + off);
         if (RESID == 16) i1w[ni] = *reinterpret_cast<const u32x2*>(idx1_16 + off);
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
 #pragma unroll
     for (int mi = 0; mi < kMB; ++mi) {
       av[mi] = *reinterpret_cast<const half8*>(abase + arow_off(mi));
-      aw[mi] = *reinterpret_cast<const half8*>(abase + arow_off(mi) + (KS > 1 ? astep : 0));
+      aw[mi] = *reinterpret_cast<const half8*>(abase + arow_off(mi) + akoff(KS > 1 ? 1 : 0));
     }
     u32x2 i0[kNB], i0n[kNB];
     uint32_t i1b[kNB], i1bn[kNB];
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
 #pragma unroll
         for (int ni = 0; ni < kNB; ++ni)
           bn[ni] = (kk + 1 < kKB) ? dequant(i0, i1b, i1w, ni, kk + 1) : dequant(i0n, i1bn, i1wn, ni, 0);
-        const uint32_t ka = uint32_t(ks + 2 < KS ? ks + 2 : KS - 1) * astep;
+        const uint32_t ka = akoff(ks + 2 < KS ? ks + 2 : KS - 1);
 #pragma unroll
         for (int mi = 0; mi < kMB; ++mi) {
 #pragma unroll
@@ -347,7 +348,8 @@ hipError_t launch_gemm_lds(const glq_layer& L, const half_t* u16, int64_t M, boo
   a.scale = 0.5f * L.wscale;
   a.sr = L.resid_scale;
   a.accumulate = int(accumulate);
-  const int grid = a.tiles < cus_of_device() ? a.tiles : cus_of_device();
+  const int cus = cus_of_device();
+  const int grid = a.tiles < cus ? a.tiles : cus;
 #define GLQ_LAUNCH(R, T)                                                                                    \
   do {                                                                                                      \
     if (codes) hipLaunchKernelGGL((gemm_lds_kernel<R, T, true>), dim3(grid), dim3(kPThreads), 0, stream, a); \

@@ -63,8 +63,9 @@ struct StoreTiledHalf {
   float scale;
   __device__ void operator()(int64_t b, int64_t i, float v) const {
     const int64_t c = off + i;
+    // groups interleave by 4 over the lane quarters: g = 16 (ks / 4) + 4 q + ks % 4
     const uint32_t g = uint32_t(c >> 3);
-    const uint32_t q = g / KS, ks = g - q * KS;
+    const uint32_t q = (g >> 2) & 3u, ks = ((g >> 4) << 2) | (g & 3u);
     const int64_t o = ((((b >> 4) * KS + ks) * 4 + q) * 16 + (b & 15)) * 8 + (c & 7);
     u[o] = from_f32<half_t>(v * scale);
   }

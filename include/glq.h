@@ -313,12 +313,15 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
 /*
  * The prefill (B > 16) steps of glq_e8rht_linear on their own, with u in the
  * matmul's fragment order ("Inference kernels": the tensor-core path for B >= 2;
- * "How it works", item 2 for the transform).  Fragment order, for n_pad = 32 KS:
- * element (b, i) of u, with group g = i / 8, k-step ks = g mod KS and quarter
- * q = g / KS, sits at half index (((b / 16) KS + ks) 4 + q) 128 + (b mod 16) 8 + i mod 8;
+ * "How it works", item 2 for the transform).  Fragment order, for n_pad = 32 KS
+ * with KS a multiple of 4 (n_pad a multiple of 128): element (b, i) of u, with
+ * group g = i / 8, k-step ks = 4 floor(g / 16) + g mod 4 and quarter
+ * q = floor(g / 4) mod 4, sits at half index
+ * (((b / 16) KS + ks) 4 + q) 128 + (b mod 16) 8 + i mod 8;
  * a buffer holds ceil(B / 16) * 16 rows (rows past B are never read into y).
  *
- * glq_prefill_u_bytes — bytes of fragment-order u for B rows (0 for an invalid n_pad).
+ * glq_prefill_u_bytes — bytes of fragment-order u for B rows (0 for an invalid n_pad
+ *   or one that is not a multiple of 128).
  * glq_e8_matmul_prefill_supported — 1 if glq_e8_matmul_prefill takes the layer:
  *   n_pad >= 256, m_pad a multiple of 256, residual stage 0, 8 bits or 16 bits in
  *   the primary pack.
@@ -331,8 +334,8 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
  * glq_e8_matmul_prefill — z [B][m_pad] fp32 = u W~^T from fragment-order u16
  *   (codewords dequantized from the LDS-resident codebook into fp16 MFMA
  *   operands, fp32 accumulation, one split: glq_output_rht takes z with S = 1).
- * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE (B < 1, or a layer the prefill matmul does
- * not take), GLQ_ERR_DTYPE, GLQ_ERR_RECIPE, GLQ_ERR_ALIGN, GLQ_ERR_WORKSPACE,
+ * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE (B < 1, n_pad below 256 or not a multiple
+ * of 128, or a layer the prefill matmul does not take), GLQ_ERR_DTYPE, GLQ_ERR_RECIPE, GLQ_ERR_ALIGN, GLQ_ERR_WORKSPACE,
  * GLQ_ERR_HIP.
  */
 size_t glq_prefill_u_bytes(int64_t B, int64_t n_pad);

@@ -82,6 +82,10 @@ def test_workspace_queries():
     assert dec >= 2 * 8192 * 4 + 2 * 32768 * 4 + 2 * 32768 * 4
     pre = lib.glq_e8rht_linear_workspace_bytes(ctypes.byref(L), 2048)
     assert pre >= 2048 * 8192 * 2 + 2 * 2048 * 32768 * 4
+    # fragment-order u: whole 16-row blocks; k-steps in blocks of 4 (n_pad a multiple of 128)
+    assert lib.glq_prefill_u_bytes(17, 2688) == 32 * 2688 * 2
+    assert lib.glq_prefill_u_bytes(17, 320) == 0
+    assert lib.glq_prefill_u_bytes(0, 1024) == 0
 
 
 # ---- validation: fake, never-dereferenced device addresses --------------------
@@ -150,6 +154,10 @@ class TestValidation:
         assert lib.glq_e8_matmul(ctypes.byref(fake_layer()), A, 0, 1, A, A, 8, None) == 6
         assert lib.glq_e8_matmul_splits(ctypes.byref(fake_layer(n_pad=32768)), 1) == 8
         assert lib.glq_e8_matmul_splits(ctypes.byref(fake_layer(n_pad=32768)), 17) == 1
+        # fragment-order input transform: n_pad >= 256 and a multiple of 128
+        assert lib.glq_input_rht_prefill(A, 0, 17, 300, 320, A, A, None, 0, None) == 2
+        assert lib.glq_input_rht_prefill(A, 0, 17, 100, 128, A, A, None, 0, None) == 2
+        assert lib.glq_input_rht_prefill(A, 0, 17, 300, 384, A, A + 8, None, 0, None) == 5
 
 
     def test_index_format(self):

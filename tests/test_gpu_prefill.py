@@ -70,3 +70,63 @@ def test_fragment_order_path_equals_row_order(gpu_codebooks, M):
     zr = glq.e8_matmul(ql, u16)
     torch.cuda.synchronize()
     assert torch.equal(zf, zr)
+
+
+# Slot-code layers at many tiles per compute unit (m_pad 8192: 32 output tiles of
+# 256; M = 1000 gives 8 token tiles of 128, the last with 104 tokens and a token
+# block of 8; M = 2049 gives 17, the last with one token).
+@pytest.mark.parametrize("resid_bits", [0, 8, 16])
+@pytest.mark.parametrize("M", [1000, 2049])
+def test_prefill_large_slot_codes(gpu_codebooks, resid_bits, M):
+    layer = synth.random_layer(1000, 8000, resid_bits, seed=M + resid_bits, n_pad=1024, m_pad=8192)
+    ql = glq.QuantizedLayer.from_synth(layer, gpu_codebooks)
+    qs = ql.to_slot_codes()
+    x = torch.from_numpy(np.random.default_rng(M).standard_normal((M, 1000)).astype(np.float32)).to(DEV)
+    say("prefill large", resid_bits, M)
+    uf = glq.input_rht_prefill(x, 1024, ql.sign_in)
+    zw = glq.e8_matmul_prefill(qs, uf, M)
+    u16 = glq.input_rht(x, 1024, ql.sign_in, torch.float16)
+    torch.cuda.synchronize()
+    want = og.matmul_z(to_f64(u16), layer.idx0, layer.idx1, resid_bits, layer.wscale, layer.resid_scale)
+    err = rel_frob(to_f64(zw[0]), want)
+    say("  rel_frob", err)
+    assert err <= 1e-5, err
+    # repeat calls are bit-identical; the whole linear keeps the prefill bound
+    assert torch.equal(glq.e8_matmul_prefill(qs, uf, M), zw)
+    y = glq.e8rht_linear(qs, x, torch.float32)
+    torch.cuda.synchronize()
+    wy = og.linear(x.double().cpu().numpy(), layer.sign_in, layer.sign_out, 1024, 8000, layer.idx0, layer.idx1,
+                   resid_bits, layer.wscale, layer.resid_scale)
+    assert rel_frob(to_f64(y), wy) <= 5e-3
+
+
+@pytest.mark.parametrize("bpw", [5, 8])
+def test_prefill_large_slot_codes_recipes(gpu_codebooks, bpw):
+    # 5-8 bpw: the second pass adds its partial products to z
+    resid_bits, extra_bits = synth.RECIPES[bpw]
+    layer = synth.random_layer(1024, 8192, resid_bits, seed=bpw, n_pad=1024, m_pad=8192, extra_bits=extra_bits)
+    qs = glq.QuantizedLayer.from_synth(layer, gpu_codebooks).to_slot_codes()
+    x = torch.from_numpy(np.random.default_rng(bpw).standard_normal((1000, 1024)).astype(np.float32)).to(DEV)
+    y = glq.e8rht_linear(qs, x, torch.float32)
+    torch.cuda.synchronize()
+    want = og.linear(x.double().cpu().numpy(), layer.sign_in, layer.sign_out, 1024, 8192, layer.idx0, layer.idx1,
+                     resid_bits, layer.wscale, layer.resid_scale, extra=layer.oracle_extra())
+    assert rel_frob(to_f64(y), want) <= 5e-3
+
+
+@pytest.mark.parametrize("M,n,n_pad", [(33, 2000, 2048), (5, 2600, 2688)])
+def test_fragment_order_layout(M, n, n_pad):
+    # the documented placement of element (b, i): group g = i / 8, k-step
+    # ks = 4 (g / 16) + g % 4, quarter q = (g / 4) % 4, half index
+    # (((b / 16) KS + ks) 4 + q) 128 + (b % 16) 8 + i % 8; rows past M are not compared
+    sign = synth.random_layer(n, 256, 0, seed=M, n_pad=n_pad, m_pad=256).sign_in
+    x = torch.randn(M, n, device=DEV, dtype=torch.bfloat16)
+    st = torch.from_numpy(sign).to(DEV)
+    uf = glq.input_rht_prefill(x, n_pad, st).view(torch.float16).cpu().numpy()
+    u = glq.input_rht(x, n_pad, st, torch.float16).cpu().numpy()
+    KS = n_pad // 32
+    b, i = np.meshgrid(np.arange(M), np.arange(n_pad), indexing="ij")
+    g = i // 8
+    ks, q = 4 * (g // 16) + g % 4, (g // 4) % 4
+    pos = (((b // 16) * KS + ks) * 4 + q) * 128 + (b % 16) * 8 + i % 8
+    assert np.array_equal(uf[pos].view(np.uint16), u.view(np.uint16))
