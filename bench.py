@@ -345,8 +345,8 @@ def bench_prefill(glq, synth, cb, dev, args, log):
     q, q_other = (q_slot, q_cb) if args.index_format == "slot" else (q_cb, q_slot)
     _, raw = synth.make_x(l.n, M, wl.act_dtype, wl.seed, 0)
     x = torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
-    assert glq.e8_matmul_prefill_supported(q)
     u = torch.empty(glq.lib().glq_prefill_u_bytes(M, l.n_pad), dtype=torch.uint8, device=dev)
+    u16 = torch.empty((M, l.n_pad), dtype=torch.float16, device=dev)
     z = torch.empty((1, M, l.m_pad), dtype=torch.float32, device=dev)
     y = torch.empty((M, l.m), dtype=torch.bfloat16, device=dev)
     ws = glq.linear_workspace(q, M, dev)
@@ -361,24 +361,32 @@ def bench_prefill(glq, synth, cb, dev, args, log):
     e1.record()
     torch.cuda.synchronize()
     lin_ms = e0.elapsed_time(e1) / args.prefill_steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.prefill_steps)]
-    # the linear's prefill steps one by one, events around the matmul (gemm_lds_kernel)
-    for a, b in evs:
-        glq.input_rht_prefill(x, l.n_pad, q.sign_in, out=u)
-        a.record()
-        glq.e8_matmul_prefill(q, u, M, out=z)
-        b.record()
-        glq.output_rht(z, l.m, q.sign_out, out=y)
-    torch.cuda.synchronize()
-    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    def matmul_ms(qq):
+        # the linear's prefill steps one by one, events around the matmul: slot codes
+        # on fragment-order u (gemm_shared_kernel), codebook indices on row-order u
+        # (gemm_lds_kernel)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.prefill_steps)]
+        frag = glq.e8_matmul_prefill_supported(qq)
+        for a, b in evs:
+            if frag:
+                glq.input_rht_prefill(x, l.n_pad, qq.sign_in, out=u)
+            else:
+                glq.input_rht(x, l.n_pad, qq.sign_in, torch.float16, out=u16)
+            a.record()
+            if frag:
+                glq.e8_matmul_prefill(qq, u, M, out=z)
+            else:
+                glq.e8_matmul(qq, u16, out=z)
+            b.record()
+            glq.output_rht(z, l.m, qq.sign_out, out=y)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])), frag
+
+    gemm_ms, frag = matmul_ms(q)
     tflops = flops / (gemm_ms * 1e-3) / 1e12
-    for a, b in evs:  # the matmul on the other index format
-        a.record()
-        glq.e8_matmul_prefill(q_other, u, M, out=z)
-        b.record()
-    torch.cuda.synchronize()
-    other_tflops = flops / (float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3) / 1e12
+    other_tflops = flops / (matmul_ms(q_other)[0] * 1e-3) / 1e12
     log("bench: prefill linear %.4f ms, MFMA matmul %.4f ms = %.1f TFLOP/s" % (lin_ms, gemm_ms, tflops))
     return {
         "workload": "SmolLM3-3B gate 2048->11008 (m_pad 16384), M=2048 tokens, 3 bpw, bf16 activations",
@@ -387,8 +395,11 @@ def bench_prefill(glq, synth, cb, dev, args, log):
         "linear_ms": round(lin_ms, 5),
         "other_index_format": {"index_format": "codebook indices" if args.index_format == "slot" else "slot codes",
                                "value": round(other_tflops, 2), "unit": "TFLOP/s"},
-        "roofline": {"bound": "mfma", "kernel": "gemm_lds_kernel (prefill matmul: codewords from the LDS "
-                     "codebook dequantized into fp16 MFMA operands, fp32 accumulation)",
+        "roofline": {"bound": "mfma", "kernel": ("gemm_shared_kernel (prefill matmul: a 128-row codeword tile per "
+                                                 "k-step dequantized from the LDS codebook into LDS, shared by four "
+                                                 "waves as fp16 MFMA operands, fp32 accumulation)") if frag else
+                     ("gemm_lds_kernel (prefill matmul: codewords from the LDS codebook dequantized per wave into "
+                      "fp16 MFMA operands, fp32 accumulation)"),
                      "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
                      "flops_per_launch": flops},

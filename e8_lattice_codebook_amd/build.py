@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "e8_codebook.cpp", "pack.cpp", "rht.hip", "dequant.hip", "gemv.hip", "gemv_lds.hip",
-           "fused_decode.hip", "gemm.hip", "gemm_lds.hip", "kv_attention.hip"]
+           "fused_decode.hip", "gemm.hip", "gemm_lds.hip", "gemm_shared.hip", "kv_attention.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-I" + INCLUDE, "-I" + CSRC, "-Wall", "-Wno-unused-function"]
 # packed fp32 arithmetic stays off for all device code

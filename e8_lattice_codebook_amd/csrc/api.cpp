@@ -7,6 +7,18 @@
 
 using namespace glq;
 
+int glq::device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
 namespace {
 
 bool valid_dtype(glq_dtype d) { return d == GLQ_F32 || d == GLQ_F16 || d == GLQ_BF16; }
@@ -140,7 +152,9 @@ LinearWs linear_ws(const glq_layer& L, int64_t B) {
     return w;
   }
   w.u_off = off;
-  off += align256(w.prefill ? tiled_u_bytes(B, L.n_pad) : size_t(B) * size_t(L.n_pad) * 4);
+  off += align256(!w.prefill ? size_t(B) * size_t(L.n_pad) * 4
+                             : gemm_shared_supported(L) || gemm_lds_supported(L) ? tiled_u_bytes(B, L.n_pad)
+                                                                                : size_t(B) * size_t(L.n_pad) * 2);
   w.uq_off = off;
   if (w.lds) off += align256(uq_bytes(B, L.n_pad));
   w.rin_off = off;
@@ -167,13 +181,20 @@ hipError_t decode_matmul(const glq_layer& L, const float* u, int64_t B, void* uq
   return launch_gemv(L, u, B, z, stream);
 }
 
-// prefill matmul of every pass: u16 tiled for the LDS kernel, else row-major
-hipError_t prefill_matmul(const glq_layer& L, const half_t* u16, int64_t M, bool tiled, float* z,
-                          hipStream_t stream) {
+// prefill matmul of every pass.  u16 in fragment order: the shared-tile kernel
+// (slot codes), else the per-wave kernel; u16 in row order: launch_gemm.
+hipError_t prefill_pass(const glq_layer& L, const half_t* u16, int64_t M, bool tiled, float* z, hipStream_t stream,
+                        bool acc) {
+  if (!tiled) return launch_gemm(L, u16, M, z, stream, acc);
+  if (gemm_shared_supported(L)) return launch_gemm_shared(L, u16, M, z, stream, acc);
+  return launch_gemm_lds(L, u16, M, true, z, stream, acc);
+}
+
+hipError_t prefill_matmul(const glq_layer& L, const half_t* u16, int64_t M, bool tiled, float* z, hipStream_t stream) {
   const Passes P = split_passes(L);
-  hipError_t e = tiled ? launch_gemm_lds(P.a, u16, M, true, z, stream) : launch_gemm(P.a, u16, M, z, stream);
+  hipError_t e = prefill_pass(P.a, u16, M, tiled, z, stream, false);
   if (e != hipSuccess || !P.two) return e;
-  return tiled ? launch_gemm_lds(P.b, u16, M, true, z, stream, true) : launch_gemm(P.b, u16, M, z, stream, true);
+  return prefill_pass(P.b, u16, M, tiled, z, stream, true);
 }
 
 template <class T>
@@ -287,7 +308,8 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
   const size_t need = matmul_ws_bytes(*layer, B);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GLQ_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 256)) return GLQ_ERR_ALIGN;
-  if (B > kDecodeMaxB) return from_hip(prefill_matmul(*layer, static_cast<const half_t*>(u), B, false, z_parts, stream));
+  if (B > kDecodeMaxB)
+    return from_hip(prefill_matmul(*layer, static_cast<const half_t*>(u), B, false, z_parts, stream));
   return from_hip(decode_matmul(*layer, static_cast<const float*>(u), B, workspace, z_parts, stream));
 }
 
@@ -298,7 +320,7 @@ size_t glq_prefill_u_bytes(int64_t B, int64_t n_pad) {
 
 int glq_e8_matmul_prefill_supported(const glq_layer* layer) {
   if (!layer || check_layer(layer, false) != GLQ_OK) return 0;
-  return gemm_lds_supported(*layer) ? 1 : 0;
+  return gemm_shared_supported(*layer) || gemm_lds_supported(*layer) ? 1 : 0;
 }
 
 glq_status glq_input_rht_prefill(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t n_pad,
@@ -320,7 +342,8 @@ glq_status glq_e8_matmul_prefill(const glq_layer* layer, const void* u16, int64_
   glq_status st = check_layer(layer, false);
   if (st != GLQ_OK) return st;
   if (!u16 || !z) return GLQ_ERR_NULL;
-  if (B < 1 || B > int64_t(1) << 31 || !gemm_lds_supported(*layer)) return GLQ_ERR_SHAPE;
+  if (B < 1 || B > int64_t(1) << 31 || !(gemm_shared_supported(*layer) || gemm_lds_supported(*layer)))
+    return GLQ_ERR_SHAPE;
   if (!aligned(u16, 16)) return GLQ_ERR_ALIGN;
   return from_hip(prefill_matmul(*layer, static_cast<const half_t*>(u16), B, true, z, stream));
 }
@@ -353,7 +376,7 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
     if (e != hipSuccess) return GLQ_ERR_HIP;
   } else {
     half_t* u = at<half_t>(workspace, w.u_off);
-    if (gemm_lds_supported(L)) {  // u in the matmul's fragment order
+    if (gemm_shared_supported(L) || gemm_lds_supported(L)) {  // u in the matmuls' fragment order
       e = launch_rht_in_tiled(x, x_dt, B, L.n, L.n_pad, L.sign_in, u, at<float>(workspace, w.rin_off), stream);
       if (e != hipSuccess) return GLQ_ERR_HIP;
       e = prefill_matmul(L, u, B, true, z, stream);

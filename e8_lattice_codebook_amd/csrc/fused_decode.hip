@@ -681,18 +681,6 @@ hipError_t launch_blocks(const BlocksArgs& a, hipStream_t stream) {
   return launch_blocks_e<YT, 1>(a, stream);
 }
 
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cus[dev] = v;
-  }
-  return cus[dev];
-}
-
 template <int R_, int X_, int Y_>
 struct Stages {
   static constexpr int R = R_, X = X_, Y = Y_;

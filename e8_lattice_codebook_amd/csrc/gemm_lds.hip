@@ -16,25 +16,27 @@
 // in LDS as fp16; a 16-bit residual stage uses the image again.  2e = 2c0 + s_r 2c1
 // is exact in fp16 (s_r = 1/4: multiples of 1/4 below 8); s / 2 is applied in the
 // epilogue.  The A operand (u, fp16) is read from global memory by every wave;
-// the four waves of a workgroup share it through L1.
+// the four waves of a workgroup share it through L1.  The linear takes this
+// kernel for layers with codebook indices (their page image leaves no LDS for
+// the shared codeword tiles of the slot-code kernel), and the matmul on row-order
+// u for every format.
 //
 // K order: at k-step ks, lane quarter q = lane / 16 of every MFMA takes group
 // 16 (ks / 4) + 4 q + ks % 4 (G = n_pad / 8 groups, KS = G / 4 k-steps), so over
 // a block of 4 k-steps a lane's indices are 4 consecutive groups and the four
 // quarters of a row read 16 consecutive groups (one 32-byte piece per row per
 // index load); A uses the same order.  The linear's input transform writes u in
-// fragment order (each 16-token x 32-k fragment 1 KiB contiguous) so that every
-// A load is one coalesced 1 KiB read; u in plain row order is also accepted.
+// fragment order (each 16-token x 32-k fragment 1 KiB contiguous, tiled_u_bytes) so
+// that every A load is one coalesced 1 KiB read; u in plain row order is also
+// accepted.
 //
 // Tile: 16 kMB tokens x kWaves * 16 kNB outputs per workgroup (kMB x kNB MFMA
 // blocks per wave); persistent workgroups, one per CU, load the image once.
-#include "lds_codebook.h"
+#include "mfma_dequant.h"
 
 namespace glq {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -63,45 +65,6 @@ struct GemmArgs {
   float sr;
   int accumulate;             // add to z (second pass of a 5-8 bpw layer)
 };
-
-// fp16 (2c_0 .. 2c_7) of a slot word w, negated (complement) when m = ~0
-__device__ __forceinline__ half8 word_to_half8(uint32_t w, uint32_t m) {
-  const uint32_t t = w ^ m ^ 0x88888888u;                   // nibble = lane + 8, or 7 - lane
-  const uint32_t nb = 0xE408E408u ^ (m & 0x000F000Fu);      // -(1024 + 8), or -(1024 + 7)
-  const half2v bias = __builtin_bit_cast(half2v, nb);
-  half2v p[4];
-  p[0] = __builtin_bit_cast(half2v, (t & 0x000F000Fu) | 0x64006400u) + bias;
-  p[1] = __builtin_bit_cast(half2v, ((t >> 4) & 0x000F000Fu) | 0x64006400u) + bias;
-  p[2] = __builtin_bit_cast(half2v, ((t >> 8) & 0x000F000Fu) | 0x64006400u) + bias;
-  p[3] = __builtin_bit_cast(half2v, ((t >> 12) & 0x000F000Fu) | 0x64006400u) + bias;
-  return half8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
-}
-
-// the codeword of the 16-bit index (page image) or slot code (slot image) in half HI of w
-template <int HI, bool CODES>
-__device__ __forceinline__ half8 primary_half8(const uint32_t* lds, uint32_t w, uint32_t two, uint32_t delta) {
-  uint32_t m, word;
-  if constexpr (CODES) {
-    word = code_word<HI>(lds, w, delta, m);
-  } else {
-    const uint32_t desc = page_desc<HI>(lds, w, two);
-    m = page_mask(desc);
-    word = slot_word<HI>(lds, w, desc, m, two);
-  }
-  return word_to_half8(word, m);
-}
-
-// 16 * byte SEL of w (a byte address into the fp16 residual table)
-template <int SEL>
-__device__ __forceinline__ uint32_t byte_x16(uint32_t w) {
-  uint32_t r;
-  const uint32_t four = 4;
-  if (SEL == 0) asm volatile("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(four), "v"(w));
-  else if (SEL == 1) asm volatile("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(four), "v"(w));
-  else if (SEL == 2) asm volatile("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(four), "v"(w));
-  else asm volatile("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(four), "v"(w));
-  return r;
-}
 
 template <int RESID, bool TILED, bool CODES>
 __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
@@ -300,30 +263,16 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
   }
 }
 
-int cus_of_device() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cus[dev] = v;
-  }
-  return cus[dev];
-}
-
 }  // namespace
 
 bool gemm_lds_supported(const glq_layer& L) {
   // K split in 4 lane quarters of whole index loads (G / 4 a multiple of kKB and of 4
-  // groups for 8-byte index loads), whole 512-output tiles, residual from the image
+  // groups for 8-byte index loads), whole 256-output tiles, residual from the image
   // or an 8-bit table
   const int64_t G = L.n_pad / 8;
   return L.n_pad >= 256 && (G / 4) % kKB == 0 && L.m_pad % kTN == 0 &&
          (L.resid_bits != 16 || L.cb2_pack == L.cb_pack);
 }
-
-size_t tiled_u_bytes(int64_t M, int64_t n_pad) { return size_t((M + 15) / 16) * 16 * size_t(n_pad) * 2; }
 
 hipError_t launch_gemm_lds(const glq_layer& L, const half_t* u16, int64_t M, bool tiled, float* z,
                            hipStream_t stream, bool accumulate) {
@@ -348,7 +297,7 @@ hipError_t launch_gemm_lds(const glq_layer& L, const half_t* u16, int64_t M, boo
   a.scale = 0.5f * L.wscale;
   a.sr = L.resid_scale;
   a.accumulate = int(accumulate);
-  const int cus = cus_of_device();
+  const int cus = device_cus();
   const int grid = a.tiles < cus ? a.tiles : cus;
 #define GLQ_LAUNCH(R, T)                                                                                    \
   do {                                                                                                      \

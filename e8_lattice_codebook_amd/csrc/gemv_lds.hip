@@ -209,18 +209,6 @@ Plan make_plan(int64_t n_pad, int64_t B) {
   return p;
 }
 
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cus[dev] = v;
-  }
-  return cus[dev];
-}
-
 
 template <int NB, int GL, int RESID, bool FULL, bool CODES>
 hipError_t launch_t(const glq_layer& L, const void* uq, int64_t B, float* z, const Plan& p, hipStream_t stream,

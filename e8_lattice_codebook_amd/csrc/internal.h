@@ -87,6 +87,9 @@ inline size_t pack_image_offset(int64_t entries) { return align256(256 + size_t(
 constexpr int kHdrSlotDwords = 5;
 constexpr int kHdrSlotDelta = 6;
 constexpr int kSlotShared = 32768;  // codes below, and complemented codes, both reach [delta, 32768)
+// Slot images larger than this get no slot format: the shared-tile prefill kernel
+// keeps the slot image, an fp16 residual table and two codeword tiles in LDS.
+constexpr int kSlotImageMaxDwords = 37632;
 inline size_t pack_slot_image_offset(int64_t entries) { return pack_image_offset(entries) + size_t(kImageMaxDwords) * 4; }
 inline size_t pack_code_of_offset(int64_t entries) { return pack_slot_image_offset(entries) + size_t(kImageMaxDwords) * 4; }
 inline size_t pack_index_of_offset(int64_t entries) { return pack_code_of_offset(entries) + align256(size_t(entries) * 2); }
@@ -136,13 +139,21 @@ size_t fused_decode_z_bytes(const glq_layer& layer);
 hipError_t launch_fused_decode(const glq_layer& layer, const void* x, glq_dtype x_dt, void* y, glq_dtype y_dt,
                                float* z_parts, hipStream_t stream);
 
-// Prefill matmul: z [M][m_pad] fp32 from u16 [M][n_pad] fp16.  launch_gemm takes the
-// LDS-codebook kernel (launch_gemm_lds) when gemm_lds_supported(layer), else the
-// kernel that gathers codewords from the pack's int8 tables.
-// tiled: u16 in fragment order [ceil(M/16)][n_pad/32][4][16][8] (tiled_u_bytes), as
-// launch_rht_in_tiled writes it; otherwise [M][n_pad].
-bool gemm_lds_supported(const glq_layer& layer);
+// Compute units of the current device (256 if the query fails), cached per device.
+int device_cus();
+
+// Prefill matmul: z [M][m_pad] fp32 from u16 fp16, either in fragment order
+// [ceil(M/16)][n_pad/32][4][16][8] (tiled_u_bytes), as launch_rht_in_tiled writes it,
+// or [M][n_pad].  launch_gemm_shared: slot-code layers (gemm_shared_supported), u16
+// in fragment order.  launch_gemm_lds: the per-wave LDS-codebook kernel on either
+// order (tiled).  launch_gemm: u16 [M][n_pad]; launch_gemm_lds when
+// gemm_lds_supported(layer), else the kernel that gathers codewords from the pack's
+// int8 tables.
+bool gemm_shared_supported(const glq_layer& layer);
 size_t tiled_u_bytes(int64_t M, int64_t n_pad);
+hipError_t launch_gemm_shared(const glq_layer& layer, const half_t* u16, int64_t M, float* z, hipStream_t stream,
+                              bool accumulate = false);
+bool gemm_lds_supported(const glq_layer& layer);
 hipError_t launch_gemm_lds(const glq_layer& layer, const half_t* u16, int64_t M, bool tiled, float* z,
                            hipStream_t stream, bool accumulate = false);
 hipError_t launch_rht_in_tiled(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t N, const int8_t* sign,

@@ -500,18 +500,6 @@ hipError_t run_dg(const KvArgs& a, int grid, int B, int stages, bool codes, void
   return launch_combine<D, G>(a, B, out, out_dt, stream);
 }
 
-int kv_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cus[dev] = v;
-  }
-  return cus[dev];
-}
-
 }  // namespace
 
 // Sub-chunks of TS tokens (the scores beside the image: TS G <= 1024; smaller when the
@@ -519,7 +507,7 @@ int kv_cus() {
 // unit per CU.
 KvPlan kv_plan(int64_t B, int64_t Hkv, int64_t G, int64_t max_seq_len) {
   KvPlan p;
-  const int64_t cus = kv_cus();
+  const int64_t cus = device_cus();
   int TS = G <= 4 ? 256 : 128;
   while (TS > 64 && B * Hkv * ((max_seq_len + TS - 1) / TS) < cus) TS >>= 1;
   const int64_t subs = B * Hkv * ((max_seq_len + TS - 1) / TS);
@@ -568,7 +556,7 @@ hipError_t launch_kv_attention(const glq_kv_cache& kv, const void* q, glq_dtype 
   a.units = int(p.units);
   a.sm_scale = sm_scale;
   a.resid_scale = kv.resid_scale;
-  const int grid = int(p.units < kv_cus() ? p.units : kv_cus());
+  const int grid = int(p.units < device_cus() ? p.units : device_cus());
   const int st = kv.stages;
   if (kv.head_dim == 64) {
     switch (G) {

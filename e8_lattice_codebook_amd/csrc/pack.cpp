@@ -236,7 +236,7 @@ glq_status build_pack(const uint16_t* cb, int64_t entries, void* out_pack, size_
   }
   const int64_t slot_dwords = kSlotShared + int64_t(lone_neg.size());
   const bool slot_ok = int64_t(lone_plain.size()) <= delta && int64_t(lone_neg.size()) <= delta &&
-                       slot_dwords <= kImageMaxDwords;
+                       slot_dwords <= kSlotImageMaxDwords;
   std::vector<uint32_t> slot_img;
   std::vector<uint16_t> code_of(size_t(entries), 0), index_of(65536, 0);
   if (slot_ok) {

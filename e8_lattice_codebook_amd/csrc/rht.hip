@@ -56,6 +56,9 @@ struct StoreScaled {  // u[b][off + i] = RN(v * scale), rows of N
 // u16 in the prefill matmul's fragment order: token b, column c = off + i of group
 // g = c / 8 (k-step ks = g mod KS, lane quarter q = g / KS, KS = n_pad / 32) at
 // (((b / 16) KS + ks) 4 + q) 128 + (b mod 16) 8 + c mod 8
+// u in the prefill matmuls' fragment order, fp16: 16-token blocks; the groups
+// interleave by 4 over the four lane quarters, g = 16 (ks / 4) + 4 q + ks % 4,
+// KS = N / 32 k-steps.
 struct StoreTiledHalf {
   half_t* u;
   uint32_t KS;
@@ -63,7 +66,6 @@ struct StoreTiledHalf {
   float scale;
   __device__ void operator()(int64_t b, int64_t i, float v) const {
     const int64_t c = off + i;
-    // groups interleave by 4 over the lane quarters: g = 16 (ks / 4) + 4 q + ks % 4
     const uint32_t g = uint32_t(c >> 3);
     const uint32_t q = (g >> 2) & 3u, ks = ((g >> 4) << 2) | (g & 3u);
     const int64_t o = ((((b >> 4) * KS + ks) * 4 + q) * 16 + (b & 15)) * 8 + (c & 7);

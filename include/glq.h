@@ -323,8 +323,9 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
  * glq_prefill_u_bytes — bytes of fragment-order u for B rows (0 for an invalid n_pad
  *   or one that is not a multiple of 128).
  * glq_e8_matmul_prefill_supported — 1 if glq_e8_matmul_prefill takes the layer:
- *   n_pad >= 256, m_pad a multiple of 256, residual stage 0, 8 bits or 16 bits in
- *   the primary pack.
+ *   n_pad >= 256 and a multiple of 128, residual stage 0, 8 bits or 16 bits in the
+ *   primary pack, and m_pad a multiple of 64 (slot codes) or of 256 (codebook
+ *   indices).
  * glq_input_rht_prefill — u = H (sign_in * [x, 0]) / sqrt(n_pad) rounded to fp16,
  *   written in fragment order.
  *   x          device [B][n] in x_dt (F32, F16 or BF16)
@@ -332,11 +333,14 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
  *   workspace  device fp32 [B][n_pad] when n_pad > 16384 (else may be NULL),
  *              glq_input_rht_workspace_bytes(B, n_pad, GLQ_F16) bytes, 256-byte aligned
  * glq_e8_matmul_prefill — z [B][m_pad] fp32 = u W~^T from fragment-order u16
- *   (codewords dequantized from the LDS-resident codebook into fp16 MFMA
- *   operands, fp32 accumulation, one split: glq_output_rht takes z with S = 1).
+ *   (codewords dequantized from the LDS-resident codebook into fp16 MFMA operands,
+ *   fp32 accumulation, one split: glq_output_rht takes z with S = 1).  Slot codes:
+ *   per k-step a 64-row codeword tile is dequantized into LDS once and shared by
+ *   four waves; codebook indices (a larger LDS image): each wave dequantizes its
+ *   own fragments.
  * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE (B < 1, n_pad below 256 or not a multiple
- * of 128, or a layer the prefill matmul does not take), GLQ_ERR_DTYPE, GLQ_ERR_RECIPE, GLQ_ERR_ALIGN, GLQ_ERR_WORKSPACE,
- * GLQ_ERR_HIP.
+ * of 128, or a layer the prefill matmul does not take), GLQ_ERR_DTYPE,
+ * GLQ_ERR_RECIPE, GLQ_ERR_ALIGN, GLQ_ERR_WORKSPACE, GLQ_ERR_HIP.
  */
 size_t glq_prefill_u_bytes(int64_t B, int64_t n_pad);
 int glq_e8_matmul_prefill_supported(const glq_layer* layer);

@@ -32,6 +32,16 @@ def x_tensor(raw, dtype, device):
 TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
+def same_products(y_index, y_slot, prefill):
+    """Slot codes name the same codewords as codebook indices, so both formats form
+    the same exact products.  The decode paths and the row-order prefill kernel run
+    the same kernel on both: bit-equal outputs.  The prefill of a slot-code layer
+    runs the shared-tile kernel (another fp32 summation order): within 1e-5."""
+    if not prefill:
+        return bool(torch.equal(y_index, y_slot))
+    return rel_frob(to_f64(y_slot), to_f64(y_index)) <= 1e-5
+
+
 def to_f64(t):
     return t.detach().to(torch.float64).cpu().numpy()
 

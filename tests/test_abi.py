@@ -84,6 +84,7 @@ def test_workspace_queries():
     assert pre >= 2048 * 8192 * 2 + 2 * 2048 * 32768 * 4
     # fragment-order u: whole 16-row blocks; k-steps in blocks of 4 (n_pad a multiple of 128)
     assert lib.glq_prefill_u_bytes(17, 2688) == 32 * 2688 * 2
+    assert lib.glq_prefill_u_bytes(33, 2688) == 48 * 2688 * 2
     assert lib.glq_prefill_u_bytes(17, 320) == 0
     assert lib.glq_prefill_u_bytes(0, 1024) == 0
 

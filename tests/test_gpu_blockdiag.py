@@ -16,7 +16,7 @@ import torch
 
 import synth
 from oracle import glq as og, hadamard
-from gpu_util import TORCH_DT, rel_frob, say, to_f64, x_tensor
+from gpu_util import TORCH_DT, rel_frob, same_products, say, to_f64, x_tensor
 
 pytestmark = pytest.mark.gpu
 glq = pytest.importorskip("e8_lattice_codebook_amd")
@@ -92,7 +92,7 @@ def test_linear_blocks(gpu_codebooks, resid_bits, n, m, B):
     ys = glq.e8rht_linear(ql.to_slot_codes(), x.to(DEV), torch.float32)
     torch.cuda.synchronize()
     assert y.shape == (B, m)
-    assert torch.equal(y, ys)
+    assert same_products(y, ys, B > 16)
     err = rel_frob(to_f64(y), _oracle(layer, x))
     say("  rel_frob", err)
     assert err <= (1e-3 if B <= 16 else 5e-3), err
@@ -122,7 +122,7 @@ def test_linear_blocks_recipes(gpu_codebooks, bpw, B):
     y = glq.e8rht_linear(ql, x.to(DEV), torch.float32)
     ys = glq.e8rht_linear(ql.to_slot_codes(), x.to(DEV), torch.float32)
     torch.cuda.synchronize()
-    assert torch.equal(y, ys)
+    assert same_products(y, ys, B > 16)
     assert rel_frob(to_f64(y), _oracle(layer, x)) <= (1e-3 if B <= 16 else 5e-3)
 
 
@@ -139,18 +139,19 @@ def test_decode_matmul_unpadded_k(gpu_codebooks, B):
 
 @pytest.mark.parametrize("M", [17, 300])
 def test_prefill_fragment_order_unpadded(gpu_codebooks, M):
-    # fragment order over K = 2688 (84 k-steps per lane quarter): the linear's
-    # prefill steps equal the row-order matmul on the same fp16 u, bit for bit,
-    # and the matmul alone is within fp32 accumulation of the oracle
+    # fragment order over K = 2688 (84 k-steps of 32, 21 index blocks): the
+    # linear's prefill steps for slot codes and the row-order matmul on the same fp16
+    # u are both within fp32 accumulation of the oracle
     layer = synth.block_layer(2688, 2560, 8, seed=M)
     ql = glq.QuantizedLayer.from_synth(layer, gpu_codebooks)
-    assert glq.e8_matmul_prefill_supported(ql)
+    qs = ql.to_slot_codes()
+    assert glq.e8_matmul_prefill_supported(qs)
     x = torch.randn(M, 2688, device=DEV, dtype=torch.bfloat16)
     uf = glq.input_rht_prefill(x, 2688, ql.sign_in)
-    zf = glq.e8_matmul_prefill(ql, uf, M)
+    zf = glq.e8_matmul_prefill(qs, uf, M)
     u16 = glq.input_rht(x, 2688, ql.sign_in, torch.float16)
     zr = glq.e8_matmul(ql, u16)
     torch.cuda.synchronize()
-    assert torch.equal(zf, zr)
     want = og.matmul_z(to_f64(u16), layer.idx0, layer.idx1, 8, layer.wscale, layer.resid_scale)
+    assert rel_frob(to_f64(zf[0]), want) <= 1e-5
     assert rel_frob(to_f64(zr[0]), want) <= 1e-5

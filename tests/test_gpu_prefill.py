@@ -57,19 +57,27 @@ def test_prefill_linear(gpu_codebooks, M):
 
 
 @pytest.mark.parametrize("M", [17, 300])
-def test_fragment_order_path_equals_row_order(gpu_codebooks, M):
-    # the linear's prefill steps (input transform into fragment order, matmul on it)
-    # give bit for bit the matmul on the same fp16 u in row order
+def test_fragment_order_path_matches_row_order(gpu_codebooks, M):
+    # the linear's prefill steps (input transform into fragment order, then the
+    # shared-tile matmul for slot codes or the per-wave matmul for codebook indices)
+    # and the per-wave matmul on the same fp16 u in row order: the same exact
+    # products, summed in other orders (fp32), all within 1e-5 of the oracle; the
+    # per-wave kernel gives the same bits on either order of u
     layer = synth.random_layer(2000, 3000, 8, seed=M + 1, n_pad=2048, m_pad=4096)
     ql = glq.QuantizedLayer.from_synth(layer, gpu_codebooks)
-    assert glq.e8_matmul_prefill_supported(ql)
+    qs = ql.to_slot_codes()
+    assert glq.e8_matmul_prefill_supported(qs) and glq.e8_matmul_prefill_supported(ql)
     x = torch.randn(M, 2000, device=DEV, dtype=torch.bfloat16)
     uf = glq.input_rht_prefill(x, ql.n_pad, ql.sign_in)
-    zf = glq.e8_matmul_prefill(ql, uf, M)
+    zs = glq.e8_matmul_prefill(qs, uf, M)
+    zi = glq.e8_matmul_prefill(ql, uf, M)
     u16 = glq.input_rht(x, ql.n_pad, ql.sign_in, torch.float16)
     zr = glq.e8_matmul(ql, u16)
     torch.cuda.synchronize()
-    assert torch.equal(zf, zr)
+    assert torch.equal(zi, zr)
+    want = og.matmul_z(to_f64(u16), layer.idx0, layer.idx1, 8, layer.wscale, layer.resid_scale)
+    assert rel_frob(to_f64(zs[0]), want) <= 1e-5
+    assert rel_frob(to_f64(zr[0]), want) <= 1e-5
 
 
 # Slot-code layers at many tiles per compute unit (m_pad 8192: 32 output tiles of
@@ -118,7 +126,8 @@ def test_prefill_large_slot_codes_recipes(gpu_codebooks, bpw):
 def test_fragment_order_layout(M, n, n_pad):
     # the documented placement of element (b, i): group g = i / 8, k-step
     # ks = 4 (g / 16) + g % 4, quarter q = (g / 4) % 4, half index
-    # (((b / 16) KS + ks) 4 + q) 128 + (b % 16) 8 + i % 8; rows past M are not compared
+    # (((b / 16) KS + ks) 4 + q) 128 + (b % 16) 8 + i % 8 with KS = n_pad / 32; rows
+    # past M are not compared
     sign = synth.random_layer(n, 256, 0, seed=M, n_pad=n_pad, m_pad=256).sign_in
     x = torch.randn(M, n, device=DEV, dtype=torch.bfloat16)
     st = torch.from_numpy(sign).to(DEV)

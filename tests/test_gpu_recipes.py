@@ -16,7 +16,7 @@ import torch
 
 import synth
 from oracle import glq as og
-from gpu_util import rel_frob, say, to_f64
+from gpu_util import rel_frob, same_products, say, to_f64
 
 pytestmark = pytest.mark.gpu
 glq = pytest.importorskip("e8_lattice_codebook_amd")
@@ -50,8 +50,8 @@ def _oracle_linear(layer, x):
 
 
 # (n, m, n_pad, m_pad, B): B = 1 two-launch path (full 64-lane rows, fewer lanes
-# per row), B = 5 staged decode, B = 130 prefill on the LDS codebook, B = 40 with
-# n_pad 64 on the prefill kernel that gathers from the int8 tables
+# per row), B = 5 staged decode, B = 130 prefill (the shared-tile kernel for slot
+# codes), B = 40 with n_pad 64 on the prefill kernel that gathers from the int8 tables
 CASES = [(5120, 700, 8192, 1024, 1), (60, 3000, 64, 4096, 1), (3000, 2000, 4096, 2048, 5),
          (2000, 3000, 2048, 4096, 130), (60, 200, 64, 256, 40)]
 
@@ -67,7 +67,7 @@ def test_linear_recipe(gpu_codebooks, bpw, n, m, n_pad, m_pad, B):
     yi = glq.e8rht_linear(ql, x.to(DEV), torch.float32)
     ys = glq.e8rht_linear(ql.to_slot_codes(), x.to(DEV), torch.float32)
     torch.cuda.synchronize()
-    assert torch.equal(yi, ys)
+    assert same_products(yi, ys, B > 16 and n_pad >= 256)
     err = rel_frob(to_f64(yi), _oracle_linear(layer, x))
     say("  rel_frob", err)
     # the bounds of the 2-4 bpw paths: the extra stages only refine the weights
@@ -105,11 +105,13 @@ def test_prefill_matmul_recipe(gpu_codebooks, bpw):
         err = rel_frob(to_f64(z[0]), want)
         say("  rel_frob", err)
         assert err <= 1e-5, (M, err)
-        # the linear's prefill steps (fragment-order u, LDS-codebook kernel) give
-        # bit for bit the row-order matmul on the same fp16 u
+        # the linear's prefill steps for slot codes (fragment-order u, shared-tile
+        # kernel, both passes) within fp32 accumulation of the oracle
         x = torch.randn(M, 1000, device=DEV, dtype=torch.bfloat16)
         uf = glq.input_rht_prefill(x, ql.n_pad, ql.sign_in)
-        zf = glq.e8_matmul_prefill(ql, uf, M)
-        zr = glq.e8_matmul(ql, glq.input_rht(x, ql.n_pad, ql.sign_in, torch.float16))
+        zf = glq.e8_matmul_prefill(ql.to_slot_codes(), uf, M)
+        u16 = glq.input_rht(x, ql.n_pad, ql.sign_in, torch.float16)
         torch.cuda.synchronize()
-        assert torch.equal(zf, zr)
+        wf = og.matmul_z(to_f64(u16), layer.idx0, layer.idx1, layer.resid_bits, layer.wscale, layer.resid_scale,
+                         extra=layer.oracle_extra())
+        assert rel_frob(to_f64(zf[0]), wf) <= 1e-5

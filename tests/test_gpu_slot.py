@@ -3,9 +3,11 @@
 glq_slot_codes maps each codebook index to a slot code once, at load time; the
 kernels then read a codeword from the slot image with one LDS access instead of
 two.  The codewords, hence the integer dot products and fp16 MFMA operands, are
-the same as with codebook indices, so every path must give bit for bit the
+the same as with codebook indices, so every decode path must give bit for bit the
 output of the index-format layer, which is itself checked against the fp64
-oracle (glq 0.5.1, "How it works" items 1-4, "Inference kernels").
+oracle (glq 0.5.1, "How it works" items 1-4, "Inference kernels").  The prefill
+of a slot-code layer runs the shared-tile kernel, whose fp32 sums run in another
+order: within 1e-5 of the index-format output.
 """
 import numpy as np
 import pytest
@@ -13,7 +15,7 @@ import torch
 
 import synth
 from oracle import glq as og
-from gpu_util import rel_frob, say, to_f64
+from gpu_util import rel_frob, same_products, say, to_f64
 
 pytestmark = pytest.mark.gpu
 glq = pytest.importorskip("e8_lattice_codebook_amd")
@@ -74,8 +76,9 @@ def _oracle(layer, x):
 
 
 # (n, m, n_pad, m_pad, B): B = 1 two-launch path (64 lanes per row, fewer, split
-# counts 1..8), B = 5 staged decode, B = 130 prefill on the LDS-codebook kernel,
-# B = 40 with n_pad 64 on the prefill kernel that gathers from the int8 table
+# counts 1..8), B = 5 staged decode, B = 130 prefill (the shared-tile kernel for
+# slot codes), B = 40 with n_pad 64 on the prefill kernel that gathers from the
+# int8 table (both formats)
 CASES = [(5120, 700, 8192, 1024, 1), (32768, 64, 32768, 64, 1), (60, 3000, 64, 4096, 1), (100, 8000, 128, 8192, 1),
          (3000, 2000, 4096, 2048, 5), (2000, 3000, 2048, 4096, 130), (60, 200, 64, 256, 40)]
 
@@ -87,7 +90,7 @@ def test_linear_slot_equals_index(gpu_codebooks, resid_bits, n, m, n_pad, m_pad,
     x = torch.from_numpy(np.random.default_rng(B).standard_normal((B, n)).astype(np.float32)).to(torch.bfloat16)
     say("slot linear", n, m, n_pad, m_pad, B, resid_bits)
     yi, ys = _both(layer, gpu_codebooks, x.to(DEV))
-    assert torch.equal(yi, ys)
+    assert same_products(yi, ys, B > 16 and n_pad >= 256)
     tol = 1e-3 if B <= 16 else 5e-3
     assert rel_frob(to_f64(ys), _oracle(layer, x)) <= tol
 
