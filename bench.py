@@ -298,7 +298,7 @@ def pmc_summary(dirs, copy_bytes):
         "# HBM traffic of one B = 1 call (%s), Devstral-Small-24B MLP decode" % " + ".join(FUSED_KERNEL_NAMES),
         "# commands (from the repository root, after cd /tmp && export TMPDIR=/tmp for the profiler):",
         "#   rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR --output-format csv -- python3 bench.py --steps 3 --warmup 1 "
-        "--no-cpu-baseline --no-prefill --no-block --no-recipes --no-blockdiag",
+        "--no-cpu-baseline --no-prefill --no-block --no-recipes --no-blockdiag --no-kv",
         "#   rocprofv3 --pmc WRITE_SIZE -d WRITE_DIR --output-format csv -- (same)",
         "#   rocprofv3 --pmc FETCH_SIZE -d COPY_FETCH_DIR --output-format csv -- python3 bench.py --calibrate-copy %d"
         % copy_bytes,
@@ -395,7 +395,7 @@ def bench_prefill(glq, synth, cb, dev, args, log):
         "linear_ms": round(lin_ms, 5),
         "other_index_format": {"index_format": "codebook indices" if args.index_format == "slot" else "slot codes",
                                "value": round(other_tflops, 2), "unit": "TFLOP/s"},
-        "roofline": {"bound": "mfma", "kernel": ("gemm_shared_kernel (prefill matmul: a 128-row codeword tile per "
+        "roofline": {"bound": "mfma", "kernel": ("gemm_shared_kernel (prefill matmul: a 64-row codeword tile per "
                                                  "k-step dequantized from the LDS codebook into LDS, shared by four "
                                                  "waves as fp16 MFMA operands, fp32 accumulation)") if frag else
                      ("gemm_lds_kernel (prefill matmul: codewords from the LDS codebook dequantized per wave into "
@@ -529,7 +529,7 @@ def bench_recipes(glq, synth, cb, dev, args, log, value_4bpw):
         log("bench: %d bpw Devstral MLP B=1: %.4f ms/step, %.1f GB/s (%d copies)" % (bpw, ms, gbs, copies))
         out["by_bpw"][str(bpw)] = {"ms_per_step": round(ms, 5), "value": round(gbs, 2),
                                    "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": step_bytes,
-                                   "launches_per_layer": 3}
+                                   "launches_per_layer": 2}
         del qls, ws
         torch.cuda.empty_cache()
     return out
