@@ -359,8 +359,9 @@ glq_status glq_e8_matmul_prefill(const glq_layer* layer, const void* u16, int64_
  *   workspace  device, >= glq_e8rht_linear_workspace_bytes(layer, B), 256-byte aligned;
  *              scratch whose contents need not be initialized.  Calls that may
  *              overlap (different streams) need separate workspaces.
- * B = 1, n_pad >= 64 and the residual stage (if any) in the primary pack or an
- * 8-bit one: two launches.  The first forms, in every workgroup, its column chunk
+ * B = 1, n_pad >= 64 and every 16-bit residual stage in the primary pack (8-bit
+ * stages always qualify; the further stages of a 5-8 bpw layer are added in the
+ * same pass): two launches.  The first forms, in every workgroup, its column chunk
  * of the input transform in LDS via H_N = H_{N/K} (x) H_K, quantizes it, walks its
  * rows against the LDS codebook and applies H_R to its block of R output rows
  * (H_{m_pad} = H_W (x) H_R); the second sums the split partials in a fixed order
