@@ -421,17 +421,11 @@ __global__ __launch_bounds__(D) void kv_combine_kernel(const float* __restrict__
   const int h = hq / G, g = hq % G;
   const int n = (min(max(seq_lens[b], 0), max_len) + T - 1) / T;
   const int64_t u0 = (int64_t(b) * Hkv + h) * splits;
-  // loads in batches of 8 chunks (in flight together), sums in chunk order
-  constexpr int CB = 8;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < n; s0 += CB) {
-    float mv[CB];
-#pragma unroll
-    for (int k = 0; k < CB; ++k) mv[k] = s0 + k < n ? part_ml[((u0 + s0 + k) * G + g) * 2] : -INFINITY;
-#pragma unroll
-    for (int k = 0; k < CB; ++k) M = fmaxf(M, mv[k]);
-  }
-  float acc = 0.0f, lsum = 0.0f;
+  // one pass over batches of 16 chunks, whose loads are in flight together: the
+  // running max is raised to the batch's, the sums are rescaled and the batch added
+  // in chunk order (up to 16 chunks: the global max, then one ordered sum)
+  constexpr int CB = 16;
+  float M = -INFINITY, acc = 0.0f, lsum = 0.0f;
   for (int s0 = 0; s0 < n; s0 += CB) {
     float mv[CB], lv[CB], ov[CB];
 #pragma unroll
@@ -441,13 +435,21 @@ __global__ __launch_bounds__(D) void kv_combine_kernel(const float* __restrict__
       lv[k] = part_ml[(u * G + g) * 2 + 1];
       ov[k] = part_o[u * G * D + g * D + d];
     }
+    float Mb = M;
+#pragma unroll
+    for (int k = 0; k < CB; ++k) Mb = s0 + k < n ? fmaxf(Mb, mv[k]) : Mb;
+    // every chunk below n holds a token, so Mb is finite; exp(-inf) = 0 on the first batch
+    const float r = __expf(M - Mb);
+    acc *= r;
+    lsum *= r;
 #pragma unroll
     for (int k = 0; k < CB; ++k) {
       if (s0 + k >= n) break;
-      const float e = __expf(mv[k] - M);
+      const float e = __expf(mv[k] - Mb);
       acc = fmaf(e, ov[k], acc);
       lsum = fmaf(e, lv[k], lsum);
     }
+    M = Mb;
   }
   float v = n > 0 ? acc / lsum : 0.0f;
   // the 8-point butterfly over the 8 consecutive threads of the group
