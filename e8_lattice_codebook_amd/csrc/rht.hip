@@ -35,7 +35,10 @@ struct LoadSignedX {  // x [B][n] -> sign[c] * x[b][c] at c = off + i, zero beyo
   const int8_t* sign;
   __device__ float operator()(int64_t b, int64_t i) const {
     const int64_t c = off + i;
-    return c < n ? to_f32<XT>(x[b * n + c]) * float(sign[c]) : 0.0f;
+    // both loads unconditional (sign has n_pad entries, x's column is clamped into its
+    // row, n >= 1), so that a thread's loads are in flight together; zero beyond n
+    const float v = to_f32<XT>(x[b * n + (c < n ? c : n - 1)]) * float(sign[c]);
+    return c < n ? v : 0.0f;
   }
 };
 
@@ -71,6 +74,26 @@ struct StoreTiledHalf {
     const int64_t o = ((((b >> 4) * KS + ks) * 4 + q) * 16 + (b & 15)) * 8 + (c & 7);
     u[o] = from_f32<half_t>(v * scale);
   }
+  // the 8 columns i .. i + 7 of one group (i a multiple of 8): one 16-byte store
+  __device__ void store8(int64_t b, int64_t i, const float (&v)[8]) const {
+    const uint32_t g = uint32_t((off + i) >> 3);
+    const uint32_t q = (g >> 2) & 3u, ks = ((g >> 4) << 2) | (g & 3u);
+    const int64_t o = ((((b >> 4) * KS + ks) * 4 + q) * 16 + (b & 15)) * 8;
+    uint32_t h[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) h[k] = __builtin_bit_cast(uint16_t, from_f32<half_t>(v[k] * scale));
+    uint4 w;
+    w.x = h[0] | (h[1] << 16);
+    w.y = h[2] | (h[3] << 16);
+    w.z = h[4] | (h[5] << 16);
+    w.w = h[6] | (h[7] << 16);
+    *reinterpret_cast<uint4*>(u + o) = w;
+  }
+};
+
+struct StoreLdsRow {  // element i of the row -> its swizzled LDS position
+  float* buf;
+  __device__ void operator()(int64_t, int64_t i, float v) const { buf[swz(int(i))] = v; }
 };
 
 struct StoreF32 {
@@ -198,6 +221,31 @@ hipError_t rht_in_x(const void* x, int64_t B, int64_t n, int64_t N, const int8_t
   return hipErrorInvalidValue;
 }
 
+// One row per workgroup (block of 2^L columns, 3 <= L <= kSingleLog2) into the
+// fragment order: the one-workgroup transform with its last pass writing back to
+// LDS, then each thread stores whole 8-column groups as single 16-byte stores.
+// The 16 rows of a 16-token block share every 256-byte span of the output, so the
+// rows go to the XCDs (workgroups are dispatched to them round-robin) in runs of
+// whole blocks, per_xcd blocks each: a span is assembled in one L2 and written back
+// whole.  Workgroups past the last row exit at once.
+template <class XT>
+__global__ __launch_bounds__(1024) void rht_in_tiled_kernel(LoadSignedX<XT> ld, StoreTiledHalf st, int L, int64_t B,
+                                                            int per_xcd) {
+  extern __shared__ float buf[];
+  const int64_t b = int64_t(blockIdx.x & 7u) * per_xcd * 16 + (blockIdx.x >> 3);
+  if (b >= B) return;
+  // the last pass reads and writes the same LDS positions in the same thread
+  fwht_row_lds(ld, StoreLdsRow{buf}, b, L, buf);
+  __syncthreads();
+  const int groups = (1 << L) >> 3;
+  for (int g = threadIdx.x; g < groups; g += blockDim.x) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = buf[swz(8 * g + j)];
+    st.store8(b, int64_t(8) * g, v);
+  }
+}
+
 // input transform into the prefill matmul's fragment order (fp16)
 template <class XT>
 hipError_t rht_in_tiled_x(const void* x, int64_t B, int64_t n, int64_t N, const int8_t* sign, half_t* u16,
@@ -205,7 +253,15 @@ hipError_t rht_in_tiled_x(const void* x, int64_t B, int64_t n, int64_t N, const 
   return for_blocks(N, [&](int64_t off, int L) {
     const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
     const LoadSignedX<XT> ld{static_cast<const XT*>(x), n, off, sign};
-    return run_block(ld, StoreTiledHalf{u16, uint32_t(N / 32), off, scale}, B, L, ws, stream);
+    const StoreTiledHalf st{u16, uint32_t(N / 32), off, scale};
+    if (L < 3 || L > kSingleLog2) return run_block(ld, st, B, L, ws, stream);
+    int threads = (1 << L) / 16;
+    if (threads < 64) threads = 64;
+    if (threads > 1024) threads = 1024;
+    const int64_t per_xcd = ((B + 15) / 16 + 7) / 8;  // 16-row blocks per XCD
+    hipLaunchKernelGGL((rht_in_tiled_kernel<XT>), dim3(unsigned(8 * per_xcd * 16)), dim3(threads), size_t(4) << L,
+                       stream, ld, st, L, B, int(per_xcd));
+    return hipGetLastError();
   });
 }
 
@@ -234,11 +290,6 @@ __device__ __forceinline__ void store8(YT* y, const float (&v)[8]) {
   w.w = h[6] | (h[7] << 16);
   *reinterpret_cast<uint4*>(y) = w;
 }
-
-struct StoreLdsRow {  // element i of the row -> its swizzled LDS position
-  float* buf;
-  __device__ void operator()(int64_t, int64_t i, float v) const { buf[swz(int(i))] = v; }
-};
 
 // The block is columns off .. off + N - 1 of rows of ldz partials (z + off and
 // sign + off are passed in) and of m outputs, mv = min(N, m - off) of them kept.
