@@ -265,12 +265,14 @@ hipError_t rht_in_tiled_x(const void* x, int64_t B, int64_t n, int64_t N, const 
   });
 }
 
-// ---- output transform of one row per workgroup, 4096 <= N <= 32768 ---------------------
+// ---- output transform, one row at a time per workgroup, 4096 <= N <= 32768 -------------
 // Thread t holds the float4s at 4 t + 4096 i (i < IT = N / 4096) of the row's split
 // sum (s = 0 .. S-1 in order, all loads of a split in flight), so bits 0-1 and the
 // bits of i (12 and up) are transformed in registers and bits 2-11 in two LDS passes
 // of 5 bits; then each thread writes 8 consecutive outputs at a time (16-byte stores
-// where y allows), sign-flipped, scaled and cast.
+// where y allows), sign-flipped, scaled and cast.  Workgroups are persistent (one per
+// CU, at most B): once a row is in LDS, the loads of the workgroup's next row are
+// issued, so they overlap the LDS passes and stores (up to 2^14-point rows).
 template <class YT>
 __device__ __forceinline__ void store8(YT* y, const float (&v)[8]);
 template <>
@@ -293,16 +295,11 @@ __device__ __forceinline__ void store8(YT* y, const float (&v)[8]) {
 
 // The block is columns off .. off + N - 1 of rows of ldz partials (z + off and
 // sign + off are passed in) and of m outputs, mv = min(N, m - off) of them kept.
-template <class YT, int IT>
-__global__ __launch_bounds__(1024) void rows_out_kernel(const float* __restrict__ z, int64_t ldz, int S, int B,
-                                                       int64_t m, int mv, const int8_t* __restrict__ sign,
-                                                       YT* __restrict__ y, float scale, int vec_y) {
-  extern __shared__ float buf[];
-  constexpr int N = 4096 * IT;
-  const int row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int c = tid * 4;
-  float4 acc[IT];
+// acc = sum over s = 0 .. S-1, in order, of the float4s at 4 t + 4096 i of row `row`
+// of split s (all loads of a group of splits in flight together)
+template <int IT>
+__device__ __forceinline__ void split_sum_row(const float* __restrict__ z, int64_t ldz, int S, int B, int row, int c,
+                                              float4 (&acc)[IT]) {
   const float* zr = z + int64_t(row) * ldz;
 #pragma unroll
   for (int i = 0; i < IT; ++i) acc[i] = *reinterpret_cast<const float4*>(zr + c + 4096 * i);
@@ -337,39 +334,63 @@ __global__ __launch_bounds__(1024) void rows_out_kernel(const float* __restrict_
       acc[i].w += v.w;
     }
   }
-  float t[4 * IT];
+}
+
+template <class YT, int IT>
+__global__ __launch_bounds__(1024) void rows_out_kernel(const float* __restrict__ z, int64_t ldz, int S, int B,
+                                                       int64_t m, int mv, const int8_t* __restrict__ sign,
+                                                       YT* __restrict__ y, float scale, int vec_y) {
+  extern __shared__ float buf[];
+  const int tid = threadIdx.x;
+  const int c = tid * 4;
+  float4 acc[IT];
+  int row = blockIdx.x;  // rows blockIdx.x, + gridDim.x, ... (the grid holds at most B workgroups)
+  split_sum_row<IT>(z, ldz, S, B, row, c, acc);
+  for (;;) {
+    float t[4 * IT];
 #pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    t[4 * i + 0] = acc[i].x;
-    t[4 * i + 1] = acc[i].y;
-    t[4 * i + 2] = acc[i].z;
-    t[4 * i + 3] = acc[i].w;
-  }
-  fwht_reg<4 * IT>(t);  // bits 0-1 and 12 + log2 i
+    for (int i = 0; i < IT; ++i) {
+      t[4 * i + 0] = acc[i].x;
+      t[4 * i + 1] = acc[i].y;
+      t[4 * i + 2] = acc[i].z;
+      t[4 * i + 3] = acc[i].w;
+    }
+    fwht_reg<4 * IT>(t);  // bits 0-1 and 12 + log2 i
 #pragma unroll
-  for (int i = 0; i < IT; ++i) {
+    for (int i = 0; i < IT; ++i) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) buf[swz(c + 4096 * i + e)] = t[4 * i + e];
-  }
-  fwht_lds_passes<StoreLdsRow, 5>(StoreLdsRow{buf}, 0, 12 + log2_exact_dev(IT), 2, buf, 12);
-  __syncthreads();
-  YT* yr = y + int64_t(row) * m;
-  if (vec_y) {
-    for (int o = tid * 8; o < mv; o += 1024 * 8) {
-      const uint2 sg = *reinterpret_cast<const uint2*>(sign + o);
-      float v[8];
+      for (int e = 0; e < 4; ++e) buf[swz(c + 4096 * i + e)] = t[4 * i + e];
+    }
+    // the next row's loads are in flight during this row's LDS passes and stores
+    // (not for 2^15-point rows, whose registers are all taken by the passes)
+    const int next = row + int(gridDim.x);
+    if constexpr (IT <= 4) {
+      if (next < B) split_sum_row<IT>(z, ldz, S, B, next, c, acc);
+    }
+    fwht_lds_passes<StoreLdsRow, 5>(StoreLdsRow{buf}, 0, 12 + log2_exact_dev(IT), 2, buf, 12);
+    __syncthreads();
+    YT* yr = y + int64_t(row) * m;
+    if (vec_y) {
+      for (int o = tid * 8; o < mv; o += 1024 * 8) {
+        const uint2 sg = *reinterpret_cast<const uint2*>(sign + o);
+        float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t neg = ((e < 4 ? sg.x : sg.y) >> (8 * (e & 3) + 7)) & 1u;
-        v[e] = __uint_as_float(__float_as_uint(buf[swz(o + e)] * scale) ^ (neg << 31));
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t neg = ((e < 4 ? sg.x : sg.y) >> (8 * (e & 3) + 7)) & 1u;
+          v[e] = __uint_as_float(__float_as_uint(buf[swz(o + e)] * scale) ^ (neg << 31));
+        }
+        store8<YT>(yr + o, v);
       }
-      store8<YT>(yr + o, v);
+    } else {
+      for (int o = tid; o < mv; o += 1024) {
+        const uint32_t neg = sign[o] < 0 ? 0x80000000u : 0u;
+        yr[o] = from_f32<YT>(__uint_as_float(__float_as_uint(buf[swz(o)] * scale) ^ neg));
+      }
     }
-  } else {
-    for (int o = tid; o < mv; o += 1024) {
-      const uint32_t neg = sign[o] < 0 ? 0x80000000u : 0u;
-      yr[o] = from_f32<YT>(__uint_as_float(__float_as_uint(buf[swz(o)] * scale) ^ neg));
-    }
+    if (next >= B) break;
+    row = next;
+    __syncthreads();  // every thread's reads of buf are done before the next row's writes
+    if constexpr (IT > 4) split_sum_row<IT>(z, ldz, S, B, row, c, acc);
   }
 }
 
@@ -386,7 +407,9 @@ hipError_t rht_out_block(const float* z, int64_t S, int64_t B, int64_t m, int64_
                       mv % 8 == 0 && (reinterpret_cast<uintptr_t>(sg) % 8 == 0);
     const float* zb = z + off;
     const size_t shmem = size_t(4) << L;
-    const dim3 grid{unsigned(B)}, block{1024};
+    // resident workgroups: one per CU (16 waves holding over 64 registers each)
+    const int64_t wgs = int64_t(device_cus());
+    const dim3 grid{unsigned(B < wgs ? B : wgs)}, block{1024};
     const int S_ = int(S), B_ = int(B), mv_ = int(mv);
     switch (L) {
       case 12: hipLaunchKernelGGL((rows_out_kernel<YT, 1>), grid, block, shmem, stream, zb, ldz, S_, B_, m, mv_, sg, yp, scale, vec_y); break;
