@@ -61,6 +61,14 @@ def test_output_rht(m, m_pad, B, S, ydt):
     assert err <= REL[ydt], err
 
 
+@pytest.mark.parametrize("m,m_pad,B,S", [(4000, 4096, 600, 3), (11008, 16384, 300, 2), (32768, 32768, 260, 1)])
+@pytest.mark.parametrize("ydt", ["f32", "bf16"])
+def test_output_rht_more_rows_than_workgroups(m, m_pad, B, S, ydt):
+    # more rows than one workgroup per CU: each workgroup takes several rows in turn,
+    # loading the next row's split sum while it transforms the current one
+    test_output_rht(m, m_pad, B, S, ydt)
+
+
 def test_output_split_order_is_fixed():
     # the same partials give bit-identical outputs on repeated calls
     dev = "cuda:0"
