@@ -1,5 +1,6 @@
 // C ABI entry points: argument validation, workspace layout and dispatch to
 // the gfx950 kernels.  Nothing here allocates, frees or synchronizes.
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 
@@ -7,16 +8,18 @@
 
 using namespace glq;
 
+// A per-device cache; threads that race on a device's first call each query the
+// attribute and store the same value (relaxed atomics: no data race).
 int glq::device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cus[dev] = v;
+    cus[dev].store(v, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return v;
 }
 
 namespace {
@@ -115,6 +118,17 @@ Passes split_passes(const glq_layer& L) {
   return P;
 }
 
+// fp16 prefill operands of the linear: fragment order (with the row exponents as
+// its trailer) for the LDS-codebook matmuls, else row order followed by them
+bool prefill_tiled(const glq_layer& L) { return gemm_shared_supported(L) || gemm_lds_supported(L); }
+size_t prefill_u_region(const glq_layer& L, int64_t B) {
+  return prefill_tiled(L) ? prefill_u_total_bytes(B, L.n_pad)
+                          : align256(size_t(B) * size_t(L.n_pad) * 2) + align256(size_t(B) * 4);
+}
+size_t prefill_rexp_off(const glq_layer& L, int64_t B) {
+  return prefill_tiled(L) ? prefill_rexp_offset(B, L.n_pad) : align256(size_t(B) * size_t(L.n_pad) * 2);
+}
+
 // Linear workspace: the buffers of the B = 1 two-launch path or of the staged path.
 struct LinearWs {
   size_t u_off, uq_off, rin_off, z_off, rout_off, total;
@@ -152,9 +166,7 @@ LinearWs linear_ws(const glq_layer& L, int64_t B) {
     return w;
   }
   w.u_off = off;
-  off += align256(!w.prefill ? size_t(B) * size_t(L.n_pad) * 4
-                             : gemm_shared_supported(L) || gemm_lds_supported(L) ? tiled_u_bytes(B, L.n_pad)
-                                                                                : size_t(B) * size_t(L.n_pad) * 2);
+  off += !w.prefill ? align256(size_t(B) * size_t(L.n_pad) * 4) : prefill_u_region(L, B);
   w.uq_off = off;
   if (w.lds) off += align256(uq_bytes(B, L.n_pad));
   w.rin_off = off;
@@ -182,20 +194,23 @@ hipError_t decode_matmul(const glq_layer& L, const float* u, int64_t B, void* uq
 }
 
 // prefill matmul of every pass.  u16 in fragment order: the shared-tile kernel
-// (slot codes), else the per-wave kernel; u16 in row order: launch_gemm.
-hipError_t prefill_pass(const glq_layer& L, const half_t* u16, int64_t M, bool tiled, float* z, hipStream_t stream,
-                        bool acc) {
-  if (!tiled) return launch_gemm(L, u16, M, z, stream, acc);
-  if (gemm_shared_supported(L)) return launch_gemm_shared(L, u16, M, z, stream, acc);
-  return launch_gemm_lds(L, u16, M, true, z, stream, acc);
+// (slot codes), else the per-wave kernel; u16 in row order: launch_gemm.  rexp:
+// the rows' power-of-two exponents (NULL: none).
+hipError_t prefill_pass(const glq_layer& L, const half_t* u16, const int32_t* rexp, int64_t M, bool tiled, float* z,
+                        hipStream_t stream, bool acc) {
+  if (!tiled) return launch_gemm(L, u16, rexp, M, z, stream, acc);
+  if (gemm_shared_supported(L)) return launch_gemm_shared(L, u16, rexp, M, z, stream, acc);
+  return launch_gemm_lds(L, u16, rexp, M, true, z, stream, acc);
 }
 
-hipError_t prefill_matmul(const glq_layer& L, const half_t* u16, int64_t M, bool tiled, float* z, hipStream_t stream) {
+hipError_t prefill_matmul(const glq_layer& L, const half_t* u16, const int32_t* rexp, int64_t M, bool tiled, float* z,
+                          hipStream_t stream) {
   const Passes P = split_passes(L);
-  hipError_t e = prefill_pass(P.a, u16, M, tiled, z, stream, false);
+  hipError_t e = prefill_pass(P.a, u16, rexp, M, tiled, z, stream, false);
   if (e != hipSuccess || !P.two) return e;
-  return prefill_pass(P.b, u16, M, tiled, z, stream, true);
+  return prefill_pass(P.b, u16, rexp, M, tiled, z, stream, true);
 }
+
 
 template <class T>
 T* at(void* base, size_t off) {
@@ -309,13 +324,18 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
   if (need > 0 && (!workspace || workspace_bytes < need)) return GLQ_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 256)) return GLQ_ERR_ALIGN;
   if (B > kDecodeMaxB)
-    return from_hip(prefill_matmul(*layer, static_cast<const half_t*>(u), B, false, z_parts, stream));
+    return from_hip(prefill_matmul(*layer, static_cast<const half_t*>(u), nullptr, B, false, z_parts, stream));
   return from_hip(decode_matmul(*layer, static_cast<const float*>(u), B, workspace, z_parts, stream));
 }
 
 size_t glq_prefill_u_bytes(int64_t B, int64_t n_pad) {
   if (B < 1 || !valid_pad(n_pad) || n_pad % 128 != 0) return 0;
-  return tiled_u_bytes(B, n_pad);
+  return prefill_u_total_bytes(B, n_pad);
+}
+
+size_t glq_prefill_row_exp_offset(int64_t B, int64_t n_pad) {
+  if (B < 1 || !valid_pad(n_pad) || n_pad % 128 != 0) return 0;
+  return prefill_rexp_offset(B, n_pad);
 }
 
 int glq_e8_matmul_prefill_supported(const glq_layer* layer) {
@@ -334,7 +354,10 @@ glq_status glq_input_rht_prefill(const void* x, glq_dtype x_dt, int64_t B, int64
   const size_t need = glq_input_rht_workspace_bytes(B, n_pad, GLQ_F16);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GLQ_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 256)) return GLQ_ERR_ALIGN;
-  return from_hip(launch_rht_in_tiled(x, x_dt, B, n, n_pad, sign_in, static_cast<half_t*>(u16),
+  int32_t* rexp = at<int32_t>(u16, prefill_rexp_offset(B, n_pad));
+  hipError_t e = launch_row_exp(x, x_dt, B, n, rexp, stream);
+  if (e != hipSuccess) return GLQ_ERR_HIP;
+  return from_hip(launch_rht_in_tiled(x, x_dt, B, n, n_pad, sign_in, rexp, static_cast<half_t*>(u16),
                                       static_cast<float*>(workspace), stream));
 }
 
@@ -345,7 +368,9 @@ glq_status glq_e8_matmul_prefill(const glq_layer* layer, const void* u16, int64_
   if (B < 1 || B > int64_t(1) << 31 || !(gemm_shared_supported(*layer) || gemm_lds_supported(*layer)))
     return GLQ_ERR_SHAPE;
   if (!aligned(u16, 16)) return GLQ_ERR_ALIGN;
-  return from_hip(prefill_matmul(*layer, static_cast<const half_t*>(u16), B, true, z, stream));
+  const int32_t* rexp =
+      reinterpret_cast<const int32_t*>(static_cast<const char*>(u16) + prefill_rexp_offset(B, layer->n_pad));
+  return from_hip(prefill_matmul(*layer, static_cast<const half_t*>(u16), rexp, B, true, z, stream));
 }
 
 size_t glq_e8rht_linear_workspace_bytes(const glq_layer* layer, int64_t B) {
@@ -375,15 +400,21 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
     e = decode_matmul(L, u, B, at<char>(workspace, w.uq_off), z, stream);
     if (e != hipSuccess) return GLQ_ERR_HIP;
   } else {
+    // fp16 operands with a power-of-two scale per row (the row exponents), undone
+    // in the matmul's fp32 epilogue
     half_t* u = at<half_t>(workspace, w.u_off);
-    if (gemm_shared_supported(L) || gemm_lds_supported(L)) {  // u in the matmuls' fragment order
-      e = launch_rht_in_tiled(x, x_dt, B, L.n, L.n_pad, L.sign_in, u, at<float>(workspace, w.rin_off), stream);
+    int32_t* rexp = at<int32_t>(workspace, w.u_off + prefill_rexp_off(L, B));
+    e = launch_row_exp(x, x_dt, B, L.n, rexp, stream);
+    if (e != hipSuccess) return GLQ_ERR_HIP;
+    if (prefill_tiled(L)) {  // u in the matmuls' fragment order
+      e = launch_rht_in_tiled(x, x_dt, B, L.n, L.n_pad, L.sign_in, rexp, u, at<float>(workspace, w.rin_off), stream);
       if (e != hipSuccess) return GLQ_ERR_HIP;
-      e = prefill_matmul(L, u, B, true, z, stream);
+      e = prefill_matmul(L, u, rexp, B, true, z, stream);
     } else {
-      e = launch_rht_in(x, x_dt, B, L.n, L.n_pad, L.sign_in, u, GLQ_F16, at<float>(workspace, w.rin_off), stream);
+      e = launch_rht_in(x, x_dt, B, L.n, L.n_pad, L.sign_in, u, GLQ_F16, at<float>(workspace, w.rin_off), stream,
+                        rexp);
       if (e != hipSuccess) return GLQ_ERR_HIP;
-      e = prefill_matmul(L, u, B, false, z, stream);
+      e = prefill_matmul(L, u, rexp, B, false, z, stream);
     }
     if (e != hipSuccess) return GLQ_ERR_HIP;
   }

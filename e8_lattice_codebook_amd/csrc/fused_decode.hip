@@ -51,7 +51,13 @@ constexpr int kRowBuf = 1024;
 constexpr int kDigOff = kImgOff + 4 * 8 * 1024;
 constexpr int kGsOff = kDigOff + 8 * 64 * 4;
 constexpr int kScOff = kGsOff + 2 * 64 * 4;
-static_assert(kScOff + 64 <= kLdsDwords - kChunkDwords, "digit region overlaps the chunk");
+// per scale block: the binary exponent of its max (int32 [64 lanes]); then the
+// workgroup's largest such exponent (one int32, LDS max)
+constexpr int kFeOff = kScOff + 64;
+constexpr int kExpOff = kFeOff + 64;
+static_assert(kExpOff + 1 <= kLdsDwords - kChunkDwords, "digit region overlaps the chunk");
+// the workgroup exponent before any block has reported one (all-zero chunks)
+constexpr int kNoExp = -1024;
 
 struct FusedArgs {
   const void* x;
@@ -339,6 +345,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) chunk[swz(c4 + e)] = t[e];
   }
+  if (tid == 0) lds[kExpOff] = uint32_t(kNoExp);  // published by the barrier below
   fwht_lds_passes(StoreLds{chunk}, 0, a.lk, 8, chunk);
   __syncthreads();
   image_store<0, 8, false, R8>(img, lds, tid);
@@ -348,26 +355,42 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   // a lane's 64 columns (one scale block) are one DPP row.  U = rint(u kUqMax / max)
   // has the balanced base-16 digits d_p = nibble p of (U + 0x8888) minus 8, whose
   // 4-bit two's complement is nibble p of W = (U + 0x8888) ^ 0x8888.
+  //
+  // The block is normalized by a power of two first: with max = f 2^fe, f in
+  // [1/2, 1), U = rint(v 2^-fe * kUqMax / f), the same U as rint(v kUqMax / max)
+  // wherever that is finite, but never inf for a tiny max.  The block's scale
+  // f / (sqrt(L) kUqMax) is kept relative to the workgroup's largest exponent E
+  // (2^(fe - E) of it), and the row partials are multiplied by 2^E once, so no
+  // scale leaves the normal range however small the chunk is.  A non-finite value
+  // makes its block's scale NaN (poison = sum of v - v is 0 or NaN), and every
+  // row partial with it.
   if (tid < 16 * LPR) {
     const int g = tid >> 1, h = tid & 1;
     const int l = g >> 3, q = g & 7;
     float v[4];
-    float mx = 0.0f;
+    float mx = 0.0f, poison = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[e] = chunk[swz(4 * tid + e)];
       mx = fmaxf(mx, fabsf(v[e]));
+      poison += v[e] - v[e];
     }
     mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x128, 0xF, 0xF, false)));
     mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x124, 0xF, 0xF, false)));
     mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x122, 0xF, 0xF, false)));
     mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x121, 0xF, 0xF, false)));
-    const float inv = mx > 0.0f ? float(kUqMax) / mx : 0.0f;
+    poison += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(poison), 0x128, 0xF, 0xF, false));
+    poison += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(poison), 0x124, 0xF, 0xF, false));
+    poison += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(poison), 0x122, 0xF, 0xF, false));
+    poison += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(poison), 0x121, 0xF, 0xF, false));
+    const bool live = mx > 0.0f && poison == 0.0f;  // a finite block with a nonzero value
+    const int fe = live ? __builtin_amdgcn_frexp_expf(mx) : 0;
+    const float inv = live ? float(kUqMax) / __builtin_amdgcn_frexp_mantf(mx) : 0.0f;
     uint32_t w[4];
     int32_t gsum = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      int U = int(rintf(v[e] * inv));
+      int U = int(rintf(__builtin_amdgcn_ldexpf(v[e], -fe) * inv));
       U = U > kUqMax ? kUqMax : (U < -kUqMax ? -kUqMax : U);
       gsum += U;
       w[e] = uint32_t(U + 0x8888) ^ 0x8888u;
@@ -390,7 +413,11 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
       pv.w = pl[3];
       *reinterpret_cast<img_x4*>(lds + kDigOff + 4 * (q * LPR + l)) = pv;
       lds[kGsOff + 4 * ((q >> 2) * LPR + l) + (q & 3)] = uint32_t(-gsum);  // negated: added on complemented reads
-      if (q == 0) lds[kScOff + l] = __float_as_uint(mx * a.sc_tab[lb]);
+      if (q == 0) {
+        lds[kScOff + l] = __float_as_uint((live ? __builtin_amdgcn_frexp_mantf(mx) : 0.0f) * a.sc_tab[lb] + poison);
+        lds[kFeOff + l] = uint32_t(fe);
+        if (live) atomicMax(reinterpret_cast<int*>(lds + kExpOff), fe);
+      }
     }
   }
   __syncthreads();
@@ -413,7 +440,10 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
     gs[0][4 * qq + 2] = int32_t(g.z);
     gs[0][4 * qq + 3] = int32_t(g.w);
   }
-  sc[0] = __uint_as_float(lds[kScOff + lane_in_row]);
+  // the chunk exponent E (wave-uniform) and the lane's scale relative to 2^E
+  const int chunk_exp = __builtin_amdgcn_readfirstlane(int(lds[kExpOff]));
+  sc[0] = __builtin_amdgcn_ldexpf(__uint_as_float(lds[kScOff + lane_in_row]),
+                                  int(lds[kFeOff + lane_in_row]) - chunk_exp);
   __syncthreads();  // every lane has its digits before image parts 8-9 overwrite them
 
   // ---- step 3: the rest of the image, then the rows
@@ -441,7 +471,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
     } else {
       v = lane_reduce(v, lpr);
     }
-    if (o < a.m_pad && lane_in_row == LPR - 1) rowbuf[swz(o - wg * (a.rs_per_wg * RPS))] = v * a.out_scale;
+    if (o < a.m_pad && lane_in_row == LPR - 1)
+      rowbuf[swz(o - wg * (a.rs_per_wg * RPS))] = __builtin_amdgcn_ldexpf(v * a.out_scale, chunk_exp);
   };
   auto load_row = [&](int r, RowIdx<GL, X16>& ix) {
     if (FULL)

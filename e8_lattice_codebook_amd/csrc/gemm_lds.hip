@@ -57,6 +57,7 @@ struct GemmArgs {
   const uint32_t* pack0_hdr;
   const uint32_t* img0;       // primary LDS image
   const int8_t* res_i8;       // 8-bit residual: int8 table [256][8] = 2c
+  const int32_t* rexp;        // the rows' power-of-two exponents (NULL: none)
   float* z;                   // [M][m_pad] fp32
   int64_t M;
   int n_pad, m_pad, G;
@@ -253,10 +254,13 @@ __global__ __launch_bounds__(kPThreads, 1) void gemm_lds_kernel(GemmArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int64_t t = t0 + mi * 16 + q * 4 + i;
         if (t < a.M) {
+          const int32_t e = a.rexp ? a.rexp[t] : 0;
           float* zr = a.z + t * a.m_pad + o_w + r16;
 #pragma unroll
-          for (int ni = 0; ni < kNB; ++ni)
-            zr[16 * ni] = a.accumulate ? zr[16 * ni] + acc[mi][ni][i] * a.scale : acc[mi][ni][i] * a.scale;
+          for (int ni = 0; ni < kNB; ++ni) {
+            const float v = row_scaled(acc[mi][ni][i] * a.scale, e);
+            zr[16 * ni] = a.accumulate ? zr[16 * ni] + v : v;
+          }
         }
       }
     }
@@ -274,10 +278,11 @@ bool gemm_lds_supported(const glq_layer& L) {
          (L.resid_bits != 16 || L.cb2_pack == L.cb_pack);
 }
 
-hipError_t launch_gemm_lds(const glq_layer& L, const half_t* u16, int64_t M, bool tiled, float* z,
-                           hipStream_t stream, bool accumulate) {
+hipError_t launch_gemm_lds(const glq_layer& L, const half_t* u16, const int32_t* rexp, int64_t M, bool tiled,
+                           float* z, hipStream_t stream, bool accumulate) {
   GemmArgs a;
   a.u = u16;
+  a.rexp = rexp;
   a.idx0 = L.idx0;
   a.idx1 = L.idx1;
   const char* p0 = static_cast<const char*>(L.cb_pack);

@@ -55,6 +55,7 @@ struct SharedArgs {
   const uint32_t* pack0_hdr;
   const uint32_t* img0;       // slot image
   const uint32_t* res_slots;  // 8-bit residual: the 256 slot words of its pack
+  const int32_t* rexp;        // the rows' power-of-two exponents (NULL: none)
   float* z;                   // [M][m_pad] fp32
   int64_t M;
   int m_pad, G, KS;
@@ -258,17 +259,20 @@ __global__ __launch_bounds__(kSThreads, 1) void gemm_shared_kernel(SharedArgs a)
       load_idx(b + 2, i0n, i1bn, i1wn);
     }
 
-    // ---- z = acc * s / 2.  D of a 16x16 block: lane l holds token l % 16 and
-    // outputs 4 (l / 16) .. + 3 of the row block
+    // ---- z = acc * s / 2 * 2^rexp[t].  D of a 16x16 block: lane l holds token
+    // l % 16 and outputs 4 (l / 16) .. + 3 of the row block
 #pragma unroll
     for (int j = 0; j < kSTB; ++j) {
       const int64_t t = (tb0 + j) * 16 + (lane & 15);
       if (t < a.M) {
+        const int32_t e = a.rexp ? a.rexp[t] : 0;
         float* zr = a.z + t * a.m_pad + o0 + 4 * (lane >> 4);
 #pragma unroll
         for (int rb = 0; rb < kSRB; ++rb) {
           floatx4* p = reinterpret_cast<floatx4*>(zr + 16 * rb);
-          const floatx4 v = acc[rb][j] * a.scale;
+          floatx4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = row_scaled(acc[rb][j][i] * a.scale, e);
           *p = a.accumulate ? *p + v : v;
         }
       }
@@ -288,10 +292,11 @@ bool gemm_shared_supported(const glq_layer& L) {
 
 size_t tiled_u_bytes(int64_t M, int64_t n_pad) { return size_t((M + 15) / 16) * 16 * size_t(n_pad) * 2; }
 
-hipError_t launch_gemm_shared(const glq_layer& L, const half_t* u16, int64_t M, float* z, hipStream_t stream,
-                              bool accumulate) {
+hipError_t launch_gemm_shared(const glq_layer& L, const half_t* u16, const int32_t* rexp, int64_t M, float* z,
+                              hipStream_t stream, bool accumulate) {
   SharedArgs a;
   a.u = u16;
+  a.rexp = rexp;
   a.idx0 = L.idx0;
   a.idx1 = L.idx1;
   const char* p0 = static_cast<const char*>(L.cb_pack);

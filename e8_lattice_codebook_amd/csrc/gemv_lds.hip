@@ -31,6 +31,7 @@ namespace glq {
 namespace {
 
 constexpr int kThreads = 1024;
+constexpr int kNoExp = -1024;  // the common exponent of all-zero blocks
 
 // quantized u: digits [B][G][4] u32 | gsum [B][G] i32 | scale [B][nblk] f32
 struct UqLayout {
@@ -60,19 +61,34 @@ __global__ __launch_bounds__(256) void quant_u_kernel(const float* __restrict__ 
   const float4 a = reinterpret_cast<const float4*>(u)[tt * 2];
   const float4 b = reinterpret_cast<const float4*>(u)[tt * 2 + 1];
   float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  float mx = 0.0f;
+  float mx = 0.0f, poison = 0.0f;  // poison: 0, or NaN when a value is not finite
 #pragma unroll
-  for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[j]));
+  for (int j = 0; j < 8; ++j) {
+    mx = fmaxf(mx, fabsf(v[j]));
+    poison += v[j] - v[j];
+  }
   // a block is 2^bg_log2 consecutive groups = consecutive threads
-  for (int off = 1; off < (1 << bg_log2); off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  const float inv = mx > 0.0f ? float(kUqMax) / mx : 0.0f;
+  for (int off = 1; off < (1 << bg_log2); off <<= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    poison += __shfl_xor(poison, off, 64);
+  }
+  // normalized by a power of two (max = f 2^fe, f in [1/2, 1)): U = rint(v 2^-fe
+  // kUqMax / f) never overflows for a tiny max
+  const bool nz = mx > 0.0f && poison == 0.0f;
+  const int fe = nz ? __builtin_amdgcn_frexp_expf(mx) : 0;
+  const float inv = nz ? float(kUqMax) / __builtin_amdgcn_frexp_mantf(mx) : 0.0f;
+  float vn[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) vn[j] = __builtin_amdgcn_ldexpf(v[j], -fe);
   uint32_t planes[4];
   int32_t s;
-  quantize_group(v, inv, planes, s);
+  quantize_group(vn, inv, planes, s);
   if (!live) return;
   reinterpret_cast<uint4*>(dig)[t] = make_uint4(planes[0], planes[1], planes[2], planes[3]);
   gsum[t] = s;
-  if ((t & ((int64_t(1) << bg_log2) - 1)) == 0) scale[t >> bg_log2] = mx / float(kUqMax);
+  // the block's max itself (NaN for a non-finite block): the matmul forms the scale
+  // max / kUqMax relative to a common power of two, so it stays in the normal range
+  if ((t & ((int64_t(1) << bg_log2) - 1)) == 0) scale[t >> bg_log2] = (nz ? mx : 0.0f) + poison;
 }
 
 template <int NB, int GL, int RESID, bool FULL, bool CODES>
@@ -103,6 +119,7 @@ __global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
   uint32_t dig[NB][GL][4];
   int32_t gs[NB][GL];
   float sc[NB];
+  int wexp[NB];
 
   // (split, row-step) of the wave's current unit, advanced without divisions
   int split = u_begin / row_steps;
@@ -151,6 +168,17 @@ __global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
         }
         sc[b] = b < B ? uq_scale[bb * nblk + (g0 >> bg_log2)] : 0.0f;
       }
+      // the block maxima relative to the wave's largest binary exponent E[b]: the
+      // lanes' scales max 2^-E / kUqMax stay normal, and 2^E is applied to the
+      // reduced row value
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        int e = sc[b] > 0.0f && sc[b] <= 3.4028235e38f ? __builtin_amdgcn_frexp_expf(sc[b]) : kNoExp;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) e = max(e, __shfl_xor(e, off, 64));
+        wexp[b] = e;
+        sc[b] = __builtin_amdgcn_ldexpf(sc[b], -e) / float(kUqMax);
+      }
     }
 
     if (unit + 1 < u_end) {
@@ -177,7 +205,8 @@ __global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
       }
       if (valid && lane_in_row == LPR - 1 && b < B) {
         float* zo = z_parts + (split * B + b) * m_pad + o;
-        *zo = accumulate ? *zo + v * out_scale : v * out_scale;
+        const float zv = __builtin_amdgcn_ldexpf(v * out_scale, wexp[b]);
+        *zo = accumulate ? *zo + zv : zv;
       }
     }
   }

@@ -101,8 +101,9 @@ glq_status build_pack(const uint16_t* cb_host, int64_t entries, void* pack_host,
 // Transforms of length N (block-diagonal when N is not a power of two).
 // Input transform; ws: fp32 [B][N] scratch, used only when a block is longer than
 // 2^kSingleLog2 and u is not fp32 of one block.
+// rexp (may be NULL): row b of x is scaled by 2^-rexp[b] as it is loaded
 hipError_t launch_rht_in(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t N, const int8_t* sign,
-                         void* u, glq_dtype u_dt, float* ws, hipStream_t stream);
+                         void* u, glq_dtype u_dt, float* ws, hipStream_t stream, const int32_t* rexp = nullptr);
 // Output transform of sum_s z[s] (rows of N); ws: fp32 [B][N] scratch used only
 // when a block is longer than 2^kSingleLog2.
 hipError_t launch_rht_out(const float* z, int64_t S, int64_t B, int64_t m, int64_t N, const int8_t* sign,
@@ -151,15 +152,34 @@ int device_cus();
 // int8 tables.
 bool gemm_shared_supported(const glq_layer& layer);
 size_t tiled_u_bytes(int64_t M, int64_t n_pad);
-hipError_t launch_gemm_shared(const glq_layer& layer, const half_t* u16, int64_t M, float* z, hipStream_t stream,
-                              bool accumulate = false);
+// fp16 prefill operands carry a power-of-two scale per row: u[b] = 2^rexp[b] * (the
+// fp16 values stored), rexp[b] chosen from max |x[b]| so that no stored value
+// exceeds 2^14 (see launch_row_exp); the matmuls apply 2^rexp[b] to row b of z in
+// fp32.  kRowExpNaN marks a row holding a value that is not finite: its z row is NaN.
+constexpr int32_t kRowExpNaN = 0x7FFFFFFF;
+// Fragment-order u16 followed (at a 256-byte boundary) by int32 rexp [ceil(M/16) 16].
+inline size_t prefill_rexp_offset(int64_t M, int64_t n_pad) { return align256(tiled_u_bytes(M, n_pad)); }
+inline size_t prefill_u_total_bytes(int64_t M, int64_t n_pad) {
+  return prefill_rexp_offset(M, n_pad) + align256(size_t((M + 15) / 16) * 16 * 4);
+}
+// rexp[b] = e with max |x[b]| < 2^(e + 14) / sqrt(n) (so |u| <= ||x[b]|| < 2^(e + 14)
+// after the orthonormal transform); 0 for a zero row, kRowExpNaN for a non-finite one
+hipError_t launch_row_exp(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int32_t* rexp, hipStream_t stream);
+// z of a row with exponent e: v 2^e (NaN for a non-finite row)
+__device__ __forceinline__ float row_scaled(float v, int32_t e) {
+  return e == kRowExpNaN ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(v, e);
+}
+hipError_t launch_gemm_shared(const glq_layer& layer, const half_t* u16, const int32_t* rexp, int64_t M, float* z,
+                              hipStream_t stream, bool accumulate = false);
 bool gemm_lds_supported(const glq_layer& layer);
-hipError_t launch_gemm_lds(const glq_layer& layer, const half_t* u16, int64_t M, bool tiled, float* z,
-                           hipStream_t stream, bool accumulate = false);
+hipError_t launch_gemm_lds(const glq_layer& layer, const half_t* u16, const int32_t* rexp, int64_t M, bool tiled,
+                           float* z, hipStream_t stream, bool accumulate = false);
+// rexp: the rows' exponents (launch_row_exp), applied to x as it is loaded
 hipError_t launch_rht_in_tiled(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t N, const int8_t* sign,
-                               half_t* u16, float* ws, hipStream_t stream);
-hipError_t launch_gemm(const glq_layer& layer, const half_t* u16, int64_t M, float* z, hipStream_t stream,
-                       bool accumulate = false);
+                               const int32_t* rexp, half_t* u16, float* ws, hipStream_t stream);
+// rexp may be NULL (no row scales)
+hipError_t launch_gemm(const glq_layer& layer, const half_t* u16, const int32_t* rexp, int64_t M, float* z,
+                       hipStream_t stream, bool accumulate = false);
 
 // Decode attention over an E8-compressed paged K/V cache: chunks of T tokens per
 // (sequence, KV head) in a persistent kernel, then the chunks merged in order.

@@ -22,6 +22,8 @@
 // pass of length N1 <= 64 per c held in registers.
 #include <math.h>
 
+#include <atomic>
+
 #include "fwht_lds.h"
 
 namespace glq {
@@ -39,6 +41,18 @@ struct LoadSignedX {  // x [B][n] -> sign[c] * x[b][c] at c = off + i, zero beyo
     // row, n >= 1), so that a thread's loads are in flight together; zero beyond n
     const float v = to_f32<XT>(x[b * n + (c < n ? c : n - 1)]) * float(sign[c]);
     return c < n ? v : 0.0f;
+  }
+};
+
+// LoadSignedX with row b scaled by 2^-rexp[b] (exact: a power of two), the fp16
+// prefill operands' row scales; a non-finite row (kRowExpNaN) is not scaled
+template <class XT>
+struct LoadSignedXRow {
+  LoadSignedX<XT> in;
+  const int32_t* rexp;
+  __device__ float operator()(int64_t b, int64_t i) const {
+    const int32_t e = rexp[b];
+    return __builtin_amdgcn_ldexpf(in(b, i), e == kRowExpNaN ? 0 : -e);
   }
 };
 
@@ -200,25 +214,60 @@ hipError_t for_blocks(int64_t N, F f) {
 
 template <class XT, class UT>
 hipError_t rht_in_typed(const void* x, int64_t B, int64_t n, int64_t N, const int8_t* sign, void* u, float* ws,
-                        hipStream_t stream) {
+                        hipStream_t stream, const int32_t* rexp) {
   return for_blocks(N, [&](int64_t off, int L) {
     const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
     const LoadSignedX<XT> ld{static_cast<const XT*>(x), n, off, sign};
     // an fp32 u is its own two-pass buffer when it is one block
     float* mid = (sizeof(UT) == 4 && off == 0 && N == (int64_t(1) << L)) ? reinterpret_cast<float*>(u) : ws;
-    return run_block(ld, StoreScaled<UT>{static_cast<UT*>(u), N, off, scale}, B, L, mid, stream);
+    const StoreScaled<UT> st{static_cast<UT*>(u), N, off, scale};
+    if (rexp) return run_block(LoadSignedXRow<XT>{ld, rexp}, st, B, L, mid, stream);
+    return run_block(ld, st, B, L, mid, stream);
   });
 }
 
 template <class XT>
 hipError_t rht_in_x(const void* x, int64_t B, int64_t n, int64_t N, const int8_t* sign, void* u, glq_dtype u_dt,
-                    float* ws, hipStream_t stream) {
+                    float* ws, hipStream_t stream, const int32_t* rexp) {
   switch (u_dt) {
-    case GLQ_F32: return rht_in_typed<XT, float>(x, B, n, N, sign, u, ws, stream);
-    case GLQ_F16: return rht_in_typed<XT, half_t>(x, B, n, N, sign, u, ws, stream);
-    case GLQ_BF16: return rht_in_typed<XT, bf16_t>(x, B, n, N, sign, u, ws, stream);
+    case GLQ_F32: return rht_in_typed<XT, float>(x, B, n, N, sign, u, ws, stream, rexp);
+    case GLQ_F16: return rht_in_typed<XT, half_t>(x, B, n, N, sign, u, ws, stream, rexp);
+    case GLQ_BF16: return rht_in_typed<XT, bf16_t>(x, B, n, N, sign, u, ws, stream, rexp);
   }
   return hipErrorInvalidValue;
+}
+
+// ---- the rows' power-of-two exponents of the fp16 prefill operands ---------------------
+// One workgroup per row: m = max |x[b]| (fmax ignores NaN; poison, the sum of v - v,
+// is 0 or NaN and catches NaN and inf), then rexp[b] = frexp exponent of m + add,
+// add = ceil(log2 sqrt(n)) - 14, so that |u| <= ||x[b]|| <= sqrt(n) m < 2^(rexp + 14).
+template <class XT>
+__global__ __launch_bounds__(256) void row_exp_kernel(const XT* __restrict__ x, int64_t n, int add,
+                                                      int32_t* __restrict__ rexp) {
+  __shared__ float red[2][4];
+  const int64_t b = blockIdx.x;
+  const XT* xr = x + b * n;
+  float mx = 0.0f, poison = 0.0f;
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    const float v = to_f32<XT>(xr[i]);
+    mx = fmaxf(mx, fabsf(v));
+    poison += v - v;
+  }
+  for (int off = 1; off < 64; off <<= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    poison += __shfl_xor(poison, off, 64);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][wave] = mx;
+    red[1][wave] = poison;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    poison = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    rexp[b] = poison != 0.0f ? kRowExpNaN : mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) + add : 0;
+  }
 }
 
 // One row per workgroup (block of 2^L columns, 3 <= L <= kSingleLog2) into the
@@ -229,8 +278,8 @@ hipError_t rht_in_x(const void* x, int64_t B, int64_t n, int64_t N, const int8_t
 // whole blocks, per_xcd blocks each: a span is assembled in one L2 and written back
 // whole.  Workgroups past the last row exit at once.
 template <class XT>
-__global__ __launch_bounds__(1024) void rht_in_tiled_kernel(LoadSignedX<XT> ld, StoreTiledHalf st, int L, int64_t B,
-                                                            int per_xcd) {
+__global__ __launch_bounds__(1024) void rht_in_tiled_kernel(LoadSignedXRow<XT> ld, StoreTiledHalf st, int L,
+                                                            int64_t B, int per_xcd) {
   extern __shared__ float buf[];
   const int64_t b = int64_t(blockIdx.x & 7u) * per_xcd * 16 + (blockIdx.x >> 3);
   if (b >= B) return;
@@ -246,13 +295,14 @@ __global__ __launch_bounds__(1024) void rht_in_tiled_kernel(LoadSignedX<XT> ld, 
   }
 }
 
-// input transform into the prefill matmul's fragment order (fp16)
+// input transform into the prefill matmul's fragment order (fp16), rows scaled by
+// 2^-rexp[b]
 template <class XT>
-hipError_t rht_in_tiled_x(const void* x, int64_t B, int64_t n, int64_t N, const int8_t* sign, half_t* u16,
-                          float* ws, hipStream_t stream) {
+hipError_t rht_in_tiled_x(const void* x, int64_t B, int64_t n, int64_t N, const int8_t* sign, const int32_t* rexp,
+                          half_t* u16, float* ws, hipStream_t stream) {
   return for_blocks(N, [&](int64_t off, int L) {
     const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
-    const LoadSignedX<XT> ld{static_cast<const XT*>(x), n, off, sign};
+    const LoadSignedXRow<XT> ld{LoadSignedX<XT>{static_cast<const XT*>(x), n, off, sign}, rexp};
     const StoreTiledHalf st{u16, uint32_t(N / 32), off, scale};
     if (L < 3 || L > kSingleLog2) return run_block(ld, st, B, L, ws, stream);
     int threads = (1 << L) / 16;
@@ -416,13 +466,17 @@ hipError_t rht_out_block(const float* z, int64_t S, int64_t B, int64_t m, int64_
       case 13: hipLaunchKernelGGL((rows_out_kernel<YT, 2>), grid, block, shmem, stream, zb, ldz, S_, B_, m, mv_, sg, yp, scale, vec_y); break;
       case 14: hipLaunchKernelGGL((rows_out_kernel<YT, 4>), grid, block, shmem, stream, zb, ldz, S_, B_, m, mv_, sg, yp, scale, vec_y); break;
       default: {
-        // 128 KiB of dynamic LDS: raise the kernel's limit once
-        static bool lds_set = false;
-        if (!lds_set) {
+        // 128 KiB of dynamic LDS: raise the kernel's limit once per device (threads
+        // racing on the first call both set it: harmless, and the flag is atomic)
+        static std::atomic<uint64_t> lds_set{0};
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+        const uint64_t bit = uint64_t(1) << (dev & 63);
+        if (!(lds_set.load(std::memory_order_relaxed) & bit)) {
           hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rows_out_kernel<YT, 8>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
           if (e != hipSuccess) return e;
-          lds_set = true;
+          lds_set.fetch_or(bit, std::memory_order_relaxed);
         }
         hipLaunchKernelGGL((rows_out_kernel<YT, 8>), grid, block, shmem, stream, zb, ldz, S_, B_, m, mv_, sg, yp,
                            scale, vec_y);
@@ -449,21 +503,35 @@ hipError_t rht_out_typed(const float* z, int64_t S, int64_t B, int64_t m, int64_
 }  // namespace
 
 hipError_t launch_rht_in(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t N, const int8_t* sign,
-                         void* u, glq_dtype u_dt, float* ws, hipStream_t stream) {
+                         void* u, glq_dtype u_dt, float* ws, hipStream_t stream, const int32_t* rexp) {
   switch (x_dt) {
-    case GLQ_F32: return rht_in_x<float>(x, B, n, N, sign, u, u_dt, ws, stream);
-    case GLQ_F16: return rht_in_x<half_t>(x, B, n, N, sign, u, u_dt, ws, stream);
-    case GLQ_BF16: return rht_in_x<bf16_t>(x, B, n, N, sign, u, u_dt, ws, stream);
+    case GLQ_F32: return rht_in_x<float>(x, B, n, N, sign, u, u_dt, ws, stream, rexp);
+    case GLQ_F16: return rht_in_x<half_t>(x, B, n, N, sign, u, u_dt, ws, stream, rexp);
+    case GLQ_BF16: return rht_in_x<bf16_t>(x, B, n, N, sign, u, u_dt, ws, stream, rexp);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_rht_in_tiled(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t N, const int8_t* sign,
-                               half_t* u16, float* ws, hipStream_t stream) {
+hipError_t launch_row_exp(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int32_t* rexp, hipStream_t stream) {
+  int c = 0;  // ceil(log2 sqrt(n))
+  while ((int64_t(1) << (2 * c)) < n) ++c;
+  const int add = c - 14;
+  const dim3 grid{unsigned(B)}, block{256};
   switch (x_dt) {
-    case GLQ_F32: return rht_in_tiled_x<float>(x, B, n, N, sign, u16, ws, stream);
-    case GLQ_F16: return rht_in_tiled_x<half_t>(x, B, n, N, sign, u16, ws, stream);
-    case GLQ_BF16: return rht_in_tiled_x<bf16_t>(x, B, n, N, sign, u16, ws, stream);
+    case GLQ_F32: hipLaunchKernelGGL(row_exp_kernel<float>, grid, block, 0, stream, static_cast<const float*>(x), n, add, rexp); break;
+    case GLQ_F16: hipLaunchKernelGGL(row_exp_kernel<half_t>, grid, block, 0, stream, static_cast<const half_t*>(x), n, add, rexp); break;
+    case GLQ_BF16: hipLaunchKernelGGL(row_exp_kernel<bf16_t>, grid, block, 0, stream, static_cast<const bf16_t*>(x), n, add, rexp); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rht_in_tiled(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t N, const int8_t* sign,
+                               const int32_t* rexp, half_t* u16, float* ws, hipStream_t stream) {
+  switch (x_dt) {
+    case GLQ_F32: return rht_in_tiled_x<float>(x, B, n, N, sign, rexp, u16, ws, stream);
+    case GLQ_F16: return rht_in_tiled_x<half_t>(x, B, n, N, sign, rexp, u16, ws, stream);
+    case GLQ_BF16: return rht_in_tiled_x<bf16_t>(x, B, n, N, sign, rexp, u16, ws, stream);
   }
   return hipErrorInvalidValue;
 }

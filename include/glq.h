@@ -25,7 +25,9 @@
  * Conventions for every entry point:
  *   - Pointers marked "device" are HIP device pointers on the current device;
  *     "host" pointers are ordinary host memory.  The caller owns every buffer;
- *     the library allocates and frees nothing and keeps no mutable state.
+ *     the library allocates and frees nothing.  Its only mutable state is a
+ *     per-device cache of the compute-unit count and of one kernel attribute,
+ *     updated atomically, so calls from several host threads are safe.
  *   - Device work is enqueued asynchronously on `stream` (0 = null stream); the
  *     library never synchronizes, so calls are safe under stream capture.
  *   - Arrays are dense and row-major.  n_pad and m_pad are powers of two in
@@ -35,6 +37,12 @@
  *     launch returns GLQ_ERR_HIP.  Faults inside kernels surface on the stream.
  *   - Results are deterministic: the same inputs give bit-identical outputs on
  *     every call (fixed-order reductions, no atomics on the data path).
+ *   - Range: the transforms run in fp32, so sqrt(n_pad) * max |x| must stay below
+ *     FLT_MAX (about 3.4e38); within it the result scales with x (y(2^k x) =
+ *     2^k y(x) while y stays in the fp32 range).  Every reduced-precision step
+ *     carries a power-of-two scale: the decode path's 16-bit fixed point per 64
+ *     columns, and the prefill path's fp16 operands per row.  A NaN or infinity in
+ *     a row of x makes that row of y NaN.
  */
 #ifndef GLQ_H
 #define GLQ_H
@@ -48,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GLQ_ABI_VERSION 3
+#define GLQ_ABI_VERSION 4
 #define GLQ_CODEBOOK_ENTRIES 65536
 #define GLQ_RESID8_ENTRIES 256
 #define GLQ_MAX_PAD (1 << 20)
@@ -320,21 +328,33 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
  * (((b / 16) KS + ks) 4 + q) 128 + (b mod 16) 8 + i mod 8;
  * a buffer holds ceil(B / 16) * 16 rows (rows past B are never read into y).
  *
- * glq_prefill_u_bytes — bytes of fragment-order u for B rows (0 for an invalid n_pad
- *   or one that is not a multiple of 128).
+ * Each row b carries a power-of-two scale: the buffer holds the fp16 values of
+ * u[b] * 2^-e[b], followed, at byte offset glq_prefill_row_exp_offset(B, n_pad), by
+ * int32 e[ceil(B / 16) * 16].  e[b] is chosen from the input row so that no stored
+ * value exceeds 2^14 in magnitude: e = frexp exponent of max |x[b]| + ceil(log2
+ * sqrt(n)) - 14 (|u| <= ||x[b]||_2 <= sqrt(n) max |x[b]|), 0 for a zero row and
+ * 0x7FFFFFFF for a row holding a NaN or an infinity (its z row is then NaN).  The
+ * fp16 values keep their relative precision at any input scale, and the matmul
+ * multiplies row b of z by 2^e[b] in fp32.
+ *
+ * glq_prefill_u_bytes — bytes of fragment-order u for B rows, the row exponents
+ *   included (0 for an invalid n_pad or one that is not a multiple of 128).
+ * glq_prefill_row_exp_offset — byte offset of the row exponents in that buffer.
  * glq_e8_matmul_prefill_supported — 1 if glq_e8_matmul_prefill takes the layer:
  *   n_pad >= 256 and a multiple of 128, residual stage 0, 8 bits or 16 bits in the
  *   primary pack, and m_pad a multiple of 64 (slot codes) or of 256 (codebook
  *   indices).
- * glq_input_rht_prefill — u = H (sign_in * [x, 0]) / sqrt(n_pad) rounded to fp16,
- *   written in fragment order.
+ * glq_input_rht_prefill — u = H (sign_in * [x, 0]) / sqrt(n_pad), each row scaled
+ *   by its 2^-e[b] and rounded to fp16, written in fragment order with the row
+ *   exponents after it.
  *   x          device [B][n] in x_dt (F32, F16 or BF16)
  *   u16        device, >= glq_prefill_u_bytes(B, n_pad), 16-byte aligned
  *   workspace  device fp32 [B][n_pad] when n_pad > 16384 (else may be NULL),
  *              glq_input_rht_workspace_bytes(B, n_pad, GLQ_F16) bytes, 256-byte aligned
- * glq_e8_matmul_prefill — z [B][m_pad] fp32 = u W~^T from fragment-order u16
- *   (codewords dequantized from the LDS-resident codebook into fp16 MFMA operands,
- *   fp32 accumulation, one split: glq_output_rht takes z with S = 1).  Slot codes:
+ * glq_e8_matmul_prefill — z [B][m_pad] fp32 = u W~^T from fragment-order u16 and
+ *   its row exponents (codewords dequantized from the LDS-resident codebook into
+ *   fp16 MFMA operands, fp32 accumulation, row b times 2^e[b]; one split:
+ *   glq_output_rht takes z with S = 1).  Slot codes:
  *   per k-step a 64-row codeword tile is dequantized into LDS once and shared by
  *   four waves; codebook indices (a larger LDS image): each wave dequantizes its
  *   own fragments.
@@ -343,6 +363,7 @@ glq_status glq_e8_matmul(const glq_layer* layer, const void* u, glq_dtype u_dt, 
  * GLQ_ERR_RECIPE, GLQ_ERR_ALIGN, GLQ_ERR_WORKSPACE, GLQ_ERR_HIP.
  */
 size_t glq_prefill_u_bytes(int64_t B, int64_t n_pad);
+size_t glq_prefill_row_exp_offset(int64_t B, int64_t n_pad);
 int glq_e8_matmul_prefill_supported(const glq_layer* layer);
 glq_status glq_input_rht_prefill(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t n_pad,
                                  const int8_t* sign_in, void* u16, void* workspace, size_t workspace_bytes,
@@ -369,8 +390,12 @@ glq_status glq_e8_matmul_prefill(const glq_layer* layer, const void* u16, int64_
  * B <= 16 otherwise: decode path (transformed activations quantized to 16-bit fixed point
  * per 64 columns, exact integer dot products against codewords gathered from the
  * LDS-resident codebook, split-K partial sums reduced in a fixed order).
- * B > 16: prefill path (transformed activations rounded to fp16, codeword tiles
- * dequantized into LDS feeding fp16 MFMA with fp32 accumulation).
+ * The fixed-point step of a 64-column block is max |u| / 30583 over the block,
+ * formed as a power of two times a normal fp32 value, so tiny blocks neither
+ * overflow nor lose precision.
+ * B > 16: prefill path (transformed activations rounded to fp16 with a power-of-two
+ * scale per row, as for glq_input_rht_prefill; codeword tiles dequantized into LDS
+ * feeding fp16 MFMA with fp32 accumulation).
  * Errors: GLQ_ERR_NULL, GLQ_ERR_SHAPE, GLQ_ERR_DTYPE, GLQ_ERR_RECIPE, GLQ_ERR_ALIGN,
  * GLQ_ERR_WORKSPACE, GLQ_ERR_HIP.
  */

@@ -58,3 +58,73 @@ def fp32_to_bf16_rn(y32):
 def layer_from(workload_key, k):
     w = synth.WORKLOADS[workload_key]
     return synth.make_layer(w.layers[k], w.resid_bits, w.seed, k)
+
+
+# ---- fp16 prefill operands built on the CPU from the oracle's transform ----------------
+# The library's prefill path stores u[b] * 2^-e[b] in fp16 with
+# e[b] = (frexp exponent of max |x[b]|) + ceil(log2 sqrt(n)) - 14 (0 for a zero row,
+# 0x7FFFFFFF for a row with a NaN or an infinity), the placement of include/glq.h's
+# fragment order, and the int32 exponents after it at a 256-byte boundary.
+ROW_EXP_NAN = 0x7FFFFFFF
+
+
+def row_exponents(x64, n):
+    x64 = np.asarray(x64, dtype=np.float64)
+    c = 0
+    while (1 << (2 * c)) < n:
+        c += 1
+    finite = np.isfinite(x64).all(axis=1)
+    mx = np.where(finite, np.abs(np.where(np.isfinite(x64), x64, 0.0)).max(axis=1), 0.0)
+    fe = np.frexp(mx)[1]
+    e = np.where(mx > 0, fe + c - 14, 0).astype(np.int64)
+    return np.where(finite, e, ROW_EXP_NAN).astype(np.int32)
+
+
+def oracle_prefill_u16(x64, sign_in, n_pad):
+    """(fp16 u [B][n_pad] as the library stores it, row exponents) from the oracle's fp64 u."""
+    from oracle import hadamard
+    x64 = np.asarray(x64, dtype=np.float64)
+    e = row_exponents(x64, x64.shape[1])
+    if hadamard.is_pow2(n_pad):
+        u = hadamard.rht_in(x64, sign_in, n_pad)
+    else:  # block-diagonal over the binary expansion of n_pad, zeros past n
+        xp = np.zeros((x64.shape[0], n_pad))
+        xp[:, :x64.shape[1]] = x64
+        u = hadamard.rht_in_blocks(xp, sign_in)
+    return (u * np.ldexp(1.0, -e.astype(np.int64))[:, None]).astype(np.float16), e
+
+
+def fragment_positions(M, n_pad):
+    KS = n_pad // 32
+    b, i = np.meshgrid(np.arange(M), np.arange(n_pad), indexing="ij")
+    g = i // 8
+    ks, q = 4 * (g // 16) + g % 4, (g // 4) % 4
+    return (((b // 16) * KS + ks) * 4 + q) * 128 + (b % 16) * 8 + i % 8
+
+
+def fragment_buffer(u16, rexp, device):
+    """The fragment-order operand buffer (fp16 values, then the row exponents) of u16 [M][n_pad]."""
+    M, n_pad = u16.shape
+    Mp = (M + 15) // 16 * 16
+    r256 = lambda v: (v + 255) // 256 * 256
+    off = r256(Mp * n_pad * 2)
+    buf = np.zeros(off + r256(Mp * 4), dtype=np.uint8)
+    halves = buf[:Mp * n_pad * 2].view(np.uint16)
+    halves[fragment_positions(M, n_pad)] = np.asarray(u16, dtype=np.float16).view(np.uint16)
+    e = np.zeros(Mp, dtype=np.int32)
+    e[:M] = rexp
+    buf[off:off + Mp * 4] = e.view(np.uint8)
+    return torch.from_numpy(buf).to(device)
+
+
+def unpack_fragment_buffer(buf, M, n_pad):
+    """(fp16 u [M][n_pad], int32 row exponents [M]) read back from a fragment-order buffer."""
+    raw = buf.cpu().numpy().view(np.uint8)
+    Mp = (M + 15) // 16 * 16
+    off = (Mp * n_pad * 2 + 255) // 256 * 256
+    halves = raw[:Mp * n_pad * 2].view(np.float16)
+    return halves[fragment_positions(M, n_pad)], raw[off:off + Mp * 4].view(np.int32)[:M].copy()
+
+
+def u16_as_f64(u16, rexp):
+    return np.asarray(u16, dtype=np.float64) * np.ldexp(1.0, np.asarray(rexp, dtype=np.int64))[:, None]

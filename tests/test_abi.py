@@ -38,7 +38,7 @@ def test_header_declarations_are_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.glq_abi_version() == 3
+    assert lib.glq_abi_version() == 4
     for s in range(9):
         assert lib.glq_status_string(s)
     assert lib.glq_status_string(0) == b"ok"
@@ -82,10 +82,15 @@ def test_workspace_queries():
     assert dec >= 2 * 8192 * 4 + 2 * 32768 * 4 + 2 * 32768 * 4
     pre = lib.glq_e8rht_linear_workspace_bytes(ctypes.byref(L), 2048)
     assert pre >= 2048 * 8192 * 2 + 2 * 2048 * 32768 * 4
-    # fragment-order u: whole 16-row blocks; k-steps in blocks of 4 (n_pad a multiple of 128)
-    assert lib.glq_prefill_u_bytes(17, 2688) == 32 * 2688 * 2
-    assert lib.glq_prefill_u_bytes(33, 2688) == 48 * 2688 * 2
+    # fragment-order u: whole 16-row blocks; k-steps in blocks of 4 (n_pad a multiple of
+    # 128); then, at a 256-byte boundary, one int32 exponent per row of those blocks
+    r256 = lambda v: (v + 255) // 256 * 256
+    assert lib.glq_prefill_row_exp_offset(17, 2688) == r256(32 * 2688 * 2)
+    assert lib.glq_prefill_u_bytes(17, 2688) == r256(32 * 2688 * 2) + r256(32 * 4)
+    assert lib.glq_prefill_row_exp_offset(33, 2688) == r256(48 * 2688 * 2)
+    assert lib.glq_prefill_u_bytes(33, 2688) == r256(48 * 2688 * 2) + r256(48 * 4)
     assert lib.glq_prefill_u_bytes(17, 320) == 0
+    assert lib.glq_prefill_row_exp_offset(17, 320) == 0
     assert lib.glq_prefill_u_bytes(0, 1024) == 0
 
 

@@ -16,7 +16,7 @@ import torch
 
 import synth
 from oracle import glq as og, hadamard
-from gpu_util import TORCH_DT, rel_frob, same_products, say, to_f64, x_tensor
+from gpu_util import TORCH_DT, fragment_buffer, oracle_prefill_u16, rel_frob, same_products, say, to_f64, x_tensor
 
 pytestmark = pytest.mark.gpu
 glq = pytest.importorskip("e8_lattice_codebook_amd")
@@ -146,12 +146,12 @@ def test_prefill_fragment_order_unpadded(gpu_codebooks, M):
     ql = glq.QuantizedLayer.from_synth(layer, gpu_codebooks)
     qs = ql.to_slot_codes()
     assert glq.e8_matmul_prefill_supported(qs)
-    x = torch.randn(M, 2688, device=DEV, dtype=torch.bfloat16)
-    uf = glq.input_rht_prefill(x, 2688, ql.sign_in)
-    zf = glq.e8_matmul_prefill(qs, uf, M)
-    u16 = glq.input_rht(x, 2688, ql.sign_in, torch.float16)
-    zr = glq.e8_matmul(ql, u16)
+    x = np.random.default_rng(M).standard_normal((M, 2688))
+    u16, e = oracle_prefill_u16(x, layer.sign_in, 2688)
+    zf = glq.e8_matmul_prefill(qs, fragment_buffer(u16, e, DEV), M)
+    zr = glq.e8_matmul(ql, torch.from_numpy(u16).to(DEV))
     torch.cuda.synchronize()
-    want = og.matmul_z(to_f64(u16), layer.idx0, layer.idx1, 8, layer.wscale, layer.resid_scale)
-    assert rel_frob(to_f64(zf[0]), want) <= 1e-5
+    want = og.matmul_z(u16.astype(np.float64), layer.idx0, layer.idx1, 8, layer.wscale, layer.resid_scale)
+    sc = np.exp2(e)[:, None]
+    assert rel_frob(to_f64(zf[0]), want * sc) <= 1e-5
     assert rel_frob(to_f64(zr[0]), want) <= 1e-5

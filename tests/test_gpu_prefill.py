@@ -14,7 +14,8 @@ import torch
 
 import synth
 from oracle import glq as og
-from gpu_util import rel_frob, say, to_f64
+from gpu_util import (fragment_buffer, oracle_prefill_u16, rel_frob, row_exponents, say, to_f64, u16_as_f64,
+                      unpack_fragment_buffer)
 
 pytestmark = pytest.mark.gpu
 glq = pytest.importorskip("e8_lattice_codebook_amd")
@@ -58,54 +59,57 @@ def test_prefill_linear(gpu_codebooks, M):
 
 @pytest.mark.parametrize("M", [17, 300])
 def test_fragment_order_path_matches_row_order(gpu_codebooks, M):
-    # the linear's prefill steps (input transform into fragment order, then the
-    # shared-tile matmul for slot codes or the per-wave matmul for codebook indices)
-    # and the per-wave matmul on the same fp16 u in row order: the same exact
+    # the same fp16 operand, built on the CPU from the oracle's transform, given to
+    # the shared-tile matmul (slot codes) and the per-wave matmul (codebook indices)
+    # in fragment order and to the per-wave matmul in row order: the same exact
     # products, summed in other orders (fp32), all within 1e-5 of the oracle; the
     # per-wave kernel gives the same bits on either order of u
     layer = synth.random_layer(2000, 3000, 8, seed=M + 1, n_pad=2048, m_pad=4096)
     ql = glq.QuantizedLayer.from_synth(layer, gpu_codebooks)
     qs = ql.to_slot_codes()
     assert glq.e8_matmul_prefill_supported(qs) and glq.e8_matmul_prefill_supported(ql)
-    x = torch.randn(M, 2000, device=DEV, dtype=torch.bfloat16)
-    uf = glq.input_rht_prefill(x, ql.n_pad, ql.sign_in)
+    x = np.random.default_rng(M).standard_normal((M, 2000)).astype(np.float32)
+    u16, _ = oracle_prefill_u16(x, layer.sign_in, 2048)
+    uf = fragment_buffer(u16, np.zeros(M, np.int32), DEV)
     zs = glq.e8_matmul_prefill(qs, uf, M)
     zi = glq.e8_matmul_prefill(ql, uf, M)
-    u16 = glq.input_rht(x, ql.n_pad, ql.sign_in, torch.float16)
-    zr = glq.e8_matmul(ql, u16)
+    zr = glq.e8_matmul(ql, torch.from_numpy(u16).to(DEV))
     torch.cuda.synchronize()
     assert torch.equal(zi, zr)
-    want = og.matmul_z(to_f64(u16), layer.idx0, layer.idx1, 8, layer.wscale, layer.resid_scale)
+    want = og.matmul_z(u16.astype(np.float64), layer.idx0, layer.idx1, 8, layer.wscale, layer.resid_scale)
     assert rel_frob(to_f64(zs[0]), want) <= 1e-5
     assert rel_frob(to_f64(zr[0]), want) <= 1e-5
 
 
 # Slot-code layers at many tiles per compute unit (m_pad 8192: 32 output tiles of
 # 256; M = 1000 gives 8 token tiles of 128, the last with 104 tokens and a token
-# block of 8; M = 2049 gives 17, the last with one token).
+# block of 8; M = 2049 gives 17, the last with one token).  The operand comes from the
+# oracle's transform with the library's row exponents (rows of x scaled over 2^40).
 @pytest.mark.parametrize("resid_bits", [0, 8, 16])
 @pytest.mark.parametrize("M", [1000, 2049])
 def test_prefill_large_slot_codes(gpu_codebooks, resid_bits, M):
     layer = synth.random_layer(1000, 8000, resid_bits, seed=M + resid_bits, n_pad=1024, m_pad=8192)
     ql = glq.QuantizedLayer.from_synth(layer, gpu_codebooks)
     qs = ql.to_slot_codes()
-    x = torch.from_numpy(np.random.default_rng(M).standard_normal((M, 1000)).astype(np.float32)).to(DEV)
+    rng = np.random.default_rng(M)
+    x = (rng.standard_normal((M, 1000)) * np.exp2(rng.integers(-20, 21, size=(M, 1)))).astype(np.float32)
     say("prefill large", resid_bits, M)
-    uf = glq.input_rht_prefill(x, 1024, ql.sign_in)
+    u16, e = oracle_prefill_u16(x, layer.sign_in, 1024)
+    uf = fragment_buffer(u16, e, DEV)
     zw = glq.e8_matmul_prefill(qs, uf, M)
-    u16 = glq.input_rht(x, 1024, ql.sign_in, torch.float16)
     torch.cuda.synchronize()
-    want = og.matmul_z(to_f64(u16), layer.idx0, layer.idx1, resid_bits, layer.wscale, layer.resid_scale)
-    err = rel_frob(to_f64(zw[0]), want)
+    want = og.matmul_z(u16_as_f64(u16, e), layer.idx0, layer.idx1, resid_bits, layer.wscale, layer.resid_scale)
+    err = rel_frob(to_f64(zw[0]) * np.exp2(-e)[:, None], want * np.exp2(-e)[:, None])
     say("  rel_frob", err)
     assert err <= 1e-5, err
     # repeat calls are bit-identical; the whole linear keeps the prefill bound
     assert torch.equal(glq.e8_matmul_prefill(qs, uf, M), zw)
-    y = glq.e8rht_linear(qs, x, torch.float32)
+    y = glq.e8rht_linear(qs, torch.from_numpy(x).to(DEV), torch.float32)
     torch.cuda.synchronize()
-    wy = og.linear(x.double().cpu().numpy(), layer.sign_in, layer.sign_out, 1024, 8000, layer.idx0, layer.idx1,
+    wy = og.linear(x.astype(np.float64), layer.sign_in, layer.sign_out, 1024, 8000, layer.idx0, layer.idx1,
                    resid_bits, layer.wscale, layer.resid_scale)
-    assert rel_frob(to_f64(y), wy) <= 5e-3
+    sc = np.exp2(-e)[:, None]
+    assert rel_frob(to_f64(y) * sc, wy * sc) <= 5e-3
 
 
 @pytest.mark.parametrize("bpw", [5, 8])
@@ -122,20 +126,29 @@ def test_prefill_large_slot_codes_recipes(gpu_codebooks, bpw):
     assert rel_frob(to_f64(y), want) <= 5e-3
 
 
-@pytest.mark.parametrize("M,n,n_pad", [(33, 2000, 2048), (5, 2600, 2688)])
+@pytest.mark.parametrize("M,n,n_pad", [(33, 2000, 2048), (5, 2600, 2688), (20, 40000, 40960)])
 def test_fragment_order_layout(M, n, n_pad):
-    # the documented placement of element (b, i): group g = i / 8, k-step
-    # ks = 4 (g / 16) + g % 4, quarter q = (g / 4) % 4, half index
-    # (((b / 16) KS + ks) 4 + q) 128 + (b % 16) 8 + i % 8 with KS = n_pad / 32; rows
-    # past M are not compared
+    # glq_input_rht_prefill writes element (b, i) at the documented placement (group
+    # g = i / 8, k-step ks = 4 (g / 16) + g % 4, quarter q = (g / 4) % 4, half index
+    # (((b / 16) KS + ks) 4 + q) 128 + (b % 16) 8 + i % 8 with KS = n_pad / 32) as the
+    # fp16 rounding of u[b] 2^-e[b], and the row exponents after it.  The exponents
+    # are integer decisions taken from x alone: bit-exact.  The values are the fp32
+    # transform rounded once to fp16: within one fp16 step of the rounding of the
+    # oracle's fp64 u.  Rows span 2^-100 .. 2^100 and include a zero row.
     sign = synth.random_layer(n, 256, 0, seed=M, n_pad=n_pad, m_pad=256).sign_in
-    x = torch.randn(M, n, device=DEV, dtype=torch.bfloat16)
-    st = torch.from_numpy(sign).to(DEV)
-    uf = glq.input_rht_prefill(x, n_pad, st).view(torch.float16).cpu().numpy()
-    u = glq.input_rht(x, n_pad, st, torch.float16).cpu().numpy()
-    KS = n_pad // 32
-    b, i = np.meshgrid(np.arange(M), np.arange(n_pad), indexing="ij")
-    g = i // 8
-    ks, q = 4 * (g // 16) + g % 4, (g // 4) % 4
-    pos = (((b // 16) * KS + ks) * 4 + q) * 128 + (b % 16) * 8 + i % 8
-    assert np.array_equal(uf[pos].view(np.uint16), u.view(np.uint16))
+    rng = np.random.default_rng(M)
+    x = rng.standard_normal((M, n)) * np.exp2(rng.integers(-100, 101, size=(M, 1)))
+    x[M // 2] = 0.0
+    xb = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    x64 = xb.double().numpy()
+    got, e = unpack_fragment_buffer(glq.input_rht_prefill(xb.to(DEV), n_pad, torch.from_numpy(sign).to(DEV)),
+                                    M, n_pad)
+    want, e_want = oracle_prefill_u16(x64, sign, n_pad)
+    assert np.array_equal(e, e_want)
+    assert np.all(np.abs(want.astype(np.float64)) <= 2.0 ** 14)
+    gi = got.view(np.int16).astype(np.int64)
+    wi = want.view(np.int16).astype(np.int64)
+    # distance in fp16 steps (sign-magnitude bit patterns as a monotone integer line)
+    key = lambda v: np.where(v < 0, -(v & 0x7FFF), v)
+    assert np.max(np.abs(key(gi) - key(wi))) <= 1
+    assert np.all(got[M // 2] == 0)

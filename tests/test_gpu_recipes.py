@@ -16,7 +16,7 @@ import torch
 
 import synth
 from oracle import glq as og
-from gpu_util import rel_frob, same_products, say, to_f64
+from gpu_util import fragment_buffer, oracle_prefill_u16, rel_frob, same_products, say, to_f64, u16_as_f64
 
 pytestmark = pytest.mark.gpu
 glq = pytest.importorskip("e8_lattice_codebook_amd")
@@ -107,11 +107,10 @@ def test_prefill_matmul_recipe(gpu_codebooks, bpw):
         assert err <= 1e-5, (M, err)
         # the linear's prefill steps for slot codes (fragment-order u, shared-tile
         # kernel, both passes) within fp32 accumulation of the oracle
-        x = torch.randn(M, 1000, device=DEV, dtype=torch.bfloat16)
-        uf = glq.input_rht_prefill(x, ql.n_pad, ql.sign_in)
-        zf = glq.e8_matmul_prefill(ql.to_slot_codes(), uf, M)
-        u16 = glq.input_rht(x, ql.n_pad, ql.sign_in, torch.float16)
+        x = np.random.default_rng(M + 1).standard_normal((M, 1000))
+        uq, e = oracle_prefill_u16(x, layer.sign_in, ql.n_pad)
+        zf = glq.e8_matmul_prefill(ql.to_slot_codes(), fragment_buffer(uq, e, DEV), M)
         torch.cuda.synchronize()
-        wf = og.matmul_z(to_f64(u16), layer.idx0, layer.idx1, layer.resid_bits, layer.wscale, layer.resid_scale,
-                         extra=layer.oracle_extra())
+        wf = og.matmul_z(u16_as_f64(uq, e), layer.idx0, layer.idx1, layer.resid_bits, layer.wscale,
+                         layer.resid_scale, extra=layer.oracle_extra())
         assert rel_frob(to_f64(zf[0]), wf) <= 1e-5
