@@ -270,6 +270,22 @@ def e8rht_linear(layer, x, y_dtype=None, workspace=None, out=None):
     return y
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GLQ_NOALLOC_SCRATCH_BYTES
+
+
+def e8rht_linear_noalloc(layer, x, y_dtype=None, out=None):
+    """The E8RHTLinear forward with the library's own device scratch as its workspace
+    (glq_e8rht_linear_noalloc): nothing is allocated by the call when `out` is given.
+    Calls that overlap on one device race on that scratch."""
+    B = x.shape[0]
+    x = x.contiguous()
+    y_dtype = y_dtype or x.dtype
+    y = out if out is not None else torch.empty((B, layer.m), dtype=y_dtype, device=x.device)
+    _lib.check(lib().glq_e8rht_linear_noalloc(ctypes.byref(layer.desc), _ptr(x), _dt(x.dtype), B, _ptr(y),
+                                              _dt(y.dtype), _stream(x.device)), "glq_e8rht_linear_noalloc")
+    return y
+
+
 class KVCache:
     """An E8-compressed paged K/V cache on the device (glq_kv_cache).
 

@@ -404,6 +404,26 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
                             glq_dtype y_dt, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * glq_e8rht_linear_noalloc — glq_e8rht_linear without a caller's workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The workspace is a device array
+ * of GLQ_NOALLOC_SCRATCH_BYTES inside the library, one per device, held until the
+ * process ends; nothing is allocated by the call.  It fits every B <= 16 call of the
+ * SmolLM2, SmolLM3 and Devstral-Small layer shapes (Devstral at B = 16 takes about
+ * 35 MiB) and prefill calls of modest M; a call whose
+ * glq_e8rht_linear_workspace_bytes(layer, B) exceeds it returns GLQ_ERR_WORKSPACE
+ * and launches nothing.  Every call on one device shares that device's array, so
+ * calls that may overlap on one device (several streams or host threads) race and
+ * must be serialized by the caller.  The array needs no initial contents and keeps
+ * whatever the last call left.
+ * Arguments, results and errors otherwise as glq_e8rht_linear (GLQ_ERR_HIP also when
+ * the array's device address cannot be obtained).
+ */
+#define GLQ_NOALLOC_SCRATCH_BYTES (64 << 20)
+glq_status glq_e8rht_linear_noalloc(const glq_layer* layer, const void* x, glq_dtype x_dt, int64_t B, void* y,
+                                    glq_dtype y_dt, hipStream_t stream);
+
+/*
  * glq_e8kv_attention_decode — one decode step of attention over an E8-compressed
  * paged K/V cache, the cache dequantized inside the kernel (Glq v0.5.0 release
  * notes, "Highlights": no decompress-to-workspace pass, an 8-point FHT butterfly
