@@ -24,7 +24,14 @@ prefill: the 2048-token prefill of the SmolLM3-3B gate shape (2048->11008,
 block_b1: the seven linears of a SmolLM3-3B decoder block (3 bpw, fp16) at B = 1,
           issued eagerly from Python and replayed from one captured HIP graph; the
           small layers are launch-bound, and the graph removes the host launch cost.
+configs: every layer of the other workloads at their batch sizes (tiny 256->256 at B=1;
+          SmolLM2 up at B=1, 5; each SmolLM3 linear at B=1, 5; Devstral at B=4, 16, the
+          staged decode path), each timed over rotating copies of its indices, in GB/s
+          and as a fraction of the HBM peak.
 cpu_baseline: the fp64 oracle on the step's layers in turn, for >= 10 s of host CPU work.
+
+--only LEG runs one leg by itself (for profiler runs); --pmc-report summarizes
+rocprofv3 --pmc folders of such a run into a counter file under profiles/.
 """
 
 import argparse
@@ -37,6 +44,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+LEGS = ["decode", "configs", "prefill", "block", "recipes", "blockdiag", "kv"]
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 METRIC = "fused E8-RHT linear: achieved HBM GB/s at B=1 decode; TFLOP/s at prefill"
@@ -65,6 +73,7 @@ def main():
     ap.add_argument("--recipe-steps", type=int, default=300)
     ap.add_argument("--no-blockdiag", action="store_true", help="skip the unpadded (block-diagonal) measurement")
     ap.add_argument("--no-kv", action="store_true", help="skip the E8 KV-cache decode attention measurement")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-layer measurement of the other configs")
     ap.add_argument("--kv-steps", type=int, default=50)
     ap.add_argument("--index-format", choices=["slot", "codebook"], default="slot",
                     help="16-bit index arrays as slot codes (default) or as codebook indices")
@@ -74,9 +83,18 @@ def main():
                     help="only summarize four rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of this "
                          "bench and of --calibrate-copy) into " + os.path.relpath(TRAFFIC_FILE, ROOT))
     ap.add_argument("--copy-bytes", type=int, default=1 << 28, help="BYTES of the --calibrate-copy run summarized")
+    ap.add_argument("--only", choices=LEGS, help="run one leg alone (profiler runs)")
+    ap.add_argument("--config-calls", type=int, default=200, help="timed calls per layer in the configs leg")
+    ap.add_argument("--pmc-report", nargs="+", metavar="ARG",
+                    help="OUT KERNEL DIR [DIR ...]: medians of every counter of the dispatches whose name "
+                         "contains KERNEL in rocprofv3 --pmc folders DIR, written to OUT with --pmc-cmd")
+    ap.add_argument("--pmc-cmd", action="append", default=[], help="a command line recorded in the report")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, args.copy_bytes)
+        return
+    if args.pmc_report:
+        pmc_report(args.pmc_report, args.pmc_cmd)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the E8RHTLinear path here has no multi-GPU "
@@ -101,6 +119,15 @@ def main():
         return
     log("bench: building codebooks")
     cb = glq.Codebooks(dev)
+    if args.only and args.only != "decode":
+        fn = {"configs": lambda: bench_configs(glq, synth, cb, dev, args, log),
+              "prefill": lambda: bench_prefill(glq, synth, cb, dev, args, log),
+              "block": lambda: bench_block_graph(glq, synth, cb, dev, args, log),
+              "recipes": lambda: bench_recipes(glq, synth, cb, dev, args, log, None),
+              "blockdiag": lambda: bench_blockdiag(glq, synth, cb, dev, args, log, None),
+              "kv": lambda: bench_kv(glq, synth, cb, dev, args, log)}[args.only]
+        print(json.dumps({"only": args.only, args.only: fn()}), flush=True)
+        return
 
     wl = synth.WORKLOADS["devstral_mlp"]
     B = args.batch
@@ -148,21 +175,19 @@ def main():
     log("bench: %.4f ms/step (wall %.4f), %.1f GB/s" % (ms_per_step, wall * 1e3 / args.steps, value))
 
     # per-call timing: at B = 1 every layer call is fused_decode_kernel followed by
-    # output_blocks_kernel; events on the launch stream around each call
-    n_ev = args.steps * len(host_layers)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
-    for i in range(args.steps):
-        row = qls[(args.warmup + i) % copies]
-        for k in range(len(row)):
-            a, b = evs[i * len(row) + k]
-            a.record()
-            glq.e8rht_linear(row[k], xs[k], out=ys[k], workspace=ws)
-            b.record()
-    torch.cuda.synchronize()
-    per_layer_ms = [float(np.mean([evs[i * len(host_layers) + k][0].elapsed_time(evs[i * len(host_layers) + k][1])
-                                   for i in range(args.steps)])) for k in range(len(host_layers))]
+    # output_blocks_kernel.  Per layer, one pair of events (on the launch stream)
+    # around `steps` back-to-back calls of that layer over the rotating copies, so
+    # the events add nothing to the calls they time.
+    per_layer_ms = []
+    for k in range(len(host_layers)):
+        e0.record()
+        for i in range(args.steps):
+            glq.e8rht_linear(qls[i % copies][k], xs[k], out=ys[k], workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        per_layer_ms.append(e0.elapsed_time(e1) / args.steps)
     achieved = sum(launch_bytes) / (sum(per_layer_ms) * 1e-3) / 1e9
-    log("bench: per-launch ms %s -> %.1f GB/s" % (["%.4f" % t for t in per_layer_ms], achieved))
+    log("bench: per-call ms %s -> %.1f GB/s" % (["%.4f" % t for t in per_layer_ms], achieved))
 
     # the other index format, same loop and step count
     other_steps = min(args.steps, 300)
@@ -187,9 +212,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
-        "arith": "activations in 16-bit fixed point per 64 columns (4 int4 digit planes), exact i32 dot "
-                 "products against the int4-packed codewords, f32 scaling, reduction and transforms",
+        "dtype": "i16 fixed point x i4 -> i32, f32 scale",
+        "arith": "activations in 16-bit fixed point per 64 columns (a power-of-two-normalized scale per "
+                 "block, 4 int4 digit planes), exact i32 dot products against the int4-packed codewords, "
+                 "f32 scaling, reduction and transforms",
         "data": "synthetic",
         "config": {
             "workload": "Devstral-Small-24B MLP decode (gate 5120->32768, up 5120->32768, down 32768->5120), "
@@ -212,13 +238,17 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(launch_bytes) if B == 1 else None,
-            "per_launch_ms": [round(t, 5) for t in per_layer_ms],
-            "bytes_per_launch": launch_bytes,
+            "per_call_ms": [round(t, 5) for t in per_layer_ms],
+            "bytes_per_call": launch_bytes,
+            "timing": "one event pair around %d back-to-back calls per layer (rotating copies)" % args.steps,
         },
     }
 
     result["other_index_format"] = {"index_format": "codebook indices" if slot else "slot codes",
                                     "value": round(other_value, 2), "unit": "GB/s", "steps": other_steps}
+
+    if not args.no_configs:
+        result["configs"] = bench_configs(glq, synth, cb, dev, args, log, devstral=(host_layers, qls, copies))
 
     if not args.no_prefill:
         result["prefill"] = bench_prefill(glq, synth, cb, dev, args, log)
@@ -333,68 +363,216 @@ def measured_traffic(launch_bytes):
         return None
 
 
+def clone_layer(glq, q):
+    """A device copy of a QuantizedLayer's index arrays (signs and codebooks shared)."""
+    return glq.QuantizedLayer(q.n, q.m, q.n_pad, q.m_pad, q.resid_bits, q.sign_in, q.sign_out, q.idx0.clone(),
+                              None if q.idx1 is None else q.idx1.clone(), q.codebooks, q.wscale, q.resid_scale,
+                              q.device, q.index_format, extra=tuple((b, i.clone(), sc) for b, i, sc in q.extra))
+
+
+def time_calls(torch, calls, reps):
+    """ms per call of `calls` (a list of callables, run in turn `reps` times) between one
+    pair of events on the current stream, after two warm-up passes."""
+    for _ in range(2):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for c in calls:
+            c()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * len(calls))
+
+
+CONFIG_LEGS = [("tiny", (1,)), ("smollm2_up", (1, 5)), ("smollm3_block", (1, 5)), ("devstral_mlp", (4, 16))]
+
+
+def bench_configs(glq, synth, cb, dev, args, log, devstral=None):
+    """Every layer of the other workloads at their batch sizes, one layer at a time:
+    slot-code copies of its indices rotated so that the calls stream about 1 GiB of
+    indices (cold past the 256 MB MALL where the layer is large enough: at most 2048
+    copies), calls timed back to back with one pair of events.  GB/s counts index,
+    activation, output and sign bytes per call; frac is against the 8 TB/s HBM peak.
+    B = 1 runs the two-launch fused decode, 2 <= B <= 16 the staged decode (input RHT,
+    quantization, LDS-codebook GEMV, output RHT)."""
+    import numpy as np
+    import torch
+
+    out = []
+    for key, batches in CONFIG_LEGS:
+        wl = synth.WORKLOADS[key]
+        ab = act_bytes(wl.act_dtype)
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[wl.act_dtype]
+        for k, shape in enumerate(wl.layers):
+            if key == "devstral_mlp" and devstral is not None:
+                host, rows, ncop = devstral
+                l = host[k]
+                cps = [row[k] for row in rows] if args.index_format == "slot" else None
+            else:
+                l = synth.make_layer(shape, wl.resid_bits, wl.seed, k)
+                cps = None
+            if cps is None:
+                q0 = glq.QuantizedLayer.from_synth(l, cb)
+                if args.index_format == "slot":
+                    q0 = q0.to_slot_codes()
+                ncop = max(2, min(2048, math.ceil((1 << 30) / l.index_bytes())))
+                cps = [q0] + [clone_layer(glq, q0) for _ in range(ncop - 1)]
+            ncop = len(cps)
+            for B in batches:
+                _, raw = synth.make_x(l.n, B, wl.act_dtype, wl.seed, k)
+                x = torch.from_numpy(raw.view(np.int16) if wl.act_dtype == "bf16" else raw).to(dev)
+                if wl.act_dtype == "bf16":
+                    x = x.view(torch.bfloat16)
+                y = torch.empty((B, l.m), dtype=tdt, device=dev)
+                ws = glq.linear_workspace(cps[0], B, dev)
+                calls = [lambda q=q: glq.e8rht_linear(q, x, out=y, workspace=ws) for q in cps]
+                reps = max(1, math.ceil(args.config_calls / ncop))
+                ms = time_calls(torch, calls, reps)
+                nbytes = l.index_bytes() + B * (l.n + l.m) * ab + l.n_pad + l.m_pad
+                gbs = nbytes / (ms * 1e-3) / 1e9
+                path = "fused B=1 (2 launches)" if B == 1 else "staged (input RHT, quantization, GEMV, output RHT)"
+                log("bench: %s %s B=%d: %.2f us per call, %.1f GB/s (%d copies)" % (key, shape.name, B, ms * 1e3,
+                                                                                   gbs, ncop))
+                out.append({"workload": key, "layer": "%s %d->%d (n_pad %d, m_pad %d)" % (
+                    shape.name, l.n, l.m, l.n_pad, l.m_pad), "B": B, "bpw": l.bpw, "path": path,
+                    "us_per_call": round(ms * 1e3, 3), "value": round(gbs, 2), "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_call": int(nbytes), "copies": ncop,
+                    "cold": bool(ncop * l.index_bytes() >= (512 << 20)), "calls_timed": reps * ncop})
+                del ws, x, y
+            del cps
+            torch.cuda.empty_cache()
+    return out
+
+
+def pmc_report(argv, cmds):
+    """OUT KERNEL DIR [DIR ...]: per-counter medians over the dispatches whose kernel name
+    contains KERNEL in rocprofv3 --pmc csv folders, with the derived MFMA, VALU and LDS
+    figures where their counters are present."""
+    import csv
+    import glob
+    import statistics
+    out_file, kname, dirs = argv[0], argv[1], argv[2:]
+    vals, names = {}, set()
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if kname in r.get("Kernel_Name", ""):
+                        vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                        names.add(r["Kernel_Name"])
+    if not vals:
+        raise SystemExit("no dispatches of %s under %s" % (kname, dirs))
+    med = {k: statistics.median(v) for k, v in vals.items()}
+    lines = ["# rocprofv3 --pmc counters (MI355X, one GPU): medians over the dispatches of %s" % kname,
+             "# kernels: %s" % "; ".join(sorted(names)),
+             "# commands (repository root; profiler runs after cd /tmp && export TMPDIR=/tmp):"]
+    lines += ["#   %s" % c for c in cmds]
+    lines += ["# values are sums over the device's XCDs / shader engines as rocprofv3 reports them"]
+    for k in sorted(med):
+        lines.append("%s: %.1f (%d dispatches)" % (k, med[k], len(vals[k])))
+    g = med.get("GRBM_GUI_ACTIVE")
+    if g:
+        xcd_cycles = g / 8.0  # GRBM_GUI_ACTIVE is summed over the 8 XCDs
+        lines.append("derived kernel_cycles_per_xcd: %.0f (%.2f us at 2.4 GHz)" % (xcd_cycles, xcd_cycles / 2400.0))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+            lines.append("derived mfma_busy_per_cu_cycle: %.4f (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8) / "
+                         "256 CUs)" % (med["SQ_VALU_MFMA_BUSY_CYCLES"] / xcd_cycles / 256.0))
+        if "SQ_INSTS_VALU_MFMA_MOPS_F16" in med:
+            fl = med["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512.0
+            lines.append("derived mfma_f16_flops: %.4g (MOPS x 512) -> %.1f TFLOP/s over the kernel cycles"
+                         % (fl, fl / (xcd_cycles / 2.4e9) / 1e12))
+        if "SQ_INSTS_VALU" in med:
+            lines.append("derived valu_busy_per_simd: %.4f (SQ_INSTS_VALU x 4 cycles / (kernel cycles x 1024 SIMDs))"
+                         % (med["SQ_INSTS_VALU"] * 4.0 / (xcd_cycles * 1024.0)))
+    if "SQ_LDS_BANK_CONFLICT" in med and "SQ_INSTS_LDS" in med:
+        lines.append("derived lds_conflict_cycles_per_lds_inst: %.2f" % (med["SQ_LDS_BANK_CONFLICT"] / med["SQ_INSTS_LDS"]))
+    os.makedirs(os.path.dirname(os.path.abspath(out_file)), exist_ok=True)
+    with open(out_file, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def bench_prefill(glq, synth, cb, dev, args, log):
+    """The 2048-token prefill of the SmolLM3-3B gate shape, 3 bpw: the whole linear, and
+    its MFMA matmul alone (events around it), on the padded layer (m_pad 16384, the
+    workload as described) and on the unpadded one (m_pad = m = 11008, block-diagonal
+    output transform).  TFLOP/s counts the matmul's algorithmic flops 2 M m_pad n_pad;
+    the nominal figure divides the layer's own 2 M m n by the same time."""
     import numpy as np
     import torch
 
     wl = synth.WORKLOADS["prefill_gateup"]
-    l = synth.make_layer(wl.layers[0], wl.resid_bits, wl.seed, 0)
     M = wl.batches[0]
-    q_cb = glq.QuantizedLayer.from_synth(l, cb)
-    q_slot = q_cb.to_slot_codes()
-    q, q_other = (q_slot, q_cb) if args.index_format == "slot" else (q_cb, q_slot)
-    _, raw = synth.make_x(l.n, M, wl.act_dtype, wl.seed, 0)
-    x = torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
-    u = torch.empty(glq.lib().glq_prefill_u_bytes(M, l.n_pad), dtype=torch.uint8, device=dev)
-    u16 = torch.empty((M, l.n_pad), dtype=torch.float16, device=dev)
-    z = torch.empty((1, M, l.m_pad), dtype=torch.float32, device=dev)
-    y = torch.empty((M, l.m), dtype=torch.bfloat16, device=dev)
-    ws = glq.linear_workspace(q, M, dev)
+
+    def measure(l):
+        q_cb = glq.QuantizedLayer.from_synth(l, cb)
+        q_slot = q_cb.to_slot_codes()
+        q, q_other = (q_slot, q_cb) if args.index_format == "slot" else (q_cb, q_slot)
+        _, raw = synth.make_x(l.n, M, wl.act_dtype, wl.seed, 0)
+        x = torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
+        u = torch.empty(glq.lib().glq_prefill_u_bytes(M, l.n_pad), dtype=torch.uint8, device=dev)
+        u16 = torch.empty((M, l.n_pad), dtype=torch.float16, device=dev)
+        z = torch.empty((1, M, l.m_pad), dtype=torch.float32, device=dev)
+        y = torch.empty((M, l.m), dtype=torch.bfloat16, device=dev)
+        ws = glq.linear_workspace(q, M, dev)
+        lin_ms = time_calls(torch, [lambda: glq.e8rht_linear(q, x, out=y, workspace=ws)], args.prefill_steps)
+
+        def matmul_ms(qq):
+            # the linear's prefill steps one by one, events around the matmul: slot codes
+            # on fragment-order u (gemm_shared_kernel), codebook indices on fragment-order
+            # u (gemm_lds_kernel)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.prefill_steps)]
+            frag = glq.e8_matmul_prefill_supported(qq)
+            for a, b in evs:
+                if frag:
+                    glq.input_rht_prefill(x, l.n_pad, qq.sign_in, out=u)
+                else:
+                    glq.input_rht(x, l.n_pad, qq.sign_in, torch.float16, out=u16)
+                a.record()
+                if frag:
+                    glq.e8_matmul_prefill(qq, u, M, out=z)
+                else:
+                    glq.e8_matmul(qq, u16, out=z)
+                b.record()
+                glq.output_rht(z, l.m, qq.sign_out, out=y)
+            torch.cuda.synchronize()
+            return float(np.mean([a.elapsed_time(b) for a, b in evs[2:]])), frag
+
+        gemm_ms, frag = matmul_ms(q)
+        other_ms, _ = matmul_ms(q_other)
+        return lin_ms, gemm_ms, other_ms, frag
+
+    l = synth.make_layer(wl.layers[0], wl.resid_bits, wl.seed, 0)
+    lin_ms, gemm_ms, other_ms, frag = measure(l)
     flops = 2.0 * M * l.m_pad * l.n_pad
-    for _ in range(3):
-        glq.e8rht_linear(q, x, out=y, workspace=ws)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.prefill_steps):
-        glq.e8rht_linear(q, x, out=y, workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    lin_ms = e0.elapsed_time(e1) / args.prefill_steps
-
-    def matmul_ms(qq):
-        # the linear's prefill steps one by one, events around the matmul: slot codes
-        # on fragment-order u (gemm_shared_kernel), codebook indices on row-order u
-        # (gemm_lds_kernel)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.prefill_steps)]
-        frag = glq.e8_matmul_prefill_supported(qq)
-        for a, b in evs:
-            if frag:
-                glq.input_rht_prefill(x, l.n_pad, qq.sign_in, out=u)
-            else:
-                glq.input_rht(x, l.n_pad, qq.sign_in, torch.float16, out=u16)
-            a.record()
-            if frag:
-                glq.e8_matmul_prefill(qq, u, M, out=z)
-            else:
-                glq.e8_matmul(qq, u16, out=z)
-            b.record()
-            glq.output_rht(z, l.m, qq.sign_out, out=y)
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs])), frag
-
-    gemm_ms, frag = matmul_ms(q)
+    nominal = 2.0 * M * l.m * l.n
     tflops = flops / (gemm_ms * 1e-3) / 1e12
-    other_tflops = flops / (matmul_ms(q_other)[0] * 1e-3) / 1e12
-    log("bench: prefill linear %.4f ms, MFMA matmul %.4f ms = %.1f TFLOP/s" % (lin_ms, gemm_ms, tflops))
+    log("bench: prefill linear %.4f ms, MFMA matmul %.4f ms = %.1f TFLOP/s (nominal %.1f)" % (
+        lin_ms, gemm_ms, tflops, nominal / (gemm_ms * 1e-3) / 1e12))
+    lu = synth.make_layer(wl.layers[0], wl.resid_bits, wl.seed, 0, block_diag=True)
+    ulin_ms, ugemm_ms, _, _ = measure(lu)
+    uflops = 2.0 * M * lu.m_pad * lu.n_pad
+    log("bench: unpadded prefill (m_pad %d) linear %.4f ms, matmul %.4f ms = %.1f TFLOP/s" % (
+        lu.m_pad, ulin_ms, ugemm_ms, uflops / (ugemm_ms * 1e-3) / 1e12))
     return {
         "workload": "SmolLM3-3B gate 2048->11008 (m_pad 16384), M=2048 tokens, 3 bpw, bf16 activations",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "linear_ms": round(lin_ms, 5),
+        "matmul_ms": round(gemm_ms, 5),
+        "nominal_tflops": round(nominal / (gemm_ms * 1e-3) / 1e12, 2),
+        "nominal_flops": nominal,
         "other_index_format": {"index_format": "codebook indices" if args.index_format == "slot" else "slot codes",
-                               "value": round(other_tflops, 2), "unit": "TFLOP/s"},
+                               "value": round(flops / (other_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s"},
+        "unpadded": {"workload": "the same layer unpadded: m_pad = m = 11008 (block-diagonal output transform "
+                                 "over 8192 + 2048 + 512 + 256)",
+                     "linear_ms": round(ulin_ms, 5), "matmul_ms": round(ugemm_ms, 5),
+                     "value": round(uflops / (ugemm_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "flops": uflops,
+                     "linear_speedup_vs_padded": round(lin_ms / ulin_ms, 3)},
         "roofline": {"bound": "mfma", "kernel": ("gemm_shared_kernel (prefill matmul: a 64-row codeword tile per "
                                                  "k-step dequantized from the LDS codebook into LDS, shared by four "
                                                  "waves as fp16 MFMA operands, fp32 accumulation)") if frag else
@@ -497,7 +675,7 @@ def bench_recipes(glq, synth, cb, dev, args, log, value_4bpw):
     out = {"workload": "Devstral-Small-24B MLP decode (gate, up, down), B=1, bf16 activations; recipes of the "
                        "bit-width table: 16+16+8, 16+16+16, 16+16+16+8, 16+16+16+16 bits per 8 weights",
            "index_format": args.index_format, "steps": args.recipe_steps, "unit": "GB/s",
-           "value_4bpw": round(value_4bpw, 2), "by_bpw": {}}
+           "value_4bpw": None if value_4bpw is None else round(value_4bpw, 2), "by_bpw": {}}
     for bpw in (5, 6, 7, 8):
         resid_bits, extra_bits = synth.RECIPES[bpw]
         host = [synth.make_layer(s, resid_bits, wl.seed, k, extra_bits=extra_bits) for k, s in enumerate(wl.layers)]
@@ -574,13 +752,14 @@ def bench_blockdiag(glq, synth, cb, dev, args, log, padded_ms):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    log("bench: unpadded Devstral MLP B=1: %.4f ms/step, %.1f GB/s (padded %.4f ms/step)" % (ms, gbs, padded_ms))
+    log("bench: unpadded Devstral MLP B=1: %.4f ms/step, %.1f GB/s" % (ms, gbs))
     out = {"workload": "Devstral-Small-24B MLP decode, B=1, bf16, 4 bpw, unpadded: gate, up 5120 -> 32768 and down "
                        "32768 -> 5120 with block-diagonal transforms over 5120 = 4096 + 1024",
            "index_format": args.index_format, "steps": args.steps, "ms_per_step": round(ms, 5),
            "value": round(gbs, 2), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
            "algorithmic_bytes_per_step": step_bytes, "index_bytes_per_step": idx_bytes,
-           "padded_ms_per_step": round(padded_ms, 5), "step_speedup_vs_padded": round(padded_ms / ms, 3)}
+           "padded_ms_per_step": None if padded_ms is None else round(padded_ms, 5),
+           "step_speedup_vs_padded": None if padded_ms is None else round(padded_ms / ms, 3)}
     del qls, ws
     torch.cuda.empty_cache()
     return out

@@ -32,10 +32,18 @@ bool valid_pad(int64_t p) {
   return p >= 8 && p <= GLQ_MAX_PAD && (is_pow2(p) || p % 64 == 0);
 }
 
-// scratch of the two-pass transform: a block longer than one workgroup's, unless
-// the output is fp32 of one block (its own scratch)
-bool rht_needs_ws(int64_t N, bool f32_out) {
-  return largest_block(N) > (int64_t(1) << kSingleLog2) && !(f32_out && is_pow2(N));
+// scratch of the two-pass transform of B rows of length N: some block runs in two
+// passes (longer than one workgroup's, or split for want of rows), unless the output
+// is fp32 of one block (its own scratch)
+bool rht_needs_ws(int64_t B, int64_t N, bool f32_out) {
+  bool two = false;
+  for (int L = 0; L < 63; ++L) {
+    if (!((N >> L) & 1)) continue;
+    int lr, lc;
+    fwht_split(B, L, &lr, &lc);
+    two = two || lc > 0;
+  }
+  return two && !(f32_out && is_pow2(N));
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -133,12 +141,25 @@ size_t prefill_rexp_off(const glq_layer& L, int64_t B) {
 struct LinearWs {
   size_t u_off, uq_off, rin_off, z_off, rout_off, total;
   int splits;
-  bool prefill, lds, fused;
+  bool prefill, lds, fused, skinny;
 };
 
 
 
 constexpr int64_t kDecodeMaxB = 16;
+// from this many activation rows up to kDecodeMaxB the decode matmul runs on the
+// matrix units (its cost per lookup no longer grows with B)
+constexpr int64_t kSkinnyMinB = 4;
+
+// the skinny MFMA decode takes every pass of the layer, and layers of at least 2^21
+// groups (smaller ones are bound by launches and the transforms, where the staged
+// integer GEMV path is as fast)
+bool skinny_ok(const glq_layer& L, int64_t B) {
+  if (B < kSkinnyMinB || B > kDecodeMaxB) return false;
+  if (L.m_pad * (L.n_pad / 8) < (int64_t(1) << 21)) return false;
+  const Passes P = split_passes(L);
+  return gemv_mfma_supported(P.a) && (!P.two || gemv_mfma_supported(P.b));
+}
 
 // the decode kernel with the LDS codebook needs the 16-bit residual stage (if
 // any) to use the primary codebook; otherwise codewords come from global memory
@@ -159,10 +180,24 @@ LinearWs linear_ws(const glq_layer& L, int64_t B) {
   w.prefill = B > kDecodeMaxB;
   w.lds = !w.prefill && decode_uses_lds(L);
   w.fused = fused_decode_supported(L, B);
+  w.skinny = !w.fused && skinny_ok(L, B);
   size_t off = 0;
   if (w.fused) {
     w.z_off = off;
     w.total = off + align256(fused_decode_z_bytes(L));
+    return w;
+  }
+  if (w.skinny) {  // fp16 u in fragment order (+ row exponents), split partials, output scratch
+    w.u_off = off;
+    off += prefill_u_total_bytes(B, L.n_pad);
+    w.rin_off = off;
+    if (rht_needs_ws(B, L.n_pad, false)) off += align256(size_t(B) * size_t(L.n_pad) * 4);
+    w.splits = gemv_mfma_splits(L.n_pad, L.m_pad);
+    w.z_off = off;
+    off += align256(size_t(w.splits) * size_t(B) * size_t(L.m_pad) * 4);
+    w.rout_off = off;
+    if (rht_needs_ws(B, L.m_pad, false)) off += align256(size_t(B) * size_t(L.m_pad) * 4);
+    w.total = off;
     return w;
   }
   w.u_off = off;
@@ -170,12 +205,12 @@ LinearWs linear_ws(const glq_layer& L, int64_t B) {
   w.uq_off = off;
   if (w.lds) off += align256(uq_bytes(B, L.n_pad));
   w.rin_off = off;
-  if (rht_needs_ws(L.n_pad, !w.prefill)) off += align256(size_t(B) * size_t(L.n_pad) * 4);
+  if (rht_needs_ws(B, L.n_pad, !w.prefill)) off += align256(size_t(B) * size_t(L.n_pad) * 4);
   w.splits = matmul_splits(L, B);
   w.z_off = off;
   off += align256(size_t(w.splits) * size_t(B) * size_t(L.m_pad) * 4);
   w.rout_off = off;
-  if (rht_needs_ws(L.m_pad, false)) off += align256(size_t(B) * size_t(L.m_pad) * 4);
+  if (rht_needs_ws(B, L.m_pad, false)) off += align256(size_t(B) * size_t(L.m_pad) * 4);
   w.total = off;
   return w;
 }
@@ -257,7 +292,7 @@ glq_status glq_slot_codes(const void* cb_pack, const uint16_t* idx, int64_t coun
 
 size_t glq_input_rht_workspace_bytes(int64_t B, int64_t n_pad, glq_dtype u_dt) {
   if (B < 1 || !valid_pad(n_pad)) return 0;
-  if (rht_needs_ws(n_pad, u_dt == GLQ_F32)) return align256(size_t(B) * size_t(n_pad) * 4);
+  if (rht_needs_ws(B, n_pad, u_dt == GLQ_F32)) return align256(size_t(B) * size_t(n_pad) * 4);
   return 0;
 }
 
@@ -275,7 +310,7 @@ glq_status glq_input_rht(const void* x, glq_dtype x_dt, int64_t B, int64_t n, in
 
 size_t glq_output_rht_workspace_bytes(int64_t B, int64_t m_pad) {
   if (B < 1 || !valid_pad(m_pad)) return 0;
-  if (rht_needs_ws(m_pad, false)) return align256(size_t(B) * size_t(m_pad) * 4);
+  if (rht_needs_ws(B, m_pad, false)) return align256(size_t(B) * size_t(m_pad) * 4);
   return 0;
 }
 
@@ -393,7 +428,20 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
     return from_hip(launch_fused_decode(L, x, x_dt, y, y_dt, at<float>(workspace, w.z_off), stream));
   hipError_t e;
   float* z = at<float>(workspace, w.z_off);
-  if (!w.prefill) {
+  if (w.skinny) {
+    // fp16 operands with a power-of-two scale per row, in the fragment order of one
+    // 16-row block; every pass of the layer on the matrix units
+    half_t* u = at<half_t>(workspace, w.u_off);
+    int32_t* rexp = at<int32_t>(workspace, w.u_off + prefill_rexp_offset(B, L.n_pad));
+    e = launch_row_exp(x, x_dt, B, L.n, rexp, stream);
+    if (e != hipSuccess) return GLQ_ERR_HIP;
+    e = launch_rht_in_tiled(x, x_dt, B, L.n, L.n_pad, L.sign_in, rexp, u, at<float>(workspace, w.rin_off), stream);
+    if (e != hipSuccess) return GLQ_ERR_HIP;
+    const Passes P = split_passes(L);
+    e = launch_gemv_mfma(P.a, u, rexp, B, z, stream, false);
+    if (e == hipSuccess && P.two) e = launch_gemv_mfma(P.b, u, rexp, B, z, stream, true);
+    if (e != hipSuccess) return GLQ_ERR_HIP;
+  } else if (!w.prefill) {
     float* u = at<float>(workspace, w.u_off);
     e = launch_rht_in(x, x_dt, B, L.n, L.n_pad, L.sign_in, u, GLQ_F32, at<float>(workspace, w.rin_off), stream);
     if (e != hipSuccess) return GLQ_ERR_HIP;

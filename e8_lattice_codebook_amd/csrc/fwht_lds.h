@@ -6,6 +6,8 @@
 // Order is Sylvester's: butterflies (a, b) -> (a + b, a - b) on every index bit.
 #pragma once
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace glq {
@@ -37,9 +39,34 @@ struct LoadSplitSum {  // sum over s = 0..S-1, in order, of z[s][b][off + i]; ro
   const float* z;
   int64_t S, B, N, off;
   __device__ float operator()(int64_t b, int64_t i) const {
-    float acc = z[b * N + off + i];
-    for (int64_t s = 1; s < S; ++s) acc += z[(s * B + b) * N + off + i];
+    const float* p = z + b * N + off + i;
+    const int64_t step = B * N;
+    float acc = p[0];
+    int64_t s = 1;
+    // eight partials in flight at a time, added in split order
+    for (; s + 8 <= S; s += 8) {
+      float t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[j] = p[(s + j) * step];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += t[j];
+    }
+    for (; s < S; ++s) acc += p[s * step];
     return acc;
+  }
+  template <int R>
+  __device__ void load_span(int64_t b, int64_t i0, float (&v)[R]) const {
+    const float* p = z + b * N + off + i0;
+    const int64_t step = B * N;
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = p[j];
+    for (int64_t s = 1; s < S; ++s) {
+      float t[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) t[j] = p[s * step + j];
+#pragma unroll
+      for (int j = 0; j < R; ++j) v[j] += t[j];
+    }
   }
 };
 
@@ -55,6 +82,26 @@ struct StoreOut {  // y[b][c] = RN(sign[c] * v * scale) for c = off + i < m
   }
 };
 
+// ---- R consecutive elements i0 .. i0 + R - 1 of a row ----------------------------------
+// By default one load call per element.  A loader with load_span(row, i0, v) (R a
+// template parameter) takes them together: the split-sum loader issues the R loads of
+// one split at a time, so a thread's loads of a split are in flight together (the sums
+// keep their split order, so the result is the same bit for bit).
+template <class Load, class = void>
+struct HasSpan : std::false_type {};
+template <class Load>
+struct HasSpan<Load, decltype(void(&Load::template load_span<1>))> : std::true_type {};
+
+template <int R, class Load>
+__device__ __forceinline__ void load_elems(const Load& ld, int64_t row, int64_t i0, float (&v)[R]) {
+  if constexpr (HasSpan<Load>::value) {
+    ld.template load_span<R>(row, i0, v);
+  } else {
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = ld(row, i0 + j);
+  }
+}
+
 // ---- one row per workgroup -------------------------------------------------------
 template <int R, class Load, class Store>
 __device__ __forceinline__ void first_pass(const Load& ld, const Store& st, int64_t row, int L, float* buf,
@@ -62,8 +109,7 @@ __device__ __forceinline__ void first_pass(const Load& ld, const Store& st, int6
   const int chunks = (1 << L) / R;
   for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
     float v[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) v[j] = ld(row, c * R + j);
+    load_elems<R>(ld, row, int64_t(c) * R, v);
     fwht_reg<R>(v);
     if (last) {
 #pragma unroll

@@ -32,10 +32,18 @@ inline int64_t smallest_block(int64_t v) { return v & -v; }
 __host__ __device__ constexpr int log2_exact_dev(int v) { return v <= 1 ? 0 : 1 + log2_exact_dev(v >> 1); }
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Two-pass split of a length-2^L transform: (row pass log2, column pass log2).
-inline void fwht_split(int L, int* l_row, int* l_col) {
-  int r = L - 6 > kSplitLog2 ? L - 6 : kSplitLog2;
-  if (r > L) r = L;
+// Rows of a transform launch below which one workgroup per row leaves most of the
+// GPU idle; such launches split every row into segments instead.
+constexpr int64_t kMinRowWgs = 128;
+// Split of a length-2^L transform over B rows: (row pass log2, column pass log2), the
+// column pass (2^l_col <= 64 points per column, in registers) empty when one workgroup
+// per row does the whole row.  Above 2^kSingleLog2 points the row pass is 2^kSplitLog2
+// (or 2^(L-6)) long; from 2^13 points with fewer than kMinRowWgs rows it is shortened
+// (to 2^kSplitLog2 points at least) until B 2^l_col reaches kMinRowWgs.
+inline void fwht_split(int64_t B, int L, int* l_row, int* l_col) {
+  int r = L;
+  if (L > kSingleLog2) r = L - 6 > kSplitLog2 ? L - 6 : kSplitLog2;
+  while (L >= 13 && (B << (L - r)) < kMinRowWgs && L - r < 6 && r - 1 >= kSplitLog2) --r;
   *l_row = r;
   *l_col = L - r;
 }
@@ -129,6 +137,14 @@ hipError_t launch_quant_u(const float* u, int64_t B, int64_t n_pad, void* uq, hi
 // accumulate: add to z_parts instead of storing (the second pass of a 5-8 bpw layer)
 hipError_t launch_gemv_lds(const glq_layer& layer, const void* uq, int64_t B, float* z_parts, hipStream_t stream,
                            bool accumulate = false);
+
+// Decode matmul for a few activation rows (4 <= B <= 16) on the matrix units: fp16
+// u in the prefill's fragment order (one 16-token block, with its row exponents),
+// z_parts [S][B][m_pad] with S = gemv_mfma_splits(n_pad, m_pad).
+bool gemv_mfma_supported(const glq_layer& layer);
+int gemv_mfma_splits(int64_t n_pad, int64_t m_pad);
+hipError_t launch_gemv_mfma(const glq_layer& layer, const half_t* u16, const int32_t* rexp, int64_t B, float* z_parts,
+                            hipStream_t stream, bool accumulate = false);
 
 // The whole linear for B = 1 in two launches (input RHT, decode matmul with the
 // LDS codebook and the row-local part of the output RHT; then the fixed-order

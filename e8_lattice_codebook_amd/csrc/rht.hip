@@ -126,6 +126,12 @@ struct SegLoad {
     const int64_t a = r & ((int64_t(1) << nseg_log2) - 1);
     return in(r >> nseg_log2, (a << seg_log2) + c);
   }
+  // a span never crosses a segment (R divides the segment length)
+  template <int R>
+  __device__ void load_span(int64_t r, int64_t c0, float (&v)[R]) const {
+    const int64_t a = r & ((int64_t(1) << nseg_log2) - 1);
+    load_elems<R>(in, r >> nseg_log2, (a << seg_log2) + c0, v);
+  }
 };
 template <class Inner>
 struct SegStore {
@@ -189,10 +195,10 @@ hipError_t run_cols(const Load& ld, const Store& st, int64_t B, int seg_log2, in
 // row pass into `mid` (rows of 2^L floats) and the column pass from it.
 template <class Load, class Store>
 hipError_t run_block(const Load& ld, const Store& st, int64_t B, int L, float* mid, hipStream_t stream) {
-  if (L <= kSingleLog2) return run_rows(ld, st, B, L, stream);
   const int64_t N = int64_t(1) << L;
   int lr, lc;
-  fwht_split(L, &lr, &lc);
+  fwht_split(B, L, &lr, &lc);
+  if (lc == 0) return run_rows(ld, st, B, L, stream);
   hipError_t e = run_rows(SegLoad<Load>{ld, lr, lc}, SegStore<StoreF32>{StoreF32{mid, N}, lr, lc}, B << lc, lr,
                           stream);
   if (e != hipSuccess) return e;
@@ -241,17 +247,40 @@ hipError_t rht_in_x(const void* x, int64_t B, int64_t n, int64_t N, const int8_t
 // One workgroup per row: m = max |x[b]| (fmax ignores NaN; poison, the sum of v - v,
 // is 0 or NaN and catches NaN and inf), then rexp[b] = frexp exponent of m + add,
 // add = ceil(log2 sqrt(n)) - 14, so that |u| <= ||x[b]|| <= sqrt(n) m < 2^(rexp + 14).
-template <class XT>
-__global__ __launch_bounds__(256) void row_exp_kernel(const XT* __restrict__ x, int64_t n, int add,
-                                                      int32_t* __restrict__ rexp) {
-  __shared__ float red[2][4];
+// With VEC the row is read as 16-byte vectors, VEC elements each, four loads in flight
+// per thread before any is used.
+template <class XT, int VEC>
+__global__ __launch_bounds__(1024) void row_exp_kernel(const XT* __restrict__ x, int64_t n, int add,
+                                                       int32_t* __restrict__ rexp) {
+  __shared__ float red[2][16];
   const int64_t b = blockIdx.x;
   const XT* xr = x + b * n;
+  const int nt = int(blockDim.x);
   float mx = 0.0f, poison = 0.0f;
-  for (int64_t i = threadIdx.x; i < n; i += 256) {
-    const float v = to_f32<XT>(xr[i]);
+  auto take = [&](float v) {
     mx = fmaxf(mx, fabsf(v));
     poison += v - v;
+  };
+  if constexpr (VEC > 1) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4* xv = reinterpret_cast<const u32x4*>(xr);
+    const int64_t nv = n / VEC;
+    for (int64_t i0 = threadIdx.x; i0 < nv; i0 += 4 * int64_t(nt)) {
+      u32x4 t[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t i = i0 + int64_t(k) * nt;
+        t[k] = xv[i < nv ? i : nv - 1];  // past the end: the last vector again (a repeat)
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const XT* e = reinterpret_cast<const XT*>(&t[k]);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) take(to_f32<XT>(e[j]));
+      }
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < n; i += nt) take(to_f32<XT>(xr[i]));
   }
   for (int off = 1; off < 64; off <<= 1) {
     mx = fmaxf(mx, __shfl_xor(mx, off, 64));
@@ -264,8 +293,12 @@ __global__ __launch_bounds__(256) void row_exp_kernel(const XT* __restrict__ x, 
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    poison = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    mx = 0.0f;
+    poison = 0.0f;
+    for (int w = 0; w < (nt >> 6); ++w) {
+      mx = fmaxf(mx, red[0][w]);
+      poison += red[1][w];
+    }
     rexp[b] = poison != 0.0f ? kRowExpNaN : mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) + add : 0;
   }
 }
@@ -304,7 +337,9 @@ hipError_t rht_in_tiled_x(const void* x, int64_t B, int64_t n, int64_t N, const 
     const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
     const LoadSignedXRow<XT> ld{LoadSignedX<XT>{static_cast<const XT*>(x), n, off, sign}, rexp};
     const StoreTiledHalf st{u16, uint32_t(N / 32), off, scale};
-    if (L < 3 || L > kSingleLog2) return run_block(ld, st, B, L, ws, stream);
+    int lr, lc;
+    fwht_split(B, L, &lr, &lc);
+    if (L < 3 || lc > 0) return run_block(ld, st, B, L, ws, stream);
     int threads = (1 << L) / 16;
     if (threads < 64) threads = 64;
     if (threads > 1024) threads = 1024;
@@ -448,7 +483,7 @@ template <class YT>
 hipError_t rht_out_block(const float* z, int64_t S, int64_t B, int64_t m, int64_t ldz, int64_t off, int L,
                          const int8_t* sign, void* y, float* ws, hipStream_t stream) {
   const float scale = float(1.0 / sqrt(double(int64_t(1) << L)));
-  if (L >= 12 && L <= 15) {
+  if (L >= 12 && L <= 15 && B >= kMinRowWgs) {
     const int64_t mv = m - off < (int64_t(1) << L) ? m - off : (int64_t(1) << L);
     // 16-byte output stores need y + off 16-byte aligned, mv % 8 == 0 and 8-byte aligned signs
     YT* yp = static_cast<YT*>(y) + off;
@@ -512,18 +547,31 @@ hipError_t launch_rht_in(const void* x, glq_dtype x_dt, int64_t B, int64_t n, in
   return hipErrorInvalidValue;
 }
 
+template <class XT>
+hipError_t row_exp_t(const void* x, int64_t B, int64_t n, int add, int32_t* rexp, hipStream_t stream) {
+  constexpr int VEC = 16 / int(sizeof(XT));
+  const bool vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (n % VEC == 0);
+  const int64_t items = vec ? n / VEC : n;
+  int threads = int(((items + 3) / 4 + 63) / 64 * 64);  // about four loads per thread
+  threads = threads < 64 ? 64 : threads > 1024 ? 1024 : threads;
+  const XT* xp = static_cast<const XT*>(x);
+  if (vec)
+    hipLaunchKernelGGL((row_exp_kernel<XT, VEC>), dim3(unsigned(B)), dim3(threads), 0, stream, xp, n, add, rexp);
+  else
+    hipLaunchKernelGGL((row_exp_kernel<XT, 1>), dim3(unsigned(B)), dim3(threads), 0, stream, xp, n, add, rexp);
+  return hipGetLastError();
+}
+
 hipError_t launch_row_exp(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int32_t* rexp, hipStream_t stream) {
   int c = 0;  // ceil(log2 sqrt(n))
   while ((int64_t(1) << (2 * c)) < n) ++c;
   const int add = c - 14;
-  const dim3 grid{unsigned(B)}, block{256};
   switch (x_dt) {
-    case GLQ_F32: hipLaunchKernelGGL(row_exp_kernel<float>, grid, block, 0, stream, static_cast<const float*>(x), n, add, rexp); break;
-    case GLQ_F16: hipLaunchKernelGGL(row_exp_kernel<half_t>, grid, block, 0, stream, static_cast<const half_t*>(x), n, add, rexp); break;
-    case GLQ_BF16: hipLaunchKernelGGL(row_exp_kernel<bf16_t>, grid, block, 0, stream, static_cast<const bf16_t*>(x), n, add, rexp); break;
-    default: return hipErrorInvalidValue;
+    case GLQ_F32: return row_exp_t<float>(x, B, n, add, rexp, stream);
+    case GLQ_F16: return row_exp_t<half_t>(x, B, n, add, rexp, stream);
+    case GLQ_BF16: return row_exp_t<bf16_t>(x, B, n, add, rexp, stream);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_rht_in_tiled(const void* x, glq_dtype x_dt, int64_t B, int64_t n, int64_t N, const int8_t* sign,

@@ -63,15 +63,23 @@ def test_workspace_queries():
     lib = _lib.load()
     assert lib.glq_codebook_pack_bytes(65536) >= 256 + 65536 * 8 + 151 * 1024
     assert lib.glq_codebook_pack_bytes(0) == 0
-    assert lib.glq_input_rht_workspace_bytes(2, 16384, 1) == 0
-    assert lib.glq_input_rht_workspace_bytes(2, 32768, 1) == 2 * 32768 * 4
-    assert lib.glq_input_rht_workspace_bytes(2, 32768, 0) == 0
-    assert lib.glq_output_rht_workspace_bytes(3, 16384) == 0
-    assert lib.glq_output_rht_workspace_bytes(3, 32768) == 3 * 32768 * 4
-    # block-diagonal lengths: scratch when a block is above 16384, also for fp32 u
-    assert lib.glq_input_rht_workspace_bytes(2, 16384 + 64, 1) == 0
-    assert lib.glq_input_rht_workspace_bytes(2, 32768 + 1024, 0) == 2 * (32768 + 1024) * 4
-    assert lib.glq_output_rht_workspace_bytes(3, 32768 + 64) == 3 * (32768 + 64) * 4
+    # one workgroup per row up to 16384 points when there are at least 128 rows
+    assert lib.glq_input_rht_workspace_bytes(128, 16384, 1) == 0
+    assert lib.glq_input_rht_workspace_bytes(128, 32768, 1) == 128 * 32768 * 4
+    assert lib.glq_input_rht_workspace_bytes(128, 32768, 0) == 0
+    assert lib.glq_output_rht_workspace_bytes(130, 16384) == 0
+    assert lib.glq_output_rht_workspace_bytes(130, 32768) == 130 * 32768 * 4
+    # fewer rows: rows of at least 8192 points are split into segments of 4096 or
+    # more (two passes through scratch) so that a launch has enough workgroups; fp32
+    # u of one block is its own scratch
+    assert lib.glq_input_rht_workspace_bytes(2, 16384, 1) == 2 * 16384 * 4
+    assert lib.glq_input_rht_workspace_bytes(2, 16384, 0) == 0
+    assert lib.glq_output_rht_workspace_bytes(3, 8192) == 3 * 8192 * 4
+    assert lib.glq_output_rht_workspace_bytes(3, 4096) == 0
+    # block-diagonal lengths: scratch when a block runs in two passes, also for fp32 u
+    assert lib.glq_input_rht_workspace_bytes(128, 16384 + 64, 1) == 0
+    assert lib.glq_input_rht_workspace_bytes(128, 32768 + 1024, 0) == 128 * (32768 + 1024) * 4
+    assert lib.glq_output_rht_workspace_bytes(130, 32768 + 64) == 130 * (32768 + 64) * 4
     assert lib.glq_input_rht_workspace_bytes(2, 100, 0) == 0   # not a transform length
     L = fake_layer(n=5120, n_pad=8192, m=32768, m_pad=32768, resid_bits=16)
     one = lib.glq_e8rht_linear_workspace_bytes(ctypes.byref(L), 1)
