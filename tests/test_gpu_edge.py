@@ -10,8 +10,11 @@ against the oracle at the path's tolerance.  Zero rows give zero outputs, outlie
 channels keep the tolerance, and a NaN or infinity in a row of x makes that row of
 y NaN (the oracle's y is NaN there too) without touching the other rows.
 
-Paths: B = 1 (the two-launch decode), B = 5 (the staged decode), M = 40 (prefill,
-the shared-tile kernel of slot codes and the per-wave kernel of codebook indices).
+Paths: B = 1 (the two-launch decode), B = 5 (the staged integer decode), M = 40
+(prefill, the shared-tile kernel of slot codes and the per-wave kernel of codebook
+indices), M = 160 (prefill with the persistent one-row-per-workgroup output
+transform), and B = 5 and 16 on a layer of 2^22 groups (2048 -> 16384: the decode on
+the matrix units, fp16 operands with row exponents).
 """
 import numpy as np
 import pytest
@@ -26,13 +29,22 @@ glq = pytest.importorskip("e8_lattice_codebook_amd")
 DEV = "cuda:0"
 
 N, M_OUT = 2048, 3000
-PATHS = [(1, "index"), (5, "index"), (1, "slot"), (5, "slot"), (40, "slot"), (40, "index")]
+PATHS = [(1, "index"), (5, "index"), (1, "slot"), (5, "slot"), (40, "slot"), (40, "index"),
+         (5, "slot-big"), (16, "index-big"), (160, "slot")]
+_LAYERS = {}
 
 
 def _layer(gpu_codebooks, fmt, resid_bits=8):
-    layer = synth.random_layer(N, M_OUT, resid_bits, seed=77 + resid_bits, n_pad=2048, m_pad=4096)
+    big = fmt.endswith("-big")
+    key = (big, resid_bits)
+    if key not in _LAYERS:
+        if big:  # 2048 -> 16384: 2^22 groups, the matrix-unit decode for 4 <= B <= 16
+            _LAYERS[key] = synth.random_layer(N, 16000, resid_bits, seed=78 + resid_bits, n_pad=2048, m_pad=16384)
+        else:
+            _LAYERS[key] = synth.random_layer(N, M_OUT, resid_bits, seed=77 + resid_bits, n_pad=2048, m_pad=4096)
+    layer = _LAYERS[key]
     ql = glq.QuantizedLayer.from_synth(layer, gpu_codebooks)
-    return layer, (ql.to_slot_codes() if fmt == "slot" else ql)
+    return layer, (ql.to_slot_codes() if fmt.startswith("slot") else ql)
 
 
 def _tol(B):
@@ -53,7 +65,10 @@ def _run(ql, x32):
 @pytest.mark.parametrize("B,fmt", PATHS)
 def test_power_of_two_scaling(gpu_codebooks, B, fmt):
     layer, ql = _layer(gpu_codebooks, fmt)
-    x = np.random.default_rng(B).standard_normal((B, N)).astype(np.float32)
+    x = np.random.default_rng(B).standard_normal((B, N))
+    # no element below 2^-5 in magnitude, so that x 2^-120 is still a normal fp32 number
+    # and every scaled input is exactly 2^k x
+    x = np.where(np.abs(x) < 2.0 ** -5, np.copysign(2.0 ** -5, x), x).astype(np.float32)
     y0 = _run(ql, x)
     want = _oracle(layer, x.astype(np.float64))
     assert rel_frob(y0, want) <= _tol(B)
