@@ -1,8 +1,9 @@
 // Host construction of the E8 codebook table (glq_e8_codebook).
 //
-// glq 0.5.1 (PyPI project page), "How it works", item 1: 65,536 vectors from the
-// first seven shells of the E8 lattice, one 16-bit index per 8-weight group;
-// "Inference kernels": the 1 MB (fp16) codebook.  E8 = D8 u (D8 + 1/2): all
+// glq 0.5.1 (PyPI project page), "How it works", item 1: the table has 2^16 points
+// of E8, the lattice points of smallest norm up to the seventh norm value counting
+// the origin, addressed by a 16-bit index per group of 8 weights; "Inference
+// kernels": stored in fp16 the table takes 1 MB.  E8 = D8 u (D8 + 1/2): all
 // coordinates integers or all half-integers, with an even coordinate sum.
 //
 // Points are enumerated by depth-first search on doubled coordinates t = 2v

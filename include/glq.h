@@ -426,8 +426,9 @@ glq_status glq_e8rht_linear_noalloc(const glq_layer* layer, const void* x, glq_d
 /*
  * glq_e8kv_attention_decode — one decode step of attention over an E8-compressed
  * paged K/V cache, the cache dequantized inside the kernel (Glq v0.5.0 release
- * notes, "Highlights": no decompress-to-workspace pass, an 8-point FHT butterfly
- * for the inverse Hadamard, flash-decoding split of long contexts).
+ * notes, "Highlights": the cache is never expanded into a separate buffer, a
+ * length-8 Hadamard transform inverts the rotation, long contexts are split over
+ * workgroups as in flash decoding).
  *   out[b][hq] = softmax_t(sm_scale q[b][hq] . K_t) . V_t over the tokens
  *   t < seq_lens[b] of sequence b, with K_t, V_t the vectors of KV head
  *   hq / (num_q_heads / num_kv_heads) at slot t mod page_size of page

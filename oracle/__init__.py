@@ -8,8 +8,8 @@ anything in here, and nothing in here imports the product path.
 
 Sources (the "glq" project pages):
   * glq 0.5.1 (PyPI project page), section "How it works", items 1, 2 and 4:
-    65,536-entry E8 codebook from the first seven shells, one 16-bit index per
-    8-weight group, 8-bit (256-entry) or 16-bit residual stages, randomized
+    a codebook of 2^16 innermost E8 points addressed by one 16-bit index per group
+    of 8 weights, 8-bit (256-entry) or 16-bit residual stages, randomized
     Hadamard transform = random sign flips followed by a fast Walsh-Hadamard
     transform, matmul taken against the indices without forming W.
   * same page, table "Bit widths": bpw -> stages; one global scale per layer.

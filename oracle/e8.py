@@ -1,8 +1,8 @@
 """E8 lattice codebook by enumeration (oracle; test infrastructure only).
 
-glq 0.5.1 (PyPI project page), "How it works", item 1: the codebook holds 65,536
-vectors in 8 dimensions taken from the first seven shells of the E8 lattice; an
-8-weight group is one 16-bit index into it.  "Inference kernels" and "How it
+glq 0.5.1 (PyPI project page), "How it works", item 1: the codebook is 2^16 points
+of the 8-dimensional E8 lattice, the innermost ones (norm values 0 up to the
+seventh), and each group of 8 weights is stored as a 16-bit index into it.  "Inference kernels" and "How it
 works", item 4, put the codebook at 1 MB, i.e. 65,536 x 8 fp16 values.
 
 E8 (Conway & Sloane, cited in the page's "Acknowledgments") is the union of

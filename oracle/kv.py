@@ -4,9 +4,9 @@ Glq v0.5.0 release notes, "Highlights" and "Scope"; glq 0.5.1 (PyPI project page
 "KV cache compression" -> "E8 lattice cache" and "Inline-dequant E8 KV": the paged
 K/V cache is compressed with the same E8 lattice quantizer as the weights to about
 a quarter of its fp16 size (the 4 bpw recipe e8_relaxed:2), and a decode attention
-kernel dequantizes it inside its tile loop, undoing the Hadamard rotation with an
-8-point FHT butterfly and splitting long contexts over workgroups
-(flash-decoding).
+kernel expands it inside its tile loop, inverting the per-group rotation with a
+radix-2 Hadamard transform of length 8 and spreading long contexts over
+workgroups (flash-decoding).
 
 Readings (listed in the design notes; the pages fix none of these details):
   * a cached K or V vector of head_dim D is D/8 groups of 8; group g is rotated by

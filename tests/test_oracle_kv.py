@@ -1,7 +1,7 @@
 """Pins of the E8 KV-cache decode attention oracle (oracle/kv.py).
 
-Glq v0.5.0 release notes, "Highlights": compressed K/V dequantized in the
-attention tile loop with an 8-point FHT butterfly undoing the Hadamard rotation;
+Glq v0.5.0 release notes, "Highlights": compressed K/V expanded inside the
+attention tile loop, a length-8 Hadamard transform inverting the rotation;
 glq 0.5.1, "KV cache compression" (E8 lattice cache, the e8_relaxed:2 recipe).
 Each pin holds independently of the oracle's own code: hand-derived groups, the
 scipy Hadamard matrix, closed forms of softmax attention (one token, equal
