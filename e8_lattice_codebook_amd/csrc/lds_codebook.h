@@ -263,6 +263,18 @@ __device__ __forceinline__ void load_image_1024(uint32_t* lds, const uint32_t* _
   image_store<0, 10, true, RESID>(r, lds, tid);
 }
 
+// sum of the eight signed 4-bit products of a and b, starting from zero: the VOP3P
+// form with an inline-constant accumulator (the compiler otherwise zeroes a register
+// for the accumulating VOP2 form)
+__device__ __forceinline__ int sdot8_zero(uint32_t a, uint32_t b) {
+  int r;
+  asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ int sdot8_acc(uint32_t a, uint32_t b, int c, bool first) {
+  return first ? sdot8_zero(a, b) : __builtin_amdgcn_sdot8(int(a), int(b), c, false);
+}
+
 // ---- one row-step: the lane's GL groups against NB activation rows -------------------
 // v[b] = T0 + sr * T1 with T_k = sum over the lane's columns of 2 c_k U (exact
 // integers, converted once to fp32): stage-0 codewords from the primary image,
@@ -332,8 +344,7 @@ __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& 
     for (int b = 0; b < NB; ++b) {
       acc0[b][0] = __mul24(m, gs[b][q]) + (q == 0 ? 0 : acc0[b][0]);
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-        acc0[b][p] = __builtin_amdgcn_sdot8(int(n), int(dig[b][q][p]), (q == 0 && p > 0) ? 0 : acc0[b][p], false);
+      for (int p = 0; p < 4; ++p) acc0[b][p] = sdot8_acc(n, dig[b][q][p], acc0[b][p], q == 0 && p > 0);
     }
     if (RESID == 16) {
       const uint32_t n1 = n1w_[q] ^ m1[q];
@@ -341,16 +352,14 @@ __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& 
       for (int b = 0; b < NB; ++b) {
         acc1[b][0] = __mul24(int32_t(m1[q]), gs[b][q]) + (q == 0 ? 0 : acc1[b][0]);
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-          acc1[b][p] = __builtin_amdgcn_sdot8(int(n1), int(dig[b][q][p]), (q == 0 && p > 0) ? 0 : acc1[b][p], false);
+        for (int p = 0; p < 4; ++p) acc1[b][p] = sdot8_acc(n1, dig[b][q][p], acc1[b][p], q == 0 && p > 0);
       }
     }
     if (RESID == 8) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-          acc1[b][p] = __builtin_amdgcn_sdot8(int(n1w_[q]), int(dig[b][q][p]), q == 0 ? 0 : acc1[b][p], false);
+        for (int p = 0; p < 4; ++p) acc1[b][p] = sdot8_acc(n1w_[q], dig[b][q][p], acc1[b][p], q == 0);
       }
     }
   }
@@ -397,8 +406,7 @@ __device__ __forceinline__ int stage16_total(const uint32_t* lds, const IdxRow<G
     const uint32_t n = nw[q] ^ mm[q];
     acc[0] = __mul24(int32_t(mm[q]), gs[0][q]) + (q == 0 ? 0 : acc[0]);
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-      acc[p] = __builtin_amdgcn_sdot8(int(n), int(dig[0][q][p]), (q == 0 && p > 0) ? 0 : acc[p], false);
+    for (int p = 0; p < 4; ++p) acc[p] = sdot8_acc(n, dig[0][q][p], acc[p], q == 0 && p > 0);
   }
   return ((acc[3] * 16 + acc[2]) * 16 + acc[1]) * 16 + acc[0];
 }
@@ -424,7 +432,7 @@ __device__ __forceinline__ int stage8_total(const uint32_t* lds, const Idx8Row<G
 #pragma unroll
   for (int q = 0; q < GL; ++q)
 #pragma unroll
-    for (int p = 0; p < 4; ++p) acc[p] = __builtin_amdgcn_sdot8(int(nw[q]), int(dig[0][q][p]), q == 0 ? 0 : acc[p], false);
+    for (int p = 0; p < 4; ++p) acc[p] = sdot8_acc(nw[q], dig[0][q][p], acc[p], q == 0);
   return ((acc[3] * 16 + acc[2]) * 16 + acc[1]) * 16 + acc[0];
 }
 
