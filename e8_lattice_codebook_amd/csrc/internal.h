@@ -63,7 +63,12 @@ template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) {
 
 template <class T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
-template <> __device__ __forceinline__ half_t from_f32<half_t>(float v) { return (half_t)v; }
+template <> __device__ __forceinline__ half_t from_f32<half_t>(float v) {
+  // v rounded to fp32 first: the empty constraint keeps the compiler from fusing the
+  // product that made v into a mixed-precision FMA rounded once to fp16
+  asm("" : "+v"(v));
+  return (half_t)v;
+}
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
   // nearest, ties to even (finite values)
   uint32_t b = __float_as_uint(v);

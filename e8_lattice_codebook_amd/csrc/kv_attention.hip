@@ -110,40 +110,75 @@ __device__ __forceinline__ void word_pairs(uint32_t w, uint32_t m, half2v (&p)[4
     p[k] = __builtin_bit_cast(half2v, ((t >> (4 * k)) & 0x000F000Fu) | 0x64006400u) + bias;
 }
 
-__device__ __forceinline__ float dpp_max(float v, int ctrl_sel) {
-  int r;
-  const int x = __float_as_int(v);
-  switch (ctrl_sel) {
-    case 0: r = __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false); break;
-    case 1: r = __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false); break;
-    case 2: r = __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false); break;
-    case 3: r = __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false); break;
-    case 4: r = __builtin_amdgcn_update_dpp(x, x, 0x142, 0xA, 0xF, false); break;
-    default: r = __builtin_amdgcn_update_dpp(x, x, 0x143, 0xC, 0xF, false); break;
-  }
-  return fmaxf(v, __int_as_float(r));
+// Over the four rows of 16 lanes (lanes l, l ^ 16, l ^ 32, l ^ 48): the max / sum in
+// every lane, the same operands in the same order in each (the swaps exchange odd and
+// even rows, then the halves of the wave)
+__device__ __forceinline__ float xq_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float xq_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// the max / sum over the 64 lanes, valid in lane 63
-__device__ __forceinline__ float wave_max63(float v) {
+// The codeword of stored value c (both stages combined) as 8 fp16: 2c0 + s_r 2c1
+template <int ST, bool CODES>
+__device__ __forceinline__ void kv_codeword(const uint32_t* img, uint32_t c0, uint32_t c1, uint32_t delta,
+                                            half2v rs2, half2v (&p)[4]) {
+  uint32_t m;
+  word_pairs(kv_word<CODES>(img, c0, delta, m), m, p);
+  if (ST == 2) {
+    half2v p1[4];
+    word_pairs(kv_word<CODES>(img, c1, delta, m), m, p1);
 #pragma unroll
-  for (int k = 0; k < 6; ++k) v = dpp_max(v, k);
-  return v;
+    for (int j = 0; j < 4; ++j) p[j] = p1[j] * rs2 + p[j];
+  }
 }
 
-template <int D, int G, int ST, bool CODES>
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+
+// Each wave streams its own tiles of 16 tokens of the unit (tiles wave, wave + 8, ...)
+// with its own online softmax; no barrier separates the phases of a tile.  Lane l is
+// (c, q) = (l mod 16, l / 16).
+//  - scores: one MFMA 16 x 16 x 32 per k-step of 32 dimensions, A = the tile's tokens
+//    (rows) x dimensions, B = dimensions x the query heads (columns, zero past G).  At
+//    k-step ks lane (c, q) holds group q KS + ks of token c, so its KS k-steps read KS
+//    consecutive groups; the query fragments match.  D gives lane (c, q) head c for
+//    tokens 4q .. 4q + 3.
+//  - softmax: per head, the max of the lane's four scores and then over the four rows
+//    of lanes; the running max and exp-sum updated, p = exp(s - max) (0 past the unit).
+//  - V: O^T += V^T W^T as GPS / 2 MFMAs 16 x 16 x 16: A = 16 rows of V's columns x the
+//    tile's tokens, B = tokens x heads, W the weights p s_v / 2.  Lane (c, q) decodes
+//    group c mod GPS of tokens 4q .. 4q + 3 (all 8 coordinates; with D = 64 row c
+//    takes coordinates 4 (c / 8) .. + 3) and already holds W for head c and those
+//    tokens: no lane exchange.  D gives lane (c, q) head c for the 4 V columns 4q + i
+//    of each MFMA, so the rescaling of the sums by exp(max_old - max_new) is the
+//    lane's own.  W is fp16 (p <= 1, rounded once); the V scales are taken relative to
+//    a running power of two 2^e (the largest scale's exponent so far), which is folded
+//    into the rescaling, so W stays in (0, 1/2].
+// At the end of the unit the waves are merged in wave order (max, sum and V sums
+// rescaled to the common max) in LDS.
+// BIG: pages of 16 tokens or more, so a tile (16 aligned tokens) lies on one page and
+// its rows are one uniform row plus per-lane constants.
+template <int D, int G, int ST, bool CODES, bool BIG>
 __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
-  constexpr int GPS = D / 8;          // groups per vector
-  constexpr int TPV = 64 / GPS;       // V phase: tokens per wave instruction (lane = token x group)
+  constexpr int GPS = D / 8;  // groups per vector
+  constexpr int KS = D / 32;  // score k-steps per vector
+  constexpr int NK = GPS / 2; // V MFMAs per tile: 16 columns each, D in all
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-  static_assert(G * D <= kKvBuf && G * GPS * 5 <= kKvBuf, "query staging fits");
+  static_assert(G * D <= kKvBuf && G * (D + 2) <= kKvBuf, "query staging and the wave merge fit");
 
   __shared__ __attribute__((aligned(16))) uint32_t img[kImageMaxDwords];
   __shared__ __attribute__((aligned(16))) float buf[kKvBuf];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the tile loop branches on it
   {
     // every load of the image in flight before the first store (clamped addresses:
     // a thread past the end rewrites the last uint4 with the value found there)
@@ -165,10 +200,16 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
     if (ti < nd) img[ti] = tail;
   }
   const uint32_t delta = CODES ? slot_delta(a.pack_hdr) : 0u;
-  const int vt = lane / GPS;                // V phase: token of the lane in a batch
-  const int vg = lane % GPS;                // V phase: group of the lane
+  const int c = lane & 15, q = lane >> 4;
+  const int vg = c % GPS;  // V: the lane's group
+  const int vh = c / GPS;  // V with D = 64: the half of the group's coordinates
   const int P = 1 << a.lp;
-  const float rs = a.resid_scale;
+  const half2v rs2 = half2v{_Float16(a.resid_scale), _Float16(a.resid_scale)};
+  // per-lane offsets from a tile's first row (BIG): K token c, V / scale tokens 4q + i
+  const int koff = c * a.Hkv * GPS + q * KS;
+  const int voff = 4 * q * a.Hkv * GPS + vg;
+  const int soff = 4 * q * a.Hkv;
+  const int vstep = a.Hkv * GPS, sstep = a.Hkv;
   __syncthreads();
 
   for (int unit = blockIdx.x; unit < a.units; unit += gridDim.x) {
@@ -181,13 +222,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
     if (t0 >= L) continue;  // the same for the whole workgroup
     const int nt_unit = min(a.T, L - t0);
     const int32_t* bt = a.block_table + int64_t(b) * a.bt_stride;
-    // row of token t: (page, slot, head); rows * D / 8 < 2^31 (checked by the caller)
-    auto row_of = [&](int t) {
-      const int pg = min(max(bt[t >> a.lp], 0), a.num_pages - 1);
-      return (pg * P + (t & (P - 1))) * a.Hkv + h;
-    };
 
-    // ---- the G query heads of h: q' = H8 q_g / sqrt(8) * sm_scale, as fp16 pairs
+    // ---- the G query heads of h: q' = H8 q_g / sqrt(8) * sm_scale
     const int64_t qbase = (int64_t(b) * a.Hkv + h) * G * D;
     for (int i = tid; i < G * D; i += kKvThreads) buf[i] = q_value(a.q, a.q_dt, qbase + i);
     __syncthreads();
@@ -207,202 +243,219 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
       for (int j = 0; j < 8; ++j) buf[tid * 8 + j] = qv[j];
     }
     __syncthreads();
-    // the scores are an MFMA 16 x 16 x 32 per k-step of 32 dimensions: A = the query
-    // heads (rows, zero past G) x dimensions, B = dimensions x 16 tokens, one codeword
-    // (8 dimensions of one token) per lane; lane l holds A row l mod 16, dimensions
-    // 8 (l / 16) .. + 7 of each k-step
-    constexpr int KS = D / 32;
-    half8 qa[KS];
-    {
-      const int hr = lane & 15;
+    half8 qb[KS];  // lane (c, q): head c, k-step ks: group q KS + ks
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        half8 v;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          v[j] = hr < G ? _Float16(buf[hr * D + ks * 32 + 8 * (lane >> 4) + j]) : _Float16(0.0f);
-        qa[ks] = v;
-      }
-    }
-    __syncthreads();  // buf becomes the chunk's scores [T][G]
-
-    // ---- the unit's tokens in sub-chunks of TS: scores, an online softmax (running
-    // max and exp-sum per head, the V sums rescaled when the max grows), V sums
-    // V: lane (token of the batch, group) sums its group of V, both stages combined
-    // exactly in fp16, over the wave's tokens; at the end of the unit the lanes of a
-    // group and then the waves are added.
-    float o[G][8];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[g][j] = 0.0f;
-    float m_run = -INFINITY, l_run = 0.0f;  // wave g < G: head g's running statistics
-    // Loads run ahead of their use: the next sub-chunk's K indices are issued once
-    // this one's scores are done (in flight during its softmax and V), its V indices
-    // once this one's V is done (in flight during the next scores).  A wave's KBV
-    // batches (wave, wave + 8, ...) cover a sub-chunk of up to 256 tokens; slots past
-    // it load a valid row and are not used.
-    constexpr int KBV = 256 / TPV / kKvWaves;
-    auto load_v = [&](int ts0, int nt, uint32_t (&c)[KBV][ST], float (&sv)[KBV]) {
-      int rows[KBV];
-#pragma unroll
-      for (int k = 0; k < KBV; ++k) {
-        const int tt = (wave + k * kKvWaves) * TPV + vt;
-        rows[k] = row_of(ts0 + (tt < nt ? tt : 0));
-      }
-#pragma unroll
-      for (int k = 0; k < KBV; ++k) {
-        c[k][0] = a.v0[rows[k] * GPS + vg];
-        if (ST == 2) c[k][ST - 1] = a.v1[rows[k] * GPS + vg];
-        sv[k] = a.vs[rows[k]];
-      }
-    };
-    // K: a wave takes token blocks wave, wave + 8, ... of 16 tokens; lane l loads
-    // token l mod 16's group 4 ks + l / 16 of every k-step ks, both stages
-    constexpr int KTB = 256 / 16 / kKvWaves;
-    const int ktok = lane & 15, kq = lane >> 4;
-    auto load_k = [&](int ts0, int nt, uint32_t (&c)[KTB][KS][ST], float (&sv)[KTB]) {
-      int rows[KTB];
-#pragma unroll
-      for (int k = 0; k < KTB; ++k) {
-        const int tt = (wave + k * kKvWaves) * 16 + ktok;
-        rows[k] = row_of(ts0 + (tt < nt ? tt : 0));
-      }
-#pragma unroll
-      for (int k = 0; k < KTB; ++k) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          c[k][ks][0] = a.k0[rows[k] * GPS + ks * 4 + kq];
-          if (ST == 2) c[k][ks][ST - 1] = a.k1[rows[k] * GPS + ks * 4 + kq];
-        }
-        sv[k] = a.ks[rows[k]];
-      }
-    };
-    uint32_t kc[KTB][KS][ST], vc[KBV][ST];
-    float kks[KTB], vvs[KBV];
-    load_k(t0, min(a.TS, nt_unit), kc, kks);
-    load_v(t0, min(a.TS, nt_unit), vc, vvs);
-    const half2v rs2 = half2v{_Float16(rs), _Float16(rs)};
-    for (int sc = 0; sc < nt_unit; sc += a.TS) {
-      const int nt = min(a.TS, nt_unit - sc);
-
-      // K: scores 0.5 s_k q' . (2 c0 + s_r 2 c1) of the sub-chunk's tokens, by MFMA
-      // (2c0 + s_r 2c1 is exact in fp16 for s_r = 1/4: multiples of 1/4 below 8)
-#pragma unroll
-      for (int k = 0; k < KTB; ++k) {
-        const int tb = wave + k * kKvWaves;
-        if (tb * 16 >= nt) break;  // the same for the whole wave
-        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          uint32_t m;
-          half2v p0[4];
-          word_pairs(kv_word<CODES>(img, kc[k][ks][0], delta, m), m, p0);
-          if (ST == 2) {
-            half2v p1[4];
-            word_pairs(kv_word<CODES>(img, kc[k][ks][ST - 1], delta, m), m, p1);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) p0[j] = p1[j] * rs2 + p0[j];
-          }
-          const half8 bk = half8{p0[0].x, p0[0].y, p0[1].x, p0[1].y, p0[2].x, p0[2].y, p0[3].x, p0[3].y};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[ks], bk, acc, 0, 0, 0);
-        }
-        const int tt = tb * 16 + ktok;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int hh = 4 * kq + i;
-          if (hh < G && tt < a.TS) buf[tt * G + hh] = tt < nt ? acc[i] * 0.5f * kks[k] : -INFINITY;
-        }
-      }
-      const int sc2 = sc + a.TS < nt_unit ? sc + a.TS : sc;  // past the unit: this one again, unused
-      load_k(t0 + sc2, min(a.TS, nt_unit - sc2), kc, kks);
-      __syncthreads();
-
-      // softmax statistics, one wave per head: p = exp(s - m_new), the factor
-      // exp(m_run - m_new) for what was summed before (0 on the first sub-chunk)
-      if (wave < G) {
-        float mx = -INFINITY;
-        for (int tt = lane; tt < nt; tt += 64) mx = fmaxf(mx, buf[tt * G + wave]);
-        mx = __shfl(wave_max63(mx), 63, 64);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __expf(m_run - m_new);
-        float sum = 0.0f;
-        for (int tt = lane; tt < nt; tt += 64) {
-          const float pv = __expf(buf[tt * G + wave] - m_new);
-          buf[tt * G + wave] = pv;
-          sum += pv;
-        }
-        sum = __shfl(lane_reduce(sum, 6), 63, 64);
-        l_run = l_run * alpha + sum;
-        m_run = m_new;
-        if (lane == 0) buf[kKvBuf - 8 + wave] = alpha;
-      }
-      __syncthreads();
-
-      // V: o += p_t * 0.5 s_v * (2c0 + s_r 2c1) over the wave's tokens
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float al = buf[kKvBuf - 8 + g];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[g][j] *= al;
-      }
-      const int vbatches = (nt + TPV - 1) / TPV;
-#pragma unroll
-      for (int k = 0; k < KBV; ++k) {
-        const int bi = wave + k * kKvWaves;
-        if (bi >= vbatches) break;
-        const int tt = bi * TPV + vt;
-        const bool valid = tt < nt;
-        const int ts = valid ? tt : 0;
-        uint32_t m;
-        half2v p0[4];
-        word_pairs(kv_word<CODES>(img, vc[k][0], delta, m), m, p0);
-        if (ST == 2) {
-          half2v p1[4];
-          word_pairs(kv_word<CODES>(img, vc[k][ST - 1], delta, m), m, p1);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) p0[j] = p1[j] * rs2 + p0[j];
-        }
-        const float f = 0.5f * vvs[k];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float sv = valid ? buf[ts * G + g] * f : 0.0f;
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            o[g][2 * kk] = fmaf(sv, float(p0[kk].x), o[g][2 * kk]);
-            o[g][2 * kk + 1] = fmaf(sv, float(p0[kk].y), o[g][2 * kk + 1]);
-          }
-        }
-      }
-      load_v(t0 + sc2, min(a.TS, nt_unit - sc2), vc, vvs);
-      __syncthreads();  // the next sub-chunk overwrites the scores
-    }
-
-    // ---- the unit's results: statistics; V sums over the lanes of a group (the
-    // lane bits above the group), then over the waves in wave order in LDS
-    if (wave < G && lane == 63) {
-      a.part_ml[(int64_t(unit) * G + wave) * 2 + 0] = m_run;
-      a.part_ml[(int64_t(unit) * G + wave) * 2 + 1] = l_run;
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int ks = 0; ks < KS; ++ks) {
+      half8 v;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
+        v[j] = c < G ? _Float16(buf[c * D + (q * KS + ks) * 8 + j]) : _Float16(0.0f);
+      qb[ks] = v;
+    }
+    __syncthreads();  // buf is free until the wave merge
+
+    // ---- the wave's tiles.  A tile's rows take two dependent loads (the block table,
+    // then the indices), so each is issued well before its use: the pages of tile
+    // i + 2 and the indices of tile i + 1 are in flight while tile i is processed.
+    // Tiles past the wave's last load a valid tile again and are not used.
+    const int ntiles = (nt_unit + 15) >> 4;
+    struct TilePages {
+      int32_t pk, pv[4];  // BIG: pk alone, the tile's page
+      int tk, tv[4];      // tokens of the unit (small pages: token 0 past its end)
+    };
+    struct TileIdx {
+      uint32_t k0[KS], k1[KS];  // K: the lane's KS groups of token c, per stage
+      uint32_t v0[4], v1[4];    // V: group vg of tokens 4q + i, per stage
+      float ksc[4], vsc[4];     // scales of tokens 4q + i
+    };
+    auto load_pages = [&](int j, TilePages& tp) {
+      const int jj = j < ntiles ? j : ntiles - 1;
+      if constexpr (BIG) {
+        tp.tk = t0 + jj * 16;
+        tp.pk = bt[tp.tk >> a.lp];
+      } else {
+        const int tk = jj * 16 + c;
+        tp.tk = t0 + (tk < nt_unit ? tk : 0);
+        tp.pk = bt[tp.tk >> a.lp];
 #pragma unroll
-        for (int bit = GPS; bit < 64; bit <<= 1) o[g][j] += __shfl_xor(o[g][j], bit, 64);
+        for (int i = 0; i < 4; ++i) {
+          const int tv = jj * 16 + 4 * q + i;
+          tp.tv[i] = t0 + (tv < nt_unit ? tv : 0);
+          tp.pv[i] = bt[tp.tv[i] >> a.lp];
+        }
+      }
+    };
+    // row of token t on page entry pg: (page, slot, head); rows * D / 8 < 2^31 (checked by
+    // the caller)
+    auto row_at = [&](int32_t pg, int t) {
+      pg = min(max(pg, 0), a.num_pages - 1);
+      return (pg * P + (t & (P - 1))) * a.Hkv + h;
+    };
+    auto load_idx = [&](const TilePages& tp, TileIdx& ti) {
+      if constexpr (BIG) {
+        // the tile's first row, uniform; the lanes' rows are fixed offsets from it
+        const int64_t r0 = row_at(__builtin_amdgcn_readfirstlane(tp.pk), tp.tk);
+        const uint16_t* pk0 = a.k0 + r0 * GPS + koff;
+        const uint16_t* pk1 = a.k1 + r0 * GPS + koff;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          ti.k0[ks] = pk0[ks];
+          ti.k1[ks] = ST == 2 ? uint32_t(pk1[ks]) : 0u;
+        }
+        const uint16_t* pv0 = a.v0 + r0 * GPS + voff;
+        const uint16_t* pv1 = a.v1 + r0 * GPS + voff;
+        const float* pks = a.ks + r0 + soff;
+        const float* pvs = a.vs + r0 + soff;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ti.v0[i] = pv0[i * vstep];
+          ti.v1[i] = ST == 2 ? uint32_t(pv1[i * vstep]) : 0u;
+          ti.ksc[i] = pks[i * sstep];
+          ti.vsc[i] = pvs[i * sstep];
+        }
+      } else {
+        const int rk = row_at(tp.pk, tp.tk);
+        const uint16_t* pk0 = a.k0 + int64_t(rk) * GPS + q * KS;
+        const uint16_t* pk1 = a.k1 + int64_t(rk) * GPS + q * KS;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          ti.k0[ks] = pk0[ks];
+          ti.k1[ks] = ST == 2 ? uint32_t(pk1[ks]) : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rv = row_at(tp.pv[i], tp.tv[i]);
+          ti.v0[i] = a.v0[int64_t(rv) * GPS + vg];
+          ti.v1[i] = ST == 2 ? uint32_t(a.v1[int64_t(rv) * GPS + vg]) : 0u;
+          ti.ksc[i] = a.ks[rv];
+          ti.vsc[i] = a.vs[rv];
+        }
+      }
+    };
+
+    floatx4 oacc[NK];  // lane (c, q): head c, V columns 4q + i of MFMA k
+#pragma unroll
+    for (int k = 0; k < NK; ++k) oacc[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.0f;  // head c; the same in the lanes of a column
+    int e_run = 0;                          // the V sums are in units of 2^(e_run - 126)
+
+    // one tile: scores, the online softmax, V (ti holds tile j's indices)
+    auto process = [&](const TileIdx& ti, int j) {
+      floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        half2v pk[4];
+        kv_codeword<ST, CODES>(img, ti.k0[ks], ti.k1[ks], delta, rs2, pk);
+        const half8 ak = half8{pk[0].x, pk[0].y, pk[1].x, pk[1].y, pk[2].x, pk[2].y, pk[3].x, pk[3].y};
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qb[ks], sacc, 0, 0, 0);
+      }
+      const int tb = j * 16 + 4 * q;  // the unit's index of the lane's first token
+      bool ok[4];
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ok[i] = tb + i < nt_unit;
+        sv[i] = ok[i] ? sacc[i] * (0.5f * ti.ksc[i]) : -INFINITY;
+      }
+      // a tile holds at least one token of the unit, so the max is finite
+      const float m_new = fmaxf(m_run, xq_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))));
+      const float alpha = __expf(m_run - m_new);  // 0 on the wave's first tile
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __expf(sv[i] - m_new);
+      l_run = l_run * alpha + xq_sum((p[0] + p[1]) + (p[2] + p[3]));
+      m_run = m_new;
+      // the V scales' running exponent: the biased exponent of the largest |s_v| so far
+      float vm = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vm = ok[i] ? fmaxf(vm, fabsf(ti.vsc[i])) : vm;
+      const int e_new = max(e_run, int(__float_as_uint(xq_max(vm)) >> 23));
+      const float r = ldexpf(alpha, e_run - e_new);
+      e_run = e_new;
+      half4v wb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wb[i] = _Float16(ok[i] ? ldexpf(p[i] * (0.5f * ti.vsc[i]), 126 - e_new) : 0.0f);
+#pragma unroll
+      for (int k = 0; k < NK; ++k) oacc[k] *= r;
+      // V: group vg of the lane's 4 tokens, coordinate k (+ 4 vh) per MFMA
+      half2v cw[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kv_codeword<ST, CODES>(img, ti.v0[i], ti.v1[i], delta, rs2, cw[i]);
+      if constexpr (D == 64) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const half2v lo0 = cw[i][0], lo1 = cw[i][1];
+          cw[i][0] = vh ? cw[i][2] : lo0;
+          cw[i][1] = vh ? cw[i][3] : lo1;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const int pr = k >> 1;
+        const half4v va = (k & 1) ? half4v{cw[0][pr].y, cw[1][pr].y, cw[2][pr].y, cw[3][pr].y}
+                                  : half4v{cw[0][pr].x, cw[1][pr].x, cw[2][pr].x, cw[3][pr].x};
+        oacc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, wb, oacc[k], 0, 0, 0);
+      }
+    };
+    // two buffers of each kind, used in turn (the loop is unrolled by two, so no
+    // buffer is copied: a copy would wait for the loads in flight into it).  The
+    // scheduling barriers keep the loads in the same issue order (pages, then indices)
+    // before the loop as at its back edge, so the counted waits at the top of the loop
+    // leave the newer loads in flight.
+    TilePages pa, pb;
+    TileIdx ia, ib;
+    load_pages(wave, pa);
+    load_pages(wave + kKvWaves, pb);
+    __builtin_amdgcn_sched_barrier(0);
+    load_idx(pa, ia);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int j = wave; j < ntiles; j += 2 * kKvWaves) {
+      load_pages(j + 2 * kKvWaves, pa);
+      __builtin_amdgcn_sched_barrier(0);
+      load_idx(pb, ib);
+      __builtin_amdgcn_sched_barrier(0);
+      process(ia, j);
+      if (j + kKvWaves >= ntiles) break;
+      load_pages(j + 3 * kKvWaves, pb);
+      __builtin_amdgcn_sched_barrier(0);
+      load_idx(pa, ia);
+      __builtin_amdgcn_sched_barrier(0);
+      process(ib, j + kKvWaves);
+    }
+
+    // ---- the waves merged in wave order: O [G][D], then M [G], L [G] in buf.  A wave
+    // without tokens has max -inf and adds nothing; wave 0 always has the first tile.
+    float* bO = buf;
+    float* bM = buf + G * D;
+    float* bL = bM + G;
     for (int ww = 0; ww < kKvWaves; ++ww) {
-      if (wave == ww && lane < GPS) {
+      if (wave == ww && c < G) {
+        const float M0 = ww == 0 ? -INFINITY : bM[c];
+        const float Mn = fmaxf(M0, m_run);
+        const float a0 = ww == 0 ? 0.0f : __expf(M0 - Mn);
+        const float a1 = m_run == -INFINITY ? 0.0f : __expf(m_run - Mn);
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int k = 0; k < NK; ++k)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            float* d = &buf[g * D + lane * 8 + j];
-            *d = ww == 0 ? o[g][j] : *d + o[g][j];
+          for (int i = 0; i < 4; ++i) {
+            const int n = 4 * q + i;  // V column of MFMA k
+            const int d = D == 128 ? 8 * n + k : 8 * (n % 8) + k + 4 * (n / 8);
+            float* dp = &bO[c * D + d];
+            const float o = ldexpf(oacc[k][i], e_run - 126);
+            *dp = (ww == 0 ? 0.0f : *dp * a0) + o * a1;
           }
+        if (q == 0) {
+          bL[c] = (ww == 0 ? 0.0f : bL[c] * a0) + l_run * a1;
+          bM[c] = Mn;
+        }
       }
       __syncthreads();
     }
-    for (int i = tid; i < G * D; i += kKvThreads) a.part_o[int64_t(unit) * G * D + i] = buf[i];
+    if (tid < G) {
+      a.part_ml[(int64_t(unit) * G + tid) * 2 + 0] = bM[tid];
+      a.part_ml[(int64_t(unit) * G + tid) * 2 + 1] = bL[tid];
+    }
+    for (int i = tid; i < G * D; i += kKvThreads) a.part_o[int64_t(unit) * G * D + i] = bO[i];
     __syncthreads();  // buf is reused by the next unit
   }
 }
@@ -463,7 +516,12 @@ __global__ __launch_bounds__(D) void kv_combine_kernel(const float* __restrict__
 
 template <int D, int G, int ST, bool CODES>
 hipError_t launch_split(const KvArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((kv_split_kernel<D, G, ST, CODES>), dim3(unsigned(grid)), dim3(kKvThreads), 0, stream, a);
+  if (a.lp >= 4)
+    hipLaunchKernelGGL((kv_split_kernel<D, G, ST, CODES, true>), dim3(unsigned(grid)), dim3(kKvThreads), 0, stream,
+                       a);
+  else
+    hipLaunchKernelGGL((kv_split_kernel<D, G, ST, CODES, false>), dim3(unsigned(grid)), dim3(kKvThreads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
