@@ -62,6 +62,7 @@ struct KvArgs {
   int num_pages;    // page indices are clamped to [0, num_pages)
   int max_len;      // seq_lens are clamped to [0, max_len] (max_seq_len, and the block table's reach)
   float sm_scale, resid_scale;
+  int rk;  // two stages with resid_scale = 2^-rk (0 <= rk <= 4): merged exactly in integers
 };
 
 __device__ __forceinline__ float q_value(const void* q, int dt, int64_t i) {
@@ -97,17 +98,75 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-// The entry's 2c as four fp16 pairs (2c_2k, 2c_2k+1) from its stored word w and m
-// (all ones: the entry is the word's negation): with t = w ^ m ^ 0x8888_8888 each
-// nibble is lane + 8 (or 7 - lane), 1024 + nibble is an exact fp16 when placed in
-// the mantissa, and the bias -(1024 + 8) (or -(1024 + 7)) leaves the value; nibbles
-// k and k + 4 hold coordinates 2k and 2k + 1.
-__device__ __forceinline__ void word_pairs(uint32_t w, uint32_t m, half2v (&p)[4]) {
-  const uint32_t t = w ^ m ^ 0x88888888u;
-  const half2v bias = __builtin_bit_cast(half2v, 0xE408E408u ^ (m & 0x000F000Fu));
+// Decoding.  The workgroup's LDS copy of the image holds every codeword word XOR
+// 0x8888_8888, so for stored value c with word w and m (all ones: the entry is the
+// word's negation) t = w ^ m has nibble j equal to 2c_j + 8 - mb (mb = m & 1): offset
+// binary either way.  Nibbles k and k + 4 hold coordinates 2k and 2k + 1.  A byte N
+// <= 255 placed as the low byte of an fp16 with high byte 0x64 reads 1024 + N
+// exactly, so the pairs come from byte permutes of the even and odd nibbles and one
+// fp16 add of the bias.
+constexpr uint32_t kC64 = 0x64646464u;
+constexpr uint32_t kSel02 = 0x04020400u;  // (byte 0, 0x64, byte 2, 0x64)
+constexpr uint32_t kSel13 = 0x04030401u;  // (byte 1, 0x64, byte 3, 0x64)
+
+// fp16 pairs (N_a + 1024, N_b + 1024) of even-nibble bytes lo and odd-nibble bytes hi,
+// plus bias nb: pairs (coordinates 0, 1), (2, 3), (4, 5), (6, 7)
+__device__ __forceinline__ void byte_pairs(uint32_t lo, uint32_t hi, uint32_t nb, half2v (&p)[4]) {
+  const half2v b = __builtin_bit_cast(half2v, nb);
+  p[0] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kC64, lo, kSel02)) + b;
+  p[1] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kC64, hi, kSel02)) + b;
+  p[2] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kC64, lo, kSel13)) + b;
+  p[3] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kC64, hi, kSel13)) + b;
+}
+
+// one stage: 2c as fp16 pairs (bias -(1032 - mb): 0xE408, or 0xE407 negated)
+__device__ __forceinline__ void stage_pairs(uint32_t w, uint32_t m, half2v (&p)[4]) {
+  const uint32_t t = w ^ m;
+  byte_pairs(t & 0x0F0F0F0Fu, (t >> 4) & 0x0F0F0F0Fu, 0xE408E408u + (m & 0xFFFEFFFFu), p);
+}
+
+// Decode constants of a call: the residual shift rk and its biases
+struct KvDecode {
+  int rk;
+  uint32_t nbase;  // -(1024 + 8 2^rk + 8) in both halves
+  uint32_t nk;     // -(2^rk) in both halves (added when stage 0 is negated)
+  half2v rs2;      // resid_scale in both halves (two stages, any scale)
+};
+
+// The LDS words of stored values c0, c1 (one codeword, both stages) and their masks
+struct CwWords {
+  uint32_t w0, m0, w1, m1;
+};
+template <int MODE, bool CODES>
+__device__ __forceinline__ CwWords kv_lookup(const uint32_t* img, uint32_t c0, uint32_t c1, uint32_t delta) {
+  CwWords r;
+  r.w0 = kv_word<CODES>(img, c0, delta, r.m0);
+  r.w1 = 0u;
+  r.m1 = 0u;
+  if constexpr (MODE != 0) r.w1 = kv_word<CODES>(img, c1, delta, r.m1);
+  return r;
+}
+
+// The codeword as 8 fp16 (pairs of coordinates), times 2^rk for MODE 1.  MODE 0: one
+// stage, 2c0.  MODE 1: resid_scale = 2^-rk, bytes N = 2^rk (2c0 + 8 - mb0) +
+// (2c1 + 8 - mb1) <= 255 merged in integers, then one bias: 2^rk 2c0 + 2c1 exactly.
+// MODE 2: any resid_scale, 2c0 + s_r 2c1 in fp16.
+template <int MODE>
+__device__ __forceinline__ void kv_decode(const CwWords& cw, const KvDecode& dc, half2v (&p)[4]) {
+  if constexpr (MODE == 0) {
+    stage_pairs(cw.w0, cw.m0, p);
+  } else if constexpr (MODE == 1) {
+    const uint32_t t0 = cw.w0 ^ cw.m0, t1 = cw.w1 ^ cw.m1;
+    const uint32_t lo = ((t0 & 0x0F0F0F0Fu) << dc.rk) + (t1 & 0x0F0F0F0Fu);
+    const uint32_t hi = (((t0 >> 4) & 0x0F0F0F0Fu) << dc.rk) + ((t1 >> 4) & 0x0F0F0F0Fu);
+    byte_pairs(lo, hi, dc.nbase + (cw.m0 & dc.nk) + (cw.m1 & 0xFFFEFFFFu), p);
+  } else {
+    half2v p1[4];
+    stage_pairs(cw.w0, cw.m0, p);
+    stage_pairs(cw.w1, cw.m1, p1);
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    p[k] = __builtin_bit_cast(half2v, ((t >> (4 * k)) & 0x000F000Fu) | 0x64006400u) + bias;
+    for (int j = 0; j < 4; ++j) p[j] = p1[j] * dc.rs2 + p[j];
+  }
 }
 
 // Over the four rows of 16 lanes (lanes l, l ^ 16, l ^ 32, l ^ 48): the max / sum in
@@ -124,20 +183,6 @@ __device__ __forceinline__ float xq_sum(float v) {
   v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-// The codeword of stored value c (both stages combined) as 8 fp16: 2c0 + s_r 2c1
-template <int ST, bool CODES>
-__device__ __forceinline__ void kv_codeword(const uint32_t* img, uint32_t c0, uint32_t c1, uint32_t delta,
-                                            half2v rs2, half2v (&p)[4]) {
-  uint32_t m;
-  word_pairs(kv_word<CODES>(img, c0, delta, m), m, p);
-  if (ST == 2) {
-    half2v p1[4];
-    word_pairs(kv_word<CODES>(img, c1, delta, m), m, p1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = p1[j] * rs2 + p[j];
-  }
 }
 
 typedef _Float16 half4v __attribute__((ext_vector_type(4)));
@@ -165,7 +210,7 @@ typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 // rescaled to the common max) in LDS.
 // BIG: pages of 16 tokens or more, so a tile (16 aligned tokens) lies on one page and
 // its rows are one uniform row plus per-lane constants.
-template <int D, int G, int ST, bool CODES, bool BIG>
+template <int D, int G, int MODE, bool CODES, bool BIG>
 __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
   constexpr int GPS = D / 8;  // groups per vector
   constexpr int KS = D / 32;  // score k-steps per vector
@@ -179,38 +224,53 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the tile loop branches on it
-  {
-    // every load of the image in flight before the first store (clamped addresses:
-    // a thread past the end rewrites the last uint4 with the value found there)
-    uint32_t nd = a.pack_hdr[CODES ? kHdrSlotDwords : 3];
-    nd = nd > uint32_t(kImageMaxDwords) ? uint32_t(kImageMaxDwords) : nd;
-    const uint32_t nd4 = nd >> 2;
-    const uint32_t last4 = nd4 > 0 ? nd4 - 1 : 0;
+  // The codebook image, copied to LDS in two steps: the loads (issued with the first
+  // unit's first reads of the cache, so their latencies overlap), then the stores.
+  // Every load is in flight before the first store (clamped addresses: a thread past
+  // the end rewrites the last uint4 with the value found there).  Codeword words (all
+  // of the slot image; past the page table of the index image) are stored in offset
+  // binary: XOR 0x8888_8888.
+  uint32_t nd = a.pack_hdr[CODES ? kHdrSlotDwords : 3];
+  nd = nd > uint32_t(kImageMaxDwords) ? uint32_t(kImageMaxDwords) : nd;
+  const uint32_t nd4 = nd >> 2;
+  const uint32_t last4 = nd4 > 0 ? nd4 - 1 : 0;
+  constexpr int kParts = (kImageMaxDwords / 4 + kKvThreads - 1) / kKvThreads;
+  constexpr uint32_t kFirstWord4 = CODES ? 0u : uint32_t(kPageCount / 4);
+  const uint32_t img_ti = (nd4 << 2) + tid;
+  auto image_loads = [&](img_x4 (&imt)[kParts], uint32_t& img_tail) {
     const img_x4* src = reinterpret_cast<const img_x4*>(a.img);
+#pragma unroll
+    for (int k = 0; k < kParts; ++k) imt[k] = src[min(uint32_t(tid + k * kKvThreads), last4)];
+    img_tail = img_ti < nd ? a.img[img_ti] : 0u;
+  };
+  auto image_stores = [&](const img_x4 (&imt)[kParts], uint32_t img_tail) {
     img_x4* dst = reinterpret_cast<img_x4*>(img);
-    constexpr int kParts = (kImageMaxDwords / 4 + kKvThreads - 1) / kKvThreads;
-    img_x4 t[kParts];
 #pragma unroll
-    for (int k = 0; k < kParts; ++k) t[k] = src[min(uint32_t(tid + k * kKvThreads), last4)];
-    uint32_t tail = 0;
-    const uint32_t ti = (nd4 << 2) + tid;
-    if (ti < nd) tail = a.img[ti];
-#pragma unroll
-    for (int k = 0; k < kParts; ++k) dst[min(uint32_t(tid + k * kKvThreads), last4)] = t[k];
-    if (ti < nd) img[ti] = tail;
-  }
+    for (int k = 0; k < kParts; ++k) {
+      const uint32_t u = min(uint32_t(tid + k * kKvThreads), last4);
+      const uint32_t x = u >= kFirstWord4 ? 0x88888888u : 0u;
+      dst[u] = img_x4{imt[k].x ^ x, imt[k].y ^ x, imt[k].z ^ x, imt[k].w ^ x};
+    }
+    if (img_ti < nd) img[img_ti] = img_tail ^ (img_ti >= kFirstWord4 * 4 ? 0x88888888u : 0u);
+  };
+  bool img_ready = false;
   const uint32_t delta = CODES ? slot_delta(a.pack_hdr) : 0u;
   const int c = lane & 15, q = lane >> 4;
   const int vg = c % GPS;  // V: the lane's group
   const int vh = c / GPS;  // V with D = 64: the half of the group's coordinates
   const int P = 1 << a.lp;
-  const half2v rs2 = half2v{_Float16(a.resid_scale), _Float16(a.resid_scale)};
+  KvDecode dc;
+  dc.rk = MODE == 1 ? a.rk : 0;
+  dc.nbase = 0xE400E400u | ((8u << dc.rk) + 8u) * 0x00010001u;
+  dc.nk = 0u - (1u << dc.rk) * 0x00010001u;
+  dc.rs2 = half2v{_Float16(a.resid_scale), _Float16(a.resid_scale)};
+  // the codewords are 2 (2c0 + s_r 2c1), times 2^rk for MODE 1
+  const float cw_scale = MODE == 1 ? ldexpf(0.5f, -dc.rk) : 0.5f;
   // per-lane offsets from a tile's first row (BIG): K token c, V / scale tokens 4q + i
   const int koff = c * a.Hkv * GPS + q * KS;
   const int voff = 4 * q * a.Hkv * GPS + vg;
   const int soff = 4 * q * a.Hkv;
   const int vstep = a.Hkv * GPS, sstep = a.Hkv;
-  __syncthreads();
 
   for (int unit = blockIdx.x; unit < a.units; unit += gridDim.x) {
     const int split = unit % a.splits;
@@ -223,41 +283,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
     const int nt_unit = min(a.T, L - t0);
     const int32_t* bt = a.block_table + int64_t(b) * a.bt_stride;
 
-    // ---- the G query heads of h: q' = H8 q_g / sqrt(8) * sm_scale
-    const int64_t qbase = (int64_t(b) * a.Hkv + h) * G * D;
-    for (int i = tid; i < G * D; i += kKvThreads) buf[i] = q_value(a.q, a.q_dt, qbase + i);
-    __syncthreads();
-    const bool qlane = tid < G * GPS;
-    float qv[8];
-    if (qlane) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qv[j] = buf[tid * 8 + j];
-      fwht_reg<8>(qv);
-      const float f = a.sm_scale * 0.35355339059327373f;  // 1 / sqrt(8)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qv[j] *= f;
-    }
-    __syncthreads();
-    if (qlane) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) buf[tid * 8 + j] = qv[j];
-    }
-    __syncthreads();
-    half8 qb[KS];  // lane (c, q): head c, k-step ks: group q KS + ks
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      half8 v;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        v[j] = c < G ? _Float16(buf[c * D + (q * KS + ks) * 8 + j]) : _Float16(0.0f);
-      qb[ks] = v;
-    }
-    __syncthreads();  // buf is free until the wave merge
+    half8 qb[KS];  // the query fragments, filled before the first tile
 
     // ---- the wave's tiles.  A tile's rows take two dependent loads (the block table,
-    // then the indices), so each is issued well before its use: the pages of tile
-    // i + 2 and the indices of tile i + 1 are in flight while tile i is processed.
-    // Tiles past the wave's last load a valid tile again and are not used.
+    // then the indices), each issued well before its use.  Tiles past the wave's last
+    // load a valid tile again and are not used.
     const int ntiles = (nt_unit + 15) >> 4;
     struct TilePages {
       int32_t pk, pv[4];  // BIG: pk alone, the tile's page
@@ -268,11 +298,16 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
       uint32_t v0[4], v1[4];    // V: group vg of tokens 4q + i, per stage
       float ksc[4], vsc[4];     // scales of tokens 4q + i
     };
+
     auto load_pages = [&](int j, TilePages& tp) {
       const int jj = j < ntiles ? j : ntiles - 1;
       if constexpr (BIG) {
         tp.tk = t0 + jj * 16;
-        tp.pk = bt[tp.tk >> a.lp];
+        // a vector load (the index in a VGPR): a scalar load in flight would make
+        // every wait for the LDS reads a wait for all of them
+        int pi = tp.tk >> a.lp;
+        asm("" : "+v"(pi));
+        tp.pk = bt[pi];
       } else {
         const int tk = jj * 16 + c;
         tp.tk = t0 + (tk < nt_unit ? tk : 0);
@@ -300,7 +335,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           ti.k0[ks] = pk0[ks];
-          ti.k1[ks] = ST == 2 ? uint32_t(pk1[ks]) : 0u;
+          ti.k1[ks] = MODE != 0 ? uint32_t(pk1[ks]) : 0u;
         }
         const uint16_t* pv0 = a.v0 + r0 * GPS + voff;
         const uint16_t* pv1 = a.v1 + r0 * GPS + voff;
@@ -309,7 +344,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ti.v0[i] = pv0[i * vstep];
-          ti.v1[i] = ST == 2 ? uint32_t(pv1[i * vstep]) : 0u;
+          ti.v1[i] = MODE != 0 ? uint32_t(pv1[i * vstep]) : 0u;
           ti.ksc[i] = pks[i * sstep];
           ti.vsc[i] = pvs[i * sstep];
         }
@@ -320,13 +355,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           ti.k0[ks] = pk0[ks];
-          ti.k1[ks] = ST == 2 ? uint32_t(pk1[ks]) : 0u;
+          ti.k1[ks] = MODE != 0 ? uint32_t(pk1[ks]) : 0u;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rv = row_at(tp.pv[i], tp.tv[i]);
           ti.v0[i] = a.v0[int64_t(rv) * GPS + vg];
-          ti.v1[i] = ST == 2 ? uint32_t(a.v1[int64_t(rv) * GPS + vg]) : 0u;
+          ti.v1[i] = MODE != 0 ? uint32_t(a.v1[int64_t(rv) * GPS + vg]) : 0u;
           ti.ksc[i] = a.ks[rv];
           ti.vsc[i] = a.vs[rv];
         }
@@ -345,7 +380,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         half2v pk[4];
-        kv_codeword<ST, CODES>(img, ti.k0[ks], ti.k1[ks], delta, rs2, pk);
+        kv_decode<MODE>(kv_lookup<MODE, CODES>(img, ti.k0[ks], ti.k1[ks], delta), dc, pk);
         const half8 ak = half8{pk[0].x, pk[0].y, pk[1].x, pk[1].y, pk[2].x, pk[2].y, pk[3].x, pk[3].y};
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qb[ks], sacc, 0, 0, 0);
       }
@@ -355,7 +390,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         ok[i] = tb + i < nt_unit;
-        sv[i] = ok[i] ? sacc[i] * (0.5f * ti.ksc[i]) : -INFINITY;
+        sv[i] = ok[i] ? sacc[i] * (cw_scale * ti.ksc[i]) : -INFINITY;
       }
       // a tile holds at least one token of the unit, so the max is finite
       const float m_new = fmaxf(m_run, xq_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))));
@@ -374,13 +409,17 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
       e_run = e_new;
       half4v wb;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wb[i] = _Float16(ok[i] ? ldexpf(p[i] * (0.5f * ti.vsc[i]), 126 - e_new) : 0.0f);
+      for (int i = 0; i < 4; ++i)
+        wb[i] = _Float16(ok[i] ? ldexpf(p[i] * (cw_scale * ti.vsc[i]), 126 - e_new) : 0.0f);
+      // the sums rescaled unless every lane's factor is 1 (no new max, no new exponent)
+      if (__builtin_amdgcn_ballot_w64(r != 1.0f) != 0) {
 #pragma unroll
-      for (int k = 0; k < NK; ++k) oacc[k] *= r;
+        for (int k = 0; k < NK; ++k) oacc[k] *= r;
+      }
       // V: group vg of the lane's 4 tokens, coordinate k (+ 4 vh) per MFMA
       half2v cw[4][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kv_codeword<ST, CODES>(img, ti.v0[i], ti.v1[i], delta, rs2, cw[i]);
+      for (int i = 0; i < 4; ++i) kv_decode<MODE>(kv_lookup<MODE, CODES>(img, ti.v0[i], ti.v1[i], delta), dc, cw[i]);
       if constexpr (D == 64) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -397,18 +436,51 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
         oacc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, wb, oacc[k], 0, 0, 0);
       }
     };
-    // two buffers of each kind, used in turn (the loop is unrolled by two, so no
-    // buffer is copied: a copy would wait for the loads in flight into it).  The
-    // scheduling barriers keep the loads in the same issue order (pages, then indices)
-    // before the loop as at its back edge, so the counted waits at the top of the loop
-    // leave the newer loads in flight.
+    // Two stages run ahead of the tile processed: its pages (two tiles ahead) and its
+    // indices (one ahead), each in two buffers used in turn.  The loop is unrolled by
+    // two, so no buffer is copied (a copy would wait for the loads in flight into it).
+    // The scheduling barriers keep the loads in the same issue order before the loop
+    // as at its back edge, so the counted waits leave the newer loads in flight.  The
+    // first unit's image loads go out between its first page and index reads.
     TilePages pa, pb;
     TileIdx ia, ib;
     load_pages(wave, pa);
     load_pages(wave + kKvWaves, pb);
     __builtin_amdgcn_sched_barrier(0);
-    load_idx(pa, ia);
+    if (!img_ready) {  // the same for the whole workgroup
+      img_x4 imt[kParts];
+      uint32_t img_tail;
+      image_loads(imt, img_tail);
+      __builtin_amdgcn_sched_barrier(0);
+      load_idx(pa, ia);
+      __builtin_amdgcn_sched_barrier(0);
+      image_stores(imt, img_tail);
+      __syncthreads();
+      img_ready = true;
+    } else {
+      load_idx(pa, ia);
+    }
     __builtin_amdgcn_sched_barrier(0);
+    // ---- the query fragments, straight from memory: lane (c, q) holds head c's groups
+    // q KS + ks (zero past G), each rotated by the 8-point Hadamard and scaled:
+    // q' = H8 q_g / sqrt(8) * sm_scale
+    {
+      const int64_t qrow = ((int64_t(b) * a.Hkv + h) * G + min(c, G - 1)) * D;
+      float qv[KS][8];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qv[ks][j] = c < G ? q_value(a.q, a.q_dt, qrow + (q * KS + ks) * 8 + j) : 0.0f;
+      const float f = a.sm_scale * 0.35355339059327373f;  // 1 / sqrt(8)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        fwht_reg<8>(qv[ks]);
+        half8 v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = _Float16(qv[ks][j] * f);
+        qb[ks] = v;
+      }
+    }
     for (int j = wave; j < ntiles; j += 2 * kKvWaves) {
       load_pages(j + 2 * kKvWaves, pa);
       __builtin_amdgcn_sched_barrier(0);
@@ -423,8 +495,52 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
       process(ib, j + kKvWaves);
     }
 
-    // ---- the waves merged in wave order: O [G][D], then M [G], L [G] in buf.  A wave
-    // without tokens has max -inf and adds nothing; wave 0 always has the first tile.
+    // ---- the waves' results merged in wave order.  On the workgroup's last unit the
+    // image is no longer needed: every wave stores its sums (in units of 1), max and
+    // exp-sum there and all threads merge them at once; otherwise the waves take turns
+    // on O [G][D], M [G], L [G] in buf.  A wave without tokens has max -inf and adds
+    // nothing; wave 0 always has the first tile.
+    auto o_dim = [&](int k, int i) {  // dimension of the lane's sum (k, i)
+      const int n = 4 * q + i;         // V column of MFMA k
+      return D == 128 ? 8 * n + k : 8 * (n % 8) + k + 4 * (n / 8);
+    };
+    if (unit + int(gridDim.x) >= a.units) {
+      __syncthreads();  // every wave is done with the image
+      float* so = reinterpret_cast<float*>(img);  // [wave][G][D]
+      float* sml = so + kKvWaves * G * D;        // [wave][G][2]
+      if (c < G) {
+#pragma unroll
+        for (int k = 0; k < NK; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) so[(wave * G + c) * D + o_dim(k, i)] = ldexpf(oacc[k][i], e_run - 126);
+        if (q == 0) {
+          sml[(wave * G + c) * 2 + 0] = m_run;
+          sml[(wave * G + c) * 2 + 1] = l_run;
+        }
+      }
+      __syncthreads();
+      for (int idx = tid; idx < G * D; idx += kKvThreads) {
+        const int g = idx / D, d = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kKvWaves; ++w) M = fmaxf(M, sml[(w * G + g) * 2]);
+        float o = 0.0f, l = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kKvWaves; ++w) {
+          const float mw = sml[(w * G + g) * 2];
+          const float aw = mw == -INFINITY ? 0.0f : __expf(mw - M);
+          o = fmaf(aw, so[(w * G + g) * D + d], o);
+          l = fmaf(aw, sml[(w * G + g) * 2 + 1], l);
+        }
+        a.part_o[int64_t(unit) * G * D + idx] = o;
+        if (d == 0) {
+          a.part_ml[(int64_t(unit) * G + g) * 2 + 0] = M;
+          a.part_ml[(int64_t(unit) * G + g) * 2 + 1] = l;
+        }
+      }
+      img_ready = false;
+      continue;
+    }
     float* bO = buf;
     float* bM = buf + G * D;
     float* bL = bM + G;
@@ -438,9 +554,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
         for (int k = 0; k < NK; ++k)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int n = 4 * q + i;  // V column of MFMA k
-            const int d = D == 128 ? 8 * n + k : 8 * (n % 8) + k + 4 * (n / 8);
-            float* dp = &bO[c * D + d];
+            float* dp = &bO[c * D + o_dim(k, i)];
             const float o = ldexpf(oacc[k][i], e_run - 126);
             *dp = (ww == 0 ? 0.0f : *dp * a0) + o * a1;
           }
@@ -514,22 +628,24 @@ __global__ __launch_bounds__(D) void kv_combine_kernel(const float* __restrict__
   out[(int64_t(b) * Hkv * G + hq) * D + d] = from_f32<OT>(v * 0.35355339059327373f);
 }
 
-template <int D, int G, int ST, bool CODES>
+template <int D, int G, int MODE, bool CODES>
 hipError_t launch_split(const KvArgs& a, int grid, hipStream_t stream) {
   if (a.lp >= 4)
-    hipLaunchKernelGGL((kv_split_kernel<D, G, ST, CODES, true>), dim3(unsigned(grid)), dim3(kKvThreads), 0, stream,
-                       a);
+    hipLaunchKernelGGL((kv_split_kernel<D, G, MODE, CODES, true>), dim3(unsigned(grid)), dim3(kKvThreads), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((kv_split_kernel<D, G, ST, CODES, false>), dim3(unsigned(grid)), dim3(kKvThreads), 0,
+    hipLaunchKernelGGL((kv_split_kernel<D, G, MODE, CODES, false>), dim3(unsigned(grid)), dim3(kKvThreads), 0,
                        stream, a);
   return hipGetLastError();
 }
 
 template <int D, int G>
 hipError_t launch_split_dg(const KvArgs& a, int grid, int stages, bool codes, hipStream_t stream) {
+  if (stages == 2 && a.rk >= 0)
+    return codes ? launch_split<D, G, 1, true>(a, grid, stream) : launch_split<D, G, 1, false>(a, grid, stream);
   if (stages == 2)
     return codes ? launch_split<D, G, 2, true>(a, grid, stream) : launch_split<D, G, 2, false>(a, grid, stream);
-  return codes ? launch_split<D, G, 1, true>(a, grid, stream) : launch_split<D, G, 1, false>(a, grid, stream);
+  return codes ? launch_split<D, G, 0, true>(a, grid, stream) : launch_split<D, G, 0, false>(a, grid, stream);
 }
 
 template <int D, int G>
@@ -616,6 +732,10 @@ hipError_t launch_kv_attention(const glq_kv_cache& kv, const void* q, glq_dtype 
   a.units = int(p.units);
   a.sm_scale = sm_scale;
   a.resid_scale = kv.resid_scale;
+  // resid_scale = 2^-rk with 0 <= rk <= 4: the stages are merged exactly in integers
+  a.rk = -1;
+  for (int k = 0; k <= 4; ++k)
+    if (kv.resid_scale == std::ldexp(1.0f, -k)) a.rk = k;
   const int grid = int(p.units < device_cus() ? p.units : device_cus());
   const int st = kv.stages;
   if (kv.head_dim == 64) {

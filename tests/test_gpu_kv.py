@@ -69,6 +69,41 @@ def test_attention_matches_oracle(gpu_codebooks, lens, Hkv, G, D, stages, P, qdt
     assert err <= 1e-3, err
 
 
+@pytest.mark.parametrize("resid_scale", [1.0, 0.5, 0.125, 0.0625, 0.3])
+def test_resid_scales(gpu_codebooks, resid_scale):
+    # two stages with other residual scales: powers of two 2^-k (k <= 4) merge the
+    # stages' integer codes exactly, any other scale combines them in fp16 (0.3 is
+    # rounded to fp16 once); both formats, within the same 1e-3 of the oracle
+    say("kv resid_scale", resid_scale)
+    cache = synth.make_kv([700, 33], 2, 128, 2, 16, seed=61)
+    cache.resid_scale = resid_scale
+    q64, raw = synth.make_q(2, 8, 128, "bf16", seed=62)
+    out = _run(gpu_codebooks, cache, raw, "bf16")
+    outs = _run(gpu_codebooks, cache, raw, "bf16", slot=True)
+    assert torch.equal(out, outs)
+    err = rel_frob(to_f64(out), _oracle(cache, q64, 1.0 / np.sqrt(128)))
+    say("  rel_frob", err)
+    assert err <= 1e-3, err
+
+
+@pytest.mark.parametrize("D,G", [(64, 2), (128, 4)])
+def test_more_units_than_compute_units(gpu_codebooks, D, G):
+    # 40 sequences x 8 KV heads: more (sequence, head, chunk) units than compute units,
+    # so workgroups take several units in turn (the waves' results merged in turns on
+    # all but the last, the image reloaded after the last one's merge); ragged lengths
+    # include 1-token and page-boundary sequences
+    lens = [1, 16, 17, 300, 255, 33] + list(np.random.default_rng(D).integers(1, 400, size=34))
+    say("kv many units", D, G, len(lens))
+    cache = synth.make_kv(lens, 8, D, 2, 16, seed=71 + D)
+    q64, raw = synth.make_q(len(lens), 8 * G, D, "bf16", seed=72)
+    out = _run(gpu_codebooks, cache, raw, "bf16")
+    outs = _run(gpu_codebooks, cache, raw, "bf16", slot=True)
+    assert torch.equal(out, outs)
+    err = rel_frob(to_f64(out), _oracle(cache, q64, 1.0 / np.sqrt(D)))
+    say("  rel_frob", err)
+    assert err <= 1e-3, err
+
+
 def test_smollm3_shape_16k(gpu_codebooks):
     # the timed shape: SmolLM3-3B attention, 16 query heads on 4 KV heads, head_dim
     # 128, 4 sequences of 16k tokens, 4 bpw cache, bf16 query (the first layer's cache
