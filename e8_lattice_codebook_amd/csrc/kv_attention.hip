@@ -267,10 +267,12 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
   // the codewords are 2 (2c0 + s_r 2c1), times 2^rk for MODE 1
   const float cw_scale = MODE == 1 ? ldexpf(0.5f, -dc.rk) : 0.5f;
   // per-lane offsets from a tile's first row (BIG): K token c, V / scale tokens 4q + i
+  const int vpair = vg & ~1;  // V: the element offset of the lane's 32-bit word in a row
   const int koff = c * a.Hkv * GPS + q * KS;
-  const int voff = 4 * q * a.Hkv * GPS + vg;
-  const int soff = 4 * q * a.Hkv;
-  const int vstep = a.Hkv * GPS, sstep = a.Hkv;
+  const int voff = (4 * q + 2 * (c & 1)) * a.Hkv * GPS + vpair;
+  const int soff = (4 * q + (c & 3)) * a.Hkv;
+  const int vstep = a.Hkv * GPS;
+  const float* sbase = (c & 4) ? a.vs : a.ks;  // the lane's scale array
 
   for (int unit = blockIdx.x; unit < a.units; unit += gridDim.x) {
     const int split = unit % a.splits;
@@ -289,16 +291,21 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
     // then the indices), each issued well before its use.  Tiles past the wave's last
     // load a valid tile again and are not used.
     const int ntiles = (nt_unit + 15) >> 4;
+    // Per tile a lane reads: K, the KS groups q KS .. + KS - 1 of token c, per stage; V,
+    // the 32-bit word of groups (vg & ~1, vg | 1) of tokens 4q + 2 (c & 1) + j (j = 0,
+    // 1), per stage, whose halves lanes c and c ^ 1 exchange (a pair of lanes reads
+    // the four tokens' words once, in 32-bit loads); one scale, k_scale (c mod 8 < 4)
+    // or v_scale of token 4q + (c mod 4), broadcast over the lane's row afterwards.
     struct TilePages {
-      int32_t pk, pv[4];  // BIG: pk alone, the tile's page
-      int tk, tv[4];      // tokens of the unit (small pages: token 0 past its end)
+      int32_t pk, pv[2], ps;  // BIG: pk alone, the tile's page
+      int tk, tv[2], ts;      // tokens of the unit (small pages: token 0 past its end)
     };
     struct TileIdx {
-      uint32_t k0[KS], k1[KS];  // K: the lane's KS groups of token c, per stage
-      uint32_t v0[4], v1[4];    // V: group vg of tokens 4q + i, per stage
-      float ksc[4], vsc[4];     // scales of tokens 4q + i
+      uint32_t k0[KS], k1[KS];  // K indices, per stage
+      uint32_t v0[2], v1[2];    // V words, per stage
+      float sc;                 // the lane's scale
     };
-
+    auto unit_token = [&](int jj, int t) { return t0 + (jj * 16 + t < nt_unit ? jj * 16 + t : 0); };
     auto load_pages = [&](int j, TilePages& tp) {
       const int jj = j < ntiles ? j : ntiles - 1;
       if constexpr (BIG) {
@@ -309,15 +316,15 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
         asm("" : "+v"(pi));
         tp.pk = bt[pi];
       } else {
-        const int tk = jj * 16 + c;
-        tp.tk = t0 + (tk < nt_unit ? tk : 0);
+        tp.tk = unit_token(jj, c);
         tp.pk = bt[tp.tk >> a.lp];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tv = jj * 16 + 4 * q + i;
-          tp.tv[i] = t0 + (tv < nt_unit ? tv : 0);
-          tp.pv[i] = bt[tp.tv[i] >> a.lp];
+        for (int j2 = 0; j2 < 2; ++j2) {
+          tp.tv[j2] = unit_token(jj, 4 * q + 2 * (c & 1) + j2);
+          tp.pv[j2] = bt[tp.tv[j2] >> a.lp];
         }
+        tp.ts = unit_token(jj, 4 * q + (c & 3));
+        tp.ps = bt[tp.ts >> a.lp];
       }
     };
     // row of token t on page entry pg: (page, slot, head); rows * D / 8 < 2^31 (checked by
@@ -325,6 +332,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
     auto row_at = [&](int32_t pg, int t) {
       pg = min(max(pg, 0), a.num_pages - 1);
       return (pg * P + (t & (P - 1))) * a.Hkv + h;
+    };
+    auto word_at = [&](const uint16_t* p) {  // 32 bits at an even element offset
+      uint32_t w;
+      __builtin_memcpy(&w, p, 4);
+      return w;
     };
     auto load_idx = [&](const TilePages& tp, TileIdx& ti) {
       if constexpr (BIG) {
@@ -337,17 +349,12 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
           ti.k0[ks] = pk0[ks];
           ti.k1[ks] = MODE != 0 ? uint32_t(pk1[ks]) : 0u;
         }
-        const uint16_t* pv0 = a.v0 + r0 * GPS + voff;
-        const uint16_t* pv1 = a.v1 + r0 * GPS + voff;
-        const float* pks = a.ks + r0 + soff;
-        const float* pvs = a.vs + r0 + soff;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ti.v0[i] = pv0[i * vstep];
-          ti.v1[i] = MODE != 0 ? uint32_t(pv1[i * vstep]) : 0u;
-          ti.ksc[i] = pks[i * sstep];
-          ti.vsc[i] = pvs[i * sstep];
+        for (int j2 = 0; j2 < 2; ++j2) {
+          ti.v0[j2] = word_at(a.v0 + r0 * GPS + voff + j2 * vstep);
+          ti.v1[j2] = MODE != 0 ? word_at(a.v1 + r0 * GPS + voff + j2 * vstep) : 0u;
         }
+        ti.sc = sbase[r0 + soff];
       } else {
         const int rk = row_at(tp.pk, tp.tk);
         const uint16_t* pk0 = a.k0 + int64_t(rk) * GPS + q * KS;
@@ -358,13 +365,12 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
           ti.k1[ks] = MODE != 0 ? uint32_t(pk1[ks]) : 0u;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rv = row_at(tp.pv[i], tp.tv[i]);
-          ti.v0[i] = a.v0[int64_t(rv) * GPS + vg];
-          ti.v1[i] = MODE != 0 ? uint32_t(a.v1[int64_t(rv) * GPS + vg]) : 0u;
-          ti.ksc[i] = a.ks[rv];
-          ti.vsc[i] = a.vs[rv];
+        for (int j2 = 0; j2 < 2; ++j2) {
+          const int64_t rv = row_at(tp.pv[j2], tp.tv[j2]);
+          ti.v0[j2] = word_at(a.v0 + rv * GPS + vpair);
+          ti.v1[j2] = MODE != 0 ? word_at(a.v1 + rv * GPS + vpair) : 0u;
         }
+        ti.sc = sbase[row_at(tp.ps, tp.ts)];
       }
     };
 
@@ -374,8 +380,45 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
     float m_run = -INFINITY, l_run = 0.0f;  // head c; the same in the lanes of a column
     int e_run = 0;                          // the V sums are in units of 2^(e_run - 126)
 
-    // one tile: scores, the online softmax, V (ti holds tile j's indices)
-    auto process = [&](const TileIdx& ti, int j) {
+    // one tile: scores, the online softmax, V (tl holds tile j's indices)
+    auto process = [&](const TileIdx& tl, int j) {
+      // V indices of tokens 4q + i, group vg: lane c's own words hold tokens 2 (c & 1)
+      // + (0, 1), its neighbour's the other two; the lane's half is (c & 1)
+      struct {
+        uint32_t k0[KS], k1[KS], v0[4], v1[4];
+        float ksc[4], vsc[4];
+      } ti;
+      const bool odd = c & 1;
+      const int hs = odd ? 16 : 0;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        ti.k0[ks] = tl.k0[ks];
+        ti.k1[ks] = tl.k1[ks];
+      }
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        const uint32_t g0 = uint32_t(__builtin_amdgcn_update_dpp(0, int(tl.v0[j2]), 0xB1, 0xF, 0xF, false));
+        ti.v0[j2] = ((odd ? g0 : tl.v0[j2]) >> hs) & 0xFFFFu;
+        ti.v0[2 + j2] = ((odd ? tl.v0[j2] : g0) >> hs) & 0xFFFFu;
+        if constexpr (MODE != 0) {
+          const uint32_t g1 = uint32_t(__builtin_amdgcn_update_dpp(0, int(tl.v1[j2]), 0xB1, 0xF, 0xF, false));
+          ti.v1[j2] = ((odd ? g1 : tl.v1[j2]) >> hs) & 0xFFFFu;
+          ti.v1[2 + j2] = ((odd ? tl.v1[j2] : g1) >> hs) & 0xFFFFu;
+        } else {
+          ti.v1[j2] = ti.v1[2 + j2] = 0u;
+        }
+      }
+      // the scales of tokens 4q + i: lanes 16q + i (k) and 16q + 4 + i (v) of the row
+      const int sci = __float_as_int(tl.sc);
+      ti.ksc[0] = __int_as_float(__builtin_amdgcn_update_dpp(0, sci, 0x150, 0xF, 0xF, false));
+      ti.ksc[1] = __int_as_float(__builtin_amdgcn_update_dpp(0, sci, 0x151, 0xF, 0xF, false));
+      ti.ksc[2] = __int_as_float(__builtin_amdgcn_update_dpp(0, sci, 0x152, 0xF, 0xF, false));
+      ti.ksc[3] = __int_as_float(__builtin_amdgcn_update_dpp(0, sci, 0x153, 0xF, 0xF, false));
+      ti.vsc[0] = __int_as_float(__builtin_amdgcn_update_dpp(0, sci, 0x154, 0xF, 0xF, false));
+      ti.vsc[1] = __int_as_float(__builtin_amdgcn_update_dpp(0, sci, 0x155, 0xF, 0xF, false));
+      ti.vsc[2] = __int_as_float(__builtin_amdgcn_update_dpp(0, sci, 0x156, 0xF, 0xF, false));
+      ti.vsc[3] = __int_as_float(__builtin_amdgcn_update_dpp(0, sci, 0x157, 0xF, 0xF, false));
+
       floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -436,29 +479,30 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
         oacc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, wb, oacc[k], 0, 0, 0);
       }
     };
-    // Two stages run ahead of the tile processed: its pages (two tiles ahead) and its
-    // indices (one ahead), each in two buffers used in turn.  The loop is unrolled by
-    // two, so no buffer is copied (a copy would wait for the loads in flight into it).
-    // The scheduling barriers keep the loads in the same issue order before the loop
-    // as at its back edge, so the counted waits leave the newer loads in flight.  The
-    // first unit's image loads go out between its first page and index reads.
-    TilePages pa, pb;
-    TileIdx ia, ib;
-    load_pages(wave, pa);
-    load_pages(wave + kKvWaves, pb);
+    // Two stages run ahead of the tile processed: its pages (two of the wave's tiles
+    // ahead) and its indices (one ahead), each in two buffers used in turn.  The loop
+    // is unrolled by two, so no buffer is copied (a copy would wait for the loads in
+    // flight into it).  The scheduling barriers keep the loads in the same issue order
+    // before the loop as at its back edge, so the counted waits leave the newer loads
+    // in flight.  The first unit's image loads go out among its first reads.
+    constexpr int W = kKvWaves;
+    TilePages pg0, pg1;
+    TileIdx ix0, ix1;
+    load_pages(wave, pg0);
+    load_pages(wave + W, pg1);
     __builtin_amdgcn_sched_barrier(0);
     if (!img_ready) {  // the same for the whole workgroup
       img_x4 imt[kParts];
       uint32_t img_tail;
       image_loads(imt, img_tail);
       __builtin_amdgcn_sched_barrier(0);
-      load_idx(pa, ia);
+      load_idx(pg0, ix0);
       __builtin_amdgcn_sched_barrier(0);
       image_stores(imt, img_tail);
       __syncthreads();
       img_ready = true;
     } else {
-      load_idx(pa, ia);
+      load_idx(pg0, ix0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- the query fragments, straight from memory: lane (c, q) holds head c's groups
@@ -481,18 +525,19 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
         qb[ks] = v;
       }
     }
-    for (int j = wave; j < ntiles; j += 2 * kKvWaves) {
-      load_pages(j + 2 * kKvWaves, pa);
+    // step k of the wave (tile j): pages of step k + 2 into the slot k mod 2, indices
+    // of step k + 1 from its pages, then tile j itself
+    auto step = [&](int j, TilePages& p_load, const TilePages& p_use, TileIdx& i_load, const TileIdx& i_use) {
+      load_pages(j + 2 * W, p_load);
       __builtin_amdgcn_sched_barrier(0);
-      load_idx(pb, ib);
+      load_idx(p_use, i_load);
       __builtin_amdgcn_sched_barrier(0);
-      process(ia, j);
-      if (j + kKvWaves >= ntiles) break;
-      load_pages(j + 3 * kKvWaves, pb);
-      __builtin_amdgcn_sched_barrier(0);
-      load_idx(pa, ia);
-      __builtin_amdgcn_sched_barrier(0);
-      process(ib, j + kKvWaves);
+      process(i_use, j);
+    };
+    for (int j = wave; j < ntiles; j += 2 * W) {
+      step(j, pg0, pg1, ix1, ix0);
+      if (j + W >= ntiles) break;
+      step(j + W, pg1, pg0, ix0, ix1);
     }
 
     // ---- the waves' results merged in wave order.  On the workgroup's last unit the
