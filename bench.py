@@ -65,6 +65,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-padded-only", action="store_true",
+                    help="time only the padded prefill workload (profiler runs of its kernels)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-block", action="store_true")
@@ -89,12 +91,19 @@ def main():
                     help="OUT KERNEL DIR [DIR ...]: medians of every counter of the dispatches whose name "
                          "contains KERNEL in rocprofv3 --pmc folders DIR, written to OUT with --pmc-cmd")
     ap.add_argument("--pmc-cmd", action="append", default=[], help="a command line recorded in the report")
+    ap.add_argument("--stats-report", nargs=2, metavar=("OUT", "DIR"),
+                    help="only summarize the kernel_stats.csv of a rocprofv3 --kernel-trace --stats folder DIR into OUT "
+                         "(commands from --pmc-cmd, notes from --note)")
+    ap.add_argument("--note", action="append", default=[], help="a note line recorded in a --stats-report")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, args.copy_bytes)
         return
     if args.pmc_report:
         pmc_report(args.pmc_report, args.pmc_cmd)
+        return
+    if args.stats_report:
+        stats_report(args.stats_report, args.pmc_cmd, args.note)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the E8RHTLinear path here has no multi-GPU "
@@ -328,7 +337,7 @@ def pmc_summary(dirs, copy_bytes):
         "# HBM traffic of one B = 1 call (%s), Devstral-Small-24B MLP decode" % " + ".join(FUSED_KERNEL_NAMES),
         "# commands (from the repository root, after cd /tmp && export TMPDIR=/tmp for the profiler):",
         "#   rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR --output-format csv -- python3 bench.py --steps 3 --warmup 1 "
-        "--no-cpu-baseline --no-prefill --no-block --no-recipes --no-blockdiag --no-kv",
+        "--no-cpu-baseline --no-prefill --no-block --no-recipes --no-blockdiag --no-kv --no-configs",
         "#   rocprofv3 --pmc WRITE_SIZE -d WRITE_DIR --output-format csv -- (same)",
         "#   rocprofv3 --pmc FETCH_SIZE -d COPY_FETCH_DIR --output-format csv -- python3 bench.py --calibrate-copy %d"
         % copy_bytes,
@@ -478,8 +487,9 @@ def pmc_report(argv, cmds):
         xcd_cycles = g / 8.0  # GRBM_GUI_ACTIVE is summed over the 8 XCDs
         lines.append("derived kernel_cycles_per_xcd: %.0f (%.2f us at 2.4 GHz)" % (xcd_cycles, xcd_cycles / 2400.0))
         if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
-            lines.append("derived mfma_busy_per_cu_cycle: %.4f (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8) / "
-                         "256 CUs)" % (med["SQ_VALU_MFMA_BUSY_CYCLES"] / xcd_cycles / 256.0))
+            # summed over the 1024 SIMDs (it reads 16 cycles per 16x16x32 f16 MFMA issued)
+            lines.append("derived mfma_busy_per_simd: %.4f (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8) / "
+                         "1024 SIMDs)" % (med["SQ_VALU_MFMA_BUSY_CYCLES"] / xcd_cycles / 1024.0))
         if "SQ_INSTS_VALU_MFMA_MOPS_F16" in med:
             fl = med["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512.0
             lines.append("derived mfma_f16_flops: %.4g (MOPS x 512) -> %.1f TFLOP/s over the kernel cycles"
@@ -489,6 +499,36 @@ def pmc_report(argv, cmds):
                          % (med["SQ_INSTS_VALU"] * 4.0 / (xcd_cycles * 1024.0)))
     if "SQ_LDS_BANK_CONFLICT" in med and "SQ_INSTS_LDS" in med:
         lines.append("derived lds_conflict_cycles_per_lds_inst: %.2f" % (med["SQ_LDS_BANK_CONFLICT"] / med["SQ_INSTS_LDS"]))
+    os.makedirs(os.path.dirname(os.path.abspath(out_file)), exist_ok=True)
+    with open(out_file, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def stats_report(argv, cmds, notes):
+    """OUT DIR: the kernels of a rocprofv3 --kernel-trace --stats csv folder, by total
+    time (microseconds), with the recorded commands and notes."""
+    import csv
+    import glob
+    out_file, folder = argv[0], argv[1]
+    files = glob.glob(os.path.join(folder, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no kernel_stats.csv under %s" % folder)
+    with open(files[0]) as fh:
+        rows = list(csv.DictReader(fh))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# rocprofv3 kernel statistics (MI355X, one GPU), durations in microseconds",
+             "# commands (repository root; profiler runs after cd /tmp && export TMPDIR=/tmp):"]
+    lines += ["#   %s" % c for c in cmds]
+    lines += ["# %s" % n for n in notes]
+    lines.append("%-100s %7s %9s %9s %9s %10s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "total_ms"))
+    for r in rows[:25]:
+        name = r["Name"]
+        if len(name) > 100:
+            name = name[:97] + "..."
+        lines.append("%-100s %7s %9.2f %9.2f %9.2f %10.3f" % (
+            name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["TotalDurationNs"]) / 1e6))
     os.makedirs(os.path.dirname(os.path.abspath(out_file)), exist_ok=True)
     with open(out_file, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -553,11 +593,18 @@ def bench_prefill(glq, synth, cb, dev, args, log):
     tflops = flops / (gemm_ms * 1e-3) / 1e12
     log("bench: prefill linear %.4f ms, MFMA matmul %.4f ms = %.1f TFLOP/s (nominal %.1f)" % (
         lin_ms, gemm_ms, tflops, nominal / (gemm_ms * 1e-3) / 1e12))
-    lu = synth.make_layer(wl.layers[0], wl.resid_bits, wl.seed, 0, block_diag=True)
-    ulin_ms, ugemm_ms, _, _ = measure(lu)
-    uflops = 2.0 * M * lu.m_pad * lu.n_pad
-    log("bench: unpadded prefill (m_pad %d) linear %.4f ms, matmul %.4f ms = %.1f TFLOP/s" % (
-        lu.m_pad, ulin_ms, ugemm_ms, uflops / (ugemm_ms * 1e-3) / 1e12))
+    unpadded = None
+    if not args.prefill_padded_only:
+        lu = synth.make_layer(wl.layers[0], wl.resid_bits, wl.seed, 0, block_diag=True)
+        ulin_ms, ugemm_ms, _, _ = measure(lu)
+        uflops = 2.0 * M * lu.m_pad * lu.n_pad
+        log("bench: unpadded prefill (m_pad %d) linear %.4f ms, matmul %.4f ms = %.1f TFLOP/s" % (
+            lu.m_pad, ulin_ms, ugemm_ms, uflops / (ugemm_ms * 1e-3) / 1e12))
+        unpadded = {"workload": "the same layer unpadded: m_pad = m = 11008 (block-diagonal output transform "
+                                "over 8192 + 2048 + 512 + 256)",
+                    "linear_ms": round(ulin_ms, 5), "matmul_ms": round(ugemm_ms, 5),
+                    "value": round(uflops / (ugemm_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "flops": uflops,
+                    "linear_speedup_vs_padded": round(lin_ms / ulin_ms, 3)}
     return {
         "workload": "SmolLM3-3B gate 2048->11008 (m_pad 16384), M=2048 tokens, 3 bpw, bf16 activations",
         "value": round(tflops, 2),
@@ -568,11 +615,7 @@ def bench_prefill(glq, synth, cb, dev, args, log):
         "nominal_flops": nominal,
         "other_index_format": {"index_format": "codebook indices" if args.index_format == "slot" else "slot codes",
                                "value": round(flops / (other_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s"},
-        "unpadded": {"workload": "the same layer unpadded: m_pad = m = 11008 (block-diagonal output transform "
-                                 "over 8192 + 2048 + 512 + 256)",
-                     "linear_ms": round(ulin_ms, 5), "matmul_ms": round(ugemm_ms, 5),
-                     "value": round(uflops / (ugemm_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "flops": uflops,
-                     "linear_speedup_vs_padded": round(lin_ms / ulin_ms, 3)},
+        "unpadded": unpadded,
         "roofline": {"bound": "mfma", "kernel": ("gemm_shared_kernel (prefill matmul: a 64-row codeword tile per "
                                                  "k-step dequantized from the LDS codebook into LDS, shared by four "
                                                  "waves as fp16 MFMA operands, fp32 accumulation)") if frag else
