@@ -8,7 +8,11 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libglq_mi355x.so")
+# GLQ_LIB_VARIANT=debug | asan selects a debug build of the same library (see build.py)
+_VARIANT = os.environ.get("GLQ_LIB_VARIANT", "release")
+LIB_NAME = {"release": "libglq_mi355x.so", "debug": "libglq_mi355x_debug.so",
+            "asan": "libglq_mi355x_asan.so"}.get(_VARIANT, "libglq_mi355x.so")
+LIB_PATH = os.path.join(_HERE, LIB_NAME)
 
 GLQ_F32, GLQ_F16, GLQ_BF16 = 0, 1, 2
 STATUS_NAMES = {
@@ -47,6 +51,7 @@ _KP = ctypes.POINTER(GlqKvCache)
 SIGNATURES = {
     "glq_abi_version": (ctypes.c_int, []),
     "glq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "glq_debug_violations": (c_i64, []),
     "glq_e8_codebook": (ctypes.c_int, [c_vp, c_i64]),
     "glq_codebook_pack_bytes": (c_sz, [c_i64]),
     "glq_codebook_pack": (ctypes.c_int, [c_vp, c_i64, c_vp, c_sz]),
@@ -82,8 +87,8 @@ def load():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libglq_mi355x.so is not built: run e8_lattice_codebook_amd/build.py "
-                          "(or __graft_entry__.build()) first")
+        raise ImportError("%s is not built: run e8_lattice_codebook_amd/build.py "
+                          "(or __graft_entry__.build()) first" % LIB_NAME)
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -258,6 +258,22 @@ extern "C" {
 
 int glq_abi_version(void) { return GLQ_ABI_VERSION; }
 
+int64_t glq_debug_violations(void) {
+#ifdef GLQ_DEBUG
+  (void)hipDeviceSynchronize();
+  using namespace glq;
+  const uint32_t parts[] = {debug_violations_rht(),       debug_violations_dequant(),   debug_violations_gemv(),
+                            debug_violations_gemv_lds(),  debug_violations_fused_decode(),
+                            debug_violations_gemm(),      debug_violations_gemm_lds(),  debug_violations_gemm_shared(),
+                            debug_violations_kv_attention(), debug_violations_noalloc(), debug_violations_gemv_mfma()};
+  int64_t total = 0;
+  for (uint32_t v : parts) total += v == 0xFFFFFFFFu ? int64_t(1) << 32 : int64_t(v);
+  return total;
+#else
+  return -1;
+#endif
+}
+
 const char* glq_status_string(glq_status s) {
   switch (s) {
     case GLQ_OK: return "ok";

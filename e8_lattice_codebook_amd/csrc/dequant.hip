@@ -194,4 +194,6 @@ hipError_t launch_dequant(const glq_layer& layer, void* w, glq_dtype w_dt, hipSt
   return hipErrorInvalidValue;
 }
 
+GLQ_DEBUG_COUNTER(debug_violations_dequant)
+
 }  // namespace glq

@@ -884,4 +884,6 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
   }
 }
 
+GLQ_DEBUG_COUNTER(debug_violations_fused_decode)
+
 }  // namespace glq

@@ -168,4 +168,6 @@ hipError_t launch_gemm(const glq_layer& L, const half_t* u16, const int32_t* rex
   return hipGetLastError();
 }
 
+GLQ_DEBUG_COUNTER(debug_violations_gemm)
+
 }  // namespace glq

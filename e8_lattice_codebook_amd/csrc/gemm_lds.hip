@@ -318,4 +318,6 @@ hipError_t launch_gemm_lds(const glq_layer& L, const half_t* u16, const int32_t*
   return hipGetLastError();
 }
 
+GLQ_DEBUG_COUNTER(debug_violations_gemm_lds)
+
 }  // namespace glq

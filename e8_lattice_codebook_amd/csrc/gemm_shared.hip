@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kSThreads, 1) void gemm_shared_kernel(SharedArgs a)
           case 2: ra = byte_x4<2>(i1b, two); break;
           default: ra = byte_x4<3>(i1b, two); break;
         }
-        x.w1 = lds_at(lds + kResOff, ra);
+        x.w1 = lds_res(lds, ra);
       }
       if (RESID == 16) {
         const uint32_t c1 = i1w[kk >> 1];
@@ -180,7 +180,10 @@ __global__ __launch_bounds__(kSThreads, 1) void gemm_shared_kernel(SharedArgs a)
     auto uload = [&](int ks, u32x4 (&f)[kSTB]) {
       const int64_t k = int64_t(ks < KS ? ks : KS - 1) * 64;  // past the end: in-bounds, never used
 #pragma unroll
-      for (int j = 0; j < kSTB; ++j) f[j] = ubase[uoff[j] + k];
+      for (int j = 0; j < kSTB; ++j) {
+        GLQ_DCHECK(uoff[j] + k + lane < tbc * KS * 64);
+        f[j] = ubase[uoff[j] + k];
+      }
     };
 
     floatx4 acc[kSRB][kSTB];
@@ -324,5 +327,7 @@ hipError_t launch_gemm_shared(const glq_layer& L, const half_t* u16, const int32
   }
   return hipGetLastError();
 }
+
+GLQ_DEBUG_COUNTER(debug_violations_gemm_shared)
 
 }  // namespace glq

@@ -239,4 +239,6 @@ hipError_t launch_gemv(const glq_layer& L, const float* u, int64_t B, float* z_p
   }
 }
 
+GLQ_DEBUG_COUNTER(debug_violations_gemv)
+
 }  // namespace glq

@@ -341,4 +341,6 @@ hipError_t launch_gemv_lds(const glq_layer& L, const void* uq, int64_t B, float*
   }
 }
 
+GLQ_DEBUG_COUNTER(debug_violations_gemv_lds)
+
 }  // namespace glq

@@ -271,4 +271,6 @@ hipError_t launch_gemv_mfma(const glq_layer& L, const half_t* u16, const int32_t
   }
 }
 
+GLQ_DEBUG_COUNTER(debug_violations_gemv_mfma)
+
 }  // namespace glq

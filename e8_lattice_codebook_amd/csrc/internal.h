@@ -8,6 +8,45 @@
 
 namespace glq {
 
+// ---- debug builds (GLQ_DEBUG) -------------------------------------------------------
+// Device-side bounds checks: a failed check adds one to its source file's counter and
+// the kernel runs on (no trap); glq_debug_violations() reads and clears the counters.
+// Release builds compile the checks away.
+#if defined(GLQ_DEBUG) && defined(__HIP__)
+static __device__ unsigned int g_debug_violations;
+#define GLQ_DCHECK(cond)                                            \
+  do {                                                              \
+    if (!(cond)) atomicAdd(&::glq::g_debug_violations, 1u);         \
+  } while (0)
+#define GLQ_DEBUG_COUNTER(fn)                                                       \
+  uint32_t fn() {                                                                   \
+    uint32_t v = 0;                                                                 \
+    const uint32_t zero = 0;                                                        \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_violations), 4) != hipSuccess)   \
+      return 0xFFFFFFFFu;                                                           \
+    (void)hipMemcpyToSymbol(HIP_SYMBOL(g_debug_violations), &zero, 4);              \
+    return v;                                                                       \
+  }
+#else
+#define GLQ_DCHECK(cond) \
+  do {                   \
+  } while (0)
+#define GLQ_DEBUG_COUNTER(fn) \
+  uint32_t fn() { return 0; }
+#endif
+// the counter of each HIP source file (debug builds; 0 otherwise)
+uint32_t debug_violations_rht();
+uint32_t debug_violations_dequant();
+uint32_t debug_violations_gemv();
+uint32_t debug_violations_gemv_lds();
+uint32_t debug_violations_fused_decode();
+uint32_t debug_violations_gemm();
+uint32_t debug_violations_gemm_lds();
+uint32_t debug_violations_gemm_shared();
+uint32_t debug_violations_kv_attention();
+uint32_t debug_violations_noalloc();
+uint32_t debug_violations_gemv_mfma();
+
 // Longest transform done by one workgroup in LDS (16384 fp32 = 64 KiB).  Longer
 // transforms use the Kronecker split H_{a*b} = H_a (x) H_b in two passes.
 constexpr int kSingleLog2 = 14;

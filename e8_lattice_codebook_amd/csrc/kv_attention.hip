@@ -74,6 +74,7 @@ __device__ __forceinline__ float q_value(const void* q, int dt, int64_t i) {
 }
 
 __device__ __forceinline__ uint32_t img_word(const uint32_t* img, uint32_t byte_addr) {
+  GLQ_DCHECK(byte_addr < uint32_t(kImageMaxDwords) * 4u);
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(img) + byte_addr);
 }
 
@@ -331,7 +332,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
     // the caller)
     auto row_at = [&](int32_t pg, int t) {
       pg = min(max(pg, 0), a.num_pages - 1);
-      return (pg * P + (t & (P - 1))) * a.Hkv + h;
+      const int r = (pg * P + (t & (P - 1))) * a.Hkv + h;
+      GLQ_DCHECK(r >= 0 && int64_t(r) < int64_t(a.num_pages) * P * a.Hkv);
+      return r;
     };
     auto word_at = [&](const uint16_t* p) {  // 32 bits at an even element offset
       uint32_t w;
@@ -342,6 +345,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void kv_split_kernel(KvArgs a) {
       if constexpr (BIG) {
         // the tile's first row, uniform; the lanes' rows are fixed offsets from it
         const int64_t r0 = row_at(__builtin_amdgcn_readfirstlane(tp.pk), tp.tk);
+        GLQ_DCHECK(r0 + int64_t(15) * a.Hkv < int64_t(a.num_pages) * P * a.Hkv);
         const uint16_t* pk0 = a.k0 + r0 * GPS + koff;
         const uint16_t* pk1 = a.k1 + r0 * GPS + koff;
 #pragma unroll
@@ -798,5 +802,7 @@ hipError_t launch_kv_attention(const glq_kv_cache& kv, const void* q, glq_dtype 
     default: return run_dg<128, 8>(a, grid, int(B), st, codes, out, out_dt, stream);
   }
 }
+
+GLQ_DEBUG_COUNTER(debug_violations_kv_attention)
 
 }  // namespace glq

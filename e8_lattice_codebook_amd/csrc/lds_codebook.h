@@ -119,6 +119,15 @@ constexpr int kLdsDwords = kResidDwords + kImageMaxDwords;
 __device__ __forceinline__ uint32_t lds_at(const uint32_t* lds, uint32_t byte_addr) {
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lds) + byte_addr);
 }
+// a word of the codebook image (byte offset from kImgOff) / of the residual slots
+__device__ __forceinline__ uint32_t lds_img(const uint32_t* lds, uint32_t byte_addr) {
+  GLQ_DCHECK(byte_addr < uint32_t(kImageMaxDwords) * 4u);
+  return lds_at(lds + kImgOff, byte_addr);
+}
+__device__ __forceinline__ uint32_t lds_res(const uint32_t* lds, uint32_t byte_addr) {
+  GLQ_DCHECK(byte_addr < uint32_t(kResidDwords) * 4u);
+  return lds_at(lds + kResOff, byte_addr);
+}
 
 // Primary-codebook lookup of the 16-bit index in half HI of word w: the page
 // descriptor (image word idx >> 8), then the slot at image byte offset
@@ -126,13 +135,13 @@ __device__ __forceinline__ uint32_t lds_at(const uint32_t* lds, uint32_t byte_ad
 // whose words are read complemented (m again).
 template <int HI>
 __device__ __forceinline__ uint32_t page_desc(const uint32_t* lds, uint32_t w, uint32_t two) {
-  return lds_at(lds + kImgOff, byte_x4<HI ? 3 : 1>(w, two));
+  return lds_img(lds, byte_x4<HI ? 3 : 1>(w, two));
 }
 __device__ __forceinline__ uint32_t page_mask(uint32_t desc) { return uint32_t(__builtin_amdgcn_sbfe(desc, 0, 1)); }
 template <int HI>
 __device__ __forceinline__ uint32_t slot_word(const uint32_t* lds, uint32_t w, uint32_t desc, uint32_t m,
                                               uint32_t two) {
-  return lds_at(lds + kImgOff, (byte_x4<HI ? 2 : 0>(w, two) ^ m) + desc);
+  return lds_img(lds, (byte_x4<HI ? 2 : 0>(w, two) ^ m) + desc);
 }
 
 // Slot-code lookup of the code in half HI of w (the slot image in LDS at kImgOff):
@@ -151,7 +160,7 @@ __device__ __forceinline__ uint32_t code_word(const uint32_t* lds, uint32_t w, u
     asm("v_xor_b32_sdwa %0, sext(%1), %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:DWORD"
         : "=v"(x) : "v"(w), "v"(m));
   }
-  return lds_at(lds + kImgOff, (x + (m & delta)) << 2);
+  return lds_img(lds, (x + (m & delta)) << 2);
 }
 
 // delta of a pack's slot-code format, clamped so that no slot leaves the image
@@ -333,7 +342,7 @@ __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& 
         case 2: a1 = byte_x4<2>(w1, two); break;
         default: a1 = byte_x4<3>(w1, two); break;
       }
-      n1w_[q] = lds_at(lds + kResOff, a1);
+      n1w_[q] = lds_res(lds, a1);
     }
   }
 #pragma unroll
@@ -426,7 +435,7 @@ __device__ __forceinline__ int stage8_total(const uint32_t* lds, const Idx8Row<G
       case 2: a1 = byte_x4<2>(w1, two); break;
       default: a1 = byte_x4<3>(w1, two); break;
     }
-    nw[q] = lds_at(lds + kResOff, a1);
+    nw[q] = lds_res(lds, a1);
   }
   int acc[4];
 #pragma unroll

@@ -42,3 +42,7 @@ extern "C" glq_status glq_e8rht_linear_noalloc(const glq_layer* layer, const voi
   // is plain scratch (no initial contents), so what an earlier call left is harmless
   return glq_e8rht_linear(layer, x, x_dt, B, y, y_dt, ws, size_t(GLQ_NOALLOC_SCRATCH_BYTES), stream);
 }
+
+namespace glq {
+GLQ_DEBUG_COUNTER(debug_violations_noalloc)
+}  // namespace glq

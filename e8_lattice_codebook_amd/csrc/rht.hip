@@ -594,4 +594,6 @@ hipError_t launch_rht_out(const float* z, int64_t S, int64_t B, int64_t m, int64
   return hipErrorInvalidValue;
 }
 
+GLQ_DEBUG_COUNTER(debug_violations_rht)
+
 }  // namespace glq

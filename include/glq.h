@@ -196,6 +196,17 @@ int glq_abi_version(void);
 const char* glq_status_string(glq_status s);
 
 /*
+ * glq_debug_violations — debug builds only (libglq_mi355x_debug.so and
+ * libglq_mi355x_asan.so, compiled with GLQ_DEBUG): the number of device-side bounds
+ * checks that failed since the previous call (reads of the LDS codebook image and
+ * residual slots, prefill operand fragments, KV cache rows), summed over the
+ * library's kernels, and clears the counts.  A failed check does not stop its kernel.
+ * Synchronizes the current device.  Returns -1 in release builds, and UINT32_MAX
+ * counts as an error reading a counter.  Not a data path: for tests and debugging.
+ */
+int64_t glq_debug_violations(void);
+
+/*
  * glq_e8_codebook — build the E8 codebook on the host ("How it works", item 1).
  * Writes the first `entries` points (entries in [1, 65536]) of E8 =
  * D8 u (D8 + 1/2) ordered by squared norm, then lexicographically ascending on

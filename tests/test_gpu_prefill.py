@@ -81,6 +81,35 @@ def test_fragment_order_path_matches_row_order(gpu_codebooks, M):
     assert rel_frob(to_f64(zr[0]), want) <= 1e-5
 
 
+@pytest.mark.parametrize("M", [17, 33, 1001])
+def test_padding_rows_do_not_reach_valid_rows(gpu_codebooks, M):
+    # the operand buffer holds whole 16-token blocks; the rows past M of the last one
+    # (and their row exponents) are filled with NaN here: the outputs of the M valid
+    # rows must not see them (each MFMA row block reads its own rows only), on both
+    # matmul kernels (shared codeword tiles for slot codes, per-wave fragments for
+    # codebook indices)
+    layer = synth.random_layer(2000, 3000, 8, seed=M + 7, n_pad=2048, m_pad=4096)
+    ql = glq.QuantizedLayer.from_synth(layer, gpu_codebooks)
+    qs = ql.to_slot_codes()
+    Mp = (M + 15) // 16 * 16
+    x = np.random.default_rng(M).standard_normal((M, 2000)).astype(np.float32)
+    u16, e = oracle_prefill_u16(x, layer.sign_in, 2048)
+    u_full = np.full((Mp, 2048), np.nan, dtype=np.float16)
+    u_full[:M] = u16
+    e_full = np.full(Mp, 0x7FFFFFFF, dtype=np.int64)  # the non-finite-row marker
+    e_full[:M] = e
+    buf = fragment_buffer(u_full, e_full.astype(np.int32), DEV)
+    want = og.matmul_z(u16_as_f64(u16, e), layer.idx0, layer.idx1, 8, layer.wscale, layer.resid_scale)
+    sc = np.exp2(-e)[:, None]
+    for q in (qs, ql):
+        say("prefill padding rows", M, q.index_format)
+        z = glq.e8_matmul_prefill(q, buf, M)
+        torch.cuda.synchronize()
+        zf = to_f64(z[0])
+        assert np.all(np.isfinite(zf)), M
+        assert rel_frob(zf * sc, want * sc) <= 1e-5
+
+
 # Slot-code layers at many tiles per compute unit (m_pad 8192: 32 output tiles of
 # 256; M = 1000 gives 8 token tiles of 128, the last with 104 tokens and a token
 # block of 8; M = 2049 gives 17, the last with one token).  The operand comes from the
