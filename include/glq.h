@@ -25,9 +25,12 @@
  * Conventions for every entry point:
  *   - Pointers marked "device" are HIP device pointers on the current device;
  *     "host" pointers are ordinary host memory.  The caller owns every buffer;
- *     the library allocates and frees nothing.  Its only mutable state is a
- *     per-device cache of the compute-unit count and of one kernel attribute,
- *     updated atomically, so calls from several host threads are safe.
+ *     the library allocates and frees nothing.  Its mutable state: a per-device
+ *     cache of the compute-unit count and of one kernel attribute, updated
+ *     atomically, so calls from several host threads are safe; the device array
+ *     that glq_e8rht_linear_noalloc uses as its workspace (one per device, shared
+ *     by its calls); and, in debug builds only, the bounds-check counters that
+ *     glq_debug_violations reads.
  *   - Device work is enqueued asynchronously on `stream` (0 = null stream); the
  *     library never synchronizes, so calls are safe under stream capture.
  *   - Arrays are dense and row-major.  n_pad and m_pad are powers of two in
