@@ -256,6 +256,10 @@ def main():
     result["other_index_format"] = {"index_format": "codebook indices" if slot else "slot codes",
                                     "value": round(other_value, 2), "unit": "GB/s", "steps": other_steps}
 
+    if args.only == "decode":
+        # the decode leg alone (profiler runs): no other leg, no CPU baseline
+        print(json.dumps(result), flush=True)
+        return
     if not args.no_configs:
         result["configs"] = bench_configs(glq, synth, cb, dev, args, log, devstral=(host_layers, qls, copies))
 

@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   }
   __syncthreads();
   uint32_t dig[1][GL][4];
-  int32_t gs[1][GL];
+  GroupSumsFor<1, GL, CODES> gs;
   float sc[1];
 #pragma unroll
   for (int q = 0; q < GL; ++q) {
@@ -435,10 +435,10 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
 #pragma unroll
   for (int qq = 0; qq < 2; ++qq) {
     const img_x4 g = *reinterpret_cast<const img_x4*>(lds + kGsOff + 4 * (qq * LPR + lane_in_row));
-    gs[0][4 * qq + 0] = int32_t(g.x);
-    gs[0][4 * qq + 1] = int32_t(g.y);
-    gs[0][4 * qq + 2] = int32_t(g.z);
-    gs[0][4 * qq + 3] = int32_t(g.w);
+    gs.set(0, 4 * qq + 0, int32_t(g.x));
+    gs.set(0, 4 * qq + 1, int32_t(g.y));
+    gs.set(0, 4 * qq + 2, int32_t(g.z));
+    gs.set(0, 4 * qq + 3, int32_t(g.w));
   }
   // the chunk exponent E (wave-uniform) and the lane's scale relative to 2^E
   const int chunk_exp = __builtin_amdgcn_readfirstlane(int(lds[kExpOff]));
@@ -480,15 +480,37 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
     else
       load_off(row_off(r < r_end ? r : r_end - 1), ix);
   };
-  // two row-steps per iteration on two register sets, each loaded one step ahead
-  RowIdx<GL, X16> m;
-  for (int r = r_begin; r < r_end; r += 2) {
-    load_row(r + 1, m);
-    row_step(n, r);
-    if (r + 1 < r_end) {
+  // The rows' index vectors are loaded ahead into a ring of register sets (rows past
+  // r_end load the last row again): with at most two index stages per row, three
+  // sets, each loaded two row-steps ahead; with more stages (5-8 bpw, whose rows
+  // already carry 3-4 vectors) two sets, one step ahead, so the sets stay in
+  // registers.  Whole turns of the ring run in a loop with no early exit (an exit
+  // merged into the loop latch makes the compiler wait for every load at the loop
+  // head), then the remaining rows.
+  constexpr bool kDeep = X16 == 0 && X8 == 0;
+  RowIdx<GL, X16> m, p;
+  int r = r_begin;
+  if constexpr (kDeep) {
+    if (r_begin < r_end) load_row(r_begin + 1, m);
+    for (; r + 2 < r_end; r += 3) {
+      load_row(r + 2, p);
+      row_step(n, r);
+      load_row(r + 3, n);
+      row_step(m, r + 1);
+      load_row(r + 4, m);
+      row_step(p, r + 2);
+    }
+    if (r < r_end) row_step(n, r);
+    if (r + 1 < r_end) row_step(m, r + 1);
+  } else {
+    (void)p;
+    for (; r + 1 < r_end; r += 2) {
+      load_row(r + 1, m);
+      row_step(n, r);
       load_row(r + 2, n);
       row_step(m, r + 1);
     }
+    if (r < r_end) row_step(n, r);
   }
 
   // ---- step 4: H_R of each of the workgroup's row blocks into z_parts[split]

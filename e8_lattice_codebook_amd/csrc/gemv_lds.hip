@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
   const uint16_t* idx1_16 = static_cast<const uint16_t*>(idx1v);
 
   uint32_t dig[NB][GL][4];
-  int32_t gs[NB][GL];
+  GroupSumsFor<NB, GL, CODES> gs;
   float sc[NB];
   int wexp[NB];
 
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void gemv_lds_kernel(
         for (int q = 0; q < GL; ++q) {
           const uint4 v = reinterpret_cast<const uint4*>(uq_dig)[bb * G + g0 + q];
           dig[b][q][0] = v.x; dig[b][q][1] = v.y; dig[b][q][2] = v.z; dig[b][q][3] = v.w;
-          gs[b][q] = -uq_sum[bb * G + g0 + q];  // negated: added on complemented reads
+          gs.set(b, q, -uq_sum[bb * G + g0 + q]);  // negated: added on complemented reads
         }
         sc[b] = b < B ? uq_scale[bb * nblk + (g0 >> bg_log2)] : 0.0f;
       }

@@ -110,6 +110,32 @@ __device__ __forceinline__ uint32_t byte_x4(uint32_t w, uint32_t two) {
   return r;
 }
 
+// 4 * the 16-bit half HI of w in one instruction
+template <int HI>
+__device__ __forceinline__ uint32_t word_x4(uint32_t w, uint32_t two) {
+  uint32_t r;
+  if constexpr (HI == 0)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_0"
+        : "=v"(r) : "v"(two), "v"(w));
+  else
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+        : "=v"(r) : "v"(two), "v"(w));
+  return r;
+}
+
+// n ^ m for the 16-bit mask (0 or 0xFFFF) in half HI of mm, sign-extended to 32 bits
+template <int HI>
+__device__ __forceinline__ uint32_t xor_half_mask(uint32_t n, uint32_t mm) {
+  uint32_t r;
+  if constexpr (HI == 0)
+    asm("v_xor_b32_sdwa %0, sext(%1), %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:DWORD"
+        : "=v"(r) : "v"(mm), "v"(n));
+  else
+    asm("v_xor_b32_sdwa %0, sext(%1), %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1 src1_sel:DWORD"
+        : "=v"(r) : "v"(mm), "v"(n));
+  return r;
+}
+
 // LDS layout of the decode kernel (dwords): [0, 256) the 8-bit residual slots,
 // [256, 256 + image) the primary image (page table, then slots).
 constexpr int kResOff = 0;
@@ -162,6 +188,22 @@ __device__ __forceinline__ uint32_t code_word(const uint32_t* lds, uint32_t w, u
   }
   return lds_img(lds, (x + (m & delta)) << 2);
 }
+
+// The slot-code lookups of both codes of w, on 16-bit halves: mm gets the two masks
+// (0 or 0xFFFF per half), each half's slot is (code ^ m) + (m & delta), formed as
+// (code ^ m) + m * ndelta2 modulo 2^16 with ndelta2 = -delta in both halves (m = -1
+// as int16).  No half can carry into the other: every slot is below 2^16.
+__device__ __forceinline__ void code_pair(const uint32_t* lds, uint32_t w, uint32_t ndelta2, uint32_t& mm,
+                                          uint32_t& n_lo, uint32_t& n_hi) {
+  const uint32_t fifteen = 0x000F000Fu, two = 2;
+  uint32_t slot;
+  asm("v_pk_ashrrev_i16 %0, %1, %2" : "=v"(mm) : "v"(fifteen), "v"(w));
+  const uint32_t x = w ^ mm;
+  asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(slot) : "v"(mm), "v"(ndelta2), "v"(x));
+  n_lo = lds_img(lds, word_x4<0>(slot, two));
+  n_hi = lds_img(lds, word_x4<1>(slot, two));
+}
+__device__ __forceinline__ uint32_t pair_ndelta(uint32_t delta) { return ((0u - delta) & 0xFFFFu) * 0x10001u; }
 
 // delta of a pack's slot-code format, clamped so that no slot leaves the image
 __device__ __forceinline__ uint32_t slot_delta(const uint32_t* pack_hdr) {
@@ -284,18 +326,63 @@ __device__ __forceinline__ int sdot8_acc(uint32_t a, uint32_t b, int c, bool fir
   return first ? sdot8_zero(a, b) : __builtin_amdgcn_sdot8(int(a), int(b), c, false);
 }
 
+// ---- the groups' activation sums -------------------------------------------------------
+// gs = -sum_j U_j of a group (|gs| < 2^18), added once per complemented read to undo
+// its -1s.  With codebook indices every lookup has a 32-bit mask m and gs is added as
+// m * gs.  With slot codes (GL >= 2) the masks of a word's two lookups are 16-bit
+// halves (0 or -1), so the sums of groups 2k and 2k + 1 are kept as two int16 pairs,
+// gs = 256 gh + gl with gl in [0, 256), and m * gs is added to the 1s and 256s digit
+// planes by two 16-bit dot products per pair.
+template <int NB, int GL, bool PAIRS>
+struct GroupSums {
+  int32_t g[NB][GL];
+  __device__ __forceinline__ void set(int b, int q, int32_t v) { g[b][q] = v; }
+};
+template <int NB, int GL>
+struct GroupSums<NB, GL, true> {
+  static_assert(GL % 2 == 0, "group sums in pairs need an even group count");
+  uint32_t lo[NB][GL / 2], hi[NB][GL / 2];
+  // groups are set in increasing q, the even one of a pair first
+  __device__ __forceinline__ void set(int b, int q, int32_t v) {
+    const uint32_t l = uint32_t(v) & 0xFFu, h = uint32_t(v >> 8) & 0xFFFFu;
+    if (q & 1) {
+      lo[b][q >> 1] |= l << 16;
+      hi[b][q >> 1] |= h << 16;
+    } else {
+      lo[b][q >> 1] = l;
+      hi[b][q >> 1] = h;
+    }
+  }
+};
+template <int NB, int GL, bool CODES>
+using GroupSumsFor = GroupSums<NB, GL, CODES && GL >= 2>;
+
+typedef short glq_short2 __attribute__((ext_vector_type(2)));
+// acc + the int16 dot product of the halves of a and b; the first one of a sum in the
+// VOP3P form with a zero accumulator (as sdot8_zero)
+__device__ __forceinline__ int sdot2_acc(uint32_t a, uint32_t b, int acc, bool first) {
+  if (first) {
+    int r;
+    asm("v_dot2_i32_i16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+  }
+  return __builtin_amdgcn_sdot2(__builtin_bit_cast(glq_short2, a), __builtin_bit_cast(glq_short2, b), acc, false);
+}
+
 // ---- one row-step: the lane's GL groups against NB activation rows -------------------
 // v[b] = T0 + sr * T1 with T_k = sum over the lane's columns of 2 c_k U (exact
 // integers, converted once to fp32): stage-0 codewords from the primary image,
 // stage-1 codewords from the primary image (16-bit residual) or the residual
 // slots (8-bit residual).  Reads go in three phases (every page descriptor,
 // every slot word, then the dot products) so the LDS latencies overlap.  On a
-// descending page the complemented word n ^ ~0 has lanes -2c - 1, and the
-// group's -sum_j U_j (gs) is added to plane 0 to undo the -1s.
+// descending page (or a negative slot code) the complemented word n ^ ~0 has
+// lanes -2c - 1, and the group's -sum_j U_j is added to undo the -1s.
 template <int NB, int GL, int RESID, bool CODES>
 __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& i0, const IdxRow<GL>& i1w,
                                          const Idx8Row<GL>& i1b, const uint32_t (&dig)[NB][GL][4],
-                                         const int32_t (&gs)[NB][GL], float sr, float (&v)[NB], uint32_t delta) {
+                                         const GroupSumsFor<NB, GL, CODES>& gs, float sr, float (&v)[NB],
+                                         uint32_t delta) {
+  constexpr bool PAIRS = CODES && GL >= 2;
   const uint32_t two = 2;
   int acc0[NB][4], acc1[NB][4];
 #pragma unroll
@@ -303,8 +390,16 @@ __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& 
 #pragma unroll
     for (int p = 0; p < 4; ++p) acc1[b][p] = 0;
   }
+  // m0/m1: per-lookup 32-bit masks, or (PAIRS) the 16-bit mask pair of index word k
   uint32_t d0[GL], d1[GL], m0[GL], m1[GL], n0w[GL], n1w_[GL];
-  if constexpr (CODES) {
+  if constexpr (PAIRS) {
+    const uint32_t nd = pair_ndelta(delta);
+#pragma unroll
+    for (int k = 0; k < GL / 2; ++k) {
+      code_pair(lds, i0.w[k], nd, m0[k], n0w[2 * k], n0w[2 * k + 1]);
+      if (RESID == 16) code_pair(lds, i1w.w[k], nd, m1[k], n1w_[2 * k], n1w_[2 * k + 1]);
+    }
+  } else if constexpr (CODES) {
 #pragma unroll
     for (int q = 0; q < GL; ++q) {
       n0w[q] = (q & 1) ? code_word<1>(lds, i0.w[q >> 1], delta, m0[q]) : code_word<0>(lds, i0.w[q >> 1], delta, m0[q]);
@@ -345,25 +440,36 @@ __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& 
       n1w_[q] = lds_res(lds, a1);
     }
   }
+  // the stage's complement corrections and dot products for group q into acc
+  auto stage_q = [&](int (&acc)[NB][4], const uint32_t (&nw)[GL], const uint32_t (&mk)[GL], int q) {
+    uint32_t n;
+    if constexpr (PAIRS) {
+      n = (q & 1) ? xor_half_mask<1>(nw[q], mk[q >> 1]) : xor_half_mask<0>(nw[q], mk[q >> 1]);
+      if ((q & 1) == 0) {
 #pragma unroll
-  for (int q = 0; q < GL; ++q) {
-    const int32_t m = int32_t(m0[q]);
-    const uint32_t n = n0w[q] ^ m0[q];
+        for (int b = 0; b < NB; ++b) {
+          acc[b][0] = sdot2_acc(mk[q >> 1], gs.lo[b][q >> 1], acc[b][0], q == 0);
+          acc[b][2] = sdot2_acc(mk[q >> 1], gs.hi[b][q >> 1], acc[b][2], q == 0);
+        }
+      }
+    } else {
+      n = nw[q] ^ mk[q];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b][0] = __mul24(int32_t(mk[q]), gs.g[b][q]) + (q == 0 ? 0 : acc[b][0]);
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      acc0[b][0] = __mul24(m, gs[b][q]) + (q == 0 ? 0 : acc0[b][0]);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) acc0[b][p] = sdot8_acc(n, dig[b][q][p], acc0[b][p], q == 0 && p > 0);
-    }
-    if (RESID == 16) {
-      const uint32_t n1 = n1w_[q] ^ m1[q];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        acc1[b][0] = __mul24(int32_t(m1[q]), gs[b][q]) + (q == 0 ? 0 : acc1[b][0]);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) acc1[b][p] = sdot8_acc(n1, dig[b][q][p], acc1[b][p], q == 0 && p > 0);
+      for (int p = 0; p < 4; ++p) {
+        const bool seeded = p == 0 || (PAIRS && p == 2);  // started by a correction above
+        acc[b][p] = sdot8_acc(n, dig[b][q][p], acc[b][p], q == 0 && !seeded);
       }
     }
+  };
+#pragma unroll
+  for (int q = 0; q < GL; ++q) {
+    stage_q(acc0, n0w, m0, q);
+    if (RESID == 16) stage_q(acc1, n1w_, m1, q);
     if (RESID == 8) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
@@ -390,11 +496,16 @@ __device__ __forceinline__ void row_dots(const uint32_t* lds, const IdxRow<GL>& 
 // row_dots) or of an 8-bit stage (the 256-entry residual slots, no complement).
 template <int GL, bool CODES>
 __device__ __forceinline__ int stage16_total(const uint32_t* lds, const IdxRow<GL>& ix,
-                                             const uint32_t (&dig)[1][GL][4], const int32_t (&gs)[1][GL],
+                                             const uint32_t (&dig)[1][GL][4], const GroupSumsFor<1, GL, CODES>& gs,
                                              uint32_t delta) {
+  constexpr bool PAIRS = CODES && GL >= 2;
   const uint32_t two = 2;
   uint32_t nw[GL], mm[GL];
-  if constexpr (CODES) {
+  if constexpr (PAIRS) {
+    const uint32_t nd = pair_ndelta(delta);
+#pragma unroll
+    for (int k = 0; k < GL / 2; ++k) code_pair(lds, ix.w[k], nd, mm[k], nw[2 * k], nw[2 * k + 1]);
+  } else if constexpr (CODES) {
 #pragma unroll
     for (int q = 0; q < GL; ++q)
       nw[q] = (q & 1) ? code_word<1>(lds, ix.w[q >> 1], delta, mm[q]) : code_word<0>(lds, ix.w[q >> 1], delta, mm[q]);
@@ -412,10 +523,22 @@ __device__ __forceinline__ int stage16_total(const uint32_t* lds, const IdxRow<G
   int acc[4];
 #pragma unroll
   for (int q = 0; q < GL; ++q) {
-    const uint32_t n = nw[q] ^ mm[q];
-    acc[0] = __mul24(int32_t(mm[q]), gs[0][q]) + (q == 0 ? 0 : acc[0]);
+    uint32_t n;
+    if constexpr (PAIRS) {
+      n = (q & 1) ? xor_half_mask<1>(nw[q], mm[q >> 1]) : xor_half_mask<0>(nw[q], mm[q >> 1]);
+      if ((q & 1) == 0) {
+        acc[0] = sdot2_acc(mm[q >> 1], gs.lo[0][q >> 1], acc[0], q == 0);
+        acc[2] = sdot2_acc(mm[q >> 1], gs.hi[0][q >> 1], acc[2], q == 0);
+      }
+    } else {
+      n = nw[q] ^ mm[q];
+      acc[0] = __mul24(int32_t(mm[q]), gs.g[0][q]) + (q == 0 ? 0 : acc[0]);
+    }
 #pragma unroll
-    for (int p = 0; p < 4; ++p) acc[p] = sdot8_acc(n, dig[0][q][p], acc[p], q == 0 && p > 0);
+    for (int p = 0; p < 4; ++p) {
+      const bool seeded = p == 0 || (PAIRS && p == 2);
+      acc[p] = sdot8_acc(n, dig[0][q][p], acc[p], q == 0 && !seeded);
+    }
   }
   return ((acc[3] * 16 + acc[2]) * 16 + acc[1]) * 16 + acc[0];
 }
