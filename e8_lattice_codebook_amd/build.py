@@ -35,7 +35,7 @@ VARIANTS = {
 }
 
 SOURCES = ["api.cpp", "e8_codebook.cpp", "pack.cpp", "rht.hip", "dequant.hip", "gemv.hip", "gemv_lds.hip",
-           "fused_decode.hip", "gemm.hip", "gemm_lds.hip", "gemm_shared.hip", "kv_attention.hip", "noalloc.hip", "gemv_mfma.hip"]
+           "fused_decode.hip", "gemm.hip", "gemm_lds.hip", "gemm_shared.hip", "kv_attention.hip", "noalloc.hip", "gemv_i8.hip"]
 
 COMMON = ["-fPIC", "-std=c++17", "-I" + INCLUDE, "-I" + CSRC, "-Wall", "-Wno-unused-function"]
 # packed fp32 arithmetic stays off for all device code

@@ -158,7 +158,7 @@ bool skinny_ok(const glq_layer& L, int64_t B) {
   if (B < kSkinnyMinB || B > kDecodeMaxB) return false;
   if (L.m_pad * (L.n_pad / 8) < (int64_t(1) << 21)) return false;
   const Passes P = split_passes(L);
-  return gemv_mfma_supported(P.a) && (!P.two || gemv_mfma_supported(P.b));
+  return gemv_i8_supported(P.a) && (!P.two || gemv_i8_supported(P.b));
 }
 
 // the decode kernel with the LDS codebook needs the 16-bit residual stage (if
@@ -187,12 +187,14 @@ LinearWs linear_ws(const glq_layer& L, int64_t B) {
     w.total = off + align256(fused_decode_z_bytes(L));
     return w;
   }
-  if (w.skinny) {  // fp16 u in fragment order (+ row exponents), split partials, output scratch
+  if (w.skinny) {  // fp32 u, its int8 planes (+ row info), split partials, output scratch
     w.u_off = off;
-    off += prefill_u_total_bytes(B, L.n_pad);
+    off += align256(size_t(B) * size_t(L.n_pad) * 4);
+    w.uq_off = off;
+    off += align256(i8_planes_bytes(L.n_pad)) + align256(16 * sizeof(I8RowInfo));
     w.rin_off = off;
-    if (rht_needs_ws(B, L.n_pad, false)) off += align256(size_t(B) * size_t(L.n_pad) * 4);
-    w.splits = gemv_mfma_splits(L.n_pad, L.m_pad);
+    if (rht_needs_ws(B, L.n_pad, true)) off += align256(size_t(B) * size_t(L.n_pad) * 4);
+    w.splits = gemv_i8_splits(L.n_pad, L.m_pad);
     w.z_off = off;
     off += align256(size_t(w.splits) * size_t(B) * size_t(L.m_pad) * 4);
     w.rout_off = off;
@@ -265,7 +267,7 @@ int64_t glq_debug_violations(void) {
   const uint32_t parts[] = {debug_violations_rht(),       debug_violations_dequant(),   debug_violations_gemv(),
                             debug_violations_gemv_lds(),  debug_violations_fused_decode(),
                             debug_violations_gemm(),      debug_violations_gemm_lds(),  debug_violations_gemm_shared(),
-                            debug_violations_kv_attention(), debug_violations_noalloc(), debug_violations_gemv_mfma()};
+                            debug_violations_kv_attention(), debug_violations_noalloc(), debug_violations_gemv_i8()};
   int64_t total = 0;
   for (uint32_t v : parts) total += v == 0xFFFFFFFFu ? int64_t(1) << 32 : int64_t(v);
   return total;
@@ -445,17 +447,18 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
   hipError_t e;
   float* z = at<float>(workspace, w.z_off);
   if (w.skinny) {
-    // fp16 operands with a power-of-two scale per row, in the fragment order of one
-    // 16-row block; every pass of the layer on the matrix units
-    half_t* u = at<half_t>(workspace, w.u_off);
-    int32_t* rexp = at<int32_t>(workspace, w.u_off + prefill_rexp_offset(B, L.n_pad));
-    e = launch_row_exp(x, x_dt, B, L.n, rexp, stream);
+    // u in fp32, then 15-bit fixed point per row as two int8 planes; every pass of the
+    // layer on the int8 matrix units
+    float* u = at<float>(workspace, w.u_off);
+    char* planes = at<char>(workspace, w.uq_off);
+    I8RowInfo* info = reinterpret_cast<I8RowInfo*>(planes + align256(i8_planes_bytes(L.n_pad)));
+    e = launch_rht_in(x, x_dt, B, L.n, L.n_pad, L.sign_in, u, GLQ_F32, at<float>(workspace, w.rin_off), stream);
     if (e != hipSuccess) return GLQ_ERR_HIP;
-    e = launch_rht_in_tiled(x, x_dt, B, L.n, L.n_pad, L.sign_in, rexp, u, at<float>(workspace, w.rin_off), stream);
+    e = launch_quant_i8(u, B, L.n_pad, planes, info, stream);
     if (e != hipSuccess) return GLQ_ERR_HIP;
     const Passes P = split_passes(L);
-    e = launch_gemv_mfma(P.a, u, rexp, B, z, stream, false);
-    if (e == hipSuccess && P.two) e = launch_gemv_mfma(P.b, u, rexp, B, z, stream, true);
+    e = launch_gemv_i8(P.a, planes, info, B, z, stream, false);
+    if (e == hipSuccess && P.two) e = launch_gemv_i8(P.b, planes, info, B, z, stream, true);
     if (e != hipSuccess) return GLQ_ERR_HIP;
   } else if (!w.prefill) {
     float* u = at<float>(workspace, w.u_off);

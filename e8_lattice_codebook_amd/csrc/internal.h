@@ -45,7 +45,7 @@ uint32_t debug_violations_gemm_lds();
 uint32_t debug_violations_gemm_shared();
 uint32_t debug_violations_kv_attention();
 uint32_t debug_violations_noalloc();
-uint32_t debug_violations_gemv_mfma();
+uint32_t debug_violations_gemv_i8();
 
 // Longest transform done by one workgroup in LDS (16384 fp32 = 64 KiB).  Longer
 // transforms use the Kronecker split H_{a*b} = H_a (x) H_b in two passes.
@@ -182,13 +182,21 @@ hipError_t launch_quant_u(const float* u, int64_t B, int64_t n_pad, void* uq, hi
 hipError_t launch_gemv_lds(const glq_layer& layer, const void* uq, int64_t B, float* z_parts, hipStream_t stream,
                            bool accumulate = false);
 
-// Decode matmul for a few activation rows (4 <= B <= 16) on the matrix units: fp16
-// u in the prefill's fragment order (one 16-token block, with its row exponents),
-// z_parts [S][B][m_pad] with S = gemv_mfma_splits(n_pad, m_pad).
-bool gemv_mfma_supported(const glq_layer& layer);
-int gemv_mfma_splits(int64_t n_pad, int64_t m_pad);
-hipError_t launch_gemv_mfma(const glq_layer& layer, const half_t* u16, const int32_t* rexp, int64_t B, float* z_parts,
-                            hipStream_t stream, bool accumulate = false);
+// Decode matmul for a few activation rows (4 <= B <= 16) on the int8 matrix units.  u
+// (fp32 [B][n_pad]) is quantized per row to 15-bit fixed point, two int8 planes in the
+// operand order (i8_planes_bytes(n_pad)) plus an I8RowInfo per row of the 16-row
+// operand; z_parts [S][B][m_pad] with S = gemv_i8_splits(n_pad, m_pad).
+struct I8RowInfo {
+  int32_t e;     // U = rint(u 2^(14 - e))
+  float poison;  // 0, or NaN for a row with a NaN or infinity
+};
+bool gemv_i8_supported(const glq_layer& layer);
+int gemv_i8_splits(int64_t n_pad, int64_t m_pad);
+size_t i8_planes_bytes(int64_t n_pad);
+hipError_t launch_quant_i8(const float* u, int64_t B, int64_t n_pad, void* planes, I8RowInfo* info,
+                           hipStream_t stream);
+hipError_t launch_gemv_i8(const glq_layer& layer, const void* planes, const I8RowInfo* info, int64_t B,
+                          float* z_parts, hipStream_t stream, bool accumulate = false);
 
 // The whole linear for B = 1 in two launches (input RHT, decode matmul with the
 // LDS codebook and the row-local part of the output RHT; then the fixed-order

@@ -2,7 +2,8 @@
 
 glq 0.5.1, "How it works" items 2-4 and "Inference kernels": the layer is linear in
 x, so y(2^k x) = 2^k y(x) exactly in the oracle.  The library's reduced-precision
-steps (16-bit fixed point per 64 columns for B <= 16, fp16 operands for B > 16)
+steps (16-bit fixed point per 64 columns or 15-bit per row for B <= 16, fp16 operands for
+B > 16)
 carry power-of-two scales, so its result scales the same way while y stays in the
 fp32 range: checked against the library's own unscaled output (relative Frobenius
 <= 1e-6, which leaves room only for subnormal rounding of the smallest outputs) and
@@ -14,7 +15,7 @@ Paths: B = 1 (the two-launch decode), B = 5 (the staged integer decode), M = 40
 (prefill, the shared-tile kernel of slot codes and the per-wave kernel of codebook
 indices), M = 160 (prefill with the persistent one-row-per-workgroup output
 transform), and B = 5 and 16 on a layer of 2^22 groups (2048 -> 16384: the decode on
-the matrix units, fp16 operands with row exponents).
+the int8 matrix units, 15-bit fixed point per row).
 """
 import numpy as np
 import pytest
