@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=1 << 28, help="BYTES of the --calibrate-copy run summarized")
     ap.add_argument("--only", choices=LEGS, help="run one leg alone (profiler runs)")
     ap.add_argument("--config-calls", type=int, default=200, help="timed calls per layer in the configs leg")
+    ap.add_argument("--config-workloads", nargs="+", metavar="KEY",
+                    help="only these workloads in the configs leg (profiler runs)")
     ap.add_argument("--pmc-report", nargs="+", metavar="ARG",
                     help="OUT KERNEL DIR [DIR ...]: medians of every counter of the dispatches whose name "
                          "contains KERNEL in rocprofv3 --pmc folders DIR, written to OUT with --pmc-cmd")
@@ -410,12 +412,15 @@ def bench_configs(glq, synth, cb, dev, args, log, devstral=None):
     copies), calls timed back to back with one pair of events.  GB/s counts index,
     activation, output and sign bytes per call; frac is against the 8 TB/s HBM peak.
     B = 1 runs the two-launch fused decode, 2 <= B <= 16 the staged decode (input RHT,
-    quantization, LDS-codebook GEMV, output RHT)."""
+    quantization, GEMV, output RHT; the GEMV on the int8 matrix units for 4 <= B <= 16 on
+    layers of at least 2^21 groups)."""
     import numpy as np
     import torch
 
     out = []
     for key, batches in CONFIG_LEGS:
+        if args.config_workloads and key not in args.config_workloads:
+            continue
         wl = synth.WORKLOADS[key]
         ab = act_bytes(wl.act_dtype)
         tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[wl.act_dtype]
@@ -446,7 +451,9 @@ def bench_configs(glq, synth, cb, dev, args, log, devstral=None):
                 ms = time_calls(torch, calls, reps)
                 nbytes = l.index_bytes() + B * (l.n + l.m) * ab + l.n_pad + l.m_pad
                 gbs = nbytes / (ms * 1e-3) / 1e9
-                path = "fused B=1 (2 launches)" if B == 1 else "staged (input RHT, quantization, GEMV, output RHT)"
+                path = ("fused B=1 (2 launches)" if B == 1 else
+                        "staged (input RHT, quantization, GEMV, output RHT; the GEMV on the int8 matrix units "
+                        "for 4 <= B <= 16 on layers of 2^21+ groups, else the LDS-codebook integer GEMV)")
                 log("bench: %s %s B=%d: %.2f us per call, %.1f GB/s (%d copies)" % (key, shape.name, B, ms * 1e3,
                                                                                    gbs, ncop))
                 out.append({"workload": key, "layer": "%s %d->%d (n_pad %d, m_pad %d)" % (
