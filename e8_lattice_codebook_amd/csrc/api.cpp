@@ -151,12 +151,12 @@ constexpr int64_t kDecodeMaxB = 16;
 // matrix units (its cost per lookup no longer grows with B)
 constexpr int64_t kSkinnyMinB = 4;
 
-// the skinny MFMA decode takes every pass of the layer, and layers of at least 2^21
+// the int8 MFMA decode takes every pass of the layer, and layers of at least 2^19
 // groups (smaller ones are bound by launches and the transforms, where the staged
 // integer GEMV path is as fast)
 bool skinny_ok(const glq_layer& L, int64_t B) {
   if (B < kSkinnyMinB || B > kDecodeMaxB) return false;
-  if (L.m_pad * (L.n_pad / 8) < (int64_t(1) << 21)) return false;
+  if (L.m_pad * (L.n_pad / 8) < (int64_t(1) << 19)) return false;
   const Passes P = split_passes(L);
   return gemv_i8_supported(P.a) && (!P.two || gemv_i8_supported(P.b));
 }

@@ -398,18 +398,25 @@ struct I8Plan {
 };
 
 I8Plan i8_plan(int64_t n_pad, int64_t m_pad) {
-  I8Plan p;
   const int KB = int(n_pad / 256);
-  p.rb = m_pad % 64 == 0 ? 4 : 1;
-  p.threads = p.rb == 4 ? i8_threads<4>() : i8_threads<1>();
-  p.row_groups = int(m_pad / (16 * p.rb));
-  // splits (powers of two dividing KB, at most 16: the output transform sums them per
-  // element) until every wave slot has a unit, keeping at least 4 blocks per unit
-  const int64_t want = int64_t(device_cus()) * (p.threads / 64);
-  int s = 1;
-  while (int64_t(p.row_groups) * s < want && KB % (2 * s) == 0 && KB / (2 * s) >= 4 && s < 16) s *= 2;
-  p.splits = s;
-  p.kbs = KB / s;
+  // four row blocks per wave (8 waves per CU) where its units fill every wave slot,
+  // else one (16 waves per CU); splits (powers of two dividing KB, at most 16: the
+  // output transform sums them per element, and at least 2 blocks per unit) until the
+  // units fill the slots
+  I8Plan p{};
+  for (const int rb : {4, 1}) {
+    if (m_pad % (16 * rb) != 0) continue;
+    p.rb = rb;
+    p.threads = rb == 4 ? i8_threads<4>() : i8_threads<1>();
+    p.row_groups = int(m_pad / (16 * rb));
+    const int64_t slots = int64_t(device_cus()) * (p.threads / 64);
+    int s = 1;
+    while (int64_t(p.row_groups) * s < slots && KB % (2 * s) == 0 && KB / (2 * s) >= 2 && s < 16) s *= 2;
+    p.splits = s;
+    if (rb == 4 && int64_t(p.row_groups) * s < slots) continue;
+    break;
+  }
+  p.kbs = KB / p.splits;
   p.lkbs = 0;
   while ((1 << p.lkbs) < p.kbs) ++p.lkbs;
   p.units = p.row_groups * p.splits;
