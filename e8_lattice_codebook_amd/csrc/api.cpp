@@ -147,16 +147,15 @@ struct LinearWs {
 
 
 constexpr int64_t kDecodeMaxB = 16;
-// from this many activation rows up to kDecodeMaxB the decode matmul runs on the
-// matrix units (its cost per lookup no longer grows with B)
-constexpr int64_t kSkinnyMinB = 4;
-
-// the int8 MFMA decode takes every pass of the layer, and layers of at least 2^19
-// groups (smaller ones are bound by launches and the transforms, where the staged
-// integer GEMV path is as fast)
+// The decode matmul runs on the int8 matrix units for 2 <= B <= kDecodeMaxB on layers
+// of at least 2^21 groups, and from 4 rows on layers of at least 2^19 groups (its cost
+// per codeword does not grow with B; smaller layers and batches are bound by launches
+// and the transforms, where the staged integer GEMV path measured faster), for every
+// pass of the layer.
 bool skinny_ok(const glq_layer& L, int64_t B) {
-  if (B < kSkinnyMinB || B > kDecodeMaxB) return false;
-  if (L.m_pad * (L.n_pad / 8) < (int64_t(1) << 19)) return false;
+  if (B < 2 || B > kDecodeMaxB) return false;
+  const int64_t groups = L.m_pad * (L.n_pad / 8);
+  if (groups < (int64_t(1) << 19) || (B < 4 && groups < (int64_t(1) << 21))) return false;
   const Passes P = split_passes(L);
   return gemv_i8_supported(P.a) && (!P.two || gemv_i8_supported(P.b));
 }
