@@ -412,8 +412,8 @@ def bench_configs(glq, synth, cb, dev, args, log, devstral=None):
     copies), calls timed back to back with one pair of events.  GB/s counts index,
     activation, output and sign bytes per call; frac is against the 8 TB/s HBM peak.
     B = 1 runs the two-launch fused decode, 2 <= B <= 16 the staged decode (input RHT,
-    quantization, GEMV, output RHT; the GEMV on the int8 matrix units for 4 <= B <= 16 on
-    layers of at least 2^21 groups)."""
+    quantization, GEMV, output RHT; the GEMV on the int8 matrix units for 2 <= B <= 16 on
+    layers of at least 2^21 groups and for 4 <= B <= 16 from 2^19)."""
     import numpy as np
     import torch
 
@@ -453,7 +453,8 @@ def bench_configs(glq, synth, cb, dev, args, log, devstral=None):
                 gbs = nbytes / (ms * 1e-3) / 1e9
                 path = ("fused B=1 (2 launches)" if B == 1 else
                         "staged (input RHT, quantization, GEMV, output RHT; the GEMV on the int8 matrix units "
-                        "for 4 <= B <= 16 on layers of 2^21+ groups, else the LDS-codebook integer GEMV)")
+                        "for 2 <= B <= 16 on layers of 2^21+ groups and 4 <= B <= 16 from 2^19, else the "
+                        "LDS-codebook integer GEMV)")
                 log("bench: %s %s B=%d: %.2f us per call, %.1f GB/s (%d copies)" % (key, shape.name, B, ms * 1e3,
                                                                                    gbs, ncop))
                 out.append({"workload": key, "layer": "%s %d->%d (n_pad %d, m_pad %d)" % (
