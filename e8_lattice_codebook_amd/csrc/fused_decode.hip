@@ -251,12 +251,24 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   const uint8_t* idx1_8 = static_cast<const uint8_t*>(a.idx1);
   const uint16_t* idx1_16 = static_cast<const uint16_t*>(a.idx1);
 
-  // the wave's row-steps
+  // the wave's row-steps.  With at most two index stages per row, the waves take the
+  // workgroup's row-steps dynamically, in chunks of three from a counter in LDS, so
+  // that no wave of a SIMD idles while another still has rows: the counter is LDS
+  // word 0 without an 8-bit stage (whose residual slots live there), else the last
+  // word of the image budget, which a slot image never reaches (slot images are at
+  // most kSlotImageMaxDwords); a page image with an 8-bit stage may fill the budget,
+  // and there, as for 5-8 bpw rows, each wave takes a fixed share.
+  // Only a workgroup with at least six row-steps per wave does so: below that, chunks of
+  // three would leave waves without rows.
+  constexpr bool kDynOk = X16 == 0 && X8 == 0 && (RESID != 8 || CODES);
+  constexpr int kCtr = RESID != 8 ? kResOff : kImgOff + kImageMaxDwords - 1;
+  static_assert(kSlotImageMaxDwords < kImageMaxDwords, "the counter word lies above every slot image");
+  const bool dyn = kDynOk && a.rs_per_wg >= 6 * (kThreads / 64);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r_wg0 = wg * a.rs_per_wg;
   const int r_wg1 = min(r_wg0 + a.rs_per_wg, a.row_steps);
-  const int per_wave = (a.rs_per_wg + (kThreads / 64) - 1) / (kThreads / 64);
-  const int r_begin = min(r_wg0 + wave * per_wave, r_wg1);
+  const int per_wave = dyn ? 3 : (a.rs_per_wg + (kThreads / 64) - 1) / (kThreads / 64);
+  const int r_begin = min(r_wg0 + wave * per_wave, r_wg1);  // dyn: the wave's first chunk
   const int r_end = min(r_begin + per_wave, r_wg1);
   auto row_off = [&](int r) {
     const int o = r * RPS + row_in_step;
@@ -446,8 +458,10 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
                                   int(lds[kFeOff + lane_in_row]) - chunk_exp);
   __syncthreads();  // every lane has its digits before image parts 8-9 overwrite them
 
-  // ---- step 3: the rest of the image, then the rows
+  // ---- step 3: the rest of the image (and the chunk counter, its word free now that
+  // the chunk of u is consumed), then the rows
   image_store<8, 10, true, R8>(img, lds, tid);
+  if (dyn && tid == 0) lds[kCtr] = 0u;
   __syncthreads();
 
   // one row-step: the lane's groups of row r against the digit planes, the
@@ -490,7 +504,46 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   constexpr bool kDeep = X16 == 0 && X8 == 0;
   RowIdx<GL, X16> m, p;
   int r = r_begin;
-  if constexpr (kDeep) {
+  if (kDynOk && dyn) {
+    // chunk ch holds row-steps r_wg0 + 3 ch .. + 2 (rows past r_wg1 load the last row
+    // again and are not computed); chunks 0 .. kW-1 go to the waves in order, the rest
+    // by the counter, each taken one chunk ahead so that the ring's loads run on
+    // across chunks.  The loop's only exit is at its head.
+    constexpr int kW = kThreads / 64;
+    const int nch = (r_wg1 - r_wg0 + 2) / 3;
+    auto take = [&]() {
+      uint32_t t = 0;
+      if (lane == 0) t = atomicAdd(lds + kCtr, 1u);
+      return kW + int(__builtin_amdgcn_readfirstlane(t));
+    };
+    auto load_at = [&](int ch, int k, RowIdx<GL, X16>& ix) {
+      int rr = r_wg0 + 3 * ch + k;
+      rr = rr < r_wg1 ? rr : r_wg1 - 1;
+      if (FULL)
+        load_full(rr, ix);
+      else
+        load_off(row_off(rr), ix);
+    };
+    auto step_at = [&](const RowIdx<GL, X16>& ix, int ch, int k) {
+      const int rr = r_wg0 + 3 * ch + k;
+      if (rr < r_wg1) row_step(ix, rr);
+    };
+    int ch = wave;
+    if (ch < nch) {
+      int nx = take();
+      load_at(ch, 1, m);
+      while (ch < nch) {
+        load_at(ch, 2, p);
+        step_at(n, ch, 0);
+        load_at(nx < nch ? nx : ch, 0, n);
+        step_at(m, ch, 1);
+        load_at(nx < nch ? nx : ch, 1, m);
+        step_at(p, ch, 2);
+        ch = nx;
+        if (ch < nch) nx = take();
+      }
+    }
+  } else if (kDeep) {
     if (r_begin < r_end) load_row(r_begin + 1, m);
     for (; r + 2 < r_end; r += 3) {
       load_row(r + 2, p);
