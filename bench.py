@@ -698,6 +698,39 @@ def bench_block_graph(glq, synth, cb, dev, args, log):
     graph_ms = e0.elapsed_time(e1) / n
     log("bench: SmolLM3 block B=1: eager %.4f ms, graph %.4f ms per block (replay equals eager: %s)" % (
         eager_ms, graph_ms, same))
+
+    # the same block with the linears that a decoder block can run together as groups
+    # (glq_e8rht_linear_group): q, k, v; o; gate, up; down -- 8 launches instead of 14
+    groups = [(0, 1, 2), (3,), (4, 5), (6,)]
+    gws = torch.empty(max(glq.linear_group_workspace_bytes([qs[k] for k in gr], 1) for gr in groups),
+                      dtype=torch.uint8, device=dev)
+
+    def block_grouped():
+        for gr in groups:
+            glq.e8rht_linear_group([qs[k] for k in gr], [xs[k] for k in gr], outs=[ys[k] for k in gr],
+                                   workspace=gws)
+
+    for _ in range(50):
+        block_grouped()
+    torch.cuda.synchronize()
+    grouped_diff = max(float((y.float() - r.float()).abs().max() / r.float().abs().max())
+                       for y, r in zip(ys, eager_ref))
+    e0.record()
+    for _ in range(n):
+        block_grouped()
+    e1.record()
+    torch.cuda.synchronize()
+    grouped_ms = e0.elapsed_time(e1) / n
+    per_group = []
+    for gr in groups:
+        e0.record()
+        for _ in range(n):
+            glq.e8rht_linear_group([qs[k] for k in gr], [xs[k] for k in gr], outs=[ys[k] for k in gr],
+                                   workspace=gws)
+        e1.record()
+        torch.cuda.synchronize()
+        per_group.append(round(e0.elapsed_time(e1) / n * 1e3, 2))
+    log("bench: SmolLM3 block B=1 grouped: %.4f ms per block; per group (us) %s" % (grouped_ms, per_group))
     return {
         "workload": "SmolLM3-3B decoder block, 7 linears (q, k, v, o 2048-wide; gate, up 2048->11008; down "
                     "11008->2048), 3 bpw, fp16 activations, B=1; %.1f MB of indices, resident in the 256 MB "
@@ -710,6 +743,15 @@ def bench_block_graph(glq, synth, cb, dev, args, log):
         "graph_gbs": round(nbytes / (graph_ms * 1e-3) / 1e9, 1),
         "replay_equals_eager": bool(same),
         "launches_per_block": 2 * len(host),
+        "grouped": {
+            "groups": "q+k+v, o, gate+up, down (glq_e8rht_linear_group: one pair of launches per group)",
+            "ms_per_block": round(grouped_ms, 5),
+            "us_per_group": per_group,
+            "gbs": round(nbytes / (grouped_ms * 1e-3) / 1e9, 1),
+            "speedup_vs_eager": round(eager_ms / grouped_ms, 3),
+            "launches_per_block": 2 * len(groups),
+            "max_rel_diff_vs_single_calls": grouped_diff,
+        },
     }
 
 

@@ -270,6 +270,43 @@ def e8rht_linear(layer, x, y_dtype=None, workspace=None, out=None):
     return y
 
 
+GROUP_MAX = 4  # GLQ_GROUP_MAX
+
+
+def _layer_array(layers):
+    arr = (GlqLayer * len(layers))()
+    for k, ql in enumerate(layers):
+        arr[k] = ql.desc
+    return arr
+
+
+def linear_group_workspace_bytes(layers, B):
+    return int(lib().glq_e8rht_linear_group_workspace_bytes(_layer_array(layers), len(layers), B))
+
+
+def e8rht_linear_group(layers, xs, y_dtype=None, workspace=None, outs=None):
+    """The E8RHTLinear forwards y_k [B, m_k] of several layers (glq_e8rht_linear_group):
+    one pair of launches at B = 1 when the layers allow it, else one call per layer.
+
+    xs: one input per layer (the same tensor may be passed for several)."""
+    if len(xs) != len(layers):
+        raise ValueError("one input per layer")
+    xs = [x.contiguous() for x in xs]
+    B = xs[0].shape[0]
+    y_dtype = y_dtype or xs[0].dtype
+    ys = outs if outs is not None else [torch.empty((B, ql.m), dtype=y_dtype, device=xs[0].device) for ql in layers]
+    arr = _layer_array(layers)
+    if workspace is None:
+        nb = int(lib().glq_e8rht_linear_group_workspace_bytes(arr, len(layers), B))
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=xs[0].device)
+    xp = (ctypes.c_void_p * len(xs))(*[_ptr(x) for x in xs])
+    yp = (ctypes.c_void_p * len(ys))(*[_ptr(y) for y in ys])
+    _lib.check(lib().glq_e8rht_linear_group(arr, len(layers), xp, _dt(xs[0].dtype), B, yp, _dt(ys[0].dtype),
+                                            _ptr(workspace), workspace.numel(), _stream(xs[0].device)),
+               "glq_e8rht_linear_group")
+    return ys
+
+
 NOALLOC_SCRATCH_BYTES = 64 << 20  # GLQ_NOALLOC_SCRATCH_BYTES
 
 

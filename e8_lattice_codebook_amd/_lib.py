@@ -73,6 +73,9 @@ SIGNATURES = {
     "glq_e8rht_linear_workspace_bytes": (c_sz, [_LP, c_i64]),
     "glq_e8rht_linear": (ctypes.c_int, [_LP, c_vp, ctypes.c_int, c_i64, c_vp, ctypes.c_int, c_vp, c_sz, c_vp]),
     "glq_e8rht_linear_noalloc": (ctypes.c_int, [_LP, c_vp, ctypes.c_int, c_i64, c_vp, ctypes.c_int, c_vp]),
+    "glq_e8rht_linear_group_workspace_bytes": (c_sz, [_LP, c_i32, c_i64]),
+    "glq_e8rht_linear_group": (ctypes.c_int, [_LP, c_i32, ctypes.POINTER(c_vp), ctypes.c_int, c_i64,
+                                              ctypes.POINTER(c_vp), ctypes.c_int, c_vp, c_sz, c_vp]),
     "glq_e8kv_attention_workspace_bytes": (c_sz, [_KP, c_i64, c_i32, c_i64]),
     "glq_e8kv_attention_decode": (ctypes.c_int, [_KP, c_vp, ctypes.c_int, c_i64, c_i32, c_vp, c_i64, c_vp, c_i64,
                                                  c_f32, c_vp, ctypes.c_int, c_vp, c_sz, c_vp]),

@@ -488,6 +488,58 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
   return from_hip(e);
 }
 
+// the group's workspace: one z_parts region per layer (the grouped launches), or the
+// largest single-layer workspace (one layer after another)
+static size_t group_ws(const glq_layer* layers, int32_t count, int64_t B, bool fused, size_t* z_off) {
+  size_t total = 0;
+  for (int32_t k = 0; k < count; ++k) {
+    if (fused) {
+      if (z_off) z_off[k] = total;
+      total += align256(fused_group_z_bytes(layers, count, k));
+    } else {
+      const size_t t = linear_ws(layers[k], B).total;
+      total = t > total ? t : total;
+    }
+  }
+  return total;
+}
+
+size_t glq_e8rht_linear_group_workspace_bytes(const glq_layer* layers, int32_t count, int64_t B) {
+  if (!layers || count < 1 || count > GLQ_GROUP_MAX || B < 1) return 0;
+  for (int32_t k = 0; k < count; ++k)
+    if (check_layer(&layers[k], true) != GLQ_OK) return 0;
+  return group_ws(layers, count, B, B == 1 && fused_group_supported(layers, count), nullptr);
+}
+
+glq_status glq_e8rht_linear_group(const glq_layer* layers, int32_t count, const void* const* x, glq_dtype x_dt,
+                                  int64_t B, void* const* y, glq_dtype y_dt, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  if (!layers || !x || !y) return GLQ_ERR_NULL;
+  if (count < 1 || count > GLQ_GROUP_MAX) return GLQ_ERR_SHAPE;
+  for (int32_t k = 0; k < count; ++k) {
+    const glq_status st = check_layer(&layers[k], true);
+    if (st != GLQ_OK) return st;
+    if (!x[k] || !y[k]) return GLQ_ERR_NULL;
+  }
+  if (B < 1 || B > int64_t(1) << 31) return GLQ_ERR_SHAPE;
+  if (!valid_dtype(x_dt) || !valid_dtype(y_dt)) return GLQ_ERR_DTYPE;
+  const bool fused = B == 1 && fused_group_supported(layers, count);
+  size_t z_off[GLQ_GROUP_MAX];
+  const size_t need = group_ws(layers, count, B, fused, z_off);
+  if (!workspace || workspace_bytes < need) return GLQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return GLQ_ERR_ALIGN;
+  if (fused) {
+    float* z[GLQ_GROUP_MAX];
+    for (int32_t k = 0; k < count; ++k) z[k] = at<float>(workspace, z_off[k]);
+    return from_hip(launch_fused_group(layers, count, x, x_dt, y, y_dt, z, stream));
+  }
+  for (int32_t k = 0; k < count; ++k) {
+    const glq_status st = glq_e8rht_linear(&layers[k], x[k], x_dt, B, y[k], y_dt, workspace, workspace_bytes, stream);
+    if (st != GLQ_OK) return st;
+  }
+  return GLQ_OK;
+}
+
 static glq_status check_kv(const glq_kv_cache* kv) {
   if (!kv) return GLQ_ERR_NULL;
   if (!kv->k_idx[0] || !kv->v_idx[0] || !kv->k_scale || !kv->v_scale || !kv->cb_pack) return GLQ_ERR_NULL;

@@ -229,8 +229,9 @@ __device__ __forceinline__ int dpp_partner1(int x) { return __builtin_amdgcn_upd
 
 // RESID: the first residual stage (0, 8 or 16 bits); X16, X8: further 16-bit stages
 // (0-2) and a trailing 8-bit stage (0-1) of a 5-8 bpw layer (after RESID 16)
+// The body of one workgroup; bid is the workgroup's number within its layer's grid.
 template <int RESID, int X16, int X8, bool FULL, bool CODES>
-__global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
+__device__ __forceinline__ void fused_decode_body(const FusedArgs& a, int bid) {
   constexpr int GL = 8;
   constexpr int R8 = (RESID == 8 || X8) ? 8 : 0;  // the 8-bit table in LDS
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsDwords];
@@ -239,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const uint32_t delta = CODES ? slot_delta(a.pack0_hdr) : 0u;
-  const int split = int(blockIdx.x) / a.wgs_per_split;
-  const int wg = int(blockIdx.x) - split * a.wgs_per_split;
+  const int split = bid / a.wgs_per_split;
+  const int wg = bid - split * a.wgs_per_split;
   const int lpr = FULL ? 6 : a.lpr_log2;
   const int LPR = 1 << lpr;
   const int RPS = 64 >> lpr;
@@ -591,7 +592,35 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
       fwht_lds_passes<StoreZ, 4>(StoreZ{zb, rows}, 0, span, 0, rowbuf, a.lr);
     }
   }
+}
 
+template <int RESID, int X16, int X8, bool FULL, bool CODES>
+__global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
+  fused_decode_body<RESID, X16, X8, FULL, CODES>(a, int(blockIdx.x));
+}
+
+// Several layers of one launch: layer k owns the workgroups [end[k-1], end[k]) of the
+// grid.  Every layer has the same stage layout (RESID, no further stages) and lanes per
+// row (FULL); the arguments of each are its own.
+constexpr int kGroupMax = 4;
+struct FusedGroupArgs {
+  FusedArgs L[kGroupMax];
+  int end[kGroupMax];
+  int count;
+};
+
+__device__ __forceinline__ int group_member(const int* end, int count, int bid) {
+  int k = 0;
+#pragma unroll
+  for (int j = 0; j < kGroupMax - 1; ++j) k += (j < count - 1 && bid >= end[j]) ? 1 : 0;
+  return k;
+}
+
+template <int RESID, bool FULL, bool CODES>
+__global__ __launch_bounds__(kThreads) void fused_group_kernel(FusedGroupArgs g) {
+  const int bid = int(blockIdx.x);
+  const int k = __builtin_amdgcn_readfirstlane(group_member(g.end, g.count, bid));
+  fused_decode_body<RESID, 0, 0, FULL, CODES>(g.L[k], bid - (k > 0 ? g.end[k - 1] : 0));
 }
 
 // ---- the cross-block part of the output transform ------------------------------------
@@ -656,9 +685,9 @@ __device__ __forceinline__ void store_vec(YT* p, const YT (&o)[CB]) {
 }
 
 template <class YT, int E, int CB>
-__global__ __launch_bounds__(64) void output_blocks_kernel(BlocksArgs a) {
+__device__ __forceinline__ void output_blocks_body(const BlocksArgs& a, int bid) {
   const int lane = threadIdx.x;
-  const int b0 = int(blockIdx.x) * CB;
+  const int b0 = bid * CB;
   const bool live = (lane * E) < a.W;
   float v[E][CB];
   uint32_t sg[E];  // sign bytes of the lane's CB outputs per block (sign_out has m_pad entries)
@@ -763,6 +792,26 @@ __global__ __launch_bounds__(64) void output_blocks_kernel(BlocksArgs a) {
   }
 }
 
+template <class YT, int E, int CB>
+__global__ __launch_bounds__(64) void output_blocks_kernel(BlocksArgs a) {
+  output_blocks_body<YT, E, CB>(a, int(blockIdx.x));
+}
+
+// the cross-block launches of several layers in one: layer k owns the waves
+// [end[k-1], end[k]); E covers the largest W of the group, CB divides every R
+struct BlocksGroupArgs {
+  BlocksArgs L[kGroupMax];
+  int end[kGroupMax];
+  int count;
+};
+
+template <class YT, int E, int CB>
+__global__ __launch_bounds__(64) void blocks_group_kernel(BlocksGroupArgs g) {
+  const int bid = int(blockIdx.x);
+  const int k = __builtin_amdgcn_readfirstlane(group_member(g.end, g.count, bid));
+  output_blocks_body<YT, E, CB>(g.L[k], bid - (k > 0 ? g.end[k - 1] : 0));
+}
+
 template <class YT, int CB>
 hipError_t launch_blocks_e(BlocksArgs a, hipStream_t stream) {
   const dim3 grid(unsigned((1 << a.lr) / CB)), block(64);
@@ -798,7 +847,8 @@ struct FusedPlan {
   bool ok;
 };
 
-FusedPlan fused_plan(const glq_layer& L) {
+// cus: the CUs the layer's launch may fill (all of them for a layer on its own)
+FusedPlan fused_plan(const glq_layer& L, int cus) {
   FusedPlan p;
   const int64_t G = L.n_pad / 8;
   const int64_t lanes = G / 8;
@@ -811,7 +861,7 @@ FusedPlan fused_plan(const glq_layer& L) {
   p.splits = int(G / (int64_t(8) << l));
   p.rps = 64 >> l;
   p.row_steps = int((L.m_pad + p.rps - 1) / p.rps);
-  int w = device_cus() / p.splits;
+  int w = cus / p.splits;
   if (w < 1) w = 1;
   const int min_per_wg = kThreads / 64;  // at least one row-step per wave
   const int wmax = (p.row_steps + min_per_wg - 1) / min_per_wg;
@@ -834,7 +884,7 @@ FusedPlan fused_plan(const glq_layer& L) {
   // rows per workgroup, plus 16 per row block above 2 that each lane of the
   // cross-block launch sums and transforms (W / 64 of them), plus a quarter for
   // R < 64 (fewer than 64 waves there); ties go to the larger R.
-  const int64_t wps = device_cus() / p.splits > 0 ? device_cus() / p.splits : 1;
+  const int64_t wps = cus / p.splits > 0 ? cus / p.splits : 1;
   const int64_t T = (L.m_pad + wps - 1) / wps;
   const int64_t cap = smallest_block(L.m_pad) < kRowBuf ? smallest_block(L.m_pad) : kRowBuf;
   int64_t best_rows = 0, best_R = 0;
@@ -860,22 +910,8 @@ FusedPlan fused_plan(const glq_layer& L) {
   return p;
 }
 
-}  // namespace
-
-bool fused_decode_supported(const glq_layer& L, int64_t B) {
-  // one activation row; 64 <= n_pad (8 groups per lane; the chunk of u, K <= 4096,
-  // always fits); the residual stage in the LDS image; row blocks as fused_plan needs
-  return B == 1 && L.n_pad >= 64 && (L.resid_bits != 16 || L.cb2_pack == L.cb_pack) && fused_plan(L).ok;
-}
-
-size_t fused_decode_z_bytes(const glq_layer& L) {
-  const FusedPlan p = fused_plan(L);
-  return size_t(p.splits) * size_t(L.m_pad) * 4;
-}
-
-hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt, void* y, glq_dtype y_dt,
-                               float* z_parts, hipStream_t stream) {
-  const FusedPlan p = fused_plan(L);
+// the first launch's arguments of one layer under plan p
+FusedArgs fused_args(const glq_layer& L, const FusedPlan& p, const void* x, glq_dtype x_dt, float* z_parts) {
   FusedArgs a;
   a.x = x;
   a.sign_in = L.sign_in;
@@ -919,6 +955,115 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
     a.sc_tab[k] = float(1.0 / (sqrt(double(int64_t(1) << k)) * double(kUqMax)));
   a.out_scale = 0.5f * L.wscale;
   a.sr = L.resid_scale;
+  return a;
+}
+
+// the second launch's arguments of one layer under plan p (vec_sign and vec_y are set
+// by the launcher, which knows its columns per wave)
+BlocksArgs blocks_args(const glq_layer& L, const FusedPlan& p, const float* z_parts, void* y) {
+  BlocksArgs b;
+  b.z = z_parts;
+  b.sign = L.sign_out;
+  b.y = y;
+  b.m = L.m;
+  b.S = p.splits;
+  b.m_pad = int(L.m_pad);
+  b.lr = p.lr;
+  b.W = p.W;
+  b.lw = log2_exact(b.W);
+  b.vec_sign = 0;
+  b.vec_y = 0;
+  for (int k = 0; k < kLenLog2s; ++k) b.sc_tab[k] = float(1.0 / sqrt(double(int64_t(1) << k)));
+  return b;
+}
+
+// the stage layout of a layer as (RESID, further 16-bit stages, further 8-bit stages)
+void stage_layout(const glq_layer& L, int& x16, int& x8) {
+  x16 = (L.n_extra >= 1 && L.extra_bits[0] == 16 ? 1 : 0) + (L.n_extra == 2 && L.extra_bits[1] == 16 ? 1 : 0);
+  x8 = L.n_extra >= 1 && L.extra_bits[L.n_extra - 1] == 8 ? 1 : 0;
+}
+
+// log2 of the lanes that share a row in the group kernel's second launch: the
+// largest W of the group needs E = W / 64 row blocks per lane (at least 1)
+int blocks_e(int lw) { return lw <= 6 ? 1 : 1 << (lw - 6); }
+int blocks_cb(int lr) { return lr >= 8 ? 4 : lr == 7 ? 2 : 1; }
+
+template <class YT, int E, int CB>
+hipError_t launch_blocks_group_ecb(BlocksGroupArgs g, int waves, hipStream_t stream) {
+  for (int k = 0; k < g.count; ++k) {
+    g.L[k].vec_sign = CB == 4 && reinterpret_cast<uintptr_t>(g.L[k].sign) % 4 == 0;
+    g.L[k].vec_y = reinterpret_cast<uintptr_t>(g.L[k].y) % (sizeof(YT) * CB) == 0;
+  }
+  hipLaunchKernelGGL((blocks_group_kernel<YT, E, CB>), dim3(unsigned(waves)), dim3(64), 0, stream, g);
+  return hipGetLastError();
+}
+
+template <class YT, int CB>
+hipError_t launch_blocks_group_cb(BlocksGroupArgs& g, int E, hipStream_t stream) {
+  int waves = 0;
+  for (int k = 0; k < g.count; ++k) {
+    waves += (1 << g.L[k].lr) / CB;
+    g.end[k] = waves;
+  }
+  switch (E) {
+    case 1: return launch_blocks_group_ecb<YT, 1, CB>(g, waves, stream);
+    case 2: return launch_blocks_group_ecb<YT, 2, CB>(g, waves, stream);
+    case 4: return launch_blocks_group_ecb<YT, 4, CB>(g, waves, stream);
+    case 8: return launch_blocks_group_ecb<YT, 8, CB>(g, waves, stream);
+    default: return launch_blocks_group_ecb<YT, 16, CB>(g, waves, stream);
+  }
+}
+
+template <class YT>
+hipError_t launch_blocks_group(BlocksGroupArgs& g, int E, int CB, hipStream_t stream) {
+  if (CB == 4) return launch_blocks_group_cb<YT, 4>(g, E, stream);
+  if (CB == 2) return launch_blocks_group_cb<YT, 2>(g, E, stream);
+  return launch_blocks_group_cb<YT, 1>(g, E, stream);
+}
+
+// the CUs each layer of a group may fill: every layer its own plan when their grids
+// fit the device together, else shares of the CUs in proportion to the layers'
+// index groups (at least one workgroup per split)
+void group_cus(const glq_layer* Ls, int count, int* cus) {
+  const int all = device_cus();
+  int64_t wgs = 0, work = 0;
+  for (int k = 0; k < count; ++k) {
+    const FusedPlan p = fused_plan(Ls[k], all);
+    wgs += int64_t(p.splits) * p.wgs_per_split;
+    work += Ls[k].m_pad * (Ls[k].n_pad / 8);
+  }
+  for (int k = 0; k < count; ++k) {
+    if (wgs <= all) {
+      cus[k] = all;
+    } else {
+      const int64_t share = int64_t(all) * (Ls[k].m_pad * (Ls[k].n_pad / 8)) / work;
+      const int splits = fused_plan(Ls[k], all).splits;
+      cus[k] = int(share > splits ? share : splits);
+    }
+  }
+}
+
+}  // namespace
+
+bool fused_decode_supported(const glq_layer& L, int64_t B) {
+  // one activation row; 64 <= n_pad (8 groups per lane; the chunk of u, K <= 4096,
+  // always fits); the residual stage in the LDS image; row blocks as fused_plan needs
+  return B == 1 && L.n_pad >= 64 && (L.resid_bits != 16 || L.cb2_pack == L.cb_pack) &&
+         fused_plan(L, device_cus()).ok;
+}
+
+size_t fused_decode_z_bytes(const glq_layer& L) {
+  const FusedPlan p = fused_plan(L, device_cus());
+  return size_t(p.splits) * size_t(L.m_pad) * 4;
+}
+
+hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt, void* y, glq_dtype y_dt,
+                               float* z_parts, hipStream_t stream) {
+  const FusedPlan p = fused_plan(L, device_cus());
+  const FusedArgs a = fused_args(L, p, x, x_dt, z_parts);
+  int x16, x8;
+  stage_layout(L, x16, x8);
+  const bool codes = L.index_format == GLQ_INDEX_SLOT;
   const dim3 grid(unsigned(p.splits * p.wgs_per_split)), block(kThreads);
   const bool full = p.lpr_log2 == 6;
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, a); };
@@ -941,21 +1086,76 @@ hipError_t launch_fused_decode(const glq_layer& L, const void* x, glq_dtype x_dt
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  BlocksArgs b;
-  b.z = z_parts;
-  b.sign = L.sign_out;
-  b.y = y;
-  b.m = L.m;
-  b.S = p.splits;
-  b.m_pad = int(L.m_pad);
-  b.lr = p.lr;
-  b.W = p.W;
-  b.lw = log2_exact(b.W);
-  for (int k = 0; k < kLenLog2s; ++k) b.sc_tab[k] = float(1.0 / sqrt(double(int64_t(1) << k)));
+  const BlocksArgs b = blocks_args(L, p, z_parts, y);
   switch (y_dt) {
     case GLQ_F32: return launch_blocks<float>(b, stream);
     case GLQ_F16: return launch_blocks<half_t>(b, stream);
     default: return launch_blocks<bf16_t>(b, stream);
+  }
+}
+
+bool fused_group_supported(const glq_layer* Ls, int count) {
+  if (count < 1 || count > kGroupMax) return false;
+  for (int k = 0; k < count; ++k) {
+    const glq_layer& L = Ls[k];
+    if (!fused_decode_supported(L, 1) || L.n_extra != 0) return false;
+    if (L.n_pad != Ls[0].n_pad || L.resid_bits != Ls[0].resid_bits || L.index_format != Ls[0].index_format)
+      return false;
+  }
+  int cus[kGroupMax];
+  group_cus(Ls, count, cus);
+  for (int k = 0; k < count; ++k)
+    if (!fused_plan(Ls[k], cus[k]).ok) return false;
+  return true;
+}
+
+size_t fused_group_z_bytes(const glq_layer* Ls, int count, int k) {
+  int cus[kGroupMax];
+  group_cus(Ls, count, cus);
+  return size_t(fused_plan(Ls[k], cus[k]).splits) * size_t(Ls[k].m_pad) * 4;
+}
+
+hipError_t launch_fused_group(const glq_layer* Ls, int count, const void* const* x, glq_dtype x_dt, void* const* y,
+                              glq_dtype y_dt, float* const* z_parts, hipStream_t stream) {
+  int cus[kGroupMax];
+  group_cus(Ls, count, cus);
+  FusedGroupArgs g;
+  BlocksGroupArgs bg;
+  int wgs = 0, E = 1, CB = 4;
+  bool full = false;
+  for (int k = 0; k < count; ++k) {
+    const FusedPlan p = fused_plan(Ls[k], cus[k]);
+    g.L[k] = fused_args(Ls[k], p, x[k], x_dt, z_parts[k]);
+    wgs += p.splits * p.wgs_per_split;
+    g.end[k] = wgs;
+    bg.L[k] = blocks_args(Ls[k], p, z_parts[k], y[k]);
+    E = blocks_e(bg.L[k].lw) > E ? blocks_e(bg.L[k].lw) : E;
+    CB = blocks_cb(p.lr) < CB ? blocks_cb(p.lr) : CB;
+    full = p.lpr_log2 == 6;  // the same for every layer: one n_pad
+  }
+  for (int k = count; k < kGroupMax; ++k) g.end[k] = bg.end[k] = 0x7FFFFFFF;
+  g.count = bg.count = count;
+  const bool codes = Ls[0].index_format == GLQ_INDEX_SLOT;
+  const dim3 grid(static_cast<unsigned>(wgs)), block(kThreads);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, g); };
+  auto launch_r = [&](auto tag) {
+    constexpr int R = decltype(tag)::R;
+    if (full)
+      codes ? go(fused_group_kernel<R, true, true>) : go(fused_group_kernel<R, true, false>);
+    else
+      codes ? go(fused_group_kernel<R, false, true>) : go(fused_group_kernel<R, false, false>);
+  };
+  switch (Ls[0].resid_bits) {
+    case 0: launch_r(Stages<0, 0, 0>{}); break;
+    case 8: launch_r(Stages<8, 0, 0>{}); break;
+    default: launch_r(Stages<16, 0, 0>{}); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (y_dt) {
+    case GLQ_F32: return launch_blocks_group<float>(bg, E, CB, stream);
+    case GLQ_F16: return launch_blocks_group<half_t>(bg, E, CB, stream);
+    default: return launch_blocks_group<bf16_t>(bg, E, CB, stream);
   }
 }
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GLQ_ABI_VERSION 4
+#define GLQ_ABI_VERSION 5
 #define GLQ_CODEBOOK_ENTRIES 65536
 #define GLQ_RESID8_ENTRIES 256
 #define GLQ_MAX_PAD (1 << 20)
@@ -416,6 +416,37 @@ glq_status glq_e8_matmul_prefill(const glq_layer* layer, const void* u16, int64_
 size_t glq_e8rht_linear_workspace_bytes(const glq_layer* layer, int64_t B);
 glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_dt, int64_t B, void* y,
                             glq_dtype y_dt, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * glq_e8rht_linear_group — count independent E8RHTLinear forwards,
+ * y[k] = glq_e8rht_linear(&layers[k], x[k]) for k < count, in as few launches as the
+ * layers allow.  For linears that read the same activations (q, k and v; gate and
+ * up) or any others whose inputs are ready together.  glq 0.5.1 (PyPI project page),
+ * "Advanced -> CUDA-graph decode wrapper": a B = 1 decode step of a small model is
+ * bound by per-kernel dispatch, not by its bytes; here the layers share the launches
+ * instead.
+ *   layers     host array of count layer descriptors (1 <= count <= GLQ_GROUP_MAX)
+ *   x, y       host arrays of count device pointers, x[k] [B][layers[k].n] in x_dt and
+ *              y[k] [B][layers[k].m] in y_dt (x[k] may be the same pointer for several
+ *              k; no y[k] may overlap another buffer of the call)
+ *   workspace  device, >= glq_e8rht_linear_group_workspace_bytes(layers, count, B),
+ *              256-byte aligned, uninitialized scratch; calls that may overlap need
+ *              separate workspaces
+ * B = 1 and layers of one n_pad, one residual stage and one index format, no further
+ * stages, each one the two-launch B = 1 path would take: one pair of launches for
+ * all of them, the device's CUs shared among the layers in proportion to their index
+ * bytes when their own plans would not fit together.  Otherwise the layers run one
+ * after another as glq_e8rht_linear on the same stream and workspace.  Every y[k] is
+ * bit-identical to the single call's result when the layers keep their own plans and
+ * equal to it within rounding order otherwise (the reductions follow each layer's plan).
+ * Errors: as glq_e8rht_linear for any layer (nothing is launched when one fails
+ * validation), GLQ_ERR_SHAPE for count outside [1, GLQ_GROUP_MAX].
+ */
+#define GLQ_GROUP_MAX 4
+size_t glq_e8rht_linear_group_workspace_bytes(const glq_layer* layers, int32_t count, int64_t B);
+glq_status glq_e8rht_linear_group(const glq_layer* layers, int32_t count, const void* const* x, glq_dtype x_dt,
+                                  int64_t B, void* const* y, glq_dtype y_dt, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /*
  * glq_e8rht_linear_noalloc — glq_e8rht_linear without a caller's workspace, for

@@ -38,7 +38,7 @@ def test_header_declarations_are_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.glq_abi_version() == 4
+    assert lib.glq_abi_version() == 5
     for s in range(9):
         assert lib.glq_status_string(s)
     assert lib.glq_status_string(0) == b"ok"
@@ -118,8 +118,37 @@ def linear_status(L, B=1, x=A, y=A, xdt=0, ydt=0, ws=A, ws_n=1 << 40):
     return _lib.load().glq_e8rht_linear(ctypes.byref(L), x, xdt, B, y, ydt, ws, ws_n, None)
 
 
+def group_status(layers, count=None, x=A, y=A, B=1, ws=A, ws_n=1 << 40):
+    arr = (_lib.GlqLayer * max(len(layers), 1))(*layers)
+    n = len(layers) if count is None else count
+    xs = (ctypes.c_void_p * max(n, 1))(*([x] * max(n, 1)))
+    ys = (ctypes.c_void_p * max(n, 1))(*([y] * max(n, 1)))
+    return _lib.load().glq_e8rht_linear_group(arr, n, xs, 0, B, ys, 0, ws, ws_n, None)
+
+
 @pytest.mark.skipif(not NO_GPU, reason="fake-pointer validation runs only where no GPU exists")
 class TestValidation:
+    def test_group(self):
+        lib = _lib.load()
+        L = fake_layer()
+        assert group_status([L], count=0) == 2
+        assert group_status([L] * 5) == 2
+        assert lib.glq_e8rht_linear_group(None, 1, None, 0, 1, None, 0, A, 1 << 40, None) == 1
+        assert group_status([L, fake_layer(idx0=None)]) == 1      # any layer's validation fails: nothing runs
+        assert group_status([L, fake_layer(resid_bits=4)]) == 4
+        assert group_status([L, L], x=None) == 1
+        assert group_status([L, L], B=0) == 2
+        assert group_status([L, L], ws_n=16) == 6
+        # one z-partial region per layer at B = 1 (one grouped launch), the largest
+        # single-layer workspace otherwise
+        arr = (_lib.GlqLayer * 2)(L, L)
+        one = lib.glq_e8rht_linear_workspace_bytes(ctypes.byref(L), 1)
+        assert lib.glq_e8rht_linear_group_workspace_bytes(arr, 2, 1) == 2 * one
+        assert lib.glq_e8rht_linear_group_workspace_bytes(arr, 2, 5) == lib.glq_e8rht_linear_workspace_bytes(
+            ctypes.byref(L), 5)
+        assert lib.glq_e8rht_linear_group_workspace_bytes(arr, 0, 1) == 0
+        assert group_status([L, L]) == 7                          # valid: no GPU to launch on
+
     def test_null_pointers(self):
         assert linear_status(fake_layer(idx0=None)) == 1
         assert linear_status(fake_layer(cb_pack=None)) == 1
