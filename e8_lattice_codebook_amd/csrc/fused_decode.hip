@@ -536,9 +536,11 @@ __device__ __forceinline__ void fused_decode_body(const FusedArgs& a, int bid) {
       while (ch < nch) {
         load_at(ch, 2, p);
         step_at(n, ch, 0);
-        load_at(nx < nch ? nx : ch, 0, n);
+        // without a next chunk the ring's loads reread the row just requested into p
+        // (its lines are already on their way into L2), not rows of HBM a chunk old
+        load_at(nx < nch ? nx : ch, nx < nch ? 0 : 2, n);
         step_at(m, ch, 1);
-        load_at(nx < nch ? nx : ch, 1, m);
+        load_at(nx < nch ? nx : ch, nx < nch ? 1 : 2, m);
         step_at(p, ch, 2);
         ch = nx;
         if (ch < nch) nx = take();
