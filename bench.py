@@ -200,6 +200,24 @@ def main():
     achieved = sum(launch_bytes) / (sum(per_layer_ms) * 1e-3) / 1e9
     log("bench: per-call ms %s -> %.1f GB/s" % (["%.4f" % t for t in per_layer_ms], achieved))
 
+    # the achievable HBM rate for context: a plain device copy of 1 GiB (reads and
+    # writes 1 GiB each), the same event timing
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * (1 << 30) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    del src, dst
+    # codeword lookups per second over the timed calls (one per group and index stage)
+    stages = 1 + (1 if wl.resid_bits else 0)
+    lookups = sum(q.m_pad * (q.n_pad // 8) for q in qls[0]) * stages
+    log("bench: plain copy %.1f GB/s; %.3g codeword lookups/s" % (copy_gbs, lookups / (sum(per_layer_ms) * 1e-3)))
+
     # the other index format, same loop and step count
     other_steps = min(args.steps, 300)
     e0.record()
@@ -252,6 +270,9 @@ def main():
             "per_call_ms": [round(t, 5) for t in per_layer_ms],
             "bytes_per_call": launch_bytes,
             "timing": "one event pair around %d back-to-back calls per layer (rotating copies)" % args.steps,
+            "copy_gbs": round(copy_gbs, 1),
+            "frac_of_copy": round(achieved / copy_gbs, 4),
+            "lookups_per_s": float("%.4g" % (lookups / (sum(per_layer_ms) * 1e-3))),
         },
     }
 

@@ -92,6 +92,12 @@ def test_uneven_cu_shares(gpu_codebooks):
     check_group(gpu_codebooks, "smollm3_block", [4, 5, 1], x_of={5: 4, 1: 4})
 
 
+def test_devstral_gate_up_shared_cus(gpu_codebooks):
+    # two 32768 x 8192 layers (64 lanes per row, bf16): 128 CUs each, 256 row-steps per
+    # workgroup, so the waves take their rows in chunks from the LDS counter
+    check_group(gpu_codebooks, "devstral_mlp", [0, 1], x_of={1: 0})
+
+
 def test_four_layers_own_inputs_codebook_indices(gpu_codebooks):
     check_group(gpu_codebooks, "smollm3_block", [0, 1, 2, 3], slot=False, own_plans=True)
 
