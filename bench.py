@@ -434,7 +434,7 @@ def bench_configs(glq, synth, cb, dev, args, log, devstral=None):
     activation, output and sign bytes per call; frac is against the 8 TB/s HBM peak.
     B = 1 runs the two-launch fused decode, 2 <= B <= 16 the staged decode (input RHT,
     quantization, GEMV, output RHT; the GEMV on the int8 matrix units for 2 <= B <= 16 on
-    layers of at least 2^21 groups and for 4 <= B <= 16 from 2^19)."""
+    layers of at least 2^21 groups and for 4 <= B <= 16 from 2^17)."""
     import numpy as np
     import torch
 
@@ -474,7 +474,7 @@ def bench_configs(glq, synth, cb, dev, args, log, devstral=None):
                 gbs = nbytes / (ms * 1e-3) / 1e9
                 path = ("fused B=1 (2 launches)" if B == 1 else
                         "staged (input RHT, quantization, GEMV, output RHT; the GEMV on the int8 matrix units "
-                        "for 2 <= B <= 16 on layers of 2^21+ groups and 4 <= B <= 16 from 2^19, else the "
+                        "for 2 <= B <= 16 on layers of 2^21+ groups and 4 <= B <= 16 from 2^17, else the "
                         "LDS-codebook integer GEMV)")
                 log("bench: %s %s B=%d: %.2f us per call, %.1f GB/s (%d copies)" % (key, shape.name, B, ms * 1e3,
                                                                                    gbs, ncop))

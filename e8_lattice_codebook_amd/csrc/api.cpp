@@ -148,14 +148,14 @@ struct LinearWs {
 
 constexpr int64_t kDecodeMaxB = 16;
 // The decode matmul runs on the int8 matrix units for 2 <= B <= kDecodeMaxB on layers
-// of at least 2^21 groups, and from 4 rows on layers of at least 2^19 groups (its cost
+// of at least 2^21 groups, and from 4 rows on layers of at least 2^17 groups (its cost
 // per codeword does not grow with B; smaller layers and batches are bound by launches
 // and the transforms, where the staged integer GEMV path measured faster), for every
 // pass of the layer.
 bool skinny_ok(const glq_layer& L, int64_t B) {
   if (B < 2 || B > kDecodeMaxB) return false;
   const int64_t groups = L.m_pad * (L.n_pad / 8);
-  if (groups < (int64_t(1) << 19) || (B < 4 && groups < (int64_t(1) << 21))) return false;
+  if (groups < (int64_t(1) << 17) || (B < 4 && groups < (int64_t(1) << 21))) return false;
   const Passes P = split_passes(L);
   return gemv_i8_supported(P.a) && (!P.two || gemv_i8_supported(P.b));
 }
