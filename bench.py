@@ -5,7 +5,10 @@ Step = one decode pass (B = 1) through the Devstral-Small 24B-shaped MLP:
 gate 5120->32768, up 5120->32768, down 32768->5120 at 4 bpw (16-bit primary +
 16-bit residual index per 8-weight group), bf16 activations; each layer runs
 input RHT, the decode matmul against the indices and output RHT.  The layers
-are independent calls on seeded synthetic data (no activation between them).
+run on seeded synthetic data (no activation between them); gate and up, whose
+inputs are ready together in an MLP, run as one glq_e8rht_linear_group call (one
+launch pair on half the CUs each), then down; the step as three single calls is
+reported beside it (one_call_per_layer).
 R copies of the three layers' index arrays (>= 1 GiB in total) are rotated so
 every step reads its indices from HBM, not from the 256 MB Infinity Cache.
 The 16-bit index arrays are relabelled once, before timing, as slot codes
@@ -15,10 +18,11 @@ reports the other format beside the headline.
 
 value   = sum over the step's layers of (index bytes + x bytes + y bytes + sign
           bytes) / step time, in GB/s (inputs resident in HBM before timing starts).
-roofline: at B = 1 each layer call is two kernel launches (fused_decode_kernel,
-          then the small output_blocks_kernel); events around every call (same
-          stream) in a second loop give their average duration; achieved = the
-          calls' bytes / their time.
+roofline: the dominant launch pair, the gate+up group (fused_group_kernel, then the
+          small blocks_group_kernel): events around back-to-back group calls (same
+          stream) give its average duration; achieved = the two layers' bytes / that
+          time.  A single layer call is fused_decode_kernel + output_blocks_kernel,
+          timed the same way for one_call_per_layer.
 prefill: the 2048-token prefill of the SmolLM3-3B gate shape (2048->11008,
           3 bpw), its MFMA matmul timed the same way, in TFLOP/s.
 block_b1: the seven linears of a SmolLM3-3B decoder block (3 bpw, fp16) at B = 1,
@@ -163,42 +167,66 @@ def main():
                     for l in host_layers]
     step_bytes = sum(launch_bytes)
 
-    def step(i):
+    grouped = B == 1  # gate and up as one launch pair (glq_e8rht_linear_group)
+    gws = torch.zeros(max(1, glq.linear_group_workspace_bytes(qls[0][:2], B)), dtype=torch.uint8, device=dev)
+
+    def step_layers(i):  # one glq_e8rht_linear call per layer
         row = qls[i % copies]
         for k in range(len(row)):
             glq.e8rht_linear(row[k], xs[k], out=ys[k], workspace=ws)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log("bench: timing %d steps" % args.steps)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log("bench: %.4f ms/step (wall %.4f), %.1f GB/s" % (ms_per_step, wall * 1e3 / args.steps, value))
+    def group_call(i):  # gate and up: their inputs are ready together in an MLP
+        row = qls[i % copies]
+        glq.e8rht_linear_group(row[:2], xs[:2], outs=ys[:2], workspace=gws)
 
-    # per-call timing: at B = 1 every layer call is fused_decode_kernel followed by
-    # output_blocks_kernel.  Per layer, one pair of events (on the launch stream)
-    # around `steps` back-to-back calls of that layer over the rotating copies, so
-    # the events add nothing to the calls they time.
-    per_layer_ms = []
-    for k in range(len(host_layers)):
+    def step_grouped(i):  # gate + up as one group, then down
+        group_call(i)
+        glq.e8rht_linear(qls[i % copies][2], xs[2], out=ys[2], workspace=ws)
+
+    step = step_grouped if grouped else step_layers
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n, first=0):
+        """ms per call of fn over n back-to-back calls, one event pair around them"""
         e0.record()
-        for i in range(args.steps):
-            glq.e8rht_linear(qls[i % copies][k], xs[k], out=ys[k], workspace=ws)
+        for i in range(n):
+            fn(first + i)
         e1.record()
         torch.cuda.synchronize()
-        per_layer_ms.append(e0.elapsed_time(e1) / args.steps)
-    achieved = sum(launch_bytes) / (sum(per_layer_ms) * 1e-3) / 1e9
-    log("bench: per-call ms %s -> %.1f GB/s" % (["%.4f" % t for t in per_layer_ms], achieved))
+        return e0.elapsed_time(e1) / n
+
+    for i in range(args.warmup):
+        step(i)
+        if grouped:
+            step_layers(i)
+    torch.cuda.synchronize()
+    log("bench: timing %d steps" % args.steps)
+    t0 = time.perf_counter()
+    ms_per_step = timed(step, args.steps, args.warmup)
+    wall = time.perf_counter() - t0
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log("bench: %.4f ms/step (wall %.4f), %.1f GB/s%s" % (ms_per_step, wall * 1e3 / args.steps, value,
+                                                          " (gate+up grouped)" if grouped else ""))
+
+    # per launch pair: at B = 1 every call is fused_decode_kernel + output_blocks_kernel,
+    # a group fused_group_kernel + blocks_group_kernel.  One pair of events (on the launch
+    # stream) around `steps` back-to-back calls over the rotating copies, so the events
+    # add nothing to the calls they time.
+    per_layer_ms = []
+    for k in range(len(host_layers)):
+        per_layer_ms.append(timed(lambda i: glq.e8rht_linear(qls[i % copies][k], xs[k], out=ys[k], workspace=ws),
+                                  args.steps))
+    achieved_layers = sum(launch_bytes) / (sum(per_layer_ms) * 1e-3) / 1e9
+    log("bench: per-call ms %s -> %.1f GB/s" % (["%.4f" % t for t in per_layer_ms], achieved_layers))
+    if grouped:
+        group_ms = timed(group_call, args.steps)
+        group_bytes = launch_bytes[0] + launch_bytes[1]
+        achieved = group_bytes / (group_ms * 1e-3) / 1e9
+        log("bench: gate+up group %.4f ms per call -> %.1f GB/s" % (group_ms, achieved))
+        layers_ms = timed(step_layers, args.steps)
+        log("bench: one call per layer: %.4f ms/step, %.1f GB/s" % (layers_ms, step_bytes / (layers_ms * 1e-3) / 1e9))
+    else:
+        achieved = achieved_layers
 
     # the achievable HBM rate for context: a plain device copy of 1 GiB (reads and
     # writes 1 GiB each), the same event timing
@@ -206,29 +234,57 @@ def main():
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
-    e0.record()
-    for _ in range(10):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2.0 * (1 << 30) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    copy_ms = timed(lambda i: dst.copy_(src), 10)
+    copy_gbs = 2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9
     del src, dst
-    # codeword lookups per second over the timed calls (one per group and index stage)
+    # codeword lookups per second over the timed step (one per group and index stage)
     stages = 1 + (1 if wl.resid_bits else 0)
     lookups = sum(q.m_pad * (q.n_pad // 8) for q in qls[0]) * stages
-    log("bench: plain copy %.1f GB/s; %.3g codeword lookups/s" % (copy_gbs, lookups / (sum(per_layer_ms) * 1e-3)))
+    log("bench: plain copy %.1f GB/s; %.3g codeword lookups/s" % (copy_gbs, lookups / (ms_per_step * 1e-3)))
 
     # the other index format, same loop and step count
     other_steps = min(args.steps, 300)
-    e0.record()
-    for i in range(other_steps):
-        row = qls_other[i % copies]
-        for k in range(len(row)):
-            glq.e8rht_linear(row[k], xs[k], out=ys[k], workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    other_value = step_bytes / (e0.elapsed_time(e1) / other_steps * 1e-3) / 1e9
+    qls, qls_other = qls_other, qls
+    other_ms = timed(step, other_steps)
+    qls, qls_other = qls_other, qls
+    other_value = step_bytes / (other_ms * 1e-3) / 1e9
     log("bench: %s indices: %.1f GB/s" % ("codebook" if slot else "slot-code", other_value))
+
+    layer_kernel = ("fused_decode_kernel + output_blocks_kernel (one E8RHTLinear call at B = 1: input RHT, "
+                    "decode matmul, row-block output transform; then the fixed-order split sum and the "
+                    "cross-block output transform)")
+    layers_roofline = {
+        "bound": "hbm",
+        "kernel": layer_kernel if B == 1 else "staged decode launches (RHT, quant_u, gemv_lds, RHT)",
+        "achieved": round(achieved_layers, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved_layers / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic(TRAFFIC_FILE) if B == 1 else None,
+        "per_call_ms": [round(t, 5) for t in per_layer_ms],
+        "bytes_per_call": launch_bytes,
+        "timing": "one event pair around %d back-to-back calls per layer (rotating copies)" % args.steps,
+    }
+    if grouped:
+        roofline = {
+            "bound": "hbm",
+            "kernel": ("fused_group_kernel + blocks_group_kernel (the gate and up E8RHTLinear calls at B = 1 in "
+                       "one launch pair, glq_e8rht_linear_group: each layer's workgroups run the fused input "
+                       "RHT, decode matmul and row-block output transform on half the CUs; then the fixed-order "
+                       "split sums and cross-block output transforms of both)"),
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(GROUP_TRAFFIC_FILE),
+            "per_launch_ms": round(group_ms, 5),
+            "bytes_per_launch": group_bytes,
+            "timing": "one event pair around %d back-to-back group calls (rotating copies)" % args.steps,
+        }
+    else:
+        roofline = dict(layers_roofline)
+    roofline.update({"copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4),
+                     "lookups_per_s": float("%.4g" % (lookups / (ms_per_step * 1e-3)))})
 
     result = {
         "metric": METRIC,
@@ -250,32 +306,20 @@ def main():
             "workload": "Devstral-Small-24B MLP decode (gate 5120->32768, up 5120->32768, down 32768->5120), "
                         "4 bpw (16+16-bit E8 indices), B=%d, bf16 activations, uniform seeded indices" % B,
             "batch": B,
+            "step": ("gate and up as one glq_e8rht_linear_group call (one launch pair), then down"
+                     if grouped else "one glq_e8rht_linear call per layer"),
             "index_format": ("slot codes: the 16-bit indices relabelled once at load (glq_slot_codes), "
                              "same entries and bytes") if slot else "codebook indices",
             "index_bytes_per_step": idx_bytes,
             "algorithmic_bytes_per_step": step_bytes,
             "rotating_copies": copies,
         },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": ("fused_decode_kernel + output_blocks_kernel (one E8RHTLinear call at B = 1: input RHT, "
-                       "decode matmul, row-block output transform; then the fixed-order split sum and the "
-                       "cross-block output transform)") if B == 1 else
-                      "staged decode launches (RHT, quant_u, gemv_lds, RHT)",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(launch_bytes) if B == 1 else None,
-            "per_call_ms": [round(t, 5) for t in per_layer_ms],
-            "bytes_per_call": launch_bytes,
-            "timing": "one event pair around %d back-to-back calls per layer (rotating copies)" % args.steps,
-            "copy_gbs": round(copy_gbs, 1),
-            "frac_of_copy": round(achieved / copy_gbs, 4),
-            "lookups_per_s": float("%.4g" % (lookups / (sum(per_layer_ms) * 1e-3))),
-        },
+        "roofline": roofline,
     }
-
+    if grouped:
+        result["one_call_per_layer"] = {
+            "ms_per_step": round(layers_ms, 5), "value": round(step_bytes / (layers_ms * 1e-3) / 1e9, 2),
+            "unit": "GB/s", "roofline": layers_roofline}
     result["other_index_format"] = {"index_format": "codebook indices" if slot else "slot codes",
                                     "value": round(other_value, 2), "unit": "GB/s", "steps": other_steps}
 
@@ -293,10 +337,12 @@ def main():
         result["block_b1"] = bench_block_graph(glq, synth, cb, dev, args, log)
 
     if not args.no_recipes and B == 1:
-        result["recipes_b1"] = bench_recipes(glq, synth, cb, dev, args, log, value)
+        # the recipes run one call per layer: compared with the same form at 4 bpw
+        result["recipes_b1"] = bench_recipes(glq, synth, cb, dev, args, log,
+                                             step_bytes / (layers_ms * 1e-3) / 1e9 if grouped else value)
 
     if not args.no_blockdiag and B == 1:
-        result["blockdiag_b1"] = bench_blockdiag(glq, synth, cb, dev, args, log, ms_per_step)
+        result["blockdiag_b1"] = bench_blockdiag(glq, synth, cb, dev, args, log, layers_ms if grouped else ms_per_step)
 
     if not args.no_kv:
         result["kv_attention"] = bench_kv(glq, synth, cb, dev, args, log)
@@ -307,9 +353,11 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-# ---- HBM traffic of the fused kernel from rocprofv3 counters -------------------------
+# ---- HBM traffic of the B = 1 launches from rocprofv3 counters -------------------------
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_decode_kernel_devstral_mlp_b1_traffic.txt")
 FUSED_KERNEL_NAMES = ("fused_decode_kernel", "output_blocks_kernel")  # the two launches of a B = 1 call
+GROUP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_group_kernel_devstral_gate_up_b1_traffic.txt")
+GROUP_KERNEL_NAMES = ("fused_group_kernel", "blocks_group_kernel")  # the two launches of the gate+up group
 KERNEL_SOURCES = ["fused_decode.hip", "lds_codebook.h", "fwht_lds.h", "internal.h"]
 
 
@@ -338,59 +386,64 @@ def _pmc_rows(folder, counter):
 
 
 def pmc_summary(dirs, copy_bytes):
-    """Write TRAFFIC_FILE: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the two kernels of
-    a B = 1 call, each scaled by bytes / counter of a plain copy of copy_bytes (reads
-    and writes copy_bytes each)."""
+    """Write TRAFFIC_FILE and GROUP_TRAFFIC_FILE: FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch) of the two kernels of a B = 1 call, and of the two kernels of the gate+up
+    group, each scaled by bytes / counter of a plain copy of copy_bytes (reads and
+    writes copy_bytes each)."""
     import numpy as np
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
-    out = {}
-    for name, folder, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
-        rows = _pmc_rows(folder, counter)
-        out[name + "_kib"] = 0.0
-        out[name + "_dispatches"] = 0
-        for kname in FUSED_KERNEL_NAMES:  # per call: the sum of the two kernels' medians
-            vals = [v for k, v in rows if kname in k]
-            out[name + "_kib"] += float(np.median(vals))
-            out[name + "_dispatches"] += len(vals)
+    rows = {"fetch": _pmc_rows(fetch_dir, "FETCH_SIZE"), "write": _pmc_rows(write_dir, "WRITE_SIZE")}
+    copy = {}
     for name, folder, counter in (("copy_fetch", cfetch_dir, "FETCH_SIZE"), ("copy_write", cwrite_dir, "WRITE_SIZE")):
-        rows = _pmc_rows(folder, counter)
-        big = max(v for _, v in rows)
-        vals = [v for _, v in rows if v > 0.5 * big]  # the copy dispatches (not small setup kernels)
-        out[name + "_kib"] = float(np.median(vals))
-    sf = copy_bytes / (out["copy_fetch_kib"] * 1024.0)
-    sw = copy_bytes / (out["copy_write_kib"] * 1024.0)
-    traffic = out["fetch_kib"] * 1024.0 * sf + out["write_kib"] * 1024.0 * sw
-    lines = [
-        "# HBM traffic of one B = 1 call (%s), Devstral-Small-24B MLP decode" % " + ".join(FUSED_KERNEL_NAMES),
-        "# commands (from the repository root, after cd /tmp && export TMPDIR=/tmp for the profiler):",
-        "#   rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR --output-format csv -- python3 bench.py --steps 3 --warmup 1 "
-        "--no-cpu-baseline --no-prefill --no-block --no-recipes --no-blockdiag --no-kv --no-configs",
-        "#   rocprofv3 --pmc WRITE_SIZE -d WRITE_DIR --output-format csv -- (same)",
-        "#   rocprofv3 --pmc FETCH_SIZE -d COPY_FETCH_DIR --output-format csv -- python3 bench.py --calibrate-copy %d"
-        % copy_bytes,
-        "#   rocprofv3 --pmc WRITE_SIZE -d COPY_WRITE_DIR --output-format csv -- (same)",
-        "#   python3 bench.py --pmc-summary FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR --copy-bytes %d"
-        % copy_bytes,
-        "kernel_source_sha256: %s" % kernel_source_hash(),
-        "fetch_kib_median: %.1f (%d dispatches)" % (out["fetch_kib"], out["fetch_dispatches"]),
-        "write_kib_median: %.1f (%d dispatches)" % (out["write_kib"], out["write_dispatches"]),
-        "copy_bytes: %d" % copy_bytes,
-        "copy_fetch_kib: %.1f -> fetch scale %.4f" % (out["copy_fetch_kib"], sf),
-        "copy_write_kib: %.1f -> write scale %.4f" % (out["copy_write_kib"], sw),
-        "traffic_bytes_per_call: %d" % int(round(traffic)),
-    ]
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as fh:
-        fh.write("\n".join(lines) + "\n")
-    print("\n".join(lines))
+        crows = _pmc_rows(folder, counter)
+        big = max(v for _, v in crows)
+        copy[name + "_kib"] = float(np.median([v for _, v in crows if v > 0.5 * big]))  # the copy dispatches
+    sf = copy_bytes / (copy["copy_fetch_kib"] * 1024.0)
+    sw = copy_bytes / (copy["copy_write_kib"] * 1024.0)
+    cmd = ("python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-prefill --no-block --no-recipes "
+           "--no-blockdiag --no-kv --no-configs")
+    for path, names, what in ((TRAFFIC_FILE, FUSED_KERNEL_NAMES, "one B = 1 call"),
+                              (GROUP_TRAFFIC_FILE, GROUP_KERNEL_NAMES, "one B = 1 gate+up group call")):
+        out = {}
+        for name in ("fetch", "write"):
+            out[name + "_kib"] = 0.0
+            out[name + "_dispatches"] = 0
+            for kname in names:  # per call: the sum of the two kernels' medians
+                vals = [v for k, v in rows[name] if kname in k]
+                out[name + "_kib"] += float(np.median(vals))
+                out[name + "_dispatches"] += len(vals)
+        traffic = out["fetch_kib"] * 1024.0 * sf + out["write_kib"] * 1024.0 * sw
+        lines = [
+            "# HBM traffic of %s (%s), Devstral-Small-24B MLP decode" % (what, " + ".join(names)),
+            "# commands (from the repository root, after cd /tmp && export TMPDIR=/tmp for the profiler):",
+            "#   rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR --output-format csv -- %s" % cmd,
+            "#   rocprofv3 --pmc WRITE_SIZE -d WRITE_DIR --output-format csv -- (same)",
+            "#   rocprofv3 --pmc FETCH_SIZE -d COPY_FETCH_DIR --output-format csv -- python3 bench.py --calibrate-copy %d"
+            % copy_bytes,
+            "#   rocprofv3 --pmc WRITE_SIZE -d COPY_WRITE_DIR --output-format csv -- (same)",
+            "#   python3 bench.py --pmc-summary FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR --copy-bytes %d"
+            % copy_bytes,
+            "kernel_source_sha256: %s" % kernel_source_hash(),
+            "fetch_kib_median: %.1f (%d dispatches)" % (out["fetch_kib"], out["fetch_dispatches"]),
+            "write_kib_median: %.1f (%d dispatches)" % (out["write_kib"], out["write_dispatches"]),
+            "copy_bytes: %d" % copy_bytes,
+            "copy_fetch_kib: %.1f -> fetch scale %.4f" % (copy["copy_fetch_kib"], sf),
+            "copy_write_kib: %.1f -> write scale %.4f" % (copy["copy_write_kib"], sw),
+            "traffic_bytes_per_call: %d" % int(round(traffic)),
+        ]
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
 
 
-def measured_traffic(launch_bytes):
-    """HBM bytes per B = 1 call from TRAFFIC_FILE, or None when it is missing or was
-    taken on other kernel sources.  The file holds medians over the three layers'
-    dispatches, so it is reported against their mean algorithmic bytes."""
+def measured_traffic(path):
+    """HBM bytes per call from a traffic file written by pmc_summary, or None when it is
+    missing or was taken on other kernel sources.  TRAFFIC_FILE holds medians over the
+    three layers' dispatches (reported against their mean algorithmic bytes);
+    GROUP_TRAFFIC_FILE those of the gate+up group calls."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             kv = dict(l.split(": ", 1) for l in fh.read().splitlines() if ": " in l and not l.startswith("#"))
         if kv.get("kernel_source_sha256") != kernel_source_hash():
             return None
