@@ -135,3 +135,23 @@ def test_group_errors(gpu_codebooks):
     with pytest.raises(glq.GLQError) as e:
         glq.e8rht_linear_group(qls, [x, x], workspace=ws)
     assert e.value.name == "GLQ_ERR_WORKSPACE"
+
+
+def test_unpadded_block_diagonal_layers(gpu_codebooks):
+    # unpadded layers (n_pad = n = 5120 = 4096 + 1024, block-diagonal transforms) sharing
+    # one input: m = 11008 (8192 + 2048 + 512 + 256) and 2560, 4 bpw, bf16
+    hosts = [synth.block_layer(5120, 11008, 16, seed=71), synth.block_layer(5120, 2560, 16, seed=72)]
+    qls = [glq.QuantizedLayer.from_synth(h, gpu_codebooks).to_slot_codes() for h in hosts]
+    x64, raw = synth.make_x(5120, 1, "bf16", 73, 0)
+    x = x_tensor(raw, "bf16", "cuda:0")
+    say("group unpadded 5120 -> 11008, 2560")
+    ys = glq.e8rht_linear_group(qls, [x, x], torch.float32)
+    singles = [glq.e8rht_linear(q, x, torch.float32) for q in qls]
+    torch.cuda.synchronize()
+    for h, y, y1 in zip(hosts, ys, singles):
+        want = og.linear(x64, h.sign_in, h.sign_out, h.n_pad, h.m, h.idx0, h.idx1, h.resid_bits, h.wscale,
+                         h.resid_scale, block_diag=True)
+        err = rel_frob(to_f64(y), want)
+        say("  rel_frob", err)
+        assert err <= DECODE_TOL, err
+        assert rel_frob(to_f64(y), to_f64(y1)) <= 1e-6
