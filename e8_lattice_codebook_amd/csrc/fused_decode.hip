@@ -602,8 +602,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(FusedArgs a) {
 }
 
 // Several layers of one launch: layer k owns the workgroups [end[k-1], end[k]) of the
-// grid.  Every layer has the same stage layout (RESID, no further stages) and lanes per
-// row (FULL); the arguments of each are its own.
+// grid.  Every layer has the same stage layout (RESID, X16, X8) and lanes per row
+// (FULL); the arguments of each are its own.
 constexpr int kGroupMax = 4;
 struct FusedGroupArgs {
   FusedArgs L[kGroupMax];
@@ -618,11 +618,11 @@ __device__ __forceinline__ int group_member(const int* end, int count, int bid) 
   return k;
 }
 
-template <int RESID, bool FULL, bool CODES>
+template <int RESID, int X16, int X8, bool FULL, bool CODES>
 __global__ __launch_bounds__(kThreads) void fused_group_kernel(FusedGroupArgs g) {
   const int bid = int(blockIdx.x);
   const int k = __builtin_amdgcn_readfirstlane(group_member(g.end, g.count, bid));
-  fused_decode_body<RESID, 0, 0, FULL, CODES>(g.L[k], bid - (k > 0 ? g.end[k - 1] : 0));
+  fused_decode_body<RESID, X16, X8, FULL, CODES>(g.L[k], bid - (k > 0 ? g.end[k - 1] : 0));
 }
 
 // ---- the cross-block part of the output transform ------------------------------------
@@ -1100,9 +1100,13 @@ bool fused_group_supported(const glq_layer* Ls, int count) {
   if (count < 1 || count > kGroupMax) return false;
   for (int k = 0; k < count; ++k) {
     const glq_layer& L = Ls[k];
-    if (!fused_decode_supported(L, 1) || L.n_extra != 0) return false;
+    if (!fused_decode_supported(L, 1)) return false;
     if (L.n_pad != Ls[0].n_pad || L.resid_bits != Ls[0].resid_bits || L.index_format != Ls[0].index_format)
       return false;
+    int x16, x8, x16_0, x8_0;
+    stage_layout(L, x16, x8);
+    stage_layout(Ls[0], x16_0, x8_0);
+    if (x16 != x16_0 || x8 != x8_0) return false;
   }
   int cus[kGroupMax];
   group_cus(Ls, count, cus);
@@ -1141,16 +1145,22 @@ hipError_t launch_fused_group(const glq_layer* Ls, int count, const void* const*
   const dim3 grid(static_cast<unsigned>(wgs)), block(kThreads);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, g); };
   auto launch_r = [&](auto tag) {
-    constexpr int R = decltype(tag)::R;
+    constexpr int R = decltype(tag)::R, X = decltype(tag)::X, Y = decltype(tag)::Y;
     if (full)
-      codes ? go(fused_group_kernel<R, true, true>) : go(fused_group_kernel<R, true, false>);
+      codes ? go(fused_group_kernel<R, X, Y, true, true>) : go(fused_group_kernel<R, X, Y, true, false>);
     else
-      codes ? go(fused_group_kernel<R, false, true>) : go(fused_group_kernel<R, false, false>);
+      codes ? go(fused_group_kernel<R, X, Y, false, true>) : go(fused_group_kernel<R, X, Y, false, false>);
   };
-  switch (Ls[0].resid_bits) {
+  int x16, x8;
+  stage_layout(Ls[0], x16, x8);
+  switch (Ls[0].resid_bits * 16 + x16 * 2 + x8) {
     case 0: launch_r(Stages<0, 0, 0>{}); break;
-    case 8: launch_r(Stages<8, 0, 0>{}); break;
-    default: launch_r(Stages<16, 0, 0>{}); break;
+    case 128: launch_r(Stages<8, 0, 0>{}); break;
+    case 256: launch_r(Stages<16, 0, 0>{}); break;
+    case 257: launch_r(Stages<16, 0, 1>{}); break;  // 16 + 16 + 8
+    case 258: launch_r(Stages<16, 1, 0>{}); break;  // 16 + 16 + 16
+    case 259: launch_r(Stages<16, 1, 1>{}); break;  // 16 + 16 + 16 + 8
+    default: launch_r(Stages<16, 2, 0>{}); break;   // 16 + 16 + 16 + 16
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -207,8 +207,8 @@ size_t fused_decode_z_bytes(const glq_layer& layer);
 // Every stage of the layer (5-8 bpw included) is summed in the one pass.
 hipError_t launch_fused_decode(const glq_layer& layer, const void* x, glq_dtype x_dt, void* y, glq_dtype y_dt,
                                float* z_parts, hipStream_t stream);
-// Up to four such layers at B = 1 in one pair of launches: same n_pad, residual
-// stage and index format, no further stages; each layer its own x, y and z_parts
+// Up to four such layers at B = 1 in one pair of launches: same n_pad, stage layout
+// and index format; each layer its own x, y and z_parts
 // (fused_group_z_bytes(layers, count, k) for layer k), the CUs shared among them.
 bool fused_group_supported(const glq_layer* layers, int count);
 size_t fused_group_z_bytes(const glq_layer* layers, int count, int k);

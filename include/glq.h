@@ -432,8 +432,9 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
  *   workspace  device, >= glq_e8rht_linear_group_workspace_bytes(layers, count, B),
  *              256-byte aligned, uninitialized scratch; calls that may overlap need
  *              separate workspaces
- * B = 1 and layers of one n_pad, one residual stage and one index format, no further
- * stages, each one the two-launch B = 1 path would take: one pair of launches for
+ * B = 1 and layers of one n_pad, one stage layout (the residual stage and any further
+ * stages of 5-8 bpw) and one index format, each one the two-launch B = 1 path would
+ * take: one pair of launches for
  * all of them, the device's CUs shared among the layers in proportion to their index
  * bytes when their own plans would not fit together.  Otherwise the layers run one
  * after another as glq_e8rht_linear on the same stream and workspace.  Every y[k] is

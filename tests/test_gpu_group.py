@@ -155,3 +155,24 @@ def test_unpadded_block_diagonal_layers(gpu_codebooks):
         say("  rel_frob", err)
         assert err <= DECODE_TOL, err
         assert rel_frob(to_f64(y), to_f64(y1)) <= 1e-6
+
+
+@pytest.mark.parametrize("bpw", [5, 6, 7, 8])
+def test_recipes_5_to_8_bpw(gpu_codebooks, bpw):
+    # the further 8/16-bit stages of 5-8 bpw in the grouped launch: two layers of one
+    # recipe sharing an input, shares of the CUs (16384 + 4096 rows at n_pad 2048)
+    hosts = [synth.recipe_layer(2048, 11008, bpw, seed=80 + bpw), synth.recipe_layer(2048, 4096, bpw, seed=90 + bpw)]
+    qls = [glq.QuantizedLayer.from_synth(h, gpu_codebooks).to_slot_codes() for h in hosts]
+    x64, raw = synth.make_x(2048, 1, "f16", 95, bpw)
+    x = x_tensor(raw, "f16", "cuda:0")
+    say("group recipes", bpw)
+    ys = glq.e8rht_linear_group(qls, [x, x], torch.float32)
+    singles = [glq.e8rht_linear(q, x, torch.float32) for q in qls]
+    torch.cuda.synchronize()
+    for h, y, y1 in zip(hosts, ys, singles):
+        want = og.linear(x64, h.sign_in, h.sign_out, h.n_pad, h.m, h.idx0, h.idx1, h.resid_bits, h.wscale,
+                         h.resid_scale, extra=h.oracle_extra())
+        err = rel_frob(to_f64(y), want)
+        say("  rel_frob", err)
+        assert err <= DECODE_TOL, (bpw, err)
+        assert rel_frob(to_f64(y), to_f64(y1)) <= 1e-6
