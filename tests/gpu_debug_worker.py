@@ -1,6 +1,7 @@
 """Run by tests/test_gpu_debug.py in a subprocess with GLQ_LIB_VARIANT=debug: the device
 bounds checks of the debug build over one call of each path (B = 1 fused decode, B = 5
-staged decode, prefill, KV attention with large and small pages), both index formats,
+staged decode, prefill, a grouped B = 1 launch, KV attention with large and small
+pages), both index formats where they apply,
 each checked against the oracle; prints one line per path and then the violations."""
 import os
 import sys
@@ -42,6 +43,19 @@ def main():
             err = rel(y.double().cpu().numpy(), want)
             print("linear B=%d format=%d rel_frob %.3g" % (B, q.index_format, err), flush=True)
             assert err <= tol, (B, err)
+    # the grouped B = 1 launches: three layers of one n_pad with uneven CU shares
+    hosts = [synth.random_layer(1000, m, 8, seed=60 + k, n_pad=1024, m_pad=mp) for k, (m, mp) in
+             enumerate(((3000, 4096), (2500, 4096), (500, 512)))]
+    qls = [glq.QuantizedLayer.from_synth(h, cb).to_slot_codes() for h in hosts]
+    x64, raw = synth.make_x(1000, 1, "f32", 61, 8)
+    x = torch.from_numpy(raw).to(DEV)
+    ys = glq.e8rht_linear_group(qls, [x, x, x], torch.float32)
+    torch.cuda.synchronize()
+    for h, y in zip(hosts, ys):
+        want = og.linear(x64, h.sign_in, h.sign_out, h.n_pad, h.m, h.idx0, h.idx1, 8, h.wscale, h.resid_scale)
+        err = rel(y.double().cpu().numpy(), want)
+        print("group m_pad=%d rel_frob %.3g" % (h.m_pad, err), flush=True)
+        assert err <= 1e-3, err
     for page in (16, 4):
         cache = synth.make_kv([300, 41], 2, 128, 2, page, seed=page)
         q64, qraw = synth.make_q(2, 8, 128, "f32", seed=page + 1)
