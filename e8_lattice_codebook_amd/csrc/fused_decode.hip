@@ -912,6 +912,12 @@ FusedPlan fused_plan(const glq_layer& L, int cus) {
   return p;
 }
 
+// the stage layout of a layer as (RESID, further 16-bit stages, further 8-bit stages)
+void stage_layout(const glq_layer& L, int& x16, int& x8) {
+  x16 = (L.n_extra >= 1 && L.extra_bits[0] == 16 ? 1 : 0) + (L.n_extra == 2 && L.extra_bits[1] == 16 ? 1 : 0);
+  x8 = L.n_extra >= 1 && L.extra_bits[L.n_extra - 1] == 8 ? 1 : 0;
+}
+
 // the first launch's arguments of one layer under plan p
 FusedArgs fused_args(const glq_layer& L, const FusedPlan& p, const void* x, glq_dtype x_dt, float* z_parts) {
   FusedArgs a;
@@ -926,8 +932,8 @@ FusedArgs fused_args(const glq_layer& L, const FusedPlan& p, const void* x, glq_
       p0 + (codes ? pack_slot_image_offset(GLQ_CODEBOOK_ENTRIES) : pack_image_offset(GLQ_CODEBOOK_ENTRIES)));
   // further stages (5-8 bpw in one pass): 16-bit ones index the primary pack, an
   // 8-bit one (always the last) the 256-entry residual pack
-  const int x16 = (L.n_extra >= 1 && L.extra_bits[0] == 16 ? 1 : 0) + (L.n_extra == 2 && L.extra_bits[1] == 16 ? 1 : 0);
-  const int x8 = L.n_extra >= 1 && L.extra_bits[L.n_extra - 1] == 8 ? 1 : 0;
+  int x16, x8;
+  stage_layout(L, x16, x8);
   for (int k = 0; k < 2; ++k) {
     a.idx_x16[k] = k < x16 ? static_cast<const uint16_t*>(L.extra_idx[k]) : nullptr;
     a.sc_x16[k] = k < x16 ? L.extra_scale[k] : 0.0f;
@@ -979,14 +985,9 @@ BlocksArgs blocks_args(const glq_layer& L, const FusedPlan& p, const float* z_pa
   return b;
 }
 
-// the stage layout of a layer as (RESID, further 16-bit stages, further 8-bit stages)
-void stage_layout(const glq_layer& L, int& x16, int& x8) {
-  x16 = (L.n_extra >= 1 && L.extra_bits[0] == 16 ? 1 : 0) + (L.n_extra == 2 && L.extra_bits[1] == 16 ? 1 : 0);
-  x8 = L.n_extra >= 1 && L.extra_bits[L.n_extra - 1] == 8 ? 1 : 0;
-}
-
-// log2 of the lanes that share a row in the group kernel's second launch: the
-// largest W of the group needs E = W / 64 row blocks per lane (at least 1)
+// The cross-block launch's shape for a layer: E = W / 64 row blocks per lane (at least
+// 1; W = 2^lw row blocks), and CB columns per wave for row blocks of 2^lr rows (as
+// launch_blocks picks them).  A group takes the largest E and the smallest CB.
 int blocks_e(int lw) { return lw <= 6 ? 1 : 1 << (lw - 6); }
 int blocks_cb(int lr) { return lr >= 8 ? 4 : lr == 7 ? 2 : 1; }
 
