@@ -11,11 +11,12 @@ against the oracle at the path's tolerance.  Zero rows give zero outputs, outlie
 channels keep the tolerance, and a NaN or infinity in a row of x makes that row of
 y NaN (the oracle's y is NaN there too) without touching the other rows.
 
-Paths: B = 1 (the two-launch decode), B = 5 (the staged integer decode), M = 40
-(prefill, the shared-tile kernel of slot codes and the per-wave kernel of codebook
-indices), M = 160 (prefill with the persistent one-row-per-workgroup output
-transform), and B = 2, 3, 5 and 16 on a layer of 2^22 groups (2048 -> 16384: the decode
-on the int8 matrix units, 15-bit fixed point per row).
+Paths: B = 1 (the two-launch decode), B = 3 on a layer of 2^20 groups (2048 -> 4096:
+the staged integer decode, 16-bit fixed point per 64 columns), B = 5 on that layer and
+B = 2, 3, 5 and 16 on a layer of 2^22 groups (2048 -> 16384) (the decode on the int8
+matrix units, 15-bit fixed point per row), M = 40 (prefill, the shared-tile kernel of
+slot codes and the per-wave kernel of codebook indices), M = 160 (prefill with the
+persistent one-row-per-workgroup output transform).
 """
 import numpy as np
 import pytest
@@ -30,7 +31,7 @@ glq = pytest.importorskip("e8_lattice_codebook_amd")
 DEV = "cuda:0"
 
 N, M_OUT = 2048, 3000
-PATHS = [(1, "index"), (5, "index"), (1, "slot"), (5, "slot"), (40, "slot"), (40, "index"),
+PATHS = [(1, "index"), (3, "index"), (5, "index"), (1, "slot"), (3, "slot"), (5, "slot"), (40, "slot"), (40, "index"),
          (2, "slot-big"), (3, "index-big"), (5, "slot-big"), (16, "index-big"), (160, "slot")]
 _LAYERS = {}
 
