@@ -26,3 +26,17 @@ def gpu_codebooks():
         pytest.skip("no GPU")
     import e8_lattice_codebook_amd as glq
     return glq.Codebooks("cuda:0")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # with the debug library (GLQ_LIB_VARIANT=debug), every GPU test run in this process
+    # also checks the device-side bounds checks: any failed check fails the session
+    if os.environ.get("GLQ_LIB_VARIANT") != "debug":
+        return
+    from e8_lattice_codebook_amd import _lib
+    if _lib._lib is None:
+        return
+    v = int(_lib.load().glq_debug_violations())
+    print("\nglq_debug_violations: %d" % v)
+    if v != 0:
+        session.exitstatus = 1
