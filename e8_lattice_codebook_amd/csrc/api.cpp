@@ -174,6 +174,24 @@ size_t matmul_ws_bytes(const glq_layer& L, int64_t B) {
   return (B <= kDecodeMaxB && decode_uses_lds(L)) ? uq_bytes(B, L.n_pad) : 0;
 }
 
+// the int8 path's workspace: fp32 u, its int8 planes (+ row info), split partials
+// (splits of them), output scratch
+void skinny_layout(const glq_layer& L, int64_t B, int splits, LinearWs& w) {
+  size_t off = 0;
+  w.u_off = off;
+  off += align256(size_t(B) * size_t(L.n_pad) * 4);
+  w.uq_off = off;
+  off += align256(i8_planes_bytes(L.n_pad)) + align256(16 * sizeof(I8RowInfo));
+  w.rin_off = off;
+  if (rht_needs_ws(B, L.n_pad, true)) off += align256(size_t(B) * size_t(L.n_pad) * 4);
+  w.splits = splits;
+  w.z_off = off;
+  off += align256(size_t(w.splits) * size_t(B) * size_t(L.m_pad) * 4);
+  w.rout_off = off;
+  if (rht_needs_ws(B, L.m_pad, false)) off += align256(size_t(B) * size_t(L.m_pad) * 4);
+  w.total = off;
+}
+
 LinearWs linear_ws(const glq_layer& L, int64_t B) {
   LinearWs w{};
   w.prefill = B > kDecodeMaxB;
@@ -186,19 +204,8 @@ LinearWs linear_ws(const glq_layer& L, int64_t B) {
     w.total = off + align256(fused_decode_z_bytes(L));
     return w;
   }
-  if (w.skinny) {  // fp32 u, its int8 planes (+ row info), split partials, output scratch
-    w.u_off = off;
-    off += align256(size_t(B) * size_t(L.n_pad) * 4);
-    w.uq_off = off;
-    off += align256(i8_planes_bytes(L.n_pad)) + align256(16 * sizeof(I8RowInfo));
-    w.rin_off = off;
-    if (rht_needs_ws(B, L.n_pad, true)) off += align256(size_t(B) * size_t(L.n_pad) * 4);
-    w.splits = gemv_i8_splits(L.n_pad, L.m_pad);
-    w.z_off = off;
-    off += align256(size_t(w.splits) * size_t(B) * size_t(L.m_pad) * 4);
-    w.rout_off = off;
-    if (rht_needs_ws(B, L.m_pad, false)) off += align256(size_t(B) * size_t(L.m_pad) * 4);
-    w.total = off;
+  if (w.skinny) {
+    skinny_layout(L, B, gemv_i8_splits(L.n_pad, L.m_pad), w);
     return w;
   }
   w.u_off = off;
@@ -488,14 +495,39 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
   return from_hip(e);
 }
 
-// the group's workspace: one z_parts region per layer (the grouped launches), or the
-// largest single-layer workspace (one layer after another)
-static size_t group_ws(const glq_layer* layers, int32_t count, int64_t B, bool fused, size_t* z_off) {
-  size_t total = 0;
+// How a group runs: GROUP_FUSED (B = 1, the fused launches), GROUP_I8 (2 <= B <= 16,
+// every layer on the int8 path in one GEMV launch), else GROUP_EACH (one call per layer).
+enum GroupMode { GROUP_EACH, GROUP_FUSED, GROUP_I8 };
+
+static GroupMode group_mode(const glq_layer* layers, int32_t count, int64_t B) {
+  if (B == 1 && fused_group_supported(layers, count)) return GROUP_FUSED;
+  if (B < 2 || B > kDecodeMaxB || count < 2) return GROUP_EACH;
   for (int32_t k = 0; k < count; ++k) {
-    if (fused) {
-      if (z_off) z_off[k] = total;
+    const glq_layer& L = layers[k];
+    // one pass per layer (no further stages), one n_pad, each on the int8 path alone
+    if (!skinny_ok(L, B) || L.n_extra != 0 || L.n_pad != layers[0].n_pad) return GROUP_EACH;
+  }
+  return gemv_i8_group_plan(layers, count, nullptr) ? GROUP_I8 : GROUP_EACH;
+}
+
+// the group's workspace: one z_parts region per layer (the fused launches), one int8
+// path workspace per layer (the GEMV launch shared), or the largest single-layer
+// workspace (one layer after another); base[k] is layer k's offset
+static size_t group_ws(const glq_layer* layers, int32_t count, int64_t B, GroupMode mode, size_t* base,
+                       LinearWs* lw) {
+  size_t total = 0;
+  int splits[GLQ_GROUP_MAX];
+  if (mode == GROUP_I8) gemv_i8_group_plan(layers, count, splits);
+  for (int32_t k = 0; k < count; ++k) {
+    if (mode == GROUP_FUSED) {
+      if (base) base[k] = total;
       total += align256(fused_group_z_bytes(layers, count, k));
+    } else if (mode == GROUP_I8) {
+      LinearWs w{};
+      skinny_layout(layers[k], B, splits[k], w);
+      if (base) base[k] = total;
+      if (lw) lw[k] = w;
+      total += align256(w.total);
     } else {
       const size_t t = linear_ws(layers[k], B).total;
       total = t > total ? t : total;
@@ -508,7 +540,7 @@ size_t glq_e8rht_linear_group_workspace_bytes(const glq_layer* layers, int32_t c
   if (!layers || count < 1 || count > GLQ_GROUP_MAX || B < 1) return 0;
   for (int32_t k = 0; k < count; ++k)
     if (check_layer(&layers[k], true) != GLQ_OK) return 0;
-  return group_ws(layers, count, B, B == 1 && fused_group_supported(layers, count), nullptr);
+  return group_ws(layers, count, B, group_mode(layers, count, B), nullptr, nullptr);
 }
 
 glq_status glq_e8rht_linear_group(const glq_layer* layers, int32_t count, const void* const* x, glq_dtype x_dt,
@@ -523,15 +555,45 @@ glq_status glq_e8rht_linear_group(const glq_layer* layers, int32_t count, const 
   }
   if (B < 1 || B > int64_t(1) << 31) return GLQ_ERR_SHAPE;
   if (!valid_dtype(x_dt) || !valid_dtype(y_dt)) return GLQ_ERR_DTYPE;
-  const bool fused = B == 1 && fused_group_supported(layers, count);
-  size_t z_off[GLQ_GROUP_MAX];
-  const size_t need = group_ws(layers, count, B, fused, z_off);
+  const GroupMode mode = group_mode(layers, count, B);
+  size_t base[GLQ_GROUP_MAX];
+  LinearWs lw[GLQ_GROUP_MAX];
+  const size_t need = group_ws(layers, count, B, mode, base, lw);
   if (!workspace || workspace_bytes < need) return GLQ_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return GLQ_ERR_ALIGN;
-  if (fused) {
+  if (mode == GROUP_FUSED) {
     float* z[GLQ_GROUP_MAX];
-    for (int32_t k = 0; k < count; ++k) z[k] = at<float>(workspace, z_off[k]);
+    for (int32_t k = 0; k < count; ++k) z[k] = at<float>(workspace, base[k]);
     return from_hip(launch_fused_group(layers, count, x, x_dt, y, y_dt, z, stream));
+  }
+  if (mode == GROUP_I8) {
+    // per layer: u, then its int8 planes; one GEMV launch for all; per layer the output RHT
+    const void* planes[GLQ_GROUP_MAX];
+    const I8RowInfo* info[GLQ_GROUP_MAX];
+    float* z[GLQ_GROUP_MAX];
+    for (int32_t k = 0; k < count; ++k) {
+      const glq_layer& L = layers[k];
+      char* ws = at<char>(workspace, base[k]);
+      float* u = at<float>(ws, lw[k].u_off);
+      char* pl = at<char>(ws, lw[k].uq_off);
+      I8RowInfo* inf = reinterpret_cast<I8RowInfo*>(pl + align256(i8_planes_bytes(L.n_pad)));
+      hipError_t e = launch_rht_in(x[k], x_dt, B, L.n, L.n_pad, L.sign_in, u, GLQ_F32, at<float>(ws, lw[k].rin_off),
+                                   stream);
+      if (e == hipSuccess) e = launch_quant_i8(u, B, L.n_pad, pl, inf, stream);
+      if (e != hipSuccess) return GLQ_ERR_HIP;
+      planes[k] = pl;
+      info[k] = inf;
+      z[k] = at<float>(ws, lw[k].z_off);
+    }
+    if (launch_gemv_i8_group(layers, count, planes, info, B, z, stream) != hipSuccess) return GLQ_ERR_HIP;
+    for (int32_t k = 0; k < count; ++k) {
+      const glq_layer& L = layers[k];
+      char* ws = at<char>(workspace, base[k]);
+      if (launch_rht_out(z[k], lw[k].splits, B, L.m, L.m_pad, L.sign_out, y[k], y_dt, at<float>(ws, lw[k].rout_off),
+                         stream) != hipSuccess)
+        return GLQ_ERR_HIP;
+    }
+    return GLQ_OK;
   }
   for (int32_t k = 0; k < count; ++k) {
     const glq_status st = glq_e8rht_linear(&layers[k], x[k], x_dt, B, y[k], y_dt, workspace, workspace_bytes, stream);

@@ -202,8 +202,9 @@ constexpr int i8_threads() {
   return RB <= 2 ? 1024 : 512;
 }
 
+// The body of one workgroup: workgroup wg of the nwg that serve this layer.
 template <int RESID, bool CODES, int RB>
-__global__ __launch_bounds__(i8_threads<RB>(), 1) void gemv_i8_kernel(I8Args a) {
+__device__ __forceinline__ void gemv_i8_body(const I8Args& a, int wg, int nwg) {
   constexpr int kT = i8_threads<RB>();
   constexpr int kW = kT / 64;
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsDwords];
@@ -215,8 +216,8 @@ __global__ __launch_bounds__(i8_threads<RB>(), 1) void gemv_i8_kernel(I8Args a) 
 
   const int q = lane >> 4;
   const int r16 = lane & 15;
-  const int wave_g = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * kW + (tid >> 6));
-  const int nwaves = int(gridDim.x) * kW;
+  const int wave_g = __builtin_amdgcn_readfirstlane(wg * kW + (tid >> 6));
+  const int nwaves = nwg * kW;
   const int n_mine = wave_g < a.units ? (a.units - 1 - wave_g) / nwaves + 1 : 0;
   const int npos = n_mine << a.lkbs;  // (unit, block) positions of the wave's stream
   const uint8_t* idx1_8 = static_cast<const uint8_t*>(a.idx1);
@@ -393,11 +394,37 @@ __global__ __launch_bounds__(i8_threads<RB>(), 1) void gemv_i8_kernel(I8Args a) 
   if (p + 1 < npos) block(p + 1, x1, f);
 }
 
+template <int RESID, bool CODES, int RB>
+__global__ __launch_bounds__(i8_threads<RB>(), 1) void gemv_i8_kernel(I8Args a) {
+  gemv_i8_body<RESID, CODES, RB>(a, int(blockIdx.x), int(gridDim.x));
+}
+
+// Several layers' GEMVs in one launch: layer k owns the workgroups [end[k-1], end[k])
+// of the grid and runs the per-layer body over them.  The layers share RESID, CODES
+// and RB; their arguments are their own.
+struct I8GroupArgs {
+  I8Args L[GLQ_GROUP_MAX];
+  int end[GLQ_GROUP_MAX];
+  int count;
+};
+
+template <int RESID, bool CODES, int RB>
+__global__ __launch_bounds__(i8_threads<RB>(), 1) void gemv_i8_group_kernel(I8GroupArgs g) {
+  const int bid = int(blockIdx.x);
+  int k = 0;
+#pragma unroll
+  for (int j = 0; j < GLQ_GROUP_MAX - 1; ++j) k += (j < g.count - 1 && bid >= g.end[j]) ? 1 : 0;
+  k = __builtin_amdgcn_readfirstlane(k);
+  const int start = k > 0 ? g.end[k - 1] : 0;
+  gemv_i8_body<RESID, CODES, RB>(g.L[k], bid - start, g.end[k] - start);
+}
+
 struct I8Plan {
   int rb, threads, splits, kbs, lkbs, row_groups, units;
 };
 
-I8Plan i8_plan(int64_t n_pad, int64_t m_pad) {
+// cus: the CUs the layer's launch may fill (all of them for a layer on its own)
+I8Plan i8_plan(int64_t n_pad, int64_t m_pad, int cus) {
   const int KB = int(n_pad / 256);
   // four row blocks per wave (8 waves per CU) where its units fill every wave slot,
   // else one (16 waves per CU); splits (powers of two dividing KB, at most 16: the
@@ -409,7 +436,7 @@ I8Plan i8_plan(int64_t n_pad, int64_t m_pad) {
     p.rb = rb;
     p.threads = rb == 4 ? i8_threads<4>() : i8_threads<1>();
     p.row_groups = int(m_pad / (16 * rb));
-    const int64_t slots = int64_t(device_cus()) * (p.threads / 64);
+    const int64_t slots = int64_t(cus) * (p.threads / 64);
     int s = 1;
     while (int64_t(p.row_groups) * s < slots && KB % (2 * s) == 0 && KB / (2 * s) >= 2 && s < 16) s *= 2;
     p.splits = s;
@@ -446,7 +473,7 @@ bool gemv_i8_supported(const glq_layer& L) {
          (L.resid_bits != 16 || L.cb2_pack == L.cb_pack);
 }
 
-int gemv_i8_splits(int64_t n_pad, int64_t m_pad) { return i8_plan(n_pad, m_pad).splits; }
+int gemv_i8_splits(int64_t n_pad, int64_t m_pad) { return i8_plan(n_pad, m_pad, device_cus()).splits; }
 
 size_t i8_planes_bytes(int64_t n_pad) { return size_t(n_pad / 64) * 2 * 64 * 16; }
 
@@ -457,9 +484,12 @@ hipError_t launch_quant_i8(const float* u, int64_t B, int64_t n_pad, void* plane
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_i8(const glq_layer& L, const void* planes, const I8RowInfo* info, int64_t B, float* z_parts,
-                          hipStream_t stream, bool accumulate) {
-  const I8Plan p = i8_plan(L.n_pad, L.m_pad);
+namespace {
+
+bool codes_of(const glq_layer& L) { return L.index_format == GLQ_INDEX_SLOT; }
+
+I8Args i8_args(const glq_layer& L, const I8Plan& p, const void* planes, const I8RowInfo* info, int64_t B,
+               float* z_parts, bool accumulate) {
   I8Args a;
   a.planes = static_cast<const u32x4*>(planes);
   a.info = info;
@@ -467,9 +497,8 @@ hipError_t launch_gemv_i8(const glq_layer& L, const void* planes, const I8RowInf
   a.idx1 = L.idx1;
   const char* p0 = static_cast<const char*>(L.cb_pack);
   a.pack0_hdr = reinterpret_cast<const uint32_t*>(p0);
-  const bool codes = L.index_format == GLQ_INDEX_SLOT;
   a.img0 = reinterpret_cast<const uint32_t*>(
-      p0 + (codes ? pack_slot_image_offset(GLQ_CODEBOOK_ENTRIES) : pack_image_offset(GLQ_CODEBOOK_ENTRIES)));
+      p0 + (codes_of(L) ? pack_slot_image_offset(GLQ_CODEBOOK_ENTRIES) : pack_image_offset(GLQ_CODEBOOK_ENTRIES)));
   a.res_slots = L.resid_bits == 8 ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(L.cb2_pack) +
                                                                      pack_image_offset(GLQ_RESID8_ENTRIES)) + kPageCount
                                    : nullptr;
@@ -484,10 +513,90 @@ hipError_t launch_gemv_i8(const glq_layer& L, const void* planes, const I8RowInf
   a.scale = 0.5 * double(L.wscale) / 16.0;
   a.sr = double(L.resid_scale);
   a.accumulate = int(accumulate);
+  return a;
+}
+
+// workgroups of a launch over p's units, at most cus of them
+int i8_grid(const I8Plan& p, int cus) {
+  const int waves = p.threads / 64;
+  const int need = (p.units + waves - 1) / waves;
+  return need < cus ? need : cus;
+}
+
+// the CUs each layer of a group may fill: its own plan when the layers' grids fit the
+// device together, else a share of the CUs in proportion to the layer's index groups
+void i8_group_cus(const glq_layer* Ls, int count, int* cus) {
+  const int all = device_cus();
+  int64_t wgs = 0, work = 0;
+  for (int k = 0; k < count; ++k) {
+    wgs += i8_grid(i8_plan(Ls[k].n_pad, Ls[k].m_pad, all), all);
+    work += Ls[k].m_pad * (Ls[k].n_pad / 8);
+  }
+  for (int k = 0; k < count; ++k) {
+    const int64_t share = int64_t(all) * (Ls[k].m_pad * (Ls[k].n_pad / 8)) / work;
+    cus[k] = wgs <= all ? all : int(share > 1 ? share : 1);
+  }
+}
+
+template <int RESID, bool CODES>
+hipError_t launch_group_t(const I8GroupArgs& g, int rb, int wgs, hipStream_t stream) {
+  const int threads = rb == 4 ? i8_threads<4>() : i8_threads<1>();
+  switch (rb) {
+    case 1: hipLaunchKernelGGL((gemv_i8_group_kernel<RESID, CODES, 1>), dim3(unsigned(wgs)), dim3(threads), 0, stream, g); break;
+    default: hipLaunchKernelGGL((gemv_i8_group_kernel<RESID, CODES, 4>), dim3(unsigned(wgs)), dim3(threads), 0, stream, g); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_i8(const glq_layer& L, const void* planes, const I8RowInfo* info, int64_t B, float* z_parts,
+                          hipStream_t stream, bool accumulate) {
+  const I8Plan p = i8_plan(L.n_pad, L.m_pad, device_cus());
+  const I8Args a = i8_args(L, p, planes, info, B, z_parts, accumulate);
   switch (L.resid_bits) {
-    case 0: return codes ? launch_t<0, true>(a, p.rb, stream) : launch_t<0, false>(a, p.rb, stream);
-    case 8: return codes ? launch_t<8, true>(a, p.rb, stream) : launch_t<8, false>(a, p.rb, stream);
-    default: return codes ? launch_t<16, true>(a, p.rb, stream) : launch_t<16, false>(a, p.rb, stream);
+    case 0: return codes_of(L) ? launch_t<0, true>(a, p.rb, stream) : launch_t<0, false>(a, p.rb, stream);
+    case 8: return codes_of(L) ? launch_t<8, true>(a, p.rb, stream) : launch_t<8, false>(a, p.rb, stream);
+    default: return codes_of(L) ? launch_t<16, true>(a, p.rb, stream) : launch_t<16, false>(a, p.rb, stream);
+  }
+}
+
+bool gemv_i8_group_plan(const glq_layer* Ls, int count, int* splits) {
+  if (count < 1 || count > GLQ_GROUP_MAX) return false;
+  int cus[GLQ_GROUP_MAX];
+  i8_group_cus(Ls, count, cus);
+  int rb = 0;
+  for (int k = 0; k < count; ++k) {
+    if (!gemv_i8_supported(Ls[k]) || Ls[k].resid_bits != Ls[0].resid_bits || codes_of(Ls[k]) != codes_of(Ls[0]))
+      return false;
+    const I8Plan p = i8_plan(Ls[k].n_pad, Ls[k].m_pad, cus[k]);
+    if (k == 0) rb = p.rb;
+    if (p.rb != rb) return false;
+    if (splits) splits[k] = p.splits;
+  }
+  return true;
+}
+
+hipError_t launch_gemv_i8_group(const glq_layer* Ls, int count, const void* const* planes,
+                                const I8RowInfo* const* info, int64_t B, float* const* z_parts, hipStream_t stream) {
+  int cus[GLQ_GROUP_MAX];
+  i8_group_cus(Ls, count, cus);
+  I8GroupArgs g;
+  int wgs = 0, rb = 1;
+  for (int k = 0; k < count; ++k) {
+    const I8Plan p = i8_plan(Ls[k].n_pad, Ls[k].m_pad, cus[k]);
+    g.L[k] = i8_args(Ls[k], p, planes[k], info[k], B, z_parts[k], false);
+    wgs += i8_grid(p, cus[k]);
+    g.end[k] = wgs;
+    rb = p.rb;  // the same for every layer (gemv_i8_group_plan)
+  }
+  for (int k = count; k < GLQ_GROUP_MAX; ++k) g.end[k] = 0x7FFFFFFF;
+  g.count = count;
+  const bool codes = codes_of(Ls[0]);
+  switch (Ls[0].resid_bits) {
+    case 0: return codes ? launch_group_t<0, true>(g, rb, wgs, stream) : launch_group_t<0, false>(g, rb, wgs, stream);
+    case 8: return codes ? launch_group_t<8, true>(g, rb, wgs, stream) : launch_group_t<8, false>(g, rb, wgs, stream);
+    default: return codes ? launch_group_t<16, true>(g, rb, wgs, stream) : launch_group_t<16, false>(g, rb, wgs, stream);
   }
 }
 

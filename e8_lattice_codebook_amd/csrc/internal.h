@@ -197,6 +197,13 @@ hipError_t launch_quant_i8(const float* u, int64_t B, int64_t n_pad, void* plane
                            hipStream_t stream);
 hipError_t launch_gemv_i8(const glq_layer& layer, const void* planes, const I8RowInfo* info, int64_t B,
                           float* z_parts, hipStream_t stream, bool accumulate = false);
+// Up to GLQ_GROUP_MAX layers' int8 GEMVs in one launch, the CUs shared among them:
+// gemv_i8_group_plan says whether the layers can share one (every layer supported, one
+// residual stage, index format and row blocks per wave) and gives each layer's split
+// count (its z_parts hold splits[k] x B x m_pad); one pass per layer, no accumulation.
+bool gemv_i8_group_plan(const glq_layer* layers, int count, int* splits);
+hipError_t launch_gemv_i8_group(const glq_layer* layers, int count, const void* const* planes,
+                                const I8RowInfo* const* info, int64_t B, float* const* z_parts, hipStream_t stream);
 
 // The whole linear for B = 1 in two launches (input RHT, decode matmul with the
 // LDS codebook and the row-local part of the output RHT; then the fixed-order

@@ -113,9 +113,27 @@ def test_other_recipes(gpu_codebooks):
 
 
 def test_fallback_batch_and_mixed_n_pad(gpu_codebooks):
-    # B = 5 and layers of different n_pad run one call after another: the single calls' bits
-    check_group(gpu_codebooks, "smollm3_block", [0, 1, 2], B=5, x_of={1: 0, 2: 0}, own_plans=True)
+    # B = 3 on layers the int8 path does not take (q, k, v: the staged decode) and layers
+    # of different n_pad run one call after another: the single calls' bits
+    check_group(gpu_codebooks, "smollm3_block", [0, 1, 2], B=3, x_of={1: 0, 2: 0}, own_plans=True)
     check_group(gpu_codebooks, "smollm3_block", [3, 6], own_plans=True)
+
+
+def test_int8_group_own_plans(gpu_codebooks):
+    # 2 <= B <= 16 with every layer on the int8 path: one GEMV launch for q, k and v at
+    # B = 5, whose grids fit the device together (each layer's own plan: single-call bits)
+    check_group(gpu_codebooks, "smollm3_block", [0, 1, 2], B=5, x_of={1: 0, 2: 0}, own_plans=True)
+
+
+@pytest.mark.parametrize("B", [4, 16])
+def test_int8_group_devstral_gate_up(gpu_codebooks, B):
+    # the Devstral gate and up layers at B = 4 and 16 on shared CUs (128 each)
+    check_group(gpu_codebooks, "devstral_mlp", [0, 1], B=B, x_of={1: 0})
+
+
+def test_int8_group_smollm3_gate_up_uneven(gpu_codebooks):
+    # SmolLM3 gate, up and k at B = 5: uneven shares of the CUs
+    check_group(gpu_codebooks, "smollm3_block", [4, 5, 1], B=5, x_of={5: 4, 1: 4})
 
 
 def test_repeat_bit_identical(gpu_codebooks):
