@@ -540,6 +540,27 @@ def bench_configs(glq, synth, cb, dev, args, log, devstral=None):
                 del ws, x, y
             del cps
             torch.cuda.empty_cache()
+        if key == "devstral_mlp" and devstral is not None and args.index_format == "slot":
+            # gate and up (one input) as one glq_e8rht_linear_group call: one int8 GEMV launch
+            host, rows, ncop = devstral
+            for B in batches:
+                _, raw = synth.make_x(host[0].n, B, wl.act_dtype, wl.seed, 0)
+                x = torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
+                ys = [torch.empty((B, l.m), dtype=tdt, device=dev) for l in host[:2]]
+                gws = torch.empty(max(1, glq.linear_group_workspace_bytes(rows[0][:2], B)), dtype=torch.uint8,
+                                  device=dev)
+                calls = [lambda r=r: glq.e8rht_linear_group(r[:2], [x, x], outs=ys, workspace=gws) for r in rows]
+                ms = time_calls(torch, calls, max(1, math.ceil(args.config_calls / len(rows))))
+                nbytes = sum(l.index_bytes() + B * (l.n + l.m) * ab + l.n_pad + l.m_pad for l in host[:2])
+                gbs = nbytes / (ms * 1e-3) / 1e9
+                log("bench: %s gate+up grouped B=%d: %.2f us per call, %.1f GB/s" % (key, B, ms * 1e3, gbs))
+                out.append({"workload": key, "layer": "gate+up as one glq_e8rht_linear_group call", "B": B,
+                            "path": "grouped int8 GEMV (one launch for both layers)",
+                            "us_per_call": round(ms * 1e3, 3), "value": round(gbs, 2), "unit": "GB/s",
+                            "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_call": int(nbytes),
+                            "copies": len(rows)})
+                del x, ys, gws
+            torch.cuda.empty_cache()
     return out
 
 

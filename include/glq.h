@@ -434,9 +434,12 @@ glq_status glq_e8rht_linear(const glq_layer* layer, const void* x, glq_dtype x_d
  *              separate workspaces
  * B = 1 and layers of one n_pad, one stage layout (the residual stage and any further
  * stages of 5-8 bpw) and one index format, each one the two-launch B = 1 path would
- * take: one pair of launches for
- * all of them, the device's CUs shared among the layers in proportion to their index
- * bytes when their own plans would not fit together.  Otherwise the layers run one
+ * take: one pair of launches for all of them, the device's CUs shared among the
+ * layers in proportion to their index bytes when their own plans would not fit
+ * together.  2 <= B <= 16 with at least two layers of one n_pad, one residual stage
+ * and index format and no further stages, each on the int8 matrix-unit path: the input
+ * transforms and activation planes per layer, one GEMV launch for all layers (CUs
+ * shared the same way), the output transforms per layer.  Otherwise the layers run one
  * after another as glq_e8rht_linear on the same stream and workspace.  Every y[k] is
  * bit-identical to the single call's result when the layers keep their own plans and
  * equal to it within rounding order otherwise (the reductions follow each layer's plan).
