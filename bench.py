@@ -540,9 +540,13 @@ def bench_configs(glq, synth, cb, dev, args, log, devstral=None):
                 del ws, x, y
             del cps
             torch.cuda.empty_cache()
-        if key == "devstral_mlp" and devstral is not None and args.index_format == "slot":
+        if key == "devstral_mlp" and args.index_format == "slot":
             # gate and up (one input) as one glq_e8rht_linear_group call: one int8 GEMV launch
-            host, rows, ncop = devstral
+            if devstral is not None:
+                host, rows, _ = devstral
+            else:  # the configs leg alone: three rotating copies of gate and up
+                host = [synth.make_layer(wl.layers[k], wl.resid_bits, wl.seed, k) for k in (0, 1)]
+                rows = [[glq.QuantizedLayer.from_synth(h, cb).to_slot_codes() for h in host] for _ in range(3)]
             for B in batches:
                 _, raw = synth.make_x(host[0].n, B, wl.act_dtype, wl.seed, 0)
                 x = torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
