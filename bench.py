@@ -137,7 +137,7 @@ def main():
     if args.only and args.only != "decode":
         fn = {"configs": lambda: bench_configs(glq, synth, cb, dev, args, log),
               "prefill": lambda: bench_prefill(glq, synth, cb, dev, args, log),
-              "block": lambda: bench_block_graph(glq, synth, cb, dev, args, log),
+              "block": lambda: {"b1": bench_block_graph(glq, synth, cb, dev, args, log), "b5": bench_block_b5(glq, synth, cb, dev, args, log)},
               "recipes": lambda: bench_recipes(glq, synth, cb, dev, args, log, None),
               "blockdiag": lambda: bench_blockdiag(glq, synth, cb, dev, args, log, None),
               "kv": lambda: bench_kv(glq, synth, cb, dev, args, log)}[args.only]
@@ -335,6 +335,7 @@ def main():
 
     if not args.no_block:
         result["block_b1"] = bench_block_graph(glq, synth, cb, dev, args, log)
+        result["block_b5"] = bench_block_b5(glq, synth, cb, dev, args, log)
 
     if not args.no_recipes and B == 1:
         # the recipes run one call per layer: compared with the same form at 4 bpw
@@ -737,6 +738,56 @@ def bench_prefill(glq, synth, cb, dev, args, log):
                      "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
                      "flops_per_launch": flops},
     }
+
+
+def bench_block_b5(glq, synth, cb, dev, args, log, B=5):
+    """The seven linears of a SmolLM3-3B block at B = 5 (3 bpw, fp16, slot codes): as
+    seven glq_e8rht_linear calls and as four glq_e8rht_linear_group calls (q+k+v, o,
+    gate+up, down), the q+k+v and gate+up groups sharing one int8 GEMV launch each."""
+    import numpy as np
+    import torch
+
+    wl = synth.WORKLOADS["smollm3_block"]
+    host = [synth.make_layer(sh, wl.resid_bits, wl.seed, k) for k, sh in enumerate(wl.layers)]
+    qs = [glq.QuantizedLayer.from_synth(l, cb) for l in host]
+    if args.index_format == "slot":
+        qs = [q.to_slot_codes() for q in qs]
+    xs = []
+    for k, l in enumerate(host):
+        _, raw = synth.make_x(l.n, B, wl.act_dtype, wl.seed, k)
+        xs.append(torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.float16))
+    ys = [torch.empty((B, l.m), dtype=torch.float16, device=dev) for l in host]
+    groups = [(0, 1, 2), (3,), (4, 5), (6,)]
+    ws = torch.empty(max(max(glq.linear_workspace_bytes(q, B) for q in qs),
+                         max(glq.linear_group_workspace_bytes([qs[k] for k in g], B) for g in groups)),
+                     dtype=torch.uint8, device=dev)
+
+    def calls():
+        for k in range(len(qs)):
+            glq.e8rht_linear(qs[k], xs[k], out=ys[k], workspace=ws)
+
+    def grouped():
+        for g in groups:
+            glq.e8rht_linear_group([qs[k] for k in g], [xs[k] for k in g], outs=[ys[k] for k in g], workspace=ws)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {"workload": "SmolLM3-3B decoder block, 7 linears, 3 bpw, fp16 activations, B=%d, indices resident in "
+                       "the 256 MB MALL across iterations" % B}
+    n = args.block_steps
+    for name, fn in (("calls", calls), ("grouped", grouped)):
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_ms_per_block"] = round(e0.elapsed_time(e1) / n, 5)
+    out["speedup_grouped"] = round(out["calls_ms_per_block"] / out["grouped_ms_per_block"], 3)
+    log("bench: SmolLM3 block B=%d: %.4f ms as seven calls, %.4f ms as four groups" % (
+        B, out["calls_ms_per_block"], out["grouped_ms_per_block"]))
+    return out
 
 
 def bench_block_graph(glq, synth, cb, dev, args, log):
